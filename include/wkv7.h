@@ -1,0 +1,186 @@
+/*
+ * wkv7.h -- C-ABI of the MI355X (gfx950) RWKV-7 WKV7 / time-mix library.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains caller memory; scratch comes from the
+ *    caller's workspace argument where a call needs one.
+ *  - Work is enqueued on `stream` (NULL = the default stream) with no host
+ *    synchronisation; results are valid once the stream has reached them.
+ *  - Token tensors are [B][T][H][N] row-major (equivalently [B][T][C] with
+ *    C = H*N, channel c = h*N + n).  States are [B][H][N][N] fp32 with
+ *    S[i][j]: i the value index (row), j the key index (column).
+ *  - Return value: 0 on success, or a negative wkv7_status.  Arguments are
+ *    validated before anything is enqueued; on error nothing is enqueued and
+ *    wkv7_last_error() describes the first problem found.
+ *  - N must be 64.  Pointers must be 16-byte aligned (8-byte for bf16 data).
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum wkv7_status {
+  WKV7_OK = 0,
+  WKV7_EINVAL = -1, /* bad shape, NULL required pointer, misalignment, bad alias */
+  WKV7_EHIP = -2,   /* a HIP launch or runtime error */
+  WKV7_ENOSPC = -3  /* workspace smaller than the size query returned */
+};
+
+enum wkv7_dtype {
+  WKV7_F32 = 0,  /* fp32 token tensors */
+  WKV7_BF16 = 1  /* bf16 token tensors (state and accumulation stay fp32) */
+};
+
+/* Thread-local description of the last error (empty string if none). */
+const char *wkv7_last_error(void);
+
+/* Checkpoint interval L used by wkv7_forward / wkv7_backward (tokens). */
+int wkv7_checkpoint_interval(void);
+
+/* Number of fp32 elements of the checkpoint buffer: B*H*ceil(T/L)*N*N. */
+size_t wkv7_checkpoint_floats(int B, int T, int H, int N);
+
+/*
+ * WKV7 forward.  Per (b,h), starting from S = s0 (NULL = zero), for t = 0..T-1
+ *     sa  = S a_t                                   (old state)
+ *     S   = S diag(w_t) + sa b_t^T + v_t k_t^T
+ *     y_t = S r_t                                   (updated state)
+ * Pages: "Foundry/cuda_kernels/timemix.cu" (forward driver, k_composites: the
+ * WKV7 kernel receives r, w, k', v', a = -kk, b = kk*a) and the per-head WKV
+ * state-backward block of "infotheory .../rwkv7/model.rs" (read-out from the
+ * updated state, rank-1 term from the old one).
+ *
+ * r,w,k,v,a,b: [B][T][H][N] of `dtype`.  y: [B][T][H][N] of `dtype` (written).
+ * s0: [B][H][N][N] fp32 or NULL.  sT: [B][H][N][N] fp32 or NULL (written;
+ * may equal s0 for an in-place state update).  ckpt: NULL, or
+ * wkv7_checkpoint_floats() fp32 laid out [B][H][ceil(T/L)][N][N], where
+ * checkpoint c is the state after c*L tokens (c = 0 holds s0); it is what
+ * wkv7_backward recomputes from.  T >= 1, B >= 1, H >= 1.
+ */
+int wkv7_forward(int B, int T, int H, int N, int dtype,
+                 const void *r, const void *w, const void *k, const void *v,
+                 const void *a, const void *b, const float *s0,
+                 void *y, float *sT, float *ckpt, hipStream_t stream);
+
+/* Workspace bytes wkv7_backward needs (0 when ckpt is supplied). */
+size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
+
+/*
+ * WKV7 backward: gradients of L = <dy, y> + <dsT, S_T> for the forward above
+ * (reverse recurrence; with G = dL/dS_t, step t back:
+ *     G += dy_t r_t^T;  dr_t = S_t^T dy_t;  dv_t = G k_t;  dk_t = G^T v_t;
+ *     db_t = G^T sa_t;  dsa = G b_t;  dw_t = colsum(G .* S_{t-1});
+ *     da_t = S_{t-1}^T dsa;  G = G diag(w_t) + dsa a_t^T ).
+ * Same pages as wkv7_forward; the model.rs block gives these local terms.
+ *
+ * ckpt: the forward's checkpoints, or NULL (then they are recomputed into the
+ * workspace).  dy: [B][T][H][N] `dtype`.  dsT, s0: fp32 [B][H][N][N] or NULL.
+ * dr,dw,dk,dv,da,db: [B][T][H][N] `dtype` (written).  ds0: fp32 or NULL.
+ */
+int wkv7_backward(int B, int T, int H, int N, int dtype,
+                  const void *r, const void *w, const void *k, const void *v,
+                  const void *a, const void *b, const float *s0, const float *ckpt,
+                  const void *dy, const float *dsT,
+                  void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                  float *ds0, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Single-token streaming decode: the T = 1 forward with the state updated in
+ * place.  Pages: the recurrence as for wkv7_forward; the per-layer streaming
+ * state of "infotheory .../rwkv7/model.rs" (LayerState.att_state, [H][N][N]).
+ * r,w,k,v,a,b,y: [B][H][N] `dtype`; state: [B][H][N][N] fp32 (read+written).
+ */
+int wkv7_step(int B, int H, int N, int dtype,
+              const void *r, const void *w, const void *k, const void *v,
+              const void *a, const void *b, float *state, void *y,
+              hipStream_t stream);
+
+/* ------------------------------------------------------------ time-mix -- */
+
+/* Block geometry.  C = H*N, N = 64; LoRA ranks Dw, Da, Dv, Dg; layer_id 0
+ * is the first block (publishes v_first, has no value-residual LoRA). */
+typedef struct {
+  int C, H, N, Dw, Da, Dv, Dg, layer_id;
+} tm_shape;
+
+/* fp32 weights, row-major [in][out] (y = x W), as on the timemix.cu page.
+ * v0/V1/V2 are ignored (may be NULL) when layer_id == 0. */
+typedef struct {
+  const float *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g; /* [C] token-shift lerp */
+  const float *Wr, *Wk, *Wv, *Wo;                       /* [C][C] */
+  const float *w0, *W1, *W2;                            /* [C], [C][Dw], [Dw][C] */
+  const float *a0, *A1, *A2;                            /* [C], [C][Da], [Da][C] */
+  const float *v0, *V1, *V2;                            /* [C], [C][Dv], [Dv][C] */
+  const float *G1, *G2;                                 /* [C][Dg], [Dg][C] */
+  const float *k_k, *k_a, *r_k;                         /* [C] */
+  const float *ln_w, *ln_b;                             /* [C] group-norm affine */
+} tm_weights;
+
+/* Gradients, same fields and shapes; every field is written (=, not +=). */
+typedef struct {
+  float *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
+  float *Wr, *Wk, *Wv, *Wo;
+  float *w0, *W1, *W2;
+  float *a0, *A1, *A2;
+  float *v0, *V1, *V2;
+  float *G1, *G2;
+  float *k_k, *k_a, *r_k;
+  float *ln_w, *ln_b;
+} tm_grads;
+
+/* Bytes of the activation cache timemix_forward can leave for the backward. */
+size_t timemix_cache_bytes(const tm_shape *s, int B, int T);
+/* Workspace bytes for timemix_forward / timemix_backward. */
+size_t timemix_forward_workspace_bytes(const tm_shape *s, int B, int T);
+size_t timemix_backward_workspace_bytes(const tm_shape *s, int B, int T);
+
+/*
+ * Time-mix forward (no residual; the block adds it).  Pages:
+ * "Foundry/cuda_kernels/timemix.cu" forward driver and kernels k_tokenshift
+ * .. k_mul; LoRA formulas from the AttentionWeights of "infotheory
+ * .../rwkv7/model.rs":
+ *   xs_c = x + (x_prev_shift - x) mu_c  for c in r,w,k,v,a,g
+ *   r = xs_r Wr; k = xs_k Wk; v = xs_v Wv
+ *   w = exp(-0.606531 sigmoid(w0 + tanh(xs_w W1) W2))
+ *   a = sigmoid(a0 + (xs_a A1) A2);  g = sigmoid(xs_g G1) G2
+ *   kk = l2norm_head(k * k_k);  k' = k (1 + (a - 1) k_a)
+ *   v' = v (layer 0, v_first := v)  or  v + (v_first - v) sigmoid(v0 + (xs_v V1) V2)
+ *   y  = WKV7(r, w, k', v', -kk, kk * a; s0)
+ *   out = ((groupnorm_head(y) * ln_w + ln_b) + (sum_head r k' r_k) v') * g  Wo
+ * x: [B][T][C]; x_prev: [B][C] or NULL (zeros) -- the token before x[:,0];
+ * v_first: [B][T][C], written on layer 0, read otherwise; s0/sT: fp32
+ * [B][H][N][N] or NULL; out: [B][T][C] (written); x_last: [B][C] or NULL
+ * (written with x[:, T-1], the next call's x_prev); cache: NULL or
+ * timemix_cache_bytes() bytes kept for timemix_backward.
+ */
+int timemix_forward(const tm_shape *s, const tm_weights *W, int B, int T,
+                    const float *x, const float *x_prev, float *v_first,
+                    const float *s0, float *sT, float *out, float *x_last,
+                    void *cache, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Time-mix backward: gradients of L = <dout, out> + <dsT, S_T>
+ * (+ <dv_first_in, v_first> on layer 0).  Pages: "Foundry/cuda_kernels/
+ * timemix.cu" backward driver (phase order) and kernels k_split ..
+ * k_tokenshift_bwd.  cache: the forward's cache for the same inputs, or NULL
+ * (the forward is recomputed into the workspace).  G: every field written.
+ * dx: [B][T][C]; dx_prev: [B][C] or NULL; dv_first_in: layer 0 only, [B][T][C]
+ * or NULL; dv_first_out: layer > 0 only, [B][T][C] or NULL; ds0: fp32 or NULL.
+ */
+int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
+                     const float *x, const float *x_prev, const float *v_first,
+                     const float *s0, const float *dout, const float *dsT,
+                     const void *cache, tm_grads *G, float *dx, float *dx_prev,
+                     const float *dv_first_in, float *dv_first_out, float *ds0,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WKV7_H */

@@ -1,0 +1,267 @@
+"""ctypes binding of the C-ABI in ``include/wkv7.h`` (argument marshalling only).
+
+Each function has the name of the C call it wraps.  PyTorch supplies device
+memory and the current HIP stream; every step of the computation runs in the
+HIP library.  Output and workspace tensors are allocated here with
+``torch.empty`` when the caller does not pass them.  If the library has not
+been built this module raises instead of falling back to anything else.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libwkv7_amd.so")
+
+WKV7_F32, WKV7_BF16 = 0, 1
+WEIGHT_FIELDS = ("mu_r", "mu_w", "mu_k", "mu_v", "mu_a", "mu_g", "Wr", "Wk", "Wv", "Wo",
+                 "w0", "W1", "W2", "a0", "A1", "A2", "v0", "V1", "V2", "G1", "G2",
+                 "k_k", "k_a", "r_k", "ln_w", "ln_b")
+
+
+class TmShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("C", "H", "N", "Dw", "Da", "Dv", "Dg", "layer_id")]
+
+
+class TmWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class TmGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class Wkv7Error(RuntimeError):
+    pass
+
+
+_lib = None
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Wkv7Error(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.wkv7_last_error.restype = ctypes.c_char_p
+        L.wkv7_checkpoint_interval.restype = _i
+        L.wkv7_checkpoint_floats.argtypes = [_i] * 4
+        L.wkv7_checkpoint_floats.restype = _sz
+        L.wkv7_forward.argtypes = [_i] * 5 + [_vp] * 11
+        L.wkv7_forward.restype = _i
+        L.wkv7_backward_workspace_bytes.argtypes = [_i] * 5
+        L.wkv7_backward_workspace_bytes.restype = _sz
+        L.wkv7_backward.argtypes = [_i] * 5 + [_vp] * 17 + [_vp, _sz, _vp]
+        L.wkv7_backward.restype = _i
+        L.wkv7_step.argtypes = [_i] * 4 + [_vp] * 9
+        L.wkv7_step.restype = _i
+        sp = ctypes.POINTER(TmShape)
+        for fn in ("timemix_cache_bytes", "timemix_forward_workspace_bytes",
+                   "timemix_backward_workspace_bytes"):
+            getattr(L, fn).argtypes = [sp, _i, _i]
+            getattr(L, fn).restype = _sz
+        L.timemix_forward.argtypes = [sp, ctypes.POINTER(TmWeights), _i, _i] + [_vp] * 9 + [_sz, _vp]
+        L.timemix_forward.restype = _i
+        L.timemix_backward.argtypes = ([sp, ctypes.POINTER(TmWeights), _i, _i] + [_vp] * 6 +
+                                       [_vp, ctypes.POINTER(TmGrads)] + [_vp] * 6 + [_sz, _vp])
+        L.timemix_backward.restype = _i
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise Wkv7Error(f"status {rc}: {lib().wkv7_last_error().decode()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _opt(t, shape, dtype, name):
+    return None if t is None else _need(t, shape, dtype, name)
+
+
+def _dt(x):
+    if x.dtype == torch.float32:
+        return WKV7_F32
+    if x.dtype == torch.bfloat16:
+        return WKV7_BF16
+    raise ValueError(f"unsupported dtype {x.dtype}")
+
+
+# ------------------------------------------------------------------ WKV7 --
+def wkv7_checkpoint_interval():
+    return lib().wkv7_checkpoint_interval()
+
+
+def wkv7_checkpoint_floats(B, T, H, N=64):
+    return lib().wkv7_checkpoint_floats(B, T, H, N)
+
+
+def wkv7_forward(r, w, k, v, a, b, s0=None, y=None, sT=None, ckpt=None,
+                 want_state=True, want_ckpt=False):
+    """y = WKV7(r, w, k, v, a, b; s0).  Returns (y, sT or None, ckpt or None)."""
+    B, T, H, N = r.shape
+    dt = r.dtype
+    for n, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _need(t, (B, T, H, N), dt, n)
+    _opt(s0, (B, H, N, N), torch.float32, "s0")
+    y = _opt(y, (B, T, H, N), dt, "y") if y is not None else torch.empty_like(r)
+    if sT is None and want_state:
+        sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32)
+    _opt(sT, (B, H, N, N), torch.float32, "sT")
+    if ckpt is None and want_ckpt:
+        ckpt = torch.empty(wkv7_checkpoint_floats(B, T, H, N), device=r.device, dtype=torch.float32)
+    _opt(ckpt, (wkv7_checkpoint_floats(B, T, H, N),), torch.float32, "ckpt")
+    _check(lib().wkv7_forward(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
+                              _p(s0), _p(y), _p(sT), _p(ckpt), _stream()))
+    return y, sT, ckpt
+
+
+def wkv7_backward(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, want_ds0=True):
+    """Gradients of <dy, y> + <dsT, S_T>.  Returns dict dr, dw, dk, dv, da, db, ds0."""
+    B, T, H, N = r.shape
+    dt = r.dtype
+    for n, t in zip(("r", "w", "k", "v", "a", "b", "dy"), (r, w, k, v, a, b, dy)):
+        _need(t, (B, T, H, N), dt, n)
+    _opt(s0, (B, H, N, N), torch.float32, "s0")
+    _opt(dsT, (B, H, N, N), torch.float32, "dsT")
+    _opt(ckpt, (wkv7_checkpoint_floats(B, T, H, N),), torch.float32, "ckpt")
+    out = {n: torch.empty_like(r) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    out["ds0"] = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_ds0 else None
+    nbytes = lib().wkv7_backward_workspace_bytes(B, T, H, N, int(ckpt is not None))
+    ws = torch.empty(max(nbytes, 1), device=r.device, dtype=torch.uint8)
+    _check(lib().wkv7_backward(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
+                               _p(s0), _p(ckpt), _p(dy), _p(dsT), _p(out["dr"]), _p(out["dw"]),
+                               _p(out["dk"]), _p(out["dv"]), _p(out["da"]), _p(out["db"]),
+                               _p(out["ds0"]), _p(ws), nbytes, _stream()))
+    return out
+
+
+def wkv7_step(r, w, k, v, a, b, state, y=None):
+    """One decode token; r..b are [B][H][N]; state [B][H][N][N] is updated in place."""
+    B, H, N = r.shape
+    dt = r.dtype
+    for n, t in zip("rwkvab", (r, w, k, v, a, b)):
+        _need(t, (B, H, N), dt, n)
+    _need(state, (B, H, N, N), torch.float32, "state")
+    y = _opt(y, (B, H, N), dt, "y") if y is not None else torch.empty_like(r)
+    _check(lib().wkv7_step(B, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
+                           _p(state), _p(y), _stream()))
+    return y
+
+
+# -------------------------------------------------------------- time-mix --
+def tm_shape(C, H, Dw, Da, Dv, Dg, layer_id, N=64):
+    return TmShape(C, H, N, Dw, Da, Dv, Dg, layer_id)
+
+
+def _weight_shapes(s):
+    C = s.C
+    shp = {n: (C,) for n in ("mu_r", "mu_w", "mu_k", "mu_v", "mu_a", "mu_g", "w0", "a0", "v0",
+                             "k_k", "k_a", "r_k", "ln_w", "ln_b")}
+    shp.update(Wr=(C, C), Wk=(C, C), Wv=(C, C), Wo=(C, C), W1=(C, s.Dw), W2=(s.Dw, C),
+               A1=(C, s.Da), A2=(s.Da, C), V1=(C, s.Dv), V2=(s.Dv, C), G1=(C, s.Dg), G2=(s.Dg, C))
+    return shp
+
+
+def _pack_weights(s, W):
+    shp = _weight_shapes(s)
+    cw = TmWeights()
+    for n in WEIGHT_FIELDS:
+        if s.layer_id == 0 and n in ("v0", "V1", "V2"):
+            setattr(cw, n, None)
+            continue
+        setattr(cw, n, _need(W[n], shp[n], torch.float32, n).data_ptr())
+    return cw
+
+
+def timemix_cache_bytes(s, B, T):
+    return lib().timemix_cache_bytes(ctypes.byref(s), B, T)
+
+
+def timemix_forward(s, W, x, x_prev=None, v_first=None, s0=None, want_state=True,
+                    want_cache=False, want_x_last=False):
+    """Returns dict out, sT, x_last, v_first, cache (None where not requested)."""
+    B, T, C = x.shape
+    H, N = s.H, s.N
+    _need(x, (B, T, C), torch.float32, "x")
+    _opt(x_prev, (B, C), torch.float32, "x_prev")
+    _opt(s0, (B, H, N, N), torch.float32, "s0")
+    if s.layer_id == 0:
+        v_first = torch.empty_like(x)
+    else:
+        _need(v_first, (B, T, C), torch.float32, "v_first")
+    cw = _pack_weights(s, W)
+    out = torch.empty_like(x)
+    sT = torch.empty((B, H, N, N), device=x.device, dtype=torch.float32) if want_state else None
+    x_last = torch.empty((B, C), device=x.device, dtype=torch.float32) if want_x_last else None
+    nbytes = timemix_cache_bytes(s, B, T)
+    buf = torch.empty(nbytes, device=x.device, dtype=torch.uint8)
+    cache = buf if want_cache else None
+    ws = None if want_cache else buf
+    _check(lib().timemix_forward(ctypes.byref(s), ctypes.byref(cw), B, T, _p(x), _p(x_prev),
+                                 _p(v_first), _p(s0), _p(sT), _p(out), _p(x_last), _p(cache),
+                                 _p(ws), 0 if ws is None else nbytes, _stream()))
+    return dict(out=out, sT=sT, x_last=x_last, v_first=v_first, cache=cache)
+
+
+def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None, cache=None,
+                     dv_first_in=None, want_dx_prev=True, want_ds0=True, want_dv_first=True):
+    """Returns dict grads (per weight), dx, dx_prev, dv_first_out, ds0."""
+    B, T, C = x.shape
+    H, N = s.H, s.N
+    _need(x, (B, T, C), torch.float32, "x")
+    _need(dout, (B, T, C), torch.float32, "dout")
+    _opt(x_prev, (B, C), torch.float32, "x_prev")
+    _opt(s0, (B, H, N, N), torch.float32, "s0")
+    _opt(dsT, (B, H, N, N), torch.float32, "dsT")
+    if s.layer_id > 0:
+        _need(v_first, (B, T, C), torch.float32, "v_first")
+    if cache is not None:
+        _need(cache, (timemix_cache_bytes(s, B, T),), torch.uint8, "cache")
+    if s.layer_id == 0:
+        _opt(dv_first_in, (B, T, C), torch.float32, "dv_first_in")
+    cw = _pack_weights(s, W)
+    shp = _weight_shapes(s)
+    grads = {}
+    cg = TmGrads()
+    for n in WEIGHT_FIELDS:
+        if s.layer_id == 0 and n in ("v0", "V1", "V2"):
+            setattr(cg, n, None)
+            continue
+        grads[n] = torch.empty(shp[n], device=x.device, dtype=torch.float32)
+        setattr(cg, n, grads[n].data_ptr())
+    dx = torch.empty_like(x)
+    dx_prev = torch.empty((B, C), device=x.device, dtype=torch.float32) if want_dx_prev else None
+    dvf_out = torch.empty_like(x) if (s.layer_id > 0 and want_dv_first) else None
+    ds0 = torch.empty((B, H, N, N), device=x.device, dtype=torch.float32) if want_ds0 else None
+    nbytes = lib().timemix_backward_workspace_bytes(ctypes.byref(s), B, T)
+    ws = torch.empty(nbytes, device=x.device, dtype=torch.uint8)
+    _check(lib().timemix_backward(ctypes.byref(s), ctypes.byref(cw), B, T, _p(x), _p(x_prev),
+                                  _p(v_first), _p(s0), _p(dout), _p(dsT), _p(cache),
+                                  ctypes.byref(cg), _p(dx), _p(dx_prev),
+                                  _p(dv_first_in if s.layer_id == 0 else None), _p(dvf_out),
+                                  _p(ds0), _p(ws), nbytes, _stream()))
+    return dict(grads=grads, dx=dx, dx_prev=dx_prev, dv_first_out=dvf_out, ds0=ds0)

@@ -1,0 +1,492 @@
+// C-ABI entry points (include/wkv7.h): argument validation, workspace carving
+// and the launch sequences of the WKV7 and time-mix calls.  Validation runs
+// before anything is enqueued, so every error path can be exercised without
+// a GPU.
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/wkv7.h"
+#include "common.hpp"
+#include "timemix_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(WKV7_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHK(expr, what)                      \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_tok_ptr(const void* p, const char* name, int dtype, bool required) {
+  if (!p) return required ? fail(WKV7_EINVAL, "%s is NULL", name) : WKV7_OK;
+  if (!aligned(p, dtype == WKV7_BF16 ? 8 : 16))
+    return fail(WKV7_EINVAL, "%s is not %d-byte aligned", name, dtype == WKV7_BF16 ? 8 : 16);
+  return WKV7_OK;
+}
+
+int check_f32_ptr(const void* p, const char* name, bool required) {
+  return check_tok_ptr(p, name, WKV7_F32, required);
+}
+
+int check_wkv_shape(int B, int T, int H, int N, int dtype) {
+  if (N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", N);
+  if (B < 1 || T < 1 || H < 1) return fail(WKV7_EINVAL, "B, T, H must be >= 1 (got %d, %d, %d)", B, T, H);
+  if (dtype != WKV7_F32 && dtype != WKV7_BF16) return fail(WKV7_EINVAL, "unknown dtype %d", dtype);
+  if ((size_t)B * T * H * N > ((size_t)1 << 40)) return fail(WKV7_EINVAL, "problem too large");
+  return WKV7_OK;
+}
+
+size_t ckpt_floats(int B, int T, int H) {
+  const int L = wkv7_ckpt_interval_const();
+  return (size_t)B * H * ((T + L - 1) / L) * WKV7_N * WKV7_N;
+}
+
+// bump allocator over a workspace (or a dry run for size queries)
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  float* take(size_t nfloats) {
+    off = (off + 255) & ~(size_t)255;
+    float* p = base ? (float*)(base + off) : nullptr;
+    off += nfloats * sizeof(float);
+    return p;
+  }
+};
+
+#define CHK(x)                 \
+  do {                         \
+    int rc_ = (x);             \
+    if (rc_ != WKV7_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+// ------------------------------------------------------------------ WKV7 --
+extern "C" const char* wkv7_last_error(void) { return g_err; }
+
+extern "C" int wkv7_checkpoint_interval(void) { return wkv7_ckpt_interval_const(); }
+
+extern "C" size_t wkv7_checkpoint_floats(int B, int T, int H, int N) {
+  if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
+  return ckpt_floats(B, T, H);
+}
+
+extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r, const void* w,
+                            const void* k, const void* v, const void* a, const void* b,
+                            const float* s0, void* y, float* sT, float* ckpt, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_wkv_shape(B, T, H, N, dtype));
+  CHK(check_tok_ptr(r, "r", dtype, true));
+  CHK(check_tok_ptr(w, "w", dtype, true));
+  CHK(check_tok_ptr(k, "k", dtype, true));
+  CHK(check_tok_ptr(v, "v", dtype, true));
+  CHK(check_tok_ptr(a, "a", dtype, true));
+  CHK(check_tok_ptr(b, "b", dtype, true));
+  CHK(check_tok_ptr(y, "y", dtype, true));
+  CHK(check_f32_ptr(s0, "s0", false));
+  CHK(check_f32_ptr(sT, "sT", false));
+  CHK(check_f32_ptr(ckpt, "ckpt", false));
+  HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, stream),
+         "wkv7_forward launch");
+  return WKV7_OK;
+}
+
+extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt) {
+  if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
+  if (have_ckpt) return 0;
+  Carver c(nullptr);
+  c.take(ckpt_floats(B, T, H));
+  return c.off;
+}
+
+extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* r, const void* w,
+                             const void* k, const void* v, const void* a, const void* b,
+                             const float* s0, const float* ckpt, const void* dy, const float* dsT,
+                             void* dr, void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_wkv_shape(B, T, H, N, dtype));
+  const char* names[] = {"r", "w", "k", "v", "a", "b", "dy", "dr", "dw", "dk", "dv", "da", "db"};
+  const void* ptrs[] = {r, w, k, v, a, b, dy, dr, dw, dk, dv, da, db};
+  for (int i = 0; i < 13; i++) CHK(check_tok_ptr(ptrs[i], names[i], dtype, true));
+  CHK(check_f32_ptr(s0, "s0", false));
+  CHK(check_f32_ptr(ckpt, "ckpt", false));
+  CHK(check_f32_ptr(dsT, "dsT", false));
+  CHK(check_f32_ptr(ds0, "ds0", false));
+  const float* ck = ckpt;
+  if (!ck) {
+    const size_t need = wkv7_backward_workspace_bytes(B, T, H, N, 0);
+    if (!ws || ws_bytes < need)
+      return fail(WKV7_ENOSPC, "workspace of %zu bytes needed to recompute checkpoints (got %zu)", need, ws_bytes);
+    CHK(check_f32_ptr(ws, "ws", true));
+    Carver cv(ws);
+    float* tmp = cv.take(ckpt_floats(B, T, H));
+    HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, stream),
+           "wkv7_backward checkpoint recompute");
+    ck = tmp;
+  }
+  HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
+                              db, ds0, stream),
+         "wkv7_backward launch");
+  return WKV7_OK;
+}
+
+extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const void* w,
+                         const void* k, const void* v, const void* a, const void* b, float* state,
+                         void* y, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_wkv_shape(B, 1, H, N, dtype));
+  const char* names[] = {"r", "w", "k", "v", "a", "b", "y"};
+  const void* ptrs[] = {r, w, k, v, a, b, y};
+  for (int i = 0; i < 7; i++) CHK(check_tok_ptr(ptrs[i], names[i], dtype, true));
+  CHK(check_f32_ptr(state, "state", true));
+  HIPCHK(wkv7_launch_step(dtype, B, H, r, w, k, v, a, b, state, y, stream), "wkv7_step launch");
+  return WKV7_OK;
+}
+
+// -------------------------------------------------------------- time-mix --
+namespace {
+
+struct TmCache {
+  float *xr, *xw, *xk, *xv, *xa, *xg;
+  float *r, *k, *v, *tw, *ow, *la, *oa, *sg, *g, *lv, *ov;
+  float *w, *a, *kk, *kmod, *vmod, *A, *Bv, *y, *tg;
+  float *mean, *rstd, *alpha, *ckpt;
+};
+
+void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m) {
+  const size_t BT = (size_t)B * T, tok = BT * s->C;
+  float** toks[] = {&m.xr, &m.xw, &m.xk, &m.xv, &m.xa, &m.xg, &m.r, &m.k, &m.v, &m.ow, &m.oa,
+                    &m.g, &m.w, &m.a, &m.kk, &m.kmod, &m.vmod, &m.A, &m.Bv, &m.y, &m.tg};
+  for (float** p : toks) *p = c.take(tok);
+  m.tw = c.take(BT * s->Dw);
+  m.la = c.take(BT * s->Da);
+  m.sg = c.take(BT * s->Dg);
+  if (s->layer_id > 0) {
+    m.lv = c.take(BT * s->Dv);
+    m.ov = c.take(tok);
+  } else {
+    m.lv = m.ov = nullptr;
+  }
+  m.mean = c.take(BT * s->H);
+  m.rstd = c.take(BT * s->H);
+  m.alpha = c.take(BT * s->H);
+  m.ckpt = c.take(ckpt_floats(B, T, s->H));
+}
+
+struct TmBwdBufs {
+  float *dtg, *dg, *dy_wkv, *dr, *dkmod, *dvmod, *gr, *gw, *gk, *gv, *gA, *gB;
+  float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *d_la, *d_lw, *d_lg, *d_lv;
+  float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg, *part_post, *part_pre, *part_shift, *splitk, *out_tmp;
+};
+
+// split-K factor for a weight gradient [Mo][No] reduced over BT tokens
+int splitk_for(int Mo, int No, int BT) {
+  const int tiles = ((Mo + 127) / 128) * ((No + 127) / 128);
+  int s = (512 + tiles - 1) / tiles;
+  const int maxs = BT / 256;
+  if (s > maxs) s = maxs;
+  return s < 1 ? 1 : s;
+}
+
+size_t splitk_scratch(const tm_shape* s, int BT) {
+  const int C = s->C;
+  size_t best = 0;
+  const int dims[] = {C, s->Dw, s->Da, s->Dg, s->layer_id > 0 ? s->Dv : 0};
+  for (int d : dims) {
+    if (d <= 0) continue;
+    const size_t x = (size_t)splitk_for(C, d, BT) * C * d;
+    if (x > best) best = x;
+    const size_t y = (size_t)splitk_for(d, C, BT) * C * d;
+    if (y > best) best = y;
+  }
+  return best;
+}
+
+void carve_bwd(Carver& c, const tm_shape* s, int B, int T, TmBwdBufs& m) {
+  const size_t BT = (size_t)B * T, tok = BT * s->C;
+  float** toks[] = {&m.dtg, &m.dg, &m.dy_wkv, &m.dr, &m.dkmod, &m.dvmod, &m.gr, &m.gw, &m.gk,
+                    &m.gv, &m.gA, &m.gB, &m.dk, &m.dv, &m.dpre_a, &m.dpre_w, &m.dxr, &m.dxw,
+                    &m.dxk, &m.dxv, &m.dxa, &m.dxg};
+  for (float** p : toks) *p = c.take(tok);
+  m.dpre_v = s->layer_id > 0 ? c.take(tok) : nullptr;
+  m.d_la = c.take(BT * s->Da);
+  m.d_lw = c.take(BT * s->Dw);
+  m.d_lg = c.take(BT * s->Dg);
+  m.d_lv = s->layer_id > 0 ? c.take(BT * s->Dv) : nullptr;
+  const int nblk = tm_num_token_blocks((int)BT);
+  m.part_post = c.take((size_t)3 * nblk * s->C);
+  m.part_pre = c.take((size_t)5 * nblk * s->C);
+  m.part_shift = c.take((size_t)6 * nblk * s->C);
+  m.splitk = c.take(splitk_scratch(s, (int)BT));
+  m.out_tmp = nullptr;
+}
+
+int check_tm_shape(const tm_shape* s, int B, int T) {
+  if (!s) return fail(WKV7_EINVAL, "shape is NULL");
+  if (s->N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", s->N);
+  if (s->H < 1 || s->C != s->H * s->N) return fail(WKV7_EINVAL, "C=%d must equal H*N=%d*%d", s->C, s->H, s->N);
+  if (B < 1 || T < 1) return fail(WKV7_EINVAL, "B, T must be >= 1 (got %d, %d)", B, T);
+  if (s->Dw < 4 || s->Da < 4 || s->Dg < 4 || s->Dw % 4 || s->Da % 4 || s->Dg % 4)
+    return fail(WKV7_EINVAL, "LoRA ranks Dw, Da, Dg must be positive multiples of 4");
+  if (s->layer_id < 0) return fail(WKV7_EINVAL, "layer_id must be >= 0");
+  if (s->layer_id > 0 && (s->Dv < 4 || s->Dv % 4))
+    return fail(WKV7_EINVAL, "LoRA rank Dv must be a positive multiple of 4 for layer_id > 0");
+  if ((size_t)B * T * s->C > ((size_t)1 << 36)) return fail(WKV7_EINVAL, "problem too large");
+  return WKV7_OK;
+}
+
+int check_weights(const tm_shape* s, const tm_weights* W) {
+  if (!W) return fail(WKV7_EINVAL, "weights is NULL");
+  const float* req[] = {W->mu_r, W->mu_w, W->mu_k, W->mu_v, W->mu_a, W->mu_g, W->Wr, W->Wk, W->Wv,
+                        W->Wo, W->w0, W->W1, W->W2, W->a0, W->A1, W->A2, W->G1, W->G2, W->k_k,
+                        W->k_a, W->r_k, W->ln_w, W->ln_b};
+  const char* nm[] = {"mu_r", "mu_w", "mu_k", "mu_v", "mu_a", "mu_g", "Wr", "Wk", "Wv", "Wo",
+                      "w0", "W1", "W2", "a0", "A1", "A2", "G1", "G2", "k_k", "k_a", "r_k",
+                      "ln_w", "ln_b"};
+  for (int i = 0; i < 23; i++) CHK(check_f32_ptr(req[i], nm[i], true));
+  if (s->layer_id > 0) {
+    CHK(check_f32_ptr(W->v0, "v0", true));
+    CHK(check_f32_ptr(W->V1, "V1", true));
+    CHK(check_f32_ptr(W->V2, "V2", true));
+  }
+  return WKV7_OK;
+}
+
+int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
+                    const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
+                    float* x_last, const TmCache& m, hipStream_t st) {
+  const int BT = B * T, C = s->C;
+  TmFwd p;
+  memset(&p, 0, sizeof(p));
+  p.BT = BT; p.T = T; p.C = C; p.layer_id = s->layer_id;
+  p.x = x; p.x_prev = x_prev;
+  p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
+  p.xr = m.xr; p.xw = m.xw; p.xk = m.xk; p.xv = m.xv; p.xa = m.xa; p.xg = m.xg; p.x_last = x_last;
+  p.k = m.k; p.v = m.v; p.ow = m.ow; p.oa = m.oa; p.ov = m.ov;
+  p.w0 = W->w0; p.a0 = W->a0; p.v0 = W->v0; p.k_k = W->k_k; p.k_a = W->k_a;
+  p.v_first = v_first;
+  p.w = m.w; p.a = m.a; p.kk = m.kk; p.kmod = m.kmod; p.vmod = m.vmod; p.A = m.A; p.Bv = m.Bv;
+  p.y = m.y; p.r = m.r; p.g = m.g; p.r_k = W->r_k; p.ln_w = W->ln_w; p.ln_b = W->ln_b;
+  p.tg = m.tg; p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha;
+
+  HIPCHK(tm_launch_shift_fwd(p, st), "token shift");
+  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xr, C, W->Wr, C, m.r, C, 0.f, 0, nullptr, 1, nullptr, st), "r proj");
+  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xk, C, W->Wk, C, m.k, C, 0.f, 0, nullptr, 1, nullptr, st), "k proj");
+  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xv, C, W->Wv, C, m.v, C, 0.f, 0, nullptr, 1, nullptr, st), "v proj");
+  HIPCHK(gemm_f32_run(false, false, BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, 0.f, 1, nullptr, 1, nullptr, st), "w lora 1");
+  HIPCHK(gemm_f32_run(false, false, BT, C, s->Dw, m.tw, s->Dw, W->W2, C, m.ow, C, 0.f, 0, nullptr, 1, nullptr, st), "w lora 2");
+  HIPCHK(gemm_f32_run(false, false, BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, 0.f, 0, nullptr, 1, nullptr, st), "a lora 1");
+  HIPCHK(gemm_f32_run(false, false, BT, C, s->Da, m.la, s->Da, W->A2, C, m.oa, C, 0.f, 0, nullptr, 1, nullptr, st), "a lora 2");
+  HIPCHK(gemm_f32_run(false, false, BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, 0.f, 2, nullptr, 1, nullptr, st), "g lora 1");
+  HIPCHK(gemm_f32_run(false, false, BT, C, s->Dg, m.sg, s->Dg, W->G2, C, m.g, C, 0.f, 0, nullptr, 1, nullptr, st), "g lora 2");
+  if (s->layer_id > 0) {
+    HIPCHK(gemm_f32_run(false, false, BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, 0.f, 0, nullptr, 1, nullptr, st), "v lora 1");
+    HIPCHK(gemm_f32_run(false, false, BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, 0.f, 0, nullptr, 1, nullptr, st), "v lora 2");
+  }
+  HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
+  HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
+                             m.ckpt, st), "wkv7 forward");
+  HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
+  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, 0.f, 0, nullptr, 1, nullptr, st), "o proj");
+  return WKV7_OK;
+}
+
+}  // namespace
+
+extern "C" size_t timemix_cache_bytes(const tm_shape* s, int B, int T) {
+  if (check_tm_shape(s, B, T) != WKV7_OK) return 0;
+  Carver c(nullptr);
+  TmCache m;
+  carve_cache(c, s, B, T, m);
+  return c.off + 256;
+}
+
+extern "C" size_t timemix_forward_workspace_bytes(const tm_shape* s, int B, int T) {
+  return timemix_cache_bytes(s, B, T);
+}
+
+extern "C" size_t timemix_backward_workspace_bytes(const tm_shape* s, int B, int T) {
+  if (check_tm_shape(s, B, T) != WKV7_OK) return 0;
+  Carver c(nullptr);
+  TmCache m;
+  carve_cache(c, s, B, T, m);
+  c.take((size_t)B * T * s->C);  // forward output when the cache is recomputed
+  TmBwdBufs bb;
+  carve_bwd(c, s, B, T, bb);
+  return c.off + 256;
+}
+
+extern "C" int timemix_forward(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
+                               const float* x_prev, float* v_first, const float* s0, float* sT,
+                               float* out, float* x_last, void* cache, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_tm_shape(s, B, T));
+  CHK(check_weights(s, W));
+  CHK(check_f32_ptr(x, "x", true));
+  CHK(check_f32_ptr(x_prev, "x_prev", false));
+  CHK(check_f32_ptr(v_first, "v_first", true));
+  CHK(check_f32_ptr(s0, "s0", false));
+  CHK(check_f32_ptr(sT, "sT", false));
+  CHK(check_f32_ptr(out, "out", true));
+  CHK(check_f32_ptr(x_last, "x_last", false));
+  void* base = cache;
+  if (!base) {
+    const size_t need = timemix_forward_workspace_bytes(s, B, T);
+    if (!ws || ws_bytes < need)
+      return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    base = ws;
+  }
+  CHK(check_f32_ptr(base, cache ? "cache" : "ws", true));
+  Carver c(base);
+  TmCache m;
+  carve_cache(c, s, B, T, m);
+  return tm_forward_impl(s, W, B, T, x, x_prev, v_first, s0, sT, out, x_last, m, stream);
+}
+
+extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, int T,
+                                const float* x, const float* x_prev, const float* v_first,
+                                const float* s0, const float* dout, const float* dsT,
+                                const void* cache, tm_grads* G, float* dx, float* dx_prev,
+                                const float* dv_first_in, float* dv_first_out, float* ds0,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_tm_shape(s, B, T));
+  CHK(check_weights(s, W));
+  if (!G) return fail(WKV7_EINVAL, "grads is NULL");
+  float* greq[] = {G->mu_r, G->mu_w, G->mu_k, G->mu_v, G->mu_a, G->mu_g, G->Wr, G->Wk, G->Wv,
+                   G->Wo, G->w0, G->W1, G->W2, G->a0, G->A1, G->A2, G->G1, G->G2, G->k_k,
+                   G->k_a, G->r_k, G->ln_w, G->ln_b};
+  for (float* p : greq) CHK(check_f32_ptr(p, "a gradient field", true));
+  if (s->layer_id > 0) {
+    CHK(check_f32_ptr(G->v0, "G.v0", true));
+    CHK(check_f32_ptr(G->V1, "G.V1", true));
+    CHK(check_f32_ptr(G->V2, "G.V2", true));
+  }
+  CHK(check_f32_ptr(x, "x", true));
+  CHK(check_f32_ptr(x_prev, "x_prev", false));
+  CHK(check_f32_ptr(v_first, "v_first", s->layer_id > 0));
+  CHK(check_f32_ptr(s0, "s0", false));
+  CHK(check_f32_ptr(dout, "dout", true));
+  CHK(check_f32_ptr(dsT, "dsT", false));
+  CHK(check_f32_ptr(dx, "dx", true));
+  CHK(check_f32_ptr(dx_prev, "dx_prev", false));
+  CHK(check_f32_ptr(dv_first_in, "dv_first_in", false));
+  CHK(check_f32_ptr(dv_first_out, "dv_first_out", false));
+  CHK(check_f32_ptr(ds0, "ds0", false));
+  CHK(check_f32_ptr(cache, "cache", false));
+  const size_t need = timemix_backward_workspace_bytes(s, B, T);
+  if (!ws || ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  CHK(check_f32_ptr(ws, "ws", true));
+
+  const int BT = B * T, C = s->C, L = s->layer_id;
+  Carver cw(ws);
+  TmCache m;
+  carve_cache(cw, s, B, T, m);  // used when the cache must be recomputed
+  float* out_tmp = cw.take((size_t)BT * C);
+  TmBwdBufs bb;
+  carve_bwd(cw, s, B, T, bb);
+  if (cache) {
+    Carver cc((void*)cache);
+    carve_cache(cc, s, B, T, m);
+  } else {
+    // layer 0 republishes v_first; send it to a scratch buffer so the caller's
+    // (const) v_first is never written
+    float* vf = L == 0 ? bb.dxg : (float*)v_first;
+    CHK(tm_forward_impl(s, W, B, T, x, x_prev, vf, s0, nullptr, out_tmp, nullptr, m, stream));
+  }
+  hipStream_t st = stream;
+
+  // output projection
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
+
+  TmBwd p;
+  memset(&p, 0, sizeof(p));
+  p.BT = BT; p.T = T; p.C = C; p.layer_id = L;
+  p.dtg = bb.dtg; p.g = m.g; p.y = m.y; p.r = m.r; p.kmod = m.kmod; p.vmod = m.vmod;
+  p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha; p.r_k = W->r_k; p.ln_w = W->ln_w; p.ln_b = W->ln_b;
+  p.dg = bb.dg; p.dy_wkv = bb.dy_wkv; p.dr = bb.dr; p.dkmod = bb.dkmod; p.dvmod = bb.dvmod;
+  p.part_post = bb.part_post;
+  p.gr = bb.gr; p.gk = bb.gk; p.gv = bb.gv; p.gw = bb.gw; p.gA = bb.gA; p.gB = bb.gB;
+  p.a = m.a; p.kk = m.kk; p.k = m.k; p.w = m.w; p.ow = m.ow; p.ov = m.ov; p.v = m.v;
+  p.v_first = v_first; p.k_a = W->k_a; p.k_k = W->k_k; p.w0 = W->w0; p.v0 = W->v0;
+  p.dvf_in = L == 0 ? dv_first_in : nullptr;
+  p.dk = bb.dk; p.dv = bb.dv; p.dpre_a = bb.dpre_a; p.dpre_w = bb.dpre_w; p.dpre_v = bb.dpre_v;
+  p.dvf_out = L > 0 ? dv_first_out : nullptr;
+  p.part_pre = bb.part_pre;
+  p.x = x; p.x_prev = x_prev;
+  p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
+  p.dxr = bb.dxr; p.dxw = bb.dxw; p.dxk = bb.dxk; p.dxv = bb.dxv; p.dxa = bb.dxa; p.dxg = bb.dxg;
+  p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
+
+  HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
+  HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
+                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0, st),
+         "wkv7 backward");
+  HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
+
+  const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
+  float* sk = bb.splitk;
+  // a: a = sigmoid(a0 + (xa A1) A2)
+  HIPCHK(gemm_f32_run(false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
+  HIPCHK(gemm_f32_run(true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
+  HIPCHK(gemm_f32_run(true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
+  // w: w = exp(-c sigmoid(w0 + tanh(xw W1) W2))
+  HIPCHK(gemm_f32_run(false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
+  HIPCHK(gemm_f32_run(true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
+  HIPCHK(gemm_f32_run(true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
+  // g: g = sigmoid(xg G1) G2
+  HIPCHK(gemm_f32_run(false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
+  HIPCHK(gemm_f32_run(true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
+  HIPCHK(gemm_f32_run(true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
+  // value residual LoRA (layer > 0)
+  if (L > 0) {
+    HIPCHK(gemm_f32_run(false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
+    HIPCHK(gemm_f32_run(true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
+    HIPCHK(gemm_f32_run(false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
+    HIPCHK(gemm_f32_run(true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
+  }
+  // r, k, v projections
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
+
+  HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
+  const int nblk = tm_num_token_blocks(BT);
+  VecOut o1 = {{G->r_k, G->ln_w, G->ln_b, nullptr, nullptr, nullptr, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_post, 3, nblk, C, o1, st), "reduce post");
+  VecOut o2 = {{G->k_a, G->k_k, G->a0, G->w0, L > 0 ? G->v0 : nullptr, nullptr, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_pre, 5, nblk, C, o2, st), "reduce pre");
+  VecOut o3 = {{G->mu_r, G->mu_w, G->mu_k, G->mu_v, G->mu_a, G->mu_g, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_shift, 6, nblk, C, o3, st), "reduce shift");
+  return WKV7_OK;
+}

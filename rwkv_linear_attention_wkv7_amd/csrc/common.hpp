@@ -1,0 +1,101 @@
+// Shared device helpers for the gfx950 (CDNA4, wave64) kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define WKV7_N 64  // head size; the kernels are written for N = 64 only
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 ----
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest, ties to even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Load 4 consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as fp32.
+template <typename T>
+__device__ __forceinline__ f4 load4(const T* p);
+template <>
+__device__ __forceinline__ f4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f4*>(p);
+}
+template <>
+__device__ __forceinline__ f4 load4<bf16_t>(const bf16_t* p) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  f4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ float load1(const T* p);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<bf16_t>(const bf16_t* p) { return bf16_to_f32(p->bits); }
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f4 v) {
+  *reinterpret_cast<f4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, f4 v) {
+  uint2 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+template <typename T>
+__device__ __forceinline__ void store1(T* p, float v);
+template <>
+__device__ __forceinline__ void store1<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store1<bf16_t>(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
+
+// ------------------------------------------------------ cross-lane sums ----
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the sum.
+__device__ __forceinline__ float rowsum16(float x) {
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, true);  // row_mirror
+  return x;
+}
+
+// Sum over lanes {l, l^16, l^32, l^48} (the four 16-lane rows of the wave);
+// every lane receives the sum of its column position.  gfx950 permlane swaps.
+__device__ __forceinline__ float rows4sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Full 64-lane wave sum, result in every lane.
+__device__ __forceinline__ float wavesum(float x) { return rows4sum(rowsum16(x)); }
+
+// --------------------------------------------------------------- launch ----
+// Workgroups are dispatched round-robin over the 8 XCDs (block g -> XCD g % 8).
+// Remap so that consecutive logical ids land on one XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int g, int n) {
+  if (n & 7) return g;
+  return (g & 7) * (n >> 3) + (g >> 3);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }

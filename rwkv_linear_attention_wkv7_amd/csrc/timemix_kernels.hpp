@@ -1,0 +1,66 @@
+// Argument blocks of the fused time-mix kernels (passed by value).
+#pragma once
+#include <hip/hip_runtime.h>
+
+constexpr int TB = 128;  // tokens per workgroup in the backward partial-sum kernels
+
+struct TmFwd {
+  int BT, T, C, layer_id;
+  const float *x, *x_prev;
+  const float *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
+  float *xr, *xw, *xk, *xv, *xa, *xg, *x_last;
+  // pre-WKV
+  const float *k, *v, *ow, *oa, *ov, *w0, *a0, *v0, *k_k, *k_a;
+  float* v_first;  // written on layer 0, read otherwise
+  float *w, *a, *kk, *kmod, *vmod, *A, *Bv;
+  // post-WKV
+  const float *y, *r, *g, *r_k, *ln_w, *ln_b;
+  float *tg, *mean, *rstd, *alpha;
+};
+
+struct TmBwd {
+  int BT, T, C, layer_id;
+  // post-WKV backward
+  const float *dtg, *g, *y, *r, *kmod, *vmod, *mean, *rstd, *alpha, *r_k, *ln_w, *ln_b;
+  float *dg, *dy_wkv, *dr, *dkmod, *dvmod, *part_post;
+  // pre-WKV backward
+  const float *gr, *gk, *gv, *gw, *gA, *gB;  // WKV7 gradients
+  const float *a, *kk, *k, *w, *ow, *ov, *v, *v_first, *k_a, *k_k, *w0, *v0, *dvf_in;
+  float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *dvf_out, *part_pre;
+  // token shift backward
+  const float *x, *x_prev, *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
+  const float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg;
+  float *dx, *dx_prev, *part_shift;
+};
+
+struct VecOut {
+  float* p[8];
+};
+
+hipError_t tm_launch_shift_fwd(const TmFwd& p, hipStream_t st);
+hipError_t tm_launch_pre_fwd(const TmFwd& p, hipStream_t st);
+hipError_t tm_launch_post_fwd(const TmFwd& p, hipStream_t st);
+int tm_num_token_blocks(int BT);
+hipError_t tm_launch_post_bwd(const TmBwd& p, hipStream_t st);
+hipError_t tm_launch_pre_bwd(const TmBwd& p, hipStream_t st);
+hipError_t tm_launch_shift_bwd(const TmBwd& p, hipStream_t st);
+hipError_t tm_launch_reduce(const float* part, int nvec, int nblk, int C, const VecOut& outs,
+                            hipStream_t st);
+
+// gemm.hip
+hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A, int lda,
+                        const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                        const float* aux, int split, float* ws, hipStream_t st);
+// wkv7_seq.hip
+hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, const void* w,
+                               const void* k, const void* v, const void* a, const void* b,
+                               const float* s0, void* y, float* sT, float* ckpt, hipStream_t st);
+hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, const void* w,
+                                const void* k, const void* v, const void* a, const void* b,
+                                const void* dy, const float* ckpt, const float* dsT, void* dr,
+                                void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
+                                hipStream_t st);
+hipError_t wkv7_launch_step(int dtype, int B, int H, const void* r, const void* w, const void* k,
+                            const void* v, const void* a, const void* b, float* state, void* y,
+                            hipStream_t st);
+int wkv7_ckpt_interval_const();

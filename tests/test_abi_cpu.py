@@ -1,0 +1,153 @@
+"""C-ABI checks that run without a GPU.
+
+The library must export every function declared in include/*.h, and every
+argument error must be reported (with a message) before anything touches the
+device, so the error paths are exercised here with host-side calls only.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from rwkv_linear_attention_wkv7_amd import binding
+    return binding.lib()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared_functions()
+    for n in ("wkv7_forward", "wkv7_backward", "wkv7_step", "timemix_forward", "timemix_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+
+
+def _err(L):
+    return L.wkv7_last_error().decode()
+
+
+A = ctypes.c_void_p(4096)      # aligned fake device address: never dereferenced here
+MIS = ctypes.c_void_p(4100)    # misaligned
+
+
+def _fwd(L, B=1, T=4, H=2, N=64, dtype=0, ptrs=None, s0=None):
+    p = ptrs or [A] * 7
+    return L.wkv7_forward(B, T, H, N, dtype, *p[:6], s0, p[6], None, None, None)
+
+
+def test_forward_rejects_bad_shapes(L):
+    assert _fwd(L, N=32) == -1 and "N=32" in _err(L)
+    assert _fwd(L, T=0) == -1 and ">= 1" in _err(L)
+    assert _fwd(L, B=0) == -1
+    assert _fwd(L, H=0) == -1
+    assert _fwd(L, dtype=7) == -1 and "dtype" in _err(L)
+
+
+def test_forward_rejects_null_and_misaligned(L):
+    assert _fwd(L, ptrs=[A, A, None, A, A, A, A]) == -1 and "k is NULL" in _err(L)
+    assert _fwd(L, ptrs=[A, A, A, A, A, A, None]) == -1 and "y is NULL" in _err(L)
+    assert _fwd(L, ptrs=[A, MIS, A, A, A, A, A]) == -1 and "aligned" in _err(L)
+    assert _fwd(L, s0=MIS) == -1 and "s0" in _err(L)
+    # bf16 data only needs 8-byte alignment
+    mis8 = ctypes.c_void_p(4104)
+    rc = L.wkv7_forward(1, 4, 2, 64, 1, mis8, A, A, A, A, A, None, ctypes.c_void_p(4098), None, None, None)
+    assert rc == -1 and "y is not 8-byte aligned" in _err(L)
+
+
+def test_backward_needs_workspace_without_checkpoints(L):
+    need = L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 0)
+    assert need >= L.wkv7_checkpoint_floats(1, 64, 4, 64) * 4
+    assert L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 1) == 0
+    ptr13 = [A] * 13
+    rc = L.wkv7_backward(1, 64, 4, 64, 0, *ptr13[:6], None, None, ptr13[6], None, *ptr13[7:13],
+                         None, A, need - 1, None)
+    assert rc == -3 and "workspace" in _err(L)
+
+
+def test_step_rejects_null_state(L):
+    rc = L.wkv7_step(2, 4, 64, 0, A, A, A, A, A, A, None, A, None)
+    assert rc == -1 and "state is NULL" in _err(L)
+    assert L.wkv7_step(2, 4, 48, 0, A, A, A, A, A, A, A, A, None) == -1
+
+
+def test_checkpoint_sizes(L):
+    Lc = L.wkv7_checkpoint_interval()
+    assert Lc >= 1
+    for T in (1, Lc, Lc + 1, 8192):
+        assert L.wkv7_checkpoint_floats(4, T, 32, 64) == 4 * 32 * (-(-T // Lc)) * 64 * 64
+    assert L.wkv7_checkpoint_floats(4, 16, 32, 32) == 0
+
+
+def _tm(C=256, H=4, Dw=32, Da=32, Dv=32, Dg=64, layer=1, N=64):
+    from rwkv_linear_attention_wkv7_amd import binding
+    return binding.TmShape(C, H, N, Dw, Da, Dv, Dg, layer)
+
+
+def _weights(layer):
+    from rwkv_linear_attention_wkv7_amd import binding
+    w = binding.TmWeights()
+    for n in binding.WEIGHT_FIELDS:
+        setattr(w, n, None if (layer == 0 and n in ("v0", "V1", "V2")) else 4096)
+    return w
+
+
+def test_timemix_forward_validation(L):
+    w = _weights(1)
+    s = _tm(C=250)
+    rc = L.timemix_forward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, A, None, None, A, None,
+                           None, A, 1 << 30, None)
+    assert rc == -1 and "C=250" in _err(L)
+    s = _tm(Dw=30)
+    rc = L.timemix_forward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, A, None, None, A, None,
+                           None, A, 1 << 30, None)
+    assert rc == -1 and "multiples of 4" in _err(L)
+    s = _tm()
+    need = L.timemix_forward_workspace_bytes(ctypes.byref(s), 2, 8)
+    rc = L.timemix_forward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, A, None, None, A, None,
+                           None, A, need - 1, None)
+    assert rc == -3 and "workspace" in _err(L)
+    w0 = _weights(0)  # layer > 0 needs the value-residual LoRA
+    rc = L.timemix_forward(ctypes.byref(s), ctypes.byref(w0), 2, 8, A, None, A, None, None, A,
+                           None, None, A, need, None)
+    assert rc == -1 and "v0" in _err(L)
+
+
+def test_timemix_backward_validation(L):
+    from rwkv_linear_attention_wkv7_amd import binding
+    s = _tm(layer=0)
+    w = _weights(0)
+    g = binding.TmGrads()
+    for n in binding.WEIGHT_FIELDS:
+        setattr(g, n, 4096)
+    g.Wk = None
+    need = L.timemix_backward_workspace_bytes(ctypes.byref(s), 2, 8)
+    assert need > L.timemix_cache_bytes(ctypes.byref(s), 2, 8)
+    rc = L.timemix_backward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, None, None, A, None,
+                            None, ctypes.byref(g), A, None, None, None, None, A, need, None)
+    assert rc == -1 and "gradient" in _err(L)
+    g.Wk = 4096
+    rc = L.timemix_backward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, None, None, A, None,
+                            None, ctypes.byref(g), A, None, None, None, None, A, need - 1, None)
+    assert rc == -3
