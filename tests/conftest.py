@@ -26,4 +26,5 @@ def hip():
     if not gpu_available():
         pytest.skip("no GPU visible")
     from rwkv_linear_attention_wkv7_amd import binding
-    return binding.lib()
+    binding.lib()
+    return binding
