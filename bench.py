@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the RWKV-7 WKV7 / time-mix hot path on one MI355X.
+
+Prints ONE JSON line.  Workloads (--workload):
+  timemix    time-mix block forward+backward, B=8 T=1024 C=768 (H=12),
+             LoRA ranks w/a/v/g = 64/64/32/128, layer > 0, fp32 (tokens/s)
+  wkv7_long  WKV7 forward+backward, B=4 T=8192 H=32 N=64, bf16 token
+             tensors, fp32 state, checkpointed backward (tokens/s)
+A step is one pass of the whole workload over one batch of seeded synthetic
+inputs that are resident in HBM before timing starts.  Steps are timed with
+HIP events on the stream the library launches on, bracketed by device
+synchronisation.
+
+"roofline" reports the workload's dominant kernel, timed live here on the
+same stream over its own loop of launches (HIP events), against MI355X peak.
+"cpu_baseline" times the f64 CPU oracle on a bounded sample of the same
+workload on the host cores (rank 0, one GPU only).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WKV7 time-mix fwd+bwd tokens/s and decode steps/s; % of HBM/MFMA peak"
+PEAK = {"hbm": (8000.0, "GB/s"), "mfma_fp32": (157.3, "TFLOP/s"), "alu_fp32": (157.3, "TFLOP/s"),
+        "mfma_bf16": (2500.0, "TFLOP/s")}
+N = 64
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_loop(fn, iters):
+    """Average ms per call of fn(), HIP events on the current stream."""
+    import torch
+    s, e = _events()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def traffic_from_profile(kernel_key, src_files):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, or None.
+
+    profiles/pmc_<kernel_key>.json holds the FETCH_SIZE/WRITE_SIZE derived bytes
+    and a hash of the kernel sources at measurement time; a changed source
+    makes the figure stale (None).
+    """
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in src_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------- workloads --
+def setup_timemix():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    B, T, C, H = 8, 1024, 768, 12
+    ranks = (64, 64, 32, 128)
+    p = synth.timemix_params(C, H, *ranks, layer_id=1, seed=0)
+    d = synth.timemix_inputs(B, T, C, seed=1)
+    dev = torch.device("cuda")
+    W = {k: torch.from_numpy(v).to(dev) for k, v in p.items()}
+    x, vf, dout = (torch.from_numpy(d[k]).to(dev) for k in ("x", "v_first", "dout"))
+    s = binding.tm_shape(C, H, *ranks, layer_id=1)
+
+    def step():
+        f = binding.timemix_forward(s, W, x, v_first=vf, want_cache=True, want_state=False)
+        binding.timemix_backward(s, W, x, dout, v_first=vf, cache=f["cache"], want_dx_prev=False,
+                                 want_ds0=False)
+
+    # dominant kernel: the fp32 MFMA GEMM of the C x C projections
+    # (X [BT][C] . W [C][C]; 2*BT*C*C flop per launch)
+    A = torch.from_numpy(d["x"].reshape(B * T, C)).to(dev)
+    Wm = W["Wr"]
+    Cout = torch.empty((B * T, C), device=dev)
+
+    def dom():
+        binding.wkv7_gemm_f32(A, Wm, Cout)
+
+    flops = 2.0 * B * T * C * C
+    roof = dict(kernel="gemm_f32 (X[8192][768] . W[768][768])", bound="mfma", work=flops,
+                unit="TFLOP/s", peak=PEAK["mfma_fp32"][0], fn=dom, key="gemm_f32_c768",
+                src=["rwkv_linear_attention_wkv7_amd/csrc/gemm.hip"])
+
+    def cpu():
+        from oracle import timemix as otm
+        from oracle import wkv7 as ow
+        Bs = 1
+        t0 = time.perf_counter()
+        out, c = otm.forward(p, d["x"][:Bs], H, 1, v_first=d["v_first"][:Bs])
+        otm.backward(p, c, d["dout"][:Bs])
+        dt = time.perf_counter() - t0
+        return dict(value=Bs * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"1 of 8 sequences (T=1024, C=768): f64 forward+backward, {dt:.1f} s")
+
+    cfg = {"workload": "time-mix block forward+backward", "B": B, "T": T, "C": C, "H": H,
+           "N": N, "lora_ranks_w_a_v_g": list(ranks), "layer_id": 1, "global_batch": B,
+           "seq_len": T, "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="f32", config=cfg, roof=roof,
+                cpu=cpu)
+
+
+def setup_wkv7_long():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    B, T, H = 4, 8192, 32
+    d = synth.wkv7_inputs(B, T, H, N, seed=3, bf16=True)
+    dev = torch.device("cuda")
+    names = ("r", "w", "k", "v", "a", "b")
+    ins = [torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in names]
+    dy = torch.from_numpy(d["dy"]).to(dev).to(torch.bfloat16)
+    ck = torch.empty(binding.wkv7_checkpoint_floats(B, T, H), device=dev)
+
+    def step():
+        binding.wkv7_forward(*ins, ckpt=ck, want_state=False)
+        binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
+
+    def dom():
+        binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
+
+    # backward algorithmic work per token-head: 19 N^2 flop for the reverse
+    # step (G += dy r^T, dr, dv, dk, db, dsa, dw, da: 2 N^2 each; G update
+    # 3 N^2) plus 7 N^2 to recompute sa and the state from the checkpoint.
+    flops = 26.0 * N * N * B * T * H
+    roof = dict(kernel="wkv7 backward (sequential, checkpointed)", bound="alu", work=flops,
+                unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom, key="wkv7_bwd_long",
+                src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+
+    def cpu():
+        from oracle import wkv7 as ow
+        hs = 16
+        sub = [d[n][:1, :, :hs].astype(np.float64) for n in names]
+        t0 = time.perf_counter()
+        ow.forward(*sub)
+        ow.backward(*sub, d["dy"][:1, :, :hs].astype(np.float64))
+        dt = time.perf_counter() - t0
+        return dict(value=(T * hs / H) / dt, unit="tokens/s", cores=ow.num_threads(),
+                    kind="oracle",
+                    sample=f"16 of 128 (b,h) pairs, T=8192: f64 forward+backward, {dt:.1f} s")
+
+    cfg = {"workload": "WKV7 forward+backward, long context", "B": B, "T": T, "H": H, "N": N,
+           "inputs": "bf16", "state": "fp32", "checkpoint_interval": binding.wkv7_checkpoint_interval(),
+           "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="bf16 in / f32 state", config=cfg,
+                roof=roof, cpu=cpu)
+
+
+WORKLOADS = {"timemix": setup_timemix, "wkv7_long": setup_wkv7_long}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="timemix", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roof-iters", type=int, default=20)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from rwkv_linear_attention_wkv7_amd import binding
+    binding.lib()
+
+    w = WORKLOADS[args.workload]()
+    for _ in range(args.warmup):
+        w["step"]()
+    torch.cuda.synchronize()
+    s, e = _events()
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(args.steps):
+        w["step"]()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = s.elapsed_time(e) / args.steps
+    value = w["tokens"] / (ms / 1e3)
+
+    r = w["roof"]
+    r["fn"]()
+    kms = time_loop(r["fn"], args.roof_iters)
+    achieved = r["work"] / (kms / 1e3) / 1e12
+    traffic = traffic_from_profile(r["key"], r["src"])
+    roofline = {"bound": r["bound"], "kernel": r["kernel"], "achieved": round(achieved, 3),
+                "peak": r["peak"], "unit": r["unit"], "frac": round(achieved / r["peak"], 4),
+                "kernel_ms": round(kms, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = w["cpu"]()
+        cpu["value"] = round(cpu["value"], 2)
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": w["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "wall_s": round(wall, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded)",
+           "config": w["config"], "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

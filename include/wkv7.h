@@ -68,7 +68,8 @@ int wkv7_forward(int B, int T, int H, int N, int dtype,
                  const void *a, const void *b, const float *s0,
                  void *y, float *sT, float *ckpt, hipStream_t stream);
 
-/* Workspace bytes wkv7_backward needs (0 when ckpt is supplied). */
+/* Workspace bytes wkv7_backward needs: fp32 column partials of the reverse
+ * pass, plus the checkpoints when have_ckpt is 0. */
 size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
 
 /*
@@ -179,6 +180,23 @@ int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
                      const void *cache, tm_grads *G, float *dx, float *dx_prev,
                      const float *dv_first_in, float *dv_first_out, float *ds0,
                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+
+/* ------------------------------------------------------------- helpers -- */
+
+/*
+ * fp32 GEMM on the matrix cores: C = op(A) op(B) + beta C, row-major, where
+ * op(A) is A [M][K] (lda) or, with transA, A^T for A stored [K][M]; op(B) is
+ * B [K][N] (ldb) or, with transB, B^T for B stored [N][K].  This is the
+ * contraction behind every projection and LoRA product of the time-mix
+ * block ("Foundry/cuda_kernels/timemix.cu", rm_gemm: all matmuls as SGEMM over
+ * the [B*T, *] token batch).  The dimensions read contiguously (K of A, N of
+ * B, M of a transposed A, K of a transposed B) must be multiples of 4 and the
+ * pointers 16-byte aligned.  No split-K (the time-mix backward splits its
+ * weight gradients internally).
+ */
+int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float *A, int lda,
+                  const float *B, int ldb, float *C, int ldc, float beta, hipStream_t stream);
 
 #ifdef __cplusplus
 }

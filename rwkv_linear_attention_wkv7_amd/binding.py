@@ -69,6 +69,8 @@ def lib():
         L.timemix_backward.argtypes = ([sp, ctypes.POINTER(TmWeights), _i, _i] + [_vp] * 6 +
                                        [_vp, ctypes.POINTER(TmGrads)] + [_vp] * 6 + [_sz, _vp])
         L.timemix_backward.restype = _i
+        L.wkv7_gemm_f32.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp]
+        L.wkv7_gemm_f32.restype = _i
         _lib = L
     return _lib
 
@@ -265,3 +267,20 @@ def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None
                                   _p(dv_first_in if s.layer_id == 0 else None), _p(dvf_out),
                                   _p(ds0), _p(ws), nbytes, _stream()))
     return dict(grads=grads, dx=dx, dx_prev=dx_prev, dv_first_out=dvf_out, ds0=ds0)
+
+
+# ------------------------------------------------------------------ GEMM --
+def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
+    """C = op(A) op(B) + beta C on the matrix cores (fp32, row-major)."""
+    M, K = (A.shape[1], A.shape[0]) if transA else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if transB else tuple(B.shape)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    for n, t in (("A", A), ("B", B)):
+        _need(t, tuple(t.shape), torch.float32, n)
+    if C is None:
+        C = torch.empty((M, N), device=A.device, dtype=torch.float32)
+    _need(C, (M, N), torch.float32, "C")
+    _check(lib().wkv7_gemm_f32(int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B),
+                               B.shape[1], _p(C), N, beta, _stream()))
+    return C

@@ -113,9 +113,9 @@ extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r
 
 extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt) {
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
-  if (have_ckpt) return 0;
   Carver c(nullptr);
-  c.take(ckpt_floats(B, T, H));
+  c.take(wkv7_bwd_partial_floats(B, T, H));
+  if (!have_ckpt) c.take(ckpt_floats(B, T, H));
   return c.off;
 }
 
@@ -133,20 +133,21 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
   CHK(check_f32_ptr(ckpt, "ckpt", false));
   CHK(check_f32_ptr(dsT, "dsT", false));
   CHK(check_f32_ptr(ds0, "ds0", false));
+  const size_t need = wkv7_backward_workspace_bytes(B, T, H, N, ckpt != nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  CHK(check_f32_ptr(ws, "ws", true));
+  Carver cv(ws);
+  float* part = cv.take(wkv7_bwd_partial_floats(B, T, H));
   const float* ck = ckpt;
   if (!ck) {
-    const size_t need = wkv7_backward_workspace_bytes(B, T, H, N, 0);
-    if (!ws || ws_bytes < need)
-      return fail(WKV7_ENOSPC, "workspace of %zu bytes needed to recompute checkpoints (got %zu)", need, ws_bytes);
-    CHK(check_f32_ptr(ws, "ws", true));
-    Carver cv(ws);
     float* tmp = cv.take(ckpt_floats(B, T, H));
     HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, stream),
            "wkv7_backward checkpoint recompute");
     ck = tmp;
   }
   HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
-                              db, ds0, stream),
+                              db, ds0, part, stream),
          "wkv7_backward launch");
   return WKV7_OK;
 }
@@ -198,6 +199,7 @@ struct TmBwdBufs {
   float *dtg, *dg, *dy_wkv, *dr, *dkmod, *dvmod, *gr, *gw, *gk, *gv, *gA, *gB;
   float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *d_la, *d_lw, *d_lg, *d_lv;
   float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg, *part_post, *part_pre, *part_shift, *splitk, *out_tmp;
+  float* wkv_part;
 };
 
 // split-K factor for a weight gradient [Mo][No] reduced over BT tokens
@@ -239,6 +241,7 @@ void carve_bwd(Carver& c, const tm_shape* s, int B, int T, TmBwdBufs& m) {
   m.part_pre = c.take((size_t)5 * nblk * s->C);
   m.part_shift = c.take((size_t)6 * nblk * s->C);
   m.splitk = c.take(splitk_scratch(s, (int)BT));
+  m.wkv_part = c.take(wkv7_bwd_partial_floats(B, T, s->H));
   m.out_tmp = nullptr;
 }
 
@@ -444,7 +447,8 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
 
   HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
   HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
-                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0, st),
+                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
+                              bb.wkv_part, st),
          "wkv7 backward");
   HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
 
@@ -488,5 +492,24 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
   HIPCHK(tm_launch_reduce(bb.part_pre, 5, nblk, C, o2, st), "reduce pre");
   VecOut o3 = {{G->mu_r, G->mu_w, G->mu_k, G->mu_v, G->mu_a, G->mu_g, nullptr, nullptr}};
   HIPCHK(tm_launch_reduce(bb.part_shift, 6, nblk, C, o3, st), "reduce shift");
+  return WKV7_OK;
+}
+
+// ----------------------------------------------------------------- GEMM --
+extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float* A, int lda,
+                             const float* B, int ldb, float* C, int ldc, float beta,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  if (M < 1 || N < 1 || K < 1) return fail(WKV7_EINVAL, "M, N, K must be >= 1");
+  CHK(check_f32_ptr(A, "A", true));
+  CHK(check_f32_ptr(B, "B", true));
+  CHK(check_f32_ptr(C, "C", true));
+  const int a_inner = transA ? M : K, b_inner = transB ? K : N;
+  if (a_inner % 4 || b_inner % 4 || lda % 4 || ldb % 4)
+    return fail(WKV7_EINVAL, "contiguous GEMM dimensions and leading dims must be multiples of 4");
+  if (lda < a_inner || ldb < b_inner || ldc < N) return fail(WKV7_EINVAL, "leading dimension too small");
+  HIPCHK(gemm_f32_run(transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr, 1,
+                      nullptr, stream),
+         "gemm launch");
   return WKV7_OK;
 }

@@ -40,6 +40,37 @@ __device__ __forceinline__ f4 load4<bf16_t>(const bf16_t* p) {
   return r;
 }
 
+// Raw (unconverted) 4-element and 1-element storage types, used to stage data
+// through registers and LDS without converting it on the way.
+template <typename T>
+struct Raw;
+template <>
+struct Raw<float> {
+  typedef f4 v4;
+  typedef float v1;
+};
+template <>
+struct Raw<bf16_t> {
+  typedef uint2 v4;
+  typedef uint16_t v1;
+};
+template <typename T>
+__device__ __forceinline__ typename Raw<T>::v4 load_raw4(const T* p) {
+  return *reinterpret_cast<const typename Raw<T>::v4*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void store_raw4(T* p, typename Raw<T>::v4 x) {
+  *reinterpret_cast<typename Raw<T>::v4*>(p) = x;
+}
+template <typename T>
+__device__ __forceinline__ typename Raw<T>::v1 load_raw1(const T* p) {
+  return *reinterpret_cast<const typename Raw<T>::v1*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void store_raw1(T* p, typename Raw<T>::v1 x) {
+  *reinterpret_cast<typename Raw<T>::v1*>(p) = x;
+}
+
 template <typename T>
 __device__ __forceinline__ float load1(const T* p);
 template <>
@@ -85,6 +116,28 @@ __device__ __forceinline__ float rows4sum(float x) {
   x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Reduce-scatter over the wave's four 16-lane rows.  On entry every lane holds
+// 4*NQ values x[cc*NQ + q] (cc < 4 = its column within a float4, q < NQ);
+// on exit lane l holds in x[q] (q < NQ) the sum over lanes {l, l^16, l^32, l^48}
+// of the values with cc == l/16.  Two permlane-swap rounds, 3*NQ swap+add pairs.
+template <int NQ>
+__device__ __forceinline__ void rows4_reduce_scatter(float (&x)[4 * NQ]) {
+  // round 1: lanes 0-31 keep cc 0,1 (+ partner's), lanes 32-63 keep cc 2,3
+#pragma unroll
+  for (int i = 0; i < 2 * NQ; i++) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + 2 * NQ]),
+                                              false, false);
+    x[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  // round 2: within each half, even rows keep the first cc, odd rows the second
+#pragma unroll
+  for (int i = 0; i < NQ; i++) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + NQ]),
+                                              false, false);
+    x[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
 }
 
 // Full 64-lane wave sum, result in every lane.

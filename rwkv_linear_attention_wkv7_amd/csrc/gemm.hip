@@ -53,63 +53,71 @@ __global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float
   const int kend = min(K, kbeg + kslice);
   C += (size_t)blockIdx.z * M * ldc;  // split-K partials (z = 0 when not split)
 
+  // Tile loads are unconditional from clamped (always valid) addresses, so a
+  // whole tile is in flight at once; out-of-range elements are zeroed when the
+  // registers are written to LDS.
   f4 ra[A4], rb[B4];
+  unsigned oka = 0, okb = 0;
 
   auto load_tiles = [&](int k0) {
+    oka = okb = 0;
 #pragma unroll
     for (int q = 0; q < A4; q++) {
       const int idx = tid + 256 * q;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
       if (!TA) {  // A[m][k], float4 along k
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
         const int m = m0 + row, k = k0 + k4 * 4;
-        if (m < M && k < kend) x = *reinterpret_cast<const f4*>(A + (size_t)m * lda + k);
+        oka |= (unsigned)(m < M && k < kend) << q;
+        ra[q] = *reinterpret_cast<const f4*>(A + (size_t)min(m, M - 1) * lda + min(k, kend - 4));
       } else {    // A stored [K][M], float4 along m
         const int kr = idx / (BM / 4), m4 = idx % (BM / 4);
         const int k = k0 + kr, m = m0 + m4 * 4;
-        if (k < kend && m < M) x = *reinterpret_cast<const f4*>(A + (size_t)k * lda + m);
+        oka |= (unsigned)(k < kend && m < M) << q;
+        ra[q] = *reinterpret_cast<const f4*>(A + (size_t)min(k, kend - 1) * lda + min(m, M - 4));
       }
-      ra[q] = x;
     }
 #pragma unroll
     for (int q = 0; q < B4; q++) {
       const int idx = tid + 256 * q;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
       if (!TB) {  // B[k][n], float4 along n
         const int kr = idx / (BN / 4), n4 = idx % (BN / 4);
         const int k = k0 + kr, n = n0 + n4 * 4;
-        if (k < kend && n < N) x = *reinterpret_cast<const f4*>(B + (size_t)k * ldb + n);
+        okb |= (unsigned)(k < kend && n < N) << q;
+        rb[q] = *reinterpret_cast<const f4*>(B + (size_t)min(k, kend - 1) * ldb + min(n, N - 4));
       } else {    // B stored [N][K], float4 along k
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
         const int n = n0 + row, k = k0 + k4 * 4;
-        if (n < N && k < kend) x = *reinterpret_cast<const f4*>(B + (size_t)n * ldb + k);
+        okb |= (unsigned)(n < N && k < kend) << q;
+        rb[q] = *reinterpret_cast<const f4*>(B + (size_t)min(n, N - 1) * ldb + min(k, kend - 4));
       }
-      rb[q] = x;
     }
   };
   auto store_tiles = [&]() {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < A4; q++) {
       const int idx = tid + 256 * q;
+      const f4 x = (oka >> q) & 1u ? ra[q] : z;
       if (!TA) {
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
 #pragma unroll
-        for (int c = 0; c < 4; c++) As[k4 * 4 + c][row] = ra[q][c];
+        for (int c = 0; c < 4; c++) As[k4 * 4 + c][row] = x[c];
       } else {
         const int kr = idx / (BM / 4), m4 = idx % (BM / 4);
-        *reinterpret_cast<f4*>(&As[kr][m4 * 4]) = ra[q];
+        *reinterpret_cast<f4*>(&As[kr][m4 * 4]) = x;
       }
     }
 #pragma unroll
     for (int q = 0; q < B4; q++) {
       const int idx = tid + 256 * q;
+      const f4 x = (okb >> q) & 1u ? rb[q] : z;
       if (!TB) {
         const int kr = idx / (BN / 4), n4 = idx % (BN / 4);
-        *reinterpret_cast<f4*>(&Bs[kr][n4 * 4]) = rb[q];
+        *reinterpret_cast<f4*>(&Bs[kr][n4 * 4]) = x;
       } else {
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
 #pragma unroll
-        for (int c = 0; c < 4; c++) Bs[k4 * 4 + c][row] = rb[q][c];
+        for (int c = 0; c < 4; c++) Bs[k4 * 4 + c][row] = x[c];
       }
     }
   };

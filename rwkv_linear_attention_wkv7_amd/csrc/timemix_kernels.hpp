@@ -59,7 +59,8 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                 const void* k, const void* v, const void* a, const void* b,
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
-                                hipStream_t st);
+                                float* part, hipStream_t st);
+size_t wkv7_bwd_partial_floats(int B, int T, int H);
 hipError_t wkv7_launch_step(int dtype, int B, int H, const void* r, const void* w, const void* k,
                             const void* v, const void* a, const void* b, float* state, void* y,
                             hipStream_t st);

@@ -9,21 +9,31 @@
 //     sa  = S a_t ;  S = S diag(w_t) + sa b_t^T + v_t k_t^T ;  y_t = S r_t
 //
 // Every state row evolves independently of the others (row i only needs
-// v_t[i] and its own sa[i]), so rows are spread over lanes: a lane owns RPT
-// rows x 4 adjacent columns, 16 lanes (one DPP row) cover the 64 columns of a
-// state row, and the row dot products (S a, S r) are 16-lane DPP sums.  The
-// per-token vectors are staged through LDS in blocks of tokens and read as
-// float4 by every row that needs them.
+// v_t[i] and its own sa[i]), so rows are spread over lanes and workgroups: a
+// lane owns RPT rows x 4 adjacent columns, 16 lanes (one DPP row) cover the 64
+// columns of a state row, and the row dot products (S a, S r) are 16-lane DPP
+// sums.  The per-token vectors are staged through LDS in blocks of 16 tokens
+// and read as float4 by every row a lane owns.
+//
+// Backward: with G = dL/dS_t the reverse step is row-local too (G rows evolve
+// independently), except for the column sums dr, dk, db, dw, da over the 64
+// rows.  Those are reduced in-thread over a lane's rows, across the wave's
+// four 16-lane rows with gfx950 permlane swaps, across the workgroup's waves
+// through LDS once per 16-token chunk, and across the workgroups that share a
+// head through fp32 partial buffers summed by a second kernel in fixed order.
 
 #include "common.hpp"
 
 namespace wkv7k {
 
 constexpr int N = WKV7_N;
-constexpr int TT = 16;    // tokens per LDS staging block (forward)
-constexpr int CKL = 16;   // checkpoint interval (tokens)
-constexpr int SUB = 8;    // backward sub-chunk kept as register history
-static_assert(CKL == 2 * SUB, "backward assumes two sub-chunks per checkpoint");
+constexpr int TT = 16;    // tokens per LDS staging block
+constexpr int CKL = 16;   // checkpoint interval (tokens) = backward chunk
+static_assert(CKL == TT, "checkpoints are taken at block starts");
+
+__device__ __forceinline__ float dot4(const float (&s)[4], f4 v) {
+  return fmaf(s[3], v[3], fmaf(s[2], v[2], fmaf(s[1], v[1], s[0] * v[0])));
+}
 
 // ------------------------------------------------------------------ forward
 // Grid: B*H*(64/(16*RPT)) workgroups of 256 threads; workgroup -> (b, h, row
@@ -37,8 +47,11 @@ __global__ __launch_bounds__(256) void fwd_seq(
     float* __restrict__ sT, float* __restrict__ ckpt) {
   constexpr int ROWS = 16 * RPT;
   constexpr int NRB = N / ROWS;
-  __shared__ f4 sv[2][TT][5][16];     // r, w, k, a, b of each staged token
-  __shared__ float svv[2][TT][ROWS];  // v of this workgroup's rows
+  // raw (unconverted) staging: r, w, k, a, b of each token, v of this slice
+  __shared__ __attribute__((aligned(16))) T sv[2][TT][5][N];
+  __shared__ __attribute__((aligned(16))) T svv[2][TT][ROWS];
+  typedef typename Raw<T>::v4 R4;
+  typedef typename Raw<T>::v1 R1;
 
   const int g = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = g / NRB, rb = g - bh * NRB;
@@ -63,50 +76,73 @@ __global__ __launch_bounds__(256) void fwd_seq(
   auto vec_ptr = [&](int vi) -> const T* {
     return vi == 0 ? r : vi == 1 ? w : vi == 2 ? k : vi == 3 ? a : bv;
   };
-  constexpr int NV4 = TT * 5 * 16;        // float4 slots per block
-  constexpr int NV4_PER = (NV4 + 255) / 256;
+  constexpr int NV4 = TT * 5 * 16;  // float4 slots per block
+  constexpr int NV4_PER = NV4 / 256;
+  static_assert(NV4 % 256 == 0, "block staging assumes 256 threads");
   constexpr int NVV_PER = (TT * ROWS + 255) / 256;
-  f4 pre[NV4_PER];
-  float prev[NVV_PER];
+  R4 pre[NV4_PER];
+  R1 prev[NVV_PER];
 
+  // thread -> (token, vector, column group) slots of the staged block
+  // Loads are unconditional from clamped (always valid) token indices so that
+  // all of them are in flight together; tokens past the end are never used.
   auto load_block = [&](int t0) {
 #pragma unroll
     for (int q = 0; q < NV4_PER; q++) {
       const int f = tid + 256 * q;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
-      if (f < NV4) {
-        const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-        if (t0 + tok < Tn) x = load4(vec_ptr(vi) + vbase + (size_t)(t0 + tok) * C + c4 * 4);
-      }
-      pre[q] = x;
+      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+      const int tc = min(t0 + tok, Tn - 1);
+      pre[q] = load_raw4(vec_ptr(vi) + vbase + (size_t)tc * C + c4 * 4);
     }
 #pragma unroll
     for (int q = 0; q < NVV_PER; q++) {
-      const int f = tid + 256 * q;
-      float x = 0.f;
-      if (f < TT * ROWS) {
-        const int tok = f / ROWS, rr = f - tok * ROWS;
-        if (t0 + tok < Tn) x = load1(v + vbase + (size_t)(t0 + tok) * C + rb * ROWS + rr);
-      }
-      prev[q] = x;
+      const int f = min(tid + 256 * q, TT * ROWS - 1);
+      const int tok = f / ROWS, rr = f - tok * ROWS;
+      const int tc = min(t0 + tok, Tn - 1);
+      prev[q] = load_raw1(v + vbase + (size_t)tc * C + rb * ROWS + rr);
     }
   };
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < NV4_PER; q++) {
       const int f = tid + 256 * q;
-      if (f < NV4) {
-        const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-        sv[buf][tok][vi][c4] = pre[q];
-      }
+      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+      store_raw4(&sv[buf][tok][vi][c4 * 4], pre[q]);
     }
 #pragma unroll
     for (int q = 0; q < NVV_PER; q++) {
       const int f = tid + 256 * q;
       if (f < TT * ROWS) {
         const int tok = f / ROWS, rr = f - tok * ROWS;
-        svv[buf][tok][rr] = prev[q];
+        store_raw1(&svv[buf][tok][rr], prev[q]);
       }
+    }
+  };
+
+  // one token; the row sums of y stay with the lane whose cg equals tt
+  float yb[RPT];
+  auto token = [&](int buf, int tt) {
+    const f4 av = load4(&sv[buf][tt][3][cg * 4]);
+    const f4 wv = load4(&sv[buf][tt][1][cg * 4]), kv = load4(&sv[buf][tt][2][cg * 4]);
+    const f4 bb = load4(&sv[buf][tt][4][cg * 4]), rv = load4(&sv[buf][tt][0][cg * 4]);
+    float sa[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) sa[m] = dot4(S[m], av);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) sa[m] = rowsum16(sa[m]);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      const float vv = load1(&svv[buf][tt][rloc0 + m]);
+#pragma unroll
+      for (int c = 0; c < 4; c++) S[m][c] = fmaf(vv, kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
+    }
+    float yy[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) yy[m] = dot4(S[m], rv);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      yy[m] = rowsum16(yy[m]);
+      yb[m] = (cg == tt) ? yy[m] : yb[m];
     }
   };
 
@@ -117,42 +153,25 @@ __global__ __launch_bounds__(256) void fwd_seq(
   for (int t0 = 0; t0 < Tn; t0 += TT, buf ^= 1) {
     const bool more = t0 + TT < Tn;
     if (more) load_block(t0 + TT);
-    const int nt = min(TT, Tn - t0);
-    for (int tt = 0; tt < nt; tt++) {
-      const int t = t0 + tt;
-      if (ckpt && (t % CKL) == 0) {
-        float* cp = ckpt + (((size_t)bh * nck + t / CKL) * N + row0) * N + cg * 4;
-#pragma unroll
-        for (int m = 0; m < RPT; m++) {
-          f4 x = {S[m][0], S[m][1], S[m][2], S[m][3]};
-          *reinterpret_cast<f4*>(cp + (size_t)m * N) = x;
-        }
-      }
-      const f4 av = sv[buf][tt][3][cg];
-      float sa[RPT];
+    if (ckpt) {
+      float* cp = ckpt + (((size_t)bh * nck + t0 / CKL) * N + row0) * N + cg * 4;
 #pragma unroll
       for (int m = 0; m < RPT; m++)
-        sa[m] = fmaf(S[m][3], av[3], fmaf(S[m][2], av[2], fmaf(S[m][1], av[1], S[m][0] * av[0])));
+        *reinterpret_cast<f4*>(cp + (size_t)m * N) = f4{S[m][0], S[m][1], S[m][2], S[m][3]};
+    }
+    const int nt = min(TT, Tn - t0);
 #pragma unroll
-      for (int m = 0; m < RPT; m++) sa[m] = rowsum16(sa[m]);
-      const f4 wv = sv[buf][tt][1][cg], kv = sv[buf][tt][2][cg], bb = sv[buf][tt][4][cg];
+    for (int m = 0; m < RPT; m++) yb[m] = 0.f;
+    if (nt == TT) {
 #pragma unroll
-      for (int m = 0; m < RPT; m++) {
-        const float vv = svv[buf][tt][rloc0 + m];
+      for (int tt = 0; tt < TT; tt++) token(buf, tt);
+    } else {
+      for (int tt = 0; tt < nt; tt++) token(buf, tt);
+    }
+    if (y && cg < nt) {
+      T* yp = y + vbase + (size_t)(t0 + cg) * C + row0;
 #pragma unroll
-        for (int c = 0; c < 4; c++) S[m][c] = fmaf(vv, kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
-      }
-      if (y) {
-        const f4 rv = sv[buf][tt][0][cg];
-        float yo = 0.f;
-#pragma unroll
-        for (int m = 0; m < RPT; m++) {
-          float d = fmaf(S[m][3], rv[3], fmaf(S[m][2], rv[2], fmaf(S[m][1], rv[1], S[m][0] * rv[0])));
-          d = rowsum16(d);
-          if (cg == m) yo = d;
-        }
-        if (cg < RPT) store1(y + vbase + (size_t)t * C + row0 + cg, yo);
-      }
+      for (int m = 0; m < RPT; m++) store1(yp + m, yb[m]);
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
@@ -160,10 +179,9 @@ __global__ __launch_bounds__(256) void fwd_seq(
 
   if (sT) {
 #pragma unroll
-    for (int m = 0; m < RPT; m++) {
-      f4 x = {S[m][0], S[m][1], S[m][2], S[m][3]};
-      *reinterpret_cast<f4*>(sT + sbase + (size_t)(row0 + m) * N + cg * 4) = x;
-    }
+    for (int m = 0; m < RPT; m++)
+      *reinterpret_cast<f4*>(sT + sbase + (size_t)(row0 + m) * N + cg * 4) =
+          f4{S[m][0], S[m][1], S[m][2], S[m][3]};
   }
 }
 
@@ -217,214 +235,230 @@ __global__ __launch_bounds__(256) void step_kernel(
 }
 
 // ----------------------------------------------------------------- backward
-// One workgroup (256 threads) per (b,h).  Thread: column group cg = tid%16,
-// rows 4*rg .. 4*rg+3 with rg = tid/16 (each wave holds 16 rows).
-// Checkpoint chunks of CKL tokens are processed last to first; each chunk is
-// recomputed from its checkpoint in two sub-chunks of SUB tokens whose states
-// are kept in registers.  Per token the column reductions (dr, dk, db, dw,
-// da: sums over the 64 rows) go in-thread over 4 rows, across the wave's
-// four 16-lane rows with permlane swaps, and across the 4 waves through LDS.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_seq(
+// Workgroup = (b, h, one of NSPLIT row slices of ROWS = RPT*RG rows), 16*RG
+// threads.  Thread: column group cg = tid%16, rows slice*ROWS + rg*RPT + m.
+// Chunks of CKL tokens are processed last to first; each is recomputed from
+// its checkpoint with the states before every token kept in registers.
+// Output: fp32 column partials part[slice][vec][B][T][H][N] for vec = dr, dk,
+// db, dw, da (summed over the slices by reduce_partials), dv directly.
+template <int RPT, int RG, typename T>
+__global__ __launch_bounds__(16 * RG) void bwd_seq(
     int B, int Tn, int H, const T* __restrict__ r, const T* __restrict__ w,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ a,
     const T* __restrict__ bv, const T* __restrict__ dy, const float* __restrict__ ckpt,
-    const float* __restrict__ dsT, T* __restrict__ dr, T* __restrict__ dw,
-    T* __restrict__ dk, T* __restrict__ dv, T* __restrict__ da, T* __restrict__ db,
+    const float* __restrict__ dsT, float* __restrict__ part, T* __restrict__ dv,
     float* __restrict__ ds0) {
-  __shared__ f4 sv[SUB][5][16];     // r, w, k, a, b
-  __shared__ float svr[SUB][2][N];  // v, dy
-  __shared__ f4 red[2][4][5][16];   // per-wave column partials: dr, dk, db, dw, da
+  constexpr int ROWS = RPT * RG, NSPLIT = N / ROWS, NW = RG / 4, NT = 16 * RG;
+  static_assert(RG % 4 == 0, "whole waves");
+  // raw staging, double-buffered: the next (earlier) chunk is fetched into
+  // registers while the current one is processed
+  __shared__ __attribute__((aligned(16))) T sv[2][CKL][5][N];   // r, w, k, a, b
+  __shared__ __attribute__((aligned(16))) T svr[2][CKL][2][ROWS];  // v, dy of this slice
+  __shared__ __attribute__((aligned(16))) float red[NW][CKL][5][N];  // per-wave column partials
+  typedef typename Raw<T>::v4 R4;
+  typedef typename Raw<T>::v1 R1;
 
-  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = g / NSPLIT, sp = g - bh * NSPLIT;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, cg = tid & 15, rg = tid >> 4;
   const int lane = tid & 63, wave = tid >> 6;
-  const int row0 = rg * 4;
+  const int rloc0 = rg * RPT;
+  const int row0 = sp * ROWS + rloc0;
   const size_t C = (size_t)H * N;
   const size_t vbase = (size_t)b * Tn * C + (size_t)h * N;
   const size_t sbase = ((size_t)b * H + h) * N * N;
+  const size_t plane = (size_t)B * Tn * C;  // elements of one gradient tensor
   const int nck = (Tn + CKL - 1) / CKL;
   auto vec_ptr = [&](int vi) -> const T* {
     return vi == 0 ? r : vi == 1 ? w : vi == 2 ? k : vi == 3 ? a : bv;
   };
-  auto out_ptr = [&](int vi) -> T* {
-    return vi == 0 ? dr : vi == 1 ? dk : vi == 2 ? db : vi == 3 ? dw : da;
-  };
 
-  float G[4][4];
+  float G[RPT][4];
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
+  for (int m = 0; m < RPT; m++) {
     f4 x = {0.f, 0.f, 0.f, 0.f};
     if (dsT) x = *reinterpret_cast<const f4*>(dsT + sbase + (size_t)(row0 + m) * N + cg * 4);
 #pragma unroll
     for (int c = 0; c < 4; c++) G[m][c] = x[c];
   }
 
-  auto stage = [&](int ts0, int ns) {
-    for (int f = tid; f < SUB * 80; f += 256) {
+  // unconditional loads from clamped token indices (all in flight together)
+  constexpr int NA = (CKL * 80 + NT - 1) / NT, NB = (CKL * 2 * ROWS + NT - 1) / NT;
+  R4 xa[NA];
+  R1 xb[NB];
+  auto fetch = [&](int c) {
+    const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
+#pragma unroll
+    for (int q = 0; q < NA; q++) {
+      const int f = min(tid + NT * q, CKL * 80 - 1);
       const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
-      if (tok < ns) x = load4(vec_ptr(vi) + vbase + (size_t)(ts0 + tok) * C + c4 * 4);
-      sv[tok][vi][c4] = x;
+      xa[q] = load_raw4(vec_ptr(vi) + vbase + (size_t)(tc0 + min(tok, ns - 1)) * C + c4 * 4);
     }
-    for (int f = tid; f < SUB * 2 * N; f += 256) {
-      const int tok = f / (2 * N), rem = f - tok * 2 * N, vi = rem / N, i = rem - vi * N;
-      float x = 0.f;
-      if (tok < ns) x = load1((vi ? dy : v) + vbase + (size_t)(ts0 + tok) * C + i);
-      svr[tok][vi][i] = x;
+#pragma unroll
+    for (int q = 0; q < NB; q++) {
+      const int f = min(tid + NT * q, CKL * 2 * ROWS - 1);
+      const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
+      xb[q] = load_raw1((vi ? dy : v) + vbase + (size_t)(tc0 + min(tok, ns - 1)) * C + sp * ROWS + i);
     }
   };
-  auto load_ckpt = [&](int c, float (&S)[4][4]) {
-    const float* cp = ckpt + (((size_t)bh * nck + c) * N + row0) * N + cg * 4;
+  auto commit = [&](int buf) {
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      f4 x = *reinterpret_cast<const f4*>(cp + (size_t)m * N);
-#pragma unroll
-      for (int cc = 0; cc < 4; cc++) S[m][cc] = x[cc];
+    for (int q = 0; q < NA; q++) {
+      const int f = tid + NT * q;
+      if (f < CKL * 80) {
+        const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+        store_raw4(&sv[buf][tok][vi][c4 * 4], xa[q]);
+      }
     }
-  };
-  // one forward token from S (in place); returns sa (full row sums) in sa[]
-  auto fwd_tok = [&](int tt, float (&S)[4][4], float (&sa)[4]) {
-    const f4 av = sv[tt][3][cg];
 #pragma unroll
-    for (int m = 0; m < 4; m++)
-      sa[m] = rowsum16(fmaf(S[m][3], av[3], fmaf(S[m][2], av[2], fmaf(S[m][1], av[1], S[m][0] * av[0]))));
-    const f4 wv = sv[tt][1][cg], kv = sv[tt][2][cg], bb = sv[tt][4][cg];
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const float vv = svr[tt][0][row0 + m];
-#pragma unroll
-      for (int c = 0; c < 4; c++) S[m][c] = fmaf(vv, kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
+    for (int q = 0; q < NB; q++) {
+      const int f = tid + NT * q;
+      if (f < CKL * 2 * ROWS) {
+        const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
+        store_raw1(&svr[buf][tok][vi][i], xb[q]);
+      }
     }
   };
 
-  int rbuf = 0;
-  for (int c = nck - 1; c >= 0; c--) {
-    const int tc0 = c * CKL, tc1 = min(Tn, tc0 + CKL);
-    const int nsub = (tc1 - tc0 + SUB - 1) / SUB;
-    // state at the start of the second sub-chunk
-    float S1[4][4];
-    if (nsub == 2) {
-      load_ckpt(c, S1);
-      __syncthreads();
-      stage(tc0, SUB);
-      __syncthreads();
-      float sa[4];
+  fetch(nck - 1);
+  commit(0);
+  int buf = 0;
+  for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
+    const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
+    __syncthreads();  // staged chunk visible; previous readers of the other buffer done
+    if (c > 0) fetch(c - 1);
+    float Sh[CKL + 1][RPT][4];
+    {
+      const float* cp = ckpt + (((size_t)bh * nck + c) * N + row0) * N + cg * 4;
 #pragma unroll
-      for (int tt = 0; tt < SUB; tt++) fwd_tok(tt, S1, sa);
+      for (int m = 0; m < RPT; m++) {
+        const f4 x = *reinterpret_cast<const f4*>(cp + (size_t)m * N);
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = x[cc];
+      }
     }
-    for (int s = nsub - 1; s >= 0; s--) {
-      const int ts0 = tc0 + s * SUB, ns = min(SUB, tc1 - ts0);
-      __syncthreads();
-      stage(ts0, ns);
-      __syncthreads();
-      float Sh[SUB + 1][4][4];
-      float sah[SUB][4];
-      if (s == 1) {
+
+    // recompute: Sh[tt] = state before token tt, sah[tt] = S a_tt
+    float sah[CKL][RPT];
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+    for (int tt = 0; tt < CKL; tt++) {
+      if (tt < ns) {
+        const f4 av = load4(&sv[buf][tt][3][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
+        const f4 kv = load4(&sv[buf][tt][2][cg * 4]), bb = load4(&sv[buf][tt][4][cg * 4]);
 #pragma unroll
-          for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = S1[m][cc];
-      } else {
-        load_ckpt(c, Sh[0]);
-      }
+        for (int m = 0; m < RPT; m++) sah[tt][m] = dot4(Sh[tt][m], av);
 #pragma unroll
-      for (int tt = 0; tt < SUB; tt++) {
+        for (int m = 0; m < RPT; m++) sah[tt][m] = rowsum16(sah[tt][m]);
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+        for (int m = 0; m < RPT; m++) {
+          const float vv = load1(&svr[buf][tt][0][rloc0 + m]);
 #pragma unroll
-          for (int cc = 0; cc < 4; cc++) Sh[tt + 1][m][cc] = Sh[tt][m][cc];
-        if (tt < ns) fwd_tok(tt, Sh[tt + 1], sah[tt]);
-      }
-#pragma unroll
-      for (int tt = SUB - 1; tt >= 0; tt--) {
-        if (tt < ns) {
-          const int t = ts0 + tt;
-          const f4 rv = sv[tt][0][cg], wv = sv[tt][1][cg], kv = sv[tt][2][cg];
-          const f4 av = sv[tt][3][cg], bb = sv[tt][4][cg];
-          float vv[4], dyv[4];
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            vv[m] = svr[tt][0][row0 + m];
-            dyv[m] = svr[tt][1][row0 + m];
-          }
-          float pr[4], pk[4], pb[4], pw[4], pa[4], dvv[4], dsa[4];
-#pragma unroll
-          for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int cc = 0; cc < 4; cc++) G[m][cc] = fmaf(dyv[m], rv[cc], G[m][cc]);
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            dvv[m] = fmaf(G[m][3], kv[3], fmaf(G[m][2], kv[2], fmaf(G[m][1], kv[1], G[m][0] * kv[0])));
-            dsa[m] = fmaf(G[m][3], bb[3], fmaf(G[m][2], bb[2], fmaf(G[m][1], bb[1], G[m][0] * bb[0])));
-          }
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            dvv[m] = rowsum16(dvv[m]);
-            dsa[m] = rowsum16(dsa[m]);
-          }
-#pragma unroll
-          for (int cc = 0; cc < 4; cc++) {
-            float xr = 0.f, xk = 0.f, xb = 0.f, xw = 0.f, xa = 0.f;
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-              xr = fmaf(Sh[tt + 1][m][cc], dyv[m], xr);
-              xk = fmaf(G[m][cc], vv[m], xk);
-              xb = fmaf(G[m][cc], sah[tt][m], xb);
-              xw = fmaf(G[m][cc], Sh[tt][m][cc], xw);
-              xa = fmaf(dsa[m], Sh[tt][m][cc], xa);
-            }
-            pr[cc] = xr; pk[cc] = xk; pb[cc] = xb; pw[cc] = xw; pa[cc] = xa;
-          }
-#pragma unroll
-          for (int m = 0; m < 4; m++)
-#pragma unroll
-            for (int cc = 0; cc < 4; cc++) G[m][cc] = fmaf(dsa[m], av[cc], G[m][cc] * wv[cc]);
-#pragma unroll
-          for (int cc = 0; cc < 4; cc++) {
-            pr[cc] = rows4sum(pr[cc]);
-            pk[cc] = rows4sum(pk[cc]);
-            pb[cc] = rows4sum(pb[cc]);
-            pw[cc] = rows4sum(pw[cc]);
-            pa[cc] = rows4sum(pa[cc]);
-          }
-          if (lane < 16) {
-            red[rbuf][wave][0][cg] = f4{pr[0], pr[1], pr[2], pr[3]};
-            red[rbuf][wave][1][cg] = f4{pk[0], pk[1], pk[2], pk[3]};
-            red[rbuf][wave][2][cg] = f4{pb[0], pb[1], pb[2], pb[3]};
-            red[rbuf][wave][3][cg] = f4{pw[0], pw[1], pw[2], pw[3]};
-            red[rbuf][wave][4][cg] = f4{pa[0], pa[1], pa[2], pa[3]};
-          }
-          if (cg < 4) {
-            float o = dvv[0];
-#pragma unroll
-            for (int m = 1; m < 4; m++)
-              if (cg == m) o = dvv[m];
-            store1(dv + vbase + (size_t)t * C + row0 + cg, o);
-          }
-          __syncthreads();
-          if (tid < 80) {
-            const int vi = tid >> 4, c4 = tid & 15;
-            f4 s4 = red[rbuf][0][vi][c4];
-            s4 += red[rbuf][1][vi][c4];
-            s4 += red[rbuf][2][vi][c4];
-            s4 += red[rbuf][3][vi][c4];
-            store4(out_ptr(vi) + vbase + (size_t)t * C + c4 * 4, s4);
-          }
-          rbuf ^= 1;
+          for (int cc = 0; cc < 4; cc++)
+            Sh[tt + 1][m][cc] = fmaf(vv, kv[cc], fmaf(sah[tt][m], bb[cc], Sh[tt][m][cc] * wv[cc]));
         }
       }
     }
+
+    float dvb[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) dvb[m] = 0.f;
+#pragma unroll
+    for (int tt = CKL - 1; tt >= 0; tt--) {
+      if (tt < ns) {
+        const f4 rv = load4(&sv[buf][tt][0][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
+        const f4 kv = load4(&sv[buf][tt][2][cg * 4]), av = load4(&sv[buf][tt][3][cg * 4]);
+        const f4 bb = load4(&sv[buf][tt][4][cg * 4]);
+        float vv[RPT], dyv[RPT], dvv[RPT], dsa[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          vv[m] = load1(&svr[buf][tt][0][rloc0 + m]);
+          dyv[m] = load1(&svr[buf][tt][1][rloc0 + m]);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; m++)
+#pragma unroll
+          for (int cc = 0; cc < 4; cc++) G[m][cc] = fmaf(dyv[m], rv[cc], G[m][cc]);
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          dvv[m] = dot4(G[m], kv);
+          dsa[m] = dot4(G[m], bb);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          dvv[m] = rowsum16(dvv[m]);
+          dsa[m] = rowsum16(dsa[m]);
+          dvb[m] = (cg == tt) ? dvv[m] : dvb[m];
+        }
+        // column partials over this lane's rows: x[cc*5 + vec], vec = dr, dk, db, dw, da
+        float x[20];
+#pragma unroll
+        for (int cc = 0; cc < 4; cc++) {
+          float xr = 0.f, xk = 0.f, xb = 0.f, xw = 0.f, xa = 0.f;
+#pragma unroll
+          for (int m = 0; m < RPT; m++) {
+            xr = fmaf(Sh[tt + 1][m][cc], dyv[m], xr);
+            xk = fmaf(G[m][cc], vv[m], xk);
+            xb = fmaf(G[m][cc], sah[tt][m], xb);
+            xw = fmaf(G[m][cc], Sh[tt][m][cc], xw);
+            xa = fmaf(dsa[m], Sh[tt][m][cc], xa);
+          }
+          x[cc * 5 + 0] = xr; x[cc * 5 + 1] = xk; x[cc * 5 + 2] = xb;
+          x[cc * 5 + 3] = xw; x[cc * 5 + 4] = xa;
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; m++)
+#pragma unroll
+          for (int cc = 0; cc < 4; cc++) G[m][cc] = fmaf(dsa[m], av[cc], G[m][cc] * wv[cc]);
+        // after the reduce-scatter lane (row-in-wave q, cg) holds the wave's sums
+        // for column 4*cg + q
+        rows4_reduce_scatter<5>(x);
+        const int col = cg * 4 + ((lane >> 4) & 3);
+#pragma unroll
+        for (int vi = 0; vi < 5; vi++) red[wave][tt][vi][col] = x[vi];
+      }
+    }
+    if (cg < ns) {
+      T* dp = dv + vbase + (size_t)(tc0 + cg) * C + row0;
+#pragma unroll
+      for (int m = 0; m < RPT; m++) store1(dp + m, dvb[m]);
+    }
+    __syncthreads();
+    for (int f = tid; f < ns * 80; f += NT) {
+      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+      f4 s4 = *reinterpret_cast<const f4*>(&red[0][tok][vi][c4 * 4]);
+#pragma unroll
+      for (int wv = 1; wv < NW; wv++) s4 += *reinterpret_cast<const f4*>(&red[wv][tok][vi][c4 * 4]);
+      *reinterpret_cast<f4*>(part + ((size_t)sp * 5 + vi) * plane + vbase + (size_t)(tc0 + tok) * C +
+                             c4 * 4) = s4;
+    }
+    if (c > 0) commit(buf ^ 1);
   }
   if (ds0) {
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      f4 x = {G[m][0], G[m][1], G[m][2], G[m][3]};
-      *reinterpret_cast<f4*>(ds0 + sbase + (size_t)(row0 + m) * N + cg * 4) = x;
-    }
+    for (int m = 0; m < RPT; m++)
+      *reinterpret_cast<f4*>(ds0 + sbase + (size_t)(row0 + m) * N + cg * 4) =
+          f4{G[m][0], G[m][1], G[m][2], G[m][3]};
   }
 }
+
+// out_vec = sum over slices of part[slice][vec] (fixed order), cast to T.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int nsplit,
+                                                           const float* __restrict__ part, T* dr,
+                                                           T* dk, T* db, T* dw, T* da) {
+  const size_t n4 = plane4 * 5;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const int vi = (int)(i / plane4);
+    const size_t e4 = i - (size_t)vi * plane4;
+    f4 s = reinterpret_cast<const f4*>(part)[((size_t)0 * 5 + vi) * plane4 + e4];
+    for (int sp = 1; sp < nsplit; sp++) s += reinterpret_cast<const f4*>(part)[((size_t)sp * 5 + vi) * plane4 + e4];
+    T* o = vi == 0 ? dr : vi == 1 ? dk : vi == 2 ? db : vi == 3 ? dw : da;
+    store4(o + e4 * 4, s);
+  }
+}
+
+int bwd_nsplit(int B, int H) { return (size_t)B * H * 2 >= 256 ? 2 : 4; }
 
 }  // namespace wkv7k
 
@@ -436,7 +470,7 @@ template <typename T>
 hipError_t launch_forward_t(int B, int T_, int H, const void* r, const void* w, const void* k,
                             const void* v, const void* a, const void* b, const float* s0, void* y,
                             float* sT, float* ckpt, hipStream_t st) {
-  constexpr int RPT = 1;
+  constexpr int RPT = 2;
   const int nblk = B * H * (N / (16 * RPT));
   hipLaunchKernelGGL((fwd_seq<RPT, T>), dim3(nblk), dim3(256), 0, st, B, T_, H,
                      (const T*)r, (const T*)w, (const T*)k, (const T*)v, (const T*)a,
@@ -448,10 +482,25 @@ template <typename T>
 hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w, const void* k,
                              const void* v, const void* a, const void* b, const void* dy,
                              const float* ckpt, const float* dsT, void* dr, void* dw, void* dk,
-                             void* dv, void* da, void* db, float* ds0, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_seq<T>), dim3(B * H), dim3(256), 0, st, B, T_, H, (const T*)r,
-                     (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                     (const T*)dy, ckpt, dsT, (T*)dr, (T*)dw, (T*)dk, (T*)dv, (T*)da, (T*)db, ds0);
+                             void* dv, void* da, void* db, float* ds0, float* part,
+                             hipStream_t st) {
+  const int ns = bwd_nsplit(B, H);
+  const dim3 grid(B * H * ns);
+  if (ns == 2)
+    hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+  else
+    hipLaunchKernelGGL((bwd_seq<2, 8, T>), grid, dim3(128), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t plane4 = (size_t)B * T_ * H * N / 4;
+  size_t blocks = (plane4 * 5 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((reduce_bwd_partials<T>), dim3((unsigned)blocks), dim3(256), 0, st, plane4, ns,
+                     part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
   return hipGetLastError();
 }
 
@@ -473,16 +522,20 @@ hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, co
   return wkv7k::launch_forward_t<float>(B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, st);
 }
 
+size_t wkv7_bwd_partial_floats(int B, int T, int H) {
+  return (size_t)wkv7k::bwd_nsplit(B, H) * 5 * B * T * H * WKV7_N;
+}
+
 hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, const void* w,
                                 const void* k, const void* v, const void* a, const void* b,
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
-                                hipStream_t st) {
+                                float* part, hipStream_t st) {
   if (dtype == 1)
     return wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk,
-                                            dv, da, db, ds0, st);
+                                            dv, da, db, ds0, part, st);
   return wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk, dv,
-                                         da, db, ds0, st);
+                                         da, db, ds0, part, st);
 }
 
 hipError_t wkv7_launch_step(int dtype, int B, int H, const void* r, const void* w, const void* k,

@@ -78,8 +78,9 @@ def test_forward_rejects_null_and_misaligned(L):
 
 def test_backward_needs_workspace_without_checkpoints(L):
     need = L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 0)
-    assert need >= L.wkv7_checkpoint_floats(1, 64, 4, 64) * 4
-    assert L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 1) == 0
+    have = L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 1)
+    assert need >= have + L.wkv7_checkpoint_floats(1, 64, 4, 64) * 4
+    assert have > 0   # column partials of the row-split reverse pass
     ptr13 = [A] * 13
     rc = L.wkv7_backward(1, 64, 4, 64, 0, *ptr13[:6], None, None, ptr13[6], None, *ptr13[7:13],
                          None, A, need - 1, None)
