@@ -2,6 +2,10 @@
 """Throughput of the RWKV-7 WKV7 / time-mix hot path on one MI355X.
 
 Prints ONE JSON line.  Workloads (--workload):
+  decode     (default) streaming decode through a 12-layer RWKV-7 stack,
+             C=256 H=4 FFN 1024, LoRA 32/32/32/64, vocab 256, 2048
+             independent streams, fp32, one token per stream per step
+             (steps/s); the step is replayed from a captured HIP graph
   timemix    time-mix block forward+backward, B=8 T=1024 C=768 (H=12),
              LoRA ranks w/a/v/g = 64/64/32/128, layer > 0, fp32 (tokens/s)
   wkv7_long  WKV7 forward+backward, B=4 T=8192 H=32 N=64, bf16 token
@@ -168,7 +172,83 @@ def setup_wkv7_long():
                 roof=roof, cpu=cpu)
 
 
-WORKLOADS = {"timemix": setup_timemix, "wkv7_long": setup_wkv7_long}
+def setup_decode():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    L, C, H, F, V, B, STEPS = 12, 256, 4, 1024, 256, 2048, 512
+    ranks = (32, 32, 32, 64)
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=0)
+    dev = torch.device("cuda")
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    w = {k: d(v) for k, v in m.items() if k != "blocks"}
+    w["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
+                    for k, v in b.items()} for b in m["blocks"]]
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=1), w)
+    tokens_np = synth.token_ids(STEPS, B, V, seed=0, name="decode_tokens")
+    tokens = torch.from_numpy(tokens_np).to(dev)
+    st = dm.new_state(B)
+    cur = torch.empty(B, dtype=torch.int32, device=dev)
+    logits = torch.empty((B, V), device=dev)
+    ws = torch.empty(binding.rwkv7_decode_workspace_bytes(dm, B), dtype=torch.uint8, device=dev)
+    cur.copy_(tokens[0])
+    binding.rwkv7_decode_step(dm, cur, st, logits=logits, ws=ws)
+    torch.cuda.synchronize()
+    for k in st:
+        st[k].zero_()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            binding.rwkv7_decode_step(dm, cur, st, logits=logits, ws=ws)
+    torch.cuda.synchronize()
+    pos = [0]
+
+    def step():
+        cur.copy_(tokens[pos[0] % STEPS])
+        g.replay()
+        pos[0] += 1
+
+    # dominant kernel: wkv7_step on one layer's state (2048 streams x 4 heads)
+    vec = [torch.from_numpy(synth.wkv7_inputs(B, 1, H, 64, seed=9)[n][:, 0].copy()).to(dev)
+           for n in ("r", "w", "k", "v", "a", "b")]
+    state1 = st["att_state"][0]
+    y1 = torch.empty_like(vec[0])
+
+    def dom():
+        binding.wkv7_step(*vec, state1, y=y1)
+
+    nbytes = 2.0 * B * H * 64 * 64 * 4 + 7.0 * B * H * 64 * 4
+    roof = dict(kernel="wkv7_step (2048 streams x 4 heads, fp32 state in place)", bound="hbm",
+                work=nbytes, unit="GB/s", peak=PEAK["hbm"][0], fn=dom, key="wkv7_step_decode",
+                src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+
+    def cpu():
+        from oracle import stack
+        from oracle import wkv7 as ow
+        ns, steps = 16, 8
+        idx = np.arange(ns) * (B // ns)
+        ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+        state = stack.init_state(ocfg, ns)
+        t0 = time.perf_counter()
+        for t in range(steps):
+            _, state = stack.decode_step(m, ocfg, tokens_np[t, idx], state)
+        dt = time.perf_counter() - t0
+        per_step_full = dt / steps * (B / ns)
+        return dict(value=1.0 / per_step_full, unit="steps/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"{ns} of {B} streams x {steps} steps (f64), {dt:.1f} s; scaled to "
+                           f"{B} streams")
+
+    cfg = {"workload": "streaming decode, 12-layer RWKV-7 stack", "n_layer": L, "C": C, "H": H,
+           "N": 64, "ffn": F, "vocab": V, "lora_ranks_w_a_v_g": list(ranks), "streams": B,
+           "tokens_per_step": B, "token_steps_available": STEPS, "graph_replay": True,
+           "global_batch": B, "seq_len": 1, "parallelism": "single GPU"}
+    return dict(step=step, tokens=1, unit="steps/s", dtype="f32", config=cfg, roof=roof, cpu=cpu,
+                extra=lambda v: {"tokens_per_s": round(v * B, 1)})
+
+
+WORKLOADS = {"decode": setup_decode, "timemix": setup_timemix, "wkv7_long": setup_wkv7_long}
 
 
 def main():
@@ -176,7 +256,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="timemix", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roof-iters", type=int, default=20)
     args = ap.parse_args()
@@ -210,7 +290,8 @@ def main():
     r = w["roof"]
     r["fn"]()
     kms = time_loop(r["fn"], args.roof_iters)
-    achieved = r["work"] / (kms / 1e3) / 1e12
+    # work: algorithmic flop (unit TFLOP/s) or bytes (unit GB/s) per launch
+    achieved = r["work"] / (kms / 1e3) / (1e12 if r["unit"] == "TFLOP/s" else 1e9)
     traffic = traffic_from_profile(r["key"], r["src"])
     roofline = {"bound": r["bound"], "kernel": r["kernel"], "achieved": round(achieved, 3),
                 "peak": r["peak"], "unit": r["unit"], "frac": round(achieved / r["peak"], 4),
@@ -226,6 +307,8 @@ def main():
            "wall_s": round(wall, 3), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded)",
            "config": w["config"], "roofline": roofline, "cpu_baseline": cpu}
+    if "extra" in w:
+        out.update(w["extra"](value))
     print(json.dumps(out), flush=True)
 
 

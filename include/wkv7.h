@@ -182,6 +182,52 @@ int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 
+/* ------------------------------------------------------ decode stack -- */
+
+/* RWKV-7 stack geometry: n_layer blocks of width C = H*N (N = 64), channel-mix
+ * width F, vocabulary V, time-mix LoRA ranks, and whether layer 0 applies the
+ * pre-norm ln0 to the embedding. */
+typedef struct {
+  int n_layer, C, H, N, F, V, Dw, Da, Dv, Dg, use_ln0;
+} rwkv7_config;
+
+/* One block: LayerNorms, time-mix weights (layer_id = block index) and the
+ * channel-mix (token-shift lerp mu_k [C], Wk [C][F], Wv [F][C]). */
+typedef struct {
+  const float *ln1_w, *ln1_b, *ln2_w, *ln2_b; /* [C] */
+  tm_weights tm;
+  const float *cm_mu_k, *cm_Wk, *cm_Wv;
+} rwkv7_block;
+
+/* Whole model.  blocks is a HOST array of n_layer rwkv7_block (the pointers
+ * inside are device pointers); ln0_w/b may be NULL when use_ln0 == 0. */
+typedef struct {
+  const float *emb;            /* [V][C] */
+  const float *ln0_w, *ln0_b;  /* [C] */
+  const float *ln_out_w, *ln_out_b;
+  const float *head;           /* [C][V] (not tied to emb) */
+  const rwkv7_block *blocks;
+} rwkv7_model;
+
+size_t rwkv7_decode_workspace_bytes(const rwkv7_config *cfg, int B);
+
+/*
+ * One streaming-decode token for B independent streams through the stack.
+ * Pages: block and model forward of "Foundry/cuda_kernels/fullmodel.cu"
+ * (fm_rwkv_fwd: h1 = LN1(x), x1 = x + TM(h1), h2 = LN2(x1), out = x1 +
+ * CM(h2); fm_cm_fwd; fm_forward: x0 = emb[token], ln_out, logits = h head)
+ * and the streaming state of "infotheory .../rwkv7/model.rs" (LayerState:
+ * att_x_prev, att_state, ffn_x_prev; layer-0 pre-norm; LayerNorm eps 1e-5).
+ * tokens: [B] int32 in [0, V) (ids outside are clamped); state tensors are
+ * read and updated in place: att_x_prev, ffn_x_prev [n_layer][B][C] (the
+ * previous token's LN1 / LN2 outputs), att_state [n_layer][B][H][N][N] fp32.
+ * logits: [B][V] fp32 (written).
+ */
+int rwkv7_decode_step(const rwkv7_config *cfg, const rwkv7_model *model, int B,
+                      const int *tokens, float *att_x_prev, float *att_state,
+                      float *ffn_x_prev, float *logits, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------- helpers -- */
 
 /*

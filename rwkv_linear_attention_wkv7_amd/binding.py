@@ -32,6 +32,22 @@ class TmGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
+class Rwkv7Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("n_layer", "C", "H", "N", "F", "V", "Dw", "Da", "Dv",
+                                            "Dg", "use_ln0")]
+
+
+class Rwkv7Block(ctypes.Structure):
+    _fields_ = ([(n, ctypes.c_void_p) for n in ("ln1_w", "ln1_b", "ln2_w", "ln2_b")] +
+                [("tm", TmWeights)] +
+                [(n, ctypes.c_void_p) for n in ("cm_mu_k", "cm_Wk", "cm_Wv")])
+
+
+class Rwkv7Model(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("emb", "ln0_w", "ln0_b", "ln_out_w", "ln_out_b",
+                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7Block))]
+
+
 class Wkv7Error(RuntimeError):
     pass
 
@@ -71,6 +87,11 @@ def lib():
         L.timemix_backward.restype = _i
         L.wkv7_gemm_f32.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp]
         L.wkv7_gemm_f32.restype = _i
+        cp = ctypes.POINTER(Rwkv7Config)
+        L.rwkv7_decode_workspace_bytes.argtypes = [cp, _i]
+        L.rwkv7_decode_workspace_bytes.restype = _sz
+        L.rwkv7_decode_step.argtypes = [cp, ctypes.POINTER(Rwkv7Model), _i] + [_vp] * 6 + [_sz, _vp]
+        L.rwkv7_decode_step.restype = _i
         _lib = L
     return _lib
 
@@ -284,3 +305,66 @@ def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
     _check(lib().wkv7_gemm_f32(int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B),
                                B.shape[1], _p(C), N, beta, _stream()))
     return C
+
+
+# ---------------------------------------------------------- decode stack --
+class DecodeModel:
+    """Device-resident weights of an RWKV-7 stack plus the C structs that
+    point at them (the structs hold raw pointers, so the tensors are kept)."""
+
+    def __init__(self, cfg, weights):
+        """cfg: dict n_layer, C, H, F, V, ranks=(Dw, Da, Dv, Dg), use_ln0.
+        weights: dict of device tensors as laid out by synth.stack_model."""
+        L, C, H, F, V = cfg["n_layer"], cfg["C"], cfg["H"], cfg["F"], cfg["V"]
+        Dw, Da, Dv, Dg = cfg["ranks"]
+        self.cfg = Rwkv7Config(L, C, H, 64, F, V, Dw, Da, Dv, Dg, int(cfg.get("use_ln0", 1)))
+        self.w = weights
+        blocks = (Rwkv7Block * L)()
+        for l, bw in enumerate(weights["blocks"]):
+            b = blocks[l]
+            for n in ("ln1_w", "ln1_b", "ln2_w", "ln2_b"):
+                setattr(b, n, _need(bw[n], (C,), torch.float32, n).data_ptr())
+            b.tm = _pack_weights(tm_shape(C, H, Dw, Da, Dv, Dg, l), bw["tm"])
+            b.cm_mu_k = _need(bw["cm_mu_k"], (C,), torch.float32, "cm_mu_k").data_ptr()
+            b.cm_Wk = _need(bw["cm_Wk"], (C, F), torch.float32, "cm_Wk").data_ptr()
+            b.cm_Wv = _need(bw["cm_Wv"], (F, C), torch.float32, "cm_Wv").data_ptr()
+        self._blocks = blocks
+        m = Rwkv7Model()
+        m.emb = _need(weights["emb"], (V, C), torch.float32, "emb").data_ptr()
+        m.head = _need(weights["head"], (C, V), torch.float32, "head").data_ptr()
+        for n in ("ln_out_w", "ln_out_b", "ln0_w", "ln0_b"):
+            t = weights.get(n)
+            setattr(m, n, None if t is None else _need(t, (C,), torch.float32, n).data_ptr())
+        m.blocks = ctypes.cast(blocks, ctypes.POINTER(Rwkv7Block))
+        self.model = m
+
+    def new_state(self, B, device="cuda"):
+        c = self.cfg
+        z = lambda *s: torch.zeros(s, device=device, dtype=torch.float32)
+        return dict(att_x_prev=z(c.n_layer, B, c.C), att_state=z(c.n_layer, B, c.H, 64, 64),
+                    ffn_x_prev=z(c.n_layer, B, c.C))
+
+
+def rwkv7_decode_workspace_bytes(dm, B):
+    return lib().rwkv7_decode_workspace_bytes(ctypes.byref(dm.cfg), B)
+
+
+def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None):
+    """One token per stream: tokens [B] int32 (device); state dict updated in place."""
+    c = dm.cfg
+    B = tokens.shape[0]
+    _need(tokens, (B,), torch.int32, "tokens")
+    _need(state["att_x_prev"], (c.n_layer, B, c.C), torch.float32, "att_x_prev")
+    _need(state["att_state"], (c.n_layer, B, c.H, 64, 64), torch.float32, "att_state")
+    _need(state["ffn_x_prev"], (c.n_layer, B, c.C), torch.float32, "ffn_x_prev")
+    if logits is None:
+        logits = torch.empty((B, c.V), device=tokens.device, dtype=torch.float32)
+    _need(logits, (B, c.V), torch.float32, "logits")
+    nbytes = rwkv7_decode_workspace_bytes(dm, B)
+    if ws is None:
+        ws = torch.empty(nbytes, device=tokens.device, dtype=torch.uint8)
+    _check(lib().rwkv7_decode_step(ctypes.byref(c), ctypes.byref(dm.model), B, _p(tokens),
+                                   _p(state["att_x_prev"]), _p(state["att_state"]),
+                                   _p(state["ffn_x_prev"]), _p(logits), _p(ws), ws.numel(),
+                                   _stream()))
+    return logits

@@ -10,6 +10,7 @@
 
 #include "../../include/wkv7.h"
 #include "common.hpp"
+#include "stack_kernels.hpp"
 #include "timemix_kernels.hpp"
 
 namespace {
@@ -175,7 +176,7 @@ struct TmCache {
   float *mean, *rstd, *alpha, *ckpt;
 };
 
-void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m) {
+void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m, bool with_ckpt = true) {
   const size_t BT = (size_t)B * T, tok = BT * s->C;
   float** toks[] = {&m.xr, &m.xw, &m.xk, &m.xv, &m.xa, &m.xg, &m.r, &m.k, &m.v, &m.ow, &m.oa,
                     &m.g, &m.w, &m.a, &m.kk, &m.kmod, &m.vmod, &m.A, &m.Bv, &m.y, &m.tg};
@@ -192,7 +193,7 @@ void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m) {
   m.mean = c.take(BT * s->H);
   m.rstd = c.take(BT * s->H);
   m.alpha = c.take(BT * s->H);
-  m.ckpt = c.take(ckpt_floats(B, T, s->H));
+  m.ckpt = with_ckpt ? c.take(ckpt_floats(B, T, s->H)) : nullptr;
 }
 
 struct TmBwdBufs {
@@ -276,9 +277,12 @@ int check_weights(const tm_shape* s, const tm_weights* W) {
   return WKV7_OK;
 }
 
+// decode: T == 1 with the WKV state updated in place (s0 == sT, no checkpoint),
+// run by the bandwidth-bound step kernel.  out = out_beta * out + tg Wo.
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
-                    float* x_last, const TmCache& m, hipStream_t st) {
+                    float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
+                    float out_beta = 0.f) {
   const int BT = B * T, C = s->C;
   TmFwd p;
   memset(&p, 0, sizeof(p));
@@ -308,10 +312,14 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     HIPCHK(gemm_f32_run(false, false, BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, 0.f, 0, nullptr, 1, nullptr, st), "v lora 2");
   }
   HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
-  HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
-                             m.ckpt, st), "wkv7 forward");
+  if (decode)
+    HIPCHK(wkv7_launch_step(WKV7_F32, B, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, sT, m.y, st),
+           "wkv7 step");
+  else
+    HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
+                               m.ckpt, st), "wkv7 forward");
   HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
-  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, 0.f, 0, nullptr, 1, nullptr, st), "o proj");
+  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;
 }
 
@@ -511,5 +519,100 @@ extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const 
   HIPCHK(gemm_f32_run(transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr, 1,
                       nullptr, stream),
          "gemm launch");
+  return WKV7_OK;
+}
+
+// --------------------------------------------------------- decode stack --
+namespace {
+
+struct DecodeBufs {
+  float *x, *h, *vf, *sh, *ka;
+  TmCache tm;
+};
+
+int check_cfg(const rwkv7_config* c, int B) {
+  if (!c) return fail(WKV7_EINVAL, "config is NULL");
+  if (c->N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", c->N);
+  if (c->H < 1 || c->C != c->H * c->N) return fail(WKV7_EINVAL, "C=%d must equal H*N", c->C);
+  if (c->C > stk_max_layernorm_width()) return fail(WKV7_EINVAL, "C=%d above the supported %d", c->C, stk_max_layernorm_width());
+  if (c->n_layer < 1 || B < 1) return fail(WKV7_EINVAL, "n_layer and B must be >= 1");
+  if (c->F < 4 || c->F % 4 || c->V < 4 || c->V % 4) return fail(WKV7_EINVAL, "F and V must be positive multiples of 4");
+  tm_shape s = {c->C, c->H, c->N, c->Dw, c->Da, c->Dv, c->Dg, c->n_layer > 1 ? 1 : 0};
+  return check_tm_shape(&s, B, 1);
+}
+
+void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
+  const size_t BC = (size_t)B * cfg->C;
+  d.x = c.take(BC);
+  d.h = c.take(BC);
+  d.vf = c.take(BC);
+  d.sh = c.take(BC);
+  d.ka = c.take((size_t)B * cfg->F);
+  tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, 1};
+  carve_cache(c, &s, B, 1, d.tm, false);
+}
+
+}  // namespace
+
+extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
+  if (check_cfg(cfg, B) != WKV7_OK) return 0;
+  Carver c(nullptr);
+  DecodeBufs d;
+  carve_decode(c, cfg, B, d);
+  return c.off + 256;
+}
+
+extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, int B,
+                                 const int* tokens, float* att_x_prev, float* att_state,
+                                 float* ffn_x_prev, float* logits, void* ws, size_t ws_bytes,
+                                 hipStream_t st) {
+  g_err[0] = 0;
+  CHK(check_cfg(cfg, B));
+  if (!M || !M->blocks) return fail(WKV7_EINVAL, "model or model->blocks is NULL");
+  CHK(check_f32_ptr(M->emb, "emb", true));
+  CHK(check_f32_ptr(M->head, "head", true));
+  CHK(check_f32_ptr(M->ln_out_w, "ln_out_w", true));
+  CHK(check_f32_ptr(M->ln_out_b, "ln_out_b", true));
+  CHK(check_f32_ptr(M->ln0_w, "ln0_w", cfg->use_ln0 != 0));
+  CHK(check_f32_ptr(M->ln0_b, "ln0_b", cfg->use_ln0 != 0));
+  CHK(check_tok_ptr(tokens, "tokens", WKV7_F32, true));
+  CHK(check_f32_ptr(att_x_prev, "att_x_prev", true));
+  CHK(check_f32_ptr(att_state, "att_state", true));
+  CHK(check_f32_ptr(ffn_x_prev, "ffn_x_prev", true));
+  CHK(check_f32_ptr(logits, "logits", true));
+  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer, H = cfg->H;
+  for (int l = 0; l < L; l++) {
+    const rwkv7_block& bl = M->blocks[l];
+    tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
+    CHK(check_weights(&s, &bl.tm));
+    const float* req[] = {bl.ln1_w, bl.ln1_b, bl.ln2_w, bl.ln2_b, bl.cm_mu_k, bl.cm_Wk, bl.cm_Wv};
+    for (const float* p : req) CHK(check_f32_ptr(p, "a block weight", true));
+  }
+  const size_t need = rwkv7_decode_workspace_bytes(cfg, B);
+  if (!ws || ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  CHK(check_f32_ptr(ws, "ws", true));
+  Carver cw(ws);
+  DecodeBufs d;
+  carve_decode(cw, cfg, B, d);
+
+  const size_t BC = (size_t)B * C, NN = (size_t)WKV7_N * WKV7_N;
+  HIPCHK(stk_launch_emb_gather(B, C, V, tokens, M->emb, d.x, st), "embedding");
+  if (cfg->use_ln0) HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln0_w, M->ln0_b, d.x, nullptr, nullptr, st), "ln0");
+  for (int l = 0; l < L; l++) {
+    const rwkv7_block& bl = M->blocks[l];
+    tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
+    float* axp = att_x_prev + (size_t)l * BC;
+    float* ast = att_state + (size_t)l * B * H * NN;
+    float* fxp = ffn_x_prev + (size_t)l * BC;
+    HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln1_w, bl.ln1_b, d.h, nullptr, nullptr, st), "ln1");
+    CHK(tm_forward_impl(&s, &bl.tm, B, 1, d.h, axp, d.vf, ast, ast, d.x, axp, d.tm, st, true, 1.f));
+    HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln2_w, bl.ln2_b, d.h, nullptr, nullptr, st), "ln2");
+    HIPCHK(stk_launch_cm_shift(B, 1, C, d.h, fxp, bl.cm_mu_k, d.sh, fxp, st), "cm shift");
+    HIPCHK(gemm_f32_run(false, false, B, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_f32_run(false, false, B, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
+  }
+  HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
+  HIPCHK(gemm_f32_run(false, false, B, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
   return WKV7_OK;
 }

@@ -22,7 +22,7 @@ namespace gemmk {
 constexpr int BK = 32;
 constexpr int PAD = 16;
 
-enum Epi { EPI_NONE = 0, EPI_TANH = 1, EPI_SIGMOID = 2, EPI_TANH_BWD = 3, EPI_SIG_BWD = 4 };
+enum Epi { EPI_NONE = 0, EPI_TANH = 1, EPI_SIGMOID = 2, EPI_TANH_BWD = 3, EPI_SIG_BWD = 4, EPI_SQRELU = 5 };
 
 __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
   switch (epi) {
@@ -30,6 +30,7 @@ __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
     case EPI_SIGMOID: return 1.0f / (1.0f + expf(-acc));
     case EPI_TANH_BWD: return acc * (1.0f - aux * aux);  // aux = tanh(.) of the forward
     case EPI_SIG_BWD: return acc * aux * (1.0f - aux);   // aux = sigmoid(.) of the forward
+    case EPI_SQRELU: return acc > 0.f ? acc * acc : 0.f;  // relu(.)^2
     default: return acc;
   }
 }
@@ -205,12 +206,18 @@ template <bool TA, bool TB>
 hipError_t launch_layout(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
                          float* C, int ldc, int S, int kslice, float beta, int epi,
                          const float* aux, hipStream_t st) {
-  // tile choice: wide tiles for wide outputs, narrower ones for the LoRA ranks
-  if (N >= 128 && M >= 128)
+  // Largest tile whose grid still gives every CU work (>= 256 workgroups),
+  // else the smallest tile.
+  auto blocks = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * S; };
+  if (blocks(128, 128) >= 256 && N >= 128)
     return launch_t<4, 4, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  if (N >= 64)
+  if (blocks(128, 64) >= 256 && N >= 64)
     return launch_t<4, 2, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  return launch_t<4, 1, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
+  if (blocks(64, 64) >= 256 && N >= 64)
+    return launch_t<2, 2, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
+  if (blocks(64, 32) >= 256)
+    return launch_t<2, 1, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
+  return launch_t<1, 1, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
 }
 
 }  // namespace gemmk

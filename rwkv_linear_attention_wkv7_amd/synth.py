@@ -128,3 +128,45 @@ def timemix_inputs(B, T, C, seed=0, with_state=False, H=None):
         out["s0"] = rng(seed, "s0").standard_normal((B, H, N, N))
         out["dsT"] = rng(seed, "dsT").standard_normal((B, H, N, N))
     return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
+
+
+def stack_model(C, H, F, V, n_layer, ranks, seed=0, use_ln0=True, perturbed=False, std=0.02):
+    """Random-init RWKV-7 stack (fp32): embedding, blocks, ln_out, head.
+
+    ranks = (Dw, Da, Dv, Dg).  LayerNorm weights 1 / biases 0 (perturbed:
+    1 + N(0, 0.1^2) / N(0, 0.1^2)); channel-mix mu_k = 0.5 + U(-0.02, 0.02).
+    """
+    def mat(name, shape):
+        return (std * rng(seed, name).standard_normal(shape)).astype(np.float32)
+
+    def ln(name):
+        w, b = np.ones(C), np.zeros(C)
+        if perturbed:
+            w = w + 0.1 * rng(seed, name + "_w").standard_normal(C)
+            b = b + 0.1 * rng(seed, name + "_b").standard_normal(C)
+        return w.astype(np.float32), b.astype(np.float32)
+
+    m = {"emb": mat("emb", (V, C)), "head": mat("head", (C, V))}
+    m["ln_out_w"], m["ln_out_b"] = ln("ln_out")
+    if use_ln0:
+        m["ln0_w"], m["ln0_b"] = ln("ln0")
+    else:
+        m["ln0_w"] = m["ln0_b"] = None
+    blocks = []
+    for l in range(n_layer):
+        bp = {}
+        bp["ln1_w"], bp["ln1_b"] = ln(f"ln1_{l}")
+        bp["ln2_w"], bp["ln2_b"] = ln(f"ln2_{l}")
+        bp["tm"] = timemix_params(C, H, *ranks, layer_id=l, seed=seed * 1000 + l + 1,
+                                  perturbed=perturbed, std=std)
+        bp["cm_mu_k"] = (0.5 + rng(seed, f"cm_mu_{l}").uniform(-0.02, 0.02, size=C)).astype(np.float32)
+        bp["cm_Wk"] = mat(f"cm_Wk_{l}", (C, F))
+        bp["cm_Wv"] = mat(f"cm_Wv_{l}", (F, C))
+        blocks.append(bp)
+    m["blocks"] = blocks
+    return m
+
+
+def token_ids(B, T, V, seed=0, name="tokens"):
+    """Uniform int32 token ids [B][T] in [0, V)."""
+    return rng(seed, name).integers(0, V, size=(B, T)).astype(np.int32)

@@ -1,0 +1,59 @@
+"""Pins for the stack oracle (CPU only): LayerNorm's textbook properties, the
+channel-mix token shift, and step-by-step decode equal to the sequence
+forward (the streaming state carries exactly what the sequence shifts)."""
+import numpy as np
+
+from oracle import stack
+from rwkv_linear_attention_wkv7_amd import synth
+
+
+def _model(perturbed=True, L=3, C=128, H=2, F=256, V=64):
+    cfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+    m = synth.stack_model(C, H, F, V, L, (16, 16, 16, 32), seed=4, perturbed=perturbed, std=0.2)
+    return m, cfg
+
+
+def test_layernorm_textbook():
+    x = np.random.default_rng(0).standard_normal((5, 7, 96)) * 3 + 1
+    y = stack.layernorm(x, np.ones(96), np.zeros(96))
+    var = x.var(axis=-1)
+    np.testing.assert_allclose(y.mean(axis=-1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=-1), var / (var + stack.LN_EPS), rtol=1e-12)
+    w, b = np.arange(96) * 0.1, np.ones(96)
+    np.testing.assert_allclose(stack.layernorm(x, w, b), y * w + b, rtol=1e-12)
+
+
+def test_channel_mix_shift_and_square_relu():
+    g = np.random.default_rng(1)
+    C, F = 16, 24
+    mu, Wk, Wv = g.uniform(0, 1, C), g.standard_normal((C, F)), g.standard_normal((F, C))
+    x = g.standard_normal((2, 3, C))
+    out = stack.channel_mix(mu, Wk, Wv, x, x_prev=None)
+    # position 1 alone, with x_prev = x[:, 0], equals position 1 of the sequence
+    o1 = stack.channel_mix(mu, Wk, Wv, x[:, 1:2], x_prev=x[:, 0])
+    np.testing.assert_allclose(o1[:, 0], out[:, 1], rtol=1e-13)
+    # first position with no previous token: sh = x (1 - mu)
+    sh = x[:, 0] * (1 - mu)
+    np.testing.assert_allclose(out[:, 0], np.maximum(sh @ Wk, 0) ** 2 @ Wv, rtol=1e-13)
+
+
+def test_decode_steps_equal_sequence_forward():
+    m, cfg = _model()
+    B, T = 3, 6
+    tok = synth.token_ids(B, T, cfg["V"], seed=2)
+    logits_seq, st_seq = stack.forward(m, cfg, tok)
+    st = stack.init_state(cfg, B)
+    for t in range(T):
+        lg, st = stack.decode_step(m, cfg, tok[:, t], st)
+        np.testing.assert_allclose(lg, logits_seq[:, t], rtol=1e-10, atol=1e-12)
+    for k in st:
+        np.testing.assert_allclose(st[k], st_seq[k], rtol=1e-10, atol=1e-12)
+
+
+def test_stream_independence():
+    """Streams do not interact: a stream's logits do not depend on the others."""
+    m, cfg = _model(L=2)
+    tok = synth.token_ids(4, 3, cfg["V"], seed=3)
+    full, _ = stack.forward(m, cfg, tok)
+    one, _ = stack.forward(m, cfg, tok[2:3])
+    np.testing.assert_allclose(one[0], full[2], rtol=1e-12, atol=1e-14)
