@@ -227,7 +227,7 @@ def setup_decode():
     def cpu():
         from oracle import stack
         from oracle import wkv7 as ow
-        ns, steps = 16, 8
+        ns, steps = 32, 64
         idx = np.arange(ns) * (B // ns)
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
         state = stack.init_state(ocfg, ns)
@@ -259,7 +259,21 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roof-iters", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (the known-size "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = 64 * 1024 * 1024
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "repeats": 3}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
