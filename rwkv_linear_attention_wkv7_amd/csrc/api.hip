@@ -298,18 +298,35 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
   p.tg = m.tg; p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha;
 
   HIPCHK(tm_launch_shift_fwd(p, st), "token shift");
-  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xr, C, W->Wr, C, m.r, C, 0.f, 0, nullptr, 1, nullptr, st), "r proj");
-  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xk, C, W->Wk, C, m.k, C, 0.f, 0, nullptr, 1, nullptr, st), "k proj");
-  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.xv, C, W->Wv, C, m.v, C, 0.f, 0, nullptr, 1, nullptr, st), "v proj");
-  HIPCHK(gemm_f32_run(false, false, BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, 0.f, 1, nullptr, 1, nullptr, st), "w lora 1");
-  HIPCHK(gemm_f32_run(false, false, BT, C, s->Dw, m.tw, s->Dw, W->W2, C, m.ow, C, 0.f, 0, nullptr, 1, nullptr, st), "w lora 2");
-  HIPCHK(gemm_f32_run(false, false, BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, 0.f, 0, nullptr, 1, nullptr, st), "a lora 1");
-  HIPCHK(gemm_f32_run(false, false, BT, C, s->Da, m.la, s->Da, W->A2, C, m.oa, C, 0.f, 0, nullptr, 1, nullptr, st), "a lora 2");
-  HIPCHK(gemm_f32_run(false, false, BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, 0.f, 2, nullptr, 1, nullptr, st), "g lora 1");
-  HIPCHK(gemm_f32_run(false, false, BT, C, s->Dg, m.sg, s->Dg, W->G2, C, m.g, C, 0.f, 0, nullptr, 1, nullptr, st), "g lora 2");
-  if (s->layer_id > 0) {
-    HIPCHK(gemm_f32_run(false, false, BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, 0.f, 0, nullptr, 1, nullptr, st), "v lora 1");
-    HIPCHK(gemm_f32_run(false, false, BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, 0.f, 0, nullptr, 1, nullptr, st), "v lora 2");
+  auto prob = [](int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
+                 int ldc, int epi) {
+    return GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, 0.f, epi, nullptr, nullptr};
+  };
+  {  // r, k, v projections: one launch
+    GemmBatch g;
+    g.count = 3;
+    g.p[0] = prob(BT, C, C, m.xr, C, W->Wr, C, m.r, C, EPI_NONE);
+    g.p[1] = prob(BT, C, C, m.xk, C, W->Wk, C, m.k, C, EPI_NONE);
+    g.p[2] = prob(BT, C, C, m.xv, C, W->Wv, C, m.v, C, EPI_NONE);
+    HIPCHK(gemm_f32_batch(false, false, g, st), "r/k/v proj");
+  }
+  {  // LoRA down-projections (tanh for w, sigmoid for g): one launch
+    GemmBatch g;
+    g.count = 3;
+    g.p[0] = prob(BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, EPI_TANH);
+    g.p[1] = prob(BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, EPI_NONE);
+    g.p[2] = prob(BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, EPI_SIGMOID);
+    if (s->layer_id > 0) g.p[g.count++] = prob(BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, EPI_NONE);
+    HIPCHK(gemm_f32_batch(false, false, g, st), "lora down");
+  }
+  {  // LoRA up-projections: one launch
+    GemmBatch g;
+    g.count = 3;
+    g.p[0] = prob(BT, C, s->Dw, m.tw, s->Dw, W->W2, C, m.ow, C, EPI_NONE);
+    g.p[1] = prob(BT, C, s->Da, m.la, s->Da, W->A2, C, m.oa, C, EPI_NONE);
+    g.p[2] = prob(BT, C, s->Dg, m.sg, s->Dg, W->G2, C, m.g, C, EPI_NONE);
+    if (s->layer_id > 0) g.p[g.count++] = prob(BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, EPI_NONE);
+    HIPCHK(gemm_f32_batch(false, false, g, st), "lora up");
   }
   HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
   if (decode)

@@ -1,28 +1,36 @@
 // fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_16x16x4_f32).
 //
-//   C[M][N] = epilogue( op(A)[M][K] . op(B)[K][N] )
+//   C[M][N] = epilogue( op(A)[M][K] . op(B)[K][N] + beta C )
 //
 // Row-major storage.  op(A) = A ([M][K], lda) or A^T (A stored [K][M]);
 // op(B) = B ([K][N], ldb) or B^T (B stored [N][K]).  These three layouts are
 // all the time-mix block needs: X W (forward), dY W^T (input gradients) and
 // X^T dY (weight gradients, reduction over the B*T tokens, split along K).
+// This is the contraction the timemix page runs through cuBLAS SGEMM over the
+// whole [B*T, *] token batch (rm_gemm).
 //
 // Tiling: 256 threads = 2x2 waves; each wave owns TI x TJ tiles of 16x16, so
-// the workgroup tile is (32 TI) x (32 TJ).  K advances in steps of BK = 32
-// through LDS (k-major, rows padded by 16 floats so the four k-rows a wave
-// reads land in disjoint bank groups); the next K tile is fetched into
-// registers while the current one is multiplied.  Any M is allowed (rows are
-// guarded); the dimensions read as float4 (K for A, N for B, or M/N for the
-// transposed operands) must be multiples of 4.
+// the workgroup tile is (32 TI) x (32 TJ).  K advances in steps of BK through
+// LDS; the next K tile is fetched into registers while the current one is
+// multiplied.  Each operand keeps its global orientation in LDS (so every LDS
+// store is a 16-byte row segment) with rows padded by 4 floats.  Inside each
+// group of 16 k the MFMA steps take k in the order 4g + s (g = lane/16 the
+// MFMA k-lane, s = step): the sum is unchanged, and a lane then finds its k
+// values of the four steps next to each other, so a row-major operand yields
+// its fragments for four MFMAs in one 16-byte LDS read.  Deep K tiles (BK up
+// to 128) keep small-tile launches from paying one global round trip per 32 k.  A launch may carry
+// up to four independent problems of the same layout (blockIdx.z selects the
+// problem; workgroups outside a smaller problem's grid exit), or one problem
+// split along K (blockIdx.z selects the slice, partials summed by
+// splitk_reduce).  Any M is allowed; the dimensions read as float4 must be
+// multiples of 4.
 
 #include "common.hpp"
+#include "gemm.hpp"
 
 namespace gemmk {
 
-constexpr int BK = 32;
-constexpr int PAD = 16;
-
-enum Epi { EPI_NONE = 0, EPI_TANH = 1, EPI_SIGMOID = 2, EPI_TANH_BWD = 3, EPI_SIG_BWD = 4, EPI_SQRELU = 5 };
+constexpr int PAD = 4;  // floats of padding per LDS row
 
 __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
   switch (epi) {
@@ -35,24 +43,34 @@ __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
   }
 }
 
-template <int TI, int TJ, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float* __restrict__ A,
-                                                int lda, const float* __restrict__ B, int ldb,
-                                                float* __restrict__ C, int ldc, int kslice,
-                                                float beta, int epi, const float* __restrict__ aux) {
+template <int TI, int TJ, int BK, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
   constexpr int BM = 32 * TI, BN = 32 * TJ;
   constexpr int A4 = BM * BK / 4 / 256;  // float4 loads per thread for the A tile
   constexpr int B4 = BN * BK / 4 / 256;
   static_assert(A4 >= 1 && B4 >= 1, "tile too small for 256 threads");
-  __shared__ float As[BK][BM + PAD];
-  __shared__ float Bs[BK][BN + PAD];
+  static_assert(A4 <= 32 && B4 <= 32, "load masks are 32 bits");
+  static_assert(BK % 16 == 0, "K tiles are whole groups of 16");
+  // A: [m][k] when A is row-major [M][K], [k][m] when stored [K][M]
+  // B: [k][n] when row-major [K][N],      [n][k] when stored [N][K]
+  __shared__ __attribute__((aligned(16))) float As[TA ? BK : BM][(TA ? BM : BK) + PAD];
+  __shared__ __attribute__((aligned(16))) float Bs[TB ? BN : BK][(TB ? BK : BN) + PAD];
+
+  const bool split = batch.count == 1 && gridDim.z > 1;
+  const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
+  const int M = P.M, N = P.N, K = P.K, lda = P.lda, ldb = P.ldb;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
+  const float* __restrict__ A = P.A;
+  const float* __restrict__ B = P.B;
+  float* __restrict__ C = P.C;
+  const int ldc = split ? N : P.ldc;
+  const int kbeg = split ? blockIdx.z * kslice : 0;
+  const int kend = split ? min(K, kbeg + kslice) : K;
+  if (split) C = P.part + (size_t)blockIdx.z * M * N;  // split-K partials, leading dim N
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int kbeg = blockIdx.z * kslice;
-  const int kend = min(K, kbeg + kslice);
-  C += (size_t)blockIdx.z * M * ldc;  // split-K partials (z = 0 when not split)
 
   // Tile loads are unconditional from clamped (always valid) addresses, so a
   // whole tile is in flight at once; out-of-range elements are zeroed when the
@@ -101,8 +119,7 @@ __global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float
       const f4 x = (oka >> q) & 1u ? ra[q] : z;
       if (!TA) {
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
-#pragma unroll
-        for (int c = 0; c < 4; c++) As[k4 * 4 + c][row] = x[c];
+        *reinterpret_cast<f4*>(&As[row][k4 * 4]) = x;
       } else {
         const int kr = idx / (BM / 4), m4 = idx % (BM / 4);
         *reinterpret_cast<f4*>(&As[kr][m4 * 4]) = x;
@@ -117,8 +134,7 @@ __global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float
         *reinterpret_cast<f4*>(&Bs[kr][n4 * 4]) = x;
       } else {
         const int row = idx / (BK / 4), k4 = idx % (BK / 4);
-#pragma unroll
-        for (int c = 0; c < 4; c++) Bs[k4 * 4 + c][row] = x[c];
+        *reinterpret_cast<f4*>(&Bs[row][k4 * 4]) = x;
       }
     }
   };
@@ -136,22 +152,39 @@ __global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float
     store_tiles();
     __syncthreads();
     if (k0 + BK < kend) load_tiles(k0 + BK);
+    const int klen = min(BK, kend - k0);  // zero-padded beyond klen; skip empty groups
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 4) {
-      float fa[TI], fb[TJ];
+    for (int kq = 0; kq < BK; kq += 16) {
+      if (kq < klen) {
+        const int kb = kq + fk * 4;  // this lane's four k of the group: kb + s, s = step
+        f4 fa[TI], fb[TJ];
 #pragma unroll
-      for (int i = 0; i < TI; i++) fa[i] = As[kk + fk][wm * 16 * TI + i * 16 + fr];
+        for (int i = 0; i < TI; i++) {
+          const int mr = wm * 16 * TI + i * 16 + fr;
+          if (!TA) fa[i] = *reinterpret_cast<const f4*>(&As[mr][kb]);
+          else fa[i] = f4{As[kb][mr], As[kb + 1][mr], As[kb + 2][mr], As[kb + 3][mr]};
+        }
 #pragma unroll
-      for (int j = 0; j < TJ; j++) fb[j] = Bs[kk + fk][wn * 16 * TJ + j * 16 + fr];
+        for (int j = 0; j < TJ; j++) {
+          const int nc = wn * 16 * TJ + j * 16 + fr;
+          if (TB) fb[j] = *reinterpret_cast<const f4*>(&Bs[nc][kb]);
+          else fb[j] = f4{Bs[kb][nc], Bs[kb + 1][nc], Bs[kb + 2][nc], Bs[kb + 3][nc]};
+        }
 #pragma unroll
-      for (int i = 0; i < TI; i++)
+        for (int s4 = 0; s4 < 4; s4++)
 #pragma unroll
-        for (int j = 0; j < TJ; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TI; i++)
+#pragma unroll
+            for (int j = 0; j < TJ; j++)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i][s4], fb[j][s4], acc[i][j], 0, 0, 0);
+      }
     }
   }
 
   // D layout of v_mfma_f32_16x16x4_f32: lane l, element v -> row 4*(l/16)+v, col l%16
+  const float beta = split ? 0.f : P.beta;
+  const int epi = split ? EPI_NONE : P.epi;
+  const float* __restrict__ aux = split ? nullptr : P.aux;
 #pragma unroll
   for (int i = 0; i < TI; i++) {
 #pragma unroll
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_f32(int M, int N, int K, const float
         const size_t o = (size_t)row * ldc + col;
         float x = acc[i][j][v];
         if (beta != 0.f) x += beta * C[o];
-        x = apply_epi(x, epi, aux ? aux[o] : 0.f);
+        x = apply_epi(x, epi, aux ? aux[(size_t)row * P.ldc + col] : 0.f);
         C[o] = x;
       }
     }
@@ -192,35 +225,62 @@ __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const 
   }
 }
 
-template <int TI, int TJ, bool TA, bool TB>
-hipError_t launch_t(int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
-                    int ldc, int S, int kslice, float beta, int epi, const float* aux,
-                    hipStream_t st) {
-  dim3 grid((N + 32 * TJ - 1) / (32 * TJ), (M + 32 * TI - 1) / (32 * TI), S);
-  hipLaunchKernelGGL((gemm_f32<TI, TJ, TA, TB>), grid, dim3(256), 0, st, M, N, K, A, lda, B, ldb,
-                     C, ldc, kslice, beta, epi, aux);
+template <int TI, int TJ, int BK, bool TA, bool TB>
+hipError_t launch_t(const GemmBatch& b, int gz, int kslice, hipStream_t st) {
+  int maxM = 0, maxN = 0;
+  for (int i = 0; i < b.count; i++) {
+    maxM = max(maxM, b.p[i].M);
+    maxN = max(maxN, b.p[i].N);
+  }
+  dim3 grid((maxN + 32 * TJ - 1) / (32 * TJ), (maxM + 32 * TI - 1) / (32 * TI), gz);
+  hipLaunchKernelGGL((gemm_f32<TI, TJ, BK, TA, TB>), grid, dim3(256), 0, st, b, kslice);
   return hipGetLastError();
 }
 
+template <int TI, int TJ, bool TA, bool TB>
+hipError_t launch_bk(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
+  // K tile depth: shallow for big tiles (plenty of MFMA work per K step),
+  // deep for small tiles so few global round trips remain.
+  if (TI * TJ >= 8 || klen <= 32) return launch_t<TI, TJ, 32, TA, TB>(b, gz, kslice, st);
+  if (klen <= 64 || TI * TJ >= 4) return launch_t<TI, TJ, 64, TA, TB>(b, gz, kslice, st);
+  return launch_t<TI, TJ, 128, TA, TB>(b, gz, kslice, st);
+}
+
 template <bool TA, bool TB>
-hipError_t launch_layout(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
-                         float* C, int ldc, int S, int kslice, float beta, int epi,
-                         const float* aux, hipStream_t st) {
+hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid still gives every CU work (>= 256 workgroups),
   // else the smallest tile.
-  auto blocks = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn) * S; };
-  if (blocks(128, 128) >= 256 && N >= 128)
-    return launch_t<4, 4, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  if (blocks(128, 64) >= 256 && N >= 64)
-    return launch_t<4, 2, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  if (blocks(64, 64) >= 256 && N >= 64)
-    return launch_t<2, 2, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  if (blocks(64, 32) >= 256)
-    return launch_t<2, 1, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
-  return launch_t<1, 1, TA, TB>(M, N, K, A, lda, B, ldb, C, ldc, S, kslice, beta, epi, aux, st);
+  int maxM = 0, maxN = 0;
+  for (int i = 0; i < b.count; i++) {
+    maxM = max(maxM, b.p[i].M);
+    maxN = max(maxN, b.p[i].N);
+  }
+  auto blocks = [&](int bm, int bn) {
+    return (long)((maxM + bm - 1) / bm) * ((maxN + bn - 1) / bn) * gz;
+  };
+  if (blocks(128, 128) >= 256 && maxN >= 128) return launch_bk<4, 4, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(128, 64) >= 256 && maxN >= 64) return launch_bk<4, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(64, 64) >= 256 && maxN >= 64) return launch_bk<2, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(64, 32) >= 256) return launch_bk<2, 1, TA, TB>(b, gz, kslice, klen, st);
+  return launch_bk<1, 1, TA, TB>(b, gz, kslice, klen, st);
+}
+
+hipError_t dispatch(bool transA, bool transB, const GemmBatch& b, int gz, int kslice, int klen,
+                    hipStream_t st) {
+  if (!transA && !transB) return launch_layout<false, false>(b, gz, kslice, klen, st);
+  if (!transA && transB) return launch_layout<false, true>(b, gz, kslice, klen, st);
+  if (transA && !transB) return launch_layout<true, false>(b, gz, kslice, klen, st);
+  return launch_layout<true, true>(b, gz, kslice, klen, st);
 }
 
 }  // namespace gemmk
+
+hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
+  if (b.count < 1 || b.count > GEMM_MAX_BATCH) return hipErrorInvalidValue;
+  int maxK = 0;
+  for (int i = 0; i < b.count; i++) maxK = max(maxK, b.p[i].K);
+  return gemmk::dispatch(transA, transB, b, b.count, maxK, maxK, st);
+}
 
 // C = epi(op(A) op(B) + beta C).  ws (may be NULL when split == 1) holds
 // split*M*N floats of split-K partials.
@@ -229,21 +289,15 @@ hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const flo
                         const float* aux, int split, float* ws, hipStream_t st) {
   using namespace gemmk;
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (split <= 1 || ws == nullptr) {
-    const int ks = K;
-    if (!transA && !transB) return launch_layout<false, false>(M, N, K, A, lda, B, ldb, C, ldc, 1, ks, beta, epi, aux, st);
-    if (!transA && transB) return launch_layout<false, true>(M, N, K, A, lda, B, ldb, C, ldc, 1, ks, beta, epi, aux, st);
-    if (transA && !transB) return launch_layout<true, false>(M, N, K, A, lda, B, ldb, C, ldc, 1, ks, beta, epi, aux, st);
-    return launch_layout<true, true>(M, N, K, A, lda, B, ldb, C, ldc, 1, ks, beta, epi, aux, st);
-  }
+  GemmBatch b;
+  b.count = 1;
+  b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, nullptr};
+  if (split <= 1 || ws == nullptr) return dispatch(transA, transB, b, 1, K, K, st);
   int kslice = (K + split - 1) / split;
-  kslice = (kslice + BK - 1) / BK * BK;
+  kslice = (kslice + 31) / 32 * 32;
   const int S = (K + kslice - 1) / kslice;
-  hipError_t e;
-  if (!transA && !transB) e = launch_layout<false, false>(M, N, K, A, lda, B, ldb, ws, N, S, kslice, 0.f, EPI_NONE, nullptr, st);
-  else if (!transA && transB) e = launch_layout<false, true>(M, N, K, A, lda, B, ldb, ws, N, S, kslice, 0.f, EPI_NONE, nullptr, st);
-  else if (transA && !transB) e = launch_layout<true, false>(M, N, K, A, lda, B, ldb, ws, N, S, kslice, 0.f, EPI_NONE, nullptr, st);
-  else e = launch_layout<true, true>(M, N, K, A, lda, B, ldb, ws, N, S, kslice, 0.f, EPI_NONE, nullptr, st);
+  b.p[0].part = ws;
+  hipError_t e = dispatch(transA, transB, b, S, kslice, kslice, st);
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)M * N / 4;
   int blocks = (int)((n4 + 255) / 256);

@@ -1,0 +1,34 @@
+// fp32 matrix-core GEMM (gemm.hip): problem descriptors and launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+
+enum GemmEpi { EPI_NONE = 0, EPI_TANH = 1, EPI_SIGMOID = 2, EPI_TANH_BWD = 3, EPI_SIG_BWD = 4, EPI_SQRELU = 5 };
+
+constexpr int GEMM_MAX_BATCH = 4;
+
+// C = epi(op(A) op(B) + beta C); aux (same layout as C) feeds the *_BWD epilogues.
+struct GemmProblem {
+  int M, N, K;
+  const float* A;
+  int lda;
+  const float* B;
+  int ldb;
+  float* C;
+  int ldc;
+  float beta;
+  int epi;
+  const float* aux;
+  float* part;  // split-K partials (internal)
+};
+
+struct GemmBatch {
+  int count;
+  GemmProblem p[GEMM_MAX_BATCH];
+};
+
+// Up to GEMM_MAX_BATCH independent problems of one layout in one launch.
+hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st);
+// One problem, optionally split along K into `split` slices (ws: split*M*N floats).
+hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A, int lda,
+                        const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                        const float* aux, int split, float* ws, hipStream_t st);

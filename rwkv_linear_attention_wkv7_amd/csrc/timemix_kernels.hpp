@@ -2,6 +2,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "gemm.hpp"
+
 constexpr int TB = 128;  // tokens per workgroup in the backward partial-sum kernels
 
 struct TmFwd {
@@ -47,10 +49,6 @@ hipError_t tm_launch_shift_bwd(const TmBwd& p, hipStream_t st);
 hipError_t tm_launch_reduce(const float* part, int nvec, int nblk, int C, const VecOut& outs,
                             hipStream_t st);
 
-// gemm.hip
-hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A, int lda,
-                        const float* B, int ldb, float* C, int ldc, float beta, int epi,
-                        const float* aux, int split, float* ws, hipStream_t st);
 // wkv7_seq.hip
 hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, const void* w,
                                const void* k, const void* v, const void* a, const void* b,

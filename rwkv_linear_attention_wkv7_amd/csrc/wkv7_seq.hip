@@ -458,7 +458,10 @@ __global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int ns
   }
 }
 
-int bwd_nsplit(int B, int H) { return (size_t)B * H * 2 >= 256 ? 2 : 4; }
+// Two 32-row slices per head: 256-thread workgroups whose LDS (sv, svr, red:
+// 128 KiB fp32) leaves one workgroup per CU; smaller slices would double the
+// partial traffic without adding resident waves.
+int bwd_nsplit(int, int) { return 2; }
 
 }  // namespace wkv7k
 
@@ -486,14 +489,9 @@ hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w,
                              hipStream_t st) {
   const int ns = bwd_nsplit(B, H);
   const dim3 grid(B * H * ns);
-  if (ns == 2)
-    hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
-                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
-  else
-    hipLaunchKernelGGL((bwd_seq<2, 8, T>), grid, dim3(128), 0, st, B, T_, H, (const T*)r,
-                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+  hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
+                     (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                     (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t plane4 = (size_t)B * T_ * H * N / 4;
