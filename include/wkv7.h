@@ -228,6 +228,43 @@ int rwkv7_decode_step(const rwkv7_config *cfg, const rwkv7_model *model, int B,
                       float *ffn_x_prev, float *logits, void *ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* --------------------------------------------------- training step -- */
+
+/* Gradients of one block / of the model; same fields and shapes as
+ * rwkv7_block / rwkv7_model, every field written (=).  blocks is a HOST array. */
+typedef struct {
+  float *ln1_w, *ln1_b, *ln2_w, *ln2_b;
+  tm_grads tm;
+  float *cm_mu_k, *cm_Wk, *cm_Wv;
+} rwkv7_block_grads;
+
+typedef struct {
+  float *emb, *ln0_w, *ln0_b, *ln_out_w, *ln_out_b, *head;
+  rwkv7_block_grads *blocks;
+} rwkv7_model_grads;
+
+size_t rwkv7_train_workspace_bytes(const rwkv7_config *cfg, int B, int T);
+
+/*
+ * One training step of next-token cross-entropy over B sequences of T tokens
+ * (zero initial state): loss = mean over tokens of log-sum-exp(logits) -
+ * logit[target]; every parameter gradient written.  Pages: whole-model
+ * forward/backward of "Foundry/cuda_kernels/fullmodel.cu" (fm_forward,
+ * fm_backward: embedding gather / scatter-add, blocks recomputed from their
+ * cached inputs in reverse, fused log-softmax CE fm_k_ce_bwd with
+ * dlogits = (softmax - onehot) / n, head not tied; layer 0 receives the
+ * v_first gradient of the later layers).  Differs from the page: every sum
+ * over tokens (parameter and embedding gradients, the loss) is done in a
+ * fixed order, so the step is bitwise reproducible.  GEMMs run in fp32 on
+ * the matrix cores; WKV7 state and accumulation are fp32.
+ * tokens, targets: [B][T] int32 device (ids outside [0, V) are clamped);
+ * loss: one fp32 device value (written).
+ */
+int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
+                     rwkv7_model_grads *grads, int B, int T, const int *tokens,
+                     const int *targets, float *loss, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
 /* ------------------------------------------------------------- helpers -- */
 
 /*

@@ -100,3 +100,115 @@ def decode_step(model, cfg, tokens, state):
     """One streaming token per stream: tokens [B] -> logits [B][V], new state."""
     logits, st = forward(model, cfg, np.asarray(tokens)[:, None], state)
     return logits[:, 0], st
+
+
+# ------------------------------------------------------------ training step --
+# Whole-model forward+backward for next-token cross-entropy, following the
+# fullmodel page's fm_forward / fm_backward: per-token CE with the
+# log-sum-exp, loss = mean over the tokens, dlogits = (softmax - onehot) / n
+# (fm_k_ce_bwd), head and embedding gradients (fm_k_emb_bwd adds each token's
+# gradient into its embedding row), and blocks walked in reverse; layer 0
+# receives the v_first gradient accumulated over the later layers.
+
+def layernorm_backward(x, w, dy, eps=LN_EPS):
+    """Gradients of y = LN(x) * w + b: returns dx, dw, db (dw, db summed over rows)."""
+    x = np.asarray(x, np.float64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    nhat = (x - mean) * rstd
+    dn = dy * w
+    dx = rstd * (dn - dn.mean(axis=-1, keepdims=True) - nhat * (dn * nhat).mean(axis=-1, keepdims=True))
+    C = x.shape[-1]
+    return dx, (dy * nhat).reshape(-1, C).sum(0), dy.reshape(-1, C).sum(0)
+
+
+def channel_mix_backward(mu_k, Wk, Wv, x, dout, x_prev=None):
+    """Gradients of channel_mix: returns dx, dx_prev, dmu_k, dWk, dWv."""
+    x = np.asarray(x, np.float64)
+    B, T, C = x.shape
+    first = np.zeros((B, 1, C)) if x_prev is None else np.asarray(x_prev, np.float64)[:, None, :]
+    prev = np.concatenate([first, x[:, :-1]], axis=1)
+    sh = x + (prev - x) * mu_k
+    fk = sh @ Wk
+    ka = np.maximum(fk, 0.0) ** 2
+    dka = dout @ Wv.T
+    dWv = ka.reshape(-1, ka.shape[-1]).T @ dout.reshape(-1, C)
+    dfk = dka * 2.0 * np.maximum(fk, 0.0)
+    dsh = dfk @ Wk.T
+    dWk = sh.reshape(-1, C).T @ dfk.reshape(-1, dfk.shape[-1])
+    dmu = (dsh * (prev - x)).reshape(-1, C).sum(0)
+    dx = dsh * (1.0 - mu_k)
+    dprev = dsh * mu_k
+    dx[:, :-1] += dprev[:, 1:]
+    return dx, dprev[:, 0], dmu, dWk, dWv
+
+
+def cross_entropy(logits, targets):
+    """Mean token CE and dlogits = (softmax - onehot) / n_tokens."""
+    z = np.asarray(logits, np.float64)
+    m = z.max(axis=-1, keepdims=True)
+    lse = m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True))
+    n = targets.size
+    ti = np.asarray(targets)[..., None]
+    loss = float(np.sum(lse[..., 0] - np.take_along_axis(z, ti, axis=-1)[..., 0]) / n)
+    p = np.exp(z - lse)
+    np.put_along_axis(p, ti, np.take_along_axis(p, ti, axis=-1) - 1.0, axis=-1)
+    return loss, p / n
+
+
+def train_step(model, cfg, tokens, targets):
+    """Loss and gradients of every parameter for one batch (zero initial state).
+
+    Returns (loss, grads) with grads mirroring the model dict (blocks[l]['tm']
+    holds the time-mix gradients).
+    """
+    m = _f64(model)
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    H = cfg["H"]
+    x = m["emb"][tokens]
+    use_ln0 = m.get("ln0_w") is not None
+    x_emb = x
+    if use_ln0:
+        x = layernorm(x, m["ln0_w"], m["ln0_b"])
+    xs, caches = [x], []
+    v_first = None
+    for l, bp in enumerate(m["blocks"]):
+        h1 = layernorm(x, bp["ln1_w"], bp["ln1_b"])
+        out, c = tm.forward(bp["tm"], h1, H, l, v_first=v_first)
+        if l == 0:
+            v_first = c["v_first"]
+        x1 = x + out
+        h2 = layernorm(x1, bp["ln2_w"], bp["ln2_b"])
+        x = x1 + channel_mix(bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], h2)
+        caches.append(dict(h1=h1, c=c, x1=x1, h2=h2))
+        xs.append(x)
+    hN = layernorm(x, m["ln_out_w"], m["ln_out_b"])
+    loss, dlog = cross_entropy(hN @ m["head"], targets)
+
+    G = {"head": hN.reshape(-1, hN.shape[-1]).T @ dlog.reshape(-1, dlog.shape[-1])}
+    dx, G["ln_out_w"], G["ln_out_b"] = layernorm_backward(x, m["ln_out_w"], dlog @ m["head"].T)
+    G["blocks"] = [None] * len(m["blocks"])
+    dvf = np.zeros_like(x)
+    for l in range(len(m["blocks"]) - 1, -1, -1):
+        bp, cc = m["blocks"][l], caches[l]
+        gb = {}
+        dh2, _, gb["cm_mu_k"], gb["cm_Wk"], gb["cm_Wv"] = channel_mix_backward(
+            bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], cc["h2"], dx)
+        d1, gb["ln2_w"], gb["ln2_b"] = layernorm_backward(cc["x1"], bp["ln2_w"], dh2)
+        dx1 = dx + d1
+        gt, dh1, _, dvf_out, _ = tm.backward(bp["tm"], cc["c"], dx1,
+                                             dv_first_in=dvf if l == 0 else None)
+        if l > 0:
+            dvf = dvf + dvf_out
+        gb["tm"] = gt
+        d0, gb["ln1_w"], gb["ln1_b"] = layernorm_backward(xs[l], bp["ln1_w"], dh1)
+        dx = dx1 + d0
+        G["blocks"][l] = gb
+    if use_ln0:
+        dx, G["ln0_w"], G["ln0_b"] = layernorm_backward(x_emb, m["ln0_w"], dx)
+    demb = np.zeros_like(m["emb"])
+    np.add.at(demb, tokens.reshape(-1), dx.reshape(-1, dx.shape[-1]))
+    G["emb"] = demb
+    return loss, G

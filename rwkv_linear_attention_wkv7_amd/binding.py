@@ -48,6 +48,17 @@ class Rwkv7Model(ctypes.Structure):
                                                "head")] + [("blocks", ctypes.POINTER(Rwkv7Block))]
 
 
+class Rwkv7BlockGrads(ctypes.Structure):
+    _fields_ = ([(n, ctypes.c_void_p) for n in ("ln1_w", "ln1_b", "ln2_w", "ln2_b")] +
+                [("tm", TmGrads)] +
+                [(n, ctypes.c_void_p) for n in ("cm_mu_k", "cm_Wk", "cm_Wv")])
+
+
+class Rwkv7ModelGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("emb", "ln0_w", "ln0_b", "ln_out_w", "ln_out_b",
+                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7BlockGrads))]
+
+
 class Wkv7Error(RuntimeError):
     pass
 
@@ -92,6 +103,11 @@ def lib():
         L.rwkv7_decode_workspace_bytes.restype = _sz
         L.rwkv7_decode_step.argtypes = [cp, ctypes.POINTER(Rwkv7Model), _i] + [_vp] * 6 + [_sz, _vp]
         L.rwkv7_decode_step.restype = _i
+        L.rwkv7_train_workspace_bytes.argtypes = [cp, _i, _i]
+        L.rwkv7_train_workspace_bytes.restype = _sz
+        L.rwkv7_train_step.argtypes = ([cp, ctypes.POINTER(Rwkv7Model), ctypes.POINTER(Rwkv7ModelGrads),
+                                        _i, _i] + [_vp] * 4 + [_sz, _vp])
+        L.rwkv7_train_step.restype = _i
         _lib = L
     return _lib
 
@@ -368,3 +384,60 @@ def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None):
                                    _p(state["ffn_x_prev"]), _p(logits), _p(ws), ws.numel(),
                                    _stream()))
     return logits
+
+
+# ---------------------------------------------------------- training step --
+class TrainGrads:
+    """Device gradient buffers mirroring a DecodeModel's weights (torch.empty)."""
+
+    def __init__(self, dm):
+        c = dm.cfg
+        dev = dm.w["emb"].device
+        e = lambda t: None if t is None else torch.empty_like(t)
+        w = dm.w
+        self.g = {k: e(w.get(k)) for k in ("emb", "head", "ln_out_w", "ln_out_b", "ln0_w", "ln0_b")}
+        self.g["blocks"] = []
+        blocks = (Rwkv7BlockGrads * c.n_layer)()
+        for l, bw in enumerate(w["blocks"]):
+            gb = {k: torch.empty_like(bw[k]) for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k",
+                                                        "cm_Wk", "cm_Wv")}
+            gb["tm"] = {}
+            b = blocks[l]
+            for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
+                setattr(b, k, gb[k].data_ptr())
+            tg = TmGrads()
+            for n in WEIGHT_FIELDS:
+                if l == 0 and n in ("v0", "V1", "V2"):
+                    setattr(tg, n, None)
+                    continue
+                gb["tm"][n] = torch.empty_like(bw["tm"][n])
+                setattr(tg, n, gb["tm"][n].data_ptr())
+            b.tm = tg
+            self.g["blocks"].append(gb)
+        self._blocks = blocks
+        mg = Rwkv7ModelGrads()
+        for n in ("emb", "head", "ln_out_w", "ln_out_b", "ln0_w", "ln0_b"):
+            t = self.g[n]
+            setattr(mg, n, None if t is None else t.data_ptr())
+        mg.blocks = ctypes.cast(blocks, ctypes.POINTER(Rwkv7BlockGrads))
+        self.struct = mg
+
+
+def rwkv7_train_workspace_bytes(dm, B, T):
+    return lib().rwkv7_train_workspace_bytes(ctypes.byref(dm.cfg), B, T)
+
+
+def rwkv7_train_step(dm, grads, tokens, targets, loss=None, ws=None):
+    """Loss (device scalar tensor) of one step; grads (TrainGrads) are written."""
+    B, T = tokens.shape
+    _need(tokens, (B, T), torch.int32, "tokens")
+    _need(targets, (B, T), torch.int32, "targets")
+    if loss is None:
+        loss = torch.empty(1, device=tokens.device, dtype=torch.float32)
+    nbytes = rwkv7_train_workspace_bytes(dm, B, T)
+    if ws is None:
+        ws = torch.empty(nbytes, device=tokens.device, dtype=torch.uint8)
+    _check(lib().rwkv7_train_step(ctypes.byref(dm.cfg), ctypes.byref(dm.model),
+                                  ctypes.byref(grads.struct), B, T, _p(tokens), _p(targets),
+                                  _p(loss), _p(ws), ws.numel(), _stream()))
+    return loss

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/wkv7.h"
 #include "common.hpp"
 #include "stack_kernels.hpp"
@@ -342,6 +344,91 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
 
 }  // namespace
 
+namespace {
+// Time-mix backward given the forward cache m and scratch bb.  dvf_accum:
+// dv_first_out += (instead of =) for layer > 0 (a stack sums it over layers).
+int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
+                     const float* x_prev, const float* v_first, const float* s0, const float* dout,
+                     const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
+                     float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
+                     float* ds0, hipStream_t st) {
+  const int BT = B * T, C = s->C, L = s->layer_id;
+
+  // output projection
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
+
+  TmBwd p;
+  memset(&p, 0, sizeof(p));
+  p.BT = BT; p.T = T; p.C = C; p.layer_id = L;
+  p.dtg = bb.dtg; p.g = m.g; p.y = m.y; p.r = m.r; p.kmod = m.kmod; p.vmod = m.vmod;
+  p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha; p.r_k = W->r_k; p.ln_w = W->ln_w; p.ln_b = W->ln_b;
+  p.dg = bb.dg; p.dy_wkv = bb.dy_wkv; p.dr = bb.dr; p.dkmod = bb.dkmod; p.dvmod = bb.dvmod;
+  p.part_post = bb.part_post;
+  p.gr = bb.gr; p.gk = bb.gk; p.gv = bb.gv; p.gw = bb.gw; p.gA = bb.gA; p.gB = bb.gB;
+  p.a = m.a; p.kk = m.kk; p.k = m.k; p.w = m.w; p.ow = m.ow; p.ov = m.ov; p.v = m.v;
+  p.v_first = v_first; p.k_a = W->k_a; p.k_k = W->k_k; p.w0 = W->w0; p.v0 = W->v0;
+  p.dvf_in = L == 0 ? dv_first_in : nullptr;
+  p.dk = bb.dk; p.dv = bb.dv; p.dpre_a = bb.dpre_a; p.dpre_w = bb.dpre_w; p.dpre_v = bb.dpre_v;
+  p.dvf_out = L > 0 ? dv_first_out : nullptr;
+  p.dvf_accum = dvf_accum ? 1 : 0;
+  p.part_pre = bb.part_pre;
+  p.x = x; p.x_prev = x_prev;
+  p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
+  p.dxr = bb.dxr; p.dxw = bb.dxw; p.dxk = bb.dxk; p.dxv = bb.dxv; p.dxa = bb.dxa; p.dxg = bb.dxg;
+  p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
+
+  HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
+  HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
+                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
+                              bb.wkv_part, st),
+         "wkv7 backward");
+  HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
+
+  const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
+  float* sk = bb.splitk;
+  // a: a = sigmoid(a0 + (xa A1) A2)
+  HIPCHK(gemm_f32_run(false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
+  HIPCHK(gemm_f32_run(true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
+  HIPCHK(gemm_f32_run(true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
+  // w: w = exp(-c sigmoid(w0 + tanh(xw W1) W2))
+  HIPCHK(gemm_f32_run(false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
+  HIPCHK(gemm_f32_run(true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
+  HIPCHK(gemm_f32_run(true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
+  // g: g = sigmoid(xg G1) G2
+  HIPCHK(gemm_f32_run(false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
+  HIPCHK(gemm_f32_run(true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
+  HIPCHK(gemm_f32_run(false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
+  HIPCHK(gemm_f32_run(true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
+  // value residual LoRA (layer > 0)
+  if (L > 0) {
+    HIPCHK(gemm_f32_run(false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
+    HIPCHK(gemm_f32_run(true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
+    HIPCHK(gemm_f32_run(false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
+    HIPCHK(gemm_f32_run(true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
+  }
+  // r, k, v projections
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
+  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
+  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
+
+  HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
+  const int nblk = tm_num_token_blocks(BT);
+  VecOut o1 = {{G->r_k, G->ln_w, G->ln_b, nullptr, nullptr, nullptr, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_post, 3, nblk, C, o1, st), "reduce post");
+  VecOut o2 = {{G->k_a, G->k_k, G->a0, G->w0, L > 0 ? G->v0 : nullptr, nullptr, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_pre, 5, nblk, C, o2, st), "reduce pre");
+  VecOut o3 = {{G->mu_r, G->mu_w, G->mu_k, G->mu_v, G->mu_a, G->mu_g, nullptr, nullptr}};
+  HIPCHK(tm_launch_reduce(bb.part_shift, 6, nblk, C, o3, st), "reduce shift");
+  return WKV7_OK;
+}
+}  // namespace
+
 extern "C" size_t timemix_cache_bytes(const tm_shape* s, int B, int T) {
   if (check_tm_shape(s, B, T) != WKV7_OK) return 0;
   Carver c(nullptr);
@@ -445,79 +532,8 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
     float* vf = L == 0 ? bb.dxg : (float*)v_first;
     CHK(tm_forward_impl(s, W, B, T, x, x_prev, vf, s0, nullptr, out_tmp, nullptr, m, stream));
   }
-  hipStream_t st = stream;
-
-  // output projection
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
-
-  TmBwd p;
-  memset(&p, 0, sizeof(p));
-  p.BT = BT; p.T = T; p.C = C; p.layer_id = L;
-  p.dtg = bb.dtg; p.g = m.g; p.y = m.y; p.r = m.r; p.kmod = m.kmod; p.vmod = m.vmod;
-  p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha; p.r_k = W->r_k; p.ln_w = W->ln_w; p.ln_b = W->ln_b;
-  p.dg = bb.dg; p.dy_wkv = bb.dy_wkv; p.dr = bb.dr; p.dkmod = bb.dkmod; p.dvmod = bb.dvmod;
-  p.part_post = bb.part_post;
-  p.gr = bb.gr; p.gk = bb.gk; p.gv = bb.gv; p.gw = bb.gw; p.gA = bb.gA; p.gB = bb.gB;
-  p.a = m.a; p.kk = m.kk; p.k = m.k; p.w = m.w; p.ow = m.ow; p.ov = m.ov; p.v = m.v;
-  p.v_first = v_first; p.k_a = W->k_a; p.k_k = W->k_k; p.w0 = W->w0; p.v0 = W->v0;
-  p.dvf_in = L == 0 ? dv_first_in : nullptr;
-  p.dk = bb.dk; p.dv = bb.dv; p.dpre_a = bb.dpre_a; p.dpre_w = bb.dpre_w; p.dpre_v = bb.dpre_v;
-  p.dvf_out = L > 0 ? dv_first_out : nullptr;
-  p.part_pre = bb.part_pre;
-  p.x = x; p.x_prev = x_prev;
-  p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
-  p.dxr = bb.dxr; p.dxw = bb.dxw; p.dxk = bb.dxk; p.dxv = bb.dxv; p.dxa = bb.dxa; p.dxg = bb.dxg;
-  p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
-
-  HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
-  HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
-                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
-                              bb.wkv_part, st),
-         "wkv7 backward");
-  HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
-
-  const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
-  float* sk = bb.splitk;
-  // a: a = sigmoid(a0 + (xa A1) A2)
-  HIPCHK(gemm_f32_run(false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
-  HIPCHK(gemm_f32_run(true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
-  HIPCHK(gemm_f32_run(true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
-  // w: w = exp(-c sigmoid(w0 + tanh(xw W1) W2))
-  HIPCHK(gemm_f32_run(false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
-  HIPCHK(gemm_f32_run(true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
-  HIPCHK(gemm_f32_run(true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
-  // g: g = sigmoid(xg G1) G2
-  HIPCHK(gemm_f32_run(false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
-  HIPCHK(gemm_f32_run(true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
-  HIPCHK(gemm_f32_run(true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
-  // value residual LoRA (layer > 0)
-  if (L > 0) {
-    HIPCHK(gemm_f32_run(false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
-    HIPCHK(gemm_f32_run(true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
-    HIPCHK(gemm_f32_run(false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
-    HIPCHK(gemm_f32_run(true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
-  }
-  // r, k, v projections
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
-
-  HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
-  const int nblk = tm_num_token_blocks(BT);
-  VecOut o1 = {{G->r_k, G->ln_w, G->ln_b, nullptr, nullptr, nullptr, nullptr, nullptr}};
-  HIPCHK(tm_launch_reduce(bb.part_post, 3, nblk, C, o1, st), "reduce post");
-  VecOut o2 = {{G->k_a, G->k_k, G->a0, G->w0, L > 0 ? G->v0 : nullptr, nullptr, nullptr, nullptr}};
-  HIPCHK(tm_launch_reduce(bb.part_pre, 5, nblk, C, o2, st), "reduce pre");
-  VecOut o3 = {{G->mu_r, G->mu_w, G->mu_k, G->mu_v, G->mu_a, G->mu_g, nullptr, nullptr}};
-  HIPCHK(tm_launch_reduce(bb.part_shift, 6, nblk, C, o3, st), "reduce shift");
-  return WKV7_OK;
+  return tm_backward_impl(s, W, B, T, x, x_prev, v_first, s0, dout, dsT, m, bb, G, dx, dx_prev,
+                          dv_first_in, dv_first_out, false, ds0, stream);
 }
 
 // ----------------------------------------------------------------- GEMM --
@@ -631,5 +647,186 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
   }
   HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_f32_run(false, false, B, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
+  return WKV7_OK;
+}
+
+// ---------------------------------------------------------- training step --
+namespace {
+
+struct TrainBufs {
+  float *block_in, *x_emb, *vf, *dvf, *h, *x1, *h2, *sh, *dsh, *dh, *dx, *dx1;
+  float *ka, *dfk, *logits, *loss_row, *part_ln, *part_cm, *splitk;
+  int *count, *off, *perm;
+  TmCache tm;
+  TmBwdBufs tb;
+};
+
+tm_shape block_shape(const rwkv7_config* c, int l) {
+  return tm_shape{c->C, c->H, c->N, c->Dw, c->Da, c->Dv, c->Dg, l};
+}
+
+void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t) {
+  const size_t BT = (size_t)B * T, tok = BT * cfg->C, L = cfg->n_layer;
+  t.block_in = c.take((L + 1) * tok);
+  t.x_emb = cfg->use_ln0 ? c.take(tok) : nullptr;
+  float** toks[] = {&t.vf, &t.dvf, &t.h, &t.x1, &t.h2, &t.sh, &t.dsh, &t.dh, &t.dx, &t.dx1};
+  for (float** p : toks) *p = c.take(tok);
+  t.ka = c.take(BT * cfg->F);
+  t.dfk = c.take(BT * cfg->F);
+  t.logits = c.take(BT * cfg->V);
+  t.loss_row = c.take(BT);
+  t.part_ln = c.take((size_t)2 * stk_num_ln_blocks((int)BT) * cfg->C);
+  t.part_cm = c.take((size_t)stk_num_shift_blocks((int)BT) * cfg->C);
+  const int C = cfg->C, F = cfg->F, V = cfg->V;
+  size_t sk = 0;
+  const int pairs[][2] = {{F, C}, {C, F}, {C, V}};
+  for (auto& pr : pairs) sk = std::max(sk, (size_t)splitk_for(pr[0], pr[1], (int)BT) * pr[0] * pr[1]);
+  t.splitk = c.take(sk);
+  t.count = (int*)c.take((size_t)V);
+  t.off = (int*)c.take((size_t)V);
+  t.perm = (int*)c.take(BT);
+  tm_shape s = block_shape(cfg, 1);
+  carve_cache(c, &s, B, T, t.tm);
+  carve_bwd(c, &s, B, T, t.tb);
+}
+
+}  // namespace
+
+extern "C" size_t rwkv7_train_workspace_bytes(const rwkv7_config* cfg, int B, int T) {
+  if (check_cfg(cfg, B) != WKV7_OK || T < 1) return 0;
+  Carver c(nullptr);
+  TrainBufs t;
+  carve_train(c, cfg, B, T, t);
+  return c.off + 256;
+}
+
+extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
+                                rwkv7_model_grads* G, int B, int T, const int* tokens,
+                                const int* targets, float* loss, void* ws, size_t ws_bytes,
+                                hipStream_t st) {
+  g_err[0] = 0;
+  CHK(check_cfg(cfg, B));
+  if (T < 1) return fail(WKV7_EINVAL, "T must be >= 1");
+  if (!M || !M->blocks || !G || !G->blocks) return fail(WKV7_EINVAL, "model/grads or their blocks are NULL");
+  CHK(check_f32_ptr(M->emb, "emb", true));
+  CHK(check_f32_ptr(M->head, "head", true));
+  CHK(check_f32_ptr(M->ln_out_w, "ln_out_w", true));
+  CHK(check_f32_ptr(M->ln_out_b, "ln_out_b", true));
+  CHK(check_f32_ptr(M->ln0_w, "ln0_w", cfg->use_ln0 != 0));
+  CHK(check_f32_ptr(M->ln0_b, "ln0_b", cfg->use_ln0 != 0));
+  float* greq[] = {G->emb, G->head, G->ln_out_w, G->ln_out_b};
+  for (float* p : greq) CHK(check_f32_ptr(p, "a model gradient", true));
+  if (cfg->use_ln0) {
+    CHK(check_f32_ptr(G->ln0_w, "grad ln0_w", true));
+    CHK(check_f32_ptr(G->ln0_b, "grad ln0_b", true));
+  }
+  CHK(check_tok_ptr(tokens, "tokens", WKV7_F32, true));
+  CHK(check_tok_ptr(targets, "targets", WKV7_F32, true));
+  CHK(check_f32_ptr(loss, "loss", true));
+  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer;
+  if ((size_t)B * T * V > ((size_t)1 << 34)) return fail(WKV7_EINVAL, "B*T*V too large");
+  for (int l = 0; l < L; l++) {
+    tm_shape s = block_shape(cfg, l);
+    CHK(check_weights(&s, &M->blocks[l].tm));
+    const rwkv7_block& bl = M->blocks[l];
+    const float* req[] = {bl.ln1_w, bl.ln1_b, bl.ln2_w, bl.ln2_b, bl.cm_mu_k, bl.cm_Wk, bl.cm_Wv};
+    for (const float* p : req) CHK(check_f32_ptr(p, "a block weight", true));
+    const rwkv7_block_grads& gb = G->blocks[l];
+    float* gq[] = {gb.ln1_w, gb.ln1_b, gb.ln2_w, gb.ln2_b, gb.cm_mu_k, gb.cm_Wk, gb.cm_Wv,
+                   gb.tm.mu_r, gb.tm.mu_w, gb.tm.mu_k, gb.tm.mu_v, gb.tm.mu_a, gb.tm.mu_g,
+                   gb.tm.Wr, gb.tm.Wk, gb.tm.Wv, gb.tm.Wo, gb.tm.w0, gb.tm.W1, gb.tm.W2, gb.tm.a0,
+                   gb.tm.A1, gb.tm.A2, gb.tm.G1, gb.tm.G2, gb.tm.k_k, gb.tm.k_a, gb.tm.r_k,
+                   gb.tm.ln_w, gb.tm.ln_b};
+    for (float* p : gq) CHK(check_f32_ptr(p, "a block gradient", true));
+    if (l > 0) {
+      CHK(check_f32_ptr(gb.tm.v0, "grad v0", true));
+      CHK(check_f32_ptr(gb.tm.V1, "grad V1", true));
+      CHK(check_f32_ptr(gb.tm.V2, "grad V2", true));
+    }
+  }
+  const size_t need = rwkv7_train_workspace_bytes(cfg, B, T);
+  if (!ws || ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  CHK(check_f32_ptr(ws, "ws", true));
+  Carver cw(ws);
+  TrainBufs t;
+  carve_train(cw, cfg, B, T, t);
+
+  const int BT = B * T;
+  const size_t tokC = (size_t)BT * C;
+  auto bin = [&](int l) { return t.block_in + (size_t)l * tokC; };
+  auto reduce_ln = [&](float* gw, float* gb) -> hipError_t {
+    VecOut o = {{gw, gb, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
+    return tm_launch_reduce(t.part_ln, 2, stk_num_ln_blocks(BT), C, o, st);
+  };
+
+  // ---------------- forward (block inputs kept for the backward)
+  HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
+  if (cfg->use_ln0)
+    HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
+  for (int l = 0; l < L; l++) {
+    const rwkv7_block& bl = M->blocks[l];
+    tm_shape s = block_shape(cfg, l);
+    float* xo = bin(l + 1);
+    HIPCHK(hipMemcpyAsync(xo, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
+    CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, xo, nullptr, t.tm, st,
+                        false, 1.f));
+    HIPCHK(stk_launch_layernorm(BT, C, xo, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
+    HIPCHK(gemm_f32_run(false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_f32_run(false, false, BT, C, F, t.ka, F, bl.cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+  }
+  HIPCHK(stk_launch_layernorm(BT, C, bin(L), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
+  HIPCHK(gemm_f32_run(false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
+  HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, st), "cross-entropy");
+
+  // ---------------- backward
+  HIPCHK(gemm_f32_run(false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
+  HIPCHK(gemm_f32_run(true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
+                      splitk_for(C, V, BT), t.splitk, st), "dhead");
+  HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(L), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
+  HIPCHK(reduce_ln(G->ln_out_w, G->ln_out_b), "ln_out grads");
+  HIPCHK(stk_launch_fill_zero(t.dvf, tokC, st), "zero dv_first");
+  for (int l = L - 1; l >= 0; l--) {
+    const rwkv7_block& bl = M->blocks[l];
+    rwkv7_block_grads& gb = G->blocks[l];
+    tm_shape s = block_shape(cfg, l);
+    // recompute this block's forward from its cached input
+    HIPCHK(hipMemcpyAsync(t.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
+    CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, t.x1, nullptr, t.tm, st,
+                        false, 1.f));
+    HIPCHK(stk_launch_layernorm(BT, C, t.x1, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
+    HIPCHK(gemm_f32_run(false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    // channel-mix backward
+    HIPCHK(gemm_f32_run(false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, t.ka, 1, nullptr, st), "dfk");
+    HIPCHK(gemm_f32_run(true, false, F, C, BT, t.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
+                        splitk_for(F, C, BT), t.splitk, st), "dWv");
+    HIPCHK(gemm_f32_run(false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
+    HIPCHK(gemm_f32_run(true, false, C, F, BT, t.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
+                        splitk_for(C, F, BT), t.splitk, st), "dWk");
+    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
+    {
+      VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
+      HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT), C, o, st), "cm mu grad");
+    }
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, t.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
+    HIPCHK(reduce_ln(gb.ln2_w, gb.ln2_b), "ln2 grads");
+    // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
+    CHK(tm_backward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, t.dx1, nullptr, t.tm, t.tb,
+                         &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
+                         nullptr, st));
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
+    HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
+  }
+  const float* demb_src = t.dx;
+  if (cfg->use_ln0) {
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, t.x_emb, M->ln0_w, t.dx, nullptr, t.dx1, t.part_ln, st), "ln0 bwd");
+    HIPCHK(reduce_ln(G->ln0_w, G->ln0_b), "ln0 grads");
+    demb_src = t.dx1;
+  }
+  HIPCHK(stk_launch_emb_bwd(BT, V, C, tokens, demb_src, t.count, t.off, t.perm, G->emb, st), "embedding bwd");
   return WKV7_OK;
 }

@@ -12,7 +12,7 @@
 namespace stk {
 
 constexpr float LN_EPS = 1e-5f;
-constexpr int MAXC4 = 16;  // LayerNorm keeps a row in registers: C <= 64 * 4 * MAXC4
+constexpr int MAXC4_LIMIT = 16;  // LayerNorm keeps a row in registers: C <= 64 * 4 * 16
 
 // out[r] = emb[clamp(tok[r])] (float4 per thread)
 __global__ __launch_bounds__(256) void emb_gather(int R, int C, int V, const int* __restrict__ tok,
@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256) void emb_gather(int R, int C, int V, const int
 
 // y = (x - mean) / sqrt(var + eps) * w + b per row; one wave per row, the row
 // held in registers (in-place safe).  mean/rstd are optional outputs.
+template <int MAXC4>
 __global__ __launch_bounds__(256) void layernorm_fwd(int R, int C, const float* __restrict__ x,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ b, float* y,
@@ -106,10 +107,23 @@ hipError_t stk_launch_emb_gather(int R, int C, int V, const int* tok, const floa
                      tok, emb, out);
   return hipGetLastError();
 }
+// float4 chunks per lane for a row of C floats: 1, 2, 4, 8 or 16
+static int ln_chunks(int C) {
+  const int need = (C / 4 + 63) / 64;
+  int j = 1;
+  while (j < need) j *= 2;
+  return j;
+}
 hipError_t stk_launch_layernorm(int R, int C, const float* x, const float* w, const float* b,
                                 float* y, float* mean, float* rstd, hipStream_t st) {
-  hipLaunchKernelGGL(stk::layernorm_fwd, dim3((R + 3) / 4), dim3(256), 0, st, R, C, x, w, b, y,
-                     mean, rstd);
+  const dim3 g((R + 3) / 4), t(256);
+  switch (ln_chunks(C)) {
+    case 1: hipLaunchKernelGGL(stk::layernorm_fwd<1>, g, t, 0, st, R, C, x, w, b, y, mean, rstd); break;
+    case 2: hipLaunchKernelGGL(stk::layernorm_fwd<2>, g, t, 0, st, R, C, x, w, b, y, mean, rstd); break;
+    case 4: hipLaunchKernelGGL(stk::layernorm_fwd<4>, g, t, 0, st, R, C, x, w, b, y, mean, rstd); break;
+    case 8: hipLaunchKernelGGL(stk::layernorm_fwd<8>, g, t, 0, st, R, C, x, w, b, y, mean, rstd); break;
+    default: hipLaunchKernelGGL(stk::layernorm_fwd<16>, g, t, 0, st, R, C, x, w, b, y, mean, rstd); break;
+  }
   return hipGetLastError();
 }
 hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float* x_prev,
@@ -118,4 +132,301 @@ hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float
                      x, x_prev, mu, sh, x_last);
   return hipGetLastError();
 }
-int stk_max_layernorm_width() { return 64 * 4 * stk::MAXC4; }
+int stk_max_layernorm_width() { return 64 * 4 * stk::MAXC4_LIMIT; }
+
+// ------------------------------------------------------ training kernels --
+namespace stk {
+
+// zero n 4-byte words (a kernel, not a memset: safe inside captured graphs)
+__global__ __launch_bounds__(256) void fill_zero(size_t n, float* __restrict__ p) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
+}
+
+constexpr int LN_ROWS = 64;  // rows per workgroup in the LayerNorm backward (partial sums)
+
+// LayerNorm backward, one wave per row (row in registers), 4 waves x 16 rows
+// per workgroup.  dx = rstd (dn - mean(dn) - nhat mean(dn nhat)) + dres,
+// dn = dy w; per-channel partials of dw = sum dy nhat and db = sum dy are
+// written as part[0|1][blk][C] (summed later in a fixed order).
+template <int MAXC4>
+__global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* __restrict__ x,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ dy,
+                                                     const float* dres, float* dx,
+                                                     float* __restrict__ part) {
+  __shared__ f4 red[2][4][MAXC4][64];
+  const int blk = blockIdx.x, nblk = gridDim.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C4 = C / 4;
+  f4 pw[MAXC4], pb[MAXC4];
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) pw[j] = pb[j] = f4{0.f, 0.f, 0.f, 0.f};
+  const int r_end = min(R, (blk + 1) * LN_ROWS);
+  for (int row = blk * LN_ROWS + wave; row < r_end; row += 4) {
+    const f4* xr = reinterpret_cast<const f4*>(x + (size_t)row * C);
+    const f4* gr = reinterpret_cast<const f4*>(dy + (size_t)row * C);
+    f4 xv[MAXC4], gv[MAXC4];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) {
+      const int c4 = lane + 64 * j;
+      xv[j] = c4 < C4 ? xr[c4] : f4{0.f, 0.f, 0.f, 0.f};
+      gv[j] = c4 < C4 ? gr[c4] : f4{0.f, 0.f, 0.f, 0.f};
+      s += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
+    }
+    const float mean = wavesum(s) / C;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) {
+      if (lane + 64 * j < C4) {
+        const f4 d = xv[j] - mean;
+        q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wavesum(q) / C + LN_EPS);
+    float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) {
+      const int c4 = lane + 64 * j;
+      if (c4 < C4) {
+        const f4 nh = (xv[j] - mean) * rstd;
+        const f4 dn = gv[j] * reinterpret_cast<const f4*>(w)[c4];
+        m1 += (dn[0] + dn[1]) + (dn[2] + dn[3]);
+        const f4 t = dn * nh;
+        m2 += (t[0] + t[1]) + (t[2] + t[3]);
+        pw[j] += gv[j] * nh;
+        pb[j] += gv[j];
+        xv[j] = nh;  // keep nhat
+        gv[j] = dn;  // keep dn
+      }
+    }
+    m1 = wavesum(m1) / C;
+    m2 = wavesum(m2) / C;
+    f4* dxr = reinterpret_cast<f4*>(dx + (size_t)row * C);
+    const f4* rr = dres ? reinterpret_cast<const f4*>(dres + (size_t)row * C) : nullptr;
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) {
+      const int c4 = lane + 64 * j;
+      if (c4 < C4) {
+        f4 o = rstd * (gv[j] - m1 - xv[j] * m2);
+        if (rr) o += rr[c4];
+        dxr[c4] = o;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) {
+    red[0][wave][j][lane] = pw[j];
+    red[1][wave][j][lane] = pb[j];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * C4; i += 256) {
+    const int v = i / C4, c4 = i - v * C4, j = c4 >> 6, l = c4 & 63;
+    f4 t = red[v][0][j][l];
+#pragma unroll
+    for (int wv = 1; wv < 4; wv++) t += red[v][wv][j][l];
+    reinterpret_cast<f4*>(part + ((size_t)v * nblk + blk) * C)[c4] = t;
+  }
+}
+
+constexpr int TBK = 128;  // tokens per workgroup in the shift backward
+
+// Channel-mix token-shift backward: dx = dsh (1 - mu) + dsh[t+1] mu,
+// dx_prev (t = 0) = dsh mu, partial dmu = sum dsh (prev - x).  Grid (C/64, token blocks).
+__global__ __launch_bounds__(256) void cm_shift_bwd(int BT, int T, int C, const float* __restrict__ x,
+                                                    const float* __restrict__ x_prev,
+                                                    const float* __restrict__ mu,
+                                                    const float* __restrict__ dsh,
+                                                    float* __restrict__ dx, float* __restrict__ dx_prev,
+                                                    float* __restrict__ part) {
+  __shared__ f4 red[16][16];
+  const int cb = blockIdx.x, blk = blockIdx.y;
+  const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int c = cb * 64 + l16 * 4;
+  const f4 m = *reinterpret_cast<const f4*>(mu + c);
+  f4 pm = {0.f, 0.f, 0.f, 0.f};
+  const int t_end = min(BT, (blk + 1) * TBK);
+  for (int bt = blk * TBK + grp; bt < t_end; bt += 16) {
+    const size_t e = (size_t)bt * C + c;
+    const int t = bt % T;
+    const f4 xv = *reinterpret_cast<const f4*>(x + e);
+    f4 prev = {0.f, 0.f, 0.f, 0.f};
+    if (t > 0) prev = *reinterpret_cast<const f4*>(x + e - C);
+    else if (x_prev) prev = *reinterpret_cast<const f4*>(x_prev + (size_t)(bt / T) * C + c);
+    const f4 g = *reinterpret_cast<const f4*>(dsh + e);
+    pm += g * (prev - xv);
+    f4 o = g * (1.0f - m);
+    if (t < T - 1) o += *reinterpret_cast<const f4*>(dsh + e + C) * m;
+    *reinterpret_cast<f4*>(dx + e) = o;
+    if (t == 0 && dx_prev) *reinterpret_cast<f4*>(dx_prev + (size_t)(bt / T) * C + c) = g * m;
+  }
+  red[grp][l16] = pm;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    f4 s = red[0][threadIdx.x];
+    for (int gi = 1; gi < 16; gi++) s += red[gi][threadIdx.x];
+    *reinterpret_cast<f4*>(part + (size_t)blk * C + cb * 64 + threadIdx.x * 4) = s;
+  }
+}
+
+// Fused log-softmax cross-entropy, one workgroup per row, in place:
+// loss_row[r] = lse - z[target];  z <- (softmax(z) - onehot(target)) / n_tok.
+__global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restrict__ z,
+                                                  const int* __restrict__ targets, float inv_n,
+                                                  float* __restrict__ loss_row) {
+  __shared__ float sm[2][4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f4* zr = reinterpret_cast<f4*>(z + (size_t)row * V);
+  const int V4 = V / 4;
+  float mx = -INFINITY;
+  for (int i = tid; i < V4; i += 256) {
+    const f4 v = zr[i];
+    mx = fmaxf(mx, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  }
+  // wave max via the sum machinery on exp-free values: use shuffles
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) sm[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sm[0][0], sm[0][1]), fmaxf(sm[0][2], sm[0][3]));
+  float s = 0.f;
+  for (int i = tid; i < V4; i += 256) {
+    const f4 v = zr[i];
+    s += (expf(v[0] - mx) + expf(v[1] - mx)) + (expf(v[2] - mx) + expf(v[3] - mx));
+  }
+  s = wavesum(s);
+  if (lane == 0) sm[1][wave] = s;
+  __syncthreads();
+  s = (sm[1][0] + sm[1][1]) + (sm[1][2] + sm[1][3]);
+  const float lse = mx + logf(s);
+  const int tgt = min(max(targets[row], 0), V - 1);
+  const float zt = z[(size_t)row * V + tgt];
+  __syncthreads();  // every thread has read z[target] before it is overwritten
+  for (int i = tid; i < V4; i += 256) {
+    const f4 v = zr[i];
+    f4 p;
+#pragma unroll
+    for (int c = 0; c < 4; c++) p[c] = expf(v[c] - lse) - ((4 * i + c) == tgt ? 1.0f : 0.0f);
+    zr[i] = p * inv_n;
+  }
+  if (tid == 0) loss_row[row] = lse - zt;
+}
+
+// loss = sum_r loss_row[r] * inv_n, fixed order (one workgroup)
+__global__ __launch_bounds__(256) void sum_rows(int R, const float* __restrict__ v, float inv_n,
+                                                float* __restrict__ out) {
+  __shared__ float sm[256];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < R; i += 256) s += v[i];
+  sm[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sm[0] * inv_n;
+}
+
+// Embedding backward without float atomics.
+// 1) integer counts per vocabulary row
+__global__ __launch_bounds__(256) void emb_count(int R, int V, const int* __restrict__ tok,
+                                                 int* __restrict__ count) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < R) atomicAdd(&count[min(max(tok[p], 0), V - 1)], 1);
+}
+// 2) exclusive scan of the counts (one workgroup of 1024 threads)
+__global__ __launch_bounds__(1024) void emb_scan(int V, const int* __restrict__ count,
+                                                 int* __restrict__ off) {
+  __shared__ int sm[1024];
+  const int per = (V + 1023) / 1024;
+  const int b = threadIdx.x * per, e = min(V, b + per);
+  int s = 0;
+  for (int i = b; i < e; i++) s += count[i];
+  sm[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
+    const int t = threadIdx.x >= o ? sm[threadIdx.x - o] : 0;
+    __syncthreads();
+    sm[threadIdx.x] += t;
+    __syncthreads();
+  }
+  int run = sm[threadIdx.x] - s;  // exclusive prefix of this thread's range
+  for (int i = b; i < e; i++) {
+    off[i] = run;
+    run += count[i];
+  }
+}
+// 3) position p goes to slot off[tok[p]] + #{q < p : tok[q] == tok[p]} (stable)
+__global__ __launch_bounds__(256) void emb_place(int R, int V, const int* __restrict__ tok,
+                                                 const int* __restrict__ off, int* __restrict__ perm) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= R) return;
+  const int v = min(max(tok[p], 0), V - 1);
+  int rank = 0;
+  for (int q = 0; q < p; q++) rank += min(max(tok[q], 0), V - 1) == v;
+  perm[off[v] + rank] = p;
+}
+// 4) demb[v] = sum of dx rows of its positions in position order; one wave per row
+__global__ __launch_bounds__(256) void emb_rows(int V, int C, const int* __restrict__ count,
+                                                const int* __restrict__ off,
+                                                const int* __restrict__ perm,
+                                                const float* __restrict__ dx,
+                                                float* __restrict__ demb) {
+  const int v = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (v >= V) return;
+  const int C4 = C / 4, n = count[v], o = off[v];
+  for (int c4 = lane; c4 < C4; c4 += 64) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < n; i++) acc += reinterpret_cast<const f4*>(dx + (size_t)perm[o + i] * C)[c4];
+    reinterpret_cast<f4*>(demb + (size_t)v * C)[c4] = acc;
+  }
+}
+
+}  // namespace stk
+
+hipError_t stk_launch_fill_zero(float* p, size_t n, hipStream_t st) {
+  hipLaunchKernelGGL(stk::fill_zero, dim3(grid_for(n)), dim3(256), 0, st, n, p);
+  return hipGetLastError();
+}
+int stk_num_ln_blocks(int R) { return (R + stk::LN_ROWS - 1) / stk::LN_ROWS; }
+int stk_num_shift_blocks(int BT) { return (BT + stk::TBK - 1) / stk::TBK; }
+
+hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
+                                    const float* dres, float* dx, float* part, hipStream_t st) {
+  const dim3 g(stk_num_ln_blocks(R)), t(256);
+  switch (ln_chunks(C)) {
+    case 1: hipLaunchKernelGGL(stk::layernorm_bwd<1>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+    case 2: hipLaunchKernelGGL(stk::layernorm_bwd<2>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+    case 4: hipLaunchKernelGGL(stk::layernorm_bwd<4>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+    case 8: hipLaunchKernelGGL(stk::layernorm_bwd<8>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+    default: hipLaunchKernelGGL(stk::layernorm_bwd<16>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+  }
+  return hipGetLastError();
+}
+hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,
+                                   const float* mu, const float* dsh, float* dx, float* dx_prev,
+                                   float* part, hipStream_t st) {
+  hipLaunchKernelGGL(stk::cm_shift_bwd, dim3(C / 64, stk_num_shift_blocks(BT)), dim3(256), 0, st,
+                     BT, T, C, x, x_prev, mu, dsh, dx, dx_prev, part);
+  return hipGetLastError();
+}
+hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
+                         hipStream_t st) {
+  const float inv_n = 1.0f / (float)R;
+  hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, inv_n, loss_row);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(stk::sum_rows, dim3(1), dim3(256), 0, st, R, loss_row, inv_n, loss);
+  return hipGetLastError();
+}
+hipError_t stk_launch_emb_bwd(int R, int V, int C, const int* tok, const float* dx, int* count,
+                              int* off, int* perm, float* demb, hipStream_t st) {
+  hipError_t e = stk_launch_fill_zero((float*)count, (size_t)V, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(stk::emb_count, dim3((R + 255) / 256), dim3(256), 0, st, R, V, tok, count);
+  hipLaunchKernelGGL(stk::emb_scan, dim3(1), dim3(1024), 0, st, V, count, off);
+  hipLaunchKernelGGL(stk::emb_place, dim3((R + 255) / 256), dim3(256), 0, st, R, V, tok, off, perm);
+  hipLaunchKernelGGL(stk::emb_rows, dim3((V + 3) / 4), dim3(256), 0, st, V, C, count, off, perm, dx,
+                     demb);
+  return hipGetLastError();
+}

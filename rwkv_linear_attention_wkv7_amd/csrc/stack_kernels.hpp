@@ -9,3 +9,15 @@ hipError_t stk_launch_layernorm(int R, int C, const float* x, const float* w, co
 hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float* x_prev,
                                const float* mu, float* sh, float* x_last, hipStream_t st);
 int stk_max_layernorm_width();
+int stk_num_ln_blocks(int R);
+int stk_num_shift_blocks(int BT);
+hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
+                                    const float* dres, float* dx, float* part, hipStream_t st);
+hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,
+                                   const float* mu, const float* dsh, float* dx, float* dx_prev,
+                                   float* part, hipStream_t st);
+hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
+                         hipStream_t st);
+hipError_t stk_launch_emb_bwd(int R, int V, int C, const int* tok, const float* dx, int* count,
+                              int* off, int* perm, float* demb, hipStream_t st);
+hipError_t stk_launch_fill_zero(float* p, size_t n, hipStream_t st);

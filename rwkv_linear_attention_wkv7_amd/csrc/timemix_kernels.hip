@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void pre_bwd(TmBwd p) {
 #pragma unroll
       for (int j = 0; j < 4; j++) nu[j] = sigm(v0[j] + ov[j]);
       st4(p.dv + e, dvmod * (1.0f - nu));
-      if (p.dvf_out) st4(p.dvf_out + e, dvmod * nu);
+      if (p.dvf_out) st4(p.dvf_out + e, p.dvf_accum ? ld4(p.dvf_out + e) + dvmod * nu : dvmod * nu);
       const f4 dpv = dvmod * (vf - v) * nu * (1.0f - nu);
       pv0 += dpv;
       st4(p.dpre_v + e, dpv);

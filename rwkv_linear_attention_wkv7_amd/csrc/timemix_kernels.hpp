@@ -29,6 +29,7 @@ struct TmBwd {
   const float *gr, *gk, *gv, *gw, *gA, *gB;  // WKV7 gradients
   const float *a, *kk, *k, *w, *ow, *ov, *v, *v_first, *k_a, *k_k, *w0, *v0, *dvf_in;
   float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *dvf_out, *part_pre;
+  int dvf_accum;  // dvf_out += instead of =
   // token shift backward
   const float *x, *x_prev, *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
   const float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg;

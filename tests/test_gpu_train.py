@@ -1,0 +1,101 @@
+"""GPU parity of rwkv7_train_step (full RWKV-7 training step: embedding,
+blocks, LM head, fused log-softmax CE, forward and backward) against the f64
+oracle.  Loss and every gradient are compared (max|gpu - oracle| /
+max|oracle|): loss <= 1e-4, gradients <= 1e-3 (fp32 end to end)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import stack
+from rwkv_linear_attention_wkv7_amd import synth
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_model(m):
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    out = {k: d(v) for k, v in m.items() if k != "blocks"}
+    out["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
+                      for k, v in b.items()} for b in m["blocks"]]
+    return out
+
+
+def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0):
+    from rwkv_linear_attention_wkv7_amd import binding
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=seed, perturbed=perturbed, std=std,
+                          use_ln0=use_ln0)
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks,
+                                  use_ln0=int(use_ln0)), _dev_model(m))
+    grads = binding.TrainGrads(dm)
+    tok = synth.token_ids(B, T + 1, V, seed=seed + 100)
+    x, y = np.ascontiguousarray(tok[:, :-1]), np.ascontiguousarray(tok[:, 1:])
+    print(f"[train] L={L} C={C} F={F} V={V} B={B} T={T}", flush=True)
+    loss = hip.rwkv7_train_step(dm, grads, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    return m, dm, grads, x, y, float(loss.item())
+
+
+def _compare(m, grads, x, y, loss, cfg):
+    ref_loss, G = stack.train_step(m, cfg, x, y)
+    assert abs(loss - ref_loss) <= 1e-4 * abs(ref_loss), (loss, ref_loss)
+    g = grads.g
+    np_ = lambda t: t.cpu().numpy()
+    for k in ("emb", "head", "ln_out_w", "ln_out_b"):
+        assert_close(k, np_(g[k]), G[k], 1e-3)
+    if g.get("ln0_w") is not None:
+        assert_close("ln0_w", np_(g["ln0_w"]), G["ln0_w"], 1e-3)
+        assert_close("ln0_b", np_(g["ln0_b"]), G["ln0_b"], 1e-3)
+    for l, gb in enumerate(g["blocks"]):
+        for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
+            assert_close(f"{k}[{l}]", np_(gb[k]), G["blocks"][l][k], 1e-3)
+        assert set(gb["tm"]) == set(G["blocks"][l]["tm"])
+        for k, v in gb["tm"].items():
+            assert_close(f"tm.{k}[{l}]", np_(v), G["blocks"][l]["tm"][k], 1e-3)
+
+
+@pytest.mark.parametrize("use_ln0", [False, True])
+def test_train_step_small(hip, use_ln0):
+    L, C, H, F, V = 3, 128, 2, 256, 512
+    m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (16, 16, 16, 32), 2, 40, seed=3,
+                                    perturbed=True, std=0.2, use_ln0=use_ln0)
+    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L))
+
+
+def test_train_step_full_model_short_batch(hip):
+    """Full model size: 24 blocks, C=1024 (H=16), FFN 4096, vocab 65536, ranks
+    64/64/32/128, std-0.02 random init; one sequence of 256 tokens so the f64
+    oracle fits; every gradient compared."""
+    L, C, H, F, V = 24, 1024, 16, 4096, 65536
+    m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 1, 256, seed=0,
+                                    perturbed=False, std=0.02, use_ln0=False)
+    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L))
+
+
+def test_train_step_full_config_properties(hip):
+    """B=4, T=2048 at the full model size.  At random init the LN output rows
+    have unit variance and the head entries N(0, 0.02^2), so the logits are
+    ~N(0, s2) with s2 = C 0.02^2 and the expected loss is
+    E[logsumexp] - E[z_target] = ln(V) + s2/2 (log of the mean of e^z);
+    every gradient is finite; two runs are bitwise identical (fixed-order
+    reductions only)."""
+    from rwkv_linear_attention_wkv7_amd import binding
+    L, C, H, F, V = 24, 1024, 16, 4096, 65536
+    m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 4, 2048, seed=0,
+                                    perturbed=False, std=0.02, use_ln0=False)
+    expect = math.log(V) + C * 0.02 ** 2 / 2
+    assert abs(loss - expect) < 3e-2, (loss, expect)
+    first = {"emb": grads.g["emb"].clone(), "head": grads.g["head"].clone(),
+             "Wr0": grads.g["blocks"][0]["tm"]["Wr"].clone(),
+             "cmk23": grads.g["blocks"][23]["cm_Wk"].clone()}
+    for t in first.values():
+        assert torch.isfinite(t).all()
+    loss2 = binding.rwkv7_train_step(dm, grads, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    assert float(loss2.item()) == loss
+    assert torch.equal(first["emb"], grads.g["emb"])
+    assert torch.equal(first["head"], grads.g["head"])
+    assert torch.equal(first["Wr0"], grads.g["blocks"][0]["tm"]["Wr"])
+    assert torch.equal(first["cmk23"], grads.g["blocks"][23]["cm_Wk"])

@@ -57,3 +57,59 @@ def test_stream_independence():
     full, _ = stack.forward(m, cfg, tok)
     one, _ = stack.forward(m, cfg, tok[2:3])
     np.testing.assert_allclose(one[0], full[2], rtol=1e-12, atol=1e-14)
+
+
+def test_cross_entropy_textbook():
+    z = np.random.default_rng(3).standard_normal((4, 5, 9))
+    t = np.random.default_rng(4).integers(0, 9, size=(4, 5))
+    loss, d = stack.cross_entropy(z, t)
+    p = np.exp(z) / np.exp(z).sum(-1, keepdims=True)
+    ref = -np.mean(np.log(np.take_along_axis(p, t[..., None], -1)))
+    np.testing.assert_allclose(loss, ref, rtol=1e-13)
+    np.testing.assert_allclose(d.sum(-1), 0.0, atol=1e-15)        # each row sums to 0
+    np.testing.assert_allclose((d * 20).sum(-1), 0.0, atol=1e-13)
+
+
+def _fd(fn, x, eps=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        mi = it.multi_index
+        old = x[mi]
+        x[mi] = old + eps
+        lp = fn()
+        x[mi] = old - eps
+        lm = fn()
+        x[mi] = old
+        g[mi] = (lp - lm) / (2 * eps)
+    return g
+
+
+def test_train_step_central_fd():
+    """Every parameter of a tiny 2-layer model against central differences of the loss."""
+    C, H, F, V, L = 8, 2, 12, 11, 2
+    cfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+    N = C // H
+    for use_ln0 in (False, True):
+        m = synth.stack_model(C, H, F, V, L, (4, 4, 4, 4), seed=6, perturbed=True, std=0.4,
+                              use_ln0=use_ln0)
+        m = stack._f64(m)
+        # tiny head size: the oracle's recurrence is N-generic
+        tok = synth.token_ids(2, 3, V, seed=1)
+        tgt = synth.token_ids(2, 3, V, seed=2)
+        loss, G = stack.train_step(m, cfg, tok, tgt)
+        fn = lambda: stack.train_step(m, cfg, tok, tgt)[0]
+        checks = [("emb", m["emb"], G["emb"]), ("head", m["head"], G["head"]),
+                  ("ln_out_w", m["ln_out_w"], G["ln_out_w"]), ("ln_out_b", m["ln_out_b"], G["ln_out_b"])]
+        if use_ln0:
+            checks += [("ln0_w", m["ln0_w"], G["ln0_w"]), ("ln0_b", m["ln0_b"], G["ln0_b"])]
+        for l in range(L):
+            bp, gb = m["blocks"][l], G["blocks"][l]
+            for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
+                checks.append((f"{k}[{l}]", bp[k], gb[k]))
+            for k in bp["tm"]:
+                checks.append((f"tm.{k}[{l}]", bp["tm"][k], gb["tm"][k]))
+        for name, p, g in checks:
+            fd = _fd(fn, p)
+            err = np.max(np.abs(fd - g)) / max(np.max(np.abs(fd)), 1e-30)
+            assert err < 1e-5, (use_ln0, name, err)
