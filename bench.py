@@ -10,6 +10,9 @@ Prints ONE JSON line.  Workloads (--workload):
              LoRA ranks w/a/v/g = 64/64/32/128, layer > 0, fp32 (tokens/s)
   wkv7_long  WKV7 forward+backward, B=4 T=8192 H=32 N=64, bf16 token
              tensors, fp32 state, checkpointed backward (tokens/s)
+  train      full training step: 24 blocks C=1024 H=16 FFN 4096, vocab
+             65536, B=4 T=2048, embedding, LM head, fused CE, forward +
+             backward; GEMMs in fp32 on the matrix cores (tokens/s)
 A step is one pass of the whole workload over one batch of seeded synthetic
 inputs that are resident in HBM before timing starts.  Steps are timed with
 HIP events on the stream the library launches on, bracketed by device
@@ -248,7 +251,65 @@ def setup_decode():
                 extra=lambda v: {"tokens_per_s": round(v * B, 1)})
 
 
-WORKLOADS = {"decode": setup_decode, "timemix": setup_timemix, "wkv7_long": setup_wkv7_long}
+def setup_train():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    L, C, H, F, V, B, T = 24, 1024, 16, 4096, 65536, 4, 2048
+    ranks = (64, 64, 32, 128)
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=0, use_ln0=False)
+    dev = torch.device("cuda")
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    w = {k: d(v) for k, v in m.items() if k != "blocks"}
+    w["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
+                    for k, v in b.items()} for b in m["blocks"]]
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=0), w)
+    grads = binding.TrainGrads(dm)
+    tok = synth.token_ids(B, T + 1, V, seed=0, name="train_tokens")
+    x = torch.from_numpy(np.ascontiguousarray(tok[:, :-1])).to(dev)
+    y = torch.from_numpy(np.ascontiguousarray(tok[:, 1:])).to(dev)
+    loss = torch.empty(1, device=dev)
+    ws = torch.empty(binding.rwkv7_train_workspace_bytes(dm, B, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws)
+
+    # dominant kernels: the fp32 matrix-core GEMMs; the timed one is the
+    # channel-mix key projection [8192][1024] . [1024][4096]
+    A = torch.randn(B * T, C, device=dev)
+    Wk = w["blocks"][0]["cm_Wk"]
+    out = torch.empty(B * T, F, device=dev)
+
+    def dom():
+        binding.wkv7_gemm_f32(A, Wk, out)
+
+    roof = dict(kernel="gemm_f32 (X[8192][1024] . Wk[1024][4096])", bound="mfma",
+                work=2.0 * B * T * C * F, unit="TFLOP/s", peak=PEAK["mfma_fp32"][0], fn=dom,
+                key="gemm_f32_c1024_f4096", src=["rwkv_linear_attention_wkv7_amd/csrc/gemm.hip"])
+
+    def cpu():
+        from oracle import stack
+        from oracle import wkv7 as ow
+        Ts = 64
+        ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+        t0 = time.perf_counter()
+        stack.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1])
+        dt = time.perf_counter() - t0
+        return dict(value=Ts / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"1 sequence x {Ts} tokens of the same model (f64 forward+backward), "
+                           f"{dt:.1f} s")
+
+    cfg = {"workload": "RWKV-7 training step (24 blocks, LM head, log-softmax CE) forward+backward",
+           "n_layer": L, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
+           "lora_ranks_w_a_v_g": list(ranks), "B": B, "T": T, "gemm": "fp32 matrix cores",
+           "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="f32", config=cfg, roof=roof,
+                cpu=cpu, extra=lambda v: {"loss": round(float(loss.item()), 5)})
+
+
+WORKLOADS = {"decode": setup_decode, "timemix": setup_timemix, "wkv7_long": setup_wkv7_long,
+             "train": setup_train}
 
 
 def main():
