@@ -12,7 +12,8 @@ Prints ONE JSON line.  Workloads (--workload):
              tensors, fp32 state, checkpointed backward (tokens/s)
   train      full training step: 24 blocks C=1024 H=16 FFN 4096, vocab
              65536, B=4 T=2048, embedding, LM head, fused CE, forward +
-             backward; GEMMs in fp32 on the matrix cores (tokens/s)
+             backward; GEMMs with bf16 operands and fp32 accumulation,
+             recurrence and elementwise steps fp32 (tokens/s)
 A step is one pass of the whole workload over one batch of seeded synthetic
 inputs that are resident in HBM before timing starts.  Steps are timed with
 HIP events on the stream the library launches on, bracketed by device
@@ -264,7 +265,8 @@ def setup_train():
     w = {k: d(v) for k, v in m.items() if k != "blocks"}
     w["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
                     for k, v in b.items()} for b in m["blocks"]]
-    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=0), w)
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=0,
+                                  gemm_dtype="bf16"), w)
     grads = binding.TrainGrads(dm)
     tok = synth.token_ids(B, T + 1, V, seed=0, name="train_tokens")
     x = torch.from_numpy(np.ascontiguousarray(tok[:, :-1])).to(dev)
@@ -275,18 +277,18 @@ def setup_train():
     def step():
         binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws)
 
-    # dominant kernels: the fp32 matrix-core GEMMs; the timed one is the
+    # dominant kernels: the bf16 matrix-core GEMMs; the timed one is the
     # channel-mix key projection [8192][1024] . [1024][4096]
     A = torch.randn(B * T, C, device=dev)
     Wk = w["blocks"][0]["cm_Wk"]
     out = torch.empty(B * T, F, device=dev)
 
     def dom():
-        binding.wkv7_gemm_f32(A, Wk, out)
+        binding.wkv7_gemm_bf16(A, Wk, out)
 
-    roof = dict(kernel="gemm_f32 (X[8192][1024] . Wk[1024][4096])", bound="mfma",
-                work=2.0 * B * T * C * F, unit="TFLOP/s", peak=PEAK["mfma_fp32"][0], fn=dom,
-                key="gemm_f32_c1024_f4096", src=["rwkv_linear_attention_wkv7_amd/csrc/gemm.hip"])
+    roof = dict(kernel="gemm_bf16 (X[8192][1024] . Wk[1024][4096])", bound="mfma",
+                work=2.0 * B * T * C * F, unit="TFLOP/s", peak=PEAK["mfma_bf16"][0], fn=dom,
+                key="gemm_bf16_c1024_f4096", src=["rwkv_linear_attention_wkv7_amd/csrc/gemm.hip"])
 
     def cpu():
         from oracle import stack
@@ -302,10 +304,10 @@ def setup_train():
 
     cfg = {"workload": "RWKV-7 training step (24 blocks, LM head, log-softmax CE) forward+backward",
            "n_layer": L, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
-           "lora_ranks_w_a_v_g": list(ranks), "B": B, "T": T, "gemm": "fp32 matrix cores",
+           "lora_ranks_w_a_v_g": list(ranks), "B": B, "T": T, "gemm": "bf16 operands, fp32 accumulation (matrix cores)",
            "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
-    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="f32", config=cfg, roof=roof,
-                cpu=cpu, extra=lambda v: {"loss": round(float(loss.item()), 5)})
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="bf16 GEMM / f32", config=cfg,
+                roof=roof, cpu=cpu, extra=lambda v: {"loss": round(float(loss.item()), 5)})
 
 
 WORKLOADS = {"decode": setup_decode, "timemix": setup_timemix, "wkv7_long": setup_wkv7_long,

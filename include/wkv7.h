@@ -186,9 +186,14 @@ int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
 
 /* RWKV-7 stack geometry: n_layer blocks of width C = H*N (N = 64), channel-mix
  * width F, vocabulary V, time-mix LoRA ranks, and whether layer 0 applies the
- * pre-norm ln0 to the embedding. */
+ * pre-norm ln0 to the embedding.  gemm_dtype selects the precision of the
+ * products in every projection, LoRA, channel-mix and head GEMM: WKV7_F32
+ * (fp32 operands) or WKV7_BF16 (operands rounded to bf16 to nearest even,
+ * fp32 accumulation, as wkv7_gemm_bf16).  Tensors stay fp32 in memory either
+ * way; the WKV7 recurrence and every elementwise step are fp32. */
 typedef struct {
   int n_layer, C, H, N, F, V, Dw, Da, Dv, Dg, use_ln0;
+  int gemm_dtype;
 } rwkv7_config;
 
 /* One block: LayerNorms, time-mix weights (layer_id = block index) and the
@@ -280,6 +285,18 @@ int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
  */
 int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float *A, int lda,
                   const float *B, int ldb, float *C, int ldc, float beta, hipStream_t stream);
+
+/*
+ * Same contraction, layouts, requirements and errors as wkv7_gemm_f32, with
+ * the operands rounded to bf16 (round to nearest even) as they are staged and
+ * the products accumulated in fp32 on the bf16 matrix cores
+ * (v_mfma_f32_16x16x32_bf16).  A, B and C stay fp32 in memory.  This is the
+ * bf16-GEMM precision the full training-step configuration names for the
+ * projections; the pages' own GEMMs are fp32 SGEMM.
+ */
+int wkv7_gemm_bf16(int transA, int transB, int M, int N, int K, const float *A, int lda,
+                   const float *B, int ldb, float *C, int ldc, float beta,
+                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ and cfg = dict(C, H, F, V, n_layer).
 import numpy as np
 
 from . import timemix as tm
+from .precision import mm
 
 LN_EPS = 1e-5
 
@@ -34,15 +35,15 @@ def layernorm(x, w, b, eps=LN_EPS):
     return (x - mean) / np.sqrt(var + eps) * w + b
 
 
-def channel_mix(mu_k, Wk, Wv, x, x_prev=None):
-    """sh = x + (shift(x) - x) mu_k;  out = relu(sh @ Wk)^2 @ Wv."""
+def channel_mix(mu_k, Wk, Wv, x, x_prev=None, gemm="f64"):
+    """sh = x + (shift(x) - x) mu_k;  out = relu(sh Wk)^2 Wv (products per `gemm`)."""
     x = np.asarray(x, np.float64)
     B, T, C = x.shape
     first = np.zeros((B, 1, C)) if x_prev is None else np.asarray(x_prev, np.float64)[:, None, :]
     prev = np.concatenate([first, x[:, :-1]], axis=1)
     sh = x + (prev - x) * mu_k
-    ka = np.maximum(sh @ Wk, 0.0) ** 2
-    return ka @ Wv
+    ka = np.maximum(mm(sh, Wk, gemm), 0.0) ** 2
+    return mm(ka, Wv, gemm)
 
 
 def _f64(m):
@@ -123,20 +124,20 @@ def layernorm_backward(x, w, dy, eps=LN_EPS):
     return dx, (dy * nhat).reshape(-1, C).sum(0), dy.reshape(-1, C).sum(0)
 
 
-def channel_mix_backward(mu_k, Wk, Wv, x, dout, x_prev=None):
+def channel_mix_backward(mu_k, Wk, Wv, x, dout, x_prev=None, gemm="f64"):
     """Gradients of channel_mix: returns dx, dx_prev, dmu_k, dWk, dWv."""
     x = np.asarray(x, np.float64)
     B, T, C = x.shape
     first = np.zeros((B, 1, C)) if x_prev is None else np.asarray(x_prev, np.float64)[:, None, :]
     prev = np.concatenate([first, x[:, :-1]], axis=1)
     sh = x + (prev - x) * mu_k
-    fk = sh @ Wk
+    fk = mm(sh, Wk, gemm)
     ka = np.maximum(fk, 0.0) ** 2
-    dka = dout @ Wv.T
-    dWv = ka.reshape(-1, ka.shape[-1]).T @ dout.reshape(-1, C)
+    dka = mm(dout, Wv.T, gemm)
+    dWv = mm(ka.reshape(-1, ka.shape[-1]).T, dout.reshape(-1, C), gemm)
     dfk = dka * 2.0 * np.maximum(fk, 0.0)
-    dsh = dfk @ Wk.T
-    dWk = sh.reshape(-1, C).T @ dfk.reshape(-1, dfk.shape[-1])
+    dsh = mm(dfk, Wk.T, gemm)
+    dWk = mm(sh.reshape(-1, C).T, dfk.reshape(-1, dfk.shape[-1]), gemm)
     dmu = (dsh * (prev - x)).reshape(-1, C).sum(0)
     dx = dsh * (1.0 - mu_k)
     dprev = dsh * mu_k
@@ -157,11 +158,13 @@ def cross_entropy(logits, targets):
     return loss, p / n
 
 
-def train_step(model, cfg, tokens, targets):
+def train_step(model, cfg, tokens, targets, gemm="f64"):
     """Loss and gradients of every parameter for one batch (zero initial state).
 
     Returns (loss, grads) with grads mirroring the model dict (blocks[l]['tm']
-    holds the time-mix gradients).
+    holds the time-mix gradients).  gemm: operand precision of every
+    projection, LoRA, channel-mix and head product ("f64" or "bf16", see
+    oracle.precision).
     """
     m = _f64(model)
     tokens = np.asarray(tokens)
@@ -176,26 +179,26 @@ def train_step(model, cfg, tokens, targets):
     v_first = None
     for l, bp in enumerate(m["blocks"]):
         h1 = layernorm(x, bp["ln1_w"], bp["ln1_b"])
-        out, c = tm.forward(bp["tm"], h1, H, l, v_first=v_first)
+        out, c = tm.forward(bp["tm"], h1, H, l, v_first=v_first, gemm=gemm)
         if l == 0:
             v_first = c["v_first"]
         x1 = x + out
         h2 = layernorm(x1, bp["ln2_w"], bp["ln2_b"])
-        x = x1 + channel_mix(bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], h2)
+        x = x1 + channel_mix(bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], h2, gemm=gemm)
         caches.append(dict(h1=h1, c=c, x1=x1, h2=h2))
         xs.append(x)
     hN = layernorm(x, m["ln_out_w"], m["ln_out_b"])
-    loss, dlog = cross_entropy(hN @ m["head"], targets)
+    loss, dlog = cross_entropy(mm(hN, m["head"], gemm), targets)
 
-    G = {"head": hN.reshape(-1, hN.shape[-1]).T @ dlog.reshape(-1, dlog.shape[-1])}
-    dx, G["ln_out_w"], G["ln_out_b"] = layernorm_backward(x, m["ln_out_w"], dlog @ m["head"].T)
+    G = {"head": mm(hN.reshape(-1, hN.shape[-1]).T, dlog.reshape(-1, dlog.shape[-1]), gemm)}
+    dx, G["ln_out_w"], G["ln_out_b"] = layernorm_backward(x, m["ln_out_w"], mm(dlog, m["head"].T, gemm))
     G["blocks"] = [None] * len(m["blocks"])
     dvf = np.zeros_like(x)
     for l in range(len(m["blocks"]) - 1, -1, -1):
         bp, cc = m["blocks"][l], caches[l]
         gb = {}
         dh2, _, gb["cm_mu_k"], gb["cm_Wk"], gb["cm_Wv"] = channel_mix_backward(
-            bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], cc["h2"], dx)
+            bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], cc["h2"], dx, gemm=gemm)
         d1, gb["ln2_w"], gb["ln2_b"] = layernorm_backward(cc["x1"], bp["ln2_w"], dh2)
         dx1 = dx + d1
         gt, dh1, _, dvf_out, _ = tm.backward(bp["tm"], cc["c"], dx1,

@@ -25,6 +25,7 @@ Parameter names (dict keys):
 import numpy as np
 
 from . import wkv7
+from .precision import mm
 
 # Decay coefficient exp(-0.606531 * sigmoid(.)) as written on the timemix.cu
 # page (RWDECAY_COEFF); the model.rs page uses 1/sqrt(e), 3.4e-7 away.
@@ -50,8 +51,11 @@ def _prev(x, x_prev):
     return np.concatenate([first, x[:, :-1, :]], axis=1)
 
 
-def forward(p, x, H, layer_id, x_prev=None, v_first=None, s0=None):
+def forward(p, x, H, layer_id, x_prev=None, v_first=None, s0=None, gemm="f64"):
     """Time-mix forward.  Returns (out [B][T][C], cache).
+
+    gemm: operand precision of the projections and LoRA products ("f64" or
+    "bf16", see oracle.precision); the backward of this cache uses the same.
 
     cache holds every intermediate (f64) plus 'v_first' (the published value
     for layer 0, the input otherwise) and 'sT' (final WKV state).
@@ -65,19 +69,19 @@ def forward(p, x, H, layer_id, x_prev=None, v_first=None, s0=None):
     d = prev - x
     xs = {c: x + d * p["mu_" + c] for c in MIX}                      # k_tokenshift
 
-    r = xs["r"] @ p["Wr"]
-    k = xs["k"] @ p["Wk"]
-    v = xs["v"] @ p["Wv"]
-    lw = xs["w"] @ p["W1"]
+    r = mm(xs["r"], p["Wr"], gemm)
+    k = mm(xs["k"], p["Wk"], gemm)
+    v = mm(xs["v"], p["Wv"], gemm)
+    lw = mm(xs["w"], p["W1"], gemm)
     tw = np.tanh(lw)                                                 # k_tanh
-    ow = tw @ p["W2"]
+    ow = mm(tw, p["W2"], gemm)
     sigw = sigmoid(p["w0"] + ow)                                     # k_decay
     w = np.exp(-DECAY * sigw)
-    la = xs["a"] @ p["A1"]
-    a = sigmoid(p["a0"] + la @ p["A2"])                              # k_bias_sigmoid
-    lg = xs["g"] @ p["G1"]
+    la = mm(xs["a"], p["A1"], gemm)
+    a = sigmoid(p["a0"] + mm(la, p["A2"], gemm))                     # k_bias_sigmoid
+    lg = mm(xs["g"], p["G1"], gemm)
     sg = sigmoid(lg)                                                 # k_sigmoid
-    g = sg @ p["G2"]
+    g = mm(sg, p["G2"], gemm)
 
     tk = (k * p["k_k"]).reshape(B, T, H, N)                          # k_tk
     nrm = np.sqrt(np.sum(tk * tk, axis=-1, keepdims=True))
@@ -90,8 +94,8 @@ def forward(p, x, H, layer_id, x_prev=None, v_first=None, s0=None):
         lv = nu = None
     else:                                                            # k_vres
         vf = np.asarray(v_first, np.float64)
-        lv = xs["v"] @ p["V1"]
-        nu = sigmoid(p["v0"] + lv @ p["V2"])
+        lv = mm(xs["v"], p["V1"], gemm)
+        nu = sigmoid(p["v0"] + mm(lv, p["V2"], gemm))
         vmod = v + (vf - v) * nu
 
     kk_c = kk.reshape(B, T, C)
@@ -108,12 +112,12 @@ def forward(p, x, H, layer_id, x_prev=None, v_first=None, s0=None):
     alpha = np.sum(hv(r) * hv(kmod) * p["r_k"].reshape(H, N), axis=-1)   # k_bonus
     yb = ygn + (alpha[..., None] * hv(vmod)).reshape(B, T, C)
     tg = yb * g                                                      # k_mul
-    out = tg @ p["Wo"]
+    out = mm(tg, p["Wo"], gemm)
 
     cache = dict(x=x, prev=prev, xs=xs, r=r, k=k, v=v, lw=lw, tw=tw, sigw=sigw, w=w,
                  la=la, a=a, sg=sg, g=g, tk=tk, nrm=nrm, kk=kk, kmod=kmod, vmod=vmod,
                  lv=lv, nu=nu, v_first=vf, A=A, Bv=Bv, y=y, sT=sT, nhat=nhat, rstd=rstd,
-                 alpha=alpha, yb=yb, tg=tg, s0=s0, H=H, N=N, layer_id=layer_id)
+                 alpha=alpha, yb=yb, tg=tg, s0=s0, H=H, N=N, layer_id=layer_id, gemm=gemm)
     return out, cache
 
 
@@ -122,9 +126,9 @@ def _colsum(z):
     return z.reshape(-1, z.shape[-1]).sum(axis=0)
 
 
-def _wgrad(xin, dout):
-    """dW = x^T dy over all tokens, for y = x @ W."""
-    return xin.reshape(-1, xin.shape[-1]).T @ dout.reshape(-1, dout.shape[-1])
+def _wgrad(xin, dout, gemm):
+    """dW = x^T dy over all tokens, for y = x W."""
+    return mm(xin.reshape(-1, xin.shape[-1]).T, dout.reshape(-1, dout.shape[-1]), gemm)
 
 
 def backward(p, cache, dout, dsT=None, dv_first_in=None):
@@ -138,6 +142,7 @@ def backward(p, cache, dout, dsT=None, dv_first_in=None):
     """
     p = _f64(p)
     c = cache
+    gemm = c.get("gemm", "f64")
     B, T, C = c["x"].shape
     H, N, L = c["H"], c["N"], c["layer_id"]
     hv = lambda z: z.reshape(B, T, H, N)
@@ -145,8 +150,8 @@ def backward(p, cache, dout, dsT=None, dv_first_in=None):
     G = {}
 
     # out = tg @ Wo
-    dtg = dout @ p["Wo"].T
-    G["Wo"] = _wgrad(c["tg"], dout)
+    dtg = mm(dout, p["Wo"].T, gemm)
+    G["Wo"] = _wgrad(c["tg"], dout, gemm)
     # tg = yb * g                                                     (k_split)
     dyb = dtg * c["g"]
     dg = dtg * c["yb"]
@@ -205,43 +210,43 @@ def backward(p, cache, dout, dsT=None, dv_first_in=None):
         dv_first_out = dvmod * nu
         dpre = dvmod * (vf - v) * nu * (1.0 - nu)
         G["v0"] = _colsum(dpre)
-        dlv = dpre @ p["V2"].T
-        G["V2"] = _wgrad(c["lv"], dpre)
-        dxv_extra = dlv @ p["V1"].T
-        G["V1"] = _wgrad(c["xs"]["v"], dlv)
+        dlv = mm(dpre, p["V2"].T, gemm)
+        G["V2"] = _wgrad(c["lv"], dpre, gemm)
+        dxv_extra = mm(dlv, p["V1"].T, gemm)
+        G["V1"] = _wgrad(c["xs"]["v"], dlv, gemm)
 
     # a = sigmoid(a0 + (xa @ A1) @ A2)                                 (k_avec_bwd)
     dpre_a = da * a * (1.0 - a)
     G["a0"] = _colsum(dpre_a)
-    dla = dpre_a @ p["A2"].T
-    G["A2"] = _wgrad(c["la"], dpre_a)
-    dxa = dla @ p["A1"].T
-    G["A1"] = _wgrad(c["xs"]["a"], dla)
+    dla = mm(dpre_a, p["A2"].T, gemm)
+    G["A2"] = _wgrad(c["la"], dpre_a, gemm)
+    dxa = mm(dla, p["A1"].T, gemm)
+    G["A1"] = _wgrad(c["xs"]["a"], dla, gemm)
 
     # w = exp(-DECAY * sigmoid(w0 + tanh(xw @ W1) @ W2))               (k_wdecay_bwd)
     sigw = c["sigw"]
     dpre_w = dw * c["w"] * (-DECAY) * sigw * (1.0 - sigw)
     G["w0"] = _colsum(dpre_w)
-    dtw = dpre_w @ p["W2"].T
-    G["W2"] = _wgrad(c["tw"], dpre_w)
+    dtw = mm(dpre_w, p["W2"].T, gemm)
+    G["W2"] = _wgrad(c["tw"], dpre_w, gemm)
     dlw = dtw * (1.0 - c["tw"] ** 2)                                 # k_tanhderiv
-    dxw = dlw @ p["W1"].T
-    G["W1"] = _wgrad(c["xs"]["w"], dlw)
+    dxw = mm(dlw, p["W1"].T, gemm)
+    G["W1"] = _wgrad(c["xs"]["w"], dlw, gemm)
 
     # g = sigmoid(xg @ G1) @ G2
-    dsg = dg @ p["G2"].T
-    G["G2"] = _wgrad(c["sg"], dg)
+    dsg = mm(dg, p["G2"].T, gemm)
+    G["G2"] = _wgrad(c["sg"], dg, gemm)
     dlg = dsg * c["sg"] * (1.0 - c["sg"])                            # k_sigderiv
-    dxg = dlg @ p["G1"].T
-    G["G1"] = _wgrad(c["xs"]["g"], dlg)
+    dxg = mm(dlg, p["G1"].T, gemm)
+    G["G1"] = _wgrad(c["xs"]["g"], dlg, gemm)
 
     # r, k, v projections
-    dxr = dr @ p["Wr"].T
-    G["Wr"] = _wgrad(c["xs"]["r"], dr)
-    dxk = dk @ p["Wk"].T
-    G["Wk"] = _wgrad(c["xs"]["k"], dk)
-    dxv = dv @ p["Wv"].T + dxv_extra
-    G["Wv"] = _wgrad(c["xs"]["v"], dv)
+    dxr = mm(dr, p["Wr"].T, gemm)
+    G["Wr"] = _wgrad(c["xs"]["r"], dr, gemm)
+    dxk = mm(dk, p["Wk"].T, gemm)
+    G["Wk"] = _wgrad(c["xs"]["k"], dk, gemm)
+    dxv = mm(dv, p["Wv"].T, gemm) + dxv_extra
+    G["Wv"] = _wgrad(c["xs"]["v"], dv, gemm)
 
     # token shift: xs_c = x (1 - mu_c) + prev mu_c                     (k_tokenshift_bwd)
     dxs = dict(r=dxr, w=dxw, k=dxk, v=dxv, a=dxa, g=dxg)

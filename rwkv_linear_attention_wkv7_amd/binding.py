@@ -34,7 +34,7 @@ class TmGrads(ctypes.Structure):
 
 class Rwkv7Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layer", "C", "H", "N", "F", "V", "Dw", "Da", "Dv",
-                                            "Dg", "use_ln0")]
+                                            "Dg", "use_ln0", "gemm_dtype")]
 
 
 class Rwkv7Block(ctypes.Structure):
@@ -98,6 +98,8 @@ def lib():
         L.timemix_backward.restype = _i
         L.wkv7_gemm_f32.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp]
         L.wkv7_gemm_f32.restype = _i
+        L.wkv7_gemm_bf16.argtypes = L.wkv7_gemm_f32.argtypes
+        L.wkv7_gemm_bf16.restype = _i
         cp = ctypes.POINTER(Rwkv7Config)
         L.rwkv7_decode_workspace_bytes.argtypes = [cp, _i]
         L.rwkv7_decode_workspace_bytes.restype = _sz
@@ -307,8 +309,7 @@ def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None
 
 
 # ------------------------------------------------------------------ GEMM --
-def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
-    """C = op(A) op(B) + beta C on the matrix cores (fp32, row-major)."""
+def _gemm(fn, A, B, C, transA, transB, beta):
     M, K = (A.shape[1], A.shape[0]) if transA else tuple(A.shape)
     K2, N = (B.shape[1], B.shape[0]) if transB else tuple(B.shape)
     if K != K2:
@@ -318,9 +319,19 @@ def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
     if C is None:
         C = torch.empty((M, N), device=A.device, dtype=torch.float32)
     _need(C, (M, N), torch.float32, "C")
-    _check(lib().wkv7_gemm_f32(int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B),
-                               B.shape[1], _p(C), N, beta, _stream()))
+    _check(fn(int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B), B.shape[1], _p(C), N,
+              beta, _stream()))
     return C
+
+
+def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
+    """C = op(A) op(B) + beta C on the matrix cores (fp32, row-major)."""
+    return _gemm(lib().wkv7_gemm_f32, A, B, C, transA, transB, beta)
+
+
+def wkv7_gemm_bf16(A, B, C=None, transA=False, transB=False, beta=0.0):
+    """As wkv7_gemm_f32 with bf16-rounded operands and fp32 accumulation."""
+    return _gemm(lib().wkv7_gemm_bf16, A, B, C, transA, transB, beta)
 
 
 # ---------------------------------------------------------- decode stack --
@@ -329,11 +340,16 @@ class DecodeModel:
     point at them (the structs hold raw pointers, so the tensors are kept)."""
 
     def __init__(self, cfg, weights):
-        """cfg: dict n_layer, C, H, F, V, ranks=(Dw, Da, Dv, Dg), use_ln0.
+        """cfg: dict n_layer, C, H, F, V, ranks=(Dw, Da, Dv, Dg), use_ln0,
+        gemm_dtype ('f32' default, or 'bf16': bf16 operands, fp32 accumulation).
         weights: dict of device tensors as laid out by synth.stack_model."""
         L, C, H, F, V = cfg["n_layer"], cfg["C"], cfg["H"], cfg["F"], cfg["V"]
         Dw, Da, Dv, Dg = cfg["ranks"]
-        self.cfg = Rwkv7Config(L, C, H, 64, F, V, Dw, Da, Dv, Dg, int(cfg.get("use_ln0", 1)))
+        gd = cfg.get("gemm_dtype", "f32")
+        if gd not in ("f32", "bf16"):
+            raise ValueError(f"gemm_dtype must be 'f32' or 'bf16', not {gd!r}")
+        self.cfg = Rwkv7Config(L, C, H, 64, F, V, Dw, Da, Dv, Dg, int(cfg.get("use_ln0", 1)),
+                               1 if gd == "bf16" else 0)
         self.w = weights
         blocks = (Rwkv7Block * L)()
         for l, bw in enumerate(weights["blocks"]):

@@ -284,7 +284,7 @@ int check_weights(const tm_shape* s, const tm_weights* W) {
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
-                    float out_beta = 0.f) {
+                    float out_beta = 0.f, int prec = GEMM_F32) {
   const int BT = B * T, C = s->C;
   TmFwd p;
   memset(&p, 0, sizeof(p));
@@ -310,7 +310,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     g.p[0] = prob(BT, C, C, m.xr, C, W->Wr, C, m.r, C, EPI_NONE);
     g.p[1] = prob(BT, C, C, m.xk, C, W->Wk, C, m.k, C, EPI_NONE);
     g.p[2] = prob(BT, C, C, m.xv, C, W->Wv, C, m.v, C, EPI_NONE);
-    HIPCHK(gemm_f32_batch(false, false, g, st), "r/k/v proj");
+    HIPCHK(gemm_batch(prec, false, false, g, st), "r/k/v proj");
   }
   {  // LoRA down-projections (tanh for w, sigmoid for g): one launch
     GemmBatch g;
@@ -319,7 +319,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     g.p[1] = prob(BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, EPI_NONE);
     g.p[2] = prob(BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, EPI_SIGMOID);
     if (s->layer_id > 0) g.p[g.count++] = prob(BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, EPI_NONE);
-    HIPCHK(gemm_f32_batch(false, false, g, st), "lora down");
+    HIPCHK(gemm_batch(prec, false, false, g, st), "lora down");
   }
   {  // LoRA up-projections: one launch
     GemmBatch g;
@@ -328,7 +328,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     g.p[1] = prob(BT, C, s->Da, m.la, s->Da, W->A2, C, m.oa, C, EPI_NONE);
     g.p[2] = prob(BT, C, s->Dg, m.sg, s->Dg, W->G2, C, m.g, C, EPI_NONE);
     if (s->layer_id > 0) g.p[g.count++] = prob(BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, EPI_NONE);
-    HIPCHK(gemm_f32_batch(false, false, g, st), "lora up");
+    HIPCHK(gemm_batch(prec, false, false, g, st), "lora up");
   }
   HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
   if (decode)
@@ -338,7 +338,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
                                m.ckpt, st), "wkv7 forward");
   HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
-  HIPCHK(gemm_f32_run(false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
+  HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;
 }
 
@@ -351,12 +351,12 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                      const float* x_prev, const float* v_first, const float* s0, const float* dout,
                      const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
                      float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
-                     float* ds0, hipStream_t st) {
+                     float* ds0, hipStream_t st, int prec = GEMM_F32) {
   const int BT = B * T, C = s->C, L = s->layer_id;
 
   // output projection
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
+  HIPCHK(gemm_run(prec, false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
 
   TmBwd p;
   memset(&p, 0, sizeof(p));
@@ -388,34 +388,34 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
   float* sk = bb.splitk;
   // a: a = sigmoid(a0 + (xa A1) A2)
-  HIPCHK(gemm_f32_run(false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
-  HIPCHK(gemm_f32_run(true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
-  HIPCHK(gemm_f32_run(true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
+  HIPCHK(gemm_run(prec, false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
+  HIPCHK(gemm_run(prec, true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
+  HIPCHK(gemm_run(prec, false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
+  HIPCHK(gemm_run(prec, true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
   // w: w = exp(-c sigmoid(w0 + tanh(xw W1) W2))
-  HIPCHK(gemm_f32_run(false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
-  HIPCHK(gemm_f32_run(true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
-  HIPCHK(gemm_f32_run(true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
+  HIPCHK(gemm_run(prec, false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
+  HIPCHK(gemm_run(prec, true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
+  HIPCHK(gemm_run(prec, false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
+  HIPCHK(gemm_run(prec, true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
   // g: g = sigmoid(xg G1) G2
-  HIPCHK(gemm_f32_run(false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
-  HIPCHK(gemm_f32_run(true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
-  HIPCHK(gemm_f32_run(false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
-  HIPCHK(gemm_f32_run(true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
+  HIPCHK(gemm_run(prec, false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
+  HIPCHK(gemm_run(prec, true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
+  HIPCHK(gemm_run(prec, false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
+  HIPCHK(gemm_run(prec, true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
   // value residual LoRA (layer > 0)
   if (L > 0) {
-    HIPCHK(gemm_f32_run(false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
-    HIPCHK(gemm_f32_run(true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
-    HIPCHK(gemm_f32_run(false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
-    HIPCHK(gemm_f32_run(true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
+    HIPCHK(gemm_run(prec, false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
+    HIPCHK(gemm_run(prec, true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
+    HIPCHK(gemm_run(prec, false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
+    HIPCHK(gemm_run(prec, true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
   }
   // r, k, v projections
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
-  HIPCHK(gemm_f32_run(false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
-  HIPCHK(gemm_f32_run(true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
+  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
+  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
+  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
 
   HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
   const int nblk = tm_num_token_blocks(BT);
@@ -537,9 +537,9 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
 }
 
 // ----------------------------------------------------------------- GEMM --
-extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float* A, int lda,
-                             const float* B, int ldb, float* C, int ldc, float beta,
-                             hipStream_t stream) {
+namespace {
+int gemm_abi(int prec, int transA, int transB, int M, int N, int K, const float* A, int lda,
+             const float* B, int ldb, float* C, int ldc, float beta, hipStream_t stream) {
   g_err[0] = 0;
   if (M < 1 || N < 1 || K < 1) return fail(WKV7_EINVAL, "M, N, K must be >= 1");
   CHK(check_f32_ptr(A, "A", true));
@@ -549,10 +549,23 @@ extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const 
   if (a_inner % 4 || b_inner % 4 || lda % 4 || ldb % 4)
     return fail(WKV7_EINVAL, "contiguous GEMM dimensions and leading dims must be multiples of 4");
   if (lda < a_inner || ldb < b_inner || ldc < N) return fail(WKV7_EINVAL, "leading dimension too small");
-  HIPCHK(gemm_f32_run(transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr, 1,
-                      nullptr, stream),
+  HIPCHK(gemm_run(prec, transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr,
+                  1, nullptr, stream),
          "gemm launch");
   return WKV7_OK;
+}
+}  // namespace
+
+extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float* A, int lda,
+                             const float* B, int ldb, float* C, int ldc, float beta,
+                             hipStream_t stream) {
+  return gemm_abi(GEMM_F32, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, stream);
+}
+
+extern "C" int wkv7_gemm_bf16(int transA, int transB, int M, int N, int K, const float* A,
+                              int lda, const float* B, int ldb, float* C, int ldc, float beta,
+                              hipStream_t stream) {
+  return gemm_abi(GEMM_BF16, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, stream);
 }
 
 // --------------------------------------------------------- decode stack --
@@ -566,6 +579,8 @@ struct DecodeBufs {
 int check_cfg(const rwkv7_config* c, int B) {
   if (!c) return fail(WKV7_EINVAL, "config is NULL");
   if (c->N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", c->N);
+  if (c->gemm_dtype != WKV7_F32 && c->gemm_dtype != WKV7_BF16)
+    return fail(WKV7_EINVAL, "gemm_dtype must be WKV7_F32 or WKV7_BF16");
   if (c->H < 1 || c->C != c->H * c->N) return fail(WKV7_EINVAL, "C=%d must equal H*N", c->C);
   if (c->C > stk_max_layernorm_width()) return fail(WKV7_EINVAL, "C=%d above the supported %d", c->C, stk_max_layernorm_width());
   if (c->n_layer < 1 || B < 1) return fail(WKV7_EINVAL, "n_layer and B must be >= 1");
@@ -601,6 +616,7 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
                                  hipStream_t st) {
   g_err[0] = 0;
   CHK(check_cfg(cfg, B));
+  const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
   if (!M || !M->blocks) return fail(WKV7_EINVAL, "model or model->blocks is NULL");
   CHK(check_f32_ptr(M->emb, "emb", true));
   CHK(check_f32_ptr(M->head, "head", true));
@@ -639,14 +655,14 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
     float* ast = att_state + (size_t)l * B * H * NN;
     float* fxp = ffn_x_prev + (size_t)l * BC;
     HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln1_w, bl.ln1_b, d.h, nullptr, nullptr, st), "ln1");
-    CHK(tm_forward_impl(&s, &bl.tm, B, 1, d.h, axp, d.vf, ast, ast, d.x, axp, d.tm, st, true, 1.f));
+    CHK(tm_forward_impl(&s, &bl.tm, B, 1, d.h, axp, d.vf, ast, ast, d.x, axp, d.tm, st, true, 1.f, prec));
     HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln2_w, bl.ln2_b, d.h, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(B, 1, C, d.h, fxp, bl.cm_mu_k, d.sh, fxp, st), "cm shift");
-    HIPCHK(gemm_f32_run(false, false, B, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(gemm_f32_run(false, false, B, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
+    HIPCHK(gemm_run(prec, false, false, B, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_run(prec, false, false, B, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
   }
   HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
-  HIPCHK(gemm_f32_run(false, false, B, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
+  HIPCHK(gemm_run(prec, false, false, B, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
   return WKV7_OK;
 }
 
@@ -706,6 +722,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
                                 hipStream_t st) {
   g_err[0] = 0;
   CHK(check_cfg(cfg, B));
+  const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
   if (T < 1) return fail(WKV7_EINVAL, "T must be >= 1");
   if (!M || !M->blocks || !G || !G->blocks) return fail(WKV7_EINVAL, "model/grads or their blocks are NULL");
   CHK(check_f32_ptr(M->emb, "emb", true));
@@ -771,19 +788,19 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     HIPCHK(hipMemcpyAsync(xo, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
     CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, xo, nullptr, t.tm, st,
-                        false, 1.f));
+                        false, 1.f, prec));
     HIPCHK(stk_launch_layernorm(BT, C, xo, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
-    HIPCHK(gemm_f32_run(false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(gemm_f32_run(false, false, BT, C, F, t.ka, F, bl.cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+    HIPCHK(gemm_run(prec, false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, t.ka, F, bl.cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(L), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
-  HIPCHK(gemm_f32_run(false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
+  HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
   HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, st), "cross-entropy");
 
   // ---------------- backward
-  HIPCHK(gemm_f32_run(false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
-  HIPCHK(gemm_f32_run(true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
+  HIPCHK(gemm_run(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
+  HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
                       splitk_for(C, V, BT), t.splitk, st), "dhead");
   HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(L), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
   HIPCHK(reduce_ln(G->ln_out_w, G->ln_out_b), "ln_out grads");
@@ -796,16 +813,16 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     HIPCHK(hipMemcpyAsync(t.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
     CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, t.x1, nullptr, t.tm, st,
-                        false, 1.f));
+                        false, 1.f, prec));
     HIPCHK(stk_launch_layernorm(BT, C, t.x1, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
-    HIPCHK(gemm_f32_run(false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_run(prec, false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
     // channel-mix backward
-    HIPCHK(gemm_f32_run(false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, t.ka, 1, nullptr, st), "dfk");
-    HIPCHK(gemm_f32_run(true, false, F, C, BT, t.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
+    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, t.ka, 1, nullptr, st), "dfk");
+    HIPCHK(gemm_run(prec, true, false, F, C, BT, t.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                         splitk_for(F, C, BT), t.splitk, st), "dWv");
-    HIPCHK(gemm_f32_run(false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
-    HIPCHK(gemm_f32_run(true, false, C, F, BT, t.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
+    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
+    HIPCHK(gemm_run(prec, true, false, C, F, BT, t.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
                         splitk_for(C, F, BT), t.splitk, st), "dWk");
     HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
@@ -817,7 +834,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
     CHK(tm_backward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, t.dx1, nullptr, t.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
-                         nullptr, st));
+                         nullptr, st, prec));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }

@@ -44,6 +44,37 @@ __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
   }
 }
 
+// Write a wave's TI x TJ accumulator tiles with beta and the epilogue.  D
+// layout of both 16x16 MFMAs used here: lane l, element v -> row 4*(l/16)+v,
+// column l%16.
+template <int TI, int TJ>
+__device__ __forceinline__ void store_acc(const GemmProblem& P, bool split, float* __restrict__ C,
+                                          int ldc, int m0, int n0, int wm, int wn, int lane,
+                                          const f4 (&acc)[TI][TJ]) {
+  const int M = P.M, N = P.N, fr = lane & 15, fk = lane >> 4;
+  const float beta = split ? 0.f : P.beta;
+  const int epi = split ? EPI_NONE : P.epi;
+  const float* __restrict__ aux = split ? nullptr : P.aux;
+#pragma unroll
+  for (int i = 0; i < TI; i++) {
+#pragma unroll
+    for (int j = 0; j < TJ; j++) {
+      const int col = n0 + wn * 16 * TJ + j * 16 + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int row = m0 + wm * 16 * TI + i * 16 + fk * 4 + v;
+        if (row >= M) continue;
+        const size_t o = (size_t)row * ldc + col;
+        float x = acc[i][j][v];
+        if (beta != 0.f) x += beta * C[o];
+        x = apply_epi(x, epi, aux ? aux[(size_t)row * P.ldc + col] : 0.f);
+        C[o] = x;
+      }
+    }
+  }
+}
+
 template <int TI, int TJ, int BK, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
   constexpr int BM = 32 * TI, BN = 32 * TJ;
@@ -182,28 +213,165 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
     }
   }
 
-  // D layout of v_mfma_f32_16x16x4_f32: lane l, element v -> row 4*(l/16)+v, col l%16
-  const float beta = split ? 0.f : P.beta;
-  const int epi = split ? EPI_NONE : P.epi;
-  const float* __restrict__ aux = split ? nullptr : P.aux;
+  store_acc<TI, TJ>(P, split, C, ldc, m0, n0, wm, wn, lane, acc);
+}
+
+// ------------------------------------------------------------- bf16 path --
+// Same tiling and epilogues with v_mfma_f32_16x16x32_bf16: operands are
+// rounded to bf16 (round to nearest even, v_cvt_pk_bf16_f32) while they are
+// staged into LDS; products accumulate in fp32.  Both operands are stored
+// k-contiguous in LDS ([rows][BK + 8] bf16, rows padded by 16 bytes so the
+// 16-byte fragment reads of 16 consecutive rows hit distinct banks): a lane's
+// MFMA fragment is 8 consecutive k of one row, one 16-byte read.  An operand
+// that is k-contiguous in memory is staged as 8-k row pieces (two float4
+// loads, one 16-byte store); a k-strided one is transposed inside each thread
+// as 4 k x 4 rows blocks (four float4 loads, four 8-byte stores), with
+// adjacent lanes on adjacent k so the stores hit distinct banks.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f8 __attribute__((ext_vector_type(8)));
+
+constexpr int BPAD = 8;  // bf16 of padding per LDS row
+
+// One operand tile: R rows (of M or N) x BK k, staged global -> registers ->
+// LDS.  KC: the operand is k-contiguous in memory (element (row, k) at
+// base[row * ld + k]); else element (row, k) is at base[k * ld + row].
+template <int R, int BK, bool KC>
+struct BfTile {
+  static constexpr int UNITS = KC ? R * BK / 8 : (BK / 4) * (R / 4);
+  static constexpr int PER = (UNITS + 255) / 256;
+  static constexpr int NF = KC ? 2 : 4;  // float4 loads per unit
+  static_assert(PER * NF <= 32, "load masks are 32 bits");
+  f4 reg[PER][NF];
+  unsigned ok;
+
+  // Unconditional loads from clamped (always valid) addresses; the mask
+  // records which float4 are inside the matrix.
+  __device__ __forceinline__ void load(const float* __restrict__ X, int ld, int r0, int rlim,
+                                       int k0, int kend, int tid) {
+    ok = 0;
 #pragma unroll
-  for (int i = 0; i < TI; i++) {
+    for (int q = 0; q < PER; q++) {
+      const int u = min(tid + 256 * q, UNITS - 1);
+      if (KC) {
+        const int row = u / (BK / 8), kc = u % (BK / 8);
+        const int r = r0 + row, k = k0 + kc * 8;
+        const float* p = X + (size_t)min(r, rlim - 1) * ld;
 #pragma unroll
-    for (int j = 0; j < TJ; j++) {
-      const int col = n0 + wn * 16 * TJ + j * 16 + fr;
-      if (col >= N) continue;
+        for (int s = 0; s < 2; s++) {
+          ok |= (unsigned)(r < rlim && k + 4 * s < kend) << (q * NF + s);
+          reg[q][s] = *reinterpret_cast<const f4*>(p + min(k + 4 * s, kend - 4));
+        }
+      } else {
+        const int kq = u % (BK / 4), rg = u / (BK / 4);
+        const int r = r0 + rg * 4, k = k0 + kq * 4;
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int row = m0 + wm * 16 * TI + i * 16 + fk * 4 + v;
-        if (row >= M) continue;
-        const size_t o = (size_t)row * ldc + col;
-        float x = acc[i][j][v];
-        if (beta != 0.f) x += beta * C[o];
-        x = apply_epi(x, epi, aux ? aux[(size_t)row * P.ldc + col] : 0.f);
-        C[o] = x;
+        for (int s = 0; s < 4; s++) {
+          ok |= (unsigned)(r < rlim && k + s < kend) << (q * NF + s);
+          reg[q][s] = *reinterpret_cast<const f4*>(X + (size_t)min(k + s, kend - 1) * ld +
+                                                   min(r, rlim - 4));
+        }
       }
     }
   }
+
+  __device__ __forceinline__ void store(__bf16 (*Xs)[BK + BPAD], int tid) const {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < PER; q++) {
+      const int u = tid + 256 * q;
+      if (UNITS % 256 != 0 && u >= UNITS) continue;
+      f4 x[NF];
+#pragma unroll
+      for (int s = 0; s < NF; s++) x[s] = (ok >> (q * NF + s)) & 1u ? reg[q][s] : z;
+      if (KC) {
+        const int row = u / (BK / 8), kc = u % (BK / 8);
+        const f8 v = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8*>(&Xs[row][kc * 8]) = __builtin_convertvector(v, bf16x8);
+      } else {
+        const int kq = u % (BK / 4), rg = u / (BK / 4);
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const f4 v = {x[0][c], x[1][c], x[2][c], x[3][c]};
+          *reinterpret_cast<bf16x4*>(&Xs[rg * 4 + c][kq * 4]) = __builtin_convertvector(v, bf16x4);
+        }
+      }
+    }
+  }
+};
+
+template <int TI, int TJ, int BK, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
+  constexpr int BM = 32 * TI, BN = 32 * TJ;
+  static_assert(BK % 32 == 0, "K tiles are whole MFMA k steps");
+  __shared__ __attribute__((aligned(16))) __bf16 As[2][BM][BK + BPAD];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BN][BK + BPAD];
+
+  const bool split = batch.count == 1 && gridDim.z > 1;
+  const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
+  const int M = P.M, N = P.N, K = P.K;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
+  float* __restrict__ C = P.C;
+  const int ldc = split ? N : P.ldc;
+  const int kbeg = split ? blockIdx.z * kslice : 0;
+  const int kend = split ? min(K, kbeg + kslice) : K;
+  if (split) C = P.part + (size_t)blockIdx.z * M * N;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 15, fk = lane >> 4;
+
+  BfTile<BM, BK, !TA> ta;  // A[m][k] is k-contiguous unless A is stored [K][M]
+  BfTile<BN, BK, TB> tb;   // B stored [N][K] is k-contiguous
+
+  f4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++)
+#pragma unroll
+    for (int j = 0; j < TJ; j++) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  if (kbeg < kend) {
+    ta.load(P.A, P.lda, m0, M, kbeg, kend, tid);
+    tb.load(P.B, P.ldb, n0, N, kbeg, kend, tid);
+    ta.store(As[0], tid);
+    tb.store(Bs[0], tid);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kbeg; k0 < kend; k0 += BK, buf ^= 1) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      ta.load(P.A, P.lda, m0, M, k0 + BK, kend, tid);
+      tb.load(P.B, P.ldb, n0, N, k0 + BK, kend, tid);
+    }
+    const int klen = kend - k0;  // zero-filled beyond klen; skip empty k steps
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      if (ks < klen) {
+        bf16x8 fa[TI], fb[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+          fa[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * 16 * TI + i * 16 + fr][ks + fk * 8]);
+#pragma unroll
+        for (int j = 0; j < TJ; j++)
+          fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * 16 * TJ + j * 16 + fr][ks + fk * 8]);
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+#pragma unroll
+          for (int j = 0; j < TJ; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) {
+      // the other buffer was last read before the previous barrier
+      ta.store(As[buf ^ 1], tid);
+      tb.store(Bs[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  store_acc<TI, TJ>(P, split, C, ldc, m0, n0, wm, wn, lane, acc);
 }
 
 // Sum S split-K partials [S][M][N] (leading dim N) into C (ldc), with beta/epilogue.
@@ -226,7 +394,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const 
   }
 }
 
-template <int TI, int TJ, int BK, bool TA, bool TB>
+template <int PREC, int TI, int TJ, int BK, bool TA, bool TB>
 hipError_t launch_t(const GemmBatch& b, int gz, int kslice, hipStream_t st) {
   int maxM = 0, maxN = 0;
   for (int i = 0; i < b.count; i++) {
@@ -234,20 +402,23 @@ hipError_t launch_t(const GemmBatch& b, int gz, int kslice, hipStream_t st) {
     maxN = max(maxN, b.p[i].N);
   }
   dim3 grid((maxN + 32 * TJ - 1) / (32 * TJ), (maxM + 32 * TI - 1) / (32 * TI), gz);
-  hipLaunchKernelGGL((gemm_f32<TI, TJ, BK, TA, TB>), grid, dim3(256), 0, st, b, kslice);
+  if (PREC == GEMM_BF16)
+    hipLaunchKernelGGL((gemm_bf16<TI, TJ, BK, TA, TB>), grid, dim3(256), 0, st, b, kslice);
+  else
+    hipLaunchKernelGGL((gemm_f32<TI, TJ, BK, TA, TB>), grid, dim3(256), 0, st, b, kslice);
   return hipGetLastError();
 }
 
-template <int TI, int TJ, bool TA, bool TB>
+template <int PREC, int TI, int TJ, bool TA, bool TB>
 hipError_t launch_bk(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // K tile depth: shallow for big tiles (plenty of MFMA work per K step),
   // deep for small tiles so few global round trips remain.
-  if (TI * TJ >= 8 || klen <= 32) return launch_t<TI, TJ, 32, TA, TB>(b, gz, kslice, st);
-  if (klen <= 64 || TI * TJ >= 4) return launch_t<TI, TJ, 64, TA, TB>(b, gz, kslice, st);
-  return launch_t<TI, TJ, 128, TA, TB>(b, gz, kslice, st);
+  if (TI * TJ >= 8 || klen <= 32) return launch_t<PREC, TI, TJ, 32, TA, TB>(b, gz, kslice, st);
+  if (klen <= 64 || TI * TJ >= 4) return launch_t<PREC, TI, TJ, 64, TA, TB>(b, gz, kslice, st);
+  return launch_t<PREC, TI, TJ, 128, TA, TB>(b, gz, kslice, st);
 }
 
-template <bool TA, bool TB>
+template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid still gives every CU work (>= 256 workgroups),
   // else the smallest tile.
@@ -259,46 +430,53 @@ hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipSt
   auto blocks = [&](int bm, int bn) {
     return (long)((maxM + bm - 1) / bm) * ((maxN + bn - 1) / bn) * gz;
   };
-  if (blocks(128, 128) >= 256 && maxN >= 128) return launch_bk<4, 4, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(128, 64) >= 256 && maxN >= 64) return launch_bk<4, 2, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(64, 64) >= 256 && maxN >= 64) return launch_bk<2, 2, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(64, 32) >= 256) return launch_bk<2, 1, TA, TB>(b, gz, kslice, klen, st);
-  return launch_bk<1, 1, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(128, 128) >= 256 && maxN >= 128) return launch_bk<PREC, 4, 4, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(128, 64) >= 256 && maxN >= 64) return launch_bk<PREC, 4, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(64, 64) >= 256 && maxN >= 64) return launch_bk<PREC, 2, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (blocks(64, 32) >= 256) return launch_bk<PREC, 2, 1, TA, TB>(b, gz, kslice, klen, st);
+  return launch_bk<PREC, 1, 1, TA, TB>(b, gz, kslice, klen, st);
 }
 
-hipError_t dispatch(bool transA, bool transB, const GemmBatch& b, int gz, int kslice, int klen,
-                    hipStream_t st) {
-  if (!transA && !transB) return launch_layout<false, false>(b, gz, kslice, klen, st);
-  if (!transA && transB) return launch_layout<false, true>(b, gz, kslice, klen, st);
-  if (transA && !transB) return launch_layout<true, false>(b, gz, kslice, klen, st);
-  return launch_layout<true, true>(b, gz, kslice, klen, st);
+template <int PREC>
+hipError_t dispatch_p(bool transA, bool transB, const GemmBatch& b, int gz, int kslice, int klen,
+                      hipStream_t st) {
+  if (!transA && !transB) return launch_layout<PREC, false, false>(b, gz, kslice, klen, st);
+  if (!transA && transB) return launch_layout<PREC, false, true>(b, gz, kslice, klen, st);
+  if (transA && !transB) return launch_layout<PREC, true, false>(b, gz, kslice, klen, st);
+  return launch_layout<PREC, true, true>(b, gz, kslice, klen, st);
+}
+
+hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int gz, int kslice,
+                    int klen, hipStream_t st) {
+  if (prec == GEMM_BF16) return dispatch_p<GEMM_BF16>(transA, transB, b, gz, kslice, klen, st);
+  return dispatch_p<GEMM_F32>(transA, transB, b, gz, kslice, klen, st);
 }
 
 }  // namespace gemmk
 
-hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
+hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
   if (b.count < 1 || b.count > GEMM_MAX_BATCH) return hipErrorInvalidValue;
   int maxK = 0;
   for (int i = 0; i < b.count; i++) maxK = max(maxK, b.p[i].K);
-  return gemmk::dispatch(transA, transB, b, b.count, maxK, maxK, st);
+  return gemmk::dispatch(prec, transA, transB, b, b.count, maxK, maxK, st);
 }
 
 // C = epi(op(A) op(B) + beta C).  ws (may be NULL when split == 1) holds
 // split*M*N floats of split-K partials.
-hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A, int lda,
-                        const float* B, int ldb, float* C, int ldc, float beta, int epi,
-                        const float* aux, int split, float* ws, hipStream_t st) {
+hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
+                    int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                    const float* aux, int split, float* ws, hipStream_t st) {
   using namespace gemmk;
   if (M <= 0 || N <= 0) return hipSuccess;
   GemmBatch b;
   b.count = 1;
   b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, nullptr};
-  if (split <= 1 || ws == nullptr) return dispatch(transA, transB, b, 1, K, K, st);
+  if (split <= 1 || ws == nullptr) return dispatch(prec, transA, transB, b, 1, K, K, st);
   int kslice = (K + split - 1) / split;
   kslice = (kslice + 31) / 32 * 32;
   const int S = (K + kslice - 1) / kslice;
   b.p[0].part = ws;
-  hipError_t e = dispatch(transA, transB, b, S, kslice, kslice, st);
+  hipError_t e = dispatch(prec, transA, transB, b, S, kslice, kslice, st);
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)M * N / 4;
   int blocks = (int)((n4 + 255) / 256);

@@ -1,4 +1,7 @@
-// fp32 matrix-core GEMM (gemm.hip): problem descriptors and launchers.
+// Matrix-core GEMM (gemm.hip): problem descriptors and launchers.  Operands
+// and results are fp32 in memory; the products run either in fp32
+// (v_mfma_f32_16x16x4_f32) or with bf16-rounded operands and fp32
+// accumulation (v_mfma_f32_16x16x32_bf16).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -8,6 +11,8 @@ enum GemmEpi {
 };
 
 constexpr int GEMM_MAX_BATCH = 4;
+
+enum GemmPrec { GEMM_F32 = 0, GEMM_BF16 = 1 };
 
 // C = epi(op(A) op(B) + beta C); aux (same layout as C) feeds the *_BWD epilogues.
 struct GemmProblem {
@@ -30,8 +35,18 @@ struct GemmBatch {
 };
 
 // Up to GEMM_MAX_BATCH independent problems of one layout in one launch.
-hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st);
+hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hipStream_t st);
 // One problem, optionally split along K into `split` slices (ws: split*M*N floats).
-hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A, int lda,
-                        const float* B, int ldb, float* C, int ldc, float beta, int epi,
-                        const float* aux, int split, float* ws, hipStream_t st);
+hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
+                    int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                    const float* aux, int split, float* ws, hipStream_t st);
+
+inline hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
+  return gemm_batch(GEMM_F32, transA, transB, b, st);
+}
+inline hipError_t gemm_f32_run(bool transA, bool transB, int M, int N, int K, const float* A,
+                               int lda, const float* B, int ldb, float* C, int ldc, float beta,
+                               int epi, const float* aux, int split, float* ws, hipStream_t st) {
+  return gemm_run(GEMM_F32, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, split,
+                  ws, st);
+}

@@ -458,10 +458,17 @@ __global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int ns
   }
 }
 
-// Two 32-row slices per head: 256-thread workgroups whose LDS (sv, svr, red:
-// 128 KiB fp32) leaves one workgroup per CU; smaller slices would double the
-// partial traffic without adding resident waves.
-int bwd_nsplit(int, int) { return 2; }
+// Row slices per head.  A 256-thread workgroup's LDS (sv, svr, red: ~122-128
+// KiB) leaves one workgroup per CU, so slices only pay while the grid still
+// fits in one pass over the 256 CUs: four 16-row slices when B*H*4 <= 256
+// (the recurrence is latency bound, so a slice of half the rows takes well
+// over half the time and the idle CUs are the larger loss), else two 32-row
+// slices (more slices would double the partial traffic and add passes).
+int bwd_nsplit(int B, int H) { return (long)B * H * 4 <= 256 ? 4 : 2; }
+
+// Forward rows per thread: 16-row workgroups (RPT = 1, four per head) while
+// B*H*4 <= 512 workgroups (at most two per CU), else 32-row ones.
+int fwd_rpt(int B, int H) { return (long)B * H * 4 <= 512 ? 1 : 2; }
 
 }  // namespace wkv7k
 
@@ -473,11 +480,14 @@ template <typename T>
 hipError_t launch_forward_t(int B, int T_, int H, const void* r, const void* w, const void* k,
                             const void* v, const void* a, const void* b, const float* s0, void* y,
                             float* sT, float* ckpt, hipStream_t st) {
-  constexpr int RPT = 2;
-  const int nblk = B * H * (N / (16 * RPT));
-  hipLaunchKernelGGL((fwd_seq<RPT, T>), dim3(nblk), dim3(256), 0, st, B, T_, H,
-                     (const T*)r, (const T*)w, (const T*)k, (const T*)v, (const T*)a,
-                     (const T*)b, s0, (T*)y, sT, ckpt);
+  if (fwd_rpt(B, H) == 1)
+    hipLaunchKernelGGL((fwd_seq<1, T>), dim3(B * H * 4), dim3(256), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b, s0, (T*)y,
+                       sT, ckpt);
+  else
+    hipLaunchKernelGGL((fwd_seq<2, T>), dim3(B * H * 2), dim3(256), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b, s0, (T*)y,
+                       sT, ckpt);
   return hipGetLastError();
 }
 
@@ -489,9 +499,14 @@ hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w,
                              hipStream_t st) {
   const int ns = bwd_nsplit(B, H);
   const dim3 grid(B * H * ns);
-  hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
-                     (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                     (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+  if (ns == 4)
+    hipLaunchKernelGGL((bwd_seq<1, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+  else
+    hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t plane4 = (size_t)B * T_ * H * N / 4;

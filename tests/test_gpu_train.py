@@ -1,7 +1,20 @@
 """GPU parity of rwkv7_train_step (full RWKV-7 training step: embedding,
 blocks, LM head, fused log-softmax CE, forward and backward) against the f64
 oracle.  Loss and every gradient are compared (max|gpu - oracle| /
-max|oracle|): loss <= 1e-4, gradients <= 1e-3 (fp32 end to end)."""
+max|oracle|): loss <= 1e-4, gradients <= 1e-3 with fp32 GEMMs (fp32 end to
+end) against the f64 oracle.  With bf16 GEMMs the oracle runs at that stated
+precision (every matrix-product operand rounded to bf16, f64 elsewhere:
+oracle.precision) and loss and gradients are held to 2e-2, the bf16
+tolerance.  At the full model size the bf16 gradients are ill-conditioned
+with respect to rounding: rounding the f64 oracle's own products to bf16
+moves its embedding gradient by ~45% (random init, std 0.02), and merely
+storing each product of the bf16 oracle as fp32 instead of f64 moves some of
+its time-mix gradients by ~9% (a cascade of flipped bf16 roundings through 24
+blocks).  So at full size the bf16 run is held to 2e-2 on the loss and on the
+head / ln_out gradients (well conditioned), and every other gradient must
+point the same way as the oracle's (cosine >= 0.95); the complete per-tensor
+2e-2 comparison runs on the small models, and the fp32-GEMM run of the same
+full-size step meets 1e-3 on every gradient."""
 import math
 
 import numpy as np
@@ -23,58 +36,81 @@ def _dev_model(m):
     return out
 
 
-def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0):
+def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0, gemm="f32"):
     from rwkv_linear_attention_wkv7_amd import binding
     m = synth.stack_model(C, H, F, V, L, ranks, seed=seed, perturbed=perturbed, std=std,
                           use_ln0=use_ln0)
     dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks,
-                                  use_ln0=int(use_ln0)), _dev_model(m))
+                                  use_ln0=int(use_ln0), gemm_dtype=gemm), _dev_model(m))
     grads = binding.TrainGrads(dm)
     tok = synth.token_ids(B, T + 1, V, seed=seed + 100)
     x, y = np.ascontiguousarray(tok[:, :-1]), np.ascontiguousarray(tok[:, 1:])
-    print(f"[train] L={L} C={C} F={F} V={V} B={B} T={T}", flush=True)
+    print(f"[train] L={L} C={C} F={F} V={V} B={B} T={T} gemm={gemm}", flush=True)
     loss = hip.rwkv7_train_step(dm, grads, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
     torch.cuda.synchronize()
     return m, dm, grads, x, y, float(loss.item())
 
 
-def _compare(m, grads, x, y, loss, cfg):
-    ref_loss, G = stack.train_step(m, cfg, x, y)
-    assert abs(loss - ref_loss) <= 1e-4 * abs(ref_loss), (loss, ref_loss)
+def _compare(m, grads, x, y, loss, cfg, gemm="f32", only=None):
+    """only: names checked at the tolerance; the rest get the cosine check."""
+    tl, tg = (1e-4, 1e-3) if gemm == "f32" else (2e-2, 2e-2)
+    ref_loss, G = stack.train_step(m, cfg, x, y, gemm="f64" if gemm == "f32" else "bf16")
+    assert abs(loss - ref_loss) <= tl * abs(ref_loss), (loss, ref_loss)
     g = grads.g
+    worst = [0.0, ""]
+    cos_min = [1.0, ""]
+
+    def chk(name, got, ref, tol):
+        if only is not None and name not in only:
+            a, b = np.asarray(got, np.float64).ravel(), np.asarray(ref, np.float64).ravel()
+            c = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+            if c < cos_min[0]:
+                cos_min[:] = [c, name]
+            assert c >= 0.95, f"{name}: cosine {c:.4f} < 0.95"
+            return
+        e = assert_close(name, got, ref, tol)
+        if e > worst[0]:
+            worst[:] = [e, name]
     np_ = lambda t: t.cpu().numpy()
     for k in ("emb", "head", "ln_out_w", "ln_out_b"):
-        assert_close(k, np_(g[k]), G[k], 1e-3)
+        chk(k, np_(g[k]), G[k], tg)
     if g.get("ln0_w") is not None:
-        assert_close("ln0_w", np_(g["ln0_w"]), G["ln0_w"], 1e-3)
-        assert_close("ln0_b", np_(g["ln0_b"]), G["ln0_b"], 1e-3)
+        chk("ln0_w", np_(g["ln0_w"]), G["ln0_w"], tg)
+        chk("ln0_b", np_(g["ln0_b"]), G["ln0_b"], tg)
     for l, gb in enumerate(g["blocks"]):
         for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
-            assert_close(f"{k}[{l}]", np_(gb[k]), G["blocks"][l][k], 1e-3)
+            chk(f"{k}[{l}]", np_(gb[k]), G["blocks"][l][k], tg)
         assert set(gb["tm"]) == set(G["blocks"][l]["tm"])
         for k, v in gb["tm"].items():
-            assert_close(f"tm.{k}[{l}]", np_(v), G["blocks"][l]["tm"][k], 1e-3)
+            chk(f"tm.{k}[{l}]", np_(v), G["blocks"][l]["tm"][k], tg)
+    print(f"[train] gemm={gemm} loss {loss:.6f} oracle {ref_loss:.6f}; worst gradient "
+          f"{worst[1]} rel err {worst[0]:.2e}; lowest cosine {cos_min[1]} {cos_min[0]:.5f}",
+          flush=True)
 
 
+@pytest.mark.parametrize("gemm", ["f32", "bf16"])
 @pytest.mark.parametrize("use_ln0", [False, True])
-def test_train_step_small(hip, use_ln0):
+def test_train_step_small(hip, use_ln0, gemm):
     L, C, H, F, V = 3, 128, 2, 256, 512
     m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (16, 16, 16, 32), 2, 40, seed=3,
-                                    perturbed=True, std=0.2, use_ln0=use_ln0)
-    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L))
+                                    perturbed=True, std=0.2, use_ln0=use_ln0, gemm=gemm)
+    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L), gemm)
 
 
-def test_train_step_full_model_short_batch(hip):
+@pytest.mark.parametrize("gemm", ["f32", "bf16"])
+def test_train_step_full_model_short_batch(hip, gemm):
     """Full model size: 24 blocks, C=1024 (H=16), FFN 4096, vocab 65536, ranks
     64/64/32/128, std-0.02 random init; one sequence of 256 tokens so the f64
     oracle fits; every gradient compared."""
     L, C, H, F, V = 24, 1024, 16, 4096, 65536
     m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 1, 256, seed=0,
-                                    perturbed=False, std=0.02, use_ln0=False)
-    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L))
+                                    perturbed=False, std=0.02, use_ln0=False, gemm=gemm)
+    only = None if gemm == "f32" else ("head", "ln_out_w", "ln_out_b")
+    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L), gemm, only)
 
 
-def test_train_step_full_config_properties(hip):
+@pytest.mark.parametrize("gemm", ["f32", "bf16"])
+def test_train_step_full_config_properties(hip, gemm):
     """B=4, T=2048 at the full model size.  At random init the LN output rows
     have unit variance and the head entries N(0, 0.02^2), so the logits are
     ~N(0, s2) with s2 = C 0.02^2 and the expected loss is
@@ -84,7 +120,7 @@ def test_train_step_full_config_properties(hip):
     from rwkv_linear_attention_wkv7_amd import binding
     L, C, H, F, V = 24, 1024, 16, 4096, 65536
     m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 4, 2048, seed=0,
-                                    perturbed=False, std=0.02, use_ln0=False)
+                                    perturbed=False, std=0.02, use_ln0=False, gemm=gemm)
     expect = math.log(V) + C * 0.02 ** 2 / 2
     assert abs(loss - expect) < 3e-2, (loss, expect)
     first = {"emb": grads.g["emb"].clone(), "head": grads.g["head"].clone(),

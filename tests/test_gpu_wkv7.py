@@ -59,6 +59,7 @@ def _check(d, y, sT, g, with_state, ftol, gtol, sel=None):
     (1, 1, 2, True),       # single token
     (3, 16, 1, False),     # exactly one checkpoint chunk
     (2, 130, 2, True),     # many chunks, ragged
+    (6, 40, 24, True),     # 144 heads: 32-row forward workgroups, two backward slices
 ])
 def test_wkv7_fp32_parity(hip, B, T, H, with_state):
     d = synth.wkv7_inputs(B, T, H, 64, seed=B * 100 + T, with_state=with_state)
