@@ -223,13 +223,14 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
 // k-contiguous in LDS ([rows][BK + 8] bf16, rows padded by 16 bytes so the
 // 16-byte fragment reads of 16 consecutive rows hit distinct banks): a lane's
 // MFMA fragment is 8 consecutive k of one row, one 16-byte read.  An operand
-// that is k-contiguous in memory is staged as 8-k row pieces (two float4
-// loads, one 16-byte store); a k-strided one is transposed inside each thread
-// as 4 k x 4 rows blocks (four float4 loads, four 8-byte stores), with
-// adjacent lanes on adjacent k so the stores hit distinct banks.
+// that is k-contiguous in memory is staged as 4-k row pieces (one float4
+// load, one 8-byte store) with adjacent lanes on adjacent pieces, so a load
+// instruction covers whole 128-byte row segments; a k-strided one is
+// transposed inside each thread as 4 k x 4 rows blocks (four float4 loads,
+// four 8-byte stores), with adjacent lanes on adjacent k so the stores hit
+// distinct banks.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f8 __attribute__((ext_vector_type(8)));
 
 constexpr int BPAD = 8;  // bf16 of padding per LDS row
 
@@ -238,12 +239,39 @@ constexpr int BPAD = 8;  // bf16 of padding per LDS row
 // base[row * ld + k]); else element (row, k) is at base[k * ld + row].
 template <int R, int BK, bool KC>
 struct BfTile {
-  static constexpr int UNITS = KC ? R * BK / 8 : (BK / 4) * (R / 4);
+  static constexpr int UNITS = KC ? R * BK / 4 : (BK / 4) * (R / 4);
   static constexpr int PER = (UNITS + 255) / 256;
-  static constexpr int NF = KC ? 2 : 4;  // float4 loads per unit
+  static constexpr int NF = KC ? 1 : 4;  // float4 loads per unit
   static_assert(PER * NF <= 32, "load masks are 32 bits");
   f4 reg[PER][NF];
   unsigned ok;
+
+  // Element offsets of this thread's float4 loads relative to the tile
+  // origin (row r0, k0): constant over the K loop, so an interior tile costs
+  // one uniform base update per stage and no per-load address arithmetic.
+  uint32_t off[PER][NF];
+  __device__ __forceinline__ void init(int ld, int tid) {
+#pragma unroll
+    for (int q = 0; q < PER; q++) {
+      const int u = min(tid + 256 * q, UNITS - 1);
+      if (KC) {
+        const int row = u / (BK / 4), k4 = u % (BK / 4);
+        off[q][0] = (uint32_t)(row * ld + k4 * 4);
+      } else {
+        const int kq = u % (BK / 4), rg = u / (BK / 4);
+#pragma unroll
+        for (int s = 0; s < 4; s++) off[q][s] = (uint32_t)((kq * 4 + s) * ld + rg * 4);
+      }
+    }
+  }
+  // Interior tile (every element inside the matrix): plain loads, all valid.
+  __device__ __forceinline__ void load_interior(const float* __restrict__ origin) {
+    ok = ~0u;
+#pragma unroll
+    for (int q = 0; q < PER; q++)
+#pragma unroll
+      for (int s = 0; s < NF; s++) reg[q][s] = *reinterpret_cast<const f4*>(origin + off[q][s]);
+  }
 
   // Unconditional loads from clamped (always valid) addresses; the mask
   // records which float4 are inside the matrix.
@@ -254,14 +282,10 @@ struct BfTile {
     for (int q = 0; q < PER; q++) {
       const int u = min(tid + 256 * q, UNITS - 1);
       if (KC) {
-        const int row = u / (BK / 8), kc = u % (BK / 8);
-        const int r = r0 + row, k = k0 + kc * 8;
-        const float* p = X + (size_t)min(r, rlim - 1) * ld;
-#pragma unroll
-        for (int s = 0; s < 2; s++) {
-          ok |= (unsigned)(r < rlim && k + 4 * s < kend) << (q * NF + s);
-          reg[q][s] = *reinterpret_cast<const f4*>(p + min(k + 4 * s, kend - 4));
-        }
+        const int row = u / (BK / 4), k4 = u % (BK / 4);
+        const int r = r0 + row, k = k0 + k4 * 4;
+        ok |= (unsigned)(r < rlim && k < kend) << q;
+        reg[q][0] = *reinterpret_cast<const f4*>(X + (size_t)min(r, rlim - 1) * ld + min(k, kend - 4));
       } else {
         const int kq = u % (BK / 4), rg = u / (BK / 4);
         const int r = r0 + rg * 4, k = k0 + kq * 4;
@@ -275,6 +299,7 @@ struct BfTile {
     }
   }
 
+  template <bool ALL>
   __device__ __forceinline__ void store(__bf16 (*Xs)[BK + BPAD], int tid) const {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -283,11 +308,10 @@ struct BfTile {
       if (UNITS % 256 != 0 && u >= UNITS) continue;
       f4 x[NF];
 #pragma unroll
-      for (int s = 0; s < NF; s++) x[s] = (ok >> (q * NF + s)) & 1u ? reg[q][s] : z;
+      for (int s = 0; s < NF; s++) x[s] = ALL || ((ok >> (q * NF + s)) & 1u) ? reg[q][s] : z;
       if (KC) {
-        const int row = u / (BK / 8), kc = u % (BK / 8);
-        const f8 v = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        *reinterpret_cast<bf16x8*>(&Xs[row][kc * 8]) = __builtin_convertvector(v, bf16x8);
+        const int row = u / (BK / 4), k4 = u % (BK / 4);
+        *reinterpret_cast<bf16x4*>(&Xs[row][k4 * 4]) = __builtin_convertvector(x[0], bf16x4);
       } else {
         const int kq = u % (BK / 4), rg = u / (BK / 4);
 #pragma unroll
@@ -324,6 +348,12 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
 
   BfTile<BM, BK, !TA> ta;  // A[m][k] is k-contiguous unless A is stored [K][M]
   BfTile<BN, BK, TB> tb;   // B stored [N][K] is k-contiguous
+  ta.init(P.lda, tid);
+  tb.init(P.ldb, tid);
+  const float* __restrict__ Ag = P.A;
+  const float* __restrict__ Bg = P.B;
+  // the M and N extent of this tile is inside the matrices (uniform)
+  const bool in_mn = m0 + BM <= M && n0 + BN <= N;
 
   f4 acc[TI][TJ];
 #pragma unroll
@@ -331,20 +361,34 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
 #pragma unroll
     for (int j = 0; j < TJ; j++) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-  if (kbeg < kend) {
-    ta.load(P.A, P.lda, m0, M, kbeg, kend, tid);
-    tb.load(P.B, P.ldb, n0, N, kbeg, kend, tid);
-    ta.store(As[0], tid);
-    tb.store(Bs[0], tid);
-  }
+  // stage k0 -> registers; returns whether every element was inside
+  auto load = [&](int k0) -> bool {
+    if (in_mn && k0 + BK <= kend) {
+      ta.load_interior(TA ? Ag + (size_t)k0 * P.lda + m0 : Ag + (size_t)m0 * P.lda + k0);
+      tb.load_interior(TB ? Bg + (size_t)n0 * P.ldb + k0 : Bg + (size_t)k0 * P.ldb + n0);
+      return true;
+    }
+    ta.load(Ag, P.lda, m0, M, k0, kend, tid);
+    tb.load(Bg, P.ldb, n0, N, k0, kend, tid);
+    return false;
+  };
+  auto store = [&](bool all, int b) {
+    if (all) {
+      ta.template store<true>(As[b], tid);
+      tb.template store<true>(Bs[b], tid);
+    } else {
+      ta.template store<false>(As[b], tid);
+      tb.template store<false>(Bs[b], tid);
+    }
+  };
+
+  if (kbeg < kend) store(load(kbeg), 0);
   __syncthreads();
   int buf = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK, buf ^= 1) {
     const bool more = k0 + BK < kend;
-    if (more) {
-      ta.load(P.A, P.lda, m0, M, k0 + BK, kend, tid);
-      tb.load(P.B, P.ldb, n0, N, k0 + BK, kend, tid);
-    }
+    bool all = true;
+    if (more) all = load(k0 + BK);
     const int klen = kend - k0;  // zero-filled beyond klen; skip empty k steps
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
@@ -363,11 +407,8 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (more) {
-      // the other buffer was last read before the previous barrier
-      ta.store(As[buf ^ 1], tid);
-      tb.store(Bs[buf ^ 1], tid);
-    }
+    // the other buffer was last read before the previous barrier
+    if (more) store(all, buf ^ 1);
     __syncthreads();
   }
 
