@@ -62,14 +62,28 @@ size_t wkv7_checkpoint_floats(int B, int T, int H, int N);
  * wkv7_checkpoint_floats() fp32 laid out [B][H][ceil(T/L)][N][N], where
  * checkpoint c is the state after c*L tokens (c = 0 holds s0); it is what
  * wkv7_backward recomputes from.  T >= 1, B >= 1, H >= 1.
+ *
+ * ws / ws_bytes: NULL, or device scratch of at least
+ * wkv7_forward_workspace_bytes() bytes (16-byte aligned; contents
+ * undefined before and after; owned by the caller, not retained).  The
+ * query is nonzero exactly for the shapes that take the chunked matrix-core
+ * kernels when given it (T >= 2L and B*H < 64: the recurrence unrolled over
+ * chunks of L tokens, intra-chunk products on MFMA; chunks whose cumulative
+ * decay leaves the fp32 exponent range of the unrolled form run token by
+ * token).  Every other shape, or ws NULL, runs the token-sequential kernel,
+ * which spreads each head over four workgroups and is the faster one once
+ * B*H reaches 64.  Both compute the same recurrence in fp32 and agree to
+ * rounding.  A ws smaller than a nonzero query returns WKV7_ENOSPC.
  */
+size_t wkv7_forward_workspace_bytes(int B, int T, int H, int N);
 int wkv7_forward(int B, int T, int H, int N, int dtype,
                  const void *r, const void *w, const void *k, const void *v,
                  const void *a, const void *b, const float *s0,
-                 void *y, float *sT, float *ckpt, hipStream_t stream);
+                 void *y, float *sT, float *ckpt, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes wkv7_backward needs: fp32 column partials of the reverse
- * pass, plus the checkpoints when have_ckpt is 0. */
+ * pass, plus, when have_ckpt is 0, the checkpoints and the chunked-forward
+ * records of their recompute. */
 size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
 
 /*

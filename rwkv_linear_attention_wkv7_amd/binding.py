@@ -78,7 +78,9 @@ def lib():
         L.wkv7_checkpoint_interval.restype = _i
         L.wkv7_checkpoint_floats.argtypes = [_i] * 4
         L.wkv7_checkpoint_floats.restype = _sz
-        L.wkv7_forward.argtypes = [_i] * 5 + [_vp] * 11
+        L.wkv7_forward_workspace_bytes.argtypes = [_i] * 4
+        L.wkv7_forward_workspace_bytes.restype = _sz
+        L.wkv7_forward.argtypes = [_i] * 5 + [_vp] * 11 + [_sz, _vp]
         L.wkv7_forward.restype = _i
         L.wkv7_backward_workspace_bytes.argtypes = [_i] * 5
         L.wkv7_backward_workspace_bytes.restype = _sz
@@ -161,8 +163,12 @@ def wkv7_checkpoint_floats(B, T, H, N=64):
 
 
 def wkv7_forward(r, w, k, v, a, b, s0=None, y=None, sT=None, ckpt=None,
-                 want_state=True, want_ckpt=False):
-    """y = WKV7(r, w, k, v, a, b; s0).  Returns (y, sT or None, ckpt or None)."""
+                 want_state=True, want_ckpt=False, chunked=True, ws=None):
+    """y = WKV7(r, w, k, v, a, b; s0).  Returns (y, sT or None, ckpt or None).
+
+    chunked: pass the workspace of the chunked matrix-core kernels (used for
+    T >= 32); False runs the token-sequential kernel at every T.  ws: a
+    preallocated uint8 device workspace (allocated here when None)."""
     B, T, H, N = r.shape
     dt = r.dtype
     for n, t in zip("rwkvab", (r, w, k, v, a, b)):
@@ -175,8 +181,15 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, y=None, sT=None, ckpt=None,
     if ckpt is None and want_ckpt:
         ckpt = torch.empty(wkv7_checkpoint_floats(B, T, H, N), device=r.device, dtype=torch.float32)
     _opt(ckpt, (wkv7_checkpoint_floats(B, T, H, N),), torch.float32, "ckpt")
+    nws = lib().wkv7_forward_workspace_bytes(B, T, H, N) if chunked else 0
+    if nws and ws is None:
+        ws = torch.empty(nws, device=r.device, dtype=torch.uint8)
+    if not nws:
+        ws = None
+    elif ws.numel() < nws:
+        raise ValueError(f"ws holds {ws.numel()} bytes, {nws} needed")
     _check(lib().wkv7_forward(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
-                              _p(s0), _p(y), _p(sT), _p(ckpt), _stream()))
+                              _p(s0), _p(y), _p(sT), _p(ckpt), _p(ws), nws, _stream()))
     return y, sT, ckpt
 
 

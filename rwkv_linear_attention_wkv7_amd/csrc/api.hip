@@ -94,9 +94,15 @@ extern "C" size_t wkv7_checkpoint_floats(int B, int T, int H, int N) {
   return ckpt_floats(B, T, H);
 }
 
+extern "C" size_t wkv7_forward_workspace_bytes(int B, int T, int H, int N) {
+  if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
+  return wkv7_use_chunked(B, T, H) ? wkv7_chunk_ws_floats(B, T, H) * sizeof(float) : 0;
+}
+
 extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r, const void* w,
                             const void* k, const void* v, const void* a, const void* b,
-                            const float* s0, void* y, float* sT, float* ckpt, hipStream_t stream) {
+                            const float* s0, void* y, float* sT, float* ckpt, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   CHK(check_wkv_shape(B, T, H, N, dtype));
   CHK(check_tok_ptr(r, "r", dtype, true));
@@ -109,7 +115,15 @@ extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r
   CHK(check_f32_ptr(s0, "s0", false));
   CHK(check_f32_ptr(sT, "sT", false));
   CHK(check_f32_ptr(ckpt, "ckpt", false));
-  HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, stream),
+  float* cws = nullptr;
+  if (ws) {
+    const size_t need = wkv7_forward_workspace_bytes(B, T, H, N);
+    if (ws_bytes < need)
+      return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    CHK(check_f32_ptr(ws, "ws", true));
+    if (need) cws = static_cast<float*>(ws);
+  }
+  HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, cws, stream),
          "wkv7_forward launch");
   return WKV7_OK;
 }
@@ -118,7 +132,10 @@ extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int 
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
   Carver c(nullptr);
   c.take(wkv7_bwd_partial_floats(B, T, H));
-  if (!have_ckpt) c.take(ckpt_floats(B, T, H));
+  if (!have_ckpt) {
+    c.take(ckpt_floats(B, T, H));
+    c.take(wkv7_forward_workspace_bytes(B, T, H, N) / sizeof(float));
+  }
   return c.off;
 }
 
@@ -145,7 +162,10 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
   const float* ck = ckpt;
   if (!ck) {
     float* tmp = cv.take(ckpt_floats(B, T, H));
-    HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, stream),
+    const size_t nc = wkv7_forward_workspace_bytes(B, T, H, N) / sizeof(float);
+    float* cws = nc ? cv.take(nc) : nullptr;
+    HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, cws,
+                               stream),
            "wkv7_backward checkpoint recompute");
     ck = tmp;
   }
@@ -176,6 +196,7 @@ struct TmCache {
   float *r, *k, *v, *tw, *ow, *la, *oa, *sg, *g, *lv, *ov;
   float *w, *a, *kk, *kmod, *vmod, *A, *Bv, *y, *tg;
   float *mean, *rstd, *alpha, *ckpt;
+  float* wkv_ws;  // chunked-forward records (nullptr: token-sequential forward)
 };
 
 void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m, bool with_ckpt = true) {
@@ -196,6 +217,8 @@ void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m, bool wi
   m.rstd = c.take(BT * s->H);
   m.alpha = c.take(BT * s->H);
   m.ckpt = with_ckpt ? c.take(ckpt_floats(B, T, s->H)) : nullptr;
+  const size_t nc = wkv7_use_chunked(B, T, s->H) ? wkv7_chunk_ws_floats(B, T, s->H) : 0;
+  m.wkv_ws = nc ? c.take(nc) : nullptr;
 }
 
 struct TmBwdBufs {
@@ -336,7 +359,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
            "wkv7 step");
   else
     HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
-                               m.ckpt, st), "wkv7 forward");
+                               m.ckpt, m.wkv_ws, st), "wkv7 forward");
   HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
   HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;

@@ -71,6 +71,17 @@ __device__ __forceinline__ void store_raw1(T* p, typename Raw<T>::v1 x) {
   *reinterpret_cast<typename Raw<T>::v1*>(p) = x;
 }
 
+// Raw 4-element value (see Raw) to fp32.
+template <typename T>
+__device__ __forceinline__ f4 raw4_to_f4(typename Raw<T>::v4 x);
+template <>
+__device__ __forceinline__ f4 raw4_to_f4<float>(f4 x) { return x; }
+template <>
+__device__ __forceinline__ f4 raw4_to_f4<bf16_t>(uint2 u) {
+  return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+}
+
 template <typename T>
 __device__ __forceinline__ float load1(const T* p);
 template <>
@@ -142,6 +153,17 @@ __device__ __forceinline__ void rows4_reduce_scatter(float (&x)[4 * NQ]) {
 
 // Full 64-lane wave sum, result in every lane.
 __device__ __forceinline__ float wavesum(float x) { return rows4sum(rowsum16(x)); }
+
+// ------------------------------------------------------------- barrier ----
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier; the clobber keeps the compiler from moving
+// memory accesses across it.  Unlike __syncthreads() it does not wait for the
+// wave's outstanding global loads and stores, so prefetches and result
+// stores stay in flight across it.  Only for loops whose waves exchange data
+// through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // --------------------------------------------------------------- launch ----
 // Workgroups are dispatched round-robin over the 8 XCDs (block g -> XCD g % 8).

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void fwd_seq(
       for (int m = 0; m < RPT; m++) store1(yp + m, yb[m]);
     }
     if (more) store_block(buf ^ 1);
-    __syncthreads();
+    lds_barrier();
   }
 
   if (sT) {
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
   int buf = 0;
   for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
     const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
-    __syncthreads();  // staged chunk visible; previous readers of the other buffer done
+    lds_barrier();  // staged chunk visible; previous readers of the other buffer done
     if (c > 0) fetch(c - 1);
     float Sh[CKL + 1][RPT][4];
     {
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
 #pragma unroll
       for (int m = 0; m < RPT; m++) store1(dp + m, dvb[m]);
     }
-    __syncthreads();
+    lds_barrier();
     for (int f = tid; f < ns * 80; f += NT) {
       const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
       f4 s4 = *reinterpret_cast<const f4*>(&red[0][tok][vi][c4 * 4]);
@@ -527,9 +527,29 @@ hipError_t launch_step_t(int B, int H, const void* r, const void* w, const void*
 
 }  // namespace wkv7k
 
+hipError_t wkv7_launch_forward_chunked(int dtype, int B, int T, int H, const void* r, const void* w,
+                                       const void* k, const void* v, const void* a, const void* b,
+                                       const float* s0, void* y, float* sT, float* ckpt, float* ws,
+                                       hipStream_t st);
+
+// Path choice.  The chunked matrix-core kernels run when a chunk workspace
+// is given, T >= 2 chunks and there are fewer than 64 (b, h) pairs; else the
+// token-sequential kernel.  Measured on MI355X (fp32, forward alone): at
+// B*H = 16, T = 8192 the chunked path takes 0.82x the sequential time; at
+// B*H = 64..512 (T = 1024..8192) 1.03-1.22x, because its per-head chunk scan
+// is latency bound while the sequential kernel spreads each head's rows over
+// four workgroups.
+bool wkv7_use_chunked(int B, int T, int H) {
+  return T >= 2 * wkv7k::CKL && (long)B * H < 64;
+}
+
 hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, const void* w,
                                const void* k, const void* v, const void* a, const void* b,
-                               const float* s0, void* y, float* sT, float* ckpt, hipStream_t st) {
+                               const float* s0, void* y, float* sT, float* ckpt, float* chunk_ws,
+                               hipStream_t st) {
+  if (chunk_ws && wkv7_use_chunked(B, T, H))
+    return wkv7_launch_forward_chunked(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, chunk_ws,
+                                       st);
   if (dtype == 1)
     return wkv7k::launch_forward_t<bf16_t>(B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, st);
   return wkv7k::launch_forward_t<float>(B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, st);

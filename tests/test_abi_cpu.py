@@ -54,7 +54,7 @@ MIS = ctypes.c_void_p(4100)    # misaligned
 
 def _fwd(L, B=1, T=4, H=2, N=64, dtype=0, ptrs=None, s0=None):
     p = ptrs or [A] * 7
-    return L.wkv7_forward(B, T, H, N, dtype, *p[:6], s0, p[6], None, None, None)
+    return L.wkv7_forward(B, T, H, N, dtype, *p[:6], s0, p[6], None, None, None, 0, None)
 
 
 def test_forward_rejects_bad_shapes(L):
@@ -72,8 +72,23 @@ def test_forward_rejects_null_and_misaligned(L):
     assert _fwd(L, s0=MIS) == -1 and "s0" in _err(L)
     # bf16 data only needs 8-byte alignment
     mis8 = ctypes.c_void_p(4104)
-    rc = L.wkv7_forward(1, 4, 2, 64, 1, mis8, A, A, A, A, A, None, ctypes.c_void_p(4098), None, None, None)
+    rc = L.wkv7_forward(1, 4, 2, 64, 1, mis8, A, A, A, A, A, None, ctypes.c_void_p(4098), None, None,
+                        None, 0, None)
     assert rc == -1 and "y is not 8-byte aligned" in _err(L)
+
+
+def test_forward_workspace_size_and_check(L):
+    # short sequences run token by token: no workspace
+    assert L.wkv7_forward_workspace_bytes(2, 31, 4, 64) == 0
+    need = L.wkv7_forward_workspace_bytes(2, 64, 4, 64)
+    assert need > 0 and need % 16 == 0
+    assert L.wkv7_forward_workspace_bytes(2, 65, 4, 64) > need  # one more chunk
+    # 64 or more (b, h) pairs take the token-sequential kernel: no workspace
+    assert L.wkv7_forward_workspace_bytes(4, 8192, 32, 64) == 0
+    assert L.wkv7_forward_workspace_bytes(1, 8192, 63, 64) > 0
+    p = [A] * 7
+    rc = L.wkv7_forward(2, 64, 4, 64, 0, *p[:6], None, p[6], None, None, A, need - 4, None)
+    assert rc == -3 and "workspace" in _err(L)
 
 
 def test_backward_needs_workspace_without_checkpoints(L):

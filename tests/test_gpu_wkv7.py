@@ -21,19 +21,19 @@ def _dev(x, dt=torch.float32):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt).contiguous()
 
 
-def _run(hip, d, dtype, with_state):
+def _run(hip, d, dtype, with_state, chunked=True):
     ins = [_dev(d[n], dtype) for n in NAMES]
     s0 = _dev(d["s0"]) if with_state else None
     dsT = _dev(d["dsT"]) if with_state else None
-    y, sT, ck = hip_forward(ins, s0)
+    y, sT, ck = hip_forward(ins, s0, chunked)
     g = hip.wkv7_backward(*ins, _dev(d["dy"], dtype), s0=s0, ckpt=ck, dsT=dsT)
     torch.cuda.synchronize()
     return y, sT, g
 
 
-def hip_forward(ins, s0):
+def hip_forward(ins, s0, chunked=True):
     from rwkv_linear_attention_wkv7_amd import binding
-    return binding.wkv7_forward(*ins, s0=s0, want_ckpt=True)
+    return binding.wkv7_forward(*ins, s0=s0, want_ckpt=True, chunked=chunked)
 
 
 def _check(d, y, sT, g, with_state, ftol, gtol, sel=None):
@@ -61,10 +61,31 @@ def _check(d, y, sT, g, with_state, ftol, gtol, sel=None):
     (2, 130, 2, True),     # many chunks, ragged
     (6, 40, 24, True),     # 144 heads: 32-row forward workgroups, two backward slices
 ])
-def test_wkv7_fp32_parity(hip, B, T, H, with_state):
+@pytest.mark.parametrize("chunked", [True, False])
+def test_wkv7_fp32_parity(hip, B, T, H, with_state, chunked):
+    """chunked: the matrix-core chunked forward (T >= 32) or, False, the
+    token-sequential forward; the backward recomputes from either's
+    checkpoints."""
     d = synth.wkv7_inputs(B, T, H, 64, seed=B * 100 + T, with_state=with_state)
-    y, sT, g = _run(hip, d, torch.float32, with_state)
+    print(f"[wkv7 fp32] B={B} T={T} H={H} state={with_state} chunked={chunked}", flush=True)
+    y, sT, g = _run(hip, d, torch.float32, with_state, chunked)
     _check(d, y, sT, g, with_state, 1e-4, 1e-3)
+
+
+def test_wkv7_extreme_decay(hip):
+    """Decays far outside the time-mix range: chunks whose cumulative decay
+    leaves the matrix-core path's exponent window (w = 1e-3 over a chunk, an
+    exact w = 0) run token by token, others (w = 1: no decay at all) stay on
+    the chunk path; forward and gradients against the oracle, fp32."""
+    d = synth.wkv7_inputs(2, 100, 2, 64, seed=21, with_state=True)
+    w = d["w"].copy()
+    w[:, 16:32] = 1e-3
+    w[0, 40, 1, 5] = 0.0
+    w[:, 64:80] = 1.0
+    d["w"] = w
+    print("[wkv7 extreme decay] B=2 T=100 H=2", flush=True)
+    y, sT, g = _run(hip, d, torch.float32, True)
+    _check(d, y, sT, g, True, 1e-4, 1e-3)
 
 
 def test_wkv7_backward_without_checkpoints(hip):
@@ -80,9 +101,10 @@ def test_wkv7_backward_without_checkpoints(hip):
         assert torch.equal(g1[n], g2[n]), n
 
 
-def test_wkv7_bf16_parity(hip):
+@pytest.mark.parametrize("chunked", [True, False])
+def test_wkv7_bf16_parity(hip, chunked):
     d = synth.wkv7_inputs(2, 200, 3, 64, seed=7, bf16=True, with_state=True)
-    y, sT, g = _run(hip, d, torch.bfloat16, True)
+    y, sT, g = _run(hip, d, torch.bfloat16, True, chunked)
     _check(d, y, sT, g, True, 2e-2, 2e-2)
 
 
@@ -95,6 +117,18 @@ def test_wkv7_bf16_long_context_full_size(hip):
     y, sT, g = _run(hip, d, torch.bfloat16, False)
     for (b, h) in ((0, 0), (3, 31), (1, 17), (2, 5)):
         _check(d, y, sT, g, False, 2e-2, 2e-2, sel=(slice(b, b + 1), slice(h, h + 1)))
+
+
+def test_wkv7_chunked_long_few_heads(hip):
+    """B=1, T=4096, H=16: few (b, h) pairs and a long sequence, the shape the
+    chunked matrix-core forward is chosen for (256 chunks per head, state
+    carried across all of them); fp32, sampled heads against the oracle."""
+    B, T, H = 1, 4096, 16
+    d = synth.wkv7_inputs(B, T, H, 64, seed=13, with_state=True)
+    print(f"[wkv7 chunked long] B={B} T={T} H={H}", flush=True)
+    y, sT, g = _run(hip, d, torch.float32, True, True)
+    for h in (0, 9, 15):
+        _check(d, y, sT, g, True, 1e-4, 1e-3, sel=(slice(0, 1), slice(h, h + 1)))
 
 
 def test_wkv7_state_passing_and_determinism(hip):
