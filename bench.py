@@ -114,13 +114,14 @@ def setup_timemix():
     def cpu():
         from oracle import timemix as otm
         from oracle import wkv7 as ow
-        Bs = 1
+        Bs = B
         t0 = time.perf_counter()
         out, c = otm.forward(p, d["x"][:Bs], H, 1, v_first=d["v_first"][:Bs])
         otm.backward(p, c, d["dout"][:Bs])
         dt = time.perf_counter() - t0
         return dict(value=Bs * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
-                    sample=f"1 of 8 sequences (T=1024, C=768): f64 forward+backward, {dt:.1f} s")
+                    sample=f"the whole workload (8 sequences, T=1024, C=768): f64 forward+backward, "
+                           f"{dt:.1f} s")
 
     cfg = {"workload": "time-mix block forward+backward", "B": B, "T": T, "C": C, "H": H,
            "N": N, "lora_ranks_w_a_v_g": list(ranks), "layer_id": 1, "global_batch": B,
@@ -161,15 +162,15 @@ def setup_wkv7_long():
 
     def cpu():
         from oracle import wkv7 as ow
-        hs = 16
-        sub = [d[n][:1, :, :hs].astype(np.float64) for n in names]
+        sub = [d[n].astype(np.float64) for n in names]
         t0 = time.perf_counter()
         ow.forward(*sub)
-        ow.backward(*sub, d["dy"][:1, :, :hs].astype(np.float64))
+        ow.backward(*sub, d["dy"].astype(np.float64))
         dt = time.perf_counter() - t0
-        return dict(value=(T * hs / H) / dt, unit="tokens/s", cores=ow.num_threads(),
+        return dict(value=(B * T) / dt, unit="tokens/s", cores=ow.num_threads(),
                     kind="oracle",
-                    sample=f"16 of 128 (b,h) pairs, T=8192: f64 forward+backward, {dt:.1f} s")
+                    sample=f"the whole workload (128 (b,h) pairs, T=8192): f64 forward+backward, "
+                           f"{dt:.1f} s")
 
     cfg = {"workload": "WKV7 forward+backward, long context", "B": B, "T": T, "H": H, "N": N,
            "inputs": "bf16", "state": "fp32", "checkpoint_interval": binding.wkv7_checkpoint_interval(),
@@ -228,12 +229,12 @@ def setup_decode():
     nbytes = 2.0 * B * H * 64 * 64 * 4 + 7.0 * B * H * 64 * 4
     roof = dict(kernel="wkv7_step (2048 streams x 4 heads, fp32 state in place)", bound="hbm",
                 work=nbytes, unit="GB/s", peak=PEAK["hbm"][0], fn=dom, key="wkv7_step_decode",
-                src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+                src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_step.hip"])
 
     def cpu():
         from oracle import stack
         from oracle import wkv7 as ow
-        ns, steps = 32, 64
+        ns, steps = 128, 64
         idx = np.arange(ns) * (B // ns)
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
         state = stack.init_state(ocfg, ns)
@@ -295,7 +296,7 @@ def setup_train():
     def cpu():
         from oracle import stack
         from oracle import wkv7 as ow
-        Ts = 64
+        Ts = 256
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
         t0 = time.perf_counter()
         stack.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1])
