@@ -91,7 +91,12 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
   const bool split = batch.count == 1 && gridDim.z > 1;
   const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
   const int M = P.M, N = P.N, K = P.K, lda = P.lda, ldb = P.ldb;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so the
+  // remap hands each XCD a contiguous band of output tiles (row-major), whose
+  // A row panels it then reads alone through its own L2.
+  const int gx = gridDim.x;
+  const int lin = xcd_remap(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
+  const int m0 = (lin / gx) * BM, n0 = (lin % gx) * BN;
   if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
   const float* __restrict__ A = P.A;
   const float* __restrict__ B = P.B;
@@ -334,7 +339,12 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
   const bool split = batch.count == 1 && gridDim.z > 1;
   const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
   const int M = P.M, N = P.N, K = P.K;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so the
+  // remap hands each XCD a contiguous band of output tiles (row-major), whose
+  // A row panels it then reads alone through its own L2.
+  const int gx = gridDim.x;
+  const int lin = xcd_remap(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
+  const int m0 = (lin / gx) * BM, n0 = (lin % gx) * BN;
   if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
   float* __restrict__ C = P.C;
   const int ldc = split ? N : P.ldc;
