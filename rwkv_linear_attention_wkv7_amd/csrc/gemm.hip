@@ -471,20 +471,25 @@ hipError_t launch_bk(const GemmBatch& b, int gz, int kslice, int klen, hipStream
 
 template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
-  // Largest tile whose grid still gives every CU work (>= 256 workgroups),
-  // else the smallest tile.
+  // Largest tile whose grid reaches 512 workgroups, or 256 when each workgroup
+  // still has >= 8M multiply-adds; else the smallest tile.  Small problems
+  // (the decode stack's 2048-row products) are latency bound and gain from
+  // more, smaller workgroups; large ones keep the 128x128 tile.  Measured on
+  // MI355X, fp32: 2048x256x256 7.2 us at 32x32 vs 8.6 at 64x32 and 11.6 at
+  // 64x64; 2048x1024x256 17.5 us at 64x64 vs 20.0 at 128x64.
   int maxM = 0, maxN = 0;
   for (int i = 0; i < b.count; i++) {
     maxM = max(maxM, b.p[i].M);
     maxN = max(maxN, b.p[i].N);
   }
-  auto blocks = [&](int bm, int bn) {
-    return (long)((maxM + bm - 1) / bm) * ((maxN + bn - 1) / bn) * gz;
+  auto fits = [&](int bm, int bn) {
+    const long wg = (long)((maxM + bm - 1) / bm) * ((maxN + bn - 1) / bn) * gz;
+    return maxN >= bn && (wg >= 512 || (wg >= 256 && (long)bm * bn * klen >= (8l << 20)));
   };
-  if (blocks(128, 128) >= 256 && maxN >= 128) return launch_bk<PREC, 4, 4, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(128, 64) >= 256 && maxN >= 64) return launch_bk<PREC, 4, 2, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(64, 64) >= 256 && maxN >= 64) return launch_bk<PREC, 2, 2, TA, TB>(b, gz, kslice, klen, st);
-  if (blocks(64, 32) >= 256) return launch_bk<PREC, 2, 1, TA, TB>(b, gz, kslice, klen, st);
+  if (fits(128, 128)) return launch_bk<PREC, 4, 4, TA, TB>(b, gz, kslice, klen, st);
+  if (fits(128, 64)) return launch_bk<PREC, 4, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (fits(64, 64)) return launch_bk<PREC, 2, 2, TA, TB>(b, gz, kslice, klen, st);
+  if (fits(64, 32)) return launch_bk<PREC, 2, 1, TA, TB>(b, gz, kslice, klen, st);
   return launch_bk<PREC, 1, 1, TA, TB>(b, gz, kslice, klen, st);
 }
 
