@@ -307,7 +307,7 @@ int check_weights(const tm_shape* s, const tm_weights* W) {
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
-                    float out_beta = 0.f, int prec = GEMM_F32) {
+                    float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false) {
   const int BT = B * T, C = s->C;
   TmFwd p;
   memset(&p, 0, sizeof(p));
@@ -322,27 +322,34 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
   p.y = m.y; p.r = m.r; p.g = m.g; p.r_k = W->r_k; p.ln_w = W->ln_w; p.ln_b = W->ln_b;
   p.tg = m.tg; p.mean = m.mean; p.rstd = m.rstd; p.alpha = m.alpha;
 
-  HIPCHK(tm_launch_shift_fwd(p, st), "token shift");
+  // shifted: the caller already wrote xr..xg (and x_last) with its LayerNorm
+  if (!shifted) HIPCHK(tm_launch_shift_fwd(p, st), "token shift");
   auto prob = [](int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
                  int ldc, int epi) {
     return GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, 0.f, epi, nullptr, nullptr};
   };
-  {  // r, k, v projections: one launch
+  {  // r, k, v projections and the LoRA down-projections (tanh for w, sigmoid
+     // for g).  Decode (latency bound, 2048-row products) runs them as one
+     // launch; larger token batches as two, so the thin LoRA products keep
+     // tiles of their own size.
     GemmBatch g;
     g.count = 3;
     g.p[0] = prob(BT, C, C, m.xr, C, W->Wr, C, m.r, C, EPI_NONE);
     g.p[1] = prob(BT, C, C, m.xk, C, W->Wk, C, m.k, C, EPI_NONE);
     g.p[2] = prob(BT, C, C, m.xv, C, W->Wv, C, m.v, C, EPI_NONE);
-    HIPCHK(gemm_batch(prec, false, false, g, st), "r/k/v proj");
-  }
-  {  // LoRA down-projections (tanh for w, sigmoid for g): one launch
-    GemmBatch g;
-    g.count = 3;
-    g.p[0] = prob(BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, EPI_TANH);
-    g.p[1] = prob(BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, EPI_NONE);
-    g.p[2] = prob(BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, EPI_SIGMOID);
-    if (s->layer_id > 0) g.p[g.count++] = prob(BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, EPI_NONE);
-    HIPCHK(gemm_batch(prec, false, false, g, st), "lora down");
+    GemmBatch l;
+    l.count = 3;
+    l.p[0] = prob(BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, EPI_TANH);
+    l.p[1] = prob(BT, s->Da, C, m.xa, C, W->A1, s->Da, m.la, s->Da, EPI_NONE);
+    l.p[2] = prob(BT, s->Dg, C, m.xg, C, W->G1, s->Dg, m.sg, s->Dg, EPI_SIGMOID);
+    if (s->layer_id > 0) l.p[l.count++] = prob(BT, s->Dv, C, m.xv, C, W->V1, s->Dv, m.lv, s->Dv, EPI_NONE);
+    if (decode) {
+      for (int i = 0; i < l.count; i++) g.p[g.count++] = l.p[i];
+      HIPCHK(gemm_batch(prec, false, false, g, st), "r/k/v + lora down");
+    } else {
+      HIPCHK(gemm_batch(prec, false, false, g, st), "r/k/v proj");
+      HIPCHK(gemm_batch(prec, false, false, l, st), "lora down");
+    }
   }
   {  // LoRA up-projections: one launch
     GemmBatch g;
@@ -677,10 +684,18 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
     float* axp = att_x_prev + (size_t)l * BC;
     float* ast = att_state + (size_t)l * B * H * NN;
     float* fxp = ffn_x_prev + (size_t)l * BC;
-    HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln1_w, bl.ln1_b, d.h, nullptr, nullptr, st), "ln1");
-    CHK(tm_forward_impl(&s, &bl.tm, B, 1, d.h, axp, d.vf, ast, ast, d.x, axp, d.tm, st, true, 1.f, prec));
-    HIPCHK(stk_launch_layernorm(B, C, d.x, bl.ln2_w, bl.ln2_b, d.h, nullptr, nullptr, st), "ln2");
-    HIPCHK(stk_launch_cm_shift(B, 1, C, d.h, fxp, bl.cm_mu_k, d.sh, fxp, st), "cm shift");
+    {  // LN1 fused with the six time-mix lerps; att_x_prev <- this token's LN1 output
+      LnMix lm{B, C, 6, d.x, bl.ln1_w, bl.ln1_b, axp, axp,
+               {bl.tm.mu_r, bl.tm.mu_w, bl.tm.mu_k, bl.tm.mu_v, bl.tm.mu_a, bl.tm.mu_g},
+               {d.tm.xr, d.tm.xw, d.tm.xk, d.tm.xv, d.tm.xa, d.tm.xg}};
+      HIPCHK(stk_launch_ln_mix(lm, st), "ln1 + shift");
+    }
+    CHK(tm_forward_impl(&s, &bl.tm, B, 1, nullptr, nullptr, d.vf, ast, ast, d.x, nullptr, d.tm, st, true,
+                        1.f, prec, true));
+    {  // LN2 fused with the channel-mix lerp; ffn_x_prev <- this token's LN2 output
+      LnMix lm{B, C, 1, d.x, bl.ln2_w, bl.ln2_b, fxp, fxp, {bl.cm_mu_k}, {d.sh}};
+      HIPCHK(stk_launch_ln_mix(lm, st), "ln2 + shift");
+    }
     HIPCHK(gemm_run(prec, false, false, B, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
     HIPCHK(gemm_run(prec, false, false, B, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
   }

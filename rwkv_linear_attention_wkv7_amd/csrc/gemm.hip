@@ -19,7 +19,7 @@
 // values of the four steps next to each other, so a row-major operand yields
 // its fragments for four MFMAs in one 16-byte LDS read.  Deep K tiles (BK up
 // to 128) keep small-tile launches from paying one global round trip per 32 k.  A launch may carry
-// up to four independent problems of the same layout (blockIdx.z selects the
+// up to eight independent problems of the same layout (blockIdx.z selects the
 // problem; workgroups outside a smaller problem's grid exit), or one problem
 // split along K (blockIdx.z selects the slice, partials summed by
 // splitk_reduce).  Any M is allowed; the dimensions read as float4 must be

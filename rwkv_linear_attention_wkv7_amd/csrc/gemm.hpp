@@ -10,7 +10,7 @@ enum GemmEpi {
   EPI_SQRELU_BWD = 6  // acc * 2 relu(f) with aux = relu(f)^2 (so relu(f) = sqrt(aux))
 };
 
-constexpr int GEMM_MAX_BATCH = 4;
+constexpr int GEMM_MAX_BATCH = 8;
 
 enum GemmPrec { GEMM_F32 = 0, GEMM_BF16 = 1 };
 

@@ -94,6 +94,53 @@ __global__ __launch_bounds__(256) void cm_shift(int BT, int T, int C, const floa
   }
 }
 
+// One token per stream (T = 1): LayerNorm of each row fused with the token
+// shift lerps that consume it.  h = LN(x); out_m = h + (prev - h) mu_m for
+// each mix m, prev = the previous token's LN output (x_prev, or 0); x_last
+// receives h (it may be x_prev: each lane reads its prev before writing).
+// One wave per row, the row in registers as in layernorm_fwd.
+template <int MAXC4>
+__global__ __launch_bounds__(256) void ln_mix(LnMix p) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.R) return;
+  const int C = p.C, C4 = C / 4;
+  const f4* xr = reinterpret_cast<const f4*>(p.x + (size_t)row * C);
+  f4 v[MAXC4];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) {
+    const int c4 = lane + 64 * j;
+    v[j] = c4 < C4 ? xr[c4] : f4{0.f, 0.f, 0.f, 0.f};
+    s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
+  }
+  const float mean = wavesum(s) / C;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) {
+    const int c4 = lane + 64 * j;
+    if (c4 < C4) {
+      const f4 d = v[j] - mean;
+      q += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wavesum(q) / C + LN_EPS);
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) {
+    const int c4 = lane + 64 * j;
+    if (c4 < C4) {
+      const size_t e = (size_t)row * C + 4 * c4;
+      const f4 h = (v[j] - mean) * rstd * reinterpret_cast<const f4*>(p.w)[c4] +
+                   reinterpret_cast<const f4*>(p.b)[c4];
+      const f4 prev = p.x_prev ? *reinterpret_cast<const f4*>(p.x_prev + e) : f4{0.f, 0.f, 0.f, 0.f};
+      if (p.x_last) *reinterpret_cast<f4*>(p.x_last + e) = h;
+      const f4 d = prev - h;
+      for (int m = 0; m < p.nmix; m++)
+        *reinterpret_cast<f4*>(p.out[m] + e) = h + d * reinterpret_cast<const f4*>(p.mu[m])[c4];
+    }
+  }
+}
+
 }  // namespace stk
 
 static unsigned grid_for(size_t n4) {
@@ -133,6 +180,18 @@ hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float
   return hipGetLastError();
 }
 int stk_max_layernorm_width() { return 64 * 4 * stk::MAXC4_LIMIT; }
+
+hipError_t stk_launch_ln_mix(const LnMix& p, hipStream_t st) {
+  const dim3 g((p.R + 3) / 4), t(256);
+  switch (ln_chunks(p.C)) {
+    case 1: hipLaunchKernelGGL(stk::ln_mix<1>, g, t, 0, st, p); break;
+    case 2: hipLaunchKernelGGL(stk::ln_mix<2>, g, t, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(stk::ln_mix<4>, g, t, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(stk::ln_mix<8>, g, t, 0, st, p); break;
+    default: hipLaunchKernelGGL(stk::ln_mix<16>, g, t, 0, st, p); break;
+  }
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------ training kernels --
 namespace stk {

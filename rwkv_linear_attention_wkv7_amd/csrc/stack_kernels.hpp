@@ -8,6 +8,17 @@ hipError_t stk_launch_layernorm(int R, int C, const float* x, const float* w, co
                                 float* y, float* mean, float* rstd, hipStream_t st);
 hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float* x_prev,
                                const float* mu, float* sh, float* x_last, hipStream_t st);
+
+// LayerNorm fused with up to six token-shift lerps, one token per row (T = 1).
+struct LnMix {
+  int R, C, nmix;
+  const float *x, *w, *b;
+  const float* x_prev;  // previous token's LN output per row, or NULL (zeros)
+  float* x_last;        // receives this token's LN output (may equal x_prev)
+  const float* mu[6];
+  float* out[6];
+};
+hipError_t stk_launch_ln_mix(const LnMix& p, hipStream_t st);
 int stk_max_layernorm_width();
 int stk_num_ln_blocks(int R);
 int stk_num_shift_blocks(int BT);
