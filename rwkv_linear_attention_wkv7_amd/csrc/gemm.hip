@@ -75,6 +75,20 @@ __device__ __forceinline__ void store_acc(const GemmProblem& P, bool split, floa
   }
 }
 
+// Output tile of this workgroup.  Workgroups go round-robin over the 8 XCDs;
+// xcd_remap hands each XCD a contiguous range of logical tile ids, and the
+// logical order walks groups of 8 tile rows column by column, so the A row
+// panels of a group stay in the XCD's L2 while the B column panels stream
+// past once per group.
+__device__ __forceinline__ void tile_origin(int BM, int BN, int& m0, int& n0) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int lin = xcd_remap(blockIdx.y * gx + blockIdx.x, gx * gy);
+  const int per_group = 8 * gx, gid = lin / per_group, first = gid * 8;
+  const int gsz = min(8, gy - first), local = lin - gid * per_group;
+  m0 = (first + local % gsz) * BM;
+  n0 = (local / gsz) * BN;
+}
+
 template <int TI, int TJ, int BK, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
   constexpr int BM = 32 * TI, BN = 32 * TJ;
@@ -91,12 +105,8 @@ __global__ __launch_bounds__(256) void gemm_f32(GemmBatch batch, int kslice) {
   const bool split = batch.count == 1 && gridDim.z > 1;
   const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
   const int M = P.M, N = P.N, K = P.K, lda = P.lda, ldb = P.ldb;
-  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so the
-  // remap hands each XCD a contiguous band of output tiles (row-major), whose
-  // A row panels it then reads alone through its own L2.
-  const int gx = gridDim.x;
-  const int lin = xcd_remap(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
-  const int m0 = (lin / gx) * BM, n0 = (lin % gx) * BN;
+  int m0, n0;
+  tile_origin(BM, BN, m0, n0);
   if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
   const float* __restrict__ A = P.A;
   const float* __restrict__ B = P.B;
@@ -339,12 +349,8 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
   const bool split = batch.count == 1 && gridDim.z > 1;
   const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
   const int M = P.M, N = P.N, K = P.K;
-  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so the
-  // remap hands each XCD a contiguous band of output tiles (row-major), whose
-  // A row panels it then reads alone through its own L2.
-  const int gx = gridDim.x;
-  const int lin = xcd_remap(blockIdx.y * gx + blockIdx.x, gx * gridDim.y);
-  const int m0 = (lin / gx) * BM, n0 = (lin % gx) * BN;
+  int m0, n0;
+  tile_origin(BM, BN, m0, n0);
   if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
   float* __restrict__ C = P.C;
   const int ldc = split ? N : P.ldc;
