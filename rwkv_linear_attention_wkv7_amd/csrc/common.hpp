@@ -83,6 +83,13 @@ __device__ __forceinline__ f4 raw4_to_f4<bf16_t>(uint2 u) {
 }
 
 template <typename T>
+__device__ __forceinline__ float raw1_to_f32(typename Raw<T>::v1 x);
+template <>
+__device__ __forceinline__ float raw1_to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float raw1_to_f32<bf16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+template <typename T>
 __device__ __forceinline__ float load1(const T* p);
 template <>
 __device__ __forceinline__ float load1<float>(const float* p) { return *p; }

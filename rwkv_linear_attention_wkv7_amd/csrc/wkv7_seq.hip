@@ -48,9 +48,11 @@ __global__ __launch_bounds__(256) void fwd_seq(
     float* __restrict__ sT, float* __restrict__ ckpt) {
   constexpr int ROWS = 16 * RPT;
   constexpr int NRB = N / ROWS;
-  // raw (unconverted) staging: r, w, k, a, b of each token, v of this slice
-  __shared__ __attribute__((aligned(16))) T sv[2][TT][5][N];
-  __shared__ __attribute__((aligned(16))) T svv[2][TT][ROWS];
+  // staging: r, w, k, a, b of each token and v of this slice travel raw
+  // (unconverted) through registers and are widened to fp32 once, when the
+  // block is written to LDS (every value is read by all 16 row groups)
+  __shared__ __attribute__((aligned(16))) float sv[2][TT][5][N];
+  __shared__ __attribute__((aligned(16))) float svv[2][TT][ROWS];
   typedef typename Raw<T>::v4 R4;
   typedef typename Raw<T>::v1 R1;
 
@@ -108,14 +110,14 @@ __global__ __launch_bounds__(256) void fwd_seq(
     for (int q = 0; q < NV4_PER; q++) {
       const int f = tid + 256 * q;
       const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-      store_raw4(&sv[buf][tok][vi][c4 * 4], pre[q]);
+      *reinterpret_cast<f4*>(&sv[buf][tok][vi][c4 * 4]) = raw4_to_f4<T>(pre[q]);
     }
 #pragma unroll
     for (int q = 0; q < NVV_PER; q++) {
       const int f = tid + 256 * q;
       if (f < TT * ROWS) {
         const int tok = f / ROWS, rr = f - tok * ROWS;
-        store_raw1(&svv[buf][tok][rr], prev[q]);
+        svv[buf][tok][rr] = raw1_to_f32<T>(prev[q]);
       }
     }
   };
@@ -202,10 +204,11 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     float* __restrict__ ds0) {
   constexpr int ROWS = RPT * RG, NSPLIT = N / ROWS, NW = RG / 4, NT = 16 * RG;
   static_assert(RG % 4 == 0, "whole waves");
-  // raw staging, double-buffered: the next (earlier) chunk is fetched into
-  // registers while the current one is processed
-  __shared__ __attribute__((aligned(16))) T sv[2][CKL][5][N];   // r, w, k, a, b
-  __shared__ __attribute__((aligned(16))) T svr[2][CKL][2][ROWS];  // v, dy of this slice
+  // staging, double-buffered, widened to fp32 once on the way into LDS: the
+  // next (earlier) chunk is fetched raw into registers while the current one
+  // is processed
+  __shared__ __attribute__((aligned(16))) float sv[2][CKL][5][N];   // r, w, k, a, b
+  __shared__ __attribute__((aligned(16))) float svr[2][CKL][2][ROWS];  // v, dy of this slice
   __shared__ __attribute__((aligned(16))) float red[NW][CKL][5][N];  // per-wave column partials
   typedef typename Raw<T>::v4 R4;
   typedef typename Raw<T>::v1 R1;
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
       const int f = tid + NT * q;
       if (f < CKL * 80) {
         const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-        store_raw4(&sv[buf][tok][vi][c4 * 4], xa[q]);
+        *reinterpret_cast<f4*>(&sv[buf][tok][vi][c4 * 4]) = raw4_to_f4<T>(xa[q]);
       }
     }
 #pragma unroll
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
       const int f = tid + NT * q;
       if (f < CKL * 2 * ROWS) {
         const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
-        store_raw1(&svr[buf][tok][vi][i], xb[q]);
+        svr[buf][tok][vi][i] = raw1_to_f32<T>(xb[q]);
       }
     }
   };
@@ -395,18 +398,41 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
 }
 
 // out_vec = sum over slices of part[slice][vec] (fixed order), cast to T.
-template <typename T>
-__global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int nsplit,
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4,
                                                            const float* __restrict__ part, T* dr,
                                                            T* dk, T* db, T* dw, T* da) {
-  const size_t n4 = plane4 * 5;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    const int vi = (int)(i / plane4);
-    const size_t e4 = i - (size_t)vi * plane4;
-    f4 s = reinterpret_cast<const f4*>(part)[((size_t)0 * 5 + vi) * plane4 + e4];
-    for (int sp = 1; sp < nsplit; sp++) s += reinterpret_cast<const f4*>(part)[((size_t)sp * 5 + vi) * plane4 + e4];
-    T* o = vi == 0 ? dr : vi == 1 ? dk : vi == 2 ? db : vi == 3 ? dw : da;
-    store4(o + e4 * 4, s);
+  // U float4 per thread per pass, every slice's loads issued together
+  // (clamped indices, guarded stores): enough loads in flight to stream the
+  // partials at HBM rate.  The slices are summed in slice order.
+  constexpr int U = 4;
+  const size_t n4 = plane4 * 5, stride = (size_t)gridDim.x * 256;
+  const f4* P = reinterpret_cast<const f4*>(part);
+  for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n4; i0 += stride * U) {
+    f4 s[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const size_t i = min(i0 + u * stride, n4 - 1);
+      const int vi = (int)(i / plane4);
+      const size_t e4 = i - (size_t)vi * plane4;
+      f4 x[NS];
+#pragma unroll
+      for (int sp = 0; sp < NS; sp++)
+        x[sp] = __builtin_nontemporal_load(P + ((size_t)sp * 5 + vi) * plane4 + e4);
+      s[u] = x[0];
+#pragma unroll
+      for (int sp = 1; sp < NS; sp++) s[u] += x[sp];
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const size_t i = i0 + u * stride;
+      if (i < n4) {
+        const int vi = (int)(i / plane4);
+        const size_t e4 = i - (size_t)vi * plane4;
+        T* o = vi == 0 ? dr : vi == 1 ? dk : vi == 2 ? db : vi == 3 ? dw : da;
+        store4(o + e4 * 4, s[u]);
+      }
+    }
   }
 }
 
@@ -462,10 +488,14 @@ hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t plane4 = (size_t)B * T_ * H * N / 4;
-  size_t blocks = (plane4 * 5 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL((reduce_bwd_partials<T>), dim3((unsigned)blocks), dim3(256), 0, st, plane4, ns,
-                     part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+  size_t blocks = (plane4 * 5 + 1023) / 1024;
+  if (blocks > 4096) blocks = 4096;
+  if (ns == 4)
+    hipLaunchKernelGGL((reduce_bwd_partials<T, 4>), dim3((unsigned)blocks), dim3(256), 0, st, plane4,
+                       part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+  else
+    hipLaunchKernelGGL((reduce_bwd_partials<T, 2>), dim3((unsigned)blocks), dim3(256), 0, st, plane4,
+                       part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
   return hipGetLastError();
 }
 
