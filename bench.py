@@ -296,7 +296,7 @@ def setup_train():
     def cpu():
         from oracle import stack
         from oracle import wkv7 as ow
-        Ts = 256
+        Ts = 768
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
         t0 = time.perf_counter()
         stack.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1])

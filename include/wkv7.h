@@ -204,10 +204,16 @@ int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
  * products in every projection, LoRA, channel-mix and head GEMM: WKV7_F32
  * (fp32 operands) or WKV7_BF16 (operands rounded to bf16 to nearest even,
  * fp32 accumulation, as wkv7_gemm_bf16).  Tensors stay fp32 in memory either
- * way; the WKV7 recurrence and every elementwise step are fp32. */
+ * way; the WKV7 recurrence and every elementwise step are fp32.
+ * train_recompute (rwkv7_train_step only): 0 keeps every block's forward
+ * activations in the workspace for its backward (about 1.1 GB per block at
+ * B=4, T=2048, C=1024, F=4096); 1 keeps only the block inputs and recomputes
+ * each block's forward in the backward (workspace for one block, one more
+ * forward pass per step).  Results are identical. */
 typedef struct {
   int n_layer, C, H, N, F, V, Dw, Da, Dv, Dg, use_ln0;
   int gemm_dtype;
+  int train_recompute;
 } rwkv7_config;
 
 /* One block: LayerNorms, time-mix weights (layer_id = block index) and the

@@ -34,7 +34,7 @@ class TmGrads(ctypes.Structure):
 
 class Rwkv7Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layer", "C", "H", "N", "F", "V", "Dw", "Da", "Dv",
-                                            "Dg", "use_ln0", "gemm_dtype")]
+                                            "Dg", "use_ln0", "gemm_dtype", "train_recompute")]
 
 
 class Rwkv7Block(ctypes.Structure):
@@ -354,7 +354,9 @@ class DecodeModel:
 
     def __init__(self, cfg, weights):
         """cfg: dict n_layer, C, H, F, V, ranks=(Dw, Da, Dv, Dg), use_ln0,
-        gemm_dtype ('f32' default, or 'bf16': bf16 operands, fp32 accumulation).
+        gemm_dtype ('f32' default, or 'bf16': bf16 operands, fp32 accumulation),
+        train_recompute (0 default: keep every block's activations for the
+        training step's backward; 1: recompute each block from its input).
         weights: dict of device tensors as laid out by synth.stack_model."""
         L, C, H, F, V = cfg["n_layer"], cfg["C"], cfg["H"], cfg["F"], cfg["V"]
         Dw, Da, Dv, Dg = cfg["ranks"]
@@ -362,7 +364,7 @@ class DecodeModel:
         if gd not in ("f32", "bf16"):
             raise ValueError(f"gemm_dtype must be 'f32' or 'bf16', not {gd!r}")
         self.cfg = Rwkv7Config(L, C, H, 64, F, V, Dw, Da, Dv, Dg, int(cfg.get("use_ln0", 1)),
-                               1 if gd == "bf16" else 0)
+                               1 if gd == "bf16" else 0, int(cfg.get("train_recompute", 0)))
         self.w = weights
         blocks = (Rwkv7Block * L)()
         for l, bw in enumerate(weights["blocks"]):

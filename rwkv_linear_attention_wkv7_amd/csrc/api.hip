@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "../../include/wkv7.h"
 #include "common.hpp"
@@ -611,6 +612,8 @@ int check_cfg(const rwkv7_config* c, int B) {
   if (c->N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", c->N);
   if (c->gemm_dtype != WKV7_F32 && c->gemm_dtype != WKV7_BF16)
     return fail(WKV7_EINVAL, "gemm_dtype must be WKV7_F32 or WKV7_BF16");
+  if (c->train_recompute != 0 && c->train_recompute != 1)
+    return fail(WKV7_EINVAL, "train_recompute must be 0 or 1");
   if (c->H < 1 || c->C != c->H * c->N) return fail(WKV7_EINVAL, "C=%d must equal H*N", c->C);
   if (c->C > stk_max_layernorm_width()) return fail(WKV7_EINVAL, "C=%d above the supported %d", c->C, stk_max_layernorm_width());
   if (c->n_layer < 1 || B < 1) return fail(WKV7_EINVAL, "n_layer and B must be >= 1");
@@ -707,11 +710,17 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
 // ---------------------------------------------------------- training step --
 namespace {
 
-struct TrainBufs {
-  float *block_in, *x_emb, *vf, *dvf, *h, *x1, *h2, *sh, *dsh, *dh, *dx, *dx1;
-  float *ka, *dfk, *logits, *loss_row, *part_ln, *part_cm, *splitk;
-  int *count, *off, *perm;
+// Activations of one block kept from the forward for its backward.
+struct BlockActs {
+  float *h, *x1, *h2, *sh, *ka;  // LN1 out, x + TM, LN2 out, cm shift, relu(sh Wk)^2
   TmCache tm;
+};
+
+struct TrainBufs {
+  float *block_in, *x_emb, *vf, *dvf, *h, *dsh, *dh, *dx, *dx1;
+  float *dfk, *logits, *loss_row, *part_ln, *part_cm, *splitk;
+  int *count, *off, *perm;
+  std::vector<BlockActs> act;  // every block's (train_recompute == 0), or one reused
   TmBwdBufs tb;
 };
 
@@ -723,9 +732,8 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   const size_t BT = (size_t)B * T, tok = BT * cfg->C, L = cfg->n_layer;
   t.block_in = c.take((L + 1) * tok);
   t.x_emb = cfg->use_ln0 ? c.take(tok) : nullptr;
-  float** toks[] = {&t.vf, &t.dvf, &t.h, &t.x1, &t.h2, &t.sh, &t.dsh, &t.dh, &t.dx, &t.dx1};
+  float** toks[] = {&t.vf, &t.dvf, &t.h, &t.dsh, &t.dh, &t.dx, &t.dx1};
   for (float** p : toks) *p = c.take(tok);
-  t.ka = c.take(BT * cfg->F);
   t.dfk = c.take(BT * cfg->F);
   t.logits = c.take(BT * cfg->V);
   t.loss_row = c.take(BT);
@@ -739,8 +747,18 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   t.count = (int*)c.take((size_t)V);
   t.off = (int*)c.take((size_t)V);
   t.perm = (int*)c.take(BT);
+  const bool keep = cfg->train_recompute == 0;
+  t.act.resize(keep ? L : 1);
+  for (size_t i = 0; i < t.act.size(); i++) {
+    BlockActs& a = t.act[i];
+    float** bt[] = {&a.h, &a.x1, &a.h2, &a.sh};
+    for (float** p : bt) *p = c.take(tok);
+    a.ka = c.take(BT * cfg->F);
+    // a reused set is sized for a block with the value-residual LoRA (layer > 0)
+    tm_shape s = block_shape(cfg, keep ? (int)i : 1);
+    carve_cache(c, &s, B, T, a.tm);
+  }
   tm_shape s = block_shape(cfg, 1);
-  carve_cache(c, &s, B, T, t.tm);
   carve_bwd(c, &s, B, T, t.tb);
 }
 
@@ -819,18 +837,31 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
   if (cfg->use_ln0)
     HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
-  for (int l = 0; l < L; l++) {
+  const bool keep = cfg->train_recompute == 0;
+  // one block forward from bin(l) into bin(l+1), activations into a
+  auto block_fwd = [&](int l, BlockActs& a) -> int {
     const rwkv7_block& bl = M->blocks[l];
     tm_shape s = block_shape(cfg, l);
-    float* xo = bin(l + 1);
-    HIPCHK(hipMemcpyAsync(xo, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
-    CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, xo, nullptr, t.tm, st,
+    HIPCHK(hipMemcpyAsync(a.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
+    CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, nullptr, a.x1, nullptr, a.tm, st,
                         false, 1.f, prec));
-    HIPCHK(stk_launch_layernorm(BT, C, xo, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
-    HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
-    HIPCHK(gemm_run(prec, false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(gemm_run(prec, false, false, BT, C, F, t.ka, F, bl.cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+    HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
+    HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    return WKV7_OK;
+  };
+
+  // ---------------- forward (every block's activations, or only its input, kept)
+  HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
+  if (cfg->use_ln0)
+    HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
+  for (int l = 0; l < L; l++) {
+    BlockActs& a = t.act[keep ? l : 0];
+    CHK(block_fwd(l, a));
+    float* xo = bin(l + 1);
+    HIPCHK(hipMemcpyAsync(xo, a.x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, a.ka, F, M->blocks[l].cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(L), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
@@ -847,30 +878,24 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     const rwkv7_block& bl = M->blocks[l];
     rwkv7_block_grads& gb = G->blocks[l];
     tm_shape s = block_shape(cfg, l);
-    // recompute this block's forward from its cached input
-    HIPCHK(hipMemcpyAsync(t.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, t.h, nullptr, nullptr, st), "ln1");
-    CHK(tm_forward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, nullptr, t.x1, nullptr, t.tm, st,
-                        false, 1.f, prec));
-    HIPCHK(stk_launch_layernorm(BT, C, t.x1, bl.ln2_w, bl.ln2_b, t.h2, nullptr, nullptr, st), "ln2");
-    HIPCHK(stk_launch_cm_shift(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.sh, nullptr, st), "cm shift");
-    HIPCHK(gemm_run(prec, false, false, BT, F, C, t.sh, C, bl.cm_Wk, F, t.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    BlockActs& a = t.act[keep ? l : 0];
+    if (!keep) CHK(block_fwd(l, a));  // recompute this block's forward from its input
     // channel-mix backward
-    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, t.ka, 1, nullptr, st), "dfk");
-    HIPCHK(gemm_run(prec, true, false, F, C, BT, t.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
+    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "dfk");
+    HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                         splitk_for(F, C, BT), t.splitk, st), "dWv");
     HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
-    HIPCHK(gemm_run(prec, true, false, C, F, BT, t.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
+    HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
                         splitk_for(C, F, BT), t.splitk, st), "dWk");
-    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, t.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
+    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
       HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT), C, o, st), "cm mu grad");
     }
-    HIPCHK(stk_launch_layernorm_bwd(BT, C, t.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
     HIPCHK(reduce_ln(gb.ln2_w, gb.ln2_b), "ln2 grads");
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
-    CHK(tm_backward_impl(&s, &bl.tm, B, T, t.h, nullptr, t.vf, nullptr, t.dx1, nullptr, t.tm, t.tb,
+    CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
                          nullptr, st, prec));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");

@@ -36,16 +36,17 @@ def _dev_model(m):
     return out
 
 
-def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0, gemm="f32"):
+def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0, gemm="f32", recompute=0):
     from rwkv_linear_attention_wkv7_amd import binding
     m = synth.stack_model(C, H, F, V, L, ranks, seed=seed, perturbed=perturbed, std=std,
                           use_ln0=use_ln0)
     dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks,
-                                  use_ln0=int(use_ln0), gemm_dtype=gemm), _dev_model(m))
+                                  use_ln0=int(use_ln0), gemm_dtype=gemm, train_recompute=recompute),
+                             _dev_model(m))
     grads = binding.TrainGrads(dm)
     tok = synth.token_ids(B, T + 1, V, seed=seed + 100)
     x, y = np.ascontiguousarray(tok[:, :-1]), np.ascontiguousarray(tok[:, 1:])
-    print(f"[train] L={L} C={C} F={F} V={V} B={B} T={T} gemm={gemm}", flush=True)
+    print(f"[train] L={L} C={C} F={F} V={V} B={B} T={T} gemm={gemm} recompute={recompute}", flush=True)
     loss = hip.rwkv7_train_step(dm, grads, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
     torch.cuda.synchronize()
     return m, dm, grads, x, y, float(loss.item())
@@ -111,7 +112,8 @@ def test_train_step_full_model_short_batch(hip, gemm):
 
 @pytest.mark.parametrize("gemm", ["f32", "bf16"])
 def test_train_step_full_config_properties(hip, gemm):
-    """B=4, T=2048 at the full model size.  At random init the LN output rows
+    """B=4, T=2048 at the full model size, every block's activations kept, and
+    the same step recomputing each block from its input.  At random init the LN output rows
     have unit variance and the head entries N(0, 0.02^2), so the logits are
     ~N(0, s2) with s2 = C 0.02^2 and the expected loss is
     E[logsumexp] - E[z_target] = ln(V) + s2/2 (log of the mean of e^z);
@@ -122,6 +124,17 @@ def test_train_step_full_config_properties(hip, gemm):
     m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 4, 2048, seed=0,
                                     perturbed=False, std=0.02, use_ln0=False, gemm=gemm)
     expect = math.log(V) + C * 0.02 ** 2 / 2
+    # the one-block workspace that recomputes each block gives the same bits
+    dm_r = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=(64, 64, 32, 128), use_ln0=0,
+                                    gemm_dtype=gemm, train_recompute=1), dm.w)
+    gr = binding.TrainGrads(dm_r)
+    loss_r = binding.rwkv7_train_step(dm_r, gr, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    assert float(loss_r.item()) == loss
+    assert torch.equal(gr.g["emb"], grads.g["emb"])
+    assert torch.equal(gr.g["blocks"][0]["tm"]["Wr"], grads.g["blocks"][0]["tm"]["Wr"])
+    assert torch.equal(gr.g["blocks"][23]["cm_Wk"], grads.g["blocks"][23]["cm_Wk"])
+    del gr, dm_r
     assert abs(loss - expect) < 3e-2, (loss, expect)
     first = {"emb": grads.g["emb"].clone(), "head": grads.g["head"].clone(),
              "Wr0": grads.g["blocks"][0]["tm"]["Wr"].clone(),
