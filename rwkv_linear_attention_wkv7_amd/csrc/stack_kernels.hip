@@ -201,9 +201,9 @@ __global__ __launch_bounds__(256) void fill_zero(size_t n, float* __restrict__ p
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-constexpr int LN_ROWS = 64;  // rows per workgroup in the LayerNorm backward (partial sums)
+constexpr int LN_ROWS = 16;  // rows per workgroup in the LayerNorm backward (partial sums)
 
-// LayerNorm backward, one wave per row (row in registers), 4 waves x 16 rows
+// LayerNorm backward, one wave per row (row in registers), 4 waves x 4 rows
 // per workgroup.  dx = rstd (dn - mean(dn) - nhat mean(dn nhat)) + dres,
 // dn = dy w; per-channel partials of dw = sum dy nhat and db = sum dy are
 // written as part[0|1][blk][C] (summed later in a fixed order).

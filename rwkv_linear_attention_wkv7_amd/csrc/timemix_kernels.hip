@@ -284,17 +284,37 @@ __global__ __launch_bounds__(256) void shift_bwd(TmBwd p) {
   write_partials<6>(q, p.part_shift, nblk, blk, p.C, cb * N);
 }
 
-// out[v][c] = sum_blk part[v][blk][c], fixed order.
-__global__ __launch_bounds__(256) void reduce_partials(const float* __restrict__ part, int nvec,
-                                                       int nblk, int C, VecOut outs) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= nvec * C) return;
-  const int v = i / C, c = i - v * C;
+// out[v][c] = sum_blk part[v][blk][c], fixed order.  A workgroup owns 64
+// columns of one vector: lane = column, each of the 16 waves sums the rows
+// b = w, w + 16, ... (four loads in flight), and wave 0 adds the 16 wave sums
+// in wave order.
+constexpr int RP_WAVES = 16;
+__global__ __launch_bounds__(64 * RP_WAVES) void reduce_partials(const float* __restrict__ part,
+                                                                 int nblk, int C, VecOut outs) {
+  const int v = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float* o = outs.p[v];
   if (!o) return;
-  float s = 0.f;
-  for (int b = 0; b < nblk; b++) s += part[((size_t)v * nblk + b) * C + c];
-  o[c] = s;
+  const int c = blockIdx.x * 64 + lane;
+  const int cc = c < C ? c : C - 1;
+  const float* src = part + (size_t)v * nblk * C + cc;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int b = w;
+  for (; b + 3 * RP_WAVES < nblk; b += 4 * RP_WAVES) {
+    s0 += src[(size_t)b * C];
+    s1 += src[(size_t)(b + RP_WAVES) * C];
+    s2 += src[(size_t)(b + 2 * RP_WAVES) * C];
+    s3 += src[(size_t)(b + 3 * RP_WAVES) * C];
+  }
+  for (; b < nblk; b += RP_WAVES) s0 += src[(size_t)b * C];
+  __shared__ float red[RP_WAVES][64];
+  red[w][lane] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (w == 0 && c < C) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RP_WAVES; i++) s += red[i][lane];
+    o[c] = s;
+  }
 }
 
 }  // namespace tmk
@@ -332,7 +352,8 @@ hipError_t tm_launch_shift_bwd(const TmBwd& p, hipStream_t st) {
 }
 hipError_t tm_launch_reduce(const float* part, int nvec, int nblk, int C, const VecOut& outs,
                             hipStream_t st) {
-  hipLaunchKernelGGL(tmk::reduce_partials, dim3((nvec * C + 255) / 256), dim3(256), 0, st, part,
-                     nvec, nblk, C, outs);
+  if (nvec < 1 || nvec > 8 || C < 1 || nblk < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tmk::reduce_partials, dim3((C + 63) / 64, nvec), dim3(64 * tmk::RP_WAVES), 0,
+                     st, part, nblk, C, outs);
   return hipGetLastError();
 }
