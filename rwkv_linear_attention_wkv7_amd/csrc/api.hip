@@ -231,11 +231,8 @@ struct TmBwdBufs {
 
 // split-K factor for a weight gradient [Mo][No] reduced over BT tokens
 int splitk_for(int Mo, int No, int BT) {
-  const int tiles = ((Mo + 127) / 128) * ((No + 127) / 128);
-  int s = (512 + tiles - 1) / tiles;
-  const int maxs = BT / 256;
-  if (s > maxs) s = maxs;
-  return s < 1 ? 1 : s;
+  // workspace for either precision's choice
+  return std::max(gemm_splitk_slices(GEMM_F32, Mo, No, BT), gemm_splitk_slices(GEMM_BF16, Mo, No, BT));
 }
 
 size_t splitk_scratch(const tm_shape* s, int BT) {

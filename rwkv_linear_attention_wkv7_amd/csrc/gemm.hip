@@ -431,6 +431,251 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
   store_acc<TI, TJ>(P, split, C, ldc, m0, n0, wm, wn, lane, acc);
 }
 
+// ------------------------------------------------------------------------
+// bf16 matrix-core GEMM with the operands copied global -> LDS by the
+// load unit itself (global_load_lds_dwordx4: no registers held while a
+// load is in flight), for 256-row tiles whose M, N and K extents are whole
+// tiles.  Each of the two LDS stages holds a 32-deep K slice of both
+// operands as fp32; fragments are converted to bf16 as they are read.
+//
+// MFMA k relabelling: the 16x16x32 MFMA sums over 8 k slots per lane group
+// fk; both operands give slot group fk the k values 4fk..4fk+3 and
+// 16+4fk..16+4fk+3 (the same relabelling on both sides, so the sum is the
+// same), which makes each half one 16-byte read.
+//
+// LDS layouts (16-byte units "slots"):
+//  * k-contiguous operand (KC): row r of the tile is 128 bytes (32 k), its
+//    4-k chunk c stored in slot c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1),
+//    so any 8 consecutive rows of a fragment read use 8 different 16-byte
+//    bank groups of a 128-byte bank row, and the 16 rows fill a 256-byte one
+//    (even rows take one half, odd rows the other).
+//  * row-contiguous operand (stored [K][R]): k-row j holds R floats, its
+//    4-row chunk c stored in slot c ^ (4 ((j >> 2) & 3)).  A lane reads 4
+//    adjacent rows at one k with one 16-byte read; those 4 rows feed 4
+//    different fragments (fragment 4p+t of a wave takes rows 64p + 4i + t,
+//    i = 0..15), so the output rows or columns of that side come out
+//    interleaved and are put back in place by the store.
+//  * The N side always uses the interleaved order (a KC B operand is copied
+//    with its rows permuted to match), so each lane ends up holding 4
+//    adjacent columns of C and the store is one float4.
+// The copy instruction writes 64 consecutive slots (1 KB) per wave; each
+// lane fetches the global 16 bytes that belong in its slot.
+namespace dmak {
+
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int BK = 32;  // k per stage
+
+// One global_load_lds_dwordx4: lane i copies the 16 bytes at base + voff to
+// LDS address lds + 16 i.  Issued as assembly so that the compiler neither
+// tracks these writes to LDS nor adds waits for them: the kernel waits on
+// vmcnt itself before the barrier that publishes a stage (the compiler's own
+// vmcnt waits stay safe, since extra outstanding copies only make them
+// stricter).  m0 holds the LDS address; nothing else here uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One operand's copy plan: R tile rows, KC or row-contiguous.  Each stage is
+// R * 32 floats = R / 8 copy instructions of 1 KB; wave w issues numbers
+// w, w + 4, ...  IL (KC only): LDS row rho holds tile row 4 (rho % (R/4)) +
+// rho / (R/4), so the rows one fragment needs in the interleaved order
+// (64p + 4i + t, i = 0..15) are 16 consecutive LDS rows.
+template <int R, bool KC, bool IL>
+struct Copy {
+  static constexpr int NI = R / 32;  // instructions per wave per stage
+  uint32_t off[NI];                  // byte offset of this lane's 16 bytes
+  __device__ __forceinline__ void init(int ld, int lane, int wave) {
+#pragma unroll
+    for (int q = 0; q < NI; q++) {
+      const int g = q * 4 + wave;
+      if (KC) {
+        const int rho = 8 * g + (lane >> 3), c = (lane & 7) ^ (lane >> 3) ^ (g & 1);
+        const int row = IL ? 4 * (rho % (R / 4)) + rho / (R / 4) : rho;
+        off[q] = (uint32_t)(row * ld + 4 * c) * 4u;
+      } else {
+        constexpr int SL = R / 4;  // slots per k-row
+        const int j = (g * 64 + lane) / SL, s = lane % SL;
+        const int c = s ^ (4 * ((j >> 2) & 3));
+        off[q] = (uint32_t)(j * ld + 4 * c) * 4u;
+      }
+    }
+  }
+  // base: global address of the stage's (row 0, k 0) element (uniform);
+  // lds: LDS byte address of the stage.
+  __device__ __forceinline__ void issue(const char* base, uint32_t lds, int wave) const {
+#pragma unroll
+    for (int q = 0; q < NI; q++) copy16(base, off[q], lds + (q * 4 + wave) * 1024);
+  }
+};
+
+__device__ __forceinline__ bf16x8 cat8(f4 lo, f4 hi) {
+  const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f4 lds4(const char* X, uint32_t byte) {
+  return *reinterpret_cast<const f4*>(X + byte);
+}
+
+// NF fragments (16 rows each) of one operand side for one stage, rows
+// woff + 16 f + (0..15) (KC, natural order) or woff + 64 (f / 4) + 4 i + f % 4
+// (interleaved: row-contiguous operands, and KC ones copied with IL).
+template <int R, bool KC, bool IL, int NF>
+__device__ __forceinline__ void frags(const char* X, int woff, int fr, int fk, bf16x8 (&out)[NF]) {
+  if (KC) {
+    const uint32_t key = (uint32_t)((fk ^ (fr & 7) ^ (fr >> 3)) * 16);
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+      // LDS row of fragment f's lane-fr row
+      const int rho = IL ? (f % 4) * (R / 4) + (woff + 64 * (f / 4)) / 4 + fr : woff + 16 * f + fr;
+      const uint32_t lo = (uint32_t)rho * 128u + key;
+      out[f] = cat8(lds4(X, lo), lds4(X, lo ^ 64u));
+    }
+  } else {
+    const uint32_t vb = (uint32_t)(4 * fk * R * 4 + (fr ^ (4 * fk)) * 16 + woff * 4);
+#pragma unroll
+    for (int p = 0; p < NF / 4; p++) {
+      f4 raw[8];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        raw[e] = lds4(X, vb + e * R * 4 + p * 256);
+        raw[4 + e] = lds4(X, vb + (16 + e) * R * 4 + p * 256);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+        out[4 * p + t] = cat8(f4{raw[0][t], raw[1][t], raw[2][t], raw[3][t]},
+                              f4{raw[4][t], raw[5][t], raw[6][t], raw[7][t]});
+    }
+  }
+}
+
+// TJ: 16-column fragments per wave (8: 256x256 tile, 4: 256x128).  Four
+// waves, each 128 rows x 16 TJ columns (8 x TJ accumulator tiles).
+template <int TJ, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_dma(GemmBatch batch, int kslice) {
+  constexpr int BM = 256, BN = 32 * TJ, TI = 8;
+  constexpr bool AKC = !TA, BKC = TB;
+  // the N side is always read in the interleaved order (float4 stores along
+  // rows of C); the M side only when A is row-contiguous
+  constexpr bool AIL = !AKC;
+  __shared__ __attribute__((aligned(1024))) float As0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) float Bs0[BN * BK];
+  __shared__ __attribute__((aligned(1024))) float As1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) float Bs1[BN * BK];
+
+  const bool split = batch.count == 1 && gridDim.z > 1;
+  const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
+  const int M = P.M, N = P.N, K = P.K;
+  int m0, n0;
+  tile_origin(BM, BN, m0, n0);
+  if (m0 >= M || n0 >= N) return;  // outside this problem's grid (uniform per workgroup)
+  float* __restrict__ C = P.C;
+  const int ldc = split ? N : P.ldc;
+  const int kbeg = split ? blockIdx.z * kslice : 0;
+  const int kend = split ? min(K, kbeg + kslice) : K;
+  if (split) C = P.part + (size_t)blockIdx.z * M * N;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 15, fk = lane >> 4;
+
+  Copy<BM, AKC, false> ca;
+  Copy<BN, BKC, true> cb;
+  ca.init(P.lda, lane, wave);
+  cb.init(P.ldb, lane, wave);
+  constexpr int NDMA = Copy<BM, AKC, false>::NI + Copy<BN, BKC, true>::NI;
+  // stage origins: (row 0, k0) of each operand tile
+  const char* Ab = reinterpret_cast<const char*>(P.A + (AKC ? (size_t)m0 * P.lda : (size_t)m0));
+  const char* Bb = reinterpret_cast<const char*>(P.B + (BKC ? (size_t)n0 * P.ldb : (size_t)n0));
+  const size_t astep = (AKC ? (size_t)BK : (size_t)BK * P.lda) * 4;
+  const size_t bstep = (BKC ? (size_t)BK : (size_t)BK * P.ldb) * 4;
+  Ab += (AKC ? (size_t)kbeg : (size_t)kbeg * P.lda) * 4;
+  Bb += (BKC ? (size_t)kbeg : (size_t)kbeg * P.ldb) * 4;
+
+  f4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; i++)
+#pragma unroll
+    for (int j = 0; j < TJ; j++) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const float* Xa, const float* Xb) {
+    bf16x8 fa[TI], fb[TJ];
+    frags<BM, AKC, AIL, TI>(reinterpret_cast<const char*>(Xa), wm * 128, fr, fk, fa);
+    frags<BN, BKC, true, TJ>(reinterpret_cast<const char*>(Xb), wn * 16 * TJ, fr, fk, fb);
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+      for (int j = 0; j < TJ; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Two stages; the copy of stage s+1 runs while stage s is multiplied.
+  // Before a stage is read every wave waits for its own copies into it
+  // (vmcnt), then the barrier makes all waves' copies visible; the barrier
+  // after the multiply frees the stage for the copy issued next.
+  const uint32_t la0 = (uint32_t)(size_t)(lds_void*)As0, lb0 = (uint32_t)(size_t)(lds_void*)Bs0;
+  const uint32_t la1 = (uint32_t)(size_t)(lds_void*)As1, lb1 = (uint32_t)(size_t)(lds_void*)Bs1;
+  const int nk = (kend - kbeg) / BK;
+  ca.issue(Ab, la0, wave);
+  cb.issue(Bb, lb0, wave);
+  for (int s = 0; s < nk; s++) {
+    const bool odd = s & 1;
+    if (s + 1 < nk) {
+      Ab += astep;
+      Bb += bstep;
+      ca.issue(Ab, odd ? la0 : la1, wave);
+      cb.issue(Bb, odd ? lb0 : lb1, wave);
+      wait_vmcnt<NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    compute(odd ? As1 : As0, odd ? Bs1 : Bs0);
+    lds_barrier();
+  }
+
+  // epilogue: fragment rows / columns back to matrix positions; lane fr
+  // holds columns 64p + 4 fr + (0..3) of a row, stored as one float4
+  const float beta = split ? 0.f : P.beta;
+  const int epi = split ? EPI_NONE : P.epi;
+  const float* __restrict__ aux = split ? nullptr : P.aux;
+#pragma unroll
+  for (int i = 0; i < TI; i++) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int r = 4 * fk + v;
+      const int row = m0 + wm * 128 + (AKC ? 16 * i + r : 64 * (i >> 2) + 4 * r + (i & 3));
+#pragma unroll
+      for (int p = 0; p < TJ / 4; p++) {
+        const int col = n0 + wn * 16 * TJ + 64 * p + 4 * fr;
+        float* o = C + (size_t)row * ldc + col;
+        f4 x = {acc[i][4 * p][v], acc[i][4 * p + 1][v], acc[i][4 * p + 2][v], acc[i][4 * p + 3][v]};
+        if (beta != 0.f) x += beta * *reinterpret_cast<const f4*>(o);
+        if (epi != EPI_NONE) {
+          const f4 ax = aux ? *reinterpret_cast<const f4*>(aux + (size_t)row * P.ldc + col) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; t++) x[t] = apply_epi(x[t], epi, ax[t]);
+        }
+        *reinterpret_cast<f4*>(o) = x;
+      }
+    }
+  }
+}
+
+}  // namespace dmak
+
 // Sum S split-K partials [S][M][N] (leading dim N) into C (ldc), with beta/epilogue.
 __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const float* __restrict__ P,
                                                      float* __restrict__ C, int ldc, float beta,
@@ -475,6 +720,47 @@ hipError_t launch_bk(const GemmBatch& b, int gz, int kslice, int klen, hipStream
   return launch_t<PREC, TI, TJ, 128, TA, TB>(b, gz, kslice, st);
 }
 
+// Direct-to-LDS bf16 kernel: every problem's M a multiple of 256, N of the
+// tile width, K (and the split-K slice) of 32, leading dimensions and
+// pointers 16-byte aligned.  Returns the fragment count per wave in N (8 or
+// 4), or 0 when the batch does not qualify.
+int dma_tj(const GemmBatch& b, int gz, int kslice) {
+  if (kslice % (2 * dmak::BK) != 0 || kslice <= 0) return 0;
+  bool n256 = true;
+  long tiles = 0;
+  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  for (int i = 0; i < b.count; i++) {
+    const GemmProblem& q = b.p[i];
+    if (q.M % 256 || q.N % 128 || q.K % (2 * dmak::BK) || q.lda % 4 || q.ldb % 4 || q.ldc % 4) return 0;
+    if (!al(q.A) || !al(q.B) || !al(q.C) || (q.aux && !al(q.aux)) || (q.part && !al(q.part))) return 0;
+    n256 = n256 && q.N % 256 == 0;
+    tiles = std::max(tiles, (long)(q.M / 256) * (q.N / 256));
+  }
+  // below half the CUs (the decode stack's small products) the
+  // register-staged tiles, which come in smaller sizes, do better
+  long t128 = 0;
+  for (int i = 0; i < b.count; i++) t128 = std::max(t128, (long)(b.p[i].M / 256) * (b.p[i].N / 128));
+  if (t128 * gz < 128) return 0;
+  return n256 && tiles * gz >= 256 ? 8 : 4;
+}
+
+template <int TJ, bool TA, bool TB>
+hipError_t launch_dma_t(const GemmBatch& b, int gz, int kslice, hipStream_t st) {
+  int maxM = 0, maxN = 0;
+  for (int i = 0; i < b.count; i++) {
+    maxM = max(maxM, b.p[i].M);
+    maxN = max(maxN, b.p[i].N);
+  }
+  dim3 grid(maxN / (32 * TJ), maxM / 256, gz);
+  hipLaunchKernelGGL((dmak::gemm_dma<TJ, TA, TB>), grid, dim3(256), 0, st, b, kslice);
+  return hipGetLastError();
+}
+
+template <bool TA, bool TB>
+hipError_t launch_dma(const GemmBatch& b, int tj, int gz, int kslice, hipStream_t st) {
+  return tj == 8 ? launch_dma_t<8, TA, TB>(b, gz, kslice, st) : launch_dma_t<4, TA, TB>(b, gz, kslice, st);
+}
+
 template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid reaches 512 workgroups, or 256 when each workgroup
@@ -510,7 +796,14 @@ hipError_t dispatch_p(bool transA, bool transB, const GemmBatch& b, int gz, int 
 
 hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int gz, int kslice,
                     int klen, hipStream_t st) {
-  if (prec == GEMM_BF16) return dispatch_p<GEMM_BF16>(transA, transB, b, gz, kslice, klen, st);
+  if (prec == GEMM_BF16) {
+    const int tj = dma_tj(b, gz, kslice);
+    if (tj && !transA && !transB) return launch_dma<false, false>(b, tj, gz, kslice, st);
+    if (tj && !transA && transB) return launch_dma<false, true>(b, tj, gz, kslice, st);
+    if (tj && transA && !transB) return launch_dma<true, false>(b, tj, gz, kslice, st);
+    if (tj) return launch_dma<true, true>(b, tj, gz, kslice, st);
+    return dispatch_p<GEMM_BF16>(transA, transB, b, gz, kslice, klen, st);
+  }
   return dispatch_p<GEMM_F32>(transA, transB, b, gz, kslice, klen, st);
 }
 
@@ -523,6 +816,22 @@ hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hi
   return gemmk::dispatch(prec, transA, transB, b, b.count, maxK, maxK, st);
 }
 
+// K slices that fill the chip: one workgroup per CU for the 256-row
+// direct-to-LDS bf16 tiles, two for the 128x128 tiles; each slice at least
+// 256 deep.
+int gemm_splitk_slices(int prec, int M, int N, int K) {
+  long want;
+  if (prec == GEMM_BF16 && M % 256 == 0 && N % 128 == 0 && K % (2 * gemmk::dmak::BK) == 0) {
+    const long tiles = (long)(M / 256) * (N % 256 == 0 ? N / 256 : N / 128);
+    want = (256 + tiles - 1) / tiles;
+  } else {
+    const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+    want = (512 + tiles - 1) / tiles;
+  }
+  want = std::min(want, (long)(K / 256));
+  return want < 1 ? 1 : (int)want;
+}
+
 // C = epi(op(A) op(B) + beta C).  ws (may be NULL when split == 1) holds
 // split*M*N floats of split-K partials.
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
@@ -533,9 +842,10 @@ hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, con
   GemmBatch b;
   b.count = 1;
   b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, nullptr};
+  if (split > 1 && ws != nullptr) split = std::min(split, gemm_splitk_slices(prec, M, N, K));
   if (split <= 1 || ws == nullptr) return dispatch(prec, transA, transB, b, 1, K, K, st);
   int kslice = (K + split - 1) / split;
-  kslice = (kslice + 31) / 32 * 32;
+  kslice = (kslice + 63) / 64 * 64;
   const int S = (K + kslice - 1) / kslice;
   b.p[0].part = ws;
   hipError_t e = dispatch(prec, transA, transB, b, S, kslice, kslice, st);

@@ -37,6 +37,9 @@ struct GemmBatch {
 // Up to GEMM_MAX_BATCH independent problems of one layout in one launch.
 hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hipStream_t st);
 // One problem, optionally split along K into `split` slices (ws: split*M*N floats).
+// Split-K slices gemm_run uses for this shape (it takes the smaller of this
+// and the split it is given, which is what its workspace holds).
+int gemm_splitk_slices(int prec, int M, int N, int K);
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
                     int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
                     const float* aux, int split, float* ws, hipStream_t st);
