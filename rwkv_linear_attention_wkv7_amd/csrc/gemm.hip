@@ -437,32 +437,35 @@ __global__ __launch_bounds__(256) void gemm_bf16(GemmBatch batch, int kslice) {
 // load is in flight), for 256-row tiles whose M, N and K extents are whole
 // tiles.  Each of the two LDS stages holds a 32-deep K slice of both
 // operands as fp32; fragments are converted to bf16 as they are read.
+// The multiply is v_mfma_f32_32x32x16_bf16, which keeps the matrix core
+// busy with one wave per SIMD (the 16x16x32 form needs two).
 //
-// MFMA k relabelling: the 16x16x32 MFMA sums over 8 k slots per lane group
-// fk; both operands give slot group fk the k values 4fk..4fk+3 and
-// 16+4fk..16+4fk+3 (the same relabelling on both sides, so the sum is the
-// same), which makes each half one 16-byte read.
+// MFMA operands: lane l (i = l % 32, h = l / 32) gives row i of a 32-row
+// fragment at 8 k values; in k-step s (16 k) of a stage, lane group h takes
+// the k values 16s + 8h + (0..7) on both operands.  Result: lane l, value r
+// is row (r & 3) + 8 (r >> 2) + 4 h, column i of the 32x32 block.
 //
 // LDS layouts (16-byte units "slots"):
-//  * k-contiguous operand (KC): row r of the tile is 128 bytes (32 k), its
-//    4-k chunk c stored in slot c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1),
-//    so any 8 consecutive rows of a fragment read use 8 different 16-byte
-//    bank groups of a 128-byte bank row, and the 16 rows fill a 256-byte one
-//    (even rows take one half, odd rows the other).
-//  * row-contiguous operand (stored [K][R]): k-row j holds R floats, its
-//    4-row chunk c stored in slot c ^ (4 ((j >> 2) & 3)).  A lane reads 4
-//    adjacent rows at one k with one 16-byte read; those 4 rows feed 4
-//    different fragments (fragment 4p+t of a wave takes rows 64p + 4i + t,
-//    i = 0..15), so the output rows or columns of that side come out
-//    interleaved and are put back in place by the store.
+//  * k-contiguous operand (KC): LDS row rho is 128 bytes (32 k), its 4-k
+//    chunk c stored in slot c ^ key(rho), key(rho) = (rho & 7) ^
+//    ((rho >> 3) & 1), so any 8 consecutive rows of a fragment read use 8
+//    different 16-byte bank groups of a 128-byte bank row, and 16 rows fill
+//    a 256-byte one (even rows take one half, odd rows the other).
+//  * row-contiguous operand (stored [K][R]): k-row j holds the R floats in
+//    order.  A lane reads 4 adjacent rows at one k with one 16-byte read;
+//    those 4 rows feed 4 different fragments (fragment t of a wave takes
+//    rows 4i + t, i = 0..31), so the output rows or columns of that side
+//    come out interleaved and are put back in place by the store.
 //  * The N side always uses the interleaved order (a KC B operand is copied
-//    with its rows permuted to match), so each lane ends up holding 4
+//    with its rows permuted to match: LDS row rho holds tile row
+//    4 (rho % (R/4)) + rho / (R/4)), so each lane ends up holding 4
 //    adjacent columns of C and the store is one float4.
 // The copy instruction writes 64 consecutive slots (1 KB) per wave; each
 // lane fetches the global 16 bytes that belong in its slot.
 namespace dmak {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int BK = 32;  // k per stage
 
 // One global_load_lds_dwordx4: lane i copies the 16 bytes at base + voff to
@@ -487,28 +490,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One operand's copy plan: R tile rows, KC or row-contiguous.  Each stage is
-// R * 32 floats = R / 8 copy instructions of 1 KB; wave w issues numbers
-// w, w + 4, ...  IL (KC only): LDS row rho holds tile row 4 (rho % (R/4)) +
-// rho / (R/4), so the rows one fragment needs in the interleaved order
-// (64p + 4i + t, i = 0..15) are 16 consecutive LDS rows.
-template <int R, bool KC, bool IL>
+// One operand's copy plan: R tile rows, KC or row-contiguous, IL (KC only):
+// interleaved row order; NW waves.  Each stage is R * 32 floats = R / 8 copy
+// instructions of 1 KB; wave w issues numbers w, w + NW, ...
+template <int R, bool KC, bool IL, int NW>
 struct Copy {
-  static constexpr int NI = R / 32;  // instructions per wave per stage
-  uint32_t off[NI];                  // byte offset of this lane's 16 bytes
+  static constexpr int NI = R / (8 * NW);  // instructions per wave per stage
+  uint32_t off[NI];                        // byte offset of this lane's 16 bytes
   __device__ __forceinline__ void init(int ld, int lane, int wave) {
 #pragma unroll
     for (int q = 0; q < NI; q++) {
-      const int g = q * 4 + wave;
+      const int g = q * NW + wave;
       if (KC) {
         const int rho = 8 * g + (lane >> 3), c = (lane & 7) ^ (lane >> 3) ^ (g & 1);
         const int row = IL ? 4 * (rho % (R / 4)) + rho / (R / 4) : rho;
         off[q] = (uint32_t)(row * ld + 4 * c) * 4u;
       } else {
-        constexpr int SL = R / 4;  // slots per k-row
-        const int j = (g * 64 + lane) / SL, s = lane % SL;
-        const int c = s ^ (4 * ((j >> 2) & 3));
-        off[q] = (uint32_t)(j * ld + 4 * c) * 4u;
+        const int e = g * 64 + lane;  // float4 index in the stage
+        off[q] = (uint32_t)((e / (R / 4)) * ld + 4 * (e % (R / 4))) * 4u;
       }
     }
   }
@@ -516,7 +515,7 @@ struct Copy {
   // lds: LDS byte address of the stage.
   __device__ __forceinline__ void issue(const char* base, uint32_t lds, int wave) const {
 #pragma unroll
-    for (int q = 0; q < NI; q++) copy16(base, off[q], lds + (q * 4 + wave) * 1024);
+    for (int q = 0; q < NI; q++) copy16(base, off[q], lds + (q * NW + wave) * 1024);
   }
 };
 
@@ -528,43 +527,51 @@ __device__ __forceinline__ f4 lds4(const char* X, uint32_t byte) {
   return *reinterpret_cast<const f4*>(X + byte);
 }
 
-// NF fragments (16 rows each) of one operand side for one stage, rows
-// woff + 16 f + (0..15) (KC, natural order) or woff + 64 (f / 4) + 4 i + f % 4
-// (interleaved: row-contiguous operands, and KC ones copied with IL).
+// NF 32-row fragments of one operand side for k-step s of a stage.  Rows of
+// fragment f: woff + 32 f + i (KC, natural order) or woff + NF i + f
+// (interleaved: row-contiguous operands, NF = 2 or 4, one 8- or 16-byte
+// read per k; KC ones copied with IL, NF = 4).
 template <int R, bool KC, bool IL, int NF>
-__device__ __forceinline__ void frags(const char* X, int woff, int fr, int fk, bf16x8 (&out)[NF]) {
+__device__ __forceinline__ void frags(const char* X, int s, int woff, int i, int h, bf16x8 (&out)[NF]) {
+  static_assert(!(KC && IL) || NF == 4, "the interleaved KC order spans 4 fragments");
+  static_assert(KC || NF == 2 || NF == 4, "row-contiguous fragments come in 2s or 4s");
   if (KC) {
-    const uint32_t key = (uint32_t)((fk ^ (fr & 7) ^ (fr >> 3)) * 16);
+    const int key = (i & 7) ^ ((i >> 3) & 1);
+    const uint32_t c0 = (uint32_t)(((4 * s + 2 * h) ^ key) * 16), c1 = (uint32_t)(((4 * s + 2 * h + 1) ^ key) * 16);
 #pragma unroll
     for (int f = 0; f < NF; f++) {
-      // LDS row of fragment f's lane-fr row
-      const int rho = IL ? (f % 4) * (R / 4) + (woff + 64 * (f / 4)) / 4 + fr : woff + 16 * f + fr;
-      const uint32_t lo = (uint32_t)rho * 128u + key;
-      out[f] = cat8(lds4(X, lo), lds4(X, lo ^ 64u));
+      const int rho = IL ? f * (R / 4) + woff / 4 + i : woff + 32 * f + i;
+      out[f] = cat8(lds4(X, (uint32_t)rho * 128u + c0), lds4(X, (uint32_t)rho * 128u + c1));
     }
+  } else if (NF == 4) {
+    const uint32_t vb = (uint32_t)((16 * s + 8 * h) * R * 4 + (woff + 4 * i) * 4);
+    f4 raw[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) raw[e] = lds4(X, vb + e * R * 4);
+#pragma unroll
+    for (int t = 0; t < NF; t++)
+      out[t] = cat8(f4{raw[0][t], raw[1][t], raw[2][t], raw[3][t]},
+                    f4{raw[4][t], raw[5][t], raw[6][t], raw[7][t]});
   } else {
-    const uint32_t vb = (uint32_t)(4 * fk * R * 4 + (fr ^ (4 * fk)) * 16 + woff * 4);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const uint32_t vb = (uint32_t)((16 * s + 8 * h) * R * 4 + (woff + 2 * i) * 4);
+    f2 raw[8];
 #pragma unroll
-    for (int p = 0; p < NF / 4; p++) {
-      f4 raw[8];
+    for (int e = 0; e < 8; e++) raw[e] = *reinterpret_cast<const f2*>(X + vb + e * R * 4);
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        raw[e] = lds4(X, vb + e * R * 4 + p * 256);
-        raw[4 + e] = lds4(X, vb + (16 + e) * R * 4 + p * 256);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; t++)
-        out[4 * p + t] = cat8(f4{raw[0][t], raw[1][t], raw[2][t], raw[3][t]},
-                              f4{raw[4][t], raw[5][t], raw[6][t], raw[7][t]});
-    }
+    for (int t = 0; t < NF; t++)
+      out[t] = cat8(f4{raw[0][t], raw[1][t], raw[2][t], raw[3][t]},
+                    f4{raw[4][t], raw[5][t], raw[6][t], raw[7][t]});
   }
 }
 
-// TJ: 16-column fragments per wave (8: 256x256 tile, 4: 256x128).  Four
-// waves, each 128 rows x 16 TJ columns (8 x TJ accumulator tiles).
+// TJ = 8: 256x256 tile, 8 waves (two per SIMD, so one wave's MFMAs cover
+// the other's LDS and barrier waits) as 4 x 2, each 64 x 128 (2 x 4 blocks
+// of 32x32).  TJ = 4: 256x128 tile, 4 waves as 4 x 1, each 64 x 128.
 template <int TJ, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_dma(GemmBatch batch, int kslice) {
-  constexpr int BM = 256, BN = 32 * TJ, TI = 8;
+__global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch, int kslice) {
+  constexpr int BM = 256, BN = 32 * TJ, NW = TJ == 8 ? 8 : 4;
+  constexpr int FA = 2, FB = 4;  // 32-row fragments per wave
   constexpr bool AKC = !TA, BKC = TB;
   // the N side is always read in the interleaved order (float4 stores along
   // rows of C); the M side only when A is row-contiguous
@@ -588,14 +595,15 @@ __global__ __launch_bounds__(256) void gemm_dma(GemmBatch batch, int kslice) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 15, fk = lane >> 4;
+  const int wa = TJ == 8 ? (wave >> 1) * 64 : wave * 64;  // wave's first row / column
+  const int wb = TJ == 8 ? (wave & 1) * 128 : 0;
+  const int i = lane & 31, h = lane >> 5;
 
-  Copy<BM, AKC, false> ca;
-  Copy<BN, BKC, true> cb;
+  Copy<BM, AKC, false, NW> ca;
+  Copy<BN, BKC, true, NW> cb;
   ca.init(P.lda, lane, wave);
   cb.init(P.ldb, lane, wave);
-  constexpr int NDMA = Copy<BM, AKC, false>::NI + Copy<BN, BKC, true>::NI;
+  constexpr int NDMA = Copy<BM, AKC, false, NW>::NI + Copy<BN, BKC, true, NW>::NI;
   // stage origins: (row 0, k0) of each operand tile
   const char* Ab = reinterpret_cast<const char*>(P.A + (AKC ? (size_t)m0 * P.lda : (size_t)m0));
   const char* Bb = reinterpret_cast<const char*>(P.B + (BKC ? (size_t)n0 * P.ldb : (size_t)n0));
@@ -604,21 +612,26 @@ __global__ __launch_bounds__(256) void gemm_dma(GemmBatch batch, int kslice) {
   Ab += (AKC ? (size_t)kbeg : (size_t)kbeg * P.lda) * 4;
   Bb += (BKC ? (size_t)kbeg : (size_t)kbeg * P.ldb) * 4;
 
-  f4 acc[TI][TJ];
+  f16v acc[FA][FB];
 #pragma unroll
-  for (int i = 0; i < TI; i++)
+  for (int a = 0; a < FA; a++)
 #pragma unroll
-    for (int j = 0; j < TJ; j++) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < FB; b++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[a][b][r] = 0.f;
 
   auto compute = [&](const float* Xa, const float* Xb) {
-    bf16x8 fa[TI], fb[TJ];
-    frags<BM, AKC, AIL, TI>(reinterpret_cast<const char*>(Xa), wm * 128, fr, fk, fa);
-    frags<BN, BKC, true, TJ>(reinterpret_cast<const char*>(Xb), wn * 16 * TJ, fr, fk, fb);
 #pragma unroll
-    for (int i = 0; i < TI; i++)
+    for (int s = 0; s < BK / 16; s++) {
+      bf16x8 fa[FA], fb[FB];
+      frags<BM, AKC, AIL, FA>(reinterpret_cast<const char*>(Xa), s, wa, i, h, fa);
+      frags<BN, BKC, true, FB>(reinterpret_cast<const char*>(Xb), s, wb, i, h, fb);
 #pragma unroll
-      for (int j = 0; j < TJ; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int a = 0; a < FA; a++)
+#pragma unroll
+        for (int b = 0; b < FB; b++)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
   };
 
   // Two stages; the copy of stage s+1 runs while stage s is multiplied.
@@ -646,30 +659,27 @@ __global__ __launch_bounds__(256) void gemm_dma(GemmBatch batch, int kslice) {
     lds_barrier();
   }
 
-  // epilogue: fragment rows / columns back to matrix positions; lane fr
-  // holds columns 64p + 4 fr + (0..3) of a row, stored as one float4
+  // epilogue: fragment rows / columns back to matrix positions; lane i
+  // holds columns 4 i + (0..3) of each row, stored as one float4
   const float beta = split ? 0.f : P.beta;
   const int epi = split ? EPI_NONE : P.epi;
   const float* __restrict__ aux = split ? nullptr : P.aux;
+  const int col = n0 + wb + 4 * i;
 #pragma unroll
-  for (int i = 0; i < TI; i++) {
+  for (int a = 0; a < FA; a++) {
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int r = 4 * fk + v;
-      const int row = m0 + wm * 128 + (AKC ? 16 * i + r : 64 * (i >> 2) + 4 * r + (i & 3));
+    for (int r = 0; r < 16; r++) {
+      const int rr = (r & 3) + 8 * (r >> 2) + 4 * h;  // row within the 32x32 block
+      const int row = m0 + wa + (AKC ? 32 * a + rr : FA * rr + a);
+      float* o = C + (size_t)row * ldc + col;
+      f4 x = {acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+      if (beta != 0.f) x += beta * *reinterpret_cast<const f4*>(o);
+      if (epi != EPI_NONE) {
+        const f4 ax = aux ? *reinterpret_cast<const f4*>(aux + (size_t)row * P.ldc + col) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < TJ / 4; p++) {
-        const int col = n0 + wn * 16 * TJ + 64 * p + 4 * fr;
-        float* o = C + (size_t)row * ldc + col;
-        f4 x = {acc[i][4 * p][v], acc[i][4 * p + 1][v], acc[i][4 * p + 2][v], acc[i][4 * p + 3][v]};
-        if (beta != 0.f) x += beta * *reinterpret_cast<const f4*>(o);
-        if (epi != EPI_NONE) {
-          const f4 ax = aux ? *reinterpret_cast<const f4*>(aux + (size_t)row * P.ldc + col) : f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; t++) x[t] = apply_epi(x[t], epi, ax[t]);
-        }
-        *reinterpret_cast<f4*>(o) = x;
+        for (int t = 0; t < 4; t++) x[t] = apply_epi(x[t], epi, ax[t]);
       }
+      *reinterpret_cast<f4*>(o) = x;
     }
   }
 }
@@ -724,7 +734,7 @@ hipError_t launch_bk(const GemmBatch& b, int gz, int kslice, int klen, hipStream
 // tile width, K (and the split-K slice) of 32, leading dimensions and
 // pointers 16-byte aligned.  Returns the fragment count per wave in N (8 or
 // 4), or 0 when the batch does not qualify.
-int dma_tj(const GemmBatch& b, int gz, int kslice) {
+int dma_tj(const GemmBatch& b, bool transA, int gz, int kslice) {
   if (kslice % (2 * dmak::BK) != 0 || kslice <= 0) return 0;
   bool n256 = true;
   long tiles = 0;
@@ -741,6 +751,7 @@ int dma_tj(const GemmBatch& b, int gz, int kslice) {
   long t128 = 0;
   for (int i = 0; i < b.count; i++) t128 = std::max(t128, (long)(b.p[i].M / 256) * (b.p[i].N / 128));
   if (t128 * gz < 128) return 0;
+  (void)transA;
   return n256 && tiles * gz >= 256 ? 8 : 4;
 }
 
@@ -752,7 +763,7 @@ hipError_t launch_dma_t(const GemmBatch& b, int gz, int kslice, hipStream_t st) 
     maxN = max(maxN, b.p[i].N);
   }
   dim3 grid(maxN / (32 * TJ), maxM / 256, gz);
-  hipLaunchKernelGGL((dmak::gemm_dma<TJ, TA, TB>), grid, dim3(256), 0, st, b, kslice);
+  hipLaunchKernelGGL((dmak::gemm_dma<TJ, TA, TB>), grid, dim3(TJ == 8 ? 512 : 256), 0, st, b, kslice);
   return hipGetLastError();
 }
 
@@ -797,7 +808,7 @@ hipError_t dispatch_p(bool transA, bool transB, const GemmBatch& b, int gz, int 
 hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int gz, int kslice,
                     int klen, hipStream_t st) {
   if (prec == GEMM_BF16) {
-    const int tj = dma_tj(b, gz, kslice);
+    const int tj = dma_tj(b, transA, gz, kslice);
     if (tj && !transA && !transB) return launch_dma<false, false>(b, tj, gz, kslice, st);
     if (tj && !transA && transB) return launch_dma<false, true>(b, tj, gz, kslice, st);
     if (tj && transA && !transB) return launch_dma<true, false>(b, tj, gz, kslice, st);
