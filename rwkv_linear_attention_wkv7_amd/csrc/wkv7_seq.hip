@@ -23,6 +23,8 @@
 // through LDS once per 16-token chunk, and across the workgroups that share a
 // head through fp32 partial buffers summed by a second kernel in fixed order.
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace wkv7k {
@@ -86,17 +88,23 @@ __global__ __launch_bounds__(256) void fwd_seq(
   R4 pre[NV4_PER];
   R1 prev[NVV_PER];
 
-  // thread -> (token, vector, column group) slots of the staged block
-  // Loads are unconditional from clamped (always valid) token indices so that
-  // all of them are in flight together; tokens past the end are never used.
+  // thread -> (token, vector, column group) slots of the staged block, fixed
+  // for the whole kernel: the source rows are resolved once.  Loads are
+  // unconditional from clamped (always valid) token indices so that all of
+  // them are in flight together; tokens past the end are never used.
+  const T* src4[NV4_PER];
+  int tok4[NV4_PER];
+#pragma unroll
+  for (int q = 0; q < NV4_PER; q++) {
+    const int f = tid + 256 * q;
+    const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+    src4[q] = vec_ptr(vi) + vbase + c4 * 4;
+    tok4[q] = tok;
+  }
   auto load_block = [&](int t0) {
 #pragma unroll
-    for (int q = 0; q < NV4_PER; q++) {
-      const int f = tid + 256 * q;
-      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-      const int tc = min(t0 + tok, Tn - 1);
-      pre[q] = load_raw4(vec_ptr(vi) + vbase + (size_t)tc * C + c4 * 4);
-    }
+    for (int q = 0; q < NV4_PER; q++)
+      pre[q] = load_raw4(src4[q] + (size_t)min(t0 + tok4[q], Tn - 1) * C);
 #pragma unroll
     for (int q = 0; q < NVV_PER; q++) {
       const int f = min(tid + 256 * q, TT * ROWS - 1);
@@ -238,24 +246,46 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     for (int c = 0; c < 4; c++) G[m][c] = x[c];
   }
 
-  // unconditional loads from clamped token indices (all in flight together)
+  // unconditional loads from clamped token indices (all in flight together).
+  // Each thread's staging slots are fixed for the whole kernel, so their
+  // source rows (tensor, column group) are resolved once here; a chunk only
+  // adds its token offset.  The chunk's checkpoint rows are fetched first,
+  // with its vectors, one chunk ahead: a wait for any staged value then
+  // covers them, and no wait ever has to reach past the column-partial
+  // stores of the chunk before (the memory counter is in order and counts
+  // stores too).
   constexpr int NA = (CKL * 80 + NT - 1) / NT, NB = (CKL * 2 * ROWS + NT - 1) / NT;
   R4 xa[NA];
   R1 xb[NB];
+  f4 xck[RPT];
+  const T* srca[NA];
+  int toka[NA];
+  const T* srcb[NB];
+  int tokb[NB];
+#pragma unroll
+  for (int q = 0; q < NA; q++) {
+    const int f = min(tid + NT * q, CKL * 80 - 1);
+    const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+    srca[q] = vec_ptr(vi) + vbase + c4 * 4;
+    toka[q] = tok;
+  }
+#pragma unroll
+  for (int q = 0; q < NB; q++) {
+    const int f = min(tid + NT * q, CKL * 2 * ROWS - 1);
+    const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
+    srcb[q] = (vi ? dy : v) + vbase + sp * ROWS + i;
+    tokb[q] = tok;
+  }
+  const float* ckrow = ckpt + ((size_t)bh * nck * N + row0) * N + cg * 4;
   auto fetch = [&](int c) {
     const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
 #pragma unroll
-    for (int q = 0; q < NA; q++) {
-      const int f = min(tid + NT * q, CKL * 80 - 1);
-      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-      xa[q] = load_raw4(vec_ptr(vi) + vbase + (size_t)(tc0 + min(tok, ns - 1)) * C + c4 * 4);
-    }
+    for (int m = 0; m < RPT; m++)
+      xck[m] = *reinterpret_cast<const f4*>(ckrow + ((size_t)c * N + m) * N);
 #pragma unroll
-    for (int q = 0; q < NB; q++) {
-      const int f = min(tid + NT * q, CKL * 2 * ROWS - 1);
-      const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
-      xb[q] = load_raw1((vi ? dy : v) + vbase + (size_t)(tc0 + min(tok, ns - 1)) * C + sp * ROWS + i);
-    }
+    for (int q = 0; q < NA; q++) xa[q] = load_raw4(srca[q] + (size_t)(tc0 + min(toka[q], ns - 1)) * C);
+#pragma unroll
+    for (int q = 0; q < NB; q++) xb[q] = load_raw1(srcb[q] + (size_t)(tc0 + min(tokb[q], ns - 1)) * C);
   };
   auto commit = [&](int buf) {
 #pragma unroll
@@ -276,29 +306,17 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     }
   };
 
-  fetch(nck - 1);
-  commit(0);
-  int buf = 0;
-  for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
-    const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
-    lds_barrier();  // staged chunk visible; previous readers of the other buffer done
-    if (c > 0) fetch(c - 1);
-    float Sh[CKL + 1][RPT][4];
-    {
-      const float* cp = ckpt + (((size_t)bh * nck + c) * N + row0) * N + cg * 4;
-#pragma unroll
-      for (int m = 0; m < RPT; m++) {
-        const f4 x = *reinterpret_cast<const f4*>(cp + (size_t)m * N);
-#pragma unroll
-        for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = x[cc];
-      }
-    }
-
+  // One chunk of ns tokens (FULL: ns == CKL, every per-token guard gone so
+  // the unrolled tokens are scheduled together).  Sh[0] is the chunk's
+  // checkpoint on entry.
+  float Sh[CKL + 1][RPT][4];
+  auto chunk = [&](auto full, int buf, int tc0, int ns) {
+    constexpr bool FULL = decltype(full)::value;
     // recompute: Sh[tt] = state before token tt, sah[tt] = S a_tt
     float sah[CKL][RPT];
 #pragma unroll
     for (int tt = 0; tt < CKL; tt++) {
-      if (tt < ns) {
+      if (FULL || tt < ns) {
         const f4 av = load4(&sv[buf][tt][3][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
         const f4 kv = load4(&sv[buf][tt][2][cg * 4]), bb = load4(&sv[buf][tt][4][cg * 4]);
 #pragma unroll
@@ -320,7 +338,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     for (int m = 0; m < RPT; m++) dvb[m] = 0.f;
 #pragma unroll
     for (int tt = CKL - 1; tt >= 0; tt--) {
-      if (tt < ns) {
+      if (FULL || tt < ns) {
         const f4 rv = load4(&sv[buf][tt][0][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
         const f4 kv = load4(&sv[buf][tt][2][cg * 4]), av = load4(&sv[buf][tt][3][cg * 4]);
         const f4 bb = load4(&sv[buf][tt][4][cg * 4]);
@@ -379,14 +397,36 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
       for (int m = 0; m < RPT; m++) store1(dp + m, dvb[m]);
     }
     lds_barrier();
-    for (int f = tid; f < ns * 80; f += NT) {
-      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-      f4 s4 = *reinterpret_cast<const f4*>(&red[0][tok][vi][c4 * 4]);
+    constexpr int NRED = (CKL * 80 + NT - 1) / NT;
 #pragma unroll
-      for (int wv = 1; wv < NW; wv++) s4 += *reinterpret_cast<const f4*>(&red[wv][tok][vi][c4 * 4]);
-      *reinterpret_cast<f4*>(part + ((size_t)sp * 5 + vi) * plane + vbase + (size_t)(tc0 + tok) * C +
-                             c4 * 4) = s4;
+    for (int q = 0; q < NRED; q++) {
+      const int f = tid + NT * q;
+      if (f < (FULL ? CKL : ns) * 80) {
+        const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+        f4 s4 = *reinterpret_cast<const f4*>(&red[0][tok][vi][c4 * 4]);
+#pragma unroll
+        for (int wv = 1; wv < NW; wv++) s4 += *reinterpret_cast<const f4*>(&red[wv][tok][vi][c4 * 4]);
+        *reinterpret_cast<f4*>(part + ((size_t)sp * 5 + vi) * plane + vbase +
+                               (size_t)(tc0 + tok) * C + c4 * 4) = s4;
+      }
     }
+  };
+
+  fetch(nck - 1);
+  commit(0);
+  int buf = 0;
+  for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
+    const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
+#pragma unroll
+    for (int m = 0; m < RPT; m++)
+#pragma unroll
+      for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = xck[m][cc];
+    lds_barrier();  // staged chunk visible; previous readers of the other buffer done
+    if (c > 0) fetch(c - 1);
+    if (ns == CKL)
+      chunk(std::true_type{}, buf, tc0, ns);
+    else
+      chunk(std::false_type{}, buf, tc0, ns);
     if (c > 0) commit(buf ^ 1);
   }
   if (ds0) {
