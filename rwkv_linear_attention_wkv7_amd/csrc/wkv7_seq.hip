@@ -132,6 +132,40 @@ __global__ __launch_bounds__(256) void fwd_seq(
 
   // one token; the row sums of y stay with the lane whose cg equals tt
   float yb[RPT];
+  struct Tok {
+    f4 av, wv, kv, bb, rv;
+    float vv[RPT];
+  };
+  auto ldtok = [&](int buf, int tt, Tok& o) {
+    o.av = load4(&sv[buf][tt][3][cg * 4]);
+    o.wv = load4(&sv[buf][tt][1][cg * 4]);
+    o.kv = load4(&sv[buf][tt][2][cg * 4]);
+    o.bb = load4(&sv[buf][tt][4][cg * 4]);
+    o.rv = load4(&sv[buf][tt][0][cg * 4]);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) o.vv[m] = load1(&svv[buf][tt][rloc0 + m]);
+  };
+  auto token_in = [&](const Tok& in, int tt) {
+    const f4 av = in.av, wv = in.wv, kv = in.kv, bb = in.bb, rv = in.rv;
+    float sa[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) sa[m] = dot4(S[m], av);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) sa[m] = rowsum16(sa[m]);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) S[m][c] = fmaf(in.vv[m], kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
+    }
+    float yy[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) yy[m] = dot4(S[m], rv);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      yy[m] = rowsum16(yy[m]);
+      yb[m] = (cg == tt) ? yy[m] : yb[m];
+    }
+  };
   auto token = [&](int buf, int tt) {
     const f4 av = load4(&sv[buf][tt][3][cg * 4]);
     const f4 wv = load4(&sv[buf][tt][1][cg * 4]), kv = load4(&sv[buf][tt][2][cg * 4]);
@@ -174,8 +208,16 @@ __global__ __launch_bounds__(256) void fwd_seq(
 #pragma unroll
     for (int m = 0; m < RPT; m++) yb[m] = 0.f;
     if (nt == TT) {
+      // the next token's inputs are read from LDS while this one runs
+      Tok tc, tn;
+      ldtok(buf, 0, tc);
 #pragma unroll
-      for (int tt = 0; tt < TT; tt++) token(buf, tt);
+      for (int tt = 0; tt < TT; tt++) {
+        if (tt + 1 < TT) ldtok(buf, tt + 1, tn);
+        __builtin_amdgcn_sched_barrier(0);
+        token_in(tc, tt);
+        tc = tn;
+      }
     } else {
       for (int tt = 0; tt < nt; tt++) token(buf, tt);
     }
@@ -287,13 +329,18 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
 #pragma unroll
     for (int q = 0; q < NB; q++) xb[q] = load_raw1(srcb[q] + (size_t)(tc0 + min(tokb[q], ns - 1)) * C);
   };
-  auto commit = [&](int buf) {
+  // Tokens past the end of a partial chunk are staged as identity steps
+  // (w = 1; r, k, v, a, b, dy = 0): the state and its gradient pass through
+  // them unchanged and contribute nothing, so the token loops need no guards.
+  auto commit = [&](int buf, int ns) {
 #pragma unroll
     for (int q = 0; q < NA; q++) {
       const int f = tid + NT * q;
       if (f < CKL * 80) {
         const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
-        *reinterpret_cast<f4*>(&sv[buf][tok][vi][c4 * 4]) = raw4_to_f4<T>(xa[q]);
+        const float pad = vi == 1 ? 1.f : 0.f;
+        *reinterpret_cast<f4*>(&sv[buf][tok][vi][c4 * 4]) =
+            tok < ns ? raw4_to_f4<T>(xa[q]) : f4{pad, pad, pad, pad};
       }
     }
 #pragma unroll
@@ -301,52 +348,89 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
       const int f = tid + NT * q;
       if (f < CKL * 2 * ROWS) {
         const int tok = f / (2 * ROWS), rem = f - tok * 2 * ROWS, vi = rem / ROWS, i = rem - vi * ROWS;
-        svr[buf][tok][vi][i] = raw1_to_f32<T>(xb[q]);
+        svr[buf][tok][vi][i] = tok < ns ? raw1_to_f32<T>(xb[q]) : 0.f;
       }
     }
   };
 
-  // One chunk of ns tokens (FULL: ns == CKL, every per-token guard gone so
-  // the unrolled tokens are scheduled together).  Sh[0] is the chunk's
-  // checkpoint on entry.
+  // One chunk of ns valid tokens, all CKL staged ones processed (identity
+  // padding), so the unrolled tokens are scheduled together.  Sh[0] is the
+  // chunk's checkpoint on entry.
   float Sh[CKL + 1][RPT][4];
-  auto chunk = [&](auto full, int buf, int tc0, int ns) {
-    constexpr bool FULL = decltype(full)::value;
-    // recompute: Sh[tt] = state before token tt, sah[tt] = S a_tt
+  auto chunk = [&](int buf, int tc0, int ns) {
+    // recompute: Sh[tt] = state before token tt, sah[tt] = S a_tt (the next
+    // token's inputs are read while the current one is processed)
     float sah[CKL][RPT];
+    struct Fw {
+      f4 av, wv, kv, bb;
+      float vv[RPT];
+    };
+    auto ldfw = [&](int tt, Fw& o) {
+      o.av = load4(&sv[buf][tt][3][cg * 4]);
+      o.wv = load4(&sv[buf][tt][1][cg * 4]);
+      o.kv = load4(&sv[buf][tt][2][cg * 4]);
+      o.bb = load4(&sv[buf][tt][4][cg * 4]);
 #pragma unroll
-    for (int tt = 0; tt < CKL; tt++) {
-      if (FULL || tt < ns) {
-        const f4 av = load4(&sv[buf][tt][3][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
-        const f4 kv = load4(&sv[buf][tt][2][cg * 4]), bb = load4(&sv[buf][tt][4][cg * 4]);
+      for (int m = 0; m < RPT; m++) o.vv[m] = load1(&svr[buf][tt][0][rloc0 + m]);
+    };
+    {
+      Fw fc, fn;
+      ldfw(0, fc);
 #pragma unroll
-        for (int m = 0; m < RPT; m++) sah[tt][m] = dot4(Sh[tt][m], av);
+      for (int tt = 0; tt < CKL; tt++) {
+        if (tt + 1 < CKL) ldfw(tt + 1, fn);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < RPT; m++) sah[tt][m] = dot4(Sh[tt][m], fc.av);
 #pragma unroll
         for (int m = 0; m < RPT; m++) sah[tt][m] = rowsum16(sah[tt][m]);
 #pragma unroll
         for (int m = 0; m < RPT; m++) {
-          const float vv = load1(&svr[buf][tt][0][rloc0 + m]);
 #pragma unroll
           for (int cc = 0; cc < 4; cc++)
-            Sh[tt + 1][m][cc] = fmaf(vv, kv[cc], fmaf(sah[tt][m], bb[cc], Sh[tt][m][cc] * wv[cc]));
+            Sh[tt + 1][m][cc] =
+                fmaf(fc.vv[m], fc.kv[cc], fmaf(sah[tt][m], fc.bb[cc], Sh[tt][m][cc] * fc.wv[cc]));
         }
+        fc = fn;
       }
     }
 
     float dvb[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; m++) dvb[m] = 0.f;
+    // one token's staged inputs; the next (earlier) token's are read from
+    // LDS while the current one is processed
+    struct Tok {
+      f4 rv, wv, kv, av, bb;
+      float vv[RPT], dyv[RPT];
+    };
+    auto ldtok = [&](int tt, Tok& o) {
+      o.rv = load4(&sv[buf][tt][0][cg * 4]);
+      o.wv = load4(&sv[buf][tt][1][cg * 4]);
+      o.kv = load4(&sv[buf][tt][2][cg * 4]);
+      o.av = load4(&sv[buf][tt][3][cg * 4]);
+      o.bb = load4(&sv[buf][tt][4][cg * 4]);
+#pragma unroll
+      for (int m = 0; m < RPT; m++) {
+        o.vv[m] = load1(&svr[buf][tt][0][rloc0 + m]);
+        o.dyv[m] = load1(&svr[buf][tt][1][rloc0 + m]);
+      }
+    };
+    Tok cur, nxt;
+    ldtok(CKL - 1, cur);
 #pragma unroll
     for (int tt = CKL - 1; tt >= 0; tt--) {
-      if (FULL || tt < ns) {
-        const f4 rv = load4(&sv[buf][tt][0][cg * 4]), wv = load4(&sv[buf][tt][1][cg * 4]);
-        const f4 kv = load4(&sv[buf][tt][2][cg * 4]), av = load4(&sv[buf][tt][3][cg * 4]);
-        const f4 bb = load4(&sv[buf][tt][4][cg * 4]);
+      {
+        if (tt > 0) ldtok(tt - 1, nxt);
+        // keep those reads here, ahead of this token's work (the scheduler
+        // would otherwise sink them below this token's LDS writes)
+        __builtin_amdgcn_sched_barrier(0);
+        const f4 rv = cur.rv, wv = cur.wv, kv = cur.kv, av = cur.av, bb = cur.bb;
         float vv[RPT], dyv[RPT], dvv[RPT], dsa[RPT];
 #pragma unroll
         for (int m = 0; m < RPT; m++) {
-          vv[m] = load1(&svr[buf][tt][0][rloc0 + m]);
-          dyv[m] = load1(&svr[buf][tt][1][rloc0 + m]);
+          vv[m] = cur.vv[m];
+          dyv[m] = cur.dyv[m];
         }
 #pragma unroll
         for (int m = 0; m < RPT; m++)
@@ -389,6 +473,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
         const int col = cg * 4 + ((lane >> 4) & 3);
 #pragma unroll
         for (int vi = 0; vi < 5; vi++) red[wave][tt][vi][col] = x[vi];
+        cur = nxt;
       }
     }
     if (cg < ns) {
@@ -401,7 +486,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
 #pragma unroll
     for (int q = 0; q < NRED; q++) {
       const int f = tid + NT * q;
-      if (f < (FULL ? CKL : ns) * 80) {
+      if (f < ns * 80) {
         const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
         f4 s4 = *reinterpret_cast<const f4*>(&red[0][tok][vi][c4 * 4]);
 #pragma unroll
@@ -413,7 +498,7 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
   };
 
   fetch(nck - 1);
-  commit(0);
+  commit(0, min(CKL, Tn - (nck - 1) * CKL));
   int buf = 0;
   for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
     const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
@@ -423,11 +508,8 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
       for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = xck[m][cc];
     lds_barrier();  // staged chunk visible; previous readers of the other buffer done
     if (c > 0) fetch(c - 1);
-    if (ns == CKL)
-      chunk(std::true_type{}, buf, tc0, ns);
-    else
-      chunk(std::false_type{}, buf, tc0, ns);
-    if (c > 0) commit(buf ^ 1);
+    chunk(buf, tc0, ns);
+    if (c > 0) commit(buf ^ 1, CKL);
   }
   if (ds0) {
 #pragma unroll
