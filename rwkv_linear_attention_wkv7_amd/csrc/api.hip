@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/wkv7.h"
@@ -630,13 +631,112 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
   carve_cache(c, &s, B, 1, d.tm, false);
 }
 
+// Streams split into two groups advanced concurrently (B >= 512): every
+// kernel of the step is either HBM bound over the whole batch (wkv7_step) or
+// a small latency-bound GEMM / row kernel, so the two groups' chains overlap
+// on the GPU.  The first group runs on the caller's stream, the second on a
+// library stream forked from it and joined back with events (both are
+// recorded into a HIP graph when the caller captures).  Group 0 has a
+// multiple of 4 streams so every group pointer keeps its alignment.
+constexpr int DECODE_SPLIT_MIN = 512;
+
+int decode_groups(int B, int nb[2]) {
+  if (B < DECODE_SPLIT_MIN) {
+    nb[0] = B;
+    nb[1] = 0;
+    return 1;
+  }
+  nb[0] = (B / 2) / 4 * 4;
+  nb[1] = B - nb[0];
+  return 2;
+}
+
+void carve_decode_all(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs d[2]) {
+  int nb[2];
+  const int g = decode_groups(B, nb);
+  for (int i = 0; i < g; i++) carve_decode(c, cfg, nb[i], d[i]);
+}
+
+// Per-device fork/join resources, created on first use outside a capture.
+struct ForkJoin {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false, failed = false;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_fj_mu;
+ForkJoin g_fj[MAX_DEVICES];
+
+// Locks g_fj_mu on success (the caller unlocks after enqueuing both groups);
+// nullptr (nothing locked) when no side stream can be had: the groups then
+// run one after the other on the caller's stream.
+ForkJoin* fork_join_acquire(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  g_fj_mu.lock();
+  ForkJoin& f = g_fj[dev];
+  if (!f.ready && !f.failed) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      g_fj_mu.unlock();  // never create resources inside a capture
+      return nullptr;
+    }
+    f.failed = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) != hipSuccess ||
+               hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess;
+    f.ready = !f.failed;
+  }
+  if (!f.ready) {
+    g_fj_mu.unlock();
+    return nullptr;
+  }
+  return &f;
+}
+
+// One group of nb streams starting at stream b0 of B: the per-layer state
+// rows, tokens and logits are the group's contiguous sub-blocks.
+int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int nb,
+               const int* tokens, float* att_x_prev, float* att_state, float* ffn_x_prev,
+               float* logits, DecodeBufs& d, int prec, hipStream_t st) {
+  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer, H = cfg->H;
+  const size_t BC = (size_t)B * C, NN = (size_t)WKV7_N * WKV7_N;
+  tokens += b0;
+  logits += (size_t)b0 * V;
+  HIPCHK(stk_launch_emb_gather(nb, C, V, tokens, M->emb, d.x, st), "embedding");
+  if (cfg->use_ln0) HIPCHK(stk_launch_layernorm(nb, C, d.x, M->ln0_w, M->ln0_b, d.x, nullptr, nullptr, st), "ln0");
+  for (int l = 0; l < L; l++) {
+    const rwkv7_block& bl = M->blocks[l];
+    tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
+    float* axp = att_x_prev + (size_t)l * BC + (size_t)b0 * C;
+    float* ast = att_state + ((size_t)l * B + b0) * H * NN;
+    float* fxp = ffn_x_prev + (size_t)l * BC + (size_t)b0 * C;
+    {  // LN1 fused with the six time-mix lerps; att_x_prev <- this token's LN1 output
+      LnMix lm{nb, C, 6, d.x, bl.ln1_w, bl.ln1_b, axp, axp,
+               {bl.tm.mu_r, bl.tm.mu_w, bl.tm.mu_k, bl.tm.mu_v, bl.tm.mu_a, bl.tm.mu_g},
+               {d.tm.xr, d.tm.xw, d.tm.xk, d.tm.xv, d.tm.xa, d.tm.xg}};
+      HIPCHK(stk_launch_ln_mix(lm, st), "ln1 + shift");
+    }
+    CHK(tm_forward_impl(&s, &bl.tm, nb, 1, nullptr, nullptr, d.vf, ast, ast, d.x, nullptr, d.tm, st,
+                        true, 1.f, prec, true));
+    {  // LN2 fused with the channel-mix lerp; ffn_x_prev <- this token's LN2 output
+      LnMix lm{nb, C, 1, d.x, bl.ln2_w, bl.ln2_b, fxp, fxp, {bl.cm_mu_k}, {d.sh}};
+      HIPCHK(stk_launch_ln_mix(lm, st), "ln2 + shift");
+    }
+    HIPCHK(gemm_run(prec, false, false, nb, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_run(prec, false, false, nb, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
+  }
+  HIPCHK(stk_launch_layernorm(nb, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
+  HIPCHK(gemm_run(prec, false, false, nb, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
+  return WKV7_OK;
+}
+
 }  // namespace
 
 extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
   if (check_cfg(cfg, B) != WKV7_OK) return 0;
   Carver c(nullptr);
-  DecodeBufs d;
-  carve_decode(c, cfg, B, d);
+  DecodeBufs d[2];
+  carve_decode_all(c, cfg, B, d);
   return c.off + 256;
 }
 
@@ -659,10 +759,9 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
   CHK(check_f32_ptr(att_state, "att_state", true));
   CHK(check_f32_ptr(ffn_x_prev, "ffn_x_prev", true));
   CHK(check_f32_ptr(logits, "logits", true));
-  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer, H = cfg->H;
-  for (int l = 0; l < L; l++) {
+  for (int l = 0; l < cfg->n_layer; l++) {
     const rwkv7_block& bl = M->blocks[l];
-    tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
+    tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
     CHK(check_weights(&s, &bl.tm));
     const float* req[] = {bl.ln1_w, bl.ln1_b, bl.ln2_w, bl.ln2_b, bl.cm_mu_k, bl.cm_Wk, bl.cm_Wv};
     for (const float* p : req) CHK(check_f32_ptr(p, "a block weight", true));
@@ -672,36 +771,33 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
   Carver cw(ws);
-  DecodeBufs d;
-  carve_decode(cw, cfg, B, d);
-
-  const size_t BC = (size_t)B * C, NN = (size_t)WKV7_N * WKV7_N;
-  HIPCHK(stk_launch_emb_gather(B, C, V, tokens, M->emb, d.x, st), "embedding");
-  if (cfg->use_ln0) HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln0_w, M->ln0_b, d.x, nullptr, nullptr, st), "ln0");
-  for (int l = 0; l < L; l++) {
-    const rwkv7_block& bl = M->blocks[l];
-    tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
-    float* axp = att_x_prev + (size_t)l * BC;
-    float* ast = att_state + (size_t)l * B * H * NN;
-    float* fxp = ffn_x_prev + (size_t)l * BC;
-    {  // LN1 fused with the six time-mix lerps; att_x_prev <- this token's LN1 output
-      LnMix lm{B, C, 6, d.x, bl.ln1_w, bl.ln1_b, axp, axp,
-               {bl.tm.mu_r, bl.tm.mu_w, bl.tm.mu_k, bl.tm.mu_v, bl.tm.mu_a, bl.tm.mu_g},
-               {d.tm.xr, d.tm.xw, d.tm.xk, d.tm.xv, d.tm.xa, d.tm.xg}};
-      HIPCHK(stk_launch_ln_mix(lm, st), "ln1 + shift");
-    }
-    CHK(tm_forward_impl(&s, &bl.tm, B, 1, nullptr, nullptr, d.vf, ast, ast, d.x, nullptr, d.tm, st, true,
-                        1.f, prec, true));
-    {  // LN2 fused with the channel-mix lerp; ffn_x_prev <- this token's LN2 output
-      LnMix lm{B, C, 1, d.x, bl.ln2_w, bl.ln2_b, fxp, fxp, {bl.cm_mu_k}, {d.sh}};
-      HIPCHK(stk_launch_ln_mix(lm, st), "ln2 + shift");
-    }
-    HIPCHK(gemm_run(prec, false, false, B, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(gemm_run(prec, false, false, B, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
+  DecodeBufs d[2];
+  carve_decode_all(cw, cfg, B, d);
+  int nb[2];
+  if (decode_groups(B, nb) == 1)
+    return decode_run(cfg, M, B, 0, B, tokens, att_x_prev, att_state, ffn_x_prev, logits, d[0],
+                      prec, st);
+  ForkJoin* fj = fork_join_acquire(st);
+  if (!fj) {  // no side stream: the groups one after the other
+    for (int g = 0; g < 2; g++)
+      CHK(decode_run(cfg, M, B, g ? nb[0] : 0, nb[g], tokens, att_x_prev, att_state, ffn_x_prev,
+                     logits, d[g], prec, st));
+    return WKV7_OK;
   }
-  HIPCHK(stk_launch_layernorm(B, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
-  HIPCHK(gemm_run(prec, false, false, B, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");
-  return WKV7_OK;
+  std::lock_guard<std::mutex> hold(g_fj_mu, std::adopt_lock);
+  HIPCHK(hipEventRecord(fj->fork, st), "decode fork");
+  HIPCHK(hipStreamWaitEvent(fj->side, fj->fork, 0), "decode fork");
+  const int rc1 = decode_run(cfg, M, B, nb[0], nb[1], tokens, att_x_prev, att_state, ffn_x_prev,
+                             logits, d[1], prec, fj->side);
+  // the join is enqueued whatever happened, so the caller's stream (or
+  // capture) never leaves the side stream dangling
+  const hipError_t ej = hipEventRecord(fj->join, fj->side);
+  const int rc0 = rc1 == WKV7_OK ? decode_run(cfg, M, B, 0, nb[0], tokens, att_x_prev, att_state,
+                                              ffn_x_prev, logits, d[0], prec, st)
+                                 : rc1;
+  HIPCHK(ej, "decode join");
+  HIPCHK(hipStreamWaitEvent(st, fj->join, 0), "decode join");
+  return rc0;
 }
 
 // ---------------------------------------------------------- training step --

@@ -28,8 +28,11 @@ def _setup(L, C, H, F, V, ranks, B, seed, perturbed, std):
     return m, dict(C=C, H=H, F=F, V=V, n_layer=L), dm
 
 
-def test_decode_small_perturbed(hip):
-    B, T = 5, 6
+@pytest.mark.parametrize("B", [5, 518])
+def test_decode_small_perturbed(hip, B):
+    """Every stream against the oracle.  B = 518 runs the step as two stream
+    groups (256 + 262) advanced concurrently on two HIP streams."""
+    T = 6
     m, ocfg, dm = _setup(3, 128, 2, 256, 64, (16, 16, 16, 32), B, seed=1, perturbed=True, std=0.2)
     tok = synth.token_ids(B, T, 64, seed=7)
     ref_logits, ref_st = stack.forward(m, ocfg, tok)
@@ -64,10 +67,12 @@ def test_decode_full_size_sampled_streams(hip):
         assert_close(k, st[k].cpu().numpy()[:, idx], ref_st[k], 1e-4)
 
 
-def test_decode_graph_replay_matches_eager(hip):
+@pytest.mark.parametrize("B", [64, 514])
+def test_decode_graph_replay_matches_eager(hip, B):
     """A captured decode step replayed several times (eager work and syncs in
-    between) gives bitwise the eager results."""
-    B, T = 64, 3
+    between) gives bitwise the eager results; at B = 514 the capture holds the
+    two concurrent stream groups (fork and join across two HIP streams)."""
+    T = 3
     m, ocfg, dm = _setup(2, 128, 2, 256, 64, (16, 16, 16, 32), B, seed=2, perturbed=True, std=0.2)
     tok = torch.from_numpy(synth.token_ids(B, T, 64, seed=8)).cuda()
     eager_st = dm.new_state(B)
