@@ -142,11 +142,10 @@ def setup_wkv7_long():
     ins = [torch.from_numpy(d[n]).to(dev).to(torch.bfloat16) for n in names]
     dy = torch.from_numpy(d["dy"]).to(dev).to(torch.bfloat16)
     ck = torch.empty(binding.wkv7_checkpoint_floats(B, T, H), device=dev)
-    fws = torch.empty(binding.lib().wkv7_forward_workspace_bytes(B, T, H, N), device=dev,
-                      dtype=torch.uint8)
 
     def step():
-        binding.wkv7_forward(*ins, ckpt=ck, want_state=False, ws=fws)
+        # token-sequential forward (no chunk workspace): the faster path here
+        binding.wkv7_forward(*ins, ckpt=ck, want_state=False, chunked=False)
         binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
 
     def dom():

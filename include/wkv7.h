@@ -66,13 +66,15 @@ size_t wkv7_checkpoint_floats(int B, int T, int H, int N);
  * ws / ws_bytes: NULL, or device scratch of at least
  * wkv7_forward_workspace_bytes() bytes (16-byte aligned; contents
  * undefined before and after; owned by the caller, not retained).  The
- * query is nonzero exactly for the shapes that take the chunked matrix-core
- * kernels when given it (T >= 2L and B*H < 64: the recurrence unrolled over
- * chunks of L tokens, intra-chunk products on MFMA; chunks whose cumulative
- * decay leaves the fp32 exponent range of the unrolled form run token by
- * token).  Every other shape, or ws NULL, runs the token-sequential kernel,
- * which spreads each head over four workgroups and is the faster one once
- * B*H reaches 64.  Both compute the same recurrence in fp32 and agree to
+ * query is nonzero exactly when T >= 2L; a workspace given for such a shape
+ * selects the chunked matrix-core kernels (the recurrence unrolled over
+ * chunks of L tokens, intra-chunk products on MFMA, a per-head state scan;
+ * chunks whose cumulative decay leaves the fp32 exponent range of the
+ * unrolled form run token by token).  ws NULL, or T < 2L, runs the
+ * token-sequential kernel, which spreads each head over four workgroups; on
+ * MI355X it is the faster of the two at every shape measured (B*H from 16
+ * to 512, T up to 8192), and it is what every other call of this library
+ * uses internally.  Both compute the same recurrence in fp32 and agree to
  * rounding.  A ws smaller than a nonzero query returns WKV7_ENOSPC.
  */
 size_t wkv7_forward_workspace_bytes(int B, int T, int H, int N);
@@ -82,8 +84,8 @@ int wkv7_forward(int B, int T, int H, int N, int dtype,
                  void *y, float *sT, float *ckpt, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes wkv7_backward needs: fp32 column partials of the reverse
- * pass, plus, when have_ckpt is 0, the checkpoints and the chunked-forward
- * records of their recompute. */
+ * pass, plus, when have_ckpt is 0, the checkpoints (recomputed by the
+ * token-sequential forward). */
 size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
 
 /*
@@ -247,6 +249,13 @@ size_t rwkv7_decode_workspace_bytes(const rwkv7_config *cfg, int B);
  * read and updated in place: att_x_prev, ffn_x_prev [n_layer][B][C] (the
  * previous token's LN1 / LN2 outputs), att_state [n_layer][B][H][N][N] fp32.
  * logits: [B][V] fp32 (written).
+ * From B = 512 on, the streams are advanced as two groups at once: the first
+ * on `stream`, the second on a stream the library creates once per device
+ * (default priority), forked from `stream` and joined back to it with events,
+ * so everything is still ordered on `stream` and a capture of `stream`
+ * records both.  The side stream is created by the first such call made
+ * outside a capture; without it the groups run one after the other on
+ * `stream`.  Calls enqueuing the split step are serialized by a lock.
  */
 int rwkv7_decode_step(const rwkv7_config *cfg, const rwkv7_model *model, int B,
                       const int *tokens, float *att_x_prev, float *att_state,

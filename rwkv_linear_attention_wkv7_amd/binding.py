@@ -163,12 +163,13 @@ def wkv7_checkpoint_floats(B, T, H, N=64):
 
 
 def wkv7_forward(r, w, k, v, a, b, s0=None, y=None, sT=None, ckpt=None,
-                 want_state=True, want_ckpt=False, chunked=True, ws=None):
+                 want_state=True, want_ckpt=False, chunked=False, ws=None):
     """y = WKV7(r, w, k, v, a, b; s0).  Returns (y, sT or None, ckpt or None).
 
-    chunked: pass the workspace of the chunked matrix-core kernels (used for
-    T >= 32); False runs the token-sequential kernel at every T.  ws: a
-    preallocated uint8 device workspace (allocated here when None)."""
+    chunked: pass the workspace that selects the chunked matrix-core kernels
+    (for T >= 32); False (the default, and the faster path on MI355X) runs the
+    token-sequential kernel.  ws: a preallocated uint8 device workspace for
+    the chunked path (allocated here when None)."""
     B, T, H, N = r.shape
     dt = r.dtype
     for n, t in zip("rwkvab", (r, w, k, v, a, b)):

@@ -98,7 +98,7 @@ extern "C" size_t wkv7_checkpoint_floats(int B, int T, int H, int N) {
 
 extern "C" size_t wkv7_forward_workspace_bytes(int B, int T, int H, int N) {
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
-  return wkv7_use_chunked(B, T, H) ? wkv7_chunk_ws_floats(B, T, H) * sizeof(float) : 0;
+  return wkv7_use_chunked(T) ? wkv7_chunk_ws_floats(B, T, H) * sizeof(float) : 0;
 }
 
 extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r, const void* w,
@@ -134,10 +134,7 @@ extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int 
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
   Carver c(nullptr);
   c.take(wkv7_bwd_partial_floats(B, T, H));
-  if (!have_ckpt) {
-    c.take(ckpt_floats(B, T, H));
-    c.take(wkv7_forward_workspace_bytes(B, T, H, N) / sizeof(float));
-  }
+  if (!have_ckpt) c.take(ckpt_floats(B, T, H));
   return c.off;
 }
 
@@ -164,9 +161,7 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
   const float* ck = ckpt;
   if (!ck) {
     float* tmp = cv.take(ckpt_floats(B, T, H));
-    const size_t nc = wkv7_forward_workspace_bytes(B, T, H, N) / sizeof(float);
-    float* cws = nc ? cv.take(nc) : nullptr;
-    HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, cws,
+    HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, nullptr, nullptr, tmp, nullptr,
                                stream),
            "wkv7_backward checkpoint recompute");
     ck = tmp;
@@ -219,8 +214,7 @@ void carve_cache(Carver& c, const tm_shape* s, int B, int T, TmCache& m, bool wi
   m.rstd = c.take(BT * s->H);
   m.alpha = c.take(BT * s->H);
   m.ckpt = with_ckpt ? c.take(ckpt_floats(B, T, s->H)) : nullptr;
-  const size_t nc = wkv7_use_chunked(B, T, s->H) ? wkv7_chunk_ws_floats(B, T, s->H) : 0;
-  m.wkv_ws = nc ? c.take(nc) : nullptr;
+  m.wkv_ws = nullptr;  // the time-mix runs the (faster) token-sequential recurrence
 }
 
 struct TmBwdBufs {

@@ -56,9 +56,9 @@ hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, co
                                const float* s0, void* y, float* sT, float* ckpt, float* chunk_ws, hipStream_t st);
 // fp32 workspace of the chunked forward (records of every (b, h, chunk)); the
 // forward takes the chunked kernels when it is given one and
-// wkv7_use_chunked(B, T, H).
+// wkv7_use_chunked(T) (T of at least two chunks).
 size_t wkv7_chunk_ws_floats(int B, int T, int H);
-bool wkv7_use_chunked(int B, int T, int H);
+bool wkv7_use_chunked(int T);
 hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, const void* w,
                                 const void* k, const void* v, const void* a, const void* b,
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,

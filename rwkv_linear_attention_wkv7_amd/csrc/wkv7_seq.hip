@@ -629,22 +629,21 @@ hipError_t wkv7_launch_forward_chunked(int dtype, int B, int T, int H, const voi
                                        const float* s0, void* y, float* sT, float* ckpt, float* ws,
                                        hipStream_t st);
 
-// Path choice.  The chunked matrix-core kernels run when a chunk workspace
-// is given, T >= 2 chunks and there are fewer than 64 (b, h) pairs; else the
-// token-sequential kernel.  Measured on MI355X (fp32, forward alone): at
-// B*H = 16, T = 8192 the chunked path takes 0.82x the sequential time; at
-// B*H = 64..512 (T = 1024..8192) 1.03-1.22x, because its per-head chunk scan
-// is latency bound while the sequential kernel spreads each head's rows over
-// four workgroups.
-bool wkv7_use_chunked(int B, int T, int H) {
-  return T >= 2 * wkv7k::CKL && (long)B * H < 64;
-}
+// Path choice.  The chunked matrix-core kernels run when the caller hands
+// over a chunk workspace and T >= 2 chunks; otherwise (and for every forward
+// the library runs internally) the token-sequential kernel.  Measured on
+// MI355X, fp32 forward alone, chunked / sequential: 1.23 / 1.00 ms at B = 1,
+// T = 8192, H = 16; 1.45 / 1.02 ms at B*H = 48; 0.28 / 0.28 ms at B = 4,
+// T = 2048, H = 16: the chunk scan is a dependent chain of about 6 000
+// cycles per 16-token chunk and head, longer than 16 sequential tokens of a
+// head whose rows are spread over four workgroups.
+bool wkv7_use_chunked(int T) { return T >= 2 * wkv7k::CKL; }
 
 hipError_t wkv7_launch_forward(int dtype, int B, int T, int H, const void* r, const void* w,
                                const void* k, const void* v, const void* a, const void* b,
                                const float* s0, void* y, float* sT, float* ckpt, float* chunk_ws,
                                hipStream_t st) {
-  if (chunk_ws && wkv7_use_chunked(B, T, H))
+  if (chunk_ws && wkv7_use_chunked(T))
     return wkv7_launch_forward_chunked(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, chunk_ws,
                                        st);
   if (dtype == 1)

@@ -93,7 +93,9 @@ def test_wkv7_backward_without_checkpoints(hip):
     d = synth.wkv7_inputs(2, 40, 2, 64, seed=5, with_state=True)
     ins = [_dev(d[n]) for n in NAMES]
     s0, dsT, dy = _dev(d["s0"]), _dev(d["dsT"]), _dev(d["dy"])
-    y, sT, ck = binding.wkv7_forward(*ins, s0=s0, want_ckpt=True)
+    # the backward recomputes missing checkpoints with the token-sequential
+    # forward, so it matches that forward's checkpoints bit for bit
+    y, sT, ck = binding.wkv7_forward(*ins, s0=s0, want_ckpt=True, chunked=False)
     g1 = binding.wkv7_backward(*ins, dy, s0=s0, ckpt=ck, dsT=dsT)
     g2 = binding.wkv7_backward(*ins, dy, s0=s0, ckpt=None, dsT=dsT)
     torch.cuda.synchronize()
@@ -108,21 +110,24 @@ def test_wkv7_bf16_parity(hip, chunked):
     _check(d, y, sT, g, True, 2e-2, 2e-2)
 
 
-def test_wkv7_bf16_long_context_full_size(hip):
+@pytest.mark.parametrize("chunked", [False, True])
+def test_wkv7_bf16_long_context_full_size(hip, chunked):
     """B=4, T=8192, H=32 bf16 (the long-context configuration), checked on
-    sampled (b, h) pairs: the recurrence of each (b, h) is independent."""
+    sampled (b, h) pairs: the recurrence of each (b, h) is independent.
+    chunked=False is the token-sequential forward the benchmark times; True
+    asks for the chunked matrix-core forward at the same size."""
     B, T, H = 4, 8192, 32
     d = synth.wkv7_inputs(B, T, H, 64, seed=3, bf16=True)
-    print(f"[wkv7 long bf16] B={B} T={T} H={H}", flush=True)
-    y, sT, g = _run(hip, d, torch.bfloat16, False)
+    print(f"[wkv7 long bf16] B={B} T={T} H={H} chunked={chunked}", flush=True)
+    y, sT, g = _run(hip, d, torch.bfloat16, False, chunked)
     for (b, h) in ((0, 0), (3, 31), (1, 17), (2, 5)):
         _check(d, y, sT, g, False, 2e-2, 2e-2, sel=(slice(b, b + 1), slice(h, h + 1)))
 
 
 def test_wkv7_chunked_long_few_heads(hip):
-    """B=1, T=4096, H=16: few (b, h) pairs and a long sequence, the shape the
-    chunked matrix-core forward is chosen for (256 chunks per head, state
-    carried across all of them); fp32, sampled heads against the oracle."""
+    """B=1, T=4096, H=16: few (b, h) pairs and a long sequence through the
+    chunked matrix-core forward (256 chunks per head, state carried across
+    all of them); fp32, sampled heads against the oracle."""
     B, T, H = 1, 4096, 16
     d = synth.wkv7_inputs(B, T, H, 64, seed=13, with_state=True)
     print(f"[wkv7 chunked long] B={B} T={T} H={H}", flush=True)
