@@ -625,44 +625,49 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
   carve_cache(c, &s, B, 1, d.tm, false);
 }
 
-// Streams split into two groups advanced concurrently (B >= 512): every
-// kernel of the step is either HBM bound over the whole batch (wkv7_step) or
-// a small latency-bound GEMM / row kernel, so the two groups' chains overlap
-// on the GPU.  The first group runs on the caller's stream, the second on a
-// library stream forked from it and joined back with events (both are
-// recorded into a HIP graph when the caller captures).  Group 0 has a
-// multiple of 4 streams so every group pointer keeps its alignment.
+// Streams split into groups advanced concurrently (B >= 512: one group per
+// 512 streams, at most DECODE_MAX_GROUPS): every kernel of the step is
+// either HBM bound over the whole batch (wkv7_step) or a small latency-bound
+// GEMM / row kernel, so the groups' chains overlap on the GPU.  Group 0 runs
+// on the caller's stream, the others on library streams forked from it and
+// joined back with events (all recorded into a HIP graph when the caller
+// captures).  Every group but the last has a multiple of 4 streams so each
+// group pointer keeps its alignment.  Measured on MI355X, 12 layers C = 256,
+// 2048 streams: 1.82 ms per step in one group, 1.64 ms in two, 2.01 ms in
+// four (smaller groups make every GEMM and row kernel less efficient).
 constexpr int DECODE_SPLIT_MIN = 512;
+constexpr int DECODE_MAX_GROUPS = 2;
 
-int decode_groups(int B, int nb[2]) {
-  if (B < DECODE_SPLIT_MIN) {
+int decode_groups(int B, int nb[DECODE_MAX_GROUPS]) {
+  const int g = B < DECODE_SPLIT_MIN ? 1 : std::min(DECODE_MAX_GROUPS, B / DECODE_SPLIT_MIN + (B % DECODE_SPLIT_MIN ? 1 : 0));
+  if (g == 1) {
     nb[0] = B;
-    nb[1] = 0;
     return 1;
   }
-  nb[0] = (B / 2) / 4 * 4;
-  nb[1] = B - nb[0];
-  return 2;
+  const int per = (B / g) / 4 * 4;
+  for (int i = 0; i < g - 1; i++) nb[i] = per;
+  nb[g - 1] = B - per * (g - 1);
+  return g;
 }
 
-void carve_decode_all(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs d[2]) {
-  int nb[2];
+void carve_decode_all(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs d[DECODE_MAX_GROUPS]) {
+  int nb[DECODE_MAX_GROUPS];
   const int g = decode_groups(B, nb);
   for (int i = 0; i < g; i++) carve_decode(c, cfg, nb[i], d[i]);
 }
 
 // Per-device fork/join resources, created on first use outside a capture.
 struct ForkJoin {
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t side[DECODE_MAX_GROUPS - 1] = {};
+  hipEvent_t fork = nullptr, join[DECODE_MAX_GROUPS - 1] = {};
   bool ready = false, failed = false;
 };
 constexpr int MAX_DEVICES = 64;
 std::mutex g_fj_mu;
 ForkJoin g_fj[MAX_DEVICES];
 
-// Locks g_fj_mu on success (the caller unlocks after enqueuing both groups);
-// nullptr (nothing locked) when no side stream can be had: the groups then
+// Locks g_fj_mu on success (the caller unlocks after enqueuing every group);
+// nullptr (nothing locked) when no side streams can be had: the groups then
 // run one after the other on the caller's stream.
 ForkJoin* fork_join_acquire(hipStream_t st) {
   int dev = 0;
@@ -675,9 +680,10 @@ ForkJoin* fork_join_acquire(hipStream_t st) {
       g_fj_mu.unlock();  // never create resources inside a capture
       return nullptr;
     }
-    f.failed = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) != hipSuccess ||
-               hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess;
+    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess;
+    for (int i = 0; i < DECODE_MAX_GROUPS - 1 && !f.failed; i++)
+      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
+                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
     f.ready = !f.failed;
   }
   if (!f.ready) {
@@ -729,7 +735,7 @@ int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int
 extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
   if (check_cfg(cfg, B) != WKV7_OK) return 0;
   Carver c(nullptr);
-  DecodeBufs d[2];
+  DecodeBufs d[DECODE_MAX_GROUPS];
   carve_decode_all(c, cfg, B, d);
   return c.off + 256;
 }
@@ -765,33 +771,47 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
   Carver cw(ws);
-  DecodeBufs d[2];
+  DecodeBufs d[DECODE_MAX_GROUPS];
   carve_decode_all(cw, cfg, B, d);
-  int nb[2];
-  if (decode_groups(B, nb) == 1)
+  int nb[DECODE_MAX_GROUPS], b0[DECODE_MAX_GROUPS];
+  const int ng = decode_groups(B, nb);
+  for (int g = 0, o = 0; g < ng; o += nb[g], g++) b0[g] = o;
+  if (ng == 1)
     return decode_run(cfg, M, B, 0, B, tokens, att_x_prev, att_state, ffn_x_prev, logits, d[0],
                       prec, st);
   ForkJoin* fj = fork_join_acquire(st);
-  if (!fj) {  // no side stream: the groups one after the other
-    for (int g = 0; g < 2; g++)
-      CHK(decode_run(cfg, M, B, g ? nb[0] : 0, nb[g], tokens, att_x_prev, att_state, ffn_x_prev,
-                     logits, d[g], prec, st));
+  if (!fj) {  // no side streams: the groups one after the other
+    for (int g = 0; g < ng; g++)
+      CHK(decode_run(cfg, M, B, b0[g], nb[g], tokens, att_x_prev, att_state, ffn_x_prev, logits,
+                     d[g], prec, st));
     return WKV7_OK;
   }
   std::lock_guard<std::mutex> hold(g_fj_mu, std::adopt_lock);
   HIPCHK(hipEventRecord(fj->fork, st), "decode fork");
-  HIPCHK(hipStreamWaitEvent(fj->side, fj->fork, 0), "decode fork");
-  const int rc1 = decode_run(cfg, M, B, nb[0], nb[1], tokens, att_x_prev, att_state, ffn_x_prev,
-                             logits, d[1], prec, fj->side);
-  // the join is enqueued whatever happened, so the caller's stream (or
-  // capture) never leaves the side stream dangling
-  const hipError_t ej = hipEventRecord(fj->join, fj->side);
-  const int rc0 = rc1 == WKV7_OK ? decode_run(cfg, M, B, 0, nb[0], tokens, att_x_prev, att_state,
-                                              ffn_x_prev, logits, d[0], prec, st)
-                                 : rc1;
+  int rc = WKV7_OK;
+  hipError_t ej = hipSuccess;
+  int forked = 0;
+  for (int g = 1; g < ng; g++) {
+    hipStream_t sg = fj->side[g - 1];
+    HIPCHK(hipStreamWaitEvent(sg, fj->fork, 0), "decode fork");
+    forked = g;
+    if (rc == WKV7_OK)
+      rc = decode_run(cfg, M, B, b0[g], nb[g], tokens, att_x_prev, att_state, ffn_x_prev, logits,
+                      d[g], prec, sg);
+    // each join is enqueued whatever happened, so the caller's stream (or
+    // capture) never leaves a side stream dangling
+    const hipError_t e = hipEventRecord(fj->join[g - 1], sg);
+    if (ej == hipSuccess) ej = e;
+  }
+  if (rc == WKV7_OK)
+    rc = decode_run(cfg, M, B, 0, nb[0], tokens, att_x_prev, att_state, ffn_x_prev, logits, d[0],
+                    prec, st);
+  for (int g = 1; g <= forked; g++) {
+    const hipError_t e = hipStreamWaitEvent(st, fj->join[g - 1], 0);
+    if (ej == hipSuccess) ej = e;
+  }
   HIPCHK(ej, "decode join");
-  HIPCHK(hipStreamWaitEvent(st, fj->join, 0), "decode join");
-  return rc0;
+  return rc;
 }
 
 // ---------------------------------------------------------- training step --
