@@ -26,13 +26,16 @@ LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("tA,tB", LAYOUTS)
 def test_gemm_layouts(hip, M, N, K, tA, tB):
-    if tA and M % 4:
-        pytest.skip("a transposed A is read along M in float4: M must be a multiple of 4")
     g = np.random.default_rng(M * 7 + N * 3 + K)
     a = g.standard_normal((K, M) if tA else (M, K)).astype(np.float32)
     b = g.standard_normal((N, K) if tB else (K, N)).astype(np.float32)
     c0 = g.standard_normal((M, N)).astype(np.float32)
     A, Bm, C = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), torch.from_numpy(c0.copy()).cuda()
+    if tA and M % 4:
+        # a transposed A is read along M in float4: rejected before any launch
+        with pytest.raises(hip.Wkv7Error, match="multiples of 4"):
+            hip.wkv7_gemm_f32(A, Bm, C, transA=tA, transB=tB, beta=0.5)
+        return
     hip.wkv7_gemm_f32(A, Bm, C, transA=tA, transB=tB, beta=0.5)
     torch.cuda.synchronize()
     opa = a.astype(np.float64).T if tA else a.astype(np.float64)
@@ -44,13 +47,16 @@ def test_gemm_layouts(hip, M, N, K, tA, tB):
 @pytest.mark.parametrize("M,N,K", SHAPES + [(8192, 4096, 1024), (1024, 1024, 8192), (260, 36, 200)])
 @pytest.mark.parametrize("tA,tB", LAYOUTS)
 def test_gemm_bf16_layouts(hip, M, N, K, tA, tB):
-    if tA and M % 4:
-        pytest.skip("a transposed A is read along M in float4: M must be a multiple of 4")
     g = np.random.default_rng(M * 5 + N * 11 + K)
     a = g.standard_normal((K, M) if tA else (M, K)).astype(np.float32)
     b = g.standard_normal((N, K) if tB else (K, N)).astype(np.float32)
     c0 = g.standard_normal((M, N)).astype(np.float32)
     A, Bm, C = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), torch.from_numpy(c0.copy()).cuda()
+    if tA and M % 4:
+        # a transposed A is read along M in float4: rejected before any launch
+        with pytest.raises(hip.Wkv7Error, match="multiples of 4"):
+            hip.wkv7_gemm_bf16(A, Bm, C, transA=tA, transB=tB, beta=0.5)
+        return
     print(f"[gemm_bf16] M={M} N={N} K={K} tA={tA} tB={tB}", flush=True)
     hip.wkv7_gemm_bf16(A, Bm, C, transA=tA, transB=tB, beta=0.5)
     torch.cuda.synchronize()
