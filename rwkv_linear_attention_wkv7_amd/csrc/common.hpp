@@ -142,14 +142,14 @@ __device__ __forceinline__ float rows4sum(float x) {
 // of the values with cc == l/16.  Two permlane-swap rounds, 3*NQ swap+add pairs.
 template <int NQ>
 __device__ __forceinline__ void rows4_reduce_scatter(float (&x)[4 * NQ]) {
-  // round 1: lanes 0-31 keep cc 0,1 (+ partner's), lanes 32-63 keep cc 2,3
+  // stage 1: lanes 0-31 keep cc 0,1 (+ partner's), lanes 32-63 keep cc 2,3
 #pragma unroll
   for (int i = 0; i < 2 * NQ; i++) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + 2 * NQ]),
                                               false, false);
     x[i] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   }
-  // round 2: within each half, even rows keep the first cc, odd rows the second
+  // stage 2: within each half, even rows keep the first cc, odd rows the second
 #pragma unroll
   for (int i = 0; i < NQ; i++) {
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + NQ]),
