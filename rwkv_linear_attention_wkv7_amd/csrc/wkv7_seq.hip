@@ -209,14 +209,16 @@ __global__ __launch_bounds__(256) void fwd_seq(
     for (int m = 0; m < RPT; m++) yb[m] = 0.f;
     if (nt == TT) {
       // the next token's inputs are read from LDS while this one runs
-      Tok tc, tn;
+      Tok tc, tn, tn2;
       ldtok(buf, 0, tc);
+      ldtok(buf, 1, tn);
 #pragma unroll
       for (int tt = 0; tt < TT; tt++) {
-        if (tt + 1 < TT) ldtok(buf, tt + 1, tn);
+        if (tt + 2 < TT) ldtok(buf, tt + 2, tn2);
         __builtin_amdgcn_sched_barrier(0);
         token_in(tc, tt);
         tc = tn;
+        tn = tn2;
       }
     } else {
       for (int tt = 0; tt < nt; tt++) token(buf, tt);
