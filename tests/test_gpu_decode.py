@@ -67,11 +67,12 @@ def test_decode_full_size_sampled_streams(hip):
         assert_close(k, st[k].cpu().numpy()[:, idx], ref_st[k], 1e-4)
 
 
-@pytest.mark.parametrize("B", [64, 514, 1540])
+@pytest.mark.parametrize("B", [64, 514, 1540, 2048])
 def test_decode_graph_replay_matches_eager(hip, B):
     """A captured decode step replayed several times (eager work and syncs in
-    between) gives bitwise the eager results; at B = 514 and 1540 the capture
-    holds two concurrent stream groups (fork and join across HIP streams)."""
+    between) gives bitwise the eager results; from B = 514 on (2048: the
+    benchmark's stream count) the capture holds two concurrent stream groups
+    (fork and join across HIP streams)."""
     T = 3
     m, ocfg, dm = _setup(2, 128, 2, 256, 64, (16, 16, 16, 32), B, seed=2, perturbed=True, std=0.2)
     tok = torch.from_numpy(synth.token_ids(B, T, 64, seed=8)).cuda()
