@@ -189,6 +189,10 @@ int timemix_forward(const tm_shape *s, const tm_weights *W, int B, int T,
  * (the forward is recomputed into the workspace).  G: every field written.
  * dx: [B][T][C]; dx_prev: [B][C] or NULL; dv_first_in: layer 0 only, [B][T][C]
  * or NULL; dv_first_out: layer > 0 only, [B][T][C] or NULL; ds0: fp32 or NULL.
+ * The weight gradients (the X^T dY products) run on a library stream forked
+ * from `stream` and joined back to it before the call returns (the
+ * rwkv7_decode_step side stream; same creation rule and lock), overlapping
+ * the input-gradient chain; everything stays ordered on `stream`.
  */
 int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
                      const float *x, const float *x_prev, const float *v_first,
@@ -290,7 +294,10 @@ size_t rwkv7_train_workspace_bytes(const rwkv7_config *cfg, int B, int T);
  * v_first gradient of the later layers).  Differs from the page: every sum
  * over tokens (parameter and embedding gradients, the loss) is done in a
  * fixed order, so the step is bitwise reproducible.  GEMMs run in fp32 on
- * the matrix cores; WKV7 state and accumulation are fp32.
+ * the matrix cores; WKV7 state and accumulation are fp32.  The weight
+ * gradients of the head, the channel-mixes and the time-mixes run on the
+ * library side stream as in timemix_backward, joined back to `stream` within
+ * every block.
  * tokens, targets: [B][T] int32 device (ids outside [0, V) are clamped);
  * loss: one fp32 device value (written).
  */

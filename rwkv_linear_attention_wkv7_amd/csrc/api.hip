@@ -187,6 +187,53 @@ extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const vo
 
 // -------------------------------------------------------------- time-mix --
 namespace {
+// Library side stream per device (default priority), forked from the
+// caller's stream and joined back with events, so work on it stays ordered
+// with the caller's stream and is recorded into a graph when the caller
+// captures.  Created by the first call that wants it outside a capture;
+// without it everything runs on the caller's stream.  g_fj_mu is held while
+// a call enqueues work that uses the shared events.
+constexpr int SIDE_STREAMS = 1;
+struct ForkJoin {
+  hipStream_t side[SIDE_STREAMS] = {};
+  hipEvent_t fork = nullptr, join[SIDE_STREAMS] = {};
+  hipEvent_t mark[2] = {};  // intermediate fork points
+  bool ready = false, failed = false;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_fj_mu;
+ForkJoin g_fj[MAX_DEVICES];
+
+// Locks g_fj_mu on success (the caller unlocks once its work is enqueued);
+// nullptr (nothing locked) when no side stream can be had.
+ForkJoin* fork_join_acquire(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  g_fj_mu.lock();
+  ForkJoin& f = g_fj[dev];
+  if (!f.ready && !f.failed) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      g_fj_mu.unlock();  // never create resources inside a capture
+      return nullptr;
+    }
+    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&f.mark[0], hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&f.mark[1], hipEventDisableTiming) != hipSuccess;
+    for (int i = 0; i < SIDE_STREAMS && !f.failed; i++)
+      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
+                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
+    f.ready = !f.failed;
+  }
+  if (!f.ready) {
+    g_fj_mu.unlock();
+    return nullptr;
+  }
+  return &f;
+}
+}  // namespace
+
+namespace {
 
 struct TmCache {
   float *xr, *xw, *xk, *xv, *xa, *xg;
@@ -374,13 +421,41 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                      const float* x_prev, const float* v_first, const float* s0, const float* dout,
                      const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
                      float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
-                     float* ds0, hipStream_t st, int prec = GEMM_F32) {
+                     float* ds0, hipStream_t st, int prec = GEMM_F32, bool caller_forks = false,
+                     ForkJoin* caller_fj = nullptr) {
   const int BT = B * T, C = s->C, L = s->layer_id;
 
+  // The weight gradients (X^T dY products, split along the tokens) feed
+  // nothing else in the backward, so they run on the library side stream
+  // while this stream carries on with the input-gradient chain.  Each waits
+  // for the point of this stream where its operands are complete (fork:
+  // start; mark[0]: after the pre-WKV backward; mark[1]: after the LoRA
+  // input gradients), only they use the split-K scratch, and this stream
+  // joins the side stream before returning, so the next call may reuse
+  // every buffer.
+  // caller_forks: the caller holds g_fj_mu and passes its side stream
+  // resources (or nullptr: none)
+  ForkJoin* fj = caller_forks ? caller_fj : fork_join_acquire(st);
+  std::unique_lock<std::mutex> hold;
+  if (fj && !caller_forks) hold = std::unique_lock<std::mutex>(g_fj_mu, std::adopt_lock);
+  hipStream_t ss = fj ? fj->side[0] : st;
+  auto fork_at = [&](hipEvent_t e) -> hipError_t {
+    if (!fj) return hipSuccess;
+    hipError_t r = hipEventRecord(e, st);
+    return r != hipSuccess ? r : hipStreamWaitEvent(ss, e, 0);
+  };
+  struct Join {  // joins the side stream on every return path
+    ForkJoin* fj;
+    hipStream_t st, ss;
+    ~Join() {
+      if (fj && hipEventRecord(fj->join[0], ss) == hipSuccess) (void)hipStreamWaitEvent(st, fj->join[0], 0);
+    }
+  } join{fj, st, ss};
+
+  HIPCHK(fork_at(fj ? fj->fork : nullptr), "backward fork");
   // output projection
   HIPCHK(gemm_run(prec, false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
-  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, st), "dWo");
-
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, ss), "dWo");
   TmBwd p;
   memset(&p, 0, sizeof(p));
   p.BT = BT; p.T = T; p.C = C; p.layer_id = L;
@@ -407,38 +482,43 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                               bb.wkv_part, st),
          "wkv7 backward");
   HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
-
   const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
   float* sk = bb.splitk;
+  HIPCHK(fork_at(fj ? fj->mark[0] : nullptr), "backward fork");
+  // r, k, v weight gradients (dr from the post-WKV backward, dk and dv from
+  // the pre-WKV backward)
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, ss), "dWr");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, ss), "dWk");
+  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, ss), "dWv");
+
   // a: a = sigmoid(a0 + (xa A1) A2)
   HIPCHK(gemm_run(prec, false, true, BT, Da, C, bb.dpre_a, C, W->A2, C, bb.d_la, Da, 0.f, 0, nullptr, 1, nullptr, st), "d_la");
-  HIPCHK(gemm_run(prec, true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, st), "dA2");
+  HIPCHK(gemm_run(prec, true, false, Da, C, BT, m.la, Da, bb.dpre_a, C, G->A2, C, 0.f, 0, nullptr, splitk_for(Da, C, BT), sk, ss), "dA2");
   HIPCHK(gemm_run(prec, false, true, BT, C, Da, bb.d_la, Da, W->A1, Da, bb.dxa, C, 0.f, 0, nullptr, 1, nullptr, st), "dxa");
-  HIPCHK(gemm_run(prec, true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, st), "dA1");
   // w: w = exp(-c sigmoid(w0 + tanh(xw W1) W2))
   HIPCHK(gemm_run(prec, false, true, BT, Dw, C, bb.dpre_w, C, W->W2, C, bb.d_lw, Dw, 0.f, 3, m.tw, 1, nullptr, st), "d_lw");
-  HIPCHK(gemm_run(prec, true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, st), "dW2");
+  HIPCHK(gemm_run(prec, true, false, Dw, C, BT, m.tw, Dw, bb.dpre_w, C, G->W2, C, 0.f, 0, nullptr, splitk_for(Dw, C, BT), sk, ss), "dW2");
   HIPCHK(gemm_run(prec, false, true, BT, C, Dw, bb.d_lw, Dw, W->W1, Dw, bb.dxw, C, 0.f, 0, nullptr, 1, nullptr, st), "dxw");
-  HIPCHK(gemm_run(prec, true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, st), "dW1");
   // g: g = sigmoid(xg G1) G2
   HIPCHK(gemm_run(prec, false, true, BT, Dg, C, bb.dg, C, W->G2, C, bb.d_lg, Dg, 0.f, 4, m.sg, 1, nullptr, st), "d_lg");
-  HIPCHK(gemm_run(prec, true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, st), "dG2");
+  HIPCHK(gemm_run(prec, true, false, Dg, C, BT, m.sg, Dg, bb.dg, C, G->G2, C, 0.f, 0, nullptr, splitk_for(Dg, C, BT), sk, ss), "dG2");
   HIPCHK(gemm_run(prec, false, true, BT, C, Dg, bb.d_lg, Dg, W->G1, Dg, bb.dxg, C, 0.f, 0, nullptr, 1, nullptr, st), "dxg");
-  HIPCHK(gemm_run(prec, true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, st), "dG1");
   // value residual LoRA (layer > 0)
   if (L > 0) {
     HIPCHK(gemm_run(prec, false, true, BT, Dv, C, bb.dpre_v, C, W->V2, C, bb.d_lv, Dv, 0.f, 0, nullptr, 1, nullptr, st), "d_lv");
-    HIPCHK(gemm_run(prec, true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, st), "dV2");
+    HIPCHK(gemm_run(prec, true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, ss), "dV2");
     HIPCHK(gemm_run(prec, false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
-    HIPCHK(gemm_run(prec, true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, st), "dV1");
   }
+  HIPCHK(fork_at(fj ? fj->mark[1] : nullptr), "backward fork");
+  HIPCHK(gemm_run(prec, true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, ss), "dA1");
+  HIPCHK(gemm_run(prec, true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, ss), "dW1");
+  HIPCHK(gemm_run(prec, true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, ss), "dG1");
+  if (L > 0)
+    HIPCHK(gemm_run(prec, true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, ss), "dV1");
   // r, k, v projections
   HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
-  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWr");
   HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
-  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xk, C, bb.dk, C, G->Wk, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWk");
   HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
-  HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xv, C, bb.dv, C, G->Wv, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, st), "dWv");
 
   HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
   const int nblk = tm_num_token_blocks(BT);
@@ -636,7 +716,7 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
 // 2048 streams: 1.82 ms per step in one group, 1.64 ms in two, 2.01 ms in
 // four (smaller groups make every GEMM and row kernel less efficient).
 constexpr int DECODE_SPLIT_MIN = 512;
-constexpr int DECODE_MAX_GROUPS = 2;
+constexpr int DECODE_MAX_GROUPS = SIDE_STREAMS + 1;
 
 int decode_groups(int B, int nb[DECODE_MAX_GROUPS]) {
   const int g = B < DECODE_SPLIT_MIN ? 1 : std::min(DECODE_MAX_GROUPS, B / DECODE_SPLIT_MIN + (B % DECODE_SPLIT_MIN ? 1 : 0));
@@ -654,43 +734,6 @@ void carve_decode_all(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs d[DE
   int nb[DECODE_MAX_GROUPS];
   const int g = decode_groups(B, nb);
   for (int i = 0; i < g; i++) carve_decode(c, cfg, nb[i], d[i]);
-}
-
-// Per-device fork/join resources, created on first use outside a capture.
-struct ForkJoin {
-  hipStream_t side[DECODE_MAX_GROUPS - 1] = {};
-  hipEvent_t fork = nullptr, join[DECODE_MAX_GROUPS - 1] = {};
-  bool ready = false, failed = false;
-};
-constexpr int MAX_DEVICES = 64;
-std::mutex g_fj_mu;
-ForkJoin g_fj[MAX_DEVICES];
-
-// Locks g_fj_mu on success (the caller unlocks after enqueuing every group);
-// nullptr (nothing locked) when no side streams can be had: the groups then
-// run one after the other on the caller's stream.
-ForkJoin* fork_join_acquire(hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
-  g_fj_mu.lock();
-  ForkJoin& f = g_fj[dev];
-  if (!f.ready && !f.failed) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-      g_fj_mu.unlock();  // never create resources inside a capture
-      return nullptr;
-    }
-    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess;
-    for (int i = 0; i < DECODE_MAX_GROUPS - 1 && !f.failed; i++)
-      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
-                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
-    f.ready = !f.failed;
-  }
-  if (!f.ready) {
-    g_fj_mu.unlock();
-    return nullptr;
-  }
-  return &f;
 }
 
 // One group of nb streams starting at stream b0 of B: the per-layer state
@@ -975,9 +1018,30 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, st), "cross-entropy");
 
   // ---------------- backward
+  // Weight gradients run on the library side stream (see tm_backward_impl):
+  // here the head's and each channel-mix's, which only use t.splitk among the
+  // scratch buffers; every block's time-mix backward joins the side stream
+  // before returning, before any buffer they read is written again.
+  ForkJoin* fj = fork_join_acquire(st);
+  std::unique_lock<std::mutex> hold;
+  if (fj) hold = std::unique_lock<std::mutex>(g_fj_mu, std::adopt_lock);
+  hipStream_t ss = fj ? fj->side[0] : st;
+  auto fork_here = [&]() -> hipError_t {
+    if (!fj) return hipSuccess;
+    hipError_t r = hipEventRecord(fj->fork, st);
+    return r != hipSuccess ? r : hipStreamWaitEvent(ss, fj->fork, 0);
+  };
+  struct Join {
+    ForkJoin* fj;
+    hipStream_t st, ss;
+    ~Join() {
+      if (fj && hipEventRecord(fj->join[0], ss) == hipSuccess) (void)hipStreamWaitEvent(st, fj->join[0], 0);
+    }
+  } join{fj, st, ss};
+  HIPCHK(fork_here(), "backward fork");
   HIPCHK(gemm_run(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
   HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
-                      splitk_for(C, V, BT), t.splitk, st), "dhead");
+                      splitk_for(C, V, BT), t.splitk, ss), "dhead");
   HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(L), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
   HIPCHK(reduce_ln(G->ln_out_w, G->ln_out_b), "ln_out grads");
   HIPCHK(stk_launch_fill_zero(t.dvf, tokC, st), "zero dv_first");
@@ -989,11 +1053,12 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     if (!keep) CHK(block_fwd(l, a));  // recompute this block's forward from its input
     // channel-mix backward
     HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "dfk");
+    HIPCHK(fork_here(), "backward fork");  // t.dx and t.dfk complete
     HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
-                        splitk_for(F, C, BT), t.splitk, st), "dWv");
-    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
+                        splitk_for(F, C, BT), t.splitk, ss), "dWv");
     HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
-                        splitk_for(C, F, BT), t.splitk, st), "dWk");
+                        splitk_for(C, F, BT), t.splitk, ss), "dWk");
+    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
     HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
@@ -1004,7 +1069,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
     CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
-                         nullptr, st, prec));
+                         nullptr, st, prec, true, fj));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }
