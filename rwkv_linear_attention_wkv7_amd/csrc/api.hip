@@ -87,6 +87,53 @@ struct Carver {
 }  // namespace
 
 // ------------------------------------------------------------------ WKV7 --
+namespace {
+// Library side stream per device (default priority), forked from the
+// caller's stream and joined back with events, so work on it stays ordered
+// with the caller's stream and is recorded into a graph when the caller
+// captures.  Created by the first call that wants it outside a capture;
+// without it everything runs on the caller's stream.  g_fj_mu is held while
+// a call enqueues work that uses the shared events.
+constexpr int SIDE_STREAMS = 1;
+struct ForkJoin {
+  hipStream_t side[SIDE_STREAMS] = {};
+  hipEvent_t fork = nullptr, join[SIDE_STREAMS] = {};
+  hipEvent_t mark[2] = {};  // intermediate fork points
+  bool ready = false, failed = false;
+};
+constexpr int MAX_DEVICES = 64;
+std::mutex g_fj_mu;
+ForkJoin g_fj[MAX_DEVICES];
+
+// Locks g_fj_mu on success (the caller unlocks once its work is enqueued);
+// nullptr (nothing locked) when no side stream can be had.
+ForkJoin* fork_join_acquire(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  g_fj_mu.lock();
+  ForkJoin& f = g_fj[dev];
+  if (!f.ready && !f.failed) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      g_fj_mu.unlock();  // never create resources inside a capture
+      return nullptr;
+    }
+    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&f.mark[0], hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&f.mark[1], hipEventDisableTiming) != hipSuccess;
+    for (int i = 0; i < SIDE_STREAMS && !f.failed; i++)
+      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
+                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
+    f.ready = !f.failed;
+  }
+  if (!f.ready) {
+    g_fj_mu.unlock();
+    return nullptr;
+  }
+  return &f;
+}
+}  // namespace
+
 extern "C" const char* wkv7_last_error(void) { return g_err; }
 
 extern "C" int wkv7_checkpoint_interval(void) { return wkv7_ckpt_interval_const(); }
@@ -134,6 +181,7 @@ extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int 
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
   Carver c(nullptr);
   c.take(wkv7_bwd_partial_floats(B, T, H));
+  c.take((size_t)2 * B * H * WKV7_N * WKV7_N);  // state-gradient hand-over between segments
   if (!have_ckpt) c.take(ckpt_floats(B, T, H));
   return c.off;
 }
@@ -158,6 +206,7 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
   CHK(check_f32_ptr(ws, "ws", true));
   Carver cv(ws);
   float* part = cv.take(wkv7_bwd_partial_floats(B, T, H));
+  float* gbuf = cv.take((size_t)2 * B * H * WKV7_N * WKV7_N);
   const float* ck = ckpt;
   if (!ck) {
     float* tmp = cv.take(ckpt_floats(B, T, H));
@@ -165,6 +214,20 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
                                stream),
            "wkv7_backward checkpoint recompute");
     ck = tmp;
+  }
+  if (wkv7_bwd_segments(T) > 1) {
+    // long sequence: the reverse pass runs in segments, each segment's
+    // partial reduction on the library side stream overlapping the next
+    // segment's pass; without a side stream, one pass
+    ForkJoin* fj = fork_join_acquire(stream);
+    if (fj) {
+      std::lock_guard<std::mutex> hold(g_fj_mu, std::adopt_lock);
+      HIPCHK(wkv7_launch_backward_segmented(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk,
+                                            dv, da, db, ds0, part, gbuf, stream, fj->side[0],
+                                            fj->mark[0], fj->join[0]),
+             "wkv7_backward launch");
+      return WKV7_OK;
+    }
   }
   HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
                               db, ds0, part, stream),
@@ -186,52 +249,6 @@ extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const vo
 }
 
 // -------------------------------------------------------------- time-mix --
-namespace {
-// Library side stream per device (default priority), forked from the
-// caller's stream and joined back with events, so work on it stays ordered
-// with the caller's stream and is recorded into a graph when the caller
-// captures.  Created by the first call that wants it outside a capture;
-// without it everything runs on the caller's stream.  g_fj_mu is held while
-// a call enqueues work that uses the shared events.
-constexpr int SIDE_STREAMS = 1;
-struct ForkJoin {
-  hipStream_t side[SIDE_STREAMS] = {};
-  hipEvent_t fork = nullptr, join[SIDE_STREAMS] = {};
-  hipEvent_t mark[2] = {};  // intermediate fork points
-  bool ready = false, failed = false;
-};
-constexpr int MAX_DEVICES = 64;
-std::mutex g_fj_mu;
-ForkJoin g_fj[MAX_DEVICES];
-
-// Locks g_fj_mu on success (the caller unlocks once its work is enqueued);
-// nullptr (nothing locked) when no side stream can be had.
-ForkJoin* fork_join_acquire(hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
-  g_fj_mu.lock();
-  ForkJoin& f = g_fj[dev];
-  if (!f.ready && !f.failed) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-      g_fj_mu.unlock();  // never create resources inside a capture
-      return nullptr;
-    }
-    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&f.mark[0], hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&f.mark[1], hipEventDisableTiming) != hipSuccess;
-    for (int i = 0; i < SIDE_STREAMS && !f.failed; i++)
-      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
-                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
-    f.ready = !f.failed;
-  }
-  if (!f.ready) {
-    g_fj_mu.unlock();
-    return nullptr;
-  }
-  return &f;
-}
-}  // namespace
 
 namespace {
 

@@ -253,7 +253,10 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ a,
     const T* __restrict__ bv, const T* __restrict__ dy, const float* __restrict__ ckpt,
     const float* __restrict__ dsT, float* __restrict__ part, T* __restrict__ dv,
-    float* __restrict__ ds0) {
+    float* __restrict__ ds0, int c_lo, int c_hi) {
+  // chunks [c_lo, c_hi) of the sequence are processed (last to first); G
+  // enters as dsT (the gradient of the state after chunk c_hi - 1) and leaves
+  // as ds0 (before chunk c_lo), so a long sequence can run as several launches
   constexpr int ROWS = RPT * RG, NSPLIT = N / ROWS, NW = RG / 4, NT = 16 * RG;
   static_assert(RG % 4 == 0, "whole waves");
   // staging, double-buffered, widened to fp32 once on the way into LDS: the
@@ -499,19 +502,19 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     }
   };
 
-  fetch(nck - 1);
-  commit(0, min(CKL, Tn - (nck - 1) * CKL));
+  fetch(c_hi - 1);
+  commit(0, min(CKL, Tn - (c_hi - 1) * CKL));
   int buf = 0;
-  for (int c = nck - 1; c >= 0; c--, buf ^= 1) {
+  for (int c = c_hi - 1; c >= c_lo; c--, buf ^= 1) {
     const int tc0 = c * CKL, ns = min(CKL, Tn - tc0);
 #pragma unroll
     for (int m = 0; m < RPT; m++)
 #pragma unroll
       for (int cc = 0; cc < 4; cc++) Sh[0][m][cc] = xck[m][cc];
     lds_barrier();  // staged chunk visible; previous readers of the other buffer done
-    if (c > 0) fetch(c - 1);
+    if (c > c_lo) fetch(c - 1);
     chunk(buf, tc0, ns);
-    if (c > 0) commit(buf ^ 1, CKL);
+    if (c > c_lo) commit(buf ^ 1, CKL);
   }
   if (ds0) {
 #pragma unroll
@@ -521,24 +524,31 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
   }
 }
 
-// out_vec = sum over slices of part[slice][vec] (fixed order), cast to T.
+// out_vec = sum over slices of part[slice][vec] (fixed order), cast to T,
+// for tokens [t_lo, t_lo + t_len) of every sequence (rows of C4 float4).
 template <typename T, int NS>
-__global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4,
-                                                           const float* __restrict__ part, T* dr,
-                                                           T* dk, T* db, T* dw, T* da) {
+__global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int Tn, int t_lo, int t_len,
+                                                           int C4, const float* __restrict__ part,
+                                                           T* dr, T* dk, T* db, T* dw, T* da) {
   // U float4 per thread per pass, every slice's loads issued together
   // (clamped indices, guarded stores): enough loads in flight to stream the
   // partials at HBM rate.  The slices are summed in slice order.
   constexpr int U = 4;
-  const size_t n4 = plane4 * 5, stride = (size_t)gridDim.x * 256;
+  const size_t seq4 = (size_t)t_len * C4;                  // float4 per sequence in range
+  const size_t seg4 = plane4 / ((size_t)Tn * C4) * seq4;   // float4 per vector in range
+  const size_t n4 = seg4 * 5, stride = (size_t)gridDim.x * 256;
   const f4* P = reinterpret_cast<const f4*>(part);
+  auto elem = [&](size_t i, int& vi) {
+    vi = (int)(i / seg4);
+    const size_t r = i - (size_t)vi * seg4, b = r / seq4;
+    return (b * Tn + t_lo) * C4 + (r - b * seq4);
+  };
   for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n4; i0 += stride * U) {
     f4 s[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const size_t i = min(i0 + u * stride, n4 - 1);
-      const int vi = (int)(i / plane4);
-      const size_t e4 = i - (size_t)vi * plane4;
+      int vi;
+      const size_t e4 = elem(min(i0 + u * stride, n4 - 1), vi);
       f4 x[NS];
 #pragma unroll
       for (int sp = 0; sp < NS; sp++)
@@ -551,8 +561,8 @@ __global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4,
     for (int u = 0; u < U; u++) {
       const size_t i = i0 + u * stride;
       if (i < n4) {
-        const int vi = (int)(i / plane4);
-        const size_t e4 = i - (size_t)vi * plane4;
+        int vi;
+        const size_t e4 = elem(i, vi);
         T* o = vi == 0 ? dr : vi == 1 ? dk : vi == 2 ? db : vi == 3 ? dw : da;
         store4(o + e4 * 4, s[u]);
       }
@@ -593,33 +603,41 @@ hipError_t launch_forward_t(int B, int T_, int H, const void* r, const void* w, 
   return hipGetLastError();
 }
 
+// The reverse pass over chunks [c_lo, c_hi), then (on `rst`) the reduction
+// of its column partials for those chunks' tokens.
 template <typename T>
 hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w, const void* k,
                              const void* v, const void* a, const void* b, const void* dy,
                              const float* ckpt, const float* dsT, void* dr, void* dw, void* dk,
-                             void* dv, void* da, void* db, float* ds0, float* part,
-                             hipStream_t st) {
+                             void* dv, void* da, void* db, float* ds0, float* part, int c_lo,
+                             int c_hi, hipStream_t st, hipStream_t rst, hipEvent_t ready) {
   const int ns = bwd_nsplit(B, H);
   const dim3 grid(B * H * ns);
   if (ns == 4)
     hipLaunchKernelGGL((bwd_seq<1, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi);
   else
     hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0);
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t plane4 = (size_t)B * T_ * H * N / 4;
-  size_t blocks = (plane4 * 5 + 1023) / 1024;
+  if (rst != st) {
+    if ((e = hipEventRecord(ready, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(rst, ready, 0)) != hipSuccess) return e;
+  }
+  const int t_lo = c_lo * CKL, t_len = min(T_, c_hi * CKL) - t_lo;
+  const int C4 = H * N / 4;
+  const size_t plane4 = (size_t)B * T_ * C4;
+  size_t blocks = ((size_t)B * t_len * C4 * 5 + 1023) / 1024;
   if (blocks > 4096) blocks = 4096;
   if (ns == 4)
-    hipLaunchKernelGGL((reduce_bwd_partials<T, 4>), dim3((unsigned)blocks), dim3(256), 0, st, plane4,
-                       part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+    hipLaunchKernelGGL((reduce_bwd_partials<T, 4>), dim3((unsigned)blocks), dim3(256), 0, rst,
+                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
   else
-    hipLaunchKernelGGL((reduce_bwd_partials<T, 2>), dim3((unsigned)blocks), dim3(256), 0, st, plane4,
-                       part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+    hipLaunchKernelGGL((reduce_bwd_partials<T, 2>), dim3((unsigned)blocks), dim3(256), 0, rst,
+                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
   return hipGetLastError();
 }
 
@@ -662,12 +680,46 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
                                 float* part, hipStream_t st) {
+  const int nck = (T + wkv7k::CKL - 1) / wkv7k::CKL;
   if (dtype == 1)
     return wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk,
-                                            dv, da, db, ds0, part, st);
+                                            dv, da, db, ds0, part, 0, nck, st, st, nullptr);
   return wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk, dv,
-                                         da, db, ds0, part, st);
+                                         da, db, ds0, part, 0, nck, st, st, nullptr);
 }
 
+int wkv7_bwd_segments(int T) {
+  // segments of at least 2048 tokens, at most 4
+  const int s = T / 2048;
+  return s < 2 ? 1 : (s > 4 ? 4 : s);
+}
+
+hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const void* r,
+                                          const void* w, const void* k, const void* v,
+                                          const void* a, const void* b, const void* dy,
+                                          const float* ckpt, const float* dsT, void* dr, void* dw,
+                                          void* dk, void* dv, void* da, void* db, float* ds0,
+                                          float* part, float* gbuf, hipStream_t st,
+                                          hipStream_t side, hipEvent_t ready, hipEvent_t done) {
+  const int nck = (T + wkv7k::CKL - 1) / wkv7k::CKL, nseg = wkv7_bwd_segments(T);
+  const size_t gsz = (size_t)B * H * WKV7_N * WKV7_N;
+  hipError_t e = hipSuccess;
+  // segments last to first; G is handed over through gbuf (ping-pong)
+  for (int sgi = nseg - 1; sgi >= 0 && e == hipSuccess; sgi--) {
+    const int c_lo = (int)((long)nck * sgi / nseg), c_hi = (int)((long)nck * (sgi + 1) / nseg);
+    const float* gin = sgi == nseg - 1 ? dsT : gbuf + (size_t)(sgi & 1) * gsz;
+    float* gout = sgi == 0 ? ds0 : gbuf + (size_t)((sgi + 1) & 1) * gsz;
+    if (dtype == 1)
+      e = wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
+                                           da, db, gout, part, c_lo, c_hi, st, side, ready);
+    else
+      e = wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
+                                          da, db, gout, part, c_lo, c_hi, st, side, ready);
+  }
+  // join the reductions back, whatever happened
+  hipError_t ej = hipEventRecord(done, side);
+  if (ej == hipSuccess) ej = hipStreamWaitEvent(st, done, 0);
+  return e != hipSuccess ? e : ej;
+}
 
 int wkv7_ckpt_interval_const() { return wkv7k::CKL; }

@@ -124,6 +124,18 @@ def test_wkv7_bf16_long_context_full_size(hip, chunked):
         _check(d, y, sT, g, False, 2e-2, 2e-2, sel=(slice(b, b + 1), slice(h, h + 1)))
 
 
+def test_wkv7_backward_segments(hip):
+    """T = 4200: the backward call runs its reverse pass as two launches (the
+    state gradient handed from one to the next) with each segment's column
+    reduction on a second stream; ragged last chunk, nonzero s0 and dsT,
+    ds0 checked; fp32 against the oracle."""
+    B, T, H = 1, 4200, 2
+    d = synth.wkv7_inputs(B, T, H, 64, seed=21, with_state=True)
+    print(f"[wkv7 segments] B={B} T={T} H={H}", flush=True)
+    y, sT, g = _run(hip, d, torch.float32, True, False)
+    _check(d, y, sT, g, True, 1e-4, 1e-3)
+
+
 def test_wkv7_chunked_long_few_heads(hip):
     """B=1, T=4096, H=16: few (b, h) pairs and a long sequence through the
     chunked matrix-core forward (256 chunks per head, state carried across
