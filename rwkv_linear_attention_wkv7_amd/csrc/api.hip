@@ -286,6 +286,7 @@ struct TmBwdBufs {
   float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *d_la, *d_lw, *d_lg, *d_lv;
   float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg, *part_post, *part_pre, *part_shift, *splitk, *out_tmp;
   float* wkv_part;
+  float* wkv_g;  // state-gradient hand-over between backward segments
 };
 
 // split-K factor for a weight gradient [Mo][No] reduced over BT tokens
@@ -325,6 +326,7 @@ void carve_bwd(Carver& c, const tm_shape* s, int B, int T, TmBwdBufs& m) {
   m.part_shift = c.take((size_t)6 * nblk * s->C);
   m.splitk = c.take(splitk_scratch(s, (int)BT));
   m.wkv_part = c.take(wkv7_bwd_partial_floats(B, T, s->H));
+  m.wkv_g = c.take((size_t)2 * B * s->H * WKV7_N * WKV7_N);
   m.out_tmp = nullptr;
 }
 
@@ -494,7 +496,14 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
 
   HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
-  HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
+  if (fj && wkv7_bwd_segments(T) > 1)  // segment reductions overlap on the side stream
+    HIPCHK(wkv7_launch_backward_segmented(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv,
+                                          bb.dy_wkv, m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA,
+                                          bb.gB, ds0, bb.wkv_part, bb.wkv_g, st, ss, fj->mark[0],
+                                          fj->join[0]),
+           "wkv7 backward");
+  else
+    HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
                               m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
                               bb.wkv_part, st),
          "wkv7 backward");

@@ -689,8 +689,8 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
 }
 
 int wkv7_bwd_segments(int T) {
-  // segments of at least 2048 tokens, at most 4
-  const int s = T / 2048;
+  // segments of at least 512 tokens, at most 4
+  const int s = T / 512;
   return s < 2 ? 1 : (s > 4 ? 4 : s);
 }
 
