@@ -99,12 +99,12 @@ size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
  * ckpt: the forward's checkpoints, or NULL (then they are recomputed into the
  * workspace).  dy: [B][T][H][N] `dtype`.  dsT, s0: fp32 [B][H][N][N] or NULL.
  * dr,dw,dk,dv,da,db: [B][T][H][N] `dtype` (written).  ds0: fp32 or NULL.
- * From T = 4096 on, the reverse pass runs as 2-4 launches over consecutive
- * token segments (last first, the state gradient handed over through the
- * workspace) and each segment's reduction of the column partials runs on
- * the library side stream of rwkv7_decode_step (same creation rule and
- * lock), overlapping the next segment's pass; it is joined back to `stream`
- * before the call returns.
+ * From T = 1024 on, the reverse pass runs as 2-4 launches over consecutive
+ * token segments of at least 512 tokens (last first, the state gradient
+ * handed over through the workspace), and each segment's reduction of the
+ * column partials runs on the library side stream of rwkv7_decode_step (same
+ * creation rule and lock), overlapping the next segment's pass; it is joined
+ * back to `stream` before the call returns.
  */
 int wkv7_backward(int B, int T, int H, int N, int dtype,
                   const void *r, const void *w, const void *k, const void *v,
