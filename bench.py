@@ -156,7 +156,7 @@ def setup_wkv7_long():
     # step (G += dy r^T, dr, dv, dk, db, dsa, dw, da: 2 N^2 each; G update
     # 3 N^2) plus 7 N^2 to recompute sa and the state from the checkpoint.
     flops = 26.0 * N * N * B * T * H
-    roof = dict(kernel="wkv7 backward (sequential, checkpointed)", bound="alu", work=flops,
+    roof = dict(kernel="wkv7 backward call (checkpointed, 4 reverse-pass segments)", bound="alu", work=flops,
                 unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom, key="wkv7_bwd_long",
                 src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
 
