@@ -14,6 +14,13 @@
  *    validated before anything is enqueued; on error nothing is enqueued and
  *    wkv7_last_error() describes the first problem found.
  *  - N must be 64.  Pointers must be 16-byte aligned (8-byte for bf16 data).
+ *  - Aliasing: no tensor a call writes may overlap any other tensor of the
+ *    call (read or written), including the workspace; tensors that are only
+ *    read may overlap each other.  The exceptions are the in-place updates
+ *    each call names (sT == s0, the decode state); anything else returns
+ *    WKV7_EINVAL naming the two tensors.
+ *  - The library keeps no state between calls beyond its loaded code:
+ *    calls are re-entrant, from any thread, on any stream.
  */
 #ifndef WKV7_H
 #define WKV7_H
@@ -27,7 +34,7 @@ extern "C" {
 
 enum wkv7_status {
   WKV7_OK = 0,
-  WKV7_EINVAL = -1, /* bad shape, NULL required pointer, misalignment, bad alias */
+  WKV7_EINVAL = -1, /* bad shape, NULL required pointer, misalignment, overlapping tensors */
   WKV7_EHIP = -2,   /* a HIP launch or runtime error */
   WKV7_ENOSPC = -3  /* workspace smaller than the size query returned */
 };
@@ -39,6 +46,27 @@ enum wkv7_dtype {
 
 /* Thread-local description of the last error (empty string if none). */
 const char *wkv7_last_error(void);
+
+/*
+ * Optional second stream for the calls that overlap independent work on it
+ * (wkv7_backward, timemix_backward, rwkv7_decode_step, rwkv7_train_step; each
+ * says what it puts there).  Owned by the caller: a default-priority stream
+ * and four events created with hipEventDisableTiming (or made by
+ * wkv7_side_create).  A call forks the side stream from `stream` with these
+ * events and joins it back to `stream` before returning, so everything stays
+ * ordered on `stream` and a graph capture of `stream` records the side work
+ * too.  The library retains nothing; one wkv7_side must not be used by two
+ * calls at the same time (they would share its events).  NULL, or a side
+ * whose stream is `stream` itself, runs everything on `stream`.
+ */
+typedef struct {
+  hipStream_t stream;
+  hipEvent_t ev[4];
+} wkv7_side;
+/* Create / destroy a wkv7_side (stream with hipStreamNonBlocking, events with
+ * hipEventDisableTiming).  destroy accepts a zeroed or partly created side. */
+int wkv7_side_create(wkv7_side *side);
+int wkv7_side_destroy(wkv7_side *side);
 
 /* Checkpoint interval L used by wkv7_forward / wkv7_backward (tokens). */
 int wkv7_checkpoint_interval(void);
@@ -99,25 +127,28 @@ size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
  * ckpt: the forward's checkpoints, or NULL (then they are recomputed into the
  * workspace).  dy: [B][T][H][N] `dtype`.  dsT, s0: fp32 [B][H][N][N] or NULL.
  * dr,dw,dk,dv,da,db: [B][T][H][N] `dtype` (written).  ds0: fp32 or NULL.
- * From T = 1024 on, the reverse pass runs as 2-4 launches over consecutive
- * token segments of at least 512 tokens (last first, the state gradient
- * handed over through the workspace), and each segment's reduction of the
- * column partials runs on the library side stream of rwkv7_decode_step (same
- * creation rule and lock), overlapping the next segment's pass; it is joined
- * back to `stream` before the call returns.
+ * ws: at least wkv7_backward_workspace_bytes() bytes (16-byte aligned;
+ * contents undefined before and after).
+ * side: NULL, or a wkv7_side; with one, from T = 1024 on the reverse pass runs
+ * as 2-4 launches over consecutive token segments of at least 512 tokens
+ * (last first, the state gradient handed over through the workspace), and
+ * each segment's reduction of the column partials runs on the side stream,
+ * overlapping the next segment's pass.
  */
 int wkv7_backward(int B, int T, int H, int N, int dtype,
                   const void *r, const void *w, const void *k, const void *v,
                   const void *a, const void *b, const float *s0, const float *ckpt,
                   const void *dy, const float *dsT,
                   void *dr, void *dw, void *dk, void *dv, void *da, void *db,
-                  float *ds0, void *ws, size_t ws_bytes, hipStream_t stream);
+                  float *ds0, void *ws, size_t ws_bytes, const wkv7_side *side,
+                  hipStream_t stream);
 
 /*
  * Single-token streaming decode: the T = 1 forward with the state updated in
  * place.  Pages: the recurrence as for wkv7_forward; the per-layer streaming
  * state of "infotheory .../rwkv7/model.rs" (LayerState.att_state, [H][N][N]).
- * r,w,k,v,a,b,y: [B][H][N] `dtype`; state: [B][H][N][N] fp32 (read+written).
+ * r,w,k,v,a,b,y: [B][H][N] `dtype`; state: [B][H][N][N] fp32 (read and
+ * written in place; y must not overlap it or the inputs).
  */
 int wkv7_step(int B, int H, int N, int dtype,
               const void *r, const void *w, const void *k, const void *v,
@@ -178,9 +209,10 @@ size_t timemix_backward_workspace_bytes(const tm_shape *s, int B, int T);
  *   out = ((groupnorm_head(y) * ln_w + ln_b) + (sum_head r k' r_k) v') * g  Wo
  * x: [B][T][C]; x_prev: [B][C] or NULL (zeros) -- the token before x[:,0];
  * v_first: [B][T][C], written on layer 0, read otherwise; s0/sT: fp32
- * [B][H][N][N] or NULL; out: [B][T][C] (written); x_last: [B][C] or NULL
- * (written with x[:, T-1], the next call's x_prev); cache: NULL or
- * timemix_cache_bytes() bytes kept for timemix_backward.
+ * [B][H][N][N] or NULL (sT may equal s0: in-place update); out: [B][T][C]
+ * (written); x_last: [B][C] or NULL (written with x[:, T-1], the next call's
+ * x_prev; it may equal x_prev when T == 1); cache: NULL or
+ * timemix_cache_bytes() bytes kept for timemix_backward (then ws is unused).
  */
 int timemix_forward(const tm_shape *s, const tm_weights *W, int B, int T,
                     const float *x, const float *x_prev, float *v_first,
@@ -195,17 +227,16 @@ int timemix_forward(const tm_shape *s, const tm_weights *W, int B, int T,
  * (the forward is recomputed into the workspace).  G: every field written.
  * dx: [B][T][C]; dx_prev: [B][C] or NULL; dv_first_in: layer 0 only, [B][T][C]
  * or NULL; dv_first_out: layer > 0 only, [B][T][C] or NULL; ds0: fp32 or NULL.
- * The weight gradients (the X^T dY products) run on a library stream forked
- * from `stream` and joined back to it before the call returns (the
- * rwkv7_decode_step side stream; same creation rule and lock), overlapping
- * the input-gradient chain; everything stays ordered on `stream`.
+ * side: NULL, or a wkv7_side on which the weight gradients (the X^T dY
+ * products) run, overlapping the input-gradient chain on `stream` (and the
+ * segmented WKV7 reverse pass as in wkv7_backward).
  */
 int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
                      const float *x, const float *x_prev, const float *v_first,
                      const float *s0, const float *dout, const float *dsT,
                      const void *cache, tm_grads *G, float *dx, float *dx_prev,
                      const float *dv_first_in, float *dv_first_out, float *ds0,
-                     void *ws, size_t ws_bytes, hipStream_t stream);
+                     void *ws, size_t ws_bytes, const wkv7_side *side, hipStream_t stream);
 
 
 /* ------------------------------------------------------ decode stack -- */
@@ -255,22 +286,20 @@ size_t rwkv7_decode_workspace_bytes(const rwkv7_config *cfg, int B);
  * CM(h2); fm_cm_fwd; fm_forward: x0 = emb[token], ln_out, logits = h head)
  * and the streaming state of "infotheory .../rwkv7/model.rs" (LayerState:
  * att_x_prev, att_state, ffn_x_prev; layer-0 pre-norm; LayerNorm eps 1e-5).
- * tokens: [B] int32 in [0, V) (ids outside are clamped); state tensors are
- * read and updated in place: att_x_prev, ffn_x_prev [n_layer][B][C] (the
- * previous token's LN1 / LN2 outputs), att_state [n_layer][B][H][N][N] fp32.
- * logits: [B][V] fp32 (written).
- * From B = 512 on, the streams are advanced as two groups at once: the first
- * on `stream`, the second on a stream the library creates once per device
- * (default priority), forked from `stream` and joined back to it with events,
- * so everything is still ordered on `stream` and a capture of `stream`
- * records both.  The side stream is created by the first such call made
- * outside a capture; without it the groups run one after the other on
- * `stream`.  Calls enqueuing the split step are serialized by a lock.
+ * tokens: [B] int32; an id outside [0, V) embeds as a zero row.  State
+ * tensors are read and updated in place: att_x_prev, ffn_x_prev
+ * [n_layer][B][C] (the previous token's LN1 / LN2 outputs), att_state
+ * [n_layer][B][H][N][N] fp32.  logits: [B][V] fp32 (written).
+ * side: NULL, or a wkv7_side; with one, from B = 512 on the streams are
+ * advanced as two groups at once, the first on `stream` and the second on
+ * the side stream (every kernel of the step is either bound by HBM over the
+ * whole batch or a small latency-bound GEMM or row kernel, so the two chains
+ * overlap).  Without one the groups run one after the other on `stream`.
  */
 int rwkv7_decode_step(const rwkv7_config *cfg, const rwkv7_model *model, int B,
                       const int *tokens, float *att_x_prev, float *att_state,
                       float *ffn_x_prev, float *logits, void *ws, size_t ws_bytes,
-                      hipStream_t stream);
+                      const wkv7_side *side, hipStream_t stream);
 
 /* --------------------------------------------------- training step -- */
 
@@ -291,26 +320,31 @@ size_t rwkv7_train_workspace_bytes(const rwkv7_config *cfg, int B, int T);
 
 /*
  * One training step of next-token cross-entropy over B sequences of T tokens
- * (zero initial state): loss = mean over tokens of log-sum-exp(logits) -
- * logit[target]; every parameter gradient written.  Pages: whole-model
- * forward/backward of "Foundry/cuda_kernels/fullmodel.cu" (fm_forward,
- * fm_backward: embedding gather / scatter-add, blocks recomputed from their
- * cached inputs in reverse, fused log-softmax CE fm_k_ce_bwd with
- * dlogits = (softmax - onehot) / n, head not tied; layer 0 receives the
- * v_first gradient of the later layers).  Differs from the page: every sum
- * over tokens (parameter and embedding gradients, the loss) is done in a
- * fixed order, so the step is bitwise reproducible.  GEMMs run in fp32 on
- * the matrix cores; WKV7 state and accumulation are fp32.  The weight
- * gradients of the head, the channel-mixes and the time-mixes run on the
- * library side stream as in timemix_backward, joined back to `stream` within
- * every block.
- * tokens, targets: [B][T] int32 device (ids outside [0, V) are clamped);
- * loss: one fp32 device value (written).
+ * (zero initial state): loss = mean over the counted tokens of
+ * log-sum-exp(logits) - logit[target]; every parameter gradient written.
+ * Pages: whole-model forward/backward of "Foundry/cuda_kernels/fullmodel.cu"
+ * (fm_forward, fm_backward: embedding gather / scatter-add, blocks walked in
+ * reverse, fused log-softmax CE fm_k_ce_bwd with a double-precision
+ * normaliser and dlogits = (softmax - onehot) / n_valid, rows of ignored
+ * targets zero, head not tied; layer 0 receives the v_first gradient of the
+ * later layers).  Differs from the page: every sum over tokens (parameter and
+ * embedding gradients, the loss) is done in a fixed order, so the step is
+ * bitwise reproducible.  The GEMMs run on the matrix cores in the precision
+ * cfg->gemm_dtype names (fp32, or bf16 operands with fp32 accumulation); the
+ * WKV7 state, its accumulation and every elementwise step are fp32.
+ * tokens, targets: [B][T] int32 device.  A token id outside [0, V) embeds as
+ * a zero row (and receives no embedding gradient); a target outside [0, V)
+ * is ignored, like the page's ignore_index: its row of dlogits is zero, it
+ * adds nothing to the loss and is not counted in n_valid (loss 0 when no
+ * target is valid).  loss: one fp32 device value (written).
+ * side: NULL, or a wkv7_side on which the weight gradients of the head, the
+ * channel-mixes and the time-mixes run (as in timemix_backward), joined back
+ * to `stream` within every block.
  */
 int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
                      rwkv7_model_grads *grads, int B, int T, const int *tokens,
                      const int *targets, float *loss, void *ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     const wkv7_side *side, hipStream_t stream);
 
 /* ------------------------------------------------------------- helpers -- */
 
@@ -332,7 +366,8 @@ int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float *A, i
  * Same contraction, layouts, requirements and errors as wkv7_gemm_f32, with
  * the operands rounded to bf16 (round to nearest even) as they are staged and
  * the products accumulated in fp32 on the bf16 matrix cores
- * (v_mfma_f32_16x16x32_bf16).  A, B and C stay fp32 in memory.  This is the
+ * (v_mfma_f32_32x32x16_bf16 for whole 256-row tiles, v_mfma_f32_16x16x32_bf16
+ * otherwise).  A, B and C stay fp32 in memory.  C must not overlap A or B.  This is the
  * bf16-GEMM precision the full training-step configuration names for the
  * projections; the pages' own GEMMs are fp32 SGEMM.
  */

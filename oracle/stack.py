@@ -46,6 +46,15 @@ def channel_mix(mu_k, Wk, Wv, x, x_prev=None, gemm="f64"):
     return mm(ka, Wv, gemm)
 
 
+def embed(emb, tokens):
+    """Rows emb[id] for each id; an id outside [0, V) gives a zero row (the
+    reading of an id the table does not hold)."""
+    tokens = np.asarray(tokens)
+    V = emb.shape[0]
+    ok = (tokens >= 0) & (tokens < V)
+    return np.where(ok[..., None], emb[np.where(ok, tokens, 0)], 0.0)
+
+
 def _f64(m):
     out = {}
     for k, v in m.items():
@@ -77,7 +86,7 @@ def forward(model, cfg, tokens, state=None):
     B, T = tokens.shape
     H = cfg["H"]
     st = init_state(cfg, B) if state is None else {k: np.array(v, np.float64) for k, v in state.items()}
-    x = m["emb"][tokens]
+    x = embed(m["emb"], tokens)
     if m.get("ln0_w") is not None:
         x = layernorm(x, m["ln0_w"], m["ln0_b"])
     v_first = None
@@ -146,16 +155,25 @@ def channel_mix_backward(mu_k, Wk, Wv, x, dout, x_prev=None, gemm="f64"):
 
 
 def cross_entropy(logits, targets):
-    """Mean token CE and dlogits = (softmax - onehot) / n_tokens."""
+    """Mean CE over the counted tokens and dlogits = (softmax - onehot) / n_valid.
+
+    As the fullmodel page's fm_k_ce_bwd does for its ignore_index, a target
+    outside [0, V) is ignored: its dlogits row is zero, it adds nothing to the
+    loss and is not counted in n_valid (loss 0 when nothing is counted)."""
     z = np.asarray(logits, np.float64)
+    targets = np.asarray(targets)
+    V = z.shape[-1]
+    ok = (targets >= 0) & (targets < V)
+    n = int(ok.sum())
     m = z.max(axis=-1, keepdims=True)
     lse = m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True))
-    n = targets.size
-    ti = np.asarray(targets)[..., None]
-    loss = float(np.sum(lse[..., 0] - np.take_along_axis(z, ti, axis=-1)[..., 0]) / n)
+    ti = np.where(ok, targets, 0)[..., None]
+    per = lse[..., 0] - np.take_along_axis(z, ti, axis=-1)[..., 0]
+    loss = float(np.sum(np.where(ok, per, 0.0)) / n) if n else 0.0
     p = np.exp(z - lse)
     np.put_along_axis(p, ti, np.take_along_axis(p, ti, axis=-1) - 1.0, axis=-1)
-    return loss, p / n
+    p = np.where(ok[..., None], p, 0.0)
+    return loss, (p / n if n else p)
 
 
 def train_step(model, cfg, tokens, targets, gemm="f64"):
@@ -170,7 +188,7 @@ def train_step(model, cfg, tokens, targets, gemm="f64"):
     tokens = np.asarray(tokens)
     B, T = tokens.shape
     H = cfg["H"]
-    x = m["emb"][tokens]
+    x = embed(m["emb"], tokens)
     use_ln0 = m.get("ln0_w") is not None
     x_emb = x
     if use_ln0:
@@ -212,6 +230,8 @@ def train_step(model, cfg, tokens, targets, gemm="f64"):
     if use_ln0:
         dx, G["ln0_w"], G["ln0_b"] = layernorm_backward(x_emb, m["ln0_w"], dx)
     demb = np.zeros_like(m["emb"])
-    np.add.at(demb, tokens.reshape(-1), dx.reshape(-1, dx.shape[-1]))
+    ids = tokens.reshape(-1)
+    ok = (ids >= 0) & (ids < demb.shape[0])
+    np.add.at(demb, ids[ok], dx.reshape(-1, dx.shape[-1])[ok])
     G["emb"] = demb
     return loss, G

@@ -8,6 +8,7 @@ been built this module raises instead of falling back to anything else.
 """
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -59,6 +60,10 @@ class Rwkv7ModelGrads(ctypes.Structure):
                                                "head")] + [("blocks", ctypes.POINTER(Rwkv7BlockGrads))]
 
 
+class Wkv7Side(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("ev", ctypes.c_void_p * 4)]
+
+
 class Wkv7Error(RuntimeError):
     pass
 
@@ -84,7 +89,7 @@ def lib():
         L.wkv7_forward.restype = _i
         L.wkv7_backward_workspace_bytes.argtypes = [_i] * 5
         L.wkv7_backward_workspace_bytes.restype = _sz
-        L.wkv7_backward.argtypes = [_i] * 5 + [_vp] * 17 + [_vp, _sz, _vp]
+        L.wkv7_backward.argtypes = [_i] * 5 + [_vp] * 17 + [_vp, _sz, _vp, _vp]
         L.wkv7_backward.restype = _i
         L.wkv7_step.argtypes = [_i] * 4 + [_vp] * 9
         L.wkv7_step.restype = _i
@@ -96,7 +101,7 @@ def lib():
         L.timemix_forward.argtypes = [sp, ctypes.POINTER(TmWeights), _i, _i] + [_vp] * 9 + [_sz, _vp]
         L.timemix_forward.restype = _i
         L.timemix_backward.argtypes = ([sp, ctypes.POINTER(TmWeights), _i, _i] + [_vp] * 6 +
-                                       [_vp, ctypes.POINTER(TmGrads)] + [_vp] * 6 + [_sz, _vp])
+                                       [_vp, ctypes.POINTER(TmGrads)] + [_vp] * 6 + [_sz, _vp, _vp])
         L.timemix_backward.restype = _i
         L.wkv7_gemm_f32.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp]
         L.wkv7_gemm_f32.restype = _i
@@ -105,13 +110,17 @@ def lib():
         cp = ctypes.POINTER(Rwkv7Config)
         L.rwkv7_decode_workspace_bytes.argtypes = [cp, _i]
         L.rwkv7_decode_workspace_bytes.restype = _sz
-        L.rwkv7_decode_step.argtypes = [cp, ctypes.POINTER(Rwkv7Model), _i] + [_vp] * 6 + [_sz, _vp]
+        L.rwkv7_decode_step.argtypes = [cp, ctypes.POINTER(Rwkv7Model), _i] + [_vp] * 6 + [_sz, _vp, _vp]
         L.rwkv7_decode_step.restype = _i
         L.rwkv7_train_workspace_bytes.argtypes = [cp, _i, _i]
         L.rwkv7_train_workspace_bytes.restype = _sz
         L.rwkv7_train_step.argtypes = ([cp, ctypes.POINTER(Rwkv7Model), ctypes.POINTER(Rwkv7ModelGrads),
-                                        _i, _i] + [_vp] * 4 + [_sz, _vp])
+                                        _i, _i] + [_vp] * 4 + [_sz, _vp, _vp])
         L.rwkv7_train_step.restype = _i
+        L.wkv7_side_create.argtypes = [ctypes.POINTER(Wkv7Side)]
+        L.wkv7_side_create.restype = _i
+        L.wkv7_side_destroy.argtypes = [ctypes.POINTER(Wkv7Side)]
+        L.wkv7_side_destroy.restype = _i
         _lib = L
     return _lib
 
@@ -123,6 +132,46 @@ def _check(rc):
 
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# One side stream (wkv7_side) per device, created by the first call that
+# wants it outside a graph capture and owned by this module; the lock keeps
+# two threads from using its events at once.
+_sides = {}
+_side_lock = threading.Lock()
+
+
+class _SideUse:
+    """Context manager giving the side pointer for the current device (or
+    None when side=False) and holding the lock while the call enqueues."""
+
+    def __init__(self, use):
+        self.use = use
+
+    def __enter__(self):
+        if not self.use:
+            return None
+        _side_lock.acquire()
+        dev = torch.cuda.current_device()
+        sd = _sides.get(dev)
+        if sd is None and torch.cuda.is_current_stream_capturing():
+            # no stream is created inside a capture: this call runs on one stream
+            _side_lock.release()
+            self.use = False
+            return None
+        if sd is None:
+            sd = Wkv7Side()
+            rc = lib().wkv7_side_create(ctypes.byref(sd))
+            if rc != 0:
+                _side_lock.release()
+                _check(rc)
+            _sides[dev] = sd
+        return ctypes.byref(sd)
+
+    def __exit__(self, *exc):
+        if self.use:
+            _side_lock.release()
+        return False
 
 
 def _p(t):
@@ -194,8 +243,10 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, y=None, sT=None, ckpt=None,
     return y, sT, ckpt
 
 
-def wkv7_backward(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, want_ds0=True):
-    """Gradients of <dy, y> + <dsT, S_T>.  Returns dict dr, dw, dk, dv, da, db, ds0."""
+def wkv7_backward(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, want_ds0=True, side=True):
+    """Gradients of <dy, y> + <dsT, S_T>.  Returns dict dr, dw, dk, dv, da, db, ds0.
+
+    side: overlap the long-sequence reductions on this module's side stream."""
     B, T, H, N = r.shape
     dt = r.dtype
     for n, t in zip(("r", "w", "k", "v", "a", "b", "dy"), (r, w, k, v, a, b, dy)):
@@ -207,10 +258,11 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, want_ds0=T
     out["ds0"] = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_ds0 else None
     nbytes = lib().wkv7_backward_workspace_bytes(B, T, H, N, int(ckpt is not None))
     ws = torch.empty(max(nbytes, 1), device=r.device, dtype=torch.uint8)
-    _check(lib().wkv7_backward(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
-                               _p(s0), _p(ckpt), _p(dy), _p(dsT), _p(out["dr"]), _p(out["dw"]),
-                               _p(out["dk"]), _p(out["dv"]), _p(out["da"]), _p(out["db"]),
-                               _p(out["ds0"]), _p(ws), nbytes, _stream()))
+    with _SideUse(side) as sd:
+        _check(lib().wkv7_backward(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a), _p(b),
+                                   _p(s0), _p(ckpt), _p(dy), _p(dsT), _p(out["dr"]), _p(out["dw"]),
+                                   _p(out["dk"]), _p(out["dv"]), _p(out["da"]), _p(out["db"]),
+                                   _p(out["ds0"]), _p(ws), nbytes, sd, _stream()))
     return out
 
 
@@ -283,7 +335,8 @@ def timemix_forward(s, W, x, x_prev=None, v_first=None, s0=None, want_state=True
 
 
 def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None, cache=None,
-                     dv_first_in=None, want_dx_prev=True, want_ds0=True, want_dv_first=True):
+                     dv_first_in=None, want_dx_prev=True, want_ds0=True, want_dv_first=True,
+                     side=True):
     """Returns dict grads (per weight), dx, dx_prev, dv_first_out, ds0."""
     B, T, C = x.shape
     H, N = s.H, s.N
@@ -314,11 +367,12 @@ def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None
     ds0 = torch.empty((B, H, N, N), device=x.device, dtype=torch.float32) if want_ds0 else None
     nbytes = lib().timemix_backward_workspace_bytes(ctypes.byref(s), B, T)
     ws = torch.empty(nbytes, device=x.device, dtype=torch.uint8)
-    _check(lib().timemix_backward(ctypes.byref(s), ctypes.byref(cw), B, T, _p(x), _p(x_prev),
-                                  _p(v_first), _p(s0), _p(dout), _p(dsT), _p(cache),
-                                  ctypes.byref(cg), _p(dx), _p(dx_prev),
-                                  _p(dv_first_in if s.layer_id == 0 else None), _p(dvf_out),
-                                  _p(ds0), _p(ws), nbytes, _stream()))
+    with _SideUse(side) as sd:
+        _check(lib().timemix_backward(ctypes.byref(s), ctypes.byref(cw), B, T, _p(x), _p(x_prev),
+                                      _p(v_first), _p(s0), _p(dout), _p(dsT), _p(cache),
+                                      ctypes.byref(cg), _p(dx), _p(dx_prev),
+                                      _p(dv_first_in if s.layer_id == 0 else None), _p(dvf_out),
+                                      _p(ds0), _p(ws), nbytes, sd, _stream()))
     return dict(grads=grads, dx=dx, dx_prev=dx_prev, dv_first_out=dvf_out, ds0=ds0)
 
 
@@ -397,7 +451,7 @@ def rwkv7_decode_workspace_bytes(dm, B):
     return lib().rwkv7_decode_workspace_bytes(ctypes.byref(dm.cfg), B)
 
 
-def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None):
+def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None, side=True):
     """One token per stream: tokens [B] int32 (device); state dict updated in place."""
     c = dm.cfg
     B = tokens.shape[0]
@@ -411,10 +465,11 @@ def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None):
     nbytes = rwkv7_decode_workspace_bytes(dm, B)
     if ws is None:
         ws = torch.empty(nbytes, device=tokens.device, dtype=torch.uint8)
-    _check(lib().rwkv7_decode_step(ctypes.byref(c), ctypes.byref(dm.model), B, _p(tokens),
-                                   _p(state["att_x_prev"]), _p(state["att_state"]),
-                                   _p(state["ffn_x_prev"]), _p(logits), _p(ws), ws.numel(),
-                                   _stream()))
+    with _SideUse(side) as sd:
+        _check(lib().rwkv7_decode_step(ctypes.byref(c), ctypes.byref(dm.model), B, _p(tokens),
+                                       _p(state["att_x_prev"]), _p(state["att_state"]),
+                                       _p(state["ffn_x_prev"]), _p(logits), _p(ws), ws.numel(),
+                                       sd, _stream()))
     return logits
 
 
@@ -459,7 +514,7 @@ def rwkv7_train_workspace_bytes(dm, B, T):
     return lib().rwkv7_train_workspace_bytes(ctypes.byref(dm.cfg), B, T)
 
 
-def rwkv7_train_step(dm, grads, tokens, targets, loss=None, ws=None):
+def rwkv7_train_step(dm, grads, tokens, targets, loss=None, ws=None, side=True):
     """Loss (device scalar tensor) of one step; grads (TrainGrads) are written."""
     B, T = tokens.shape
     _need(tokens, (B, T), torch.int32, "tokens")
@@ -469,7 +524,8 @@ def rwkv7_train_step(dm, grads, tokens, targets, loss=None, ws=None):
     nbytes = rwkv7_train_workspace_bytes(dm, B, T)
     if ws is None:
         ws = torch.empty(nbytes, device=tokens.device, dtype=torch.uint8)
-    _check(lib().rwkv7_train_step(ctypes.byref(dm.cfg), ctypes.byref(dm.model),
-                                  ctypes.byref(grads.struct), B, T, _p(tokens), _p(targets),
-                                  _p(loss), _p(ws), ws.numel(), _stream()))
+    with _SideUse(side) as sd:
+        _check(lib().rwkv7_train_step(ctypes.byref(dm.cfg), ctypes.byref(dm.model),
+                                      ctypes.byref(grads.struct), B, T, _p(tokens), _p(targets),
+                                      _p(loss), _p(ws), ws.numel(), sd, _stream()))
     return loss

@@ -9,7 +9,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 #include <vector>
 
 #include "../../include/wkv7.h"
@@ -60,6 +59,11 @@ int check_wkv_shape(int B, int T, int H, int N, int dtype) {
   return WKV7_OK;
 }
 
+size_t tok_bytes(int B, int T, int H, int dtype) {
+  return (size_t)B * T * H * WKV7_N * (dtype == WKV7_BF16 ? 2 : 4);
+}
+size_t state_bytes(int B, int H) { return (size_t)B * H * WKV7_N * WKV7_N * sizeof(float); }
+
 size_t ckpt_floats(int B, int T, int H) {
   const int L = wkv7_ckpt_interval_const();
   return (size_t)B * H * ((T + L - 1) / L) * WKV7_N * WKV7_N;
@@ -84,57 +88,82 @@ struct Carver {
     if (rc_ != WKV7_OK) return rc_; \
   } while (0)
 
+// Byte ranges a call reads and writes.  check() fails with WKV7_EINVAL when a
+// written range overlaps any other range (read or written); ranges that are
+// only read may overlap.  NULL pointers and empty ranges are skipped.
+// Permitted in-place updates (s0 == sT, the decode state) are entered once,
+// as written.
+struct Spans {
+  struct S {
+    uintptr_t lo, hi;
+    bool w;
+    const char* name;
+  };
+  std::vector<S> v;
+  void rd(const void* p, size_t bytes, const char* n) {
+    if (p && bytes) v.push_back({(uintptr_t)p, (uintptr_t)p + bytes, false, n});
+  }
+  void wr(const void* p, size_t bytes, const char* n) {
+    if (p && bytes) v.push_back({(uintptr_t)p, (uintptr_t)p + bytes, true, n});
+  }
+  int check() {
+    std::sort(v.begin(), v.end(), [](const S& a, const S& b) { return a.lo < b.lo; });
+    // sweep in address order: the furthest end of every range so far and of
+    // every written range so far
+    uintptr_t end_any = 0, end_w = 0;
+    const char *n_any = "", *n_w = "";
+    for (const S& x : v) {
+      if (x.lo < end_w) return fail(WKV7_EINVAL, "%s overlaps %s (written)", x.name, n_w);
+      if (x.w && x.lo < end_any) return fail(WKV7_EINVAL, "%s (written) overlaps %s", x.name, n_any);
+      if (x.hi > end_any) { end_any = x.hi; n_any = x.name; }
+      if (x.w && x.hi > end_w) { end_w = x.hi; n_w = x.name; }
+    }
+    return WKV7_OK;
+  }
+};
+
+// Optional caller-owned side stream: ev[0] fork, ev[1] and ev[2]
+// intermediate fork points, ev[3] join.  nullptr when none (or when it is the
+// caller's stream itself): everything then runs on the caller's stream.
+int check_side(const wkv7_side* side, hipStream_t st, const wkv7_side*& use) {
+  use = nullptr;
+  if (!side) return WKV7_OK;
+  if (!side->stream) return fail(WKV7_EINVAL, "side->stream is NULL");
+  for (int i = 0; i < 4; i++)
+    if (!side->ev[i]) return fail(WKV7_EINVAL, "side->ev[%d] is NULL", i);
+  if (side->stream != st) use = side;
+  return WKV7_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ WKV7 --
-namespace {
-// Library side stream per device (default priority), forked from the
-// caller's stream and joined back with events, so work on it stays ordered
-// with the caller's stream and is recorded into a graph when the caller
-// captures.  Created by the first call that wants it outside a capture;
-// without it everything runs on the caller's stream.  g_fj_mu is held while
-// a call enqueues work that uses the shared events.
-constexpr int SIDE_STREAMS = 1;
-struct ForkJoin {
-  hipStream_t side[SIDE_STREAMS] = {};
-  hipEvent_t fork = nullptr, join[SIDE_STREAMS] = {};
-  hipEvent_t mark[2] = {};  // intermediate fork points
-  bool ready = false, failed = false;
-};
-constexpr int MAX_DEVICES = 64;
-std::mutex g_fj_mu;
-ForkJoin g_fj[MAX_DEVICES];
-
-// Locks g_fj_mu on success (the caller unlocks once its work is enqueued);
-// nullptr (nothing locked) when no side stream can be had.
-ForkJoin* fork_join_acquire(hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
-  g_fj_mu.lock();
-  ForkJoin& f = g_fj[dev];
-  if (!f.ready && !f.failed) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-      g_fj_mu.unlock();  // never create resources inside a capture
-      return nullptr;
-    }
-    f.failed = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&f.mark[0], hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&f.mark[1], hipEventDisableTiming) != hipSuccess;
-    for (int i = 0; i < SIDE_STREAMS && !f.failed; i++)
-      f.failed = hipStreamCreateWithFlags(&f.side[i], hipStreamNonBlocking) != hipSuccess ||
-                 hipEventCreateWithFlags(&f.join[i], hipEventDisableTiming) != hipSuccess;
-    f.ready = !f.failed;
-  }
-  if (!f.ready) {
-    g_fj_mu.unlock();
-    return nullptr;
-  }
-  return &f;
-}
-}  // namespace
-
 extern "C" const char* wkv7_last_error(void) { return g_err; }
+
+extern "C" int wkv7_side_create(wkv7_side* side) {
+  g_err[0] = 0;
+  if (!side) return fail(WKV7_EINVAL, "side is NULL");
+  memset(side, 0, sizeof(*side));
+  hipError_t e = hipStreamCreateWithFlags(&side->stream, hipStreamNonBlocking);
+  for (int i = 0; i < 4 && e == hipSuccess; i++)
+    e = hipEventCreateWithFlags(&side->ev[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)wkv7_side_destroy(side);
+    return hip_fail(e, "wkv7_side_create");
+  }
+  return WKV7_OK;
+}
+
+extern "C" int wkv7_side_destroy(wkv7_side* side) {
+  g_err[0] = 0;
+  if (!side) return WKV7_OK;
+  hipError_t e = hipSuccess, x;
+  for (int i = 0; i < 4; i++)
+    if (side->ev[i] && (x = hipEventDestroy(side->ev[i])) != hipSuccess && e == hipSuccess) e = x;
+  if (side->stream && (x = hipStreamDestroy(side->stream)) != hipSuccess && e == hipSuccess) e = x;
+  memset(side, 0, sizeof(*side));
+  return e == hipSuccess ? WKV7_OK : hip_fail(e, "wkv7_side_destroy");
+}
 
 extern "C" int wkv7_checkpoint_interval(void) { return wkv7_ckpt_interval_const(); }
 
@@ -172,6 +201,18 @@ extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r
     CHK(check_f32_ptr(ws, "ws", true));
     if (need) cws = static_cast<float*>(ws);
   }
+  {
+    const size_t tb = tok_bytes(B, T, H, dtype), sb = state_bytes(B, H);
+    Spans sp;
+    sp.rd(r, tb, "r"); sp.rd(w, tb, "w"); sp.rd(k, tb, "k");
+    sp.rd(v, tb, "v"); sp.rd(a, tb, "a"); sp.rd(b, tb, "b");
+    if (s0 != sT) sp.rd(s0, sb, "s0");  // s0 == sT: the state is updated in place
+    sp.wr(y, tb, "y");
+    sp.wr(sT, sb, "sT");
+    sp.wr(ckpt, ckpt_floats(B, T, H) * sizeof(float), "ckpt");
+    if (cws) sp.wr(cws, wkv7_forward_workspace_bytes(B, T, H, N), "ws");
+    CHK(sp.check());
+  }
   HIPCHK(wkv7_launch_forward(dtype, B, T, H, r, w, k, v, a, b, s0, y, sT, ckpt, cws, stream),
          "wkv7_forward launch");
   return WKV7_OK;
@@ -186,11 +227,19 @@ extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int 
   return c.off;
 }
 
+namespace {
+int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void* w, const void* k,
+                      const void* v, const void* a, const void* b, const float* s0,
+                      const float* ckpt, const void* dy, const float* dsT, void* dr, void* dw,
+                      void* dk, void* dv, void* da, void* db, float* ds0, void* ws,
+                      const wkv7_side* sd, hipStream_t stream);
+}  // namespace
+
 extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* r, const void* w,
                              const void* k, const void* v, const void* a, const void* b,
                              const float* s0, const float* ckpt, const void* dy, const float* dsT,
                              void* dr, void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             void* ws, size_t ws_bytes, const wkv7_side* side, hipStream_t stream) {
   g_err[0] = 0;
   CHK(check_wkv_shape(B, T, H, N, dtype));
   const char* names[] = {"r", "w", "k", "v", "a", "b", "dy", "dr", "dw", "dk", "dv", "da", "db"};
@@ -204,6 +253,32 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
+  const wkv7_side* sd = nullptr;
+  CHK(check_side(side, stream, sd));
+  {
+    const size_t tb = tok_bytes(B, T, H, dtype), sb = state_bytes(B, H);
+    Spans sp;
+    for (int i = 0; i < 7; i++) sp.rd(ptrs[i], tb, names[i]);
+    for (int i = 7; i < 13; i++) sp.wr(ptrs[i], tb, names[i]);
+    sp.rd(s0, sb, "s0");
+    sp.rd(dsT, sb, "dsT");
+    sp.rd(ckpt, ckpt_floats(B, T, H) * sizeof(float), "ckpt");
+    sp.wr(ds0, sb, "ds0");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
+  return wkv7_backward_run(B, T, H, dtype, r, w, k, v, a, b, s0, ckpt, dy, dsT, dr, dw, dk, dv, da,
+                           db, ds0, ws, sd, stream);
+}
+
+namespace {
+// The backward's launches, arguments already validated; ws holds
+// wkv7_backward_workspace_bytes(.., ckpt != NULL).
+int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void* w, const void* k,
+                      const void* v, const void* a, const void* b, const float* s0,
+                      const float* ckpt, const void* dy, const float* dsT, void* dr, void* dw,
+                      void* dk, void* dv, void* da, void* db, float* ds0, void* ws,
+                      const wkv7_side* sd, hipStream_t stream) {
   Carver cv(ws);
   float* part = cv.take(wkv7_bwd_partial_floats(B, T, H));
   float* gbuf = cv.take((size_t)2 * B * H * WKV7_N * WKV7_N);
@@ -215,25 +290,22 @@ extern "C" int wkv7_backward(int B, int T, int H, int N, int dtype, const void* 
            "wkv7_backward checkpoint recompute");
     ck = tmp;
   }
-  if (wkv7_bwd_segments(T) > 1) {
+  if (sd && wkv7_bwd_segments(T) > 1) {
     // long sequence: the reverse pass runs in segments, each segment's
-    // partial reduction on the library side stream overlapping the next
-    // segment's pass; without a side stream, one pass
-    ForkJoin* fj = fork_join_acquire(stream);
-    if (fj) {
-      std::lock_guard<std::mutex> hold(g_fj_mu, std::adopt_lock);
-      HIPCHK(wkv7_launch_backward_segmented(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk,
-                                            dv, da, db, ds0, part, gbuf, stream, fj->side[0],
-                                            fj->mark[0], fj->join[0]),
-             "wkv7_backward launch");
-      return WKV7_OK;
-    }
+    // partial reduction on the side stream overlapping the next segment's
+    // pass; without a side stream, one pass
+    HIPCHK(wkv7_launch_backward_segmented(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk,
+                                          dv, da, db, ds0, part, gbuf, stream, sd->stream,
+                                          sd->ev[1], sd->ev[3]),
+           "wkv7_backward launch");
+    return WKV7_OK;
   }
   HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
                               db, ds0, part, stream),
          "wkv7_backward launch");
   return WKV7_OK;
 }
+}  // namespace
 
 extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const void* w,
                          const void* k, const void* v, const void* a, const void* b, float* state,
@@ -244,6 +316,14 @@ extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const vo
   const void* ptrs[] = {r, w, k, v, a, b, y};
   for (int i = 0; i < 7; i++) CHK(check_tok_ptr(ptrs[i], names[i], dtype, true));
   CHK(check_f32_ptr(state, "state", true));
+  {
+    const size_t tb = tok_bytes(B, 1, H, dtype);
+    Spans sp;
+    for (int i = 0; i < 6; i++) sp.rd(ptrs[i], tb, names[i]);
+    sp.wr(y, tb, "y");
+    sp.wr(state, state_bytes(B, H), "state");  // read and written in place
+    CHK(sp.check());
+  }
   HIPCHK(wkv7_launch_step(dtype, B, H, r, w, k, v, a, b, state, y, stream), "wkv7_step launch");
   return WKV7_OK;
 }
@@ -361,6 +441,27 @@ int check_weights(const tm_shape* s, const tm_weights* W) {
   return WKV7_OK;
 }
 
+// Byte ranges of a time-mix block's weights (or gradients, same shapes).
+template <typename WT>
+void tm_weight_spans(Spans& sp, const tm_shape* s, const WT* W, bool written) {
+  const size_t C = s->C, f = sizeof(float);
+  auto add = [&](const void* p, size_t n, const char* nm) {
+    if (written) sp.wr(p, n * f, nm); else sp.rd(p, n * f, nm);
+  };
+  const void* vec[] = {W->mu_r, W->mu_w, W->mu_k, W->mu_v, W->mu_a, W->mu_g, W->w0, W->a0,
+                       W->k_k, W->k_a, W->r_k, W->ln_w, W->ln_b};
+  const char* vn[] = {"mu_r", "mu_w", "mu_k", "mu_v", "mu_a", "mu_g", "w0", "a0", "k_k", "k_a",
+                      "r_k", "ln_w", "ln_b"};
+  for (int i = 0; i < 13; i++) add(vec[i], C, vn[i]);
+  add(W->Wr, C * C, "Wr"); add(W->Wk, C * C, "Wk"); add(W->Wv, C * C, "Wv"); add(W->Wo, C * C, "Wo");
+  add(W->W1, C * s->Dw, "W1"); add(W->W2, C * s->Dw, "W2");
+  add(W->A1, C * s->Da, "A1"); add(W->A2, C * s->Da, "A2");
+  add(W->G1, C * s->Dg, "G1"); add(W->G2, C * s->Dg, "G2");
+  if (s->layer_id > 0) {
+    add(W->v0, C, "v0"); add(W->V1, C * s->Dv, "V1"); add(W->V2, C * s->Dv, "V2");
+  }
+}
+
 // decode: T == 1 with the WKV state updated in place (s0 == sT, no checkpoint),
 // run by the bandwidth-bound step kernel.  out = out_beta * out + tg Wo.
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
@@ -440,8 +541,7 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                      const float* x_prev, const float* v_first, const float* s0, const float* dout,
                      const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
                      float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
-                     float* ds0, hipStream_t st, int prec = GEMM_F32, bool caller_forks = false,
-                     ForkJoin* caller_fj = nullptr) {
+                     float* ds0, hipStream_t st, int prec, const wkv7_side* sd) {
   const int BT = B * T, C = s->C, L = s->layer_id;
 
   // The weight gradients (X^T dY products, split along the tokens) feed
@@ -452,26 +552,22 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   // input gradients), only they use the split-K scratch, and this stream
   // joins the side stream before returning, so the next call may reuse
   // every buffer.
-  // caller_forks: the caller holds g_fj_mu and passes its side stream
-  // resources (or nullptr: none)
-  ForkJoin* fj = caller_forks ? caller_fj : fork_join_acquire(st);
-  std::unique_lock<std::mutex> hold;
-  if (fj && !caller_forks) hold = std::unique_lock<std::mutex>(g_fj_mu, std::adopt_lock);
-  hipStream_t ss = fj ? fj->side[0] : st;
-  auto fork_at = [&](hipEvent_t e) -> hipError_t {
-    if (!fj) return hipSuccess;
-    hipError_t r = hipEventRecord(e, st);
-    return r != hipSuccess ? r : hipStreamWaitEvent(ss, e, 0);
+  // sd: the caller's side stream (nullptr: none, everything on st)
+  hipStream_t ss = sd ? sd->stream : st;
+  auto fork_at = [&](int ev) -> hipError_t {
+    if (!sd) return hipSuccess;
+    hipError_t r = hipEventRecord(sd->ev[ev], st);
+    return r != hipSuccess ? r : hipStreamWaitEvent(ss, sd->ev[ev], 0);
   };
   struct Join {  // joins the side stream on every return path
-    ForkJoin* fj;
-    hipStream_t st, ss;
+    const wkv7_side* sd;
+    hipStream_t st;
     ~Join() {
-      if (fj && hipEventRecord(fj->join[0], ss) == hipSuccess) (void)hipStreamWaitEvent(st, fj->join[0], 0);
+      if (sd && hipEventRecord(sd->ev[3], sd->stream) == hipSuccess) (void)hipStreamWaitEvent(st, sd->ev[3], 0);
     }
-  } join{fj, st, ss};
+  } join{sd, st};
 
-  HIPCHK(fork_at(fj ? fj->fork : nullptr), "backward fork");
+  HIPCHK(fork_at(0), "backward fork");
   // output projection
   HIPCHK(gemm_run(prec, false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
   HIPCHK(gemm_run(prec, true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, ss), "dWo");
@@ -496,11 +592,11 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
 
   HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
-  if (fj && wkv7_bwd_segments(T) > 1)  // segment reductions overlap on the side stream
+  if (sd && wkv7_bwd_segments(T) > 1)  // segment reductions overlap on the side stream
     HIPCHK(wkv7_launch_backward_segmented(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv,
                                           bb.dy_wkv, m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA,
-                                          bb.gB, ds0, bb.wkv_part, bb.wkv_g, st, ss, fj->mark[0],
-                                          fj->join[0]),
+                                          bb.gB, ds0, bb.wkv_part, bb.wkv_g, st, ss, sd->ev[1],
+                                          sd->ev[3]),
            "wkv7 backward");
   else
     HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
@@ -510,7 +606,7 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
   const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;
   float* sk = bb.splitk;
-  HIPCHK(fork_at(fj ? fj->mark[0] : nullptr), "backward fork");
+  HIPCHK(fork_at(1), "backward fork");
   // r, k, v weight gradients (dr from the post-WKV backward, dk and dv from
   // the pre-WKV backward)
   HIPCHK(gemm_run(prec, true, false, C, C, BT, m.xr, C, bb.dr, C, G->Wr, C, 0.f, 0, nullptr, splitk_for(C, C, BT), sk, ss), "dWr");
@@ -535,7 +631,7 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
     HIPCHK(gemm_run(prec, true, false, Dv, C, BT, m.lv, Dv, bb.dpre_v, C, G->V2, C, 0.f, 0, nullptr, splitk_for(Dv, C, BT), sk, ss), "dV2");
     HIPCHK(gemm_run(prec, false, true, BT, C, Dv, bb.d_lv, Dv, W->V1, Dv, bb.dxv, C, 0.f, 0, nullptr, 1, nullptr, st), "dxv lora");
   }
-  HIPCHK(fork_at(fj ? fj->mark[1] : nullptr), "backward fork");
+  HIPCHK(fork_at(2), "backward fork");
   HIPCHK(gemm_run(prec, true, false, C, Da, BT, m.xa, C, bb.d_la, Da, G->A1, Da, 0.f, 0, nullptr, splitk_for(C, Da, BT), sk, ss), "dA1");
   HIPCHK(gemm_run(prec, true, false, C, Dw, BT, m.xw, C, bb.d_lw, Dw, G->W1, Dw, 0.f, 0, nullptr, splitk_for(C, Dw, BT), sk, ss), "dW1");
   HIPCHK(gemm_run(prec, true, false, C, Dg, BT, m.xg, C, bb.d_lg, Dg, G->G1, Dg, 0.f, 0, nullptr, splitk_for(C, Dg, BT), sk, ss), "dG1");
@@ -603,6 +699,22 @@ extern "C" int timemix_forward(const tm_shape* s, const tm_weights* W, int B, in
     base = ws;
   }
   CHK(check_f32_ptr(base, cache ? "cache" : "ws", true));
+  {
+    const size_t tb = (size_t)B * T * s->C * sizeof(float), rb = (size_t)B * s->C * sizeof(float);
+    const size_t sb = state_bytes(B, s->H);
+    Spans sp;
+    tm_weight_spans(sp, s, W, false);
+    sp.rd(x, tb, "x");
+    // x_last may replace x_prev in place for one token (the same thread reads, then writes)
+    if (!(T == 1 && x_last == x_prev)) sp.rd(x_prev, rb, "x_prev");
+    if (s->layer_id == 0) sp.wr(v_first, tb, "v_first"); else sp.rd(v_first, tb, "v_first");
+    if (s0 != sT) sp.rd(s0, sb, "s0");
+    sp.wr(sT, sb, "sT");
+    sp.wr(out, tb, "out");
+    sp.wr(x_last, rb, "x_last");
+    sp.wr(base, timemix_cache_bytes(s, B, T), cache ? "cache" : "ws");
+    CHK(sp.check());
+  }
   Carver c(base);
   TmCache m;
   carve_cache(c, s, B, T, m);
@@ -614,7 +726,8 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
                                 const float* s0, const float* dout, const float* dsT,
                                 const void* cache, tm_grads* G, float* dx, float* dx_prev,
                                 const float* dv_first_in, float* dv_first_out, float* ds0,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+                                void* ws, size_t ws_bytes, const wkv7_side* side,
+                                hipStream_t stream) {
   g_err[0] = 0;
   CHK(check_tm_shape(s, B, T));
   CHK(check_weights(s, W));
@@ -644,6 +757,29 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
+  const wkv7_side* sd = nullptr;
+  CHK(check_side(side, stream, sd));
+  {
+    const size_t tb = (size_t)B * T * s->C * sizeof(float), rb = (size_t)B * s->C * sizeof(float);
+    const size_t sb = state_bytes(B, s->H);
+    Spans sp;
+    tm_weight_spans(sp, s, W, false);
+    tm_weight_spans(sp, s, G, true);
+    sp.rd(x, tb, "x");
+    sp.rd(x_prev, rb, "x_prev");
+    if (s->layer_id > 0) sp.rd(v_first, tb, "v_first");
+    sp.rd(s0, sb, "s0");
+    sp.rd(dout, tb, "dout");
+    sp.rd(dsT, sb, "dsT");
+    sp.rd(cache, cache ? timemix_cache_bytes(s, B, T) : 0, "cache");
+    if (s->layer_id == 0) sp.rd(dv_first_in, tb, "dv_first_in");
+    sp.wr(dx, tb, "dx");
+    sp.wr(dx_prev, rb, "dx_prev");
+    if (s->layer_id > 0) sp.wr(dv_first_out, tb, "dv_first_out");
+    sp.wr(ds0, sb, "ds0");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
 
   const int BT = B * T, C = s->C, L = s->layer_id;
   Carver cw(ws);
@@ -662,7 +798,7 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
     CHK(tm_forward_impl(s, W, B, T, x, x_prev, vf, s0, nullptr, out_tmp, nullptr, m, stream));
   }
   return tm_backward_impl(s, W, B, T, x, x_prev, v_first, s0, dout, dsT, m, bb, G, dx, dx_prev,
-                          dv_first_in, dv_first_out, false, ds0, stream);
+                          dv_first_in, dv_first_out, false, ds0, stream, GEMM_F32, sd);
 }
 
 // ----------------------------------------------------------------- GEMM --
@@ -678,6 +814,15 @@ int gemm_abi(int prec, int transA, int transB, int M, int N, int K, const float*
   if (a_inner % 4 || b_inner % 4 || lda % 4 || ldb % 4)
     return fail(WKV7_EINVAL, "contiguous GEMM dimensions and leading dims must be multiples of 4");
   if (lda < a_inner || ldb < b_inner || ldc < N) return fail(WKV7_EINVAL, "leading dimension too small");
+  {
+    const size_t f = sizeof(float);
+    const size_t a_rows = transA ? K : M, b_rows = transB ? N : K;
+    Spans sp;
+    sp.rd(A, ((a_rows - 1) * lda + a_inner) * f, "A");
+    sp.rd(B, ((b_rows - 1) * ldb + b_inner) * f, "B");
+    sp.wr(C, ((size_t)(M - 1) * ldc + N) * f, "C");
+    CHK(sp.check());
+  }
   HIPCHK(gemm_run(prec, transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr,
                   1, nullptr, stream),
          "gemm launch");
@@ -742,7 +887,7 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
 // 2048 streams: 1.82 ms per step in one group, 1.64 ms in two, 2.01 ms in
 // four (smaller groups make every GEMM and row kernel less efficient).
 constexpr int DECODE_SPLIT_MIN = 512;
-constexpr int DECODE_MAX_GROUPS = SIDE_STREAMS + 1;
+constexpr int DECODE_MAX_GROUPS = 2;  // the caller's stream and the side stream
 
 int decode_groups(int B, int nb[DECODE_MAX_GROUPS]) {
   const int g = B < DECODE_SPLIT_MIN ? 1 : std::min(DECODE_MAX_GROUPS, B / DECODE_SPLIT_MIN + (B % DECODE_SPLIT_MIN ? 1 : 0));
@@ -801,6 +946,33 @@ int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int
 
 }  // namespace
 
+namespace {
+// Byte ranges of a model's weights (or of its gradients, same shapes).
+template <typename MT>
+void model_spans(Spans& sp, const rwkv7_config* cfg, const MT* M, bool written) {
+  const size_t f = sizeof(float), C = cfg->C, F = cfg->F, V = cfg->V;
+  auto add = [&](const void* p, size_t n, const char* nm) {
+    if (written) sp.wr(p, n * f, nm); else sp.rd(p, n * f, nm);
+  };
+  add(M->emb, V * C, "emb");
+  add(M->head, C * V, "head");
+  add(M->ln_out_w, C, "ln_out_w");
+  add(M->ln_out_b, C, "ln_out_b");
+  if (cfg->use_ln0) {
+    add(M->ln0_w, C, "ln0_w");
+    add(M->ln0_b, C, "ln0_b");
+  }
+  for (int l = 0; l < cfg->n_layer; l++) {
+    const auto& bl = M->blocks[l];
+    add(bl.ln1_w, C, "ln1_w"); add(bl.ln1_b, C, "ln1_b");
+    add(bl.ln2_w, C, "ln2_w"); add(bl.ln2_b, C, "ln2_b");
+    add(bl.cm_mu_k, C, "cm_mu_k"); add(bl.cm_Wk, C * F, "cm_Wk"); add(bl.cm_Wv, F * C, "cm_Wv");
+    tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
+    tm_weight_spans(sp, &s, &bl.tm, written);
+  }
+}
+}  // namespace
+
 extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
   if (check_cfg(cfg, B) != WKV7_OK) return 0;
   Carver c(nullptr);
@@ -812,7 +984,7 @@ extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
 extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, int B,
                                  const int* tokens, float* att_x_prev, float* att_state,
                                  float* ffn_x_prev, float* logits, void* ws, size_t ws_bytes,
-                                 hipStream_t st) {
+                                 const wkv7_side* side, hipStream_t st) {
   g_err[0] = 0;
   CHK(check_cfg(cfg, B));
   const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
@@ -839,6 +1011,20 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
+  const wkv7_side* sd = nullptr;
+  CHK(check_side(side, st, sd));
+  {
+    const size_t f = sizeof(float), L = cfg->n_layer, BC = (size_t)B * cfg->C;
+    Spans sp;
+    model_spans(sp, cfg, M, false);
+    sp.rd(tokens, (size_t)B * sizeof(int), "tokens");
+    sp.wr(att_x_prev, L * BC * f, "att_x_prev");  // the state tensors are updated in place
+    sp.wr(att_state, L * state_bytes(B, cfg->H), "att_state");
+    sp.wr(ffn_x_prev, L * BC * f, "ffn_x_prev");
+    sp.wr(logits, (size_t)B * cfg->V * f, "logits");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
   Carver cw(ws);
   DecodeBufs d[DECODE_MAX_GROUPS];
   carve_decode_all(cw, cfg, B, d);
@@ -848,37 +1034,25 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
   if (ng == 1)
     return decode_run(cfg, M, B, 0, B, tokens, att_x_prev, att_state, ffn_x_prev, logits, d[0],
                       prec, st);
-  ForkJoin* fj = fork_join_acquire(st);
-  if (!fj) {  // no side streams: the groups one after the other
+  if (!sd) {  // no side stream: the groups one after the other
     for (int g = 0; g < ng; g++)
       CHK(decode_run(cfg, M, B, b0[g], nb[g], tokens, att_x_prev, att_state, ffn_x_prev, logits,
                      d[g], prec, st));
     return WKV7_OK;
   }
-  std::lock_guard<std::mutex> hold(g_fj_mu, std::adopt_lock);
-  HIPCHK(hipEventRecord(fj->fork, st), "decode fork");
-  int rc = WKV7_OK;
-  hipError_t ej = hipSuccess;
-  int forked = 0;
-  for (int g = 1; g < ng; g++) {
-    hipStream_t sg = fj->side[g - 1];
-    HIPCHK(hipStreamWaitEvent(sg, fj->fork, 0), "decode fork");
-    forked = g;
-    if (rc == WKV7_OK)
-      rc = decode_run(cfg, M, B, b0[g], nb[g], tokens, att_x_prev, att_state, ffn_x_prev, logits,
-                      d[g], prec, sg);
-    // each join is enqueued whatever happened, so the caller's stream (or
-    // capture) never leaves a side stream dangling
-    const hipError_t e = hipEventRecord(fj->join[g - 1], sg);
-    if (ej == hipSuccess) ej = e;
-  }
+  // group 1 on the side stream, forked from and joined back to `st`
+  HIPCHK(hipEventRecord(sd->ev[0], st), "decode fork");
+  HIPCHK(hipStreamWaitEvent(sd->stream, sd->ev[0], 0), "decode fork");
+  int rc = decode_run(cfg, M, B, b0[1], nb[1], tokens, att_x_prev, att_state, ffn_x_prev, logits,
+                      d[1], prec, sd->stream);
+  // the join is enqueued whatever happened, so the caller's stream (or
+  // capture) never leaves the side stream dangling
+  hipError_t ej = hipEventRecord(sd->ev[3], sd->stream);
   if (rc == WKV7_OK)
     rc = decode_run(cfg, M, B, 0, nb[0], tokens, att_x_prev, att_state, ffn_x_prev, logits, d[0],
                     prec, st);
-  for (int g = 1; g <= forked; g++) {
-    const hipError_t e = hipStreamWaitEvent(st, fj->join[g - 1], 0);
-    if (ej == hipSuccess) ej = e;
-  }
+  const hipError_t e = hipStreamWaitEvent(st, sd->ev[3], 0);
+  if (ej == hipSuccess) ej = e;
   HIPCHK(ej, "decode join");
   return rc;
 }
@@ -895,7 +1069,7 @@ struct BlockActs {
 struct TrainBufs {
   float *block_in, *x_emb, *vf, *dvf, *h, *dsh, *dh, *dx, *dx1;
   float *dfk, *logits, *loss_row, *part_ln, *part_cm, *splitk;
-  int *count, *off, *perm;
+  int *count, *off, *perm, *n_valid;
   std::vector<BlockActs> act;  // every block's (train_recompute == 0), or one reused
   TmBwdBufs tb;
 };
@@ -923,6 +1097,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   t.count = (int*)c.take((size_t)V);
   t.off = (int*)c.take((size_t)V);
   t.perm = (int*)c.take(BT);
+  t.n_valid = (int*)c.take(1);
   const bool keep = cfg->train_recompute == 0;
   t.act.resize(keep ? L : 1);
   for (size_t i = 0; i < t.act.size(); i++) {
@@ -951,7 +1126,7 @@ extern "C" size_t rwkv7_train_workspace_bytes(const rwkv7_config* cfg, int B, in
 extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
                                 rwkv7_model_grads* G, int B, int T, const int* tokens,
                                 const int* targets, float* loss, void* ws, size_t ws_bytes,
-                                hipStream_t st) {
+                                const wkv7_side* side, hipStream_t st) {
   g_err[0] = 0;
   CHK(check_cfg(cfg, B));
   const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
@@ -997,6 +1172,18 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
+  const wkv7_side* sd = nullptr;
+  CHK(check_side(side, st, sd));
+  {
+    Spans sp;
+    model_spans(sp, cfg, M, false);
+    model_spans(sp, cfg, G, true);
+    sp.rd(tokens, (size_t)B * T * sizeof(int), "tokens");
+    sp.rd(targets, (size_t)B * T * sizeof(int), "targets");
+    sp.wr(loss, sizeof(float), "loss");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
   Carver cw(ws);
   TrainBufs t;
   carve_train(cw, cfg, B, T, t);
@@ -1009,10 +1196,6 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     return tm_launch_reduce(t.part_ln, 2, stk_num_ln_blocks(BT), C, o, st);
   };
 
-  // ---------------- forward (block inputs kept for the backward)
-  HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
-  if (cfg->use_ln0)
-    HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
   const bool keep = cfg->train_recompute == 0;
   // one block forward from bin(l) into bin(l+1), activations into a
   auto block_fwd = [&](int l, BlockActs& a) -> int {
@@ -1041,29 +1224,26 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(L), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
-  HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, st), "cross-entropy");
+  HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, t.n_valid, st), "cross-entropy");
 
   // ---------------- backward
-  // Weight gradients run on the library side stream (see tm_backward_impl):
-  // here the head's and each channel-mix's, which only use t.splitk among the
-  // scratch buffers; every block's time-mix backward joins the side stream
-  // before returning, before any buffer they read is written again.
-  ForkJoin* fj = fork_join_acquire(st);
-  std::unique_lock<std::mutex> hold;
-  if (fj) hold = std::unique_lock<std::mutex>(g_fj_mu, std::adopt_lock);
-  hipStream_t ss = fj ? fj->side[0] : st;
+  // Weight gradients run on the side stream (see tm_backward_impl): here the
+  // head's and each channel-mix's, which only use t.splitk among the scratch
+  // buffers; every block's time-mix backward joins the side stream before
+  // returning, before any buffer they read is written again.
+  hipStream_t ss = sd ? sd->stream : st;
   auto fork_here = [&]() -> hipError_t {
-    if (!fj) return hipSuccess;
-    hipError_t r = hipEventRecord(fj->fork, st);
-    return r != hipSuccess ? r : hipStreamWaitEvent(ss, fj->fork, 0);
+    if (!sd) return hipSuccess;
+    hipError_t r = hipEventRecord(sd->ev[0], st);
+    return r != hipSuccess ? r : hipStreamWaitEvent(ss, sd->ev[0], 0);
   };
   struct Join {
-    ForkJoin* fj;
-    hipStream_t st, ss;
+    const wkv7_side* sd;
+    hipStream_t st;
     ~Join() {
-      if (fj && hipEventRecord(fj->join[0], ss) == hipSuccess) (void)hipStreamWaitEvent(st, fj->join[0], 0);
+      if (sd && hipEventRecord(sd->ev[3], sd->stream) == hipSuccess) (void)hipStreamWaitEvent(st, sd->ev[3], 0);
     }
-  } join{fj, st, ss};
+  } join{sd, st};
   HIPCHK(fork_here(), "backward fork");
   HIPCHK(gemm_run(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
   HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
@@ -1095,7 +1275,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
     CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
-                         nullptr, st, prec, true, fj));
+                         nullptr, st, prec, sd));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }

@@ -473,11 +473,14 @@ constexpr int BK = 32;  // k per stage
 // tracks these writes to LDS nor adds waits for them: the kernel waits on
 // vmcnt itself before the barrier that publishes a stage (the compiler's own
 // vmcnt waits stay safe, since extra outstanding copies only make them
-// stricter).  m0 holds the LDS address; nothing else here uses m0.
+// stricter).  m0 holds the LDS address; nothing else here uses m0.  An
+// SALU write of m0 needs one wait state before an LDS-DMA load reads it; the
+// compiler inserts that nop for its own LDS-DMA but cannot see into this asm,
+// so the s_nop is written here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16(const char* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");

@@ -14,7 +14,7 @@ namespace stk {
 constexpr float LN_EPS = 1e-5f;
 constexpr int MAXC4_LIMIT = 16;  // LayerNorm keeps a row in registers: C <= 64 * 4 * 16
 
-// out[r] = emb[clamp(tok[r])] (float4 per thread)
+// out[r] = emb[tok[r]] (float4 per thread); an id outside [0, V) gives a zero row
 __global__ __launch_bounds__(256) void emb_gather(int R, int C, int V, const int* __restrict__ tok,
                                                   const float* __restrict__ emb,
                                                   float* __restrict__ out) {
@@ -23,8 +23,10 @@ __global__ __launch_bounds__(256) void emb_gather(int R, int C, int V, const int
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
     const size_t row = i / C4;
     const int c4 = (int)(i - row * C4);
-    const int id = min(max(tok[row], 0), V - 1);
-    reinterpret_cast<f4*>(out)[i] = reinterpret_cast<const f4*>(emb + (size_t)id * C)[c4];
+    const int id = tok[row];
+    reinterpret_cast<f4*>(out)[i] = (unsigned)id < (unsigned)V
+                                        ? reinterpret_cast<const f4*>(emb + (size_t)id * C)[c4]
+                                        : f4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -328,15 +330,41 @@ __global__ __launch_bounds__(256) void cm_shift_bwd(int BT, int T, int C, const 
   }
 }
 
+// Number of targets in [0, V) (the counted tokens; one workgroup).
+__global__ __launch_bounds__(256) void count_valid(int R, int V, const int* __restrict__ targets,
+                                                   int* __restrict__ n_valid) {
+  __shared__ int sm[4];
+  int c = 0;
+  for (int i = threadIdx.x; i < R; i += 256) c += (unsigned)targets[i] < (unsigned)V;
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) n_valid[0] = (sm[0] + sm[1]) + (sm[2] + sm[3]);
+}
+
 // Fused log-softmax cross-entropy, one workgroup per row, in place:
-// loss_row[r] = lse - z[target];  z <- (softmax(z) - onehot(target)) / n_tok.
+// loss_row[r] = lse - z[target];  z <- (softmax(z) - onehot(target)) / n_valid.
+// A target outside [0, V) is ignored: zero row, zero loss term.  The maximum
+// is exact; each exp(z - max) is an fp32 term in (0, 1], and their sum, its
+// log and so lse are in double (the fullmodel page's fm_k_ce_bwd keeps the
+// normaliser in double).
 __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restrict__ z,
-                                                  const int* __restrict__ targets, float inv_n,
+                                                  const int* __restrict__ targets,
+                                                  const int* __restrict__ n_valid,
                                                   float* __restrict__ loss_row) {
-  __shared__ float sm[2][4];
+  __shared__ float smx[4];
+  __shared__ double ssum[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   f4* zr = reinterpret_cast<f4*>(z + (size_t)row * V);
   const int V4 = V / 4;
+  const int tgt = targets[row];
+  if ((unsigned)tgt >= (unsigned)V) {  // ignored row (uniform per workgroup)
+    for (int i = tid; i < V4; i += 256) zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+    if (tid == 0) loss_row[row] = 0.f;
+    return;
+  }
+  const int nv = n_valid[0];
+  const float inv_n = (float)(1.0 / (double)nv);  // nv >= 1 here
   float mx = -INFINITY;
   for (int i = tid; i < V4; i += 256) {
     const f4 v = zr[i];
@@ -344,20 +372,20 @@ __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restric
   }
   // wave max via the sum machinery on exp-free values: use shuffles
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) sm[0][wave] = mx;
+  if (lane == 0) smx[wave] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(sm[0][0], sm[0][1]), fmaxf(sm[0][2], sm[0][3]));
-  float s = 0.f;
+  mx = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+  double s = 0.0;
   for (int i = tid; i < V4; i += 256) {
     const f4 v = zr[i];
-    s += (expf(v[0] - mx) + expf(v[1] - mx)) + (expf(v[2] - mx) + expf(v[3] - mx));
+    s += (double)((expf(v[0] - mx) + expf(v[1] - mx)) + (expf(v[2] - mx) + expf(v[3] - mx)));
   }
-  s = wavesum(s);
-  if (lane == 0) sm[1][wave] = s;
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) ssum[wave] = s;
   __syncthreads();
-  s = (sm[1][0] + sm[1][1]) + (sm[1][2] + sm[1][3]);
-  const float lse = mx + logf(s);
-  const int tgt = min(max(targets[row], 0), V - 1);
+  s = (ssum[0] + ssum[1]) + (ssum[2] + ssum[3]);
+  const double lse_d = (double)mx + log(s);
+  const float lse = (float)lse_d;
   const float zt = z[(size_t)row * V + tgt];
   __syncthreads();  // every thread has read z[target] before it is overwritten
   for (int i = tid; i < V4; i += 256) {
@@ -367,11 +395,13 @@ __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restric
     for (int c = 0; c < 4; c++) p[c] = expf(v[c] - lse) - ((4 * i + c) == tgt ? 1.0f : 0.0f);
     zr[i] = p * inv_n;
   }
-  if (tid == 0) loss_row[row] = lse - zt;
+  if (tid == 0) loss_row[row] = (float)(lse_d - (double)zt);
 }
 
-// loss = sum_r loss_row[r] * inv_n, fixed order (one workgroup)
-__global__ __launch_bounds__(256) void sum_rows(int R, const float* __restrict__ v, float inv_n,
+// loss = sum_r loss_row[r] / n_valid (0 when no target is valid), fixed order
+// (one workgroup)
+__global__ __launch_bounds__(256) void sum_rows(int R, const float* __restrict__ v,
+                                                const int* __restrict__ n_valid,
                                                 float* __restrict__ out) {
   __shared__ float sm[256];
   float s = 0.f;
@@ -382,7 +412,10 @@ __global__ __launch_bounds__(256) void sum_rows(int R, const float* __restrict__
     if (threadIdx.x < w) sm[threadIdx.x] += sm[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[0] = sm[0] * inv_n;
+  if (threadIdx.x == 0) {
+    const int nv = n_valid[0];
+    out[0] = nv > 0 ? (float)((double)sm[0] / (double)nv) : 0.f;
+  }
 }
 
 // Embedding backward without float atomics.
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(256) void sum_rows(int R, const float* __restrict__
 __global__ __launch_bounds__(256) void emb_count(int R, int V, const int* __restrict__ tok,
                                                  int* __restrict__ count) {
   const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p < R) atomicAdd(&count[min(max(tok[p], 0), V - 1)], 1);
+  if (p < R && (unsigned)tok[p] < (unsigned)V) atomicAdd(&count[tok[p]], 1);
 }
 // 2) exclusive scan of the counts (one workgroup of 1024 threads)
 __global__ __launch_bounds__(1024) void emb_scan(int V, const int* __restrict__ count,
@@ -414,14 +447,16 @@ __global__ __launch_bounds__(1024) void emb_scan(int V, const int* __restrict__ 
     run += count[i];
   }
 }
-// 3) position p goes to slot off[tok[p]] + #{q < p : tok[q] == tok[p]} (stable)
+// 3) position p goes to slot off[tok[p]] + #{q < p : tok[q] == tok[p]} (stable);
+// positions with an id outside [0, V) are not placed (no gradient row)
 __global__ __launch_bounds__(256) void emb_place(int R, int V, const int* __restrict__ tok,
                                                  const int* __restrict__ off, int* __restrict__ perm) {
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= R) return;
-  const int v = min(max(tok[p], 0), V - 1);
+  const int v = tok[p];
+  if ((unsigned)v >= (unsigned)V) return;
   int rank = 0;
-  for (int q = 0; q < p; q++) rank += min(max(tok[q], 0), V - 1) == v;
+  for (int q = 0; q < p; q++) rank += tok[q] == v;
   perm[off[v] + rank] = p;
 }
 // 4) demb[v] = sum of dx rows of its positions in position order; one wave per row
@@ -470,12 +505,13 @@ hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const f
   return hipGetLastError();
 }
 hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
-                         hipStream_t st) {
-  const float inv_n = 1.0f / (float)R;
-  hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, inv_n, loss_row);
+                         int* n_valid, hipStream_t st) {
+  hipLaunchKernelGGL(stk::count_valid, dim3(1), dim3(256), 0, st, R, V, targets, n_valid);
+  hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, n_valid,
+                     loss_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stk::sum_rows, dim3(1), dim3(256), 0, st, R, loss_row, inv_n, loss);
+  hipLaunchKernelGGL(stk::sum_rows, dim3(1), dim3(256), 0, st, R, loss_row, n_valid, loss);
   return hipGetLastError();
 }
 hipError_t stk_launch_emb_bwd(int R, int V, int C, const int* tok, const float* dx, int* count,

@@ -27,8 +27,10 @@ hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w
 hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,
                                    const float* mu, const float* dsh, float* dx, float* dx_prev,
                                    float* part, hipStream_t st);
+// Fused CE over R rows of V logits (in place: dlogits); n_valid: one int of
+// scratch (the count of targets in [0, V)).
 hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
-                         hipStream_t st);
+                         int* n_valid, hipStream_t st);
 hipError_t stk_launch_emb_bwd(int R, int V, int C, const int* tok, const float* dx, int* count,
                               int* off, int* perm, float* demb, hipStream_t st);
 hipError_t stk_launch_fill_zero(float* p, size_t n, hipStream_t st);

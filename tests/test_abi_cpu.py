@@ -31,6 +31,18 @@ def L():
     return binding.lib()
 
 
+@pytest.fixture(scope="module")
+def Lfake(L):
+    """The library, for calls made with fake device addresses.  Every such
+    call must fail validation; so that a check that wrongly passed could never
+    launch a kernel on those addresses, these tests run only on a host that
+    sees no GPU."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("calls with fake device addresses run only where no GPU is visible")
+    return L
+
+
 def test_header_declares_the_five_calls():
     names = _declared_functions()
     for n in ("wkv7_forward", "wkv7_backward", "wkv7_step", "timemix_forward", "timemix_backward"):
@@ -57,7 +69,8 @@ def _fwd(L, B=1, T=4, H=2, N=64, dtype=0, ptrs=None, s0=None):
     return L.wkv7_forward(B, T, H, N, dtype, *p[:6], s0, p[6], None, None, None, 0, None)
 
 
-def test_forward_rejects_bad_shapes(L):
+def test_forward_rejects_bad_shapes(Lfake):
+    L = Lfake
     assert _fwd(L, N=32) == -1 and "N=32" in _err(L)
     assert _fwd(L, T=0) == -1 and ">= 1" in _err(L)
     assert _fwd(L, B=0) == -1
@@ -65,7 +78,8 @@ def test_forward_rejects_bad_shapes(L):
     assert _fwd(L, dtype=7) == -1 and "dtype" in _err(L)
 
 
-def test_forward_rejects_null_and_misaligned(L):
+def test_forward_rejects_null_and_misaligned(Lfake):
+    L = Lfake
     assert _fwd(L, ptrs=[A, A, None, A, A, A, A]) == -1 and "k is NULL" in _err(L)
     assert _fwd(L, ptrs=[A, A, A, A, A, A, None]) == -1 and "y is NULL" in _err(L)
     assert _fwd(L, ptrs=[A, MIS, A, A, A, A, A]) == -1 and "aligned" in _err(L)
@@ -77,7 +91,8 @@ def test_forward_rejects_null_and_misaligned(L):
     assert rc == -1 and "y is not 8-byte aligned" in _err(L)
 
 
-def test_forward_workspace_size_and_check(L):
+def test_forward_workspace_size_and_check(Lfake):
+    L = Lfake
     # short sequences run token by token: no workspace
     assert L.wkv7_forward_workspace_bytes(2, 31, 4, 64) == 0
     need = L.wkv7_forward_workspace_bytes(2, 64, 4, 64)
@@ -91,18 +106,20 @@ def test_forward_workspace_size_and_check(L):
     assert rc == -3 and "workspace" in _err(L)
 
 
-def test_backward_needs_workspace_without_checkpoints(L):
+def test_backward_needs_workspace_without_checkpoints(Lfake):
+    L = Lfake
     need = L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 0)
     have = L.wkv7_backward_workspace_bytes(1, 64, 4, 64, 1)
     assert need >= have + L.wkv7_checkpoint_floats(1, 64, 4, 64) * 4
     assert have > 0   # column partials of the row-split reverse pass
     ptr13 = [A] * 13
     rc = L.wkv7_backward(1, 64, 4, 64, 0, *ptr13[:6], None, None, ptr13[6], None, *ptr13[7:13],
-                         None, A, need - 1, None)
+                         None, A, need - 1, None, None)
     assert rc == -3 and "workspace" in _err(L)
 
 
-def test_step_rejects_null_state(L):
+def test_step_rejects_null_state(Lfake):
+    L = Lfake
     rc = L.wkv7_step(2, 4, 64, 0, A, A, A, A, A, A, None, A, None)
     assert rc == -1 and "state is NULL" in _err(L)
     assert L.wkv7_step(2, 4, 48, 0, A, A, A, A, A, A, A, A, None) == -1
@@ -129,7 +146,8 @@ def _weights(layer):
     return w
 
 
-def test_timemix_forward_validation(L):
+def test_timemix_forward_validation(Lfake):
+    L = Lfake
     w = _weights(1)
     s = _tm(C=250)
     rc = L.timemix_forward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, A, None, None, A, None,
@@ -150,7 +168,8 @@ def test_timemix_forward_validation(L):
     assert rc == -1 and "v0" in _err(L)
 
 
-def test_timemix_backward_validation(L):
+def test_timemix_backward_validation(Lfake):
+    L = Lfake
     from rwkv_linear_attention_wkv7_amd import binding
     s = _tm(layer=0)
     w = _weights(0)
@@ -161,9 +180,135 @@ def test_timemix_backward_validation(L):
     need = L.timemix_backward_workspace_bytes(ctypes.byref(s), 2, 8)
     assert need > L.timemix_cache_bytes(ctypes.byref(s), 2, 8)
     rc = L.timemix_backward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, None, None, A, None,
-                            None, ctypes.byref(g), A, None, None, None, None, A, need, None)
+                            None, ctypes.byref(g), A, None, None, None, None, A, need, None, None)
     assert rc == -1 and "gradient" in _err(L)
     g.Wk = 4096
     rc = L.timemix_backward(ctypes.byref(s), ctypes.byref(w), 2, 8, A, None, None, None, A, None,
-                            None, ctypes.byref(g), A, None, None, None, None, A, need - 1, None)
+                            None, ctypes.byref(g), A, None, None, None, None, A, need - 1, None, None)
     assert rc == -3
+
+
+# ---------------------------------------------------------------- aliasing --
+# Every call rejects a written tensor that overlaps another of its tensors.
+# The fake addresses below are spaced 256 MiB apart, so only the overlaps a
+# test creates on purpose exist; every case fails validation, so nothing is
+# ever launched.
+_SP = 1 << 28
+
+
+def _addrs(n, base=1 << 32):
+    return [ctypes.c_void_p(base + i * _SP) for i in range(n)]
+
+
+def _fwd_alias(L, p, s0=None, sT=None, ckpt=None):
+    return L.wkv7_forward(1, 64, 2, 64, 0, *p[:6], s0, p[6], sT, ckpt, None, 0, None)
+
+
+def test_forward_rejects_overlapping_outputs(Lfake):
+    L = Lfake
+    p = _addrs(10)
+    q = p[:6] + [p[0]]                       # y == r
+    assert _fwd_alias(L, q) == -1 and "overlaps" in _err(L) and "y" in _err(L)
+    q = p[:6] + [ctypes.c_void_p(p[3].value + 4096)]   # y inside v
+    assert _fwd_alias(L, q) == -1 and "overlaps" in _err(L)
+    # sT overlapping (not equal to) s0
+    assert _fwd_alias(L, p[:7], s0=p[7], sT=ctypes.c_void_p(p[7].value + 64)) == -1
+    assert "sT" in _err(L) and "s0" in _err(L)
+    # checkpoints over an input
+    assert _fwd_alias(L, p[:7], ckpt=p[2]) == -1 and "ckpt" in _err(L)
+
+
+def test_backward_rejects_overlaps(Lfake):
+    L = Lfake
+    p = _addrs(20)
+    need = L.wkv7_backward_workspace_bytes(1, 64, 2, 64, 1)
+
+    def bwd(ptr13, s0=None, ckpt=p[14], dsT=None, ds0=None, ws=p[15]):
+        return L.wkv7_backward(1, 64, 2, 64, 0, *ptr13[:6], s0, ckpt, ptr13[6], dsT, *ptr13[7:13],
+                               ds0, ws, need, None, None)
+
+    base = p[:13]
+    q = list(base)
+    q[7] = q[6]                               # dr == dy
+    assert bwd(q) == -1 and "overlaps" in _err(L)
+    assert bwd(base, ds0=ctypes.c_void_p(p[15].value + 1024)) == -1   # ds0 inside ws
+    assert "ds0" in _err(L) or "ws" in _err(L)
+    assert bwd(base, dsT=p[16], ds0=p[16]) == -1 and "ds0" in _err(L)  # no in-place state gradient
+    q = list(base)
+    q[12] = p[14]                             # db over the checkpoints
+    assert bwd(q) == -1 and "ckpt" in _err(L)
+
+
+def test_step_rejects_output_over_state(Lfake):
+    L = Lfake
+    p = _addrs(9)
+    rc = L.wkv7_step(2, 4, 64, 0, *p[:6], p[7], ctypes.c_void_p(p[7].value + 256), None)
+    assert rc == -1 and "overlaps" in _err(L)
+    rc = L.wkv7_step(2, 4, 64, 0, *p[:6], p[7], p[1], None)   # y == w
+    assert rc == -1 and "overlaps" in _err(L)
+
+
+def _tm_weights_at(base, layer):
+    from rwkv_linear_attention_wkv7_amd import binding
+    w = binding.TmWeights()
+    for i, n in enumerate(binding.WEIGHT_FIELDS):
+        setattr(w, n, None if (layer == 0 and n in ("v0", "V1", "V2")) else base + i * _SP)
+    return w
+
+
+def test_timemix_rejects_overlaps(Lfake):
+    L = Lfake
+    from rwkv_linear_attention_wkv7_amd import binding
+    s = _tm(layer=1)
+    w = _tm_weights_at(1 << 40, 1)
+    x, xp, vf, s0, sT, out, xl, ws = _addrs(8, base=1 << 44)
+    need = L.timemix_forward_workspace_bytes(ctypes.byref(s), 2, 8)
+
+    def fwd(**kw):
+        a = dict(x=x, xp=xp, vf=vf, s0=s0, sT=sT, out=out, xl=xl, ws=ws)
+        a.update(kw)
+        return L.timemix_forward(ctypes.byref(s), ctypes.byref(w), 2, 8, a["x"], a["xp"], a["vf"],
+                                 a["s0"], a["sT"], a["out"], a["xl"], None, a["ws"], need, None)
+
+    assert fwd(out=x) == -1 and "overlaps" in _err(L)
+    assert fwd(out=ctypes.c_void_p(w.Wo)) == -1 and "Wo" in _err(L)    # output over a weight
+    assert fwd(xl=xp) == -1 and "x_last" in _err(L)   # in place only for one token
+    assert fwd(ws=ctypes.c_void_p(out.value + 256)) == -1
+    # backward: a gradient over a weight, dx over dout
+    g = binding.TmGrads()
+    for i, n in enumerate(binding.WEIGHT_FIELDS):
+        setattr(g, n, (1 << 42) + i * _SP)
+    nb = L.timemix_backward_workspace_bytes(ctypes.byref(s), 2, 8)
+    dout, dx = _addrs(2, base=1 << 45)
+
+    def bwd(dxp=dx):
+        return L.timemix_backward(ctypes.byref(s), ctypes.byref(w), 2, 8, x, None, vf, None, dout,
+                                  None, None, ctypes.byref(g), dxp, None, None, None, None, ws, nb,
+                                  None, None)
+    assert bwd(dxp=dout) == -1 and "overlaps" in _err(L)
+    g.Wk = w.Wk
+    assert bwd() == -1 and "Wk" in _err(L)
+
+
+def test_gemm_rejects_output_over_operand(Lfake):
+    L = Lfake
+    a, b = _addrs(2)
+    assert L.wkv7_gemm_f32(0, 0, 64, 64, 64, a, 64, b, 64, a, 64, 0.0, None) == -1
+    assert "overlaps" in _err(L)
+    c = ctypes.c_void_p(b.value + 64 * 63 * 4)   # C starts in B's last row
+    assert L.wkv7_gemm_bf16(0, 0, 64, 64, 64, a, 64, b, 64, c, 64, 0.0, None) == -1
+
+
+def test_side_stream_validation(Lfake):
+    L = Lfake
+    from rwkv_linear_attention_wkv7_amd import binding
+    p = _addrs(16)
+    need = L.wkv7_backward_workspace_bytes(1, 64, 2, 64, 1)
+    sd = binding.Wkv7Side()
+    sd.stream = 12345
+    for i in range(3):
+        sd.ev[i] = 1000 + i       # ev[3] left NULL
+    rc = L.wkv7_backward(1, 64, 2, 64, 0, *p[:6], None, p[14], p[6], None, *p[7:13], None, p[15],
+                         need, ctypes.byref(sd), None)
+    assert rc == -1 and "ev[3]" in _err(L)
+    assert L.wkv7_side_destroy(None) == 0

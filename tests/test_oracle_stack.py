@@ -70,6 +70,34 @@ def test_cross_entropy_textbook():
     np.testing.assert_allclose((d * 20).sum(-1), 0.0, atol=1e-13)
 
 
+def test_cross_entropy_ignored_targets():
+    """Targets outside [0, V) are ignored (the fullmodel page's ignore_index):
+    the loss is the textbook mean over the counted tokens only, ignored rows
+    of dlogits are zero and the others are scaled by 1 / n_valid."""
+    z = np.random.default_rng(5).standard_normal((3, 4, 7))
+    t = np.random.default_rng(6).integers(0, 7, size=(3, 4))
+    t[0, 1], t[2, 3], t[1, 0] = -1, 7, 100
+    loss, d = stack.cross_entropy(z, t)
+    ok = (t >= 0) & (t < 7)
+    p = np.exp(z) / np.exp(z).sum(-1, keepdims=True)
+    lp = np.log(np.take_along_axis(p, np.where(ok, t, 0)[..., None], -1))[..., 0]
+    np.testing.assert_allclose(loss, -lp[ok].mean(), rtol=1e-13)
+    assert np.all(d[~ok] == 0.0)
+    one = np.zeros_like(z)
+    np.put_along_axis(one, np.where(ok, t, 0)[..., None], 1.0, -1)
+    np.testing.assert_allclose(d[ok], (p - one)[ok] / ok.sum(), rtol=1e-12, atol=1e-15)
+    # nothing counted: zero loss and zero gradient
+    loss0, d0 = stack.cross_entropy(z, np.full((3, 4), -1))
+    assert loss0 == 0.0 and np.all(d0 == 0.0)
+
+
+def test_embedding_out_of_range_ids_are_zero_rows():
+    emb = np.random.default_rng(7).standard_normal((5, 3))
+    x = stack.embed(emb, np.array([[0, 4, -1, 5, 2]]))
+    np.testing.assert_array_equal(x[0, [0, 1, 4]], emb[[0, 4, 2]])
+    assert np.all(x[0, [2, 3]] == 0.0)
+
+
 def _fd(fn, x, eps=1e-6):
     g = np.zeros_like(x)
     it = np.nditer(x, flags=["multi_index"])
@@ -97,6 +125,8 @@ def test_train_step_central_fd():
         # tiny head size: the oracle's recurrence is N-generic
         tok = synth.token_ids(2, 3, V, seed=1)
         tgt = synth.token_ids(2, 3, V, seed=2)
+        # one out-of-range id (zero row, no gradient) and one ignored target
+        tok[1, 1], tgt[0, 2] = V + 3, -1
         loss, G = stack.train_step(m, cfg, tok, tgt)
         fn = lambda: stack.train_step(m, cfg, tok, tgt)[0]
         checks = [("emb", m["emb"], G["emb"]), ("head", m["head"], G["head"]),
