@@ -19,8 +19,9 @@
  *    read may overlap each other.  The exceptions are the in-place updates
  *    each call names (sT == s0, the decode state); anything else returns
  *    WKV7_EINVAL naming the two tensors.
- *  - The library keeps no state between calls beyond its loaded code:
- *    calls are re-entrant, from any thread, on any stream.
+ *  - The library keeps no state between calls beyond its loaded code (and
+ *    the fixed device scratch of wkv7_backward_noalloc): calls are
+ *    re-entrant, from any thread, on any stream.
  */
 #ifndef WKV7_H
 #define WKV7_H
@@ -142,6 +143,25 @@ int wkv7_backward(int B, int T, int H, int N, int dtype,
                   void *dr, void *dw, void *dk, void *dv, void *da, void *db,
                   float *ds0, void *ws, size_t ws_bytes, const wkv7_side *side,
                   hipStream_t stream);
+
+/*
+ * wkv7_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments, results and errors, with no workspace
+ * argument.  Its scratch (wkv7_backward_workspace_bytes(B, T, H, N,
+ * ckpt != NULL) bytes) comes from a fixed 64 MiB device array that each
+ * device holds until the process ends; a shape needing more returns
+ * WKV7_ENOSPC before anything is enqueued.  The call allocates nothing.  Every
+ * call on one device shares that device's array, so calls that overlap on
+ * one device (two streams, or two threads) race and must be serialised by
+ * the caller.
+ */
+int wkv7_backward_noalloc(int B, int T, int H, int N, int dtype,
+                          const void *r, const void *w, const void *k, const void *v,
+                          const void *a, const void *b, const float *s0, const float *ckpt,
+                          const void *dy, const float *dsT,
+                          void *dr, void *dw, void *dk, void *dv, void *da, void *db,
+                          float *ds0, const wkv7_side *side, hipStream_t stream);
 
 /*
  * Single-token streaming decode: the T = 1 forward with the state updated in

@@ -91,6 +91,8 @@ def lib():
         L.wkv7_backward_workspace_bytes.restype = _sz
         L.wkv7_backward.argtypes = [_i] * 5 + [_vp] * 17 + [_vp, _sz, _vp, _vp]
         L.wkv7_backward.restype = _i
+        L.wkv7_backward_noalloc.argtypes = [_i] * 5 + [_vp] * 17 + [_vp, _vp]
+        L.wkv7_backward_noalloc.restype = _i
         L.wkv7_step.argtypes = [_i] * 4 + [_vp] * 9
         L.wkv7_step.restype = _i
         sp = ctypes.POINTER(TmShape)
@@ -263,6 +265,33 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, want_ds0=T
                                    _p(s0), _p(ckpt), _p(dy), _p(dsT), _p(out["dr"]), _p(out["dw"]),
                                    _p(out["dk"]), _p(out["dv"]), _p(out["da"]), _p(out["db"]),
                                    _p(out["ds0"]), _p(ws), nbytes, sd, _stream()))
+    return out
+
+
+def wkv7_backward_noalloc(r, w, k, v, a, b, dy, s0=None, ckpt=None, dsT=None, out=None,
+                          side=True):
+    """wkv7_backward with the library's fixed device scratch instead of a
+    workspace.  out: optional dict of preallocated gradient tensors (dr, dw,
+    dk, dv, da, db, ds0), so that the call itself allocates nothing."""
+    B, T, H, N = r.shape
+    dt = r.dtype
+    for n, t in zip(("r", "w", "k", "v", "a", "b", "dy"), (r, w, k, v, a, b, dy)):
+        _need(t, (B, T, H, N), dt, n)
+    _opt(s0, (B, H, N, N), torch.float32, "s0")
+    _opt(dsT, (B, H, N, N), torch.float32, "dsT")
+    _opt(ckpt, (wkv7_checkpoint_floats(B, T, H, N),), torch.float32, "ckpt")
+    if out is None:
+        out = {n: torch.empty_like(r) for n in ("dr", "dw", "dk", "dv", "da", "db")}
+        out["ds0"] = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32)
+    for n in ("dr", "dw", "dk", "dv", "da", "db"):
+        _need(out[n], (B, T, H, N), dt, n)
+    _opt(out.get("ds0"), (B, H, N, N), torch.float32, "ds0")
+    with _SideUse(side) as sd:
+        _check(lib().wkv7_backward_noalloc(B, T, H, N, _dt(r), _p(r), _p(w), _p(k), _p(v), _p(a),
+                                           _p(b), _p(s0), _p(ckpt), _p(dy), _p(dsT), _p(out["dr"]),
+                                           _p(out["dw"]), _p(out["dk"]), _p(out["dv"]),
+                                           _p(out["da"]), _p(out["db"]), _p(out.get("ds0")), sd,
+                                           _stream()))
     return out
 
 

@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/wkv7.h"
@@ -306,6 +308,80 @@ int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void*
   return WKV7_OK;
 }
 }  // namespace
+
+// ---------------------------------------------- backward without allocation --
+// Fixed device scratch of wkv7_backward_noalloc, for callers that cannot
+// allocate (graph capture, tight serving loops).  Each device holds its own
+// copy until the process ends; host code never uses the array's name as an
+// address, only the pointer hipGetSymbolAddress returns for the current
+// device (looked up once per device and kept).  Every call on a device
+// shares that device's copy: calls that overlap on one device race.
+namespace {
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[NOALLOC_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(WKV7_EINVAL, "device %d beyond the %d the fixed scratch serves", dev,
+                NOALLOC_MAX_DEVICES);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(WKV7_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return WKV7_OK;
+}
+}  // namespace
+
+extern "C" int wkv7_backward_noalloc(int B, int T, int H, int N, int dtype, const void* r,
+                                     const void* w, const void* k, const void* v, const void* a,
+                                     const void* b, const float* s0, const float* ckpt,
+                                     const void* dy, const float* dsT, void* dr, void* dw,
+                                     void* dk, void* dv, void* da, void* db, float* ds0,
+                                     const wkv7_side* side, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_wkv_shape(B, T, H, N, dtype));
+  const char* names[] = {"r", "w", "k", "v", "a", "b", "dy", "dr", "dw", "dk", "dv", "da", "db"};
+  const void* ptrs[] = {r, w, k, v, a, b, dy, dr, dw, dk, dv, da, db};
+  for (int i = 0; i < 13; i++) CHK(check_tok_ptr(ptrs[i], names[i], dtype, true));
+  CHK(check_f32_ptr(s0, "s0", false));
+  CHK(check_f32_ptr(ckpt, "ckpt", false));
+  CHK(check_f32_ptr(dsT, "dsT", false));
+  CHK(check_f32_ptr(ds0, "ds0", false));
+  const size_t need = wkv7_backward_workspace_bytes(B, T, H, N, ckpt != nullptr);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(WKV7_ENOSPC, "this shape needs %zu bytes of scratch; the fixed scratch of "
+                "wkv7_backward_noalloc holds %zu (use wkv7_backward with a workspace)",
+                need, NOALLOC_SCRATCH_BYTES);
+  const wkv7_side* sd = nullptr;
+  CHK(check_side(side, stream, sd));
+  {
+    const size_t tb = tok_bytes(B, T, H, dtype), sb = state_bytes(B, H);
+    Spans sp;
+    for (int i = 0; i < 7; i++) sp.rd(ptrs[i], tb, names[i]);
+    for (int i = 7; i < 13; i++) sp.wr(ptrs[i], tb, names[i]);
+    sp.rd(s0, sb, "s0");
+    sp.rd(dsT, sb, "dsT");
+    sp.rd(ckpt, ckpt_floats(B, T, H) * sizeof(float), "ckpt");
+    sp.wr(ds0, sb, "ds0");
+    CHK(sp.check());
+  }
+  void* ws = nullptr;
+  CHK(scratch_of_current_device(&ws));
+  return wkv7_backward_run(B, T, H, dtype, r, w, k, v, a, b, s0, ckpt, dy, dsT, dr, dw, dk, dv, da,
+                           db, ds0, ws, sd, stream);
+}
 
 extern "C" int wkv7_step(int B, int H, int N, int dtype, const void* r, const void* w,
                          const void* k, const void* v, const void* a, const void* b, float* state,

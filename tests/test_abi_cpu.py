@@ -312,3 +312,20 @@ def test_side_stream_validation(Lfake):
                          need, ctypes.byref(sd), None)
     assert rc == -1 and "ev[3]" in _err(L)
     assert L.wkv7_side_destroy(None) == 0
+
+
+def test_backward_noalloc_rejects_shapes_beyond_its_scratch(Lfake):
+    """The fixed-scratch backward refuses, before any device call, a shape
+    whose scratch exceeds its 64 MiB array."""
+    L = Lfake
+    p = _addrs(16)
+    B, T, H = 4, 8192, 32
+    assert L.wkv7_backward_workspace_bytes(B, T, H, 64, 1) > (64 << 20)
+    rc = L.wkv7_backward_noalloc(B, T, H, 64, 0, *p[:6], None, p[14], p[6], None, *p[7:13], None,
+                                 None, None)
+    assert rc == -3 and "fixed scratch" in _err(L)
+    q = list(p[:13])
+    q[8] = q[6]   # dw == dy: overlap checks as wkv7_backward
+    rc = L.wkv7_backward_noalloc(1, 64, 2, 64, 0, *q[:6], None, p[14], q[6], None, *q[7:13], None,
+                                 None, None)
+    assert rc == -1 and "overlaps" in _err(L)
