@@ -1,8 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the RWKV-7 WKV7 / time-mix hot path on one MI355X.
 
-Prints ONE JSON line.  Workloads (--workload):
-  decode     (default) streaming decode through a 12-layer RWKV-7 stack,
+Prints ONE JSON line.  By default every workload below runs in turn; the
+line's headline ("value") is the streaming decode, and "configs" holds one
+record per workload (median ms per step, throughput, roofline of its
+dominant kernel, CPU-oracle baseline).  --workload NAME runs one of them as
+the headline alone.  Workloads:
+  wkv7_small WKV7 forward+backward, B=1 T=64 H=4 N=64, fp32 (the small
+             configuration; latency bound: microseconds per step)
+  decode     streaming decode through a 12-layer RWKV-7 stack,
              C=256 H=4 FFN 1024, LoRA 32/32/32/64, vocab 256, 2048
              independent streams, fp32, one token per stream per step
              (steps/s); the step is replayed from a captured HIP graph
@@ -15,9 +21,10 @@ Prints ONE JSON line.  Workloads (--workload):
              backward; GEMMs with bf16 operands and fp32 accumulation,
              recurrence and elementwise steps fp32 (tokens/s)
 A step is one pass of the whole workload over one batch of seeded synthetic
-inputs that are resident in HBM before timing starts.  Steps are timed with
-HIP events on the stream the library launches on, bracketed by device
-synchronisation.
+inputs that are resident in HBM before timing starts.  Each step is timed
+with its own pair of HIP events on the stream the library launches on; the
+K timed steps are bracketed by device synchronisation, and ms_per_step is
+their median (the mean is reported beside it).
 
 "roofline" reports the workload's dominant kernel, timed live here on the
 same stream over its own loop of launches (HIP events), against MI355X peak.
@@ -46,17 +53,24 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_loop(fn, iters):
-    """Average ms per call of fn(), HIP events on the current stream."""
+def time_calls(fn, iters):
+    """Per-call ms of `iters` calls of fn(): one pair of HIP events per call on
+    the current stream (the stream the library launches on), bracketed by
+    device synchronisation.  Returns (median, mean, wall seconds)."""
+    import statistics
+
     import torch
-    s, e = _events()
+    ev = [_events() for _ in range(iters)]
     torch.cuda.synchronize()
-    s.record()
-    for _ in range(iters):
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
         fn()
-    e.record()
+        e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in ev]
+    return statistics.median(ms), sum(ms) / len(ms), wall
 
 
 def traffic_from_profile(kernel_key, src_files):
@@ -79,6 +93,52 @@ def traffic_from_profile(kernel_key, src_files):
 
 
 # --------------------------------------------------------------- workloads --
+def setup_wkv7_small():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    B, T, H = 1, 64, 4
+    d = synth.wkv7_inputs(B, T, H, N, seed=0)
+    dev = torch.device("cuda")
+    names = ("r", "w", "k", "v", "a", "b")
+    ins = [torch.from_numpy(d[n]).to(dev) for n in names]
+    dy = torch.from_numpy(d["dy"]).to(dev)
+    ck = torch.empty(binding.wkv7_checkpoint_floats(B, T, H), device=dev)
+
+    def step():
+        binding.wkv7_forward(*ins, ckpt=ck, want_state=False)
+        binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
+
+    def dom():
+        binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
+
+    flops = 26.0 * N * N * B * T * H
+    roof = dict(kernel="wkv7 backward call (B=1 T=64 H=4: 16 workgroups, latency bound)",
+                bound="alu", work=flops, unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom,
+                key="wkv7_bwd_small", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+
+    def cpu():
+        from oracle import wkv7 as ow
+        sub = [d[n].astype(np.float64) for n in names]
+        dy64 = d["dy"].astype(np.float64)
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 2.0:
+            ow.forward(*sub)
+            ow.backward(*sub, dy64)
+            reps += 1
+        dt = time.perf_counter() - t0
+        return dict(value=reps * B * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"the whole workload (4 heads, T=64) {reps} times: f64 forward+backward, "
+                           f"{dt:.1f} s")
+
+    cfg = {"workload": "WKV7 forward+backward, small", "B": B, "T": T, "H": H, "N": N,
+           "dtype": "fp32", "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="f32", config=cfg, roof=roof,
+                cpu=cpu, extra=lambda v, ms: {"us_per_step": round(ms * 1e3, 2)})
+
+
 def setup_timemix():
     import numpy as np
     import torch
@@ -131,7 +191,7 @@ def setup_timemix():
                 cpu=cpu)
 
 
-def setup_wkv7_long():
+def setup_wkv7_long(chunked=False):
     import numpy as np
     import torch
 
@@ -144,9 +204,15 @@ def setup_wkv7_long():
     dy = torch.from_numpy(d["dy"]).to(dev).to(torch.bfloat16)
     ck = torch.empty(binding.wkv7_checkpoint_floats(B, T, H), device=dev)
 
+    fws = None
+    if chunked:
+        fws = torch.empty(binding.lib().wkv7_forward_workspace_bytes(B, T, H, N), dtype=torch.uint8,
+                          device=dev)
+
     def step():
-        # token-sequential forward (no chunk workspace): the faster path here
-        binding.wkv7_forward(*ins, ckpt=ck, want_state=False, chunked=False)
+        # token-sequential forward (no chunk workspace): the faster path here;
+        # chunked=True times the chunked matrix-core forward instead
+        binding.wkv7_forward(*ins, ckpt=ck, want_state=False, chunked=chunked, ws=fws)
         binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
 
     def dom():
@@ -173,6 +239,7 @@ def setup_wkv7_long():
                            f"{dt:.1f} s")
 
     cfg = {"workload": "WKV7 forward+backward, long context", "B": B, "T": T, "H": H, "N": N,
+           "forward": "chunked (matrix cores)" if chunked else "token-sequential",
            "inputs": "bf16", "state": "fp32", "checkpoint_interval": binding.wkv7_checkpoint_interval(),
            "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
     return dict(step=step, tokens=B * T, unit="tokens/s", dtype="bf16 in / f32 state", config=cfg,
@@ -252,7 +319,7 @@ def setup_decode():
            "tokens_per_step": B, "token_steps_available": STEPS, "graph_replay": True,
            "global_batch": B, "seq_len": 1, "parallelism": "single GPU"}
     return dict(step=step, tokens=1, unit="steps/s", dtype="f32", config=cfg, roof=roof, cpu=cpu,
-                extra=lambda v: {"tokens_per_s": round(v * B, 1)})
+                extra=lambda v, ms: {"tokens_per_s": round(v * B, 1)})
 
 
 def setup_train():
@@ -310,11 +377,58 @@ def setup_train():
            "lora_ranks_w_a_v_g": list(ranks), "B": B, "T": T, "gemm": "bf16 operands, fp32 accumulation (matrix cores)",
            "global_batch": B, "seq_len": T, "parallelism": "single GPU"}
     return dict(step=step, tokens=B * T, unit="tokens/s", dtype="bf16 GEMM / f32", config=cfg,
-                roof=roof, cpu=cpu, extra=lambda v: {"loss": round(float(loss.item()), 5)})
+                roof=roof, cpu=cpu, extra=lambda v, ms: {"loss": round(float(loss.item()), 5)})
 
 
-WORKLOADS = {"decode": setup_decode, "timemix": setup_timemix, "wkv7_long": setup_wkv7_long,
-             "train": setup_train}
+WORKLOADS = {"wkv7_small": setup_wkv7_small, "decode": setup_decode, "timemix": setup_timemix,
+             "wkv7_long": setup_wkv7_long, "train": setup_train,
+             "wkv7_long_chunked": lambda: setup_wkv7_long(chunked=True)}
+ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train")
+
+
+def run_workload(name, steps, warmup, roof_iters, with_cpu):
+    """One workload: warm-up, K timed steps, the dominant kernel's roofline
+    loop, optionally the CPU-oracle baseline.  Returns its record."""
+    import torch
+    w = WORKLOADS[name]()
+    for _ in range(warmup):
+        w["step"]()
+    torch.cuda.synchronize()
+    ms, ms_mean, wall = time_calls(w["step"], steps)
+    value = w["tokens"] / (ms / 1e3)
+
+    r = w["roof"]
+    r["fn"]()
+    kms, kms_mean, _ = time_calls(r["fn"], roof_iters)
+    # work: algorithmic flop (unit TFLOP/s) or bytes (unit GB/s) per launch
+    achieved = r["work"] / (kms / 1e3) / (1e12 if r["unit"] == "TFLOP/s" else 1e9)
+    traffic = traffic_from_profile(r["key"], r["src"])
+    roofline = {"bound": r["bound"], "kernel": r["kernel"], "achieved": round(achieved, 3),
+                "peak": r["peak"], "unit": r["unit"], "frac": round(achieved / r["peak"], 4),
+                "kernel_ms": round(kms, 4), "kernel_ms_mean": round(kms_mean, 4),
+                "traffic": traffic}
+    if r["bound"] == "alu":
+        # the published fp32 vector peak counts packed FMA (two per lane); the
+        # kernels here issue one fp32 FMA per lane: 256 CUs x 64 lanes x 2 flop
+        # x 2.4 GHz
+        roofline["peak_without_packed_fp32"] = PEAK_ALU_NO_PACKED
+        roofline["frac_without_packed_fp32"] = round(achieved / PEAK_ALU_NO_PACKED, 4)
+    cpu = None
+    if with_cpu:
+        cpu = w["cpu"]()
+        cpu["value"] = round(cpu["value"], 2)
+    rec = {"value": round(value, 1), "unit": w["unit"], "steps": steps, "warmup": warmup,
+           "ms_per_step": round(ms, 4), "ms_per_step_mean": round(ms_mean, 4),
+           "wall_s": round(wall, 3), "dtype": w["dtype"], "config": w["config"],
+           "roofline": roofline, "cpu_baseline": cpu}
+    if "extra" in w:
+        rec.update(w["extra"](value, ms))
+    del w
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -322,7 +436,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=sorted(WORKLOADS) + ["all"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roof-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -352,49 +466,24 @@ def main():
     from rwkv_linear_attention_wkv7_amd import binding
     binding.lib()
 
-    w = WORKLOADS[args.workload]()
-    for _ in range(args.warmup):
-        w["step"]()
-    torch.cuda.synchronize()
-    s, e = _events()
-    t0 = time.perf_counter()
-    s.record()
-    for _ in range(args.steps):
-        w["step"]()
-    e.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = s.elapsed_time(e) / args.steps
-    value = w["tokens"] / (ms / 1e3)
-
-    r = w["roof"]
-    r["fn"]()
-    kms = time_loop(r["fn"], args.roof_iters)
-    # work: algorithmic flop (unit TFLOP/s) or bytes (unit GB/s) per launch
-    achieved = r["work"] / (kms / 1e3) / (1e12 if r["unit"] == "TFLOP/s" else 1e9)
-    traffic = traffic_from_profile(r["key"], r["src"])
-    roofline = {"bound": r["bound"], "kernel": r["kernel"], "achieved": round(achieved, 3),
-                "peak": r["peak"], "unit": r["unit"], "frac": round(achieved / r["peak"], 4),
-                "kernel_ms": round(kms, 4), "traffic": traffic}
-    if r["bound"] == "alu":
-        # the published fp32 vector peak counts packed FMA (two per lane); the
-        # kernels here issue one fp32 FMA per lane: 256 CUs x 64 lanes x 2 flop
-        # x 2.4 GHz
-        roofline["peak_without_packed_fp32"] = PEAK_ALU_NO_PACKED
-        roofline["frac_without_packed_fp32"] = round(achieved / PEAK_ALU_NO_PACKED, 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = w["cpu"]()
-        cpu["value"] = round(cpu["value"], 2)
-
-    out = {"metric": METRIC, "value": round(value, 1), "unit": w["unit"], "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-           "wall_s": round(wall, 3), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic (seeded)",
-           "config": w["config"], "roofline": roofline, "cpu_baseline": cpu}
-    if "extra" in w:
-        out.update(w["extra"](value))
+    names = ORDER if args.workload == "all" else (args.workload,)
+    head = "decode" if args.workload == "all" else args.workload
+    recs = {}
+    for n in names:
+        print(f"[bench] {n}", file=sys.stderr, flush=True)
+        recs[n] = run_workload(n, args.steps, args.warmup, args.roof_iters,
+                               not args.no_cpu_baseline)
+    h = recs[head]
+    out = {"metric": METRIC, "value": h["value"], "unit": h["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+           "wall_s": h["wall_s"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": h["dtype"], "data": "synthetic (seeded)",
+           "config": h["config"], "roofline": h["roofline"], "cpu_baseline": h["cpu_baseline"]}
+    for k in ("ms_per_step_mean", "tokens_per_s", "us_per_step", "loss"):
+        if k in h:
+            out[k] = h[k]
+    if len(recs) > 1:
+        out["configs"] = recs
     print(json.dumps(out), flush=True)
 
 
