@@ -170,3 +170,28 @@ def stack_model(C, H, F, V, n_layer, ranks, seed=0, use_ln0=True, perturbed=Fals
 def token_ids(B, T, V, seed=0, name="tokens"):
     """Uniform int32 token ids [B][T] in [0, V)."""
     return rng(seed, name).integers(0, V, size=(B, T)).astype(np.int32)
+
+
+def gdn_config(nk, nv, dk, dv, kk=4, seed=0, rms_eps=1e-6):
+    """Frozen GatedDeltaNet weights: conv taps ~ N(0, 1/kk) [c_dim][kk],
+    A_log ~ U(-2, 1) (decay rates e^A_log in (0.14, 2.7)), dt_bias ~ N(0, 0.5^2),
+    norm ~ 1 + N(0, 0.1^2) [dv]."""
+    c_dim = 2 * nk * dk + nv * dv
+    return dict(nk=nk, nv=nv, dk=dk, dv=dv, kk=kk, rms_eps=rms_eps,
+                conv=(rng(seed, "gdn_conv").standard_normal((c_dim, kk)) / np.sqrt(kk)).astype(np.float32),
+                A_log=rng(seed, "gdn_A_log").uniform(-2.0, 1.0, size=nv).astype(np.float32),
+                dt_bias=(0.5 * rng(seed, "gdn_dt_bias").standard_normal(nv)).astype(np.float32),
+                norm=(1.0 + 0.1 * rng(seed, "gdn_norm").standard_normal(dv)).astype(np.float32))
+
+
+def gdn_inputs(B, T, cfg, seed=0):
+    """raw [B][T][c_dim], z [B][T][nv dv], a, b [B][T][nv], dout [B][T][nv dv],
+    all ~ N(0, 1) (fp32): the projections feeding one GatedDeltaNet layer."""
+    nk, nv, dk, dv = cfg["nk"], cfg["nv"], cfg["dk"], cfg["dv"]
+    c_dim = 2 * nk * dk + nv * dv
+    out = dict(raw=rng(seed, "gdn_raw").standard_normal((B, T, c_dim)),
+               z=rng(seed, "gdn_z").standard_normal((B, T, nv * dv)),
+               a=rng(seed, "gdn_a").standard_normal((B, T, nv)),
+               b=rng(seed, "gdn_b").standard_normal((B, T, nv)),
+               dout=rng(seed, "gdn_dout").standard_normal((B, T, nv * dv)))
+    return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
