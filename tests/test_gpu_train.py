@@ -10,11 +10,16 @@ with respect to rounding: rounding the f64 oracle's own products to bf16
 moves its embedding gradient by ~45% (random init, std 0.02), and merely
 storing each product of the bf16 oracle as fp32 instead of f64 moves some of
 its time-mix gradients by ~9% (a cascade of flipped bf16 roundings through 24
-blocks).  So at full size the bf16 run is held to 2e-2 on the loss and on the
-head / ln_out gradients (well conditioned), and every other gradient must
-point the same way as the oracle's (cosine >= 0.95); the complete per-tensor
-2e-2 comparison runs on the small models, and the fp32-GEMM run of the same
-full-size step meets 1e-3 on every gradient."""
+blocks).  So at the full model size (24 blocks) every bf16 gradient is held
+to a bound calibrated by the oracle's own bf16 spread: err(gpu vs f64 oracle)
+<= 2 err(bf16 oracle vs f64 oracle) + 1e-3, per tensor (scale-aware: every
+spread is below 0.5, so a gradient off by a factor of 2 fails).  At the configuration's batch and
+width with two blocks (B=4, T=2048, C=1024, vocab 65536), where the cascade
+is short, loss and every gradient are held to 2e-2 against the bf16-operand
+oracle, run one sequence at a time (the loss is a mean over tokens, so the
+batch gradient is the mean of the per-sequence ones).  The complete
+per-tensor 2e-2 comparison also runs on the small models, and the fp32-GEMM
+run of the full-size step meets 1e-3 on every gradient."""
 import math
 
 import numpy as np
@@ -52,41 +57,57 @@ def _run(hip, L, C, H, F, V, ranks, B, T, seed, perturbed, std, use_ln0, gemm="f
     return m, dm, grads, x, y, float(loss.item())
 
 
-def _compare(m, grads, x, y, loss, cfg, gemm="f32", only=None):
-    """only: names checked at the tolerance; the rest get the cosine check."""
+def _pairs(g, G):
+    """(name, gpu tensor, oracle array) for every gradient of the model."""
+    for k in ("emb", "head", "ln_out_w", "ln_out_b", "ln0_w", "ln0_b"):
+        if g.get(k) is not None:
+            yield k, g[k], G[k]
+    for l, gb in enumerate(g["blocks"]):
+        for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
+            yield f"{k}[{l}]", gb[k], G["blocks"][l][k]
+        assert set(gb["tm"]) == set(G["blocks"][l]["tm"])
+        for k, v in gb["tm"].items():
+            yield f"tm.{k}[{l}]", v, G["blocks"][l]["tm"][k]
+
+
+def _compare(m, grads, x, y, loss, cfg, gemm="f32"):
+    """Every gradient at the tolerance against the oracle at the run's precision."""
     tl, tg = (1e-4, 1e-3) if gemm == "f32" else (2e-2, 2e-2)
     ref_loss, G = stack.train_step(m, cfg, x, y, gemm="f64" if gemm == "f32" else "bf16")
     assert abs(loss - ref_loss) <= tl * abs(ref_loss), (loss, ref_loss)
-    g = grads.g
     worst = [0.0, ""]
-    cos_min = [1.0, ""]
-
-    def chk(name, got, ref, tol):
-        if only is not None and name not in only:
-            a, b = np.asarray(got, np.float64).ravel(), np.asarray(ref, np.float64).ravel()
-            c = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
-            if c < cos_min[0]:
-                cos_min[:] = [c, name]
-            assert c >= 0.95, f"{name}: cosine {c:.4f} < 0.95"
-            return
-        e = assert_close(name, got, ref, tol)
+    for name, got, ref in _pairs(grads.g, G):
+        e = assert_close(name, got.cpu().numpy(), ref, tg)
         if e > worst[0]:
             worst[:] = [e, name]
-    np_ = lambda t: t.cpu().numpy()
-    for k in ("emb", "head", "ln_out_w", "ln_out_b"):
-        chk(k, np_(g[k]), G[k], tg)
-    if g.get("ln0_w") is not None:
-        chk("ln0_w", np_(g["ln0_w"]), G["ln0_w"], tg)
-        chk("ln0_b", np_(g["ln0_b"]), G["ln0_b"], tg)
-    for l, gb in enumerate(g["blocks"]):
-        for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
-            chk(f"{k}[{l}]", np_(gb[k]), G["blocks"][l][k], tg)
-        assert set(gb["tm"]) == set(G["blocks"][l]["tm"])
-        for k, v in gb["tm"].items():
-            chk(f"tm.{k}[{l}]", np_(v), G["blocks"][l]["tm"][k], tg)
     print(f"[train] gemm={gemm} loss {loss:.6f} oracle {ref_loss:.6f}; worst gradient "
-          f"{worst[1]} rel err {worst[0]:.2e}; lowest cosine {cos_min[1]} {cos_min[0]:.5f}",
-          flush=True)
+          f"{worst[1]} rel err {worst[0]:.2e}", flush=True)
+
+
+def _compare_calibrated(m, grads, x, y, loss, cfg):
+    """bf16 GEMMs at the full model size: per tensor, err(gpu vs f64 oracle) <=
+    2 err(bf16-operand oracle vs f64 oracle) + 1e-3; loss at 2e-2.  The GPU
+    run and the bf16-operand oracle are two draws of the same rounding
+    cascade (fp32 against f64 accumulation flips different bf16 roundings), so
+    their distances to the f64 result differ by a random factor; every spread
+    here is below 0.5, so a gradient off by a factor of 2 or of the wrong
+    sign still fails."""
+    from tests.parity import rel_err
+    l64, G64 = stack.train_step(m, cfg, x, y, gemm="f64")
+    l16, G16 = stack.train_step(m, cfg, x, y, gemm="bf16")
+    assert abs(loss - l64) <= 2e-2 * abs(l64), (loss, l64)
+    ref16 = dict((n, r) for n, _, r in _pairs(grads.g, G16))
+    ratios = []
+    for name, got, r64 in _pairs(grads.g, G64):
+        spread = rel_err(ref16[name], r64)
+        e = rel_err(got.cpu().numpy(), r64)
+        ratios.append((e / (2.0 * spread + 1e-3), e, spread, name))
+    ratios.sort(reverse=True)
+    print(f"[train] bf16 full size: loss {loss:.6f} f64 oracle {l64:.6f}; {len(ratios)} tensors; "
+          f"err / bound, highest: " + ", ".join(f"{n} {q:.3f} (err {e:.2e}, spread {s:.2e})"
+                                               for q, e, s, n in ratios[:6]), flush=True)
+    bad = [r for r in ratios if r[0] > 1.0]
+    assert not bad, f"{len(bad)} tensors above 2 x oracle bf16 spread + 1e-3, e.g. {bad[:3]}"
 
 
 @pytest.mark.parametrize("gemm", ["f32", "bf16"])
@@ -106,8 +127,11 @@ def test_train_step_full_model_short_batch(hip, gemm):
     L, C, H, F, V = 24, 1024, 16, 4096, 65536
     m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), 1, 256, seed=0,
                                     perturbed=False, std=0.02, use_ln0=False, gemm=gemm)
-    only = None if gemm == "f32" else ("head", "ln_out_w", "ln_out_b")
-    _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L), gemm, only)
+    cfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+    if gemm == "f32":
+        _compare(m, grads, x, y, loss, cfg, gemm)
+    else:
+        _compare_calibrated(m, grads, x, y, loss, cfg)
 
 
 @pytest.mark.parametrize("gemm", ["f32", "bf16"])
@@ -148,3 +172,66 @@ def test_train_step_full_config_properties(hip, gemm):
     assert torch.equal(first["head"], grads.g["head"])
     assert torch.equal(first["Wr0"], grads.g["blocks"][0]["tm"]["Wr"])
     assert torch.equal(first["cmk23"], grads.g["blocks"][23]["cm_Wk"])
+
+
+# ---- the configuration's batch and width (B=4, T=2048, C=1024, FFN 4096,
+# vocab 65536, ranks 64/64/32/128, bf16 GEMMs) with two blocks: the GPU step
+# runs once on the whole batch; the bf16-operand oracle runs one sequence per
+# test and the per-sequence results are averaged, then compared.
+_C4 = {}
+_C4_B, _C4_T, _C4_L = 4, 2048, 2
+
+
+def _flat(G):
+    """name -> tensor/array for a nested gradient dict (GPU or oracle)."""
+    for k, v in G.items():
+        if k == "blocks":
+            for l, b in enumerate(v):
+                for kk, vv in b.items():
+                    if kk == "tm":
+                        for k3, v3 in vv.items():
+                            yield f"tm.{k3}[{l}]", v3
+                    else:
+                        yield f"{kk}[{l}]", vv
+        elif v is not None:
+            yield k, v
+
+
+def _c4_gpu(hip):
+    if "gpu" not in _C4:
+        L, C, H, F, V = _C4_L, 1024, 16, 4096, 65536
+        m, dm, grads, x, y, loss = _run(hip, L, C, H, F, V, (64, 64, 32, 128), _C4_B, _C4_T, seed=5,
+                                        perturbed=False, std=0.02, use_ln0=False, gemm="bf16")
+        g = {n: t.cpu().numpy() for n, t in _flat(grads.g)}
+        _C4.update(gpu=g, loss=loss, m=m, x=x, y=y, cfg=dict(C=C, H=H, F=F, V=V, n_layer=L),
+                   acc={}, acc_loss=0.0, done=set())
+        del dm, grads
+        torch.cuda.empty_cache()
+    return _C4
+
+
+@pytest.mark.parametrize("b", range(_C4_B))
+def test_train_step_config_batch_two_blocks_sequence(hip, b):
+    st = _c4_gpu(hip)
+    print(f"[train c4 batch] oracle sequence {b}", flush=True)
+    lb, Gb = stack.train_step(st["m"], st["cfg"], st["x"][b:b + 1], st["y"][b:b + 1], gemm="bf16")
+    for name, r in _flat(Gb):
+        st["acc"][name] = st["acc"].get(name, 0.0) + np.asarray(r) / _C4_B
+    st["acc_loss"] += lb / _C4_B
+    st["done"].add(b)
+
+
+def test_train_step_config_batch_two_blocks_compare(hip):
+    st = _c4_gpu(hip)
+    if st["done"] != set(range(_C4_B)):
+        pytest.skip("needs every per-sequence oracle test of this batch first")
+    assert set(st["gpu"]) == set(st["acc"])
+    assert abs(st["loss"] - st["acc_loss"]) <= 2e-2 * abs(st["acc_loss"]), (st["loss"], st["acc_loss"])
+    worst = [0.0, ""]
+    for name in sorted(st["gpu"]):
+        e = assert_close(name, st["gpu"][name], st["acc"][name], 2e-2)
+        if e > worst[0]:
+            worst[:] = [e, name]
+    print(f"[train c4 batch] loss {st['loss']:.6f} oracle {st['acc_loss']:.6f}; worst gradient "
+          f"{worst[1]} rel err {worst[0]:.2e} over {len(st['gpu'])} tensors", flush=True)
+    _C4.clear()
