@@ -16,6 +16,9 @@ the headline alone.  Workloads:
              LoRA ranks w/a/v/g = 64/64/32/128, layer > 0, fp32 (tokens/s)
   wkv7_long  WKV7 forward+backward, B=4 T=8192 H=32 N=64, bf16 token
              tensors, fp32 state, checkpointed backward (tokens/s)
+  gdn        GatedDeltaNet layer forward + through-gradient backward, B=2
+             windows of T=4096, 16 key heads / 32 value heads of size 128,
+             4 causal conv taps, fp32 (tokens/s)
   train      full training step: 24 blocks C=1024 H=16 FFN 4096, vocab
              65536, B=4 T=2048, embedding, LM head, fused CE, forward +
              backward; GEMMs with bf16 operands and fp32 accumulation,
@@ -380,10 +383,81 @@ def setup_train():
                 roof=roof, cpu=cpu, extra=lambda v, ms: {"loss": round(float(loss.item()), 5)})
 
 
+def setup_gdn():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    B, T, nk, nv, dk, dv, kk = 2, 4096, 16, 32, 128, 128, 4
+    cfg = synth.gdn_config(nk, nv, dk, dv, kk=kk, seed=0)
+    d = synth.gdn_inputs(B, T, cfg, seed=0)
+    dev = torch.device("cuda")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    layer = binding.Gdn(nk, nv, dk, dv, kk, cfg["rms_eps"], t(cfg["conv"]), t(cfg["A_log"]),
+                        t(cfg["dt_bias"]), t(cfg["norm"]))
+    ins = [t(d[k]) for k in ("raw", "z", "a", "b")]
+    dout = t(d["dout"])
+    cache = torch.empty(binding.gdn_cache_bytes(layer, B, T), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, nv * dv), device=dev)
+    ws = torch.empty(binding.lib().gdn_backward_workspace_bytes(
+        ctypes_byref(layer.shape), B, T, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.gdn_forward(layer, *ins, out=out, cache=cache)
+        binding.gdn_backward(layer, *ins, dout, cache=cache, ws=ws)
+
+    def dom():
+        binding.gdn_backward(layer, *ins, dout, cache=cache, ws=ws)
+
+    # the backward's recurrence per token and value head: 5 dk dv flop to
+    # recompute the state (decay, kv, update) and 14 dk dv for the reverse
+    # step (dS += q^ do, S do, dS^T k^, dS_pre, dS u + S_pre dkv, <dS_pre, S>,
+    # g dS_pre)
+    flops = 19.0 * dk * dv * B * T * nv
+    roof = dict(kernel="gdn_backward call (recurrence from 16-token checkpoints + RMSNorm, "
+                       "gate and l2-norm chain, conv backward)", bound="alu", work=flops,
+                unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom, key="gdn_bwd",
+                src=["rwkv_linear_attention_wkv7_amd/csrc/gdn.hip"])
+
+    def cpu():
+        from oracle import gdn as og
+        from oracle import wkv7 as ow
+        kd = nk * dk
+        heads = np.arange(2)
+        ch = np.concatenate([np.arange(dk), kd + np.arange(dk),
+                             2 * kd + (heads[:, None] * dv + np.arange(dv)).ravel()])
+        vc = (heads[:, None] * dv + np.arange(dv)).ravel()
+        f64 = lambda x: np.asarray(x, np.float64)
+        sub = {k: (f64(v) if isinstance(v, np.ndarray) else v) for k, v in cfg.items()}
+        sub.update(nk=1, nv=2, conv=f64(cfg["conv"])[ch], A_log=f64(cfg["A_log"])[heads],
+                   dt_bias=f64(cfg["dt_bias"])[heads])
+        t0 = time.perf_counter()
+        _, c = og.forward(f64(d["raw"][0][:, ch]), f64(d["z"][0][:, vc]), f64(d["a"][0][:, heads]),
+                          f64(d["b"][0][:, heads]), sub)
+        og.backward(c, f64(d["dout"][0][:, vc]))
+        dt = time.perf_counter() - t0
+        scale = B * nk  # windows x key-head groups in the workload
+        return dict(value=B * T / (dt * scale), unit="tokens/s", cores=ow.num_threads(),
+                    kind="oracle",
+                    sample=f"one key-head group (2 value heads) of one window, T={T}: f64 forward+"
+                           f"backward, {dt:.1f} s; scaled to the {scale} groups of the workload")
+
+    cfgd = {"workload": "GatedDeltaNet layer forward+backward (through-gradients)", "B": B, "T": T,
+            "nk": nk, "nv": nv, "dk": dk, "dv": dv, "conv_taps": kk, "global_batch": B,
+            "seq_len": T, "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="f32", config=cfgd, roof=roof,
+                cpu=cpu)
+
+
+def ctypes_byref(x):
+    import ctypes
+    return ctypes.byref(x)
+
+
 WORKLOADS = {"wkv7_small": setup_wkv7_small, "decode": setup_decode, "timemix": setup_timemix,
-             "wkv7_long": setup_wkv7_long, "train": setup_train,
+             "wkv7_long": setup_wkv7_long, "train": setup_train, "gdn": setup_gdn,
              "wkv7_long_chunked": lambda: setup_wkv7_long(chunked=True)}
-ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train")
+ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train", "gdn")
 
 
 def run_workload(name, steps, warmup, roof_iters, with_cpu):

@@ -366,6 +366,58 @@ int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
                      const int *targets, float *loss, void *ws, size_t ws_bytes,
                      const wkv7_side *side, hipStream_t stream);
 
+/* -------------------------------------------------- GatedDeltaNet layer -- */
+
+/* Geometry of one GatedDeltaNet layer: nk key heads of size dk, nv value
+ * heads of size dv (nv a multiple of nk, at most 16 value heads per key
+ * head, grouped-query sharing), kk causal convolution taps (1..8), RMSNorm
+ * epsilon.  The HIP kernels take dk and dv in {64, 128}.
+ * c_dim = 2 nk dk + nv dv projection channels (q | k | v). */
+typedef struct {
+  int nk, nv, dk, dv, kk;
+  float rms_eps;
+} gdn_shape;
+
+/* Frozen fp32 weights: conv [c_dim][kk] (tap kk-1 multiplies the current
+ * position), A_log [nv], dt_bias [nv], norm [dv]. */
+typedef struct {
+  const float *conv, *A_log, *dt_bias, *norm;
+} gdn_weights;
+
+/* Bytes of the activations gdn_forward keeps for gdn_backward. */
+size_t gdn_cache_bytes(const gdn_shape *s, int B, int T);
+/* Workspace bytes of gdn_backward (plus the cache when have_cache is 0). */
+size_t gdn_backward_workspace_bytes(const gdn_shape *s, int B, int T, int have_cache);
+
+/*
+ * GatedDeltaNet forward over B independent windows of T positions, each from
+ * a fresh (zero) state.  Page: "cortiq_engine/fcd_ops.rs", GatedDeltaNet
+ * section (gdn_conv_fwd, gdn_group_fwd, gdn_seq_fwd):
+ *   pre = causal depthwise conv(raw), cq = silu(pre)
+ *   q^ = q / (sqrt(|q|^2 + 1e-6) sqrt(dk)), k^ = k / sqrt(|k|^2 + 1e-6)
+ *   g = exp(-exp(A_log) softplus(a + dt_bias)) (softplus(x) = x above 20),
+ *   beta = sigmoid(b); per value head, S [dk][dv] from zero:
+ *     S = g S;  kv = S^T k^;  S = S + k^ (beta (v - kv))^T;  o = S^T q^
+ *   out = o / sqrt(mean(o^2) + rms_eps) * norm * silu(z)   (norm before gate)
+ * raw: [B][T][c_dim]; z, out: [B][T][nv][dv]; a, b: [B][T][nv]; all fp32.
+ * cache: NULL, or gdn_cache_bytes() bytes that receive the activations the
+ * backward reuses (with NULL the call needs ws of gdn_cache_bytes() bytes).
+ */
+int gdn_forward(const gdn_shape *s, const gdn_weights *W, int B, int T, const float *raw,
+                const float *z, const float *a, const float *b, float *out, void *cache,
+                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gradients of <dout, out> with respect to raw, z, a and b (every weight
+ * frozen: the page's through-backward gdn_seq_bwd).  cache: the forward's
+ * cache for the same inputs, or NULL (the forward is recomputed into ws).
+ * draw [B][T][c_dim], dz [B][T][nv][dv], da, db [B][T][nv] (written).
+ */
+int gdn_backward(const gdn_shape *s, const gdn_weights *W, int B, int T, const float *raw,
+                 const float *z, const float *a, const float *b, const float *dout,
+                 const void *cache, float *draw, float *dz, float *da, float *db, void *ws,
+                 size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------- helpers -- */
 
 /*

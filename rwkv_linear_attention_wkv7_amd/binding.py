@@ -60,6 +60,14 @@ class Rwkv7ModelGrads(ctypes.Structure):
                                                "head")] + [("blocks", ctypes.POINTER(Rwkv7BlockGrads))]
 
 
+class GdnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("nk", "nv", "dk", "dv", "kk")] + [("rms_eps", ctypes.c_float)]
+
+
+class GdnWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("conv", "A_log", "dt_bias", "norm")]
+
+
 class Wkv7Side(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("ev", ctypes.c_void_p * 4)]
 
@@ -119,6 +127,15 @@ def lib():
         L.rwkv7_train_step.argtypes = ([cp, ctypes.POINTER(Rwkv7Model), ctypes.POINTER(Rwkv7ModelGrads),
                                         _i, _i] + [_vp] * 4 + [_sz, _vp, _vp])
         L.rwkv7_train_step.restype = _i
+        gp, gw = ctypes.POINTER(GdnShape), ctypes.POINTER(GdnWeights)
+        L.gdn_cache_bytes.argtypes = [gp, _i, _i]
+        L.gdn_cache_bytes.restype = _sz
+        L.gdn_backward_workspace_bytes.argtypes = [gp, _i, _i, _i]
+        L.gdn_backward_workspace_bytes.restype = _sz
+        L.gdn_forward.argtypes = [gp, gw, _i, _i] + [_vp] * 7 + [_sz, _vp]
+        L.gdn_forward.restype = _i
+        L.gdn_backward.argtypes = [gp, gw, _i, _i] + [_vp] * 11 + [_sz, _vp]
+        L.gdn_backward.restype = _i
         L.wkv7_side_create.argtypes = [ctypes.POINTER(Wkv7Side)]
         L.wkv7_side_create.restype = _i
         L.wkv7_side_destroy.argtypes = [ctypes.POINTER(Wkv7Side)]
@@ -558,3 +575,62 @@ def rwkv7_train_step(dm, grads, tokens, targets, loss=None, ws=None, side=True):
                                       ctypes.byref(grads.struct), B, T, _p(tokens), _p(targets),
                                       _p(loss), _p(ws), ws.numel(), sd, _stream()))
     return loss
+
+
+# ------------------------------------------------------------ GatedDeltaNet --
+class Gdn:
+    """A GatedDeltaNet layer's geometry and frozen device weights (the C
+    structs hold raw pointers, so the tensors are kept here)."""
+
+    def __init__(self, nk, nv, dk, dv, kk, rms_eps, conv, A_log, dt_bias, norm):
+        self.shape = GdnShape(nk, nv, dk, dv, kk, rms_eps)
+        cdim = 2 * nk * dk + nv * dv
+        self.cdim = cdim
+        self.w = dict(conv=_need(conv, (cdim, kk), torch.float32, "conv"),
+                      A_log=_need(A_log, (nv,), torch.float32, "A_log"),
+                      dt_bias=_need(dt_bias, (nv,), torch.float32, "dt_bias"),
+                      norm=_need(norm, (dv,), torch.float32, "norm"))
+        self.weights = GdnWeights(*(self.w[k].data_ptr() for k in ("conv", "A_log", "dt_bias", "norm")))
+
+    def _inputs(self, raw, z, a, b):
+        s = self.shape
+        B, T = raw.shape[:2]
+        _need(raw, (B, T, self.cdim), torch.float32, "raw")
+        _need(z, (B, T, s.nv * s.dv), torch.float32, "z")
+        _need(a, (B, T, s.nv), torch.float32, "a")
+        _need(b, (B, T, s.nv), torch.float32, "b")
+        return B, T
+
+
+def gdn_cache_bytes(layer, B, T):
+    return lib().gdn_cache_bytes(ctypes.byref(layer.shape), B, T)
+
+
+def gdn_forward(layer, raw, z, a, b, want_cache=True, out=None, cache=None):
+    """out [B][T][nv dv]; returns (out, cache or None)."""
+    B, T = layer._inputs(raw, z, a, b)
+    s = layer.shape
+    out = _opt(out, (B, T, s.nv * s.dv), torch.float32, "out") if out is not None else \
+        torch.empty((B, T, s.nv * s.dv), device=raw.device, dtype=torch.float32)
+    n = gdn_cache_bytes(layer, B, T)
+    buf = cache if cache is not None else torch.empty(n, device=raw.device, dtype=torch.uint8)
+    _check(lib().gdn_forward(ctypes.byref(s), ctypes.byref(layer.weights), B, T, _p(raw), _p(z),
+                             _p(a), _p(b), _p(out), _p(buf if want_cache else None),
+                             _p(None if want_cache else buf), 0 if want_cache else n, _stream()))
+    return out, (buf if want_cache else None)
+
+
+def gdn_backward(layer, raw, z, a, b, dout, cache=None, ws=None):
+    """Gradients of <dout, out>: dict draw, dz, da, db."""
+    B, T = layer._inputs(raw, z, a, b)
+    s = layer.shape
+    _need(dout, (B, T, s.nv * s.dv), torch.float32, "dout")
+    g = dict(draw=torch.empty_like(raw), dz=torch.empty_like(z), da=torch.empty_like(a),
+             db=torch.empty_like(b))
+    n = lib().gdn_backward_workspace_bytes(ctypes.byref(s), B, T, int(cache is not None))
+    if ws is None:
+        ws = torch.empty(n, device=raw.device, dtype=torch.uint8)
+    _check(lib().gdn_backward(ctypes.byref(s), ctypes.byref(layer.weights), B, T, _p(raw), _p(z),
+                              _p(a), _p(b), _p(dout), _p(cache), _p(g["draw"]), _p(g["dz"]),
+                              _p(g["da"]), _p(g["db"]), _p(ws), ws.numel(), _stream()))
+    return g

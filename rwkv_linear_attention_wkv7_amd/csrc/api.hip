@@ -15,6 +15,7 @@
 
 #include "../../include/wkv7.h"
 #include "common.hpp"
+#include "gdn.hpp"
 #include "stack_kernels.hpp"
 #include "timemix_kernels.hpp"
 
@@ -1362,5 +1363,168 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     demb_src = t.dx1;
   }
   HIPCHK(stk_launch_emb_bwd(BT, V, C, tokens, demb_src, t.count, t.off, t.perm, G->emb, st), "embedding bwd");
+  return WKV7_OK;
+}
+
+// ------------------------------------------------------------ GatedDeltaNet --
+namespace {
+
+int check_gdn(const gdn_shape* s, const gdn_weights* W, int B, int T) {
+  if (!s || !W) return fail(WKV7_EINVAL, "shape or weights is NULL");
+  if ((s->dk != 64 && s->dk != 128) || (s->dv != 64 && s->dv != 128))
+    return fail(WKV7_EINVAL, "dk and dv must be 64 or 128 (got %d, %d)", s->dk, s->dv);
+  if (s->nk < 1 || s->nv < 1 || s->nv % s->nk || s->nv / s->nk > 16)
+    return fail(WKV7_EINVAL, "nv must be a multiple of nk with at most 16 value heads per key head");
+  if (s->kk < 1 || s->kk > 8) return fail(WKV7_EINVAL, "kk must be in 1..8 (got %d)", s->kk);
+  if (!(s->rms_eps >= 0.f)) return fail(WKV7_EINVAL, "rms_eps must be >= 0");
+  if (B < 1 || T < 1) return fail(WKV7_EINVAL, "B, T must be >= 1 (got %d, %d)", B, T);
+  const size_t cdim = 2 * (size_t)s->nk * s->dk + (size_t)s->nv * s->dv;
+  if ((size_t)B * T * cdim > ((size_t)1 << 36)) return fail(WKV7_EINVAL, "problem too large");
+  CHK(check_f32_ptr(W->conv, "conv", true));
+  CHK(check_f32_ptr(W->A_log, "A_log", true));
+  CHK(check_f32_ptr(W->dt_bias, "dt_bias", true));
+  CHK(check_f32_ptr(W->norm, "norm", true));
+  return WKV7_OK;
+}
+
+size_t gdn_cdim(const gdn_shape* s) { return 2 * (size_t)s->nk * s->dk + (size_t)s->nv * s->dv; }
+
+void carve_gdn_cache(Carver& c, const gdn_shape* s, int B, int T, GdnArgs& p) {
+  const size_t BT = (size_t)B * T, cd = gdn_cdim(s);
+  p.pre = c.take(BT * cd);
+  p.cq = c.take(BT * cd);
+  p.qh = c.take(BT * s->nk * s->dk);
+  p.kh = c.take(BT * s->nk * s->dk);
+  p.g = c.take(BT * s->nv);
+  p.beta = c.take(BT * s->nv);
+  p.o = c.take(BT * s->nv * s->dv);
+  p.ckpt = c.take(gdn_ckpt_floats(B, T, s->nv, s->dk, s->dv));
+}
+
+void carve_gdn_bwd(Carver& c, const gdn_shape* s, int B, int T, GdnArgs& p) {
+  const size_t BT = (size_t)B * T;
+  p.dobuf = c.take(BT * s->nv * s->dv);
+  p.dcq = c.take(BT * gdn_cdim(s));
+  p.part = c.take(gdn_partial_floats(B, T, s->nv, s->dk, s->dv));
+}
+
+void gdn_fill(GdnArgs& p, const gdn_shape* s, const gdn_weights* W, int B, int T,
+              const float* raw, const float* z, const float* a, const float* b) {
+  p.B = B; p.T = T; p.nk = s->nk; p.nv = s->nv; p.dk = s->dk; p.dv = s->dv; p.kk = s->kk;
+  p.rms_eps = s->rms_eps;
+  p.raw = raw; p.z = z; p.a = a; p.b = b;
+  p.conv = W->conv; p.A_log = W->A_log; p.dt_bias = W->dt_bias; p.norm = W->norm;
+}
+
+void gdn_input_spans(Spans& sp, const gdn_shape* s, int B, int T, const float* raw,
+                     const float* z, const float* a, const float* b, const gdn_weights* W) {
+  const size_t BT = (size_t)B * T, f = sizeof(float);
+  sp.rd(raw, BT * gdn_cdim(s) * f, "raw");
+  sp.rd(z, BT * s->nv * s->dv * f, "z");
+  sp.rd(a, BT * s->nv * f, "a");
+  sp.rd(b, BT * s->nv * f, "b");
+  sp.rd(W->conv, gdn_cdim(s) * s->kk * f, "conv");
+  sp.rd(W->A_log, s->nv * f, "A_log");
+  sp.rd(W->dt_bias, s->nv * f, "dt_bias");
+  sp.rd(W->norm, s->dv * f, "norm");
+}
+
+}  // namespace
+
+extern "C" size_t gdn_cache_bytes(const gdn_shape* s, int B, int T) {
+  if (!s || B < 1 || T < 1) return 0;
+  Carver c(nullptr);
+  GdnArgs p;
+  carve_gdn_cache(c, s, B, T, p);
+  return c.off + 256;
+}
+
+extern "C" size_t gdn_backward_workspace_bytes(const gdn_shape* s, int B, int T, int have_cache) {
+  if (!s || B < 1 || T < 1) return 0;
+  Carver c(nullptr);
+  GdnArgs p;
+  if (!have_cache) carve_gdn_cache(c, s, B, T, p);
+  carve_gdn_bwd(c, s, B, T, p);
+  return c.off + 256;
+}
+
+extern "C" int gdn_forward(const gdn_shape* s, const gdn_weights* W, int B, int T, const float* raw,
+                           const float* z, const float* a, const float* b, float* out, void* cache,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_gdn(s, W, B, T));
+  const float* ins[] = {raw, z, a, b, out};
+  const char* nm[] = {"raw", "z", "a", "b", "out"};
+  for (int i = 0; i < 5; i++) CHK(check_f32_ptr(ins[i], nm[i], true));
+  const size_t need = gdn_cache_bytes(s, B, T);
+  void* base = cache;
+  if (!base) {
+    if (!ws || ws_bytes < need)
+      return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    base = ws;
+  }
+  CHK(check_f32_ptr(base, cache ? "cache" : "ws", true));
+  {
+    Spans sp;
+    gdn_input_spans(sp, s, B, T, raw, z, a, b, W);
+    sp.wr(out, (size_t)B * T * s->nv * s->dv * sizeof(float), "out");
+    sp.wr(base, need, cache ? "cache" : "ws");
+    CHK(sp.check());
+  }
+  GdnArgs p;
+  memset(&p, 0, sizeof(p));
+  gdn_fill(p, s, W, B, T, raw, z, a, b);
+  Carver c(base);
+  carve_gdn_cache(c, s, B, T, p);
+  p.out = out;
+  HIPCHK(gdn_launch_forward(p, stream), "gdn_forward launch");
+  return WKV7_OK;
+}
+
+extern "C" int gdn_backward(const gdn_shape* s, const gdn_weights* W, int B, int T, const float* raw,
+                            const float* z, const float* a, const float* b, const float* dout,
+                            const void* cache, float* draw, float* dz, float* da, float* db,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_gdn(s, W, B, T));
+  const float* ins[] = {raw, z, a, b, dout, draw, dz, da, db};
+  const char* nm[] = {"raw", "z", "a", "b", "dout", "draw", "dz", "da", "db"};
+  for (int i = 0; i < 9; i++) CHK(check_f32_ptr(ins[i], nm[i], true));
+  CHK(check_f32_ptr(cache, "cache", false));
+  const size_t need = gdn_backward_workspace_bytes(s, B, T, cache != nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  CHK(check_f32_ptr(ws, "ws", true));
+  {
+    const size_t BT = (size_t)B * T, f = sizeof(float);
+    Spans sp;
+    gdn_input_spans(sp, s, B, T, raw, z, a, b, W);
+    sp.rd(dout, BT * s->nv * s->dv * f, "dout");
+    sp.rd(cache, cache ? gdn_cache_bytes(s, B, T) : 0, "cache");
+    sp.wr(draw, BT * gdn_cdim(s) * f, "draw");
+    sp.wr(dz, BT * s->nv * s->dv * f, "dz");
+    sp.wr(da, BT * s->nv * f, "da");
+    sp.wr(db, BT * s->nv * f, "db");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
+  GdnArgs p;
+  memset(&p, 0, sizeof(p));
+  gdn_fill(p, s, W, B, T, raw, z, a, b);
+  Carver cw(ws);
+  if (!cache) carve_gdn_cache(cw, s, B, T, p);
+  carve_gdn_bwd(cw, s, B, T, p);
+  if (!cache) {
+    // recompute the cache; the forward's output itself is not needed, so it
+    // goes to dobuf, which the backward's first kernel overwrites
+    p.out = p.dobuf;
+    HIPCHK(gdn_launch_forward(p, stream), "gdn_backward forward recompute");
+  } else {
+    Carver cc((void*)cache);
+    carve_gdn_cache(cc, s, B, T, p);
+  }
+  p.dout = dout;
+  p.dz = dz; p.draw = draw; p.da = da; p.db = db;
+  HIPCHK(gdn_launch_backward(p, stream), "gdn_backward launch");
   return WKV7_OK;
 }

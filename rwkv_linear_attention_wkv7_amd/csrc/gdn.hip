@@ -1,0 +1,625 @@
+// GatedDeltaNet layer on gfx950, forward and through-gradient backward
+// ("cortiq_engine/fcd_ops.rs", GatedDeltaNet through-backward section).
+//
+// Per window of T positions from a fresh state:
+//   pre = causal depthwise conv(raw), cq = silu(pre)   [c_dim = 2 nk dk + nv dv]
+//   q^ = q / (sqrt(|q|^2 + 1e-6) sqrt(dk)), k^ = k / sqrt(|k|^2 + 1e-6)
+//   g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+//   per v-head: S <- g S; kv = S^T k^; S <- S + k^ (beta (v - kv))^T; o = S^T q^
+//   out = o / sqrt(mean(o^2) + eps) * norm * silu(z)
+//
+// S is [dk][dv].  In the forward every value column j of S evolves on its
+// own (kv[j], the update of column j and o[j] only touch column j), so a
+// workgroup owns 16 columns of one (batch, head): 16 lanes per column (one
+// DPP row), each lane dk/16 key rows, and the column sums kv and o are
+// 16-lane DPP sums.  The per-token inputs are staged through LDS in blocks
+// of 16 tokens, and the state is checkpointed at every block start.  The
+// backward walks the blocks in reverse, recomputes each block's states from
+// its checkpoint, and runs the reverse step per column; the sums that cross
+// columns (dq^ and dk^ over the value index, dg and dbeta over columns) are
+// reduced across the wave's four columns with permlane swaps, across the
+// four waves through LDS, and across the column blocks through fp32
+// partials summed in a fixed order by the chain kernel.
+
+#include "common.hpp"
+#include "gdn.hpp"
+
+namespace gdnk {
+
+constexpr int TT = 16;   // tokens per staging block = checkpoint interval
+constexpr int CB = 16;   // value columns per workgroup
+constexpr int RF = 4;    // backward: tokens per flush of the cross-column sums
+constexpr float L2_EPS = 1e-6f;
+constexpr float SP_CUT = 20.0f;
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigm(x); }
+__device__ __forceinline__ float silu_grad(float x) {
+  const float s = sigm(x);
+  return s * (1.0f + x * (1.0f - s));
+}
+__device__ __forceinline__ float softplus(float x) { return x > SP_CUT ? x : log1pf(expf(x)); }
+__device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+
+// ----------------------------------------------------------- convolution --
+// pre[b][t][c] = sum_j raw[b][t - (kk-1) + j][c] conv[c][j] (zero before the
+// window), cq = silu(pre); four channels per thread.
+__global__ __launch_bounds__(256) void conv_fwd(int BT, int T, int cdim, int kk,
+                                                const float* __restrict__ raw,
+                                                const float* __restrict__ conv,
+                                                float* __restrict__ pre, float* __restrict__ cq) {
+  const size_t n4 = (size_t)BT * cdim / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const size_t e = i * 4;
+    const size_t bt = e / cdim;
+    const int c = (int)(e - bt * cdim);
+    const int t = (int)(bt % T);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kk; j++) {
+      const int back = kk - 1 - j;
+      if (t - back < 0) continue;
+      const f4 x = ld4(raw + e - (size_t)back * cdim);
+#pragma unroll
+      for (int m = 0; m < 4; m++) acc[m] = fmaf(x[m], conv[(size_t)(c + m) * kk + j], acc[m]);
+    }
+    st4(pre + e, acc);
+    f4 s;
+#pragma unroll
+    for (int m = 0; m < 4; m++) s[m] = silu(acc[m]);
+    st4(cq + e, s);
+  }
+}
+
+// draw[b][t][c] = sum_j dpre[b][t + (kk-1) - j][c] conv[c][j] over positions
+// inside the window, dpre = dcq silu'(pre).
+__global__ __launch_bounds__(256) void conv_bwd(int BT, int T, int cdim, int kk,
+                                                const float* __restrict__ pre,
+                                                const float* __restrict__ dcq,
+                                                const float* __restrict__ conv,
+                                                float* __restrict__ draw) {
+  const size_t n4 = (size_t)BT * cdim / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const size_t e = i * 4;
+    const size_t bt = e / cdim;
+    const int c = (int)(e - bt * cdim);
+    const int t = (int)(bt % T);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kk; j++) {
+      const int fwd = kk - 1 - j;
+      if (t + fwd >= T) continue;
+      const size_t ef = e + (size_t)fwd * cdim;
+      const f4 p = ld4(pre + ef), d = ld4(dcq + ef);
+#pragma unroll
+      for (int m = 0; m < 4; m++)
+        acc[m] = fmaf(d[m] * silu_grad(p[m]), conv[(size_t)(c + m) * kk + j], acc[m]);
+    }
+    st4(draw + e, acc);
+  }
+}
+
+// --------------------------------------------------- normalised q/k, gates --
+// One 16-lane group per (token, k-head): q^ and k^ (DK/16 values per lane);
+// lanes l < rep also make g and beta of v-head ko * rep + l.
+template <int DK>
+__global__ __launch_bounds__(256) void prep(int BT, int nk, int nv, int cdim,
+                                            const float* __restrict__ cq,
+                                            const float* __restrict__ a,
+                                            const float* __restrict__ bb,
+                                            const float* __restrict__ A_log,
+                                            const float* __restrict__ dt_bias,
+                                            float* __restrict__ qh, float* __restrict__ kh,
+                                            float* __restrict__ g, float* __restrict__ beta) {
+  constexpr int R4 = DK / 64;  // float4 per lane
+  const size_t gid = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= (size_t)BT * nk) return;
+  const size_t bt = gid / nk;
+  const int ko = (int)(gid - bt * nk);
+  const int kd = nk * DK, rep = nv / nk;
+  const float* qr = cq + bt * cdim + (size_t)ko * DK;
+  const float* kr = qr + kd;
+  f4 q[R4], k[R4];
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int m = 0; m < R4; m++) {
+    q[m] = ld4(qr + l16 * 4 + 64 * m);
+    k[m] = ld4(kr + l16 * 4 + 64 * m);
+    sq += (q[m][0] * q[m][0] + q[m][1] * q[m][1]) + (q[m][2] * q[m][2] + q[m][3] * q[m][3]);
+    sk += (k[m][0] * k[m][0] + k[m][1] * k[m][1]) + (k[m][2] * k[m][2] + k[m][3] * k[m][3]);
+  }
+  sq = rowsum16(sq) + L2_EPS;
+  sk = rowsum16(sk) + L2_EPS;
+  const float invq = 1.0f / (sqrtf(sq) * sqrtf((float)DK)), invk = 1.0f / sqrtf(sk);
+  float* qo = qh + gid * DK;
+  float* ko_ = kh + gid * DK;
+#pragma unroll
+  for (int m = 0; m < R4; m++) {
+    st4(qo + l16 * 4 + 64 * m, q[m] * invq);
+    st4(ko_ + l16 * 4 + 64 * m, k[m] * invk);
+  }
+  if (l16 < rep) {
+    const int h = ko * rep + l16;
+    const size_t i = bt * nv + h;
+    g[i] = expf(-expf(A_log[h]) * softplus(a[i] + dt_bias[h]));
+    beta[i] = sigm(bb[i]);
+  }
+}
+
+// ------------------------------------------------------ gated RMSNorm --
+// One 16-lane group per (token, v-head): out = o inv norm silu(z),
+// inv = 1 / sqrt(mean(o^2) + eps).  dv = 64 * NV4.
+template <int NV4>
+__global__ __launch_bounds__(256) void rms_fwd(int BTH, int nv, float eps,
+                                               const float* __restrict__ o,
+                                               const float* __restrict__ z,
+                                               const float* __restrict__ norm,
+                                               float* __restrict__ out) {
+  constexpr int DV = 64 * NV4;
+  const size_t gid = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= (size_t)BTH) return;
+  const size_t base = gid * DV;
+  f4 ov[NV4];
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < NV4; m++) {
+    ov[m] = ld4(o + base + l16 * 4 + 64 * m);
+    s += (ov[m][0] * ov[m][0] + ov[m][1] * ov[m][1]) + (ov[m][2] * ov[m][2] + ov[m][3] * ov[m][3]);
+  }
+  const float inv = 1.0f / sqrtf(rowsum16(s) / DV + eps);
+#pragma unroll
+  for (int m = 0; m < NV4; m++) {
+    const int j = l16 * 4 + 64 * m;
+    const f4 zz = ld4(z + base + j), w = ld4(norm + j);
+    f4 r;
+#pragma unroll
+    for (int c = 0; c < 4; c++) r[c] = ov[m][c] * inv * w[c] * silu(zz[c]);
+    st4(out + base + j, r);
+  }
+}
+
+// dz = dout o inv norm silu'(z);  do = inv w_eff dout - o inv^3 mean(dout w_eff o),
+// w_eff = norm silu(z).
+template <int NV4>
+__global__ __launch_bounds__(256) void rms_bwd(int BTH, int nv, float eps,
+                                               const float* __restrict__ o,
+                                               const float* __restrict__ z,
+                                               const float* __restrict__ norm,
+                                               const float* __restrict__ dout,
+                                               float* __restrict__ dz, float* __restrict__ dobuf) {
+  constexpr int DV = 64 * NV4;
+  const size_t gid = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= (size_t)BTH) return;
+  const size_t base = gid * DV;
+  f4 ov[NV4], dv4[NV4], zz[NV4];
+  float s = 0.f, sd = 0.f;
+#pragma unroll
+  for (int m = 0; m < NV4; m++) {
+    const int j = l16 * 4 + 64 * m;
+    ov[m] = ld4(o + base + j);
+    dv4[m] = ld4(dout + base + j);
+    zz[m] = ld4(z + base + j);
+    const f4 w = ld4(norm + j);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      s += ov[m][c] * ov[m][c];
+      sd += dv4[m][c] * w[c] * silu(zz[m][c]) * ov[m][c];
+    }
+  }
+  const float inv = 1.0f / sqrtf(rowsum16(s) / DV + eps);
+  const float coef = rowsum16(sd) / DV * inv * inv * inv;
+#pragma unroll
+  for (int m = 0; m < NV4; m++) {
+    const int j = l16 * 4 + 64 * m;
+    const f4 w = ld4(norm + j);
+    f4 dzz, d;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      dzz[c] = dv4[m][c] * ov[m][c] * inv * w[c] * silu_grad(zz[m][c]);
+      d[c] = inv * w[c] * silu(zz[m][c]) * dv4[m][c] - ov[m][c] * coef;
+    }
+    st4(dz + base + j, dzz);
+    st4(dobuf + base + j, d);
+  }
+}
+
+// ------------------------------------------------------------ recurrence --
+// Workgroup (b, h, column block), 256 threads: column cl = tid / 16 of the
+// block (one DPP row), row group rg = tid % 16 owning key rows
+// rg * RPL .. rg * RPL + RPL - 1.  Block inputs staged in LDS; a partial
+// last block is padded with identity tokens (g = 1, beta = 0, k^ = q^ = 0).
+template <int DK>
+struct Stage {
+  float k[2][TT][DK];
+  float q[2][TT][DK];
+  float v[2][TT][CB];
+  float d[2][TT][CB];  // do (backward only)
+  float g[2][TT];
+  float b[2][TT];
+};
+
+template <int DK>
+__device__ __forceinline__ void stage_block(Stage<DK>& st, int buf, int t0, int T, int nv, int dv,
+                                            int cdim, int kvoff, size_t bT, int h, int ko,
+                                            int col0, const float* qh, const float* kh,
+                                            const float* cq, const float* gg, const float* be,
+                                            const float* dob, bool with_do, int nk) {
+  // k^, q^: TT * DK floats each, float4 per thread slot
+  constexpr int NQ4 = TT * DK / 4;
+  const int tid = threadIdx.x;
+  for (int f = tid; f < 2 * NQ4; f += 256) {
+    const int which = f / NQ4, r = f - which * NQ4, tok = r / (DK / 4), c4 = r - tok * (DK / 4);
+    const int t = t0 + tok;
+    f4 x = {0.f, 0.f, 0.f, 0.f};
+    if (t < T) x = ld4((which ? qh : kh) + ((bT + t) * nk + ko) * DK + c4 * 4);
+    st4(which ? &st.q[buf][tok][c4 * 4] : &st.k[buf][tok][c4 * 4], x);
+  }
+  for (int f = tid; f < TT * CB; f += 256) {
+    const int tok = f / CB, c = f - tok * CB, t = t0 + tok;
+    st.v[buf][tok][c] = t < T ? cq[(bT + t) * cdim + kvoff + (size_t)h * dv + col0 + c] : 0.f;
+    if (with_do) st.d[buf][tok][c] = t < T ? dob[((bT + t) * nv + h) * dv + col0 + c] : 0.f;
+  }
+  if (tid < TT) {
+    const int t = t0 + tid;
+    st.g[buf][tid] = t < T ? gg[(bT + t) * nv + h] : 1.f;
+    st.b[buf][tid] = t < T ? be[(bT + t) * nv + h] : 0.f;
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int dv, int cdim,
+                                               const float* __restrict__ qh,
+                                               const float* __restrict__ kh,
+                                               const float* __restrict__ cq,
+                                               const float* __restrict__ gg,
+                                               const float* __restrict__ be,
+                                               float* __restrict__ o, float* __restrict__ ckpt) {
+  constexpr int RPL = DK / 16;
+  __shared__ __attribute__((aligned(16))) Stage<DK> st;
+  const int ncb = dv / CB;
+  const int g_ = blockIdx.x;
+  const int bh = g_ / ncb, cb = g_ - bh * ncb;
+  const int b = bh / nv, h = bh - b * nv, ko = h / (nv / nk);
+  const int tid = threadIdx.x, rg = tid & 15, cl = tid >> 4;
+  const int col0 = cb * CB, col = col0 + cl;
+  const size_t bT = (size_t)b * T;
+  const int kvoff = 2 * nk * DK;
+  const int nblk = (T + TT - 1) / TT;
+  float s[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; i++) s[i] = 0.f;
+  stage_block<DK>(st, 0, 0, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be, nullptr,
+                  false, nk);
+  __syncthreads();
+  int buf = 0;
+  for (int blk = 0; blk < nblk; blk++, buf ^= 1) {
+    const int t0 = blk * TT;
+    if (ckpt) {
+      float* cp = ckpt + (((size_t)bh * nblk + blk) * dv + col) * DK + rg * RPL;
+#pragma unroll
+      for (int i = 0; i < RPL; i += 4) st4(cp + i, f4{s[i], s[i + 1], s[i + 2], s[i + 3]});
+    }
+    float ob = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+      const float gt = st.g[buf][tt], bt_ = st.b[buf][tt], vt = st.v[buf][tt][cl];
+      float kr[RPL], qr[RPL];
+#pragma unroll
+      for (int i = 0; i < RPL; i += 4) {
+        const f4 x = ld4(&st.k[buf][tt][rg * RPL + i]), y = ld4(&st.q[buf][tt][rg * RPL + i]);
+        kr[i] = x[0]; kr[i + 1] = x[1]; kr[i + 2] = x[2]; kr[i + 3] = x[3];
+        qr[i] = y[0]; qr[i + 1] = y[1]; qr[i + 2] = y[2]; qr[i + 3] = y[3];
+      }
+      float kv = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        s[i] *= gt;
+        kv = fmaf(s[i], kr[i], kv);
+      }
+      kv = rowsum16(kv);
+      const float u = bt_ * (vt - kv);
+      float ov = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        s[i] = fmaf(kr[i], u, s[i]);
+        ov = fmaf(s[i], qr[i], ov);
+      }
+      ov = rowsum16(ov);
+      ob = rg == tt ? ov : ob;
+    }
+    if (t0 + rg < T) o[((bT + t0 + rg) * nv + h) * dv + col] = ob;
+    __syncthreads();  // every wave is done with the other buffer's previous block
+    if (blk + 1 < nblk) {
+      stage_block<DK>(st, buf ^ 1, t0 + TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq,
+                      gg, be, nullptr, false, nk);
+      __syncthreads();
+    }
+  }
+}
+
+// Partials per (column block, b, t, h): [0, DK) dq^, [DK, 2 DK) dk^, 2 DK dg,
+// 2 DK + 1 dbeta (sums over the block's 16 columns).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int dv, int cdim,
+                                               const float* __restrict__ qh,
+                                               const float* __restrict__ kh,
+                                               const float* __restrict__ cq,
+                                               const float* __restrict__ gg,
+                                               const float* __restrict__ be,
+                                               const float* __restrict__ dob,
+                                               const float* __restrict__ ckpt,
+                                               float* __restrict__ part, float* __restrict__ dcq) {
+  constexpr int RPL = DK / 16, PW = 2 * DK + 2;
+  __shared__ __attribute__((aligned(16))) Stage<DK> st;
+  // cross-column sums of RF tokens (flushed to the partials every RF tokens,
+  // so the LDS of two workgroups fits one CU)
+  __shared__ __attribute__((aligned(16))) float red[4][RF][PW];
+  const int ncb = dv / CB;
+  const int g_ = blockIdx.x;
+  const int bh = g_ / ncb, cb = g_ - bh * ncb;
+  const int b = bh / nv, h = bh - b * nv, ko = h / (nv / nk);
+  const int tid = threadIdx.x, rg = tid & 15, cl = tid >> 4, lane = tid & 63, wave = tid >> 6;
+  const int col0 = cb * CB, col = col0 + cl;
+  const size_t bT = (size_t)b * T;
+  const int kvoff = 2 * nk * DK;
+  const int nblk = (T + TT - 1) / TT;
+  const size_t pstride = (size_t)B * T * nv * PW;  // one column block's partials
+
+  float G[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; i++) G[i] = 0.f;
+  int buf = 0;
+  stage_block<DK>(st, 0, (nblk - 1) * TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg,
+                  be, dob, true, nk);
+  __syncthreads();
+  for (int blk = nblk - 1; blk >= 0; blk--, buf ^= 1) {
+    const int t0 = blk * TT;
+    // recompute: Sh[tt] = state before token tt, kvh[tt] = S_pre^T k^ (this column)
+    float Sh[TT + 1][RPL], kvh[TT];
+    const float* cp = ckpt + (((size_t)bh * nblk + blk) * dv + col) * DK + rg * RPL;
+#pragma unroll
+    for (int i = 0; i < RPL; i += 4) {
+      const f4 x = ld4(cp + i);
+      Sh[0][i] = x[0]; Sh[0][i + 1] = x[1]; Sh[0][i + 2] = x[2]; Sh[0][i + 3] = x[3];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+      const float gt = st.g[buf][tt], bt_ = st.b[buf][tt], vt = st.v[buf][tt][cl];
+      float kv = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) kv = fmaf(Sh[tt][i] * gt, st.k[buf][tt][rg * RPL + i], kv);
+      kv = rowsum16(kv);
+      kvh[tt] = kv;
+      const float u = bt_ * (vt - kv);
+#pragma unroll
+      for (int i = 0; i < RPL; i++) Sh[tt + 1][i] = fmaf(st.k[buf][tt][rg * RPL + i], u, Sh[tt][i] * gt);
+    }
+    float dvb = 0.f;
+#pragma unroll
+    for (int tt = TT - 1; tt >= 0; tt--) {
+      const float gt = st.g[buf][tt], bt_ = st.b[buf][tt], vt = st.v[buf][tt][cl];
+      const float dot = st.d[buf][tt][cl];
+      float kr[RPL], qr[RPL];
+#pragma unroll
+      for (int i = 0; i < RPL; i += 4) {
+        const f4 x = ld4(&st.k[buf][tt][rg * RPL + i]), y = ld4(&st.q[buf][tt][rg * RPL + i]);
+        kr[i] = x[0]; kr[i + 1] = x[1]; kr[i + 2] = x[2]; kr[i + 3] = x[3];
+        qr[i] = y[0]; qr[i + 1] = y[1]; qr[i + 2] = y[2]; qr[i + 3] = y[3];
+      }
+      // o = S_t^T q^: G += q^ do; dq^ += S_t do
+      float pq[RPL], pk[RPL];
+      float du = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        G[i] = fmaf(qr[i], dot, G[i]);
+        pq[i] = Sh[tt + 1][i] * dot;
+        du = fmaf(G[i], kr[i], du);
+      }
+      du = rowsum16(du);
+      // S_t = S_pre + k^ u^T, u = beta (v - kv)
+      const float vmk = vt - kvh[tt];
+      const float u = bt_ * vmk;
+      const float dkv = -bt_ * du;
+      dvb = rg == tt ? bt_ * du : dvb;
+      float dgp = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        const float dsp = fmaf(kr[i], dkv, G[i]);                 // dS_pre
+        pk[i] = fmaf(gt * Sh[tt][i], dkv, G[i] * u);               // dS u + S_pre dkv
+        dgp = fmaf(dsp, Sh[tt][i], dgp);
+        G[i] = gt * dsp;
+      }
+      dgp = rowsum16(dgp);
+      // sums over the wave's four columns (lanes l, l^16, l^32, l^48)
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        pq[i] = rows4sum(pq[i]);
+        pk[i] = rows4sum(pk[i]);
+      }
+      const float sg = rows4sum(dgp), sb = rows4sum(du * vmk);
+      const int slot = tt % RF;
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < RPL; i += 4) {
+          st4(&red[wave][slot][rg * RPL + i], f4{pq[i], pq[i + 1], pq[i + 2], pq[i + 3]});
+          st4(&red[wave][slot][DK + rg * RPL + i], f4{pk[i], pk[i + 1], pk[i + 2], pk[i + 3]});
+        }
+        if (lane == 0) {
+          red[wave][slot][2 * DK] = sg;
+          red[wave][slot][2 * DK + 1] = sb;
+        }
+      }
+      if (slot == 0) {  // tokens tt .. tt + RF - 1 complete: sum the four waves
+        lds_barrier();
+        for (int f = tid; f < RF * PW; f += 256) {
+          const int k = f / PW, c = f - k * PW, t = t0 + tt + k;
+          if (t < T) {
+            const float v = (red[0][k][c] + red[1][k][c]) + (red[2][k][c] + red[3][k][c]);
+            part[cb * pstride + ((bT + t) * nv + h) * PW + c] = v;
+          }
+        }
+        lds_barrier();  // red consumed before the next tokens write it
+      }
+    }
+    if (t0 + rg < T) dcq[(bT + t0 + rg) * cdim + kvoff + (size_t)h * dv + col] = dvb;
+    if (blk > 0)
+      stage_block<DK>(st, buf ^ 1, t0 - TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg,
+                      be, dob, true, nk);
+    __syncthreads();  // red consumed; the next block's staging visible
+  }
+}
+
+// Sums the partials (column blocks, then the rep v-heads of the k-head, in
+// fixed order) and applies the chain rule of the normalisations and gates:
+// one 16-lane group per (token, k-head).
+//   dq = invq dq^ - q (dq^.q) invq / (|q|^2 + eps), likewise dk;
+//   da = dg g (-exp(A_log)) sigmoid(a + dt_bias);  db = dbeta beta (1 - beta)
+template <int DK>
+__global__ __launch_bounds__(256) void chain(int B, int T, int nk, int nv, int ncb, int cdim,
+                                             const float* __restrict__ part,
+                                             const float* __restrict__ cq,
+                                             const float* __restrict__ a,
+                                             const float* __restrict__ A_log,
+                                             const float* __restrict__ dt_bias,
+                                             const float* __restrict__ gg,
+                                             const float* __restrict__ be,
+                                             float* __restrict__ dcq, float* __restrict__ da,
+                                             float* __restrict__ db) {
+  constexpr int R4 = DK / 64, PW = 2 * DK + 2;
+  const size_t BT = (size_t)B * T;
+  const size_t gid = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
+  if (gid >= BT * nk) return;
+  const size_t bt = gid / nk;
+  const int ko = (int)(gid - bt * nk);
+  const int rep = nv / nk, kd = nk * DK;
+  const size_t pstride = BT * nv * PW;
+  f4 dq[R4], dk[R4];
+#pragma unroll
+  for (int m = 0; m < R4; m++) dq[m] = dk[m] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < rep; r++) {
+    const int h = ko * rep + r;
+    float sgd = 0.f, sbd = 0.f;
+    for (int c = 0; c < ncb; c++) {
+      const float* p = part + c * pstride + (bt * nv + h) * PW;
+#pragma unroll
+      for (int m = 0; m < R4; m++) {
+        dq[m] += ld4(p + l16 * 4 + 64 * m);
+        dk[m] += ld4(p + DK + l16 * 4 + 64 * m);
+      }
+      sgd += p[2 * DK];
+      sbd += p[2 * DK + 1];
+    }
+    if (l16 == 0) {
+      const size_t i = bt * nv + h;
+      const float gt = gg[i], bt_ = be[i];
+      da[i] = sgd * gt * (-expf(A_log[h])) * sigm(a[i] + dt_bias[h]);
+      db[i] = sbd * bt_ * (1.0f - bt_);
+    }
+  }
+  const float* qr = cq + bt * cdim + (size_t)ko * DK;
+  const float* kr = qr + kd;
+  f4 q[R4], k[R4];
+  float sq = 0.f, sk = 0.f, pq = 0.f, pk = 0.f;
+#pragma unroll
+  for (int m = 0; m < R4; m++) {
+    q[m] = ld4(qr + l16 * 4 + 64 * m);
+    k[m] = ld4(kr + l16 * 4 + 64 * m);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      sq += q[m][c] * q[m][c];
+      sk += k[m][c] * k[m][c];
+      pq += dq[m][c] * q[m][c];
+      pk += dk[m][c] * k[m][c];
+    }
+  }
+  const float nq2 = rowsum16(sq) + L2_EPS, nk2 = rowsum16(sk) + L2_EPS;
+  pq = rowsum16(pq);
+  pk = rowsum16(pk);
+  const float invq = 1.0f / (sqrtf(nq2) * sqrtf((float)DK)), invk = 1.0f / sqrtf(nk2);
+  const float cqf = pq * invq / nq2, ckf = pk * invk / nk2;
+  float* dqo = dcq + bt * cdim + (size_t)ko * DK;
+  float* dko = dqo + kd;
+#pragma unroll
+  for (int m = 0; m < R4; m++) {
+    st4(dqo + l16 * 4 + 64 * m, invq * dq[m] - q[m] * cqf);
+    st4(dko + l16 * 4 + 64 * m, invk * dk[m] - k[m] * ckf);
+  }
+}
+
+}  // namespace gdnk
+
+// ------------------------------------------------------------- launchers --
+static unsigned grid4(size_t n4) {
+  size_t b = (n4 + 255) / 256;
+  return (unsigned)(b > 8192 ? 8192 : (b < 1 ? 1 : b));
+}
+
+size_t gdn_ckpt_floats(int B, int T, int nv, int dk, int dv) {
+  return (size_t)B * nv * ((T + gdnk::TT - 1) / gdnk::TT) * dv * dk;
+}
+size_t gdn_partial_floats(int B, int T, int nv, int dk, int dv) {
+  return (size_t)(dv / gdnk::CB) * B * T * nv * (2 * dk + 2);
+}
+
+hipError_t gdn_launch_forward(const GdnArgs& p, hipStream_t st) {
+  const int BT = p.B * p.T, cdim = 2 * p.nk * p.dk + p.nv * p.dv;
+  hipLaunchKernelGGL(gdnk::conv_fwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT, p.T,
+                     cdim, p.kk, p.raw, p.conv, p.pre, p.cq);
+  const unsigned gq = (unsigned)(((size_t)BT * p.nk + 15) / 16);
+  if (p.dk == 128)
+    hipLaunchKernelGGL(gdnk::prep<128>, dim3(gq), dim3(256), 0, st, BT, p.nk, p.nv, cdim, p.cq,
+                       p.a, p.b, p.A_log, p.dt_bias, p.qh, p.kh, p.g, p.beta);
+  else
+    hipLaunchKernelGGL(gdnk::prep<64>, dim3(gq), dim3(256), 0, st, BT, p.nk, p.nv, cdim, p.cq, p.a,
+                       p.b, p.A_log, p.dt_bias, p.qh, p.kh, p.g, p.beta);
+  const dim3 gs(p.B * p.nv * (p.dv / gdnk::CB));
+  if (p.dk == 128)
+    hipLaunchKernelGGL(gdnk::fwd_seq<128>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt);
+  else
+    hipLaunchKernelGGL(gdnk::fwd_seq<64>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt);
+  const int BTH = BT * p.nv;
+  const unsigned gr = (unsigned)(((size_t)BTH + 15) / 16);
+  if (p.dv == 128)
+    hipLaunchKernelGGL(gdnk::rms_fwd<2>, dim3(gr), dim3(256), 0, st, BTH, p.nv, p.rms_eps, p.o,
+                       p.z, p.norm, p.out);
+  else
+    hipLaunchKernelGGL(gdnk::rms_fwd<1>, dim3(gr), dim3(256), 0, st, BTH, p.nv, p.rms_eps, p.o,
+                       p.z, p.norm, p.out);
+  return hipGetLastError();
+}
+
+hipError_t gdn_launch_backward(const GdnArgs& p, hipStream_t st) {
+  const int BT = p.B * p.T, cdim = 2 * p.nk * p.dk + p.nv * p.dv;
+  const int BTH = BT * p.nv;
+  const unsigned gr = (unsigned)(((size_t)BTH + 15) / 16);
+  if (p.dv == 128)
+    hipLaunchKernelGGL(gdnk::rms_bwd<2>, dim3(gr), dim3(256), 0, st, BTH, p.nv, p.rms_eps, p.o,
+                       p.z, p.norm, p.dout, p.dz, p.dobuf);
+  else
+    hipLaunchKernelGGL(gdnk::rms_bwd<1>, dim3(gr), dim3(256), 0, st, BTH, p.nv, p.rms_eps, p.o,
+                       p.z, p.norm, p.dout, p.dz, p.dobuf);
+  const dim3 gs(p.B * p.nv * (p.dv / gdnk::CB));
+  if (p.dk == 128)
+    hipLaunchKernelGGL(gdnk::bwd_seq<128>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.part, p.dcq);
+  else
+    hipLaunchKernelGGL(gdnk::bwd_seq<64>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.part, p.dcq);
+  const unsigned gq = (unsigned)(((size_t)BT * p.nk + 15) / 16);
+  const int ncb = p.dv / gdnk::CB;
+  if (p.dk == 128)
+    hipLaunchKernelGGL(gdnk::chain<128>, dim3(gq), dim3(256), 0, st, p.B, p.T, p.nk, p.nv, ncb,
+                       cdim, p.part, p.cq, p.a, p.A_log, p.dt_bias, p.g, p.beta, p.dcq, p.da,
+                       p.db);
+  else
+    hipLaunchKernelGGL(gdnk::chain<64>, dim3(gq), dim3(256), 0, st, p.B, p.T, p.nk, p.nv, ncb, cdim,
+                       p.part, p.cq, p.a, p.A_log, p.dt_bias, p.g, p.beta, p.dcq, p.da, p.db);
+  hipLaunchKernelGGL(gdnk::conv_bwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT, p.T,
+                     cdim, p.kk, p.pre, p.dcq, p.conv, p.draw);
+  return hipGetLastError();
+}

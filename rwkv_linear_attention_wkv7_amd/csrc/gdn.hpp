@@ -1,0 +1,23 @@
+// Launch arguments of the GatedDeltaNet kernels (gdn.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+struct GdnArgs {
+  int B, T, nk, nv, dk, dv, kk;
+  float rms_eps;
+  // inputs and frozen weights
+  const float *raw, *z, *a, *b, *conv, *A_log, *dt_bias, *norm;
+  // forward activations (the cache): pre and cq [B][T][c_dim], qh and kh
+  // [B][T][nk][dk], g and beta [B][T][nv], o [B][T][nv][dv], ckpt
+  // [B][nv][ceil(T/16)][dv][dk]
+  float *pre, *cq, *qh, *kh, *g, *beta, *o, *ckpt;
+  float* out;  // [B][T][nv][dv]
+  // backward
+  const float* dout;
+  float *dz, *dobuf, *dcq, *part, *draw, *da, *db;
+};
+
+size_t gdn_ckpt_floats(int B, int T, int nv, int dk, int dv);
+size_t gdn_partial_floats(int B, int T, int nv, int dk, int dv);
+hipError_t gdn_launch_forward(const GdnArgs& p, hipStream_t st);
+hipError_t gdn_launch_backward(const GdnArgs& p, hipStream_t st);
