@@ -176,18 +176,25 @@ def cross_entropy(logits, targets):
     return loss, (p / n if n else p)
 
 
-def train_step(model, cfg, tokens, targets, gemm="f64"):
-    """Loss and gradients of every parameter for one batch (zero initial state).
+def train_step(model, cfg, tokens, targets, gemm="f64", state=None):
+    """Loss and gradients of every parameter for one batch.
 
     Returns (loss, grads) with grads mirroring the model dict (blocks[l]['tm']
     holds the time-mix gradients).  gemm: operand precision of every
     projection, LoRA, channel-mix and head product ("f64" or "bf16", see
-    oracle.precision).
+    oracle.precision).  state: None (zero initial state) or a streaming state
+    (init_state layout) the batch starts from; the gradients stop at it
+    (truncated backpropagation through time: the state is an input, not a
+    function of the parameters).
     """
     m = _f64(model)
     tokens = np.asarray(tokens)
     B, T = tokens.shape
     H = cfg["H"]
+    st = None if state is None else {k: np.asarray(v, np.float64) for k, v in state.items()}
+    xp_tm = lambda l: None if st is None else st["att_x_prev"][l]
+    s0_tm = lambda l: None if st is None else st["att_state"][l]
+    xp_cm = lambda l: None if st is None else st["ffn_x_prev"][l]
     x = embed(m["emb"], tokens)
     use_ln0 = m.get("ln0_w") is not None
     x_emb = x
@@ -197,12 +204,14 @@ def train_step(model, cfg, tokens, targets, gemm="f64"):
     v_first = None
     for l, bp in enumerate(m["blocks"]):
         h1 = layernorm(x, bp["ln1_w"], bp["ln1_b"])
-        out, c = tm.forward(bp["tm"], h1, H, l, v_first=v_first, gemm=gemm)
+        out, c = tm.forward(bp["tm"], h1, H, l, x_prev=xp_tm(l), v_first=v_first, s0=s0_tm(l),
+                            gemm=gemm)
         if l == 0:
             v_first = c["v_first"]
         x1 = x + out
         h2 = layernorm(x1, bp["ln2_w"], bp["ln2_b"])
-        x = x1 + channel_mix(bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], h2, gemm=gemm)
+        x = x1 + channel_mix(bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], h2, x_prev=xp_cm(l),
+                             gemm=gemm)
         caches.append(dict(h1=h1, c=c, x1=x1, h2=h2))
         xs.append(x)
     hN = layernorm(x, m["ln_out_w"], m["ln_out_b"])
@@ -216,7 +225,7 @@ def train_step(model, cfg, tokens, targets, gemm="f64"):
         bp, cc = m["blocks"][l], caches[l]
         gb = {}
         dh2, _, gb["cm_mu_k"], gb["cm_Wk"], gb["cm_Wv"] = channel_mix_backward(
-            bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], cc["h2"], dx, gemm=gemm)
+            bp["cm_mu_k"], bp["cm_Wk"], bp["cm_Wv"], cc["h2"], dx, x_prev=xp_cm(l), gemm=gemm)
         d1, gb["ln2_w"], gb["ln2_b"] = layernorm_backward(cc["x1"], bp["ln2_w"], dh2)
         dx1 = dx + d1
         gt, dh1, _, dvf_out, _ = tm.backward(bp["tm"], cc["c"], dx1,
