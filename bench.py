@@ -16,6 +16,10 @@ the headline alone.  Workloads:
              LoRA ranks w/a/v/g = 64/64/32/128, layer > 0, fp32 (tokens/s)
   wkv7_long  WKV7 forward+backward, B=4 T=8192 H=32 N=64, bf16 token
              tensors, fp32 state, checkpointed backward (tokens/s)
+  online     online TBPTT training segments on the decode model (12 layers,
+             C=256, vocab 256): 256 streams x 64 steps from their live state,
+             backward through the segment, Adam update, live-state replay,
+             fp32 (tokens/s)
   gdn        GatedDeltaNet layer forward + through-gradient backward, B=2
              windows of T=4096, 16 key heads / 32 value heads of size 128,
              4 causal conv taps, fp32 (tokens/s)
@@ -449,6 +453,74 @@ def setup_gdn():
                 cpu=cpu)
 
 
+def setup_online():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    L, C, H, F, V, B, S = 12, 256, 4, 1024, 256, 256, 64
+    ranks = (32, 32, 32, 64)
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=0)
+    dev = torch.device("cuda")
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    w = {k: d(v) for k, v in m.items() if k != "blocks"}
+    w["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
+                    for k, v in b.items()} for b in m["blocks"]]
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=1), w)
+    grads = binding.TrainGrads(dm)
+    am, av = binding.TrainGrads(dm, zero=True), binding.TrainGrads(dm, zero=True)
+    nseg = 8
+    tok = synth.token_ids(B, nseg * S + 1, V, seed=0, name="online_tokens")
+    seg = lambda a, j: torch.from_numpy(np.ascontiguousarray(a[:, j * S:(j + 1) * S])).to(dev)
+    xs = [seg(tok[:, :-1], j) for j in range(nseg)]
+    ys = [seg(tok[:, 1:], j) for j in range(nseg)]
+    state = dm.new_state(B)
+    loss = torch.empty(1, device=dev)
+    ws = torch.empty(binding.rwkv7_online_workspace_bytes(dm, B, S), dtype=torch.uint8, device=dev)
+    pos = [0]
+
+    def step():
+        j = pos[0] % nseg
+        t_ = pos[0] + 1
+        binding.rwkv7_online_segment(dm, grads, xs[j], ys[j], state, optimizer="adam", lr=1e-4,
+                                     step=t_, adam_m=am, adam_v=av, loss=loss, ws=ws)
+        pos[0] += 1
+
+    # dominant products: the fp32 channel-mix key GEMM of the segment,
+    # [B*S][256] . [256][1024]
+    A = torch.randn(B * S, C, device=dev)
+    Wk = w["blocks"][0]["cm_Wk"]
+    out = torch.empty(B * S, F, device=dev)
+
+    def dom():
+        binding.wkv7_gemm_f32(A, Wk, out)
+
+    roof = dict(kernel="gemm_f32 (X[16384][256] . Wk[256][1024])", bound="mfma",
+                work=2.0 * B * S * C * F, unit="TFLOP/s", peak=PEAK["mfma_fp32"][0], fn=dom,
+                key="gemm_f32_online", src=["rwkv_linear_attention_wkv7_amd/csrc/gemm.hip"])
+
+    def cpu():
+        from oracle import online, stack
+        from oracle import wkv7 as ow
+        ns = 4
+        ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
+        st0 = stack.init_state(ocfg, ns)
+        t0 = time.perf_counter()
+        online.train_segment(m, ocfg, tok[:ns, :S], tok[:ns, 1:S + 1], st0, "adam", lr=1e-4)
+        dt = time.perf_counter() - t0
+        return dict(value=ns * S / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"one segment of {ns} of the {B} streams x {S} steps (f64 gradients, "
+                           f"Adam update, replay), {dt:.1f} s; streams are independent")
+
+    cfgd = {"workload": "online TBPTT training segments on the 12-layer decode model",
+            "n_layer": L, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
+            "lora_ranks_w_a_v_g": list(ranks), "streams": B, "segment_steps": S,
+            "optimizer": "Adam (lr 1e-4)", "global_batch": B, "seq_len": S,
+            "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * S, unit="tokens/s", dtype="f32", config=cfgd, roof=roof,
+                cpu=cpu, extra=lambda v, ms: {"loss": round(float(loss.item()), 5)})
+
+
 def ctypes_byref(x):
     import ctypes
     return ctypes.byref(x)
@@ -456,8 +528,9 @@ def ctypes_byref(x):
 
 WORKLOADS = {"wkv7_small": setup_wkv7_small, "decode": setup_decode, "timemix": setup_timemix,
              "wkv7_long": setup_wkv7_long, "train": setup_train, "gdn": setup_gdn,
+             "online": setup_online,
              "wkv7_long_chunked": lambda: setup_wkv7_long(chunked=True)}
-ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train", "gdn")
+ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train", "online", "gdn")
 
 
 def run_workload(name, steps, warmup, roof_iters, with_cpu):

@@ -366,6 +366,50 @@ int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
                      const int *targets, float *loss, void *ws, size_t ws_bytes,
                      const wkv7_side *side, hipStream_t stream);
 
+/* --------------------------------------------- online TBPTT training -- */
+
+/* Optimiser of rwkv7_online_segment.  optimizer 0: SGD, p -= lr clip(g);
+ * 1: Adam (b1 = 0.9, b2 = 0.999, eps = 1e-8), m = b1 m + (1 - b1) clip(g),
+ * v = b2 v + (1 - b2) clip(g)^2, p -= lr (m / (1 - b1^step)) /
+ * (sqrt(v / (1 - b2^step)) + eps), with step the index of this update (1 for
+ * the first).  clip > 0 clamps every gradient element to [-clip, clip];
+ * clip = 0 leaves them. */
+typedef struct {
+  int optimizer;
+  float lr, clip;
+  int step;
+} rwkv7_optim;
+
+size_t rwkv7_online_workspace_bytes(const rwkv7_config *cfg, int B, int S);
+
+/*
+ * One online training segment for B streams of S (token, target) steps
+ * starting from the streams' live decode state.  Page: "infotheory
+ * .../rwkvzip/rwkv7/model.rs", online_train_segment_tbptt (checkpointed
+ * forward, reverse replay carrying the recurrent gradient, update, live-state
+ * replay) and apply_full_gradients (SGD / Adam, AdamStep constants):
+ *   1. loss and gradients of the mean next-token cross-entropy over the B*S
+ *      steps, backpropagated through the segment and truncated at its start
+ *      (the start state is an input); written into `grads`;
+ *   2. every parameter updated in place (the weights the model's pointers
+ *      address are written, though the struct declares them const) with the
+ *      optimiser `opt`; Adam reads and writes the moment mirrors adam_m and
+ *      adam_v (zero before the first update; NULL for SGD);
+ *   3. the segment replayed from the start state with the updated weights;
+ *      att_x_prev, att_state, ffn_x_prev (layout of rwkv7_decode_step) hold
+ *      the start state on entry and the new live state on return.
+ * The page replays its checkpointed chunks one at a time to bound memory;
+ * the gradient is the same, and here the whole segment's activations live in
+ * the workspace.  Token ids and targets as in rwkv7_train_step.
+ * side: as in rwkv7_train_step.
+ */
+int rwkv7_online_segment(const rwkv7_config *cfg, const rwkv7_model *model,
+                         rwkv7_model_grads *grads, rwkv7_model_grads *adam_m,
+                         rwkv7_model_grads *adam_v, const rwkv7_optim *opt, int B, int S,
+                         const int *tokens, const int *targets, float *att_x_prev,
+                         float *att_state, float *ffn_x_prev, float *loss, void *ws,
+                         size_t ws_bytes, const wkv7_side *side, hipStream_t stream);
+
 /* -------------------------------------------------- GatedDeltaNet layer -- */
 
 /* Geometry of one GatedDeltaNet layer: nk key heads of size dk, nv value

@@ -68,6 +68,11 @@ class GdnWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("conv", "A_log", "dt_bias", "norm")]
 
 
+class Rwkv7Optim(ctypes.Structure):
+    _fields_ = [("optimizer", ctypes.c_int), ("lr", ctypes.c_float), ("clip", ctypes.c_float),
+                ("step", ctypes.c_int)]
+
+
 class Wkv7Side(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("ev", ctypes.c_void_p * 4)]
 
@@ -136,6 +141,13 @@ def lib():
         L.gdn_forward.restype = _i
         L.gdn_backward.argtypes = [gp, gw, _i, _i] + [_vp] * 11 + [_sz, _vp]
         L.gdn_backward.restype = _i
+        L.rwkv7_online_workspace_bytes.argtypes = [cp, _i, _i]
+        L.rwkv7_online_workspace_bytes.restype = _sz
+        mg = ctypes.POINTER(Rwkv7ModelGrads)
+        L.rwkv7_online_segment.argtypes = ([cp, ctypes.POINTER(Rwkv7Model), mg, mg, mg,
+                                            ctypes.POINTER(Rwkv7Optim), _i, _i] + [_vp] * 7 +
+                                           [_sz, _vp, _vp])
+        L.rwkv7_online_segment.restype = _i
         L.wkv7_side_create.argtypes = [ctypes.POINTER(Wkv7Side)]
         L.wkv7_side_create.restype = _i
         L.wkv7_side_destroy.argtypes = [ctypes.POINTER(Wkv7Side)]
@@ -521,19 +533,21 @@ def rwkv7_decode_step(dm, tokens, state, logits=None, ws=None, side=True):
 
 # ---------------------------------------------------------- training step --
 class TrainGrads:
-    """Device gradient buffers mirroring a DecodeModel's weights (torch.empty)."""
+    """Device buffers mirroring a DecodeModel's weights (torch.empty, or zeros
+    with zero=True: the Adam moments of rwkv7_online_segment)."""
 
-    def __init__(self, dm):
+    def __init__(self, dm, zero=False):
         c = dm.cfg
         dev = dm.w["emb"].device
-        e = lambda t: None if t is None else torch.empty_like(t)
+        mk = torch.zeros_like if zero else torch.empty_like
+        e = lambda t: None if t is None else mk(t)
         w = dm.w
         self.g = {k: e(w.get(k)) for k in ("emb", "head", "ln_out_w", "ln_out_b", "ln0_w", "ln0_b")}
         self.g["blocks"] = []
         blocks = (Rwkv7BlockGrads * c.n_layer)()
         for l, bw in enumerate(w["blocks"]):
-            gb = {k: torch.empty_like(bw[k]) for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k",
-                                                        "cm_Wk", "cm_Wv")}
+            gb = {k: mk(bw[k]) for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k",
+                                          "cm_Wk", "cm_Wv")}
             gb["tm"] = {}
             b = blocks[l]
             for k in ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "cm_mu_k", "cm_Wk", "cm_Wv"):
@@ -543,7 +557,7 @@ class TrainGrads:
                 if l == 0 and n in ("v0", "V1", "V2"):
                     setattr(tg, n, None)
                     continue
-                gb["tm"][n] = torch.empty_like(bw["tm"][n])
+                gb["tm"][n] = mk(bw["tm"][n])
                 setattr(tg, n, gb["tm"][n].data_ptr())
             b.tm = tg
             self.g["blocks"].append(gb)
@@ -634,3 +648,41 @@ def gdn_backward(layer, raw, z, a, b, dout, cache=None, ws=None):
                               _p(a), _p(b), _p(dout), _p(cache), _p(g["draw"]), _p(g["dz"]),
                               _p(g["da"]), _p(g["db"]), _p(ws), ws.numel(), _stream()))
     return g
+
+
+# ------------------------------------------------------ online training --
+def rwkv7_online_workspace_bytes(dm, B, S):
+    return lib().rwkv7_online_workspace_bytes(ctypes.byref(dm.cfg), B, S)
+
+
+def rwkv7_online_segment(dm, grads, tokens, targets, state, optimizer="adam", lr=1e-3, clip=0.0,
+                         step=1, adam_m=None, adam_v=None, loss=None, ws=None, side=True):
+    """One online TBPTT segment: grads written, dm's weights updated in place,
+    state (dict as DecodeModel.new_state) advanced to the live state after
+    replaying the segment with the new weights.  adam_m / adam_v: TrainGrads
+    made with zero=True (Adam only).  Returns the segment's loss (device)."""
+    c = dm.cfg
+    B, S = tokens.shape
+    _need(tokens, (B, S), torch.int32, "tokens")
+    _need(targets, (B, S), torch.int32, "targets")
+    _need(state["att_x_prev"], (c.n_layer, B, c.C), torch.float32, "att_x_prev")
+    _need(state["att_state"], (c.n_layer, B, c.H, 64, 64), torch.float32, "att_state")
+    _need(state["ffn_x_prev"], (c.n_layer, B, c.C), torch.float32, "ffn_x_prev")
+    if optimizer not in ("sgd", "adam"):
+        raise ValueError(f"optimizer must be 'sgd' or 'adam', not {optimizer!r}")
+    adam = optimizer == "adam"
+    opt = Rwkv7Optim(1 if adam else 0, lr, clip, step)
+    if loss is None:
+        loss = torch.empty(1, device=tokens.device, dtype=torch.float32)
+    n = rwkv7_online_workspace_bytes(dm, B, S)
+    if ws is None:
+        ws = torch.empty(n, device=tokens.device, dtype=torch.uint8)
+    mp = ctypes.byref(adam_m.struct) if adam else None
+    vp = ctypes.byref(adam_v.struct) if adam else None
+    with _SideUse(side) as sd:
+        _check(lib().rwkv7_online_segment(ctypes.byref(c), ctypes.byref(dm.model),
+                                          ctypes.byref(grads.struct), mp, vp, ctypes.byref(opt), B, S,
+                                          _p(tokens), _p(targets), _p(state["att_x_prev"]),
+                                          _p(state["att_state"]), _p(state["ffn_x_prev"]), _p(loss),
+                                          _p(ws), ws.numel(), sd, _stream()))
+    return loss

@@ -16,6 +16,7 @@
 #include "../../include/wkv7.h"
 #include "common.hpp"
 #include "gdn.hpp"
+#include "optim.hpp"
 #include "stack_kernels.hpp"
 #include "timemix_kernels.hpp"
 
@@ -546,6 +547,9 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
                     float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false) {
   const int BT = B * T, C = s->C;
+  if (s->layer_id > 0 && (!m.lv || !m.ov))
+    return fail(WKV7_EHIP, "internal: activation set without value-residual buffers for layer %d",
+                s->layer_id);
   TmFwd p;
   memset(&p, 0, sizeof(p));
   p.BT = BT; p.T = T; p.C = C; p.layer_id = s->layer_id;
@@ -1200,13 +1204,14 @@ extern "C" size_t rwkv7_train_workspace_bytes(const rwkv7_config* cfg, int B, in
   return c.off + 256;
 }
 
-extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
-                                rwkv7_model_grads* G, int B, int T, const int* tokens,
-                                const int* targets, float* loss, void* ws, size_t ws_bytes,
-                                const wkv7_side* side, hipStream_t st) {
-  g_err[0] = 0;
+namespace {
+// Arguments shared by rwkv7_train_step and rwkv7_online_segment; `extra`
+// adds the caller's other tensors to the overlap check.
+int check_train(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* G, int B, int T,
+                const int* tokens, const int* targets, float* loss, void* ws, size_t ws_bytes,
+                size_t need, const wkv7_side* side, hipStream_t st, const wkv7_side*& sd,
+                Spans& sp) {
   CHK(check_cfg(cfg, B));
-  const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
   if (T < 1) return fail(WKV7_EINVAL, "T must be >= 1");
   if (!M || !M->blocks || !G || !G->blocks) return fail(WKV7_EINVAL, "model/grads or their blocks are NULL");
   CHK(check_f32_ptr(M->emb, "emb", true));
@@ -1224,7 +1229,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   CHK(check_tok_ptr(tokens, "tokens", WKV7_F32, true));
   CHK(check_tok_ptr(targets, "targets", WKV7_F32, true));
   CHK(check_f32_ptr(loss, "loss", true));
-  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer;
+  const int V = cfg->V, L = cfg->n_layer;
   if ((size_t)B * T * V > ((size_t)1 << 34)) return fail(WKV7_EINVAL, "B*T*V too large");
   for (int l = 0; l < L; l++) {
     tm_shape s = block_shape(cfg, l);
@@ -1245,25 +1250,34 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
       CHK(check_f32_ptr(gb.tm.V2, "grad V2", true));
     }
   }
-  const size_t need = rwkv7_train_workspace_bytes(cfg, B, T);
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
-  const wkv7_side* sd = nullptr;
   CHK(check_side(side, st, sd));
-  {
-    Spans sp;
-    model_spans(sp, cfg, M, false);
-    model_spans(sp, cfg, G, true);
-    sp.rd(tokens, (size_t)B * T * sizeof(int), "tokens");
-    sp.rd(targets, (size_t)B * T * sizeof(int), "targets");
-    sp.wr(loss, sizeof(float), "loss");
-    sp.wr(ws, need, "ws");
-    CHK(sp.check());
-  }
-  Carver cw(ws);
-  TrainBufs t;
-  carve_train(cw, cfg, B, T, t);
+  model_spans(sp, cfg, G, true);
+  sp.rd(tokens, (size_t)B * T * sizeof(int), "tokens");
+  sp.rd(targets, (size_t)B * T * sizeof(int), "targets");
+  sp.wr(loss, sizeof(float), "loss");
+  sp.wr(ws, need, "ws");
+  return WKV7_OK;
+}
+
+// The training step's launches; arguments validated.  st0: NULL (zero
+// initial state) or the streaming state the batch starts from (per layer
+// att_x_prev [B][C], att_state [B][H][N][N], ffn_x_prev [B][C]); the
+// gradients stop at it.
+struct StartState {
+  const float *att_x_prev, *att_state, *ffn_x_prev;
+};
+int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* G, int B, int T,
+              const int* tokens, const int* targets, float* loss, const StartState* st0, TrainBufs& t,
+              const wkv7_side* sd, hipStream_t st) {
+  const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
+  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer;
+  const size_t NN = (size_t)WKV7_N * WKV7_N;
+  auto xp_tm = [&](int l) -> const float* { return st0 ? st0->att_x_prev + (size_t)l * B * C : nullptr; };
+  auto s0_tm = [&](int l) -> const float* { return st0 ? st0->att_state + (size_t)l * B * cfg->H * NN : nullptr; };
+  auto xp_cm = [&](int l) -> const float* { return st0 ? st0->ffn_x_prev + (size_t)l * B * C : nullptr; };
 
   const int BT = B * T;
   const size_t tokC = (size_t)BT * C;
@@ -1280,10 +1294,10 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     tm_shape s = block_shape(cfg, l);
     HIPCHK(hipMemcpyAsync(a.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
-    CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, nullptr, a.x1, nullptr, a.tm, st,
-                        false, 1.f, prec));
+    CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), nullptr, a.x1, nullptr, a.tm,
+                        st, false, 1.f, prec));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
-    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
     HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
     return WKV7_OK;
   };
@@ -1342,7 +1356,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
                         splitk_for(C, F, BT), t.splitk, ss), "dWk");
     HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
-    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, nullptr, bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
+    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
       HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT), C, o, st), "cm mu grad");
@@ -1350,7 +1364,7 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
     HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
     HIPCHK(reduce_ln(gb.ln2_w, gb.ln2_b), "ln2 grads");
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
-    CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, nullptr, t.vf, nullptr, t.dx1, nullptr, a.tm, t.tb,
+    CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
                          nullptr, st, prec, sd));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
@@ -1364,6 +1378,200 @@ extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
   }
   HIPCHK(stk_launch_emb_bwd(BT, V, C, tokens, demb_src, t.count, t.off, t.perm, G->emb, st), "embedding bwd");
   return WKV7_OK;
+}
+}  // namespace
+
+extern "C" int rwkv7_train_step(const rwkv7_config* cfg, const rwkv7_model* M,
+                                rwkv7_model_grads* G, int B, int T, const int* tokens,
+                                const int* targets, float* loss, void* ws, size_t ws_bytes,
+                                const wkv7_side* side, hipStream_t st) {
+  g_err[0] = 0;
+  const wkv7_side* sd = nullptr;
+  Spans sp;
+  const size_t need = rwkv7_train_workspace_bytes(cfg, B, T);
+  CHK(check_train(cfg, M, G, B, T, tokens, targets, loss, ws, ws_bytes, need, side, st, sd, sp));
+  model_spans(sp, cfg, M, false);
+  CHK(sp.check());
+  Carver cw(ws);
+  TrainBufs t;
+  carve_train(cw, cfg, B, T, t);
+  return train_run(cfg, M, G, B, T, tokens, targets, loss, nullptr, t, sd, st);
+}
+
+
+// ------------------------------------------------------ online TBPTT segment --
+namespace {
+
+// Every parameter tensor of the model with its gradient, Adam moments (or
+// NULL) and element count, in one fixed order.
+template <typename Fn>
+void for_each_param(const rwkv7_config* cfg, const rwkv7_model* M, const rwkv7_model_grads* G,
+                    const rwkv7_model_grads* Mm, const rwkv7_model_grads* Vv, Fn fn) {
+  const size_t C = cfg->C, F = cfg->F, V = cfg->V;
+  auto P = [](const float* p) { return const_cast<float*>(p); };
+  auto one = [&](const float* p, float* g, float* m, float* v, size_t n) { fn(P(p), g, m, v, n); };
+  one(M->emb, G->emb, Mm ? Mm->emb : nullptr, Vv ? Vv->emb : nullptr, V * C);
+  one(M->head, G->head, Mm ? Mm->head : nullptr, Vv ? Vv->head : nullptr, C * V);
+  one(M->ln_out_w, G->ln_out_w, Mm ? Mm->ln_out_w : nullptr, Vv ? Vv->ln_out_w : nullptr, C);
+  one(M->ln_out_b, G->ln_out_b, Mm ? Mm->ln_out_b : nullptr, Vv ? Vv->ln_out_b : nullptr, C);
+  if (cfg->use_ln0) {
+    one(M->ln0_w, G->ln0_w, Mm ? Mm->ln0_w : nullptr, Vv ? Vv->ln0_w : nullptr, C);
+    one(M->ln0_b, G->ln0_b, Mm ? Mm->ln0_b : nullptr, Vv ? Vv->ln0_b : nullptr, C);
+  }
+  typedef const float* const tm_weights::*WF;
+  typedef float* tm_grads::*GF;
+  struct TmField {
+    WF w;
+    GF g;
+    int rows, cols;  // in units: 0 -> C, -1 Dw, -2 Da, -3 Dv, -4 Dg, 1 -> 1
+    bool v_lora;
+  };
+  static const TmField tmf[] = {
+      {&tm_weights::mu_r, &tm_grads::mu_r, 1, 0, false}, {&tm_weights::mu_w, &tm_grads::mu_w, 1, 0, false},
+      {&tm_weights::mu_k, &tm_grads::mu_k, 1, 0, false}, {&tm_weights::mu_v, &tm_grads::mu_v, 1, 0, false},
+      {&tm_weights::mu_a, &tm_grads::mu_a, 1, 0, false}, {&tm_weights::mu_g, &tm_grads::mu_g, 1, 0, false},
+      {&tm_weights::Wr, &tm_grads::Wr, 0, 0, false},     {&tm_weights::Wk, &tm_grads::Wk, 0, 0, false},
+      {&tm_weights::Wv, &tm_grads::Wv, 0, 0, false},     {&tm_weights::Wo, &tm_grads::Wo, 0, 0, false},
+      {&tm_weights::w0, &tm_grads::w0, 1, 0, false},     {&tm_weights::W1, &tm_grads::W1, 0, -1, false},
+      {&tm_weights::W2, &tm_grads::W2, -1, 0, false},    {&tm_weights::a0, &tm_grads::a0, 1, 0, false},
+      {&tm_weights::A1, &tm_grads::A1, 0, -2, false},    {&tm_weights::A2, &tm_grads::A2, -2, 0, false},
+      {&tm_weights::v0, &tm_grads::v0, 1, 0, true},      {&tm_weights::V1, &tm_grads::V1, 0, -3, true},
+      {&tm_weights::V2, &tm_grads::V2, -3, 0, true},     {&tm_weights::G1, &tm_grads::G1, 0, -4, false},
+      {&tm_weights::G2, &tm_grads::G2, -4, 0, false},    {&tm_weights::k_k, &tm_grads::k_k, 1, 0, false},
+      {&tm_weights::k_a, &tm_grads::k_a, 1, 0, false},   {&tm_weights::r_k, &tm_grads::r_k, 1, 0, false},
+      {&tm_weights::ln_w, &tm_grads::ln_w, 1, 0, false}, {&tm_weights::ln_b, &tm_grads::ln_b, 1, 0, false}};
+  auto dim = [&](int u) -> size_t {
+    return u == 0 ? C : u == 1 ? 1 : u == -1 ? cfg->Dw : u == -2 ? cfg->Da : u == -3 ? cfg->Dv : cfg->Dg;
+  };
+  for (int l = 0; l < cfg->n_layer; l++) {
+    const rwkv7_block& b = M->blocks[l];
+    const rwkv7_block_grads& g = G->blocks[l];
+    const rwkv7_block_grads* bm = Mm ? &Mm->blocks[l] : nullptr;
+    const rwkv7_block_grads* bv = Vv ? &Vv->blocks[l] : nullptr;
+    one(b.ln1_w, g.ln1_w, bm ? bm->ln1_w : nullptr, bv ? bv->ln1_w : nullptr, C);
+    one(b.ln1_b, g.ln1_b, bm ? bm->ln1_b : nullptr, bv ? bv->ln1_b : nullptr, C);
+    one(b.ln2_w, g.ln2_w, bm ? bm->ln2_w : nullptr, bv ? bv->ln2_w : nullptr, C);
+    one(b.ln2_b, g.ln2_b, bm ? bm->ln2_b : nullptr, bv ? bv->ln2_b : nullptr, C);
+    one(b.cm_mu_k, g.cm_mu_k, bm ? bm->cm_mu_k : nullptr, bv ? bv->cm_mu_k : nullptr, C);
+    one(b.cm_Wk, g.cm_Wk, bm ? bm->cm_Wk : nullptr, bv ? bv->cm_Wk : nullptr, C * F);
+    one(b.cm_Wv, g.cm_Wv, bm ? bm->cm_Wv : nullptr, bv ? bv->cm_Wv : nullptr, F * C);
+    for (const TmField& tf : tmf) {
+      if (tf.v_lora && l == 0) continue;
+      one(b.tm.*(tf.w), g.tm.*(tf.g), bm ? bm->tm.*(tf.g) : nullptr, bv ? bv->tm.*(tf.g) : nullptr,
+          dim(tf.rows) * dim(tf.cols));
+    }
+  }
+}
+
+// The segment replayed with the updated weights from the start state: the
+// forward of every block, writing each layer's new streaming state (the WKV
+// state in place; the two token-shift states through xl, then copied).
+int replay_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int T, const int* tokens,
+               float* axp, float* ast, float* fxp, TrainBufs& t, float* xl, hipStream_t st) {
+  const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
+  const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer, BT = B * T;
+  const size_t tokC = (size_t)BT * C, BC = (size_t)B * C, NN = (size_t)WKV7_N * WKV7_N;
+  auto bin = [&](int l) { return t.block_in + (size_t)l * tokC; };
+  HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
+  if (cfg->use_ln0)
+    HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
+  const bool keep = cfg->train_recompute == 0;
+  for (int l = 0; l < L; l++) {
+    // the layer's own activation set (kept mode: sized for its layer id) or
+    // the one reused set (sized for a block with the value-residual LoRA)
+    BlockActs& a = t.act[keep ? l : 0];
+    const rwkv7_block& bl = M->blocks[l];
+    tm_shape s = block_shape(cfg, l);
+    float* st_l = ast + (size_t)l * B * cfg->H * NN;
+    HIPCHK(hipMemcpyAsync(a.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
+    CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, axp + (size_t)l * BC, t.vf, st_l, st_l, a.x1,
+                        xl + (size_t)l * BC, a.tm, st, false, 1.f, prec));
+    HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, fxp + (size_t)l * BC, bl.cm_mu_k, a.sh,
+                               xl + (size_t)(L + l) * BC, st), "cm shift");
+    HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(hipMemcpyAsync(bin(l + 1), a.x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, a.ka, F, bl.cm_Wv, C, bin(l + 1), C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+  }
+  HIPCHK(hipMemcpyAsync(axp, xl, (size_t)L * BC * sizeof(float), hipMemcpyDeviceToDevice, st), "state copy");
+  HIPCHK(hipMemcpyAsync(fxp, xl + (size_t)L * BC, (size_t)L * BC * sizeof(float), hipMemcpyDeviceToDevice, st), "state copy");
+  return WKV7_OK;
+}
+
+}  // namespace
+
+extern "C" size_t rwkv7_online_workspace_bytes(const rwkv7_config* cfg, int B, int S) {
+  if (check_cfg(cfg, B) != WKV7_OK || S < 1) return 0;
+  Carver c(nullptr);
+  TrainBufs t;
+  carve_train(c, cfg, B, S, t);
+  c.take((size_t)2 * cfg->n_layer * B * cfg->C);  // the replay's new token-shift states
+  return c.off + 256;
+}
+
+extern "C" int rwkv7_online_segment(const rwkv7_config* cfg, const rwkv7_model* M,
+                                    rwkv7_model_grads* G, rwkv7_model_grads* adam_m,
+                                    rwkv7_model_grads* adam_v, const rwkv7_optim* opt, int B, int S,
+                                    const int* tokens, const int* targets, float* att_x_prev,
+                                    float* att_state, float* ffn_x_prev, float* loss, void* ws,
+                                    size_t ws_bytes, const wkv7_side* side, hipStream_t st) {
+  g_err[0] = 0;
+  if (!opt) return fail(WKV7_EINVAL, "optimiser settings are NULL");
+  if (opt->optimizer != 0 && opt->optimizer != 1) return fail(WKV7_EINVAL, "optimizer must be 0 (SGD) or 1 (Adam)");
+  if (!(opt->lr >= 0.f) || !(opt->clip >= 0.f) || opt->lr > 1e30f || opt->clip > 1e30f)
+    return fail(WKV7_EINVAL, "lr and clip must be finite and >= 0");
+  const bool adam = opt->optimizer == 1;
+  if (adam && opt->step < 1) return fail(WKV7_EINVAL, "Adam step must be >= 1 (got %d)", opt->step);
+  if (adam && (!adam_m || !adam_v || !adam_m->blocks || !adam_v->blocks))
+    return fail(WKV7_EINVAL, "Adam needs both moment mirrors");
+  CHK(check_f32_ptr(att_x_prev, "att_x_prev", true));
+  CHK(check_f32_ptr(att_state, "att_state", true));
+  CHK(check_f32_ptr(ffn_x_prev, "ffn_x_prev", true));
+  const wkv7_side* sd = nullptr;
+  Spans sp;
+  const size_t need = rwkv7_online_workspace_bytes(cfg, B, S);
+  CHK(check_train(cfg, M, G, B, S, tokens, targets, loss, ws, ws_bytes, need, side, st, sd, sp));
+  int bad = 0;
+  if (adam)
+    for_each_param(cfg, M, G, adam_m, adam_v, [&](float*, float*, float* m, float* v, size_t) {
+      if (bad == 0 && (check_f32_ptr(m, "an Adam moment", true) || check_f32_ptr(v, "an Adam moment", true))) bad = 1;
+    });
+  if (bad) return WKV7_EINVAL;
+  model_spans(sp, cfg, M, true);  // the weights are updated in place
+  if (adam) {
+    model_spans(sp, cfg, adam_m, true);
+    model_spans(sp, cfg, adam_v, true);
+  }
+  const size_t f = sizeof(float), L = cfg->n_layer, BC = (size_t)B * cfg->C;
+  sp.wr(att_x_prev, L * BC * f, "att_x_prev");  // start state in, live state out
+  sp.wr(att_state, L * state_bytes(B, cfg->H), "att_state");
+  sp.wr(ffn_x_prev, L * BC * f, "ffn_x_prev");
+  CHK(sp.check());
+
+  Carver cw(ws);
+  TrainBufs t;
+  carve_train(cw, cfg, B, S, t);
+  float* xl = cw.take(2 * L * BC);
+  // 1. gradients of the segment from the start state (truncated there)
+  const StartState s0{att_x_prev, att_state, ffn_x_prev};
+  CHK(train_run(cfg, M, G, B, S, tokens, targets, loss, &s0, t, sd, st));
+  // 2. the update, up to OPT_MAX tensors per launch
+  OptBatch ob;
+  memset(&ob, 0, sizeof(ob));
+  hipError_t e = hipSuccess;
+  auto flush = [&]() {
+    if (ob.n && e == hipSuccess) e = opt_launch(ob, adam ? 1 : 0, opt->lr, opt->clip, opt->step, st);
+    ob.n = 0;
+  };
+  for_each_param(cfg, M, G, adam_m, adam_v, [&](float* p, float* g, float* m, float* v, size_t n) {
+    ob.p[ob.n] = p; ob.g[ob.n] = g; ob.m[ob.n] = m; ob.v[ob.n] = v; ob.count[ob.n] = n;
+    if (++ob.n == OPT_MAX) flush();
+  });
+  flush();
+  HIPCHK(e, "parameter update");
+  // 3. the live state: the segment replayed with the updated weights
+  return replay_run(cfg, M, B, S, tokens, att_x_prev, att_state, ffn_x_prev, t, xl, st);
 }
 
 // ------------------------------------------------------------ GatedDeltaNet --
