@@ -21,7 +21,7 @@ the headline alone.  Workloads:
              backward through the segment, Adam update, live-state replay,
              fp32 (tokens/s)
   gdn        GatedDeltaNet layer forward + through-gradient backward, B=2
-             windows of T=4096, 16 key heads / 32 value heads of size 128,
+             windows of T=4096, 12 key heads / 24 value heads of size 128,
              4 causal conv taps, fp32 (tokens/s)
   train      full training step: 24 blocks C=1024 H=16 FFN 4096, vocab
              65536, B=4 T=2048, embedding, LM head, fused CE, forward +
@@ -392,7 +392,7 @@ def setup_gdn():
     import torch
 
     from rwkv_linear_attention_wkv7_amd import binding, synth
-    B, T, nk, nv, dk, dv, kk = 2, 4096, 16, 32, 128, 128, 4
+    B, T, nk, nv, dk, dv, kk = 2, 4096, 12, 24, 128, 128, 4
     cfg = synth.gdn_config(nk, nv, dk, dv, kk=kk, seed=0)
     d = synth.gdn_inputs(B, T, cfg, seed=0)
     dev = torch.device("cuda")

@@ -92,11 +92,11 @@ def test_gdn_backward_without_cache(hip):
 
 
 def test_gdn_full_size_sampled_groups(hip):
-    """B=2, T=4096, nk=16, nv=32, dk=dv=128, 4 taps (the benchmarked layer):
+    """B=2, T=4096, nk=12, nv=24, dk=dv=128, 4 taps (the benchmarked layer):
     two key-head groups of window 1 against the oracle at full length."""
-    cfg = synth.gdn_config(16, 32, 128, 128, kk=4, seed=0)
+    cfg = synth.gdn_config(12, 24, 128, 128, kk=4, seed=0)
     d = synth.gdn_inputs(2, 4096, cfg, seed=0)
-    print("[gdn] full size B=2 T=4096 nk=16 nv=32 dk=dv=128", flush=True)
+    print("[gdn] full size B=2 T=4096 nk=12 nv=24 dk=dv=128", flush=True)
     out, g = _run(hip, cfg, d)
-    for grp in (0, 15):
+    for grp in (0, 11):
         _check_window(cfg, d, 1, out, g, group=grp)
