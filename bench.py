@@ -60,6 +60,20 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+CPU_MIN_S = 10.0  # seconds of oracle work per cpu_baseline sample
+
+
+def repeat_for(fn, min_s=CPU_MIN_S):
+    """Run fn until at least min_s seconds have passed: (repetitions, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return reps, dt
+
+
 def time_calls(fn, iters):
     """Per-call ms of `iters` calls of fn(): one pair of HIP events per call on
     the current stream (the stream the library launches on), bracketed by
@@ -129,13 +143,12 @@ def setup_wkv7_small():
         from oracle import wkv7 as ow
         sub = [d[n].astype(np.float64) for n in names]
         dy64 = d["dy"].astype(np.float64)
-        reps = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < 2.0:
+
+        def one():
             ow.forward(*sub)
             ow.backward(*sub, dy64)
-            reps += 1
-        dt = time.perf_counter() - t0
+
+        reps, dt = repeat_for(one)
         return dict(value=reps * B * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
                     sample=f"the whole workload (4 heads, T=64) {reps} times: f64 forward+backward, "
                            f"{dt:.1f} s")
@@ -182,14 +195,14 @@ def setup_timemix():
     def cpu():
         from oracle import timemix as otm
         from oracle import wkv7 as ow
-        Bs = B
-        t0 = time.perf_counter()
-        out, c = otm.forward(p, d["x"][:Bs], H, 1, v_first=d["v_first"][:Bs])
-        otm.backward(p, c, d["dout"][:Bs])
-        dt = time.perf_counter() - t0
-        return dict(value=Bs * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
-                    sample=f"the whole workload (8 sequences, T=1024, C=768): f64 forward+backward, "
-                           f"{dt:.1f} s")
+        def one():
+            out, c = otm.forward(p, d["x"], H, 1, v_first=d["v_first"])
+            otm.backward(p, c, d["dout"])
+
+        reps, dt = repeat_for(one)
+        return dict(value=reps * B * T / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"the whole workload (8 sequences, T=1024, C=768) {reps} times: f64 "
+                           f"forward+backward, {dt:.1f} s")
 
     cfg = {"workload": "time-mix block forward+backward", "B": B, "T": T, "C": C, "H": H,
            "N": N, "lora_ranks_w_a_v_g": list(ranks), "layer_id": 1, "global_batch": B,
@@ -236,14 +249,17 @@ def setup_wkv7_long(chunked=False):
     def cpu():
         from oracle import wkv7 as ow
         sub = [d[n].astype(np.float64) for n in names]
-        t0 = time.perf_counter()
-        ow.forward(*sub)
-        ow.backward(*sub, d["dy"].astype(np.float64))
-        dt = time.perf_counter() - t0
-        return dict(value=(B * T) / dt, unit="tokens/s", cores=ow.num_threads(),
+        dy64 = d["dy"].astype(np.float64)
+
+        def one():
+            ow.forward(*sub)
+            ow.backward(*sub, dy64)
+
+        reps, dt = repeat_for(one)
+        return dict(value=reps * B * T / dt, unit="tokens/s", cores=ow.num_threads(),
                     kind="oracle",
-                    sample=f"the whole workload (128 (b,h) pairs, T=8192): f64 forward+backward, "
-                           f"{dt:.1f} s")
+                    sample=f"the whole workload (128 (b,h) pairs, T=8192) {reps} times: f64 "
+                           f"forward+backward, {dt:.1f} s")
 
     cfg = {"workload": "WKV7 forward+backward, long context", "B": B, "T": T, "H": H, "N": N,
            "forward": "chunked (matrix cores)" if chunked else "token-sequential",
@@ -308,14 +324,16 @@ def setup_decode():
     def cpu():
         from oracle import stack
         from oracle import wkv7 as ow
-        ns, steps = 128, 64
+        ns = 128
         idx = np.arange(ns) * (B // ns)
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
-        state = stack.init_state(ocfg, ns)
-        t0 = time.perf_counter()
-        for t in range(steps):
-            _, state = stack.decode_step(m, ocfg, tokens_np[t, idx], state)
-        dt = time.perf_counter() - t0
+        box = dict(state=stack.init_state(ocfg, ns), t=0)
+
+        def one():
+            _, box["state"] = stack.decode_step(m, ocfg, tokens_np[box["t"] % STEPS, idx], box["state"])
+            box["t"] += 1
+
+        steps, dt = repeat_for(one)
         per_step_full = dt / steps * (B / ns)
         return dict(value=1.0 / per_step_full, unit="steps/s", cores=ow.num_threads(), kind="oracle",
                     sample=f"{ns} of {B} streams x {steps} steps (f64), {dt:.1f} s; scaled to "
@@ -372,12 +390,10 @@ def setup_train():
         from oracle import wkv7 as ow
         Ts = 768
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
-        t0 = time.perf_counter()
-        stack.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1])
-        dt = time.perf_counter() - t0
-        return dict(value=Ts / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
-                    sample=f"1 sequence x {Ts} tokens of the same model (f64 forward+backward), "
-                           f"{dt:.1f} s")
+        reps, dt = repeat_for(lambda: stack.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1]))
+        return dict(value=reps * Ts / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"1 sequence x {Ts} tokens of the same model (f64 forward+backward) "
+                           f"{reps} times, {dt:.1f} s")
 
     cfg = {"workload": "RWKV-7 training step (24 blocks, LM head, log-softmax CE) forward+backward",
            "n_layer": L, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
@@ -435,16 +451,21 @@ def setup_gdn():
         sub = {k: (f64(v) if isinstance(v, np.ndarray) else v) for k, v in cfg.items()}
         sub.update(nk=1, nv=2, conv=f64(cfg["conv"])[ch], A_log=f64(cfg["A_log"])[heads],
                    dt_bias=f64(cfg["dt_bias"])[heads])
-        t0 = time.perf_counter()
-        _, c = og.forward(f64(d["raw"][0][:, ch]), f64(d["z"][0][:, vc]), f64(d["a"][0][:, heads]),
-                          f64(d["b"][0][:, heads]), sub)
-        og.backward(c, f64(d["dout"][0][:, vc]))
-        dt = time.perf_counter() - t0
+        ins64 = (f64(d["raw"][0][:, ch]), f64(d["z"][0][:, vc]), f64(d["a"][0][:, heads]),
+                 f64(d["b"][0][:, heads]))
+        dout64 = f64(d["dout"][0][:, vc])
+
+        def one():
+            _, c = og.forward(*ins64, sub)
+            og.backward(c, dout64)
+
+        reps, dt = repeat_for(one)
         scale = B * nk  # windows x key-head groups in the workload
-        return dict(value=B * T / (dt * scale), unit="tokens/s", cores=ow.num_threads(),
+        return dict(value=reps * B * T / (dt * scale), unit="tokens/s", cores=ow.num_threads(),
                     kind="oracle",
-                    sample=f"one key-head group (2 value heads) of one window, T={T}: f64 forward+"
-                           f"backward, {dt:.1f} s; scaled to the {scale} groups of the workload")
+                    sample=f"one key-head group (2 value heads) of one window, T={T}, {reps} times: "
+                           f"f64 forward+backward, {dt:.1f} s; scaled to the {scale} groups of the "
+                           f"workload")
 
     cfgd = {"workload": "GatedDeltaNet layer forward+backward (through-gradients)", "B": B, "T": T,
             "nk": nk, "nv": nv, "dk": dk, "dv": dv, "conv_taps": kk, "global_batch": B,
@@ -505,12 +526,11 @@ def setup_online():
         ns = 4
         ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L)
         st0 = stack.init_state(ocfg, ns)
-        t0 = time.perf_counter()
-        online.train_segment(m, ocfg, tok[:ns, :S], tok[:ns, 1:S + 1], st0, "adam", lr=1e-4)
-        dt = time.perf_counter() - t0
-        return dict(value=ns * S / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+        reps, dt = repeat_for(lambda: online.train_segment(m, ocfg, tok[:ns, :S], tok[:ns, 1:S + 1],
+                                                           st0, "adam", lr=1e-4))
+        return dict(value=reps * ns * S / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
                     sample=f"one segment of {ns} of the {B} streams x {S} steps (f64 gradients, "
-                           f"Adam update, replay), {dt:.1f} s; streams are independent")
+                           f"Adam update, replay) {reps} times, {dt:.1f} s; streams are independent")
 
     cfgd = {"workload": "online TBPTT training segments on the 12-layer decode model",
             "n_layer": L, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
