@@ -480,16 +480,25 @@ int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float *A, i
 
 /*
  * Same contraction, layouts, requirements and errors as wkv7_gemm_f32, with
- * the operands rounded to bf16 (round to nearest even) as they are staged and
- * the products accumulated in fp32 on the bf16 matrix cores
- * (v_mfma_f32_32x32x16_bf16 for whole 256-row tiles, v_mfma_f32_16x16x32_bf16
- * otherwise).  A, B and C stay fp32 in memory.  C must not overlap A or B.  This is the
- * bf16-GEMM precision the full training-step configuration names for the
- * projections; the pages' own GEMMs are fp32 SGEMM.
+ * the operands rounded to bf16 (round to nearest even) and the products
+ * accumulated in fp32 on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16 for
+ * whole 256-row tiles, v_mfma_f32_16x16x32_bf16 otherwise).  A, B and C stay
+ * fp32 in memory.  C must not overlap A, B or ws.  This is the bf16-GEMM
+ * precision the full training-step configuration names for the projections;
+ * the pages' own GEMMs are fp32 SGEMM.
+ *
+ * ws (optional, 256-byte aligned, ws_bytes >= the query when not NULL):
+ * with it, a product on whole 256 x 128 tiles with K a multiple of 64 and
+ * A not transposed first rounds A and B once into ws as bf16, stored
+ * k-contiguous, and the matrix cores read those copies with no conversion in
+ * the loop; without it (NULL) the operands are rounded as they are read from
+ * LDS.  Both give the same bits.  The query returns 0 for shapes that do
+ * not use it.  ENOSPC when ws is given and smaller than the query.
  */
+size_t wkv7_gemm_bf16_workspace_bytes(int transA, int transB, int M, int N, int K);
 int wkv7_gemm_bf16(int transA, int transB, int M, int N, int K, const float *A, int lda,
-                   const float *B, int ldb, float *C, int ldc, float beta,
-                   hipStream_t stream);
+                   const float *B, int ldb, float *C, int ldc, float beta, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -120,8 +120,10 @@ def lib():
         L.timemix_backward.restype = _i
         L.wkv7_gemm_f32.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp]
         L.wkv7_gemm_f32.restype = _i
-        L.wkv7_gemm_bf16.argtypes = L.wkv7_gemm_f32.argtypes
+        L.wkv7_gemm_bf16.argtypes = [_i] * 5 + [_vp, _i, _vp, _i, _vp, _i, ctypes.c_float, _vp, _sz, _vp]
         L.wkv7_gemm_bf16.restype = _i
+        L.wkv7_gemm_bf16_workspace_bytes.argtypes = [_i] * 5
+        L.wkv7_gemm_bf16_workspace_bytes.restype = _sz
         cp = ctypes.POINTER(Rwkv7Config)
         L.rwkv7_decode_workspace_bytes.argtypes = [cp, _i]
         L.rwkv7_decode_workspace_bytes.restype = _sz
@@ -435,7 +437,9 @@ def timemix_backward(s, W, x, dout, x_prev=None, v_first=None, s0=None, dsT=None
 
 
 # ------------------------------------------------------------------ GEMM --
-def _gemm(fn, A, B, C, transA, transB, beta):
+def _gemm(fn, A, B, C, transA, transB, beta, ws=False):
+    """ws: False (the fp32 call, no workspace argument), None (bf16 without
+    one), True (bf16 with a workspace allocated here) or a uint8 tensor."""
     M, K = (A.shape[1], A.shape[0]) if transA else tuple(A.shape)
     K2, N = (B.shape[1], B.shape[0]) if transB else tuple(B.shape)
     if K != K2:
@@ -445,8 +449,13 @@ def _gemm(fn, A, B, C, transA, transB, beta):
     if C is None:
         C = torch.empty((M, N), device=A.device, dtype=torch.float32)
     _need(C, (M, N), torch.float32, "C")
-    _check(fn(int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B), B.shape[1], _p(C), N,
-              beta, _stream()))
+    args = [int(transA), int(transB), M, N, K, _p(A), A.shape[1], _p(B), B.shape[1], _p(C), N, beta]
+    if ws is not False:
+        if ws is True:
+            n = lib().wkv7_gemm_bf16_workspace_bytes(int(transA), int(transB), M, N, K)
+            ws = torch.empty(n, device=A.device, dtype=torch.uint8) if n else None
+        args += [_p(ws), 0 if ws is None else ws.numel()]
+    _check(fn(*args, _stream()))
     return C
 
 
@@ -455,9 +464,15 @@ def wkv7_gemm_f32(A, B, C=None, transA=False, transB=False, beta=0.0):
     return _gemm(lib().wkv7_gemm_f32, A, B, C, transA, transB, beta)
 
 
-def wkv7_gemm_bf16(A, B, C=None, transA=False, transB=False, beta=0.0):
-    """As wkv7_gemm_f32 with bf16-rounded operands and fp32 accumulation."""
-    return _gemm(lib().wkv7_gemm_bf16, A, B, C, transA, transB, beta)
+def wkv7_gemm_bf16_workspace_bytes(M, N, K, transA=False, transB=False):
+    return lib().wkv7_gemm_bf16_workspace_bytes(int(transA), int(transB), M, N, K)
+
+
+def wkv7_gemm_bf16(A, B, C=None, transA=False, transB=False, beta=0.0, ws=True):
+    """As wkv7_gemm_f32 with bf16-rounded operands and fp32 accumulation.
+    ws: True allocates the bf16-copy workspace the shape asks for, None runs
+    without one (operands rounded in LDS), or a uint8 device tensor."""
+    return _gemm(lib().wkv7_gemm_bf16, A, B, C, transA, transB, beta, ws=ws)
 
 
 # ---------------------------------------------------------- decode stack --

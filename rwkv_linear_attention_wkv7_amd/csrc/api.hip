@@ -885,7 +885,8 @@ extern "C" int timemix_backward(const tm_shape* s, const tm_weights* W, int B, i
 // ----------------------------------------------------------------- GEMM --
 namespace {
 int gemm_abi(int prec, int transA, int transB, int M, int N, int K, const float* A, int lda,
-             const float* B, int ldb, float* C, int ldc, float beta, hipStream_t stream) {
+             const float* B, int ldb, float* C, int ldc, float beta, void* ws, size_t ws_bytes,
+             hipStream_t stream) {
   g_err[0] = 0;
   if (M < 1 || N < 1 || K < 1) return fail(WKV7_EINVAL, "M, N, K must be >= 1");
   CHK(check_f32_ptr(A, "A", true));
@@ -902,8 +903,15 @@ int gemm_abi(int prec, int transA, int transB, int M, int N, int K, const float*
     sp.rd(A, ((a_rows - 1) * lda + a_inner) * f, "A");
     sp.rd(B, ((b_rows - 1) * ldb + b_inner) * f, "B");
     sp.wr(C, ((size_t)(M - 1) * ldc + N) * f, "C");
+    if (ws) sp.wr(ws, ws_bytes, "ws");
     CHK(sp.check());
   }
+  if (ws && ((uintptr_t)ws & 255)) return fail(WKV7_EINVAL, "ws must be 256-byte aligned");
+  // operands packed to bf16 only when the workspace holds the whole copy
+  const size_t need = (prec == GEMM_BF16 && !transA) ? gemm_pack_need(M, N, K) : 0;
+  if (ws && ws_bytes < need)
+    return fail(WKV7_ENOSPC, "workspace %zu bytes, this GEMM needs %zu", ws_bytes, need);
+  GemmPackScope pack_scope(need && ws ? ws : nullptr, ws_bytes);
   HIPCHK(gemm_run(prec, transA != 0, transB != 0, M, N, K, A, lda, B, ldb, C, ldc, beta, 0, nullptr,
                   1, nullptr, stream),
          "gemm launch");
@@ -914,13 +922,21 @@ int gemm_abi(int prec, int transA, int transB, int M, int N, int K, const float*
 extern "C" int wkv7_gemm_f32(int transA, int transB, int M, int N, int K, const float* A, int lda,
                              const float* B, int ldb, float* C, int ldc, float beta,
                              hipStream_t stream) {
-  return gemm_abi(GEMM_F32, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, stream);
+  return gemm_abi(GEMM_F32, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, nullptr, 0,
+                  stream);
+}
+
+extern "C" size_t wkv7_gemm_bf16_workspace_bytes(int transA, int transB, int M, int N, int K) {
+  (void)transB;
+  if (M < 1 || N < 1 || K < 1 || transA) return 0;
+  return gemm_pack_need(M, N, K);
 }
 
 extern "C" int wkv7_gemm_bf16(int transA, int transB, int M, int N, int K, const float* A,
                               int lda, const float* B, int ldb, float* C, int ldc, float beta,
-                              hipStream_t stream) {
-  return gemm_abi(GEMM_BF16, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, stream);
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  return gemm_abi(GEMM_BF16, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, ws, ws_bytes,
+                  stream);
 }
 
 // --------------------------------------------------------- decode stack --
@@ -1153,7 +1169,25 @@ struct TrainBufs {
   int *count, *off, *perm, *n_valid;
   std::vector<BlockActs> act;  // every block's (train_recompute == 0), or one reused
   TmBwdBufs tb;
+  float* pack = nullptr;  // bf16 operand copies of the GEMMs (gemm_dtype == WKV7_BF16)
+  size_t pack_bytes = 0;
 };
+
+// Largest arena of bf16 operand copies any one GEMM launch of the training
+// step asks for (the X W and dY W^T products; the X^T dY ones read fp32).
+size_t train_pack_bytes(const rwkv7_config* cfg, size_t BT) {
+  const int C = cfg->C, F = cfg->F, V = cfg->V, M = (int)BT;
+  const int D[4] = {cfg->Dw, cfg->Da, cfg->Dg, cfg->Dv};
+  size_t best = 3 * gemm_pack_need(M, C, C);  // r, k, v in one launch
+  size_t down = 0, up = 0;
+  for (int d : D) {
+    down += gemm_pack_need(M, d, C);
+    up += gemm_pack_need(M, C, d);
+  }
+  best = std::max({best, down, up, gemm_pack_need(M, F, C), gemm_pack_need(M, C, F),
+                   gemm_pack_need(M, V, C), gemm_pack_need(M, C, V)});
+  return best;
+}
 
 tm_shape block_shape(const rwkv7_config* c, int l) {
   return tm_shape{c->C, c->H, c->N, c->Dw, c->Da, c->Dv, c->Dg, l};
@@ -1169,7 +1203,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   t.logits = c.take(BT * cfg->V);
   t.loss_row = c.take(BT);
   t.part_ln = c.take((size_t)2 * stk_num_ln_blocks((int)BT) * cfg->C);
-  t.part_cm = c.take((size_t)stk_num_shift_blocks((int)BT) * cfg->C);
+  t.part_cm = c.take((size_t)stk_num_shift_blocks((int)BT, cfg->C) * cfg->C);
   const int C = cfg->C, F = cfg->F, V = cfg->V;
   size_t sk = 0;
   const int pairs[][2] = {{F, C}, {C, F}, {C, V}};
@@ -1179,6 +1213,10 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   t.off = (int*)c.take((size_t)V);
   t.perm = (int*)c.take(BT);
   t.n_valid = (int*)c.take(1);
+  if (cfg->gemm_dtype == WKV7_BF16) {
+    t.pack_bytes = train_pack_bytes(cfg, BT);
+    t.pack = c.take(t.pack_bytes / sizeof(float));
+  }
   const bool keep = cfg->train_recompute == 0;
   t.act.resize(keep ? L : 1);
   for (size_t i = 0; i < t.act.size(); i++) {
@@ -1273,6 +1311,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
               const int* tokens, const int* targets, float* loss, const StartState* st0, TrainBufs& t,
               const wkv7_side* sd, hipStream_t st) {
   const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
+  GemmPackScope pack_scope(t.pack, t.pack_bytes);  // bf16 operand copies (null for fp32)
   const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer;
   const size_t NN = (size_t)WKV7_N * WKV7_N;
   auto xp_tm = [&](int l) -> const float* { return st0 ? st0->att_x_prev + (size_t)l * B * C : nullptr; };
@@ -1359,7 +1398,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
-      HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT), C, o, st), "cm mu grad");
+      HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT, C), C, o, st), "cm mu grad");
     }
     HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
     HIPCHK(reduce_ln(gb.ln2_w, gb.ln2_b), "ln2 grads");
@@ -1469,6 +1508,7 @@ void for_each_param(const rwkv7_config* cfg, const rwkv7_model* M, const rwkv7_m
 int replay_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int T, const int* tokens,
                float* axp, float* ast, float* fxp, TrainBufs& t, float* xl, hipStream_t st) {
   const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
+  GemmPackScope pack_scope(t.pack, t.pack_bytes);
   const int C = cfg->C, F = cfg->F, V = cfg->V, L = cfg->n_layer, BT = B * T;
   const size_t tokC = (size_t)BT * C, BC = (size_t)B * C, NN = (size_t)WKV7_N * WKV7_N;
   auto bin = [&](int l) { return t.block_in + (size_t)l * tokC; };

@@ -494,10 +494,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One operand's copy plan: R tile rows, KC or row-contiguous, IL (KC only):
-// interleaved row order; NW waves.  Each stage is R * 32 floats = R / 8 copy
-// instructions of 1 KB; wave w issues numbers w, w + NW, ...
-template <int R, bool KC, bool IL, int NW>
+// interleaved row order; NW waves; ES bytes per element (4: fp32, 2: bf16,
+// KC only).  Each stage is R rows of 128 bytes (32 fp32 or 64 bf16 k) = R / 8
+// copy instructions of 1 KB; wave w issues numbers w, w + NW, ...
+template <int R, bool KC, bool IL, int NW, int ES = 4>
 struct Copy {
+  static_assert(ES == 4 || (ES == 2 && KC), "bf16 operands are copied k-contiguous");
   static constexpr int NI = R / (8 * NW);  // instructions per wave per stage
   uint32_t off[NI];                        // byte offset of this lane's 16 bytes
   __device__ __forceinline__ void init(int ld, int lane, int wave) {
@@ -507,7 +509,7 @@ struct Copy {
       if (KC) {
         const int rho = 8 * g + (lane >> 3), c = (lane & 7) ^ (lane >> 3) ^ (g & 1);
         const int row = IL ? 4 * (rho % (R / 4)) + rho / (R / 4) : rho;
-        off[q] = (uint32_t)(row * ld + 4 * c) * 4u;
+        off[q] = (uint32_t)(row * ld) * (uint32_t)ES + 16u * (uint32_t)c;
       } else {
         const int e = g * 64 + lane;  // float4 index in the stage
         off[q] = (uint32_t)((e / (R / 4)) * ld + 4 * (e % (R / 4))) * 4u;
@@ -568,12 +570,32 @@ __device__ __forceinline__ void frags(const char* X, int s, int woff, int i, int
   }
 }
 
+// NF 32-row fragments of a k-contiguous bf16 operand for k-step s of a stage
+// (rows as in frags): a 128-byte LDS row holds 64 k as 8 slots of 8 bf16, the
+// lane group h of k-step s takes slot 2 s + h, one 16-byte read per fragment.
+template <int R, bool IL, int NF>
+__device__ __forceinline__ void frags_bf(const char* X, int s, int woff, int i, int h, bf16x8 (&out)[NF]) {
+  static_assert(!IL || NF == 4, "the interleaved KC order spans 4 fragments");
+  const int key = (i & 7) ^ ((i >> 3) & 1);
+  const uint32_t c = (uint32_t)(((2 * s + h) ^ key) * 16);
+#pragma unroll
+  for (int f = 0; f < NF; f++) {
+    const int rho = IL ? f * (R / 4) + woff / 4 + i : woff + 32 * f + i;
+    out[f] = *reinterpret_cast<const bf16x8*>(X + (uint32_t)rho * 128u + c);
+  }
+}
+
 // TJ = 8: 256x256 tile, 8 waves (two per SIMD, so one wave's MFMAs cover
 // the other's LDS and barrier waits) as 4 x 2, each 64 x 128 (2 x 4 blocks
 // of 32x32).  TJ = 4: 256x128 tile, 4 waves as 4 x 1, each 64 x 128.
-template <int TJ, bool TA, bool TB>
+// BF: both operands are bf16 in global memory, k-contiguous (A [M][K], B
+// [N][K], leading dimensions in bf16 elements), copied as they are: 64 k per
+// stage and no conversion in the multiply loop.
+template <int TJ, bool TA, bool TB, bool BF = false>
 __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch, int kslice) {
+  static_assert(!BF || (!TA && TB), "bf16 operands come k-contiguous");
   constexpr int BM = 256, BN = 32 * TJ, NW = TJ == 8 ? 8 : 4;
+  constexpr int ES = BF ? 2 : 4, KST = BF ? 64 : BK;  // element bytes, k per stage
   constexpr int FA = 2, FB = 4;  // 32-row fragments per wave
   constexpr bool AKC = !TA, BKC = TB;
   // the N side is always read in the interleaved order (float4 stores along
@@ -602,18 +624,18 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
   const int wb = TJ == 8 ? (wave & 1) * 128 : 0;
   const int i = lane & 31, h = lane >> 5;
 
-  Copy<BM, AKC, false, NW> ca;
-  Copy<BN, BKC, true, NW> cb;
+  Copy<BM, AKC, false, NW, ES> ca;
+  Copy<BN, BKC, true, NW, ES> cb;
   ca.init(P.lda, lane, wave);
   cb.init(P.ldb, lane, wave);
-  constexpr int NDMA = Copy<BM, AKC, false, NW>::NI + Copy<BN, BKC, true, NW>::NI;
-  // stage origins: (row 0, k0) of each operand tile
-  const char* Ab = reinterpret_cast<const char*>(P.A + (AKC ? (size_t)m0 * P.lda : (size_t)m0));
-  const char* Bb = reinterpret_cast<const char*>(P.B + (BKC ? (size_t)n0 * P.ldb : (size_t)n0));
-  const size_t astep = (AKC ? (size_t)BK : (size_t)BK * P.lda) * 4;
-  const size_t bstep = (BKC ? (size_t)BK : (size_t)BK * P.ldb) * 4;
-  Ab += (AKC ? (size_t)kbeg : (size_t)kbeg * P.lda) * 4;
-  Bb += (BKC ? (size_t)kbeg : (size_t)kbeg * P.ldb) * 4;
+  constexpr int NDMA = Copy<BM, AKC, false, NW, ES>::NI + Copy<BN, BKC, true, NW, ES>::NI;
+  // stage origins: (row 0, k0) of each operand tile, in bytes
+  const char* Ab = reinterpret_cast<const char*>(P.A) + (AKC ? (size_t)m0 * P.lda * ES : (size_t)m0 * 4);
+  const char* Bb = reinterpret_cast<const char*>(P.B) + (BKC ? (size_t)n0 * P.ldb * ES : (size_t)n0 * 4);
+  const size_t astep = AKC ? (size_t)KST * ES : (size_t)BK * P.lda * 4;
+  const size_t bstep = BKC ? (size_t)KST * ES : (size_t)BK * P.ldb * 4;
+  Ab += AKC ? (size_t)kbeg * ES : (size_t)kbeg * P.lda * 4;
+  Bb += BKC ? (size_t)kbeg * ES : (size_t)kbeg * P.ldb * 4;
 
   f16v acc[FA][FB];
 #pragma unroll
@@ -625,10 +647,15 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
 
   auto compute = [&](const float* Xa, const float* Xb) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; s++) {
+    for (int s = 0; s < KST / 16; s++) {
       bf16x8 fa[FA], fb[FB];
-      frags<BM, AKC, AIL, FA>(reinterpret_cast<const char*>(Xa), s, wa, i, h, fa);
-      frags<BN, BKC, true, FB>(reinterpret_cast<const char*>(Xb), s, wb, i, h, fb);
+      if constexpr (BF) {
+        frags_bf<BM, false, FA>(reinterpret_cast<const char*>(Xa), s, wa, i, h, fa);
+        frags_bf<BN, true, FB>(reinterpret_cast<const char*>(Xb), s, wb, i, h, fb);
+      } else {
+        frags<BM, AKC, AIL, FA>(reinterpret_cast<const char*>(Xa), s, wa, i, h, fa);
+        frags<BN, BKC, true, FB>(reinterpret_cast<const char*>(Xb), s, wb, i, h, fb);
+      }
 #pragma unroll
       for (int a = 0; a < FA; a++)
 #pragma unroll
@@ -643,7 +670,7 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
   // after the multiply frees the stage for the copy issued next.
   const uint32_t la0 = (uint32_t)(size_t)(lds_void*)As0, lb0 = (uint32_t)(size_t)(lds_void*)Bs0;
   const uint32_t la1 = (uint32_t)(size_t)(lds_void*)As1, lb1 = (uint32_t)(size_t)(lds_void*)Bs1;
-  const int nk = (kend - kbeg) / BK;
+  const int nk = (kend - kbeg) / KST;
   ca.issue(Ab, la0, wave);
   cb.issue(Bb, lb0, wave);
   for (int s = 0; s < nk; s++) {
@@ -688,6 +715,51 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
 }
 
 }  // namespace dmak
+
+// ------------------------------------------------------------------ packs --
+// Operands rounded to bf16 (round to nearest even) once and stored
+// k-contiguous for the bf16 mode of gemm_dma.
+// dst[r][c] = bf16(src[r][c]), R x K (K a multiple of 8), dst leading dim K.
+__global__ __launch_bounds__(256) void pack_bf16(int R, int K, const float* __restrict__ src, int lds,
+                                                 __bf16* __restrict__ dst) {
+  const int K8 = K / 8;
+  const size_t n = (size_t)R * K8;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int r = (int)(i / K8), c = (int)(i - (size_t)r * K8) * 8;
+    const f4* p = reinterpret_cast<const f4*>(src + (size_t)r * lds + c);
+    const bf16x4 lo = __builtin_convertvector(p[0], bf16x4), hi = __builtin_convertvector(p[1], bf16x4);
+    *reinterpret_cast<bf16x8*>(dst + (size_t)r * K + c) =
+        bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// dst[n][k] = bf16(src[k][n]) for a K x N source (K and N multiples of 64),
+// dst leading dim K.  A 64 x 64 tile per workgroup through LDS: rows of the
+// source read as float4, rows of the result written as 16 bytes.
+__global__ __launch_bounds__(256) void pack_bf16_t(int K, int N, const float* __restrict__ src, int lds,
+                                                   __bf16* __restrict__ dst) {
+  __shared__ float tile[64][65];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int k = tid / 16 + 16 * j, c = (tid % 16) * 4;
+    const f4 v = *reinterpret_cast<const f4*>(src + (size_t)(k0 + k) * lds + n0 + c);
+    tile[k][c] = v[0];
+    tile[k][c + 1] = v[1];
+    tile[k][c + 2] = v[2];
+    tile[k][c + 3] = v[3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int n = tid / 8 + 32 * j, kq = (tid % 8) * 8;
+    const f4 lo = {tile[kq][n], tile[kq + 1][n], tile[kq + 2][n], tile[kq + 3][n]};
+    const f4 hi = {tile[kq + 4][n], tile[kq + 5][n], tile[kq + 6][n], tile[kq + 7][n]};
+    const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+    *reinterpret_cast<bf16x8*>(dst + (size_t)(n0 + n) * K + k0 + kq) =
+        bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
 
 // Sum S split-K partials [S][M][N] (leading dim N) into C (ldc), with beta/epilogue.
 __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const float* __restrict__ P,
@@ -775,6 +847,67 @@ hipError_t launch_dma(const GemmBatch& b, int tj, int gz, int kslice, hipStream_
   return tj == 8 ? launch_dma_t<8, TA, TB>(b, gz, kslice, st) : launch_dma_t<4, TA, TB>(b, gz, kslice, st);
 }
 
+// The caller's arena for bf16 operand copies (set for the duration of one
+// library call on the calling thread; null: operands are converted in LDS).
+thread_local char* tl_pack = nullptr;
+thread_local size_t tl_pack_bytes = 0;
+
+constexpr size_t PACK_MAX_A = (size_t)64 << 20;   // elements: larger activations are read as fp32
+constexpr size_t PACK_MAX_B = (size_t)128 << 20;  // elements of a packed weight
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The bf16 mode of gemm_dma: every operand of the batch is rounded to bf16
+// once into the arena, k-contiguous (A [M][K] as is, B to [N][K]: as is when
+// it is stored [N][K], transposed otherwise), then multiplied without any
+// conversion in the loop.  Returns hipErrorNotSupported when the batch does
+// not take this path.
+hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, int kslice,
+                             hipStream_t st) {
+  size_t need = 0;
+  for (int i = 0; i < b.count; i++) {
+    const size_t n = gemm_pack_need(b.p[i].M, b.p[i].N, b.p[i].K);
+    if (n == 0) return hipErrorNotSupported;
+    need += n;
+  }
+  if (!tl_pack || need > tl_pack_bytes) return hipErrorNotSupported;
+  GemmBatch pb = b;
+  char* cur = tl_pack;
+  for (int i = 0; i < b.count; i++) {
+    const GemmProblem& q = b.p[i];
+    __bf16* pa = reinterpret_cast<__bf16*>(cur);
+    cur += align256((size_t)q.M * q.K * 2);
+    __bf16* pbm = reinterpret_cast<__bf16*>(cur);
+    cur += align256((size_t)q.N * q.K * 2);
+    auto blocks = [](size_t n8) { return (int)std::min<size_t>((n8 + 255) / 256, 4096); };
+    hipLaunchKernelGGL(pack_bf16, dim3(blocks((size_t)q.M * q.K / 8)), dim3(256), 0, st, q.M, q.K, q.A,
+                       q.lda, pa);
+    if (transB)
+      hipLaunchKernelGGL(pack_bf16, dim3(blocks((size_t)q.N * q.K / 8)), dim3(256), 0, st, q.N, q.K,
+                         q.B, q.ldb, pbm);
+    else
+      hipLaunchKernelGGL(pack_bf16_t, dim3(q.N / 64, q.K / 64), dim3(256), 0, st, q.K, q.N, q.B, q.ldb,
+                         pbm);
+    pb.p[i].A = reinterpret_cast<const float*>(pa);
+    pb.p[i].lda = q.K;
+    pb.p[i].B = reinterpret_cast<const float*>(pbm);
+    pb.p[i].ldb = q.K;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int maxM = 0, maxN = 0;
+  for (int i = 0; i < pb.count; i++) {
+    maxM = max(maxM, pb.p[i].M);
+    maxN = max(maxN, pb.p[i].N);
+  }
+  dim3 grid(maxN / (32 * tj), maxM / 256, gz);
+  if (tj == 8)
+    hipLaunchKernelGGL((dmak::gemm_dma<8, false, true, true>), grid, dim3(512), 0, st, pb, kslice);
+  else
+    hipLaunchKernelGGL((dmak::gemm_dma<4, false, true, true>), grid, dim3(256), 0, st, pb, kslice);
+  return hipGetLastError();
+}
+
 template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid reaches 512 workgroups, or 256 when each workgroup
@@ -812,6 +945,10 @@ hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int 
                     int klen, hipStream_t st) {
   if (prec == GEMM_BF16) {
     const int tj = dma_tj(b, transA, gz, kslice);
+    if (tj && !transA) {
+      const hipError_t e = launch_dma_packed(b, transB, tj, gz, kslice, st);
+      if (e != hipErrorNotSupported) return e;
+    }
     if (tj && !transA && !transB) return launch_dma<false, false>(b, tj, gz, kslice, st);
     if (tj && !transA && transB) return launch_dma<false, true>(b, tj, gz, kslice, st);
     if (tj && transA && !transB) return launch_dma<true, false>(b, tj, gz, kslice, st);
@@ -822,6 +959,18 @@ hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int 
 }
 
 }  // namespace gemmk
+
+size_t gemm_pack_need(int M, int N, int K) {
+  using namespace gemmk;
+  if (M % 256 || N % 128 || K % 64 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if ((size_t)M * K > PACK_MAX_A || (size_t)N * K > PACK_MAX_B) return 0;
+  return align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
+}
+
+void gemm_set_pack_arena(void* p, size_t bytes) {
+  gemmk::tl_pack = reinterpret_cast<char*>(p);
+  gemmk::tl_pack_bytes = p ? bytes : 0;
+}
 
 hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
   if (b.count < 1 || b.count > GEMM_MAX_BATCH) return hipErrorInvalidValue;

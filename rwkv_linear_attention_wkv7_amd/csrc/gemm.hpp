@@ -1,7 +1,7 @@
 // Matrix-core GEMM (gemm.hip): problem descriptors and launchers.  Operands
 // and results are fp32 in memory; the products run either in fp32
 // (v_mfma_f32_16x16x4_f32) or with bf16-rounded operands and fp32
-// accumulation (v_mfma_f32_16x16x32_bf16).
+// accumulation (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_16x16x32_bf16).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -43,6 +43,23 @@ int gemm_splitk_slices(int prec, int M, int N, int K);
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
                     int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
                     const float* aux, int split, float* ws, hipStream_t st);
+
+// bf16 operand copies.  A bf16 problem that the direct-to-LDS kernel takes
+// (M a multiple of 256, N of 128, K of 64), and that is not X^T dY, rounds
+// its operands to bf16 once into an arena, stored k-contiguous, and
+// multiplies them with no conversion in the loop, when the calling thread
+// has set an arena large enough for the whole launch (the sum of
+// gemm_pack_need over its problems).  The arena belongs to the caller's
+// workspace; the setting lasts until it is cleared (GemmPackScope), and the
+// GEMMs that use it must run one after another on one stream.
+size_t gemm_pack_need(int M, int N, int K);  // bytes, 0 when the shape does not qualify
+void gemm_set_pack_arena(void* p, size_t bytes);
+struct GemmPackScope {
+  GemmPackScope(void* p, size_t bytes) { gemm_set_pack_arena(p, bytes); }
+  ~GemmPackScope() { gemm_set_pack_arena(nullptr, 0); }
+  GemmPackScope(const GemmPackScope&) = delete;
+  GemmPackScope& operator=(const GemmPackScope&) = delete;
+};
 
 inline hipError_t gemm_f32_batch(bool transA, bool transB, const GemmBatch& b, hipStream_t st) {
   return gemm_batch(GEMM_F32, transA, transB, b, st);

@@ -290,43 +290,74 @@ __global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* 
   }
 }
 
-constexpr int TBK = 128;  // tokens per workgroup in the shift backward
+constexpr int SB_TOK = 8;  // consecutive tokens per thread in the shift backward
+
+// Float4 columns a thread group covers, and groups per workgroup, for width C:
+// up to 256 columns side by side; narrower rows stack 256 / (C/4) token
+// groups in one workgroup.
+__host__ __device__ inline int sb_lanes(int C) { return C / 4 < 256 ? C / 4 : 256; }
+__host__ __device__ inline int sb_groups(int C) { return 256 / sb_lanes(C); }
 
 // Channel-mix token-shift backward: dx = dsh (1 - mu) + dsh[t+1] mu,
-// dx_prev (t = 0) = dsh mu, partial dmu = sum dsh (prev - x).  Grid (C/64, token blocks).
+// dx_prev (t = 0) = dsh mu, partial dmu = sum dsh (prev - x).
+// Grid (channel blocks of 256 float4 columns, token blocks).  A thread owns
+// one float4 column and walks SB_TOK consecutive tokens, carrying the
+// previous token's x and the next token's dsh in registers, so x, dsh and dx
+// each cross HBM once and every wave touches 1 KB of one row per access.
+// Each workgroup writes one partial row of dmu (its groups summed through LDS).
 __global__ __launch_bounds__(256) void cm_shift_bwd(int BT, int T, int C, const float* __restrict__ x,
                                                     const float* __restrict__ x_prev,
                                                     const float* __restrict__ mu,
                                                     const float* __restrict__ dsh,
                                                     float* __restrict__ dx, float* __restrict__ dx_prev,
                                                     float* __restrict__ part) {
-  __shared__ f4 red[16][16];
-  const int cb = blockIdx.x, blk = blockIdx.y;
-  const int l16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const int c = cb * 64 + l16 * 4;
-  const f4 m = *reinterpret_cast<const f4*>(mu + c);
+  __shared__ f4 red[256];
+  const int C4 = C / 4, lanes = sb_lanes(C), G = sb_groups(C);
+  const int grp = threadIdx.x / lanes, l = threadIdx.x - grp * lanes;
+  const int c4 = blockIdx.x * 256 + l;
+  const f4* X = reinterpret_cast<const f4*>(x);
+  const f4* D = reinterpret_cast<const f4*>(dsh);
+  f4* DX = reinterpret_cast<f4*>(dx);
   f4 pm = {0.f, 0.f, 0.f, 0.f};
-  const int t_end = min(BT, (blk + 1) * TBK);
-  for (int bt = blk * TBK + grp; bt < t_end; bt += 16) {
-    const size_t e = (size_t)bt * C + c;
-    const int t = bt % T;
-    const f4 xv = *reinterpret_cast<const f4*>(x + e);
-    f4 prev = {0.f, 0.f, 0.f, 0.f};
-    if (t > 0) prev = *reinterpret_cast<const f4*>(x + e - C);
-    else if (x_prev) prev = *reinterpret_cast<const f4*>(x_prev + (size_t)(bt / T) * C + c);
-    const f4 g = *reinterpret_cast<const f4*>(dsh + e);
-    pm += g * (prev - xv);
-    f4 o = g * (1.0f - m);
-    if (t < T - 1) o += *reinterpret_cast<const f4*>(dsh + e + C) * m;
-    *reinterpret_cast<f4*>(dx + e) = o;
-    if (t == 0 && dx_prev) *reinterpret_cast<f4*>(dx_prev + (size_t)(bt / T) * C + c) = g * m;
+  const int bt0 = (blockIdx.y * G + grp) * SB_TOK;
+  const int bt1 = min(BT, bt0 + SB_TOK);
+  if (grp < G && c4 < C4 && bt0 < bt1) {
+    const f4 m = reinterpret_cast<const f4*>(mu)[c4];
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    auto xprev = [&](int b) {
+      return x_prev ? reinterpret_cast<const f4*>(x_prev)[(size_t)b * C4 + c4] : zero;
+    };
+    int t = bt0 % T, b = bt0 / T;
+    f4 prev = t > 0 ? X[(size_t)(bt0 - 1) * C4 + c4] : xprev(b);
+    f4 g = D[(size_t)bt0 * C4 + c4];
+    for (int bt = bt0; bt < bt1; bt++) {
+      const size_t e = (size_t)bt * C4 + c4;
+      const f4 xv = X[e];
+      const bool last = t == T - 1;
+      const f4 gn = last ? zero : D[e + C4];  // the next token of the same sequence
+      pm += g * (prev - xv);
+      DX[e] = g * (1.0f - m) + gn * m;
+      if (t == 0 && dx_prev) reinterpret_cast<f4*>(dx_prev)[(size_t)b * C4 + c4] = g * m;
+      if (last) {  // the next token opens sequence b + 1
+        t = 0;
+        b++;
+        if (bt + 1 < bt1) {
+          prev = xprev(b);
+          g = D[e + C4];
+        }
+      } else {
+        t++;
+        prev = xv;
+        g = gn;
+      }
+    }
   }
-  red[grp][l16] = pm;
+  red[threadIdx.x] = pm;
   __syncthreads();
-  if (threadIdx.x < 16) {
-    f4 s = red[0][threadIdx.x];
-    for (int gi = 1; gi < 16; gi++) s += red[gi][threadIdx.x];
-    *reinterpret_cast<f4*>(part + (size_t)blk * C + cb * 64 + threadIdx.x * 4) = s;
+  if (grp == 0 && c4 < C4) {
+    f4 s = red[l];
+    for (int gi = 1; gi < G; gi++) s += red[gi * lanes + l];
+    reinterpret_cast<f4*>(part + (size_t)blockIdx.y * C)[c4] = s;
   }
 }
 
@@ -394,6 +425,66 @@ __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restric
 #pragma unroll
     for (int c = 0; c < 4; c++) p[c] = expf(v[c] - lse) - ((4 * i + c) == tgt ? 1.0f : 0.0f);
     zr[i] = p * inv_n;
+  }
+  if (tid == 0) loss_row[row] = (float)(lse_d - (double)zt);
+}
+
+// The same cross-entropy with the row held in registers: 1024 threads, NV4
+// float4 per thread (V <= 4096 NV4), so the logits are read once and written
+// once.  The arithmetic per float4 and the reductions' precisions are those
+// of ce_fwd_bwd (fp32 max and terms, double sum and LSE).
+template <int NV4>
+__global__ __launch_bounds__(1024) void ce_fwd_bwd_reg(int R, int V, float* __restrict__ z,
+                                                       const int* __restrict__ targets,
+                                                       const int* __restrict__ n_valid,
+                                                       float* __restrict__ loss_row) {
+  __shared__ float smx[16];
+  __shared__ double ssum[16];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f4* zr = reinterpret_cast<f4*>(z + (size_t)row * V);
+  const int V4 = V / 4;
+  const int tgt = targets[row];
+  if ((unsigned)tgt >= (unsigned)V) {  // ignored row (uniform per workgroup)
+    for (int i = tid; i < V4; i += 1024) zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+    if (tid == 0) loss_row[row] = 0.f;
+    return;
+  }
+  const float zt = tid == 0 ? z[(size_t)row * V + tgt] : 0.f;  // read before any write (barriers below)
+  f4 v[NV4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV4; i++) {
+    const int idx = tid + i * 1024;
+    v[i] = idx < V4 ? zr[idx] : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    mx = fmaxf(mx, fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3])));
+  }
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) smx[wave] = mx;
+  __syncthreads();
+  mx = smx[0];
+  for (int w = 1; w < 16; w++) mx = fmaxf(mx, smx[w]);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < NV4; i++)
+    if (tid + i * 1024 < V4)
+      s += (double)((expf(v[i][0] - mx) + expf(v[i][1] - mx)) + (expf(v[i][2] - mx) + expf(v[i][3] - mx)));
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) ssum[wave] = s;
+  __syncthreads();
+  s = 0.0;
+  for (int w = 0; w < 16; w++) s += ssum[w];
+  const double lse_d = (double)mx + log(s);
+  const float lse = (float)lse_d;
+  const float inv_n = (float)(1.0 / (double)n_valid[0]);  // >= 1 here
+#pragma unroll
+  for (int i = 0; i < NV4; i++) {
+    const int idx = tid + i * 1024;
+    if (idx < V4) {
+      f4 p;
+#pragma unroll
+      for (int c = 0; c < 4; c++) p[c] = expf(v[i][c] - lse) - ((4 * idx + c) == tgt ? 1.0f : 0.0f);
+      zr[idx] = p * inv_n;
+    }
   }
   if (tid == 0) loss_row[row] = (float)(lse_d - (double)zt);
 }
@@ -483,7 +574,10 @@ hipError_t stk_launch_fill_zero(float* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 int stk_num_ln_blocks(int R) { return (R + stk::LN_ROWS - 1) / stk::LN_ROWS; }
-int stk_num_shift_blocks(int BT) { return (BT + stk::TBK - 1) / stk::TBK; }
+int stk_num_shift_blocks(int BT, int C) {
+  const int per = stk::sb_groups(C) * stk::SB_TOK;
+  return (BT + per - 1) / per;
+}
 
 hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
                                     const float* dres, float* dx, float* part, hipStream_t st) {
@@ -500,15 +594,25 @@ hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w
 hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,
                                    const float* mu, const float* dsh, float* dx, float* dx_prev,
                                    float* part, hipStream_t st) {
-  hipLaunchKernelGGL(stk::cm_shift_bwd, dim3(C / 64, stk_num_shift_blocks(BT)), dim3(256), 0, st,
+  hipLaunchKernelGGL(stk::cm_shift_bwd, dim3((C / 4 + 255) / 256, stk_num_shift_blocks(BT, C)), dim3(256), 0, st,
                      BT, T, C, x, x_prev, mu, dsh, dx, dx_prev, part);
   return hipGetLastError();
 }
 hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
                          int* n_valid, hipStream_t st) {
   hipLaunchKernelGGL(stk::count_valid, dim3(1), dim3(256), 0, st, R, V, targets, n_valid);
-  hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, n_valid,
-                     loss_row);
+  const int V4 = V / 4;
+  if (V4 >= 1024 && V4 <= 16 * 1024) {  // the row fits in the registers of 1024 threads
+    const dim3 g(R), t(1024);
+    if (V4 <= 1024) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<1>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+    else if (V4 <= 2048) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<2>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+    else if (V4 <= 4096) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<4>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+    else if (V4 <= 8192) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<8>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+    else hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<16>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+  } else {
+    hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, n_valid,
+                       loss_row);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(stk::sum_rows, dim3(1), dim3(256), 0, st, R, loss_row, n_valid, loss);

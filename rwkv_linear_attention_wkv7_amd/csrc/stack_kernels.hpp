@@ -21,7 +21,8 @@ struct LnMix {
 hipError_t stk_launch_ln_mix(const LnMix& p, hipStream_t st);
 int stk_max_layernorm_width();
 int stk_num_ln_blocks(int R);
-int stk_num_shift_blocks(int BT);
+// partial rows of the channel-mix shift backward (one per workgroup of tokens)
+int stk_num_shift_blocks(int BT, int C);
 hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
                                     const float* dres, float* dx, float* part, hipStream_t st);
 hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,

@@ -296,7 +296,25 @@ def test_gemm_rejects_output_over_operand(Lfake):
     assert L.wkv7_gemm_f32(0, 0, 64, 64, 64, a, 64, b, 64, a, 64, 0.0, None) == -1
     assert "overlaps" in _err(L)
     c = ctypes.c_void_p(b.value + 64 * 63 * 4)   # C starts in B's last row
-    assert L.wkv7_gemm_bf16(0, 0, 64, 64, 64, a, 64, b, 64, c, 64, 0.0, None) == -1
+    assert L.wkv7_gemm_bf16(0, 0, 64, 64, 64, a, 64, b, 64, c, 64, 0.0, None, 0, None) == -1
+
+
+def test_gemm_bf16_workspace(L, Lfake):
+    """The bf16-copy workspace: (M + N) K bf16 values for whole 256 x 128
+    tiles with K a multiple of 64 and A not transposed, else none; a given
+    workspace smaller than that is ENOSPC, one overlapping C is EINVAL."""
+    q = L.wkv7_gemm_bf16_workspace_bytes
+    assert q(0, 0, 8192, 4096, 1024) == (8192 + 4096) * 1024 * 2
+    assert q(0, 1, 8192, 1024, 4096) == (8192 + 1024) * 4096 * 2
+    assert q(1, 0, 1024, 4096, 8192) == 0          # X^T dY reads fp32
+    assert q(0, 0, 8192, 4096, 96) == 0            # K not a multiple of 64
+    assert q(0, 0, 100, 4096, 1024) == 0           # M not a multiple of 256
+    a, b, c, w = _addrs(4, base=1 << 40)
+    need = q(0, 0, 256, 128, 64)
+    assert L.wkv7_gemm_bf16(0, 0, 256, 128, 64, a, 64, b, 128, c, 128, 0.0, w, need - 1, None) == -3
+    assert "needs" in _err(L)
+    assert L.wkv7_gemm_bf16(0, 0, 256, 128, 64, a, 64, b, 128, c, 128, 0.0, c, need, None) == -1
+    assert "overlaps" in _err(L)
 
 
 def test_side_stream_validation(Lfake):

@@ -67,3 +67,28 @@ def test_gemm_bf16_layouts(hip, M, N, K, tA, tB):
     assert_close("C (bf16 operands)", out, ref_r, 1e-5)
     ref = op(a.astype(np.float64), tA) @ op(b.astype(np.float64), tB) + 0.5 * c0.astype(np.float64)
     assert_close("C", out, ref, 2e-2)
+
+
+@pytest.mark.parametrize("M,N,K,tB", [(8192, 4096, 1024, False), (8192, 1024, 4096, True),
+                                      (2048, 2048, 256, False), (8192, 768, 768, True),
+                                      (4096, 65536, 1024, False)])
+def test_gemm_bf16_copies_give_the_same_bits(hip, M, N, K, tB):
+    """With a workspace the operands are rounded to bf16 once into it
+    (k-contiguous; B transposed when stored [K][N]) and multiplied without
+    conversion; without one they are rounded as they are read from LDS.  The
+    roundings and the order of the k steps are the same, so the results are
+    bitwise equal; and they match the f64 product of the rounded operands."""
+    g = np.random.default_rng(M + N + K)
+    a = g.standard_normal((M, K)).astype(np.float32)
+    b = g.standard_normal((N, K) if tB else (K, N)).astype(np.float32)
+    A, Bm = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    assert hip.wkv7_gemm_bf16_workspace_bytes(M, N, K, transB=tB) == (M + N) * K * 2
+    print(f"[gemm_bf16 copies] M={M} N={N} K={K} tB={tB}", flush=True)
+    c1 = hip.wkv7_gemm_bf16(A, Bm, transB=tB, ws=None)
+    c2 = hip.wkv7_gemm_bf16(A, Bm, transB=tB, ws=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    rows = np.random.default_rng(1).choice(M, 64, replace=False)
+    ar, br = synth.round_bf16(a[rows]).astype(np.float64), synth.round_bf16(b).astype(np.float64)
+    ref = ar @ (br.T if tB else br)
+    assert_close("C rows (bf16 operands)", c2.cpu().numpy()[rows], ref, 1e-5)

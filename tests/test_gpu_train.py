@@ -119,6 +119,29 @@ def test_train_step_small(hip, use_ln0, gemm):
     _compare(m, grads, x, y, loss, dict(C=C, H=H, F=F, V=V, n_layer=L), gemm)
 
 
+@pytest.mark.parametrize("V", [6148, 65536])
+def test_train_step_ragged_wide_vocab_ignored_targets(hip, V):
+    """Sequences of 37 tokens (the channel-mix shift backward's per-thread
+    token runs cross sequence boundaries), a vocabulary wide enough for the
+    register-resident cross-entropy (6148: a partial last register slice),
+    and targets outside [0, V) (-1 and V) that are ignored: zero dlogits rows,
+    no loss term, the mean over the counted positions."""
+    from rwkv_linear_attention_wkv7_amd import binding
+    L, C, H, F, B, T = 1, 128, 2, 256, 3, 37
+    ranks = (16, 16, 16, 32)
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=21, perturbed=True, std=0.2, use_ln0=False)
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=0),
+                             _dev_model(m))
+    grads = binding.TrainGrads(dm)
+    tok = synth.token_ids(B, T + 1, V, seed=22)
+    x, y = np.ascontiguousarray(tok[:, :-1]), np.ascontiguousarray(tok[:, 1:]).copy()
+    y[0, 3], y[1, 0], y[2, T - 1], y[2, 10] = -1, V, -1, V + 7
+    print(f"[train] ragged T={T} V={V} with ignored targets", flush=True)
+    loss = hip.rwkv7_train_step(dm, grads, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    _compare(m, grads, x, y, float(loss.item()), dict(C=C, H=H, F=F, V=V, n_layer=L))
+
+
 @pytest.mark.parametrize("gemm", ["f32", "bf16"])
 def test_train_step_full_model_short_batch(hip, gemm):
     """Full model size: 24 blocks, C=1024 (H=16), FFN 4096, vocab 65536, ranks
