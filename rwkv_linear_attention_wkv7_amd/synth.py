@@ -167,6 +167,34 @@ def stack_model(C, H, F, V, n_layer, ranks, seed=0, use_ln0=True, perturbed=Fals
     return m
 
 
+def attn_blocks(C, F, n_attn, seed=0, perturbed=False, std=0.02):
+    """Random-init attention blocks of a hybrid stack (fp32): LayerNorms as
+    stack_model, Wq, Wk, Wv, Wo [C][C] and channel-mix Wk [C][F], Wv [F][C]
+    ~ N(0, std^2), mu_k = 0.5 + U(-0.02, 0.02)."""
+    def mat(name, shape):
+        return (std * rng(seed, name).standard_normal(shape)).astype(np.float32)
+
+    def ln(name):
+        w, b = np.ones(C), np.zeros(C)
+        if perturbed:
+            w = w + 0.1 * rng(seed, name + "_w").standard_normal(C)
+            b = b + 0.1 * rng(seed, name + "_b").standard_normal(C)
+        return w.astype(np.float32), b.astype(np.float32)
+
+    out = []
+    for a in range(n_attn):
+        ab = {}
+        ab["ln1_w"], ab["ln1_b"] = ln(f"attn_ln1_{a}")
+        ab["ln2_w"], ab["ln2_b"] = ln(f"attn_ln2_{a}")
+        for w in ("Wq", "Wk", "Wv", "Wo"):
+            ab[w] = mat(f"attn_{w}_{a}", (C, C))
+        ab["cm_mu_k"] = (0.5 + rng(seed, f"attn_cm_mu_{a}").uniform(-0.02, 0.02, size=C)).astype(np.float32)
+        ab["cm_Wk"] = mat(f"attn_cm_Wk_{a}", (C, F))
+        ab["cm_Wv"] = mat(f"attn_cm_Wv_{a}", (F, C))
+        out.append(ab)
+    return out
+
+
 def token_ids(B, T, V, seed=0, name="tokens"):
     """Uniform int32 token ids [B][T] in [0, V)."""
     return rng(seed, name).integers(0, V, size=(B, T)).astype(np.int32)
