@@ -27,6 +27,7 @@
 #define WKV7_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -461,6 +462,34 @@ int gdn_backward(const gdn_shape *s, const gdn_weights *W, int B, int T, const f
                  const float *z, const float *a, const float *b, const float *dout,
                  const void *cache, float *draw, float *dz, float *da, float *db, void *ws,
                  size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------ MoBA sparse attention --
+ * The attention core of the hybrid stack's attention blocks.  Page:
+ * "Foundry/cuda_kernels/fullmodel.cu", fm_attn_core_fwd and the attention
+ * part of fm_attn_bwd (the selection kernel itself is not on the page; the
+ * reading below is MoBA's gating).  Per (batch, head), head size N = 64,
+ * scale 1/8: keys form chunks of `chunk` positions; query t (chunk
+ * cur = t / chunk) attends to its own chunk up to itself and to the
+ * (topk - 1) earlier chunks with the highest q_t . mean(k over the chunk)
+ * (ties: the lower chunk index); y_t = softmax over those keys of
+ * q_t . k / 8, times v.  With topk >= the number of chunks this is causal
+ * softmax attention.
+ * q, k, v, y, dy, dq, dk, dv: [B][T][H][N] fp32 (16-byte aligned).
+ * lse: [B][H][T] fp32, the row log-sum-exp; sel: [B][H][T] 64-bit masks of
+ * the attended chunks (bit c: chunk c).  At most 64 chunks per sequence;
+ * 1 <= topk <= 64.  ws: moba_workspace_bytes() bytes (both calls).
+ * Every output is written, summed in a fixed order (no atomics).
+ */
+size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk);
+int moba_forward(int B, int T, int H, int N, int chunk, int topk, const float *q, const float *k,
+                 const float *v, float *y, float *lse, uint64_t *sel, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+/* Gradients of <dy, y> with the selection sel held fixed (as the page's
+ * backward does): needs the forward's y, lse and sel for the same q, k, v. */
+int moba_backward(int B, int T, int H, int N, int chunk, const float *q, const float *k,
+                  const float *v, const float *y, const float *lse, const uint64_t *sel,
+                  const float *dy, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
 
 /* ------------------------------------------------------------- helpers -- */
 

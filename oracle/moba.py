@@ -70,27 +70,50 @@ def allowed(sel, chunk):
     return mask & (tau[None, :] <= np.arange(T)[:, None])
 
 
-def core_forward(q, k, v, H, chunk, topk):
-    """MoBA core over [B][T][C] q, k, v (C = H N): y [B][T][C] and a cache."""
+def core_forward(q, k, v, H, chunk, topk, sel=None):
+    """MoBA core over [B][T][C] q, k, v (C = H N): y [B][T][C] and a cache
+    (P, the key mask, the row log-sum-exp lse [B][H][T] and the selection).
+
+    sel: None (select here), or the selection to use, bool [B][H][T][chunks]:
+    the selection is a discrete decision taken on floating-point scores, so a
+    comparison with another implementation checks the two selections on
+    their own and then evaluates the attention for the same one."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     B, T, C = q.shape
     N = C // H
+    nc = (T + chunk - 1) // chunk
     scale = 1.0 / np.sqrt(N)
     y = np.zeros_like(q)
     P = np.zeros((B, H, T, T))
     masks = np.zeros((B, H, T, T), dtype=bool)
+    lse = np.zeros((B, H, T))
+    sels = np.zeros((B, H, T, nc), dtype=bool)
     for b in range(B):
         for h in range(H):
             sl = slice(h * N, (h + 1) * N)
             qh, kh, vh = q[b, :, sl], k[b, :, sl], v[b, :, sl]
-            mask = allowed(select(qh, kh, chunk, topk), chunk)
+            sels[b, h] = select(qh, kh, chunk, topk) if sel is None else sel[b, h]
+            mask = allowed(sels[b, h], chunk)
             s = np.where(mask, scale * (qh @ kh.T), -np.inf)
-            s = s - s.max(axis=1, keepdims=True)
-            p = np.where(mask, np.exp(s), 0.0)
-            p /= p.sum(axis=1, keepdims=True)
+            mx = s.max(axis=1, keepdims=True)
+            e = np.where(mask, np.exp(s - mx), 0.0)
+            z = e.sum(axis=1, keepdims=True)
+            p = e / z
             y[b, :, sl] = p @ vh
             P[b, h], masks[b, h] = p, mask
-    return y, dict(q=q, k=k, v=v, P=P, mask=masks, H=H, scale=scale)
+            lse[b, h] = (mx + np.log(z))[:, 0]
+    return y, dict(q=q, k=k, v=v, P=P, mask=masks, lse=lse, sel=sels, H=H, scale=scale)
+
+
+def chunk_scores(q, k, chunk):
+    """Gating scores [T][chunks] of one head: q_t . mean(k over chunk c)
+    (the selection ranks the earlier chunks by these)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    T = q.shape[0]
+    nc = (T + chunk - 1) // chunk
+    kbar = np.stack([k[c * chunk:(c + 1) * chunk].mean(axis=0) for c in range(nc)])
+    return q @ kbar.T
 
 
 def core_backward(cache, dy):

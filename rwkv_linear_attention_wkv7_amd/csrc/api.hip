@@ -16,6 +16,7 @@
 #include "../../include/wkv7.h"
 #include "common.hpp"
 #include "gdn.hpp"
+#include "moba.hpp"
 #include "optim.hpp"
 #include "stack_kernels.hpp"
 #include "timemix_kernels.hpp"
@@ -1774,5 +1775,92 @@ extern "C" int gdn_backward(const gdn_shape* s, const gdn_weights* W, int B, int
   p.dout = dout;
   p.dz = dz; p.draw = draw; p.da = da; p.db = db;
   HIPCHK(gdn_launch_backward(p, stream), "gdn_backward launch");
+  return WKV7_OK;
+}
+
+// ------------------------------------------------------- MoBA attention --
+namespace {
+int check_moba(int B, int T, int H, int N, int chunk, int topk) {
+  if (N != WKV7_N) return fail(WKV7_EINVAL, "head size N=%d unsupported (must be 64)", N);
+  if (B < 1 || T < 1 || H < 1) return fail(WKV7_EINVAL, "B, T, H must be >= 1 (got %d, %d, %d)", B, T, H);
+  if (chunk < 1) return fail(WKV7_EINVAL, "chunk must be >= 1 (got %d)", chunk);
+  if (moba_num_chunks(T, chunk) > 64)
+    return fail(WKV7_EINVAL, "T=%d in chunks of %d gives %d chunks (at most 64)", T, chunk,
+                moba_num_chunks(T, chunk));
+  if (topk < 1 || topk > 64) return fail(WKV7_EINVAL, "topk must be in [1, 64] (got %d)", topk);
+  if ((size_t)B * T * H * N > ((size_t)1 << 36)) return fail(WKV7_EINVAL, "problem too large");
+  return WKV7_OK;
+}
+int check_sel_ptr(const void* p, const char* name) {
+  if (!p) return fail(WKV7_EINVAL, "%s is NULL", name);
+  if ((uintptr_t)p & 7) return fail(WKV7_EINVAL, "%s must be 8-byte aligned", name);
+  return WKV7_OK;
+}
+}  // namespace
+
+extern "C" size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk) {
+  if (check_moba(B, T, H, N, chunk, 1) != WKV7_OK) return 0;
+  const size_t kb = moba_kbar_floats(B, T, H, chunk), d = (size_t)B * H * T;
+  return std::max(kb, d) * sizeof(float);
+}
+
+extern "C" int moba_forward(int B, int T, int H, int N, int chunk, int topk, const float* q,
+                            const float* k, const float* v, float* y, float* lse, uint64_t* sel,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_moba(B, T, H, N, chunk, topk));
+  const float* ptr[] = {q, k, v, y, lse, (const float*)ws};
+  const char* nm[] = {"q", "k", "v", "y", "lse", "ws"};
+  for (int i = 0; i < 6; i++) CHK(check_f32_ptr(ptr[i], nm[i], true));
+  CHK(check_sel_ptr(sel, "sel"));
+  const size_t need = moba_workspace_bytes(B, T, H, N, chunk);
+  if (ws_bytes < need) return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  {
+    const size_t tok = (size_t)B * T * H * N * sizeof(float), row = (size_t)B * H * T;
+    Spans sp;
+    sp.rd(q, tok, "q");
+    sp.rd(k, tok, "k");
+    sp.rd(v, tok, "v");
+    sp.wr(y, tok, "y");
+    sp.wr(lse, row * sizeof(float), "lse");
+    sp.wr(sel, row * sizeof(uint64_t), "sel");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
+  HIPCHK(moba_launch_forward(B, T, H, chunk, topk, q, k, v, y, lse, sel, (float*)ws, stream),
+         "moba_forward launch");
+  return WKV7_OK;
+}
+
+extern "C" int moba_backward(int B, int T, int H, int N, int chunk, const float* q, const float* k,
+                             const float* v, const float* y, const float* lse, const uint64_t* sel,
+                             const float* dy, float* dq, float* dk, float* dv, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  CHK(check_moba(B, T, H, N, chunk, 1));
+  const float* ptr[] = {q, k, v, y, lse, dy, dq, dk, dv, (const float*)ws};
+  const char* nm[] = {"q", "k", "v", "y", "lse", "dy", "dq", "dk", "dv", "ws"};
+  for (int i = 0; i < 10; i++) CHK(check_f32_ptr(ptr[i], nm[i], true));
+  CHK(check_sel_ptr(sel, "sel"));
+  const size_t need = moba_workspace_bytes(B, T, H, N, chunk);
+  if (ws_bytes < need) return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  {
+    const size_t tok = (size_t)B * T * H * N * sizeof(float), row = (size_t)B * H * T;
+    Spans sp;
+    sp.rd(q, tok, "q");
+    sp.rd(k, tok, "k");
+    sp.rd(v, tok, "v");
+    sp.rd(y, tok, "y");
+    sp.rd(dy, tok, "dy");
+    sp.rd(lse, row * sizeof(float), "lse");
+    sp.rd(sel, row * sizeof(uint64_t), "sel");
+    sp.wr(dq, tok, "dq");
+    sp.wr(dk, tok, "dk");
+    sp.wr(dv, tok, "dv");
+    sp.wr(ws, need, "ws");
+    CHK(sp.check());
+  }
+  HIPCHK(moba_launch_backward(B, T, H, chunk, q, k, v, y, lse, sel, dy, dq, dk, dv, (float*)ws, stream),
+         "moba_backward launch");
   return WKV7_OK;
 }
