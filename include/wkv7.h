@@ -278,6 +278,12 @@ typedef struct {
   int n_layer, C, H, N, F, V, Dw, Da, Dv, Dg, use_ln0;
   int gemm_dtype;
   int train_recompute;
+  /* Hybrid stack (rwkv7_train_step only; 0 elsewhere): n_attn MoBA attention
+   * blocks interleaved with the n_layer RWKV-7 blocks as the fullmodel page's
+   * fm_build does: after every n_layer / n_attn RWKV-7 blocks one attention
+   * block, then the remaining RWKV-7 blocks.  moba_chunk and moba_topk are
+   * the attention's chunk length and chunk count (moba_forward). */
+  int n_attn, moba_chunk, moba_topk;
 } rwkv7_config;
 
 /* One block: LayerNorms, time-mix weights (layer_id = block index) and the
@@ -288,14 +294,27 @@ typedef struct {
   const float *cm_mu_k, *cm_Wk, *cm_Wv;
 } rwkv7_block;
 
+/* One MoBA attention block of a hybrid stack.  Page: "Foundry/cuda_kernels/
+ * fullmodel.cu", fm_attn_fwd / fm_attn_bwd: h1 = LN1(x); q, k, v = h1 Wq,
+ * h1 Wk, h1 Wv (heads of 64, [in][out] weights); y = the MoBA core
+ * (moba_forward); x1 = x + y Wo; h2 = LN2(x1); out = x1 + channel-mix(h2),
+ * the channel-mix as in rwkv7_block. */
+typedef struct {
+  const float *ln1_w, *ln1_b, *ln2_w, *ln2_b; /* [C] */
+  const float *Wq, *Wk, *Wv, *Wo;             /* [C][C] */
+  const float *cm_mu_k, *cm_Wk, *cm_Wv;
+} rwkv7_attn_block;
+
 /* Whole model.  blocks is a HOST array of n_layer rwkv7_block (the pointers
- * inside are device pointers); ln0_w/b may be NULL when use_ln0 == 0. */
+ * inside are device pointers); ln0_w/b may be NULL when use_ln0 == 0; attn
+ * a HOST array of n_attn rwkv7_attn_block (NULL when n_attn == 0). */
 typedef struct {
   const float *emb;            /* [V][C] */
   const float *ln0_w, *ln0_b;  /* [C] */
   const float *ln_out_w, *ln_out_b;
   const float *head;           /* [C][V] (not tied to emb) */
   const rwkv7_block *blocks;
+  const rwkv7_attn_block *attn;
 } rwkv7_model;
 
 size_t rwkv7_decode_workspace_bytes(const rwkv7_config *cfg, int B);
@@ -333,8 +352,15 @@ typedef struct {
 } rwkv7_block_grads;
 
 typedef struct {
+  float *ln1_w, *ln1_b, *ln2_w, *ln2_b;
+  float *Wq, *Wk, *Wv, *Wo;
+  float *cm_mu_k, *cm_Wk, *cm_Wv;
+} rwkv7_attn_grads;
+
+typedef struct {
   float *emb, *ln0_w, *ln0_b, *ln_out_w, *ln_out_b, *head;
   rwkv7_block_grads *blocks;
+  rwkv7_attn_grads *attn; /* HOST array of n_attn (NULL when n_attn == 0) */
 } rwkv7_model_grads;
 
 size_t rwkv7_train_workspace_bytes(const rwkv7_config *cfg, int B, int T);
@@ -361,6 +387,12 @@ size_t rwkv7_train_workspace_bytes(const rwkv7_config *cfg, int B, int T);
  * side: NULL, or a wkv7_side on which the weight gradients of the head, the
  * channel-mixes and the time-mixes run (as in timemix_backward), joined back
  * to `stream` within every block.
+ * Hybrid stack (cfg->n_attn > 0): the attention blocks (model->attn, their
+ * gradients grads->attn) sit in fm_build's interleave; their core is
+ * moba_forward / moba_backward with cfg->moba_chunk and cfg->moba_topk (at
+ * most 64 chunks per sequence), the backward holding the selection fixed as
+ * the page does; the RWKV-7 blocks keep their layer indices 0 .. n_layer-1
+ * (layer 0 publishes v_first).
  */
 int rwkv7_train_step(const rwkv7_config *cfg, const rwkv7_model *model,
                      rwkv7_model_grads *grads, int B, int T, const int *tokens,

@@ -35,7 +35,20 @@ class TmGrads(ctypes.Structure):
 
 class Rwkv7Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layer", "C", "H", "N", "F", "V", "Dw", "Da", "Dv",
-                                            "Dg", "use_ln0", "gemm_dtype", "train_recompute")]
+                                            "Dg", "use_ln0", "gemm_dtype", "train_recompute",
+                                            "n_attn", "moba_chunk", "moba_topk")]
+
+
+ATTN_FIELDS = ("ln1_w", "ln1_b", "ln2_w", "ln2_b", "Wq", "Wk", "Wv", "Wo", "cm_mu_k", "cm_Wk",
+               "cm_Wv")
+
+
+class Rwkv7AttnBlock(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ATTN_FIELDS]
+
+
+class Rwkv7AttnGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ATTN_FIELDS]
 
 
 class Rwkv7Block(ctypes.Structure):
@@ -46,7 +59,8 @@ class Rwkv7Block(ctypes.Structure):
 
 class Rwkv7Model(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("emb", "ln0_w", "ln0_b", "ln_out_w", "ln_out_b",
-                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7Block))]
+                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7Block)),
+                                                           ("attn", ctypes.POINTER(Rwkv7AttnBlock))]
 
 
 class Rwkv7BlockGrads(ctypes.Structure):
@@ -57,7 +71,8 @@ class Rwkv7BlockGrads(ctypes.Structure):
 
 class Rwkv7ModelGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("emb", "ln0_w", "ln0_b", "ln_out_w", "ln_out_b",
-                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7BlockGrads))]
+                                               "head")] + [("blocks", ctypes.POINTER(Rwkv7BlockGrads)),
+                                                           ("attn", ctypes.POINTER(Rwkv7AttnGrads))]
 
 
 class GdnShape(ctypes.Structure):
@@ -490,15 +505,20 @@ class DecodeModel:
         """cfg: dict n_layer, C, H, F, V, ranks=(Dw, Da, Dv, Dg), use_ln0,
         gemm_dtype ('f32' default, or 'bf16': bf16 operands, fp32 accumulation),
         train_recompute (0 default: keep every block's activations for the
-        training step's backward; 1: recompute each block from its input).
-        weights: dict of device tensors as laid out by synth.stack_model."""
+        training step's backward; 1: recompute each block from its input),
+        n_attn (0 default), moba_chunk, moba_topk: MoBA attention blocks of a
+        hybrid stack (training step only).
+        weights: dict of device tensors as laid out by synth.stack_model, plus
+        "attn": the attention blocks (synth.attn_blocks) when n_attn > 0."""
         L, C, H, F, V = cfg["n_layer"], cfg["C"], cfg["H"], cfg["F"], cfg["V"]
         Dw, Da, Dv, Dg = cfg["ranks"]
         gd = cfg.get("gemm_dtype", "f32")
         if gd not in ("f32", "bf16"):
             raise ValueError(f"gemm_dtype must be 'f32' or 'bf16', not {gd!r}")
+        NA = int(cfg.get("n_attn", 0))
         self.cfg = Rwkv7Config(L, C, H, 64, F, V, Dw, Da, Dv, Dg, int(cfg.get("use_ln0", 1)),
-                               1 if gd == "bf16" else 0, int(cfg.get("train_recompute", 0)))
+                               1 if gd == "bf16" else 0, int(cfg.get("train_recompute", 0)), NA,
+                               int(cfg.get("moba_chunk", 0)), int(cfg.get("moba_topk", 0)))
         self.w = weights
         blocks = (Rwkv7Block * L)()
         for l, bw in enumerate(weights["blocks"]):
@@ -517,6 +537,14 @@ class DecodeModel:
             t = weights.get(n)
             setattr(m, n, None if t is None else _need(t, (C,), torch.float32, n).data_ptr())
         m.blocks = ctypes.cast(blocks, ctypes.POINTER(Rwkv7Block))
+        if NA:
+            attn = (Rwkv7AttnBlock * NA)()
+            shapes = dict(Wq=(C, C), Wk=(C, C), Wv=(C, C), Wo=(C, C), cm_Wk=(C, F), cm_Wv=(F, C))
+            for a, aw in enumerate(weights["attn"]):
+                for n in ATTN_FIELDS:
+                    setattr(attn[a], n, _need(aw[n], shapes.get(n, (C,)), torch.float32, n).data_ptr())
+            self._attn = attn
+            m.attn = ctypes.cast(attn, ctypes.POINTER(Rwkv7AttnBlock))
         self.model = m
 
     def new_state(self, B, device="cuda"):
@@ -588,6 +616,16 @@ class TrainGrads:
             t = self.g[n]
             setattr(mg, n, None if t is None else t.data_ptr())
         mg.blocks = ctypes.cast(blocks, ctypes.POINTER(Rwkv7BlockGrads))
+        if c.n_attn:
+            self.g["attn"] = []
+            attn = (Rwkv7AttnGrads * c.n_attn)()
+            for a, aw in enumerate(w["attn"]):
+                ga = {n: mk(aw[n]) for n in ATTN_FIELDS}
+                for n in ATTN_FIELDS:
+                    setattr(attn[a], n, ga[n].data_ptr())
+                self.g["attn"].append(ga)
+            self._attn = attn
+            mg.attn = ctypes.cast(attn, ctypes.POINTER(Rwkv7AttnGrads))
         self.struct = mg
 
 

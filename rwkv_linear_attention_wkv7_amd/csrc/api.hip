@@ -959,6 +959,9 @@ int check_cfg(const rwkv7_config* c, int B) {
   if (c->C > stk_max_layernorm_width()) return fail(WKV7_EINVAL, "C=%d above the supported %d", c->C, stk_max_layernorm_width());
   if (c->n_layer < 1 || B < 1) return fail(WKV7_EINVAL, "n_layer and B must be >= 1");
   if (c->F < 4 || c->F % 4 || c->V < 4 || c->V % 4) return fail(WKV7_EINVAL, "F and V must be positive multiples of 4");
+  if (c->n_attn < 0) return fail(WKV7_EINVAL, "n_attn must be >= 0");
+  if (c->n_attn > 0 && (c->moba_chunk < 1 || c->moba_topk < 1 || c->moba_topk > 64))
+    return fail(WKV7_EINVAL, "attention blocks need moba_chunk >= 1 and moba_topk in [1, 64]");
   tm_shape s = {c->C, c->H, c->N, c->Dw, c->Da, c->Dv, c->Dg, c->n_layer > 1 ? 1 : 0};
   return check_tm_shape(&s, B, 1);
 }
@@ -1068,11 +1071,19 @@ void model_spans(Spans& sp, const rwkv7_config* cfg, const MT* M, bool written) 
     tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
     tm_weight_spans(sp, &s, &bl.tm, written);
   }
+  for (int a = 0; a < cfg->n_attn; a++) {
+    const auto& ab = M->attn[a];
+    add(ab.ln1_w, C, "attn ln1_w"); add(ab.ln1_b, C, "attn ln1_b");
+    add(ab.ln2_w, C, "attn ln2_w"); add(ab.ln2_b, C, "attn ln2_b");
+    add(ab.Wq, C * C, "Wq"); add(ab.Wk, C * C, "attn Wk"); add(ab.Wv, C * C, "attn Wv");
+    add(ab.Wo, C * C, "attn Wo");
+    add(ab.cm_mu_k, C, "attn cm_mu_k"); add(ab.cm_Wk, C * F, "attn cm_Wk"); add(ab.cm_Wv, F * C, "attn cm_Wv");
+  }
 }
 }  // namespace
 
 extern "C" size_t rwkv7_decode_workspace_bytes(const rwkv7_config* cfg, int B) {
-  if (check_cfg(cfg, B) != WKV7_OK) return 0;
+  if (check_cfg(cfg, B) != WKV7_OK || cfg->n_attn != 0) return 0;
   Carver c(nullptr);
   DecodeBufs d[DECODE_MAX_GROUPS];
   carve_decode_all(c, cfg, B, d);
@@ -1085,6 +1096,7 @@ extern "C" int rwkv7_decode_step(const rwkv7_config* cfg, const rwkv7_model* M, 
                                  const wkv7_side* side, hipStream_t st) {
   g_err[0] = 0;
   CHK(check_cfg(cfg, B));
+  if (cfg->n_attn != 0) return fail(WKV7_EINVAL, "attention blocks are supported by rwkv7_train_step only");
   const int prec = cfg->gemm_dtype == WKV7_BF16 ? GEMM_BF16 : GEMM_F32;
   if (!M || !M->blocks) return fail(WKV7_EINVAL, "model or model->blocks is NULL");
   CHK(check_f32_ptr(M->emb, "emb", true));
@@ -1172,6 +1184,15 @@ struct TrainBufs {
   TmBwdBufs tb;
   float* pack = nullptr;  // bf16 operand copies of the GEMMs (gemm_dtype == WKV7_BF16)
   size_t pack_bytes = 0;
+  // attention blocks (n_attn > 0): activations of each (or one reused set)
+  // and the backward's buffers
+  struct AttnActs {
+    float *h, *q, *k, *v, *y, *x1, *h2, *sh, *ka, *lse;
+    uint64_t* sel;
+  };
+  std::vector<AttnActs> aact;
+  float *dyc = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *mws = nullptr;
+  size_t mws_bytes = 0;
 };
 
 // Largest arena of bf16 operand copies any one GEMM launch of the training
@@ -1196,7 +1217,7 @@ tm_shape block_shape(const rwkv7_config* c, int l) {
 
 void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t) {
   const size_t BT = (size_t)B * T, tok = BT * cfg->C, L = cfg->n_layer;
-  t.block_in = c.take((L + 1) * tok);
+  t.block_in = c.take((L + cfg->n_attn + 1) * tok);
   t.x_emb = cfg->use_ln0 ? c.take(tok) : nullptr;
   float** toks[] = {&t.vf, &t.dvf, &t.h, &t.dsh, &t.dh, &t.dx, &t.dx1};
   for (float** p : toks) *p = c.take(tok);
@@ -1231,6 +1252,21 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   }
   tm_shape s = block_shape(cfg, 1);
   carve_bwd(c, &s, B, T, t.tb);
+  if (cfg->n_attn > 0) {
+    const size_t rows = BT / T * cfg->H * T;  // B H T
+    t.aact.resize(keep ? cfg->n_attn : 1);
+    for (auto& a : t.aact) {
+      float** bt[] = {&a.h, &a.q, &a.k, &a.v, &a.y, &a.x1, &a.h2, &a.sh};
+      for (float** p : bt) *p = c.take(tok);
+      a.ka = c.take(BT * cfg->F);
+      a.lse = c.take(rows);
+      a.sel = (uint64_t*)c.take(2 * rows);
+    }
+    float** bb[] = {&t.dyc, &t.dq, &t.dk, &t.dv};
+    for (float** p : bb) *p = c.take(tok);
+    t.mws_bytes = std::max(moba_kbar_floats(B, T, cfg->H, cfg->moba_chunk), rows) * sizeof(float);
+    t.mws = c.take(t.mws_bytes / sizeof(float));
+  }
 }
 
 }  // namespace
@@ -1289,6 +1325,21 @@ int check_train(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads
       CHK(check_f32_ptr(gb.tm.V2, "grad V2", true));
     }
   }
+  if (cfg->n_attn > 0) {
+    if (!M->attn || !G->attn) return fail(WKV7_EINVAL, "model/grads attn arrays are NULL with n_attn > 0");
+    if (moba_num_chunks(T, cfg->moba_chunk) > 64)
+      return fail(WKV7_EINVAL, "T=%d in chunks of %d gives more than 64 chunks", T, cfg->moba_chunk);
+    for (int a = 0; a < cfg->n_attn; a++) {
+      const rwkv7_attn_block& ab = M->attn[a];
+      const float* req[] = {ab.ln1_w, ab.ln1_b, ab.ln2_w, ab.ln2_b, ab.Wq, ab.Wk, ab.Wv, ab.Wo,
+                            ab.cm_mu_k, ab.cm_Wk, ab.cm_Wv};
+      for (const float* p : req) CHK(check_f32_ptr(p, "an attention-block weight", true));
+      const rwkv7_attn_grads& ga = G->attn[a];
+      float* gq[] = {ga.ln1_w, ga.ln1_b, ga.ln2_w, ga.ln2_b, ga.Wq, ga.Wk, ga.Wv, ga.Wo,
+                     ga.cm_mu_k, ga.cm_Wk, ga.cm_Wv};
+      for (float* p : gq) CHK(check_f32_ptr(p, "an attention-block gradient", true));
+    }
+  }
   if (!ws || ws_bytes < need)
     return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   CHK(check_f32_ptr(ws, "ws", true));
@@ -1308,6 +1359,24 @@ int check_train(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads
 struct StartState {
   const float *att_x_prev, *att_state, *ffn_x_prev;
 };
+
+// Stack order of a hybrid model (the fullmodel page's fm_build): after every
+// n_layer / n_attn RWKV-7 blocks one attention block, then the remaining
+// RWKV-7 blocks.  Entries: (0, RWKV-7 block index) or (1, attention block index).
+std::vector<std::pair<int, int>> block_order(int n_rwkv, int n_attn) {
+  std::vector<std::pair<int, int>> o;
+  if (n_attn == 0) {
+    for (int i = 0; i < n_rwkv; i++) o.push_back({0, i});
+    return o;
+  }
+  const int interval = n_rwkv / n_attn;
+  for (int a = 0; a < n_attn; a++) {
+    for (int j = a * interval; j < (a + 1) * interval; j++) o.push_back({0, j});
+    o.push_back({1, a});
+  }
+  for (int j = n_attn * interval; j < n_rwkv; j++) o.push_back({0, j});
+  return o;
+}
 int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* G, int B, int T,
               const int* tokens, const int* targets, float* loss, const StartState* st0, TrainBufs& t,
               const wkv7_side* sd, hipStream_t st) {
@@ -1328,12 +1397,12 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
   };
 
   const bool keep = cfg->train_recompute == 0;
-  // one block forward from bin(l) into bin(l+1), activations into a
-  auto block_fwd = [&](int l, BlockActs& a) -> int {
+  // RWKV-7 block l's forward from xin (its output is x1 + ka Wv), activations into a
+  auto block_fwd = [&](int l, const float* xin, BlockActs& a) -> int {
     const rwkv7_block& bl = M->blocks[l];
     tm_shape s = block_shape(cfg, l);
-    HIPCHK(hipMemcpyAsync(a.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
+    HIPCHK(hipMemcpyAsync(a.x1, xin, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, xin, bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
     CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), nullptr, a.x1, nullptr, a.tm,
                         st, false, 1.f, prec));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
@@ -1341,19 +1410,52 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
     return WKV7_OK;
   };
+  // attention block i's forward from xin (its output is x1 + ka Wv)
+  const int H = cfg->H;
+  auto attn_fwd = [&](int i, const float* xin, TrainBufs::AttnActs& a) -> int {
+    const rwkv7_attn_block& ab = M->attn[i];
+    HIPCHK(hipMemcpyAsync(a.x1, xin, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(stk_launch_layernorm(BT, C, xin, ab.ln1_w, ab.ln1_b, a.h, nullptr, nullptr, st), "attn ln1");
+    {
+      GemmBatch g;
+      g.count = 3;
+      const float* W[3] = {ab.Wq, ab.Wk, ab.Wv};
+      float* out[3] = {a.q, a.k, a.v};
+      for (int j = 0; j < 3; j++) g.p[j] = GemmProblem{BT, C, C, a.h, C, W[j], C, out[j], C, 0.f, EPI_NONE, nullptr, nullptr};
+      HIPCHK(gemm_batch(prec, false, false, g, st), "q/k/v proj");
+    }
+    HIPCHK(moba_launch_forward(B, T, H, cfg->moba_chunk, cfg->moba_topk, a.q, a.k, a.v, a.y, a.lse, a.sel,
+                               t.mws, st), "moba forward");
+    HIPCHK(gemm_run(prec, false, false, BT, C, C, a.y, C, ab.Wo, C, a.x1, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "o proj");
+    HIPCHK(stk_launch_layernorm(BT, C, a.x1, ab.ln2_w, ab.ln2_b, a.h2, nullptr, nullptr, st), "attn ln2");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, ab.cm_mu_k, a.sh, nullptr, st), "attn cm shift");
+    HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, ab.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "attn cm key");
+    return WKV7_OK;
+  };
+  const auto order = block_order(L, cfg->n_attn);
+  const int NB = (int)order.size();
 
   // ---------------- forward (every block's activations, or only its input, kept)
   HIPCHK(stk_launch_emb_gather(BT, C, V, tokens, M->emb, cfg->use_ln0 ? t.x_emb : bin(0), st), "embedding");
   if (cfg->use_ln0)
     HIPCHK(stk_launch_layernorm(BT, C, t.x_emb, M->ln0_w, M->ln0_b, bin(0), nullptr, nullptr, st), "ln0");
-  for (int l = 0; l < L; l++) {
-    BlockActs& a = t.act[keep ? l : 0];
-    CHK(block_fwd(l, a));
-    float* xo = bin(l + 1);
-    HIPCHK(hipMemcpyAsync(xo, a.x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(gemm_run(prec, false, false, BT, C, F, a.ka, F, M->blocks[l].cm_Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+  for (int pos = 0; pos < NB; pos++) {
+    const int i = order[pos].second;
+    const float *x1, *ka, *Wv;
+    if (order[pos].first == 0) {
+      BlockActs& a = t.act[keep ? i : 0];
+      CHK(block_fwd(i, bin(pos), a));
+      x1 = a.x1, ka = a.ka, Wv = M->blocks[i].cm_Wv;
+    } else {
+      TrainBufs::AttnActs& a = t.aact[keep ? i : 0];
+      CHK(attn_fwd(i, bin(pos), a));
+      x1 = a.x1, ka = a.ka, Wv = M->attn[i].cm_Wv;
+    }
+    float* xo = bin(pos + 1);
+    HIPCHK(hipMemcpyAsync(xo, x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, ka, F, Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
   }
-  HIPCHK(stk_launch_layernorm(BT, C, bin(L), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
+  HIPCHK(stk_launch_layernorm(BT, C, bin(NB), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
   HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, t.n_valid, st), "cross-entropy");
 
@@ -1379,15 +1481,70 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
   HIPCHK(gemm_run(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
   HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
                       splitk_for(C, V, BT), t.splitk, ss), "dhead");
-  HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(L), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
+  HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(NB), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
   HIPCHK(reduce_ln(G->ln_out_w, G->ln_out_b), "ln_out grads");
   HIPCHK(stk_launch_fill_zero(t.dvf, tokC, st), "zero dv_first");
-  for (int l = L - 1; l >= 0; l--) {
+  auto join_side = [&]() -> hipError_t {
+    if (!sd) return hipSuccess;
+    hipError_t r = hipEventRecord(sd->ev[2], ss);
+    return r != hipSuccess ? r : hipStreamWaitEvent(st, sd->ev[2], 0);
+  };
+  // attention block i's backward (upstream t.dx; result into t.dx)
+  auto attn_bwd = [&](int i, int pos) -> int {
+    const rwkv7_attn_block& ab = M->attn[i];
+    rwkv7_attn_grads& ga = G->attn[i];
+    TrainBufs::AttnActs& a = t.aact[keep ? i : 0];
+    if (!keep) CHK(attn_fwd(i, bin(pos), a));  // recompute this block's forward from its input
+    // channel-mix backward (as in the RWKV-7 blocks)
+    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, ab.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "attn dfk");
+    HIPCHK(fork_here(), "backward fork");
+    HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, ga.cm_Wv, C, 0.f, EPI_NONE, nullptr,
+                    splitk_for(F, C, BT), t.splitk, ss), "attn dWv");
+    HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, ga.cm_Wk, F, 0.f, EPI_NONE, nullptr,
+                    splitk_for(C, F, BT), t.splitk, ss), "attn dWk");
+    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, ab.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "attn dsh");
+    HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, nullptr, ab.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "attn cm shift bwd");
+    {
+      VecOut o = {{ga.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
+      HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT, C), C, o, st), "attn cm mu grad");
+    }
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, ab.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "attn ln2 bwd");
+    HIPCHK(reduce_ln(ga.ln2_w, ga.ln2_b), "attn ln2 grads");
+    // output projection: dy_core = dx1 Wo^T, dWo = y^T dx1
+    HIPCHK(gemm_run(prec, false, true, BT, C, C, t.dx1, C, ab.Wo, C, t.dyc, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "attn dy");
+    HIPCHK(fork_here(), "backward fork");  // t.dx1 complete
+    HIPCHK(gemm_run(prec, true, false, C, C, BT, a.y, C, t.dx1, C, ga.Wo, C, 0.f, EPI_NONE, nullptr,
+                    splitk_for(C, C, BT), t.splitk, ss), "attn dWo");
+    HIPCHK(moba_launch_backward(B, T, H, cfg->moba_chunk, a.q, a.k, a.v, a.y, a.lse, a.sel, t.dyc, t.dq,
+                                t.dk, t.dv, t.mws, st), "moba backward");
+    HIPCHK(fork_here(), "backward fork");  // dq, dk, dv complete
+    const float* dqkv[3] = {t.dq, t.dk, t.dv};
+    const float* Wqkv[3] = {ab.Wq, ab.Wk, ab.Wv};
+    float* gqkv[3] = {ga.Wq, ga.Wk, ga.Wv};
+    for (int j = 0; j < 3; j++) {
+      HIPCHK(gemm_run(prec, true, false, C, C, BT, a.h, C, dqkv[j], C, gqkv[j], C, 0.f, EPI_NONE, nullptr,
+                      splitk_for(C, C, BT), t.splitk, ss), "attn dWq/dWk/dWv");
+      HIPCHK(gemm_run(prec, false, true, BT, C, C, dqkv[j], C, Wqkv[j], C, t.dh, C, j ? 1.f : 0.f, EPI_NONE,
+                      nullptr, 1, nullptr, st), "attn dh1");
+    }
+    // the side stream's weight gradients read t.dx, t.dx1 and this block's
+    // activations: joined before t.dx is written again
+    HIPCHK(join_side(), "backward join");
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), ab.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "attn ln1 bwd");
+    HIPCHK(reduce_ln(ga.ln1_w, ga.ln1_b), "attn ln1 grads");
+    return WKV7_OK;
+  };
+  for (int pos = NB - 1; pos >= 0; pos--) {
+    if (order[pos].first == 1) {
+      CHK(attn_bwd(order[pos].second, pos));
+      continue;
+    }
+    const int l = order[pos].second;
     const rwkv7_block& bl = M->blocks[l];
     rwkv7_block_grads& gb = G->blocks[l];
     tm_shape s = block_shape(cfg, l);
     BlockActs& a = t.act[keep ? l : 0];
-    if (!keep) CHK(block_fwd(l, a));  // recompute this block's forward from its input
+    if (!keep) CHK(block_fwd(l, bin(pos), a));  // recompute this block's forward from its input
     // channel-mix backward
     HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "dfk");
     HIPCHK(fork_here(), "backward fork");  // t.dx and t.dfk complete
@@ -1407,7 +1564,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
                          nullptr, st, prec, sd));
-    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(l), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }
   const float* demb_src = t.dx;
@@ -1543,7 +1700,7 @@ int replay_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int T, cons
 }  // namespace
 
 extern "C" size_t rwkv7_online_workspace_bytes(const rwkv7_config* cfg, int B, int S) {
-  if (check_cfg(cfg, B) != WKV7_OK || S < 1) return 0;
+  if (check_cfg(cfg, B) != WKV7_OK || S < 1 || cfg->n_attn != 0) return 0;
   Carver c(nullptr);
   TrainBufs t;
   carve_train(c, cfg, B, S, t);
@@ -1558,6 +1715,7 @@ extern "C" int rwkv7_online_segment(const rwkv7_config* cfg, const rwkv7_model* 
                                     float* att_state, float* ffn_x_prev, float* loss, void* ws,
                                     size_t ws_bytes, const wkv7_side* side, hipStream_t st) {
   g_err[0] = 0;
+  if (cfg && cfg->n_attn != 0) return fail(WKV7_EINVAL, "attention blocks are supported by rwkv7_train_step only");
   if (!opt) return fail(WKV7_EINVAL, "optimiser settings are NULL");
   if (opt->optimizer != 0 && opt->optimizer != 1) return fail(WKV7_EINVAL, "optimizer must be 0 (SGD) or 1 (Adam)");
   if (!(opt->lr >= 0.f) || !(opt->clip >= 0.f) || opt->lr > 1e30f || opt->clip > 1e30f)
