@@ -20,6 +20,10 @@ the headline alone.  Workloads:
              C=256, vocab 256): 256 streams x 64 steps from their live state,
              backward through the segment, Adam update, live-state replay,
              fp32 (tokens/s)
+  hybrid     hybrid training step: 12 RWKV-7 blocks and 4 MoBA attention
+             blocks (one after every three), C=1024 H=16 FFN 4096, vocab 65536,
+             B=4 T=2048, attention in chunks of 64 with top-4 chunks, bf16
+             GEMM operands (tokens/s)
   gdn        GatedDeltaNet layer forward + through-gradient backward, B=2
              windows of T=4096, 12 key heads / 24 value heads of size 128,
              4 causal conv taps, fp32 (tokens/s)
@@ -408,6 +412,78 @@ def setup_train():
                 roof=roof, cpu=cpu, extra=lambda v, ms: {"loss": round(float(loss.item()), 5)})
 
 
+def moba_attended_keys(T, chunk, topk):
+    """Keys each query attends, summed over the T queries of one head: its own
+    chunk up to itself plus min(topk - 1, earlier chunks) full chunks."""
+    return sum(t % chunk + 1 + chunk * min(topk - 1, t // chunk) for t in range(T))
+
+
+def setup_hybrid():
+    import numpy as np
+    import torch
+
+    from rwkv_linear_attention_wkv7_amd import binding, synth
+    L, NA, C, H, F, V, B, T = 12, 4, 1024, 16, 4096, 65536, 4, 2048
+    chunk, topk = 64, 4
+    ranks = (64, 64, 32, 128)
+    m = synth.stack_model(C, H, F, V, L, ranks, seed=0, use_ln0=False)
+    m["attn"] = synth.attn_blocks(C, F, NA, seed=0)
+    dev = torch.device("cuda")
+    d = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    w = {k: d(v) for k, v in m.items() if k not in ("blocks", "attn")}
+    w["blocks"] = [{k: ({kk: d(vv) for kk, vv in v.items()} if k == "tm" else d(v))
+                    for k, v in b.items()} for b in m["blocks"]]
+    w["attn"] = [{k: d(v) for k, v in a.items()} for a in m["attn"]]
+    dm = binding.DecodeModel(dict(n_layer=L, C=C, H=H, F=F, V=V, ranks=ranks, use_ln0=0,
+                                  gemm_dtype="bf16", n_attn=NA, moba_chunk=chunk, moba_topk=topk), w)
+    grads = binding.TrainGrads(dm)
+    tok = synth.token_ids(B, T + 1, V, seed=0, name="hybrid_tokens")
+    x = torch.from_numpy(np.ascontiguousarray(tok[:, :-1])).to(dev)
+    y = torch.from_numpy(np.ascontiguousarray(tok[:, 1:])).to(dev)
+    loss = torch.empty(1, device=dev)
+    ws = torch.empty(binding.rwkv7_train_workspace_bytes(dm, B, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws)
+
+    # dominant kernel of the attention: the MoBA core backward of one block
+    # ([4][2048][16 x 64] q, k, v), against the fp32 ALU ceiling: 5 products of
+    # 2 N flop per attended (query, key) pair (S recomputed, dP, dQ, dK, dV)
+    g = torch.Generator(device=dev).manual_seed(0)
+    q, k, v, dy = (torch.randn(B, T, C, device=dev, generator=g) for _ in range(4))
+    yo, lse, sel = binding.moba_forward(q, k, v, H, chunk, topk)
+    mws = torch.empty(binding.lib().moba_workspace_bytes(B, T, H, 64, chunk), dtype=torch.uint8,
+                      device=dev)
+
+    def dom():
+        binding.moba_backward(q, k, v, yo, lse, sel, dy, H, chunk, ws=mws)
+
+    flops = 5.0 * 2 * 64 * moba_attended_keys(T, chunk, topk) * B * H
+    roof = dict(kernel=f"moba_backward (B={B} T={T} H={H}, chunks of {chunk}, top-{topk}: dQ pass + "
+                       "dK/dV pass)", bound="alu", work=flops, unit="TFLOP/s",
+                peak=PEAK["alu_fp32"][0], fn=dom, key="moba_bwd",
+                src=["rwkv_linear_attention_wkv7_amd/csrc/moba.hip"])
+
+    def cpu():
+        from oracle import moba
+        from oracle import wkv7 as ow
+        Ts = 512
+        ocfg = dict(C=C, H=H, F=F, V=V, n_layer=L, n_attn=NA, chunk=chunk, topk=topk)
+        reps, dt = repeat_for(lambda: moba.train_step(m, ocfg, tok[:1, :Ts], tok[:1, 1:Ts + 1]))
+        return dict(value=reps * Ts / dt, unit="tokens/s", cores=ow.num_threads(), kind="oracle",
+                    sample=f"1 sequence x {Ts} tokens of the same model (f64 forward+backward) "
+                           f"{reps} times, {dt:.1f} s")
+
+    cfg = {"workload": "hybrid RWKV-7 / MoBA training step (12 RWKV-7 + 4 attention blocks, LM head, "
+                       "log-softmax CE) forward+backward",
+           "n_layer": L, "n_attn": NA, "C": C, "H": H, "N": 64, "ffn": F, "vocab": V,
+           "moba_chunk": chunk, "moba_topk": topk, "lora_ranks_w_a_v_g": list(ranks), "B": B, "T": T,
+           "gemm": "bf16 operands, fp32 accumulation (matrix cores)", "global_batch": B, "seq_len": T,
+           "parallelism": "single GPU"}
+    return dict(step=step, tokens=B * T, unit="tokens/s", dtype="bf16 GEMM / f32", config=cfg,
+                roof=roof, cpu=cpu, extra=lambda v, ms: {"loss": round(float(loss.item()), 5)})
+
+
 def setup_gdn():
     import numpy as np
     import torch
@@ -553,9 +629,9 @@ def ctypes_byref(x):
 
 WORKLOADS = {"wkv7_small": setup_wkv7_small, "decode": setup_decode, "timemix": setup_timemix,
              "wkv7_long": setup_wkv7_long, "train": setup_train, "gdn": setup_gdn,
-             "online": setup_online,
+             "online": setup_online, "hybrid": setup_hybrid,
              "wkv7_long_chunked": lambda: setup_wkv7_long(chunked=True)}
-ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train", "online", "gdn")
+ORDER = ("wkv7_small", "decode", "timemix", "wkv7_long", "train", "online", "gdn", "hybrid")
 
 
 def run_workload(name, steps, warmup, roof_iters, with_cpu):
