@@ -452,11 +452,11 @@ def setup_hybrid():
     g = torch.Generator(device=dev).manual_seed(0)
     q, k, v, dy = (torch.randn(B, T, C, device=dev, generator=g) for _ in range(4))
     yo, lse, sel = binding.moba_forward(q, k, v, H, chunk, topk)
-    mws = torch.empty(binding.lib().moba_workspace_bytes(B, T, H, 64, chunk), dtype=torch.uint8,
+    mws = torch.empty(binding.lib().moba_workspace_bytes(B, T, H, 64, chunk, topk), dtype=torch.uint8,
                       device=dev)
 
     def dom():
-        binding.moba_backward(q, k, v, yo, lse, sel, dy, H, chunk, ws=mws)
+        binding.moba_backward(q, k, v, yo, lse, sel, dy, H, chunk, topk, ws=mws)
 
     flops = 5.0 * 2 * 64 * moba_attended_keys(T, chunk, topk) * B * H
     roof = dict(kernel=f"moba_backward (B={B} T={T} H={H}, chunks of {chunk}, top-{topk}: dQ pass + "

@@ -509,16 +509,20 @@ int gdn_backward(const gdn_shape *s, const gdn_weights *W, int B, int T, const f
  * q, k, v, y, dy, dq, dk, dv: [B][T][H][N] fp32 (16-byte aligned).
  * lse: [B][H][T] fp32, the row log-sum-exp; sel: [B][H][T] 64-bit masks of
  * the attended chunks (bit c: chunk c).  At most 64 chunks per sequence;
- * 1 <= topk <= 64.  ws: moba_workspace_bytes() bytes (both calls).
+ * 1 <= topk <= 64.  ws: moba_workspace_bytes() bytes (both calls, the same
+ * chunk and topk).  With chunks of 64 keys only the selected (query, chunk)
+ * pairs are computed: per chunk the queries that selected it are gathered,
+ * their per-chunk softmax partials merged per query; other chunk lengths
+ * walk 64-query tiles over the 64-key tiles any of their queries selected.
  * Every output is written, summed in a fixed order (no atomics).
  */
-size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk);
+size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk, int topk);
 int moba_forward(int B, int T, int H, int N, int chunk, int topk, const float *q, const float *k,
                  const float *v, float *y, float *lse, uint64_t *sel, void *ws, size_t ws_bytes,
                  hipStream_t stream);
 /* Gradients of <dy, y> with the selection sel held fixed (as the page's
  * backward does): needs the forward's y, lse and sel for the same q, k, v. */
-int moba_backward(int B, int T, int H, int N, int chunk, const float *q, const float *k,
+int moba_backward(int B, int T, int H, int N, int chunk, int topk, const float *q, const float *k,
                   const float *v, const float *y, const float *lse, const uint64_t *sel,
                   const float *dy, float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
                   hipStream_t stream);

@@ -158,11 +158,11 @@ def lib():
         L.gdn_forward.restype = _i
         L.gdn_backward.argtypes = [gp, gw, _i, _i] + [_vp] * 11 + [_sz, _vp]
         L.gdn_backward.restype = _i
-        L.moba_workspace_bytes.argtypes = [_i] * 5
+        L.moba_workspace_bytes.argtypes = [_i] * 6
         L.moba_workspace_bytes.restype = _sz
         L.moba_forward.argtypes = [_i] * 6 + [_vp] * 7 + [_sz, _vp]
         L.moba_forward.restype = _i
-        L.moba_backward.argtypes = [_i] * 5 + [_vp] * 11 + [_sz, _vp]
+        L.moba_backward.argtypes = [_i] * 6 + [_vp] * 11 + [_sz, _vp]
         L.moba_backward.restype = _i
         L.rwkv7_online_workspace_bytes.argtypes = [cp, _i, _i]
         L.rwkv7_online_workspace_bytes.restype = _sz
@@ -758,7 +758,7 @@ def moba_forward(q, k, v, H, chunk, topk, y=None, ws=None):
         y = torch.empty_like(q)
     lse = torch.empty((B, H, T), device=q.device, dtype=torch.float32)
     sel = torch.empty((B, H, T), device=q.device, dtype=torch.int64)
-    n = lib().moba_workspace_bytes(B, T, H, C // H, chunk)
+    n = lib().moba_workspace_bytes(B, T, H, C // H, chunk, topk)
     if ws is None:
         ws = torch.empty(max(n, 1), device=q.device, dtype=torch.uint8)
     _check(lib().moba_forward(B, T, H, C // H, chunk, topk, _p(q), _p(k), _p(v), _p(y), _p(lse),
@@ -766,17 +766,18 @@ def moba_forward(q, k, v, H, chunk, topk, y=None, ws=None):
     return y, lse, sel
 
 
-def moba_backward(q, k, v, y, lse, sel, dy, H, chunk, ws=None):
-    """Gradients (dq, dk, dv) of <dy, y> with the selection sel held fixed."""
+def moba_backward(q, k, v, y, lse, sel, dy, H, chunk, topk, ws=None):
+    """Gradients (dq, dk, dv) of <dy, y> with the selection sel held fixed
+    (chunk and topk as in the forward)."""
     B, T, C = q.shape
     for n, t in (("q", q), ("k", k), ("v", v), ("y", y), ("dy", dy)):
         _need(t, (B, T, C), torch.float32, n)
     _need(lse, (B, H, T), torch.float32, "lse")
     _need(sel, (B, H, T), torch.int64, "sel")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    n = lib().moba_workspace_bytes(B, T, H, C // H, chunk)
+    n = lib().moba_workspace_bytes(B, T, H, C // H, chunk, topk)
     if ws is None:
         ws = torch.empty(max(n, 1), device=q.device, dtype=torch.uint8)
-    _check(lib().moba_backward(B, T, H, C // H, chunk, _p(q), _p(k), _p(v), _p(y), _p(lse), _p(sel),
+    _check(lib().moba_backward(B, T, H, C // H, chunk, topk, _p(q), _p(k), _p(v), _p(y), _p(lse), _p(sel),
                                _p(dy), _p(dq), _p(dk), _p(dv), _p(ws), ws.numel(), _stream()))
     return dq, dk, dv

@@ -1264,8 +1264,8 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
     }
     float** bb[] = {&t.dyc, &t.dq, &t.dk, &t.dv};
     for (float** p : bb) *p = c.take(tok);
-    t.mws_bytes = std::max(moba_kbar_floats(B, T, cfg->H, cfg->moba_chunk), rows) * sizeof(float);
-    t.mws = c.take(t.mws_bytes / sizeof(float));
+    t.mws_bytes = moba_ws_bytes(B, T, cfg->H, cfg->moba_chunk, cfg->moba_topk);
+    t.mws = c.take(t.mws_bytes / sizeof(float) + 1);
   }
 }
 
@@ -1515,8 +1515,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     HIPCHK(fork_here(), "backward fork");  // t.dx1 complete
     HIPCHK(gemm_run(prec, true, false, C, C, BT, a.y, C, t.dx1, C, ga.Wo, C, 0.f, EPI_NONE, nullptr,
                     splitk_for(C, C, BT), t.splitk, ss), "attn dWo");
-    HIPCHK(moba_launch_backward(B, T, H, cfg->moba_chunk, a.q, a.k, a.v, a.y, a.lse, a.sel, t.dyc, t.dq,
-                                t.dk, t.dv, t.mws, st), "moba backward");
+    HIPCHK(moba_launch_backward(B, T, H, cfg->moba_chunk, cfg->moba_topk, a.q, a.k, a.v, a.y, a.lse, a.sel,
+                                t.dyc, t.dq, t.dk, t.dv, t.mws, st), "moba backward");
     HIPCHK(fork_here(), "backward fork");  // dq, dk, dv complete
     const float* dqkv[3] = {t.dq, t.dk, t.dv};
     const float* Wqkv[3] = {ab.Wq, ab.Wk, ab.Wv};
@@ -1956,10 +1956,9 @@ int check_sel_ptr(const void* p, const char* name) {
 }
 }  // namespace
 
-extern "C" size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk) {
-  if (check_moba(B, T, H, N, chunk, 1) != WKV7_OK) return 0;
-  const size_t kb = moba_kbar_floats(B, T, H, chunk), d = (size_t)B * H * T;
-  return std::max(kb, d) * sizeof(float);
+extern "C" size_t moba_workspace_bytes(int B, int T, int H, int N, int chunk, int topk) {
+  if (check_moba(B, T, H, N, chunk, topk) != WKV7_OK) return 0;
+  return moba_ws_bytes(B, T, H, chunk, topk);
 }
 
 extern "C" int moba_forward(int B, int T, int H, int N, int chunk, int topk, const float* q,
@@ -1971,7 +1970,7 @@ extern "C" int moba_forward(int B, int T, int H, int N, int chunk, int topk, con
   const char* nm[] = {"q", "k", "v", "y", "lse", "ws"};
   for (int i = 0; i < 6; i++) CHK(check_f32_ptr(ptr[i], nm[i], true));
   CHK(check_sel_ptr(sel, "sel"));
-  const size_t need = moba_workspace_bytes(B, T, H, N, chunk);
+  const size_t need = moba_workspace_bytes(B, T, H, N, chunk, topk);
   if (ws_bytes < need) return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   {
     const size_t tok = (size_t)B * T * H * N * sizeof(float), row = (size_t)B * H * T;
@@ -1985,22 +1984,22 @@ extern "C" int moba_forward(int B, int T, int H, int N, int chunk, int topk, con
     sp.wr(ws, need, "ws");
     CHK(sp.check());
   }
-  HIPCHK(moba_launch_forward(B, T, H, chunk, topk, q, k, v, y, lse, sel, (float*)ws, stream),
+  HIPCHK(moba_launch_forward(B, T, H, chunk, topk, q, k, v, y, lse, sel, ws, stream),
          "moba_forward launch");
   return WKV7_OK;
 }
 
-extern "C" int moba_backward(int B, int T, int H, int N, int chunk, const float* q, const float* k,
-                             const float* v, const float* y, const float* lse, const uint64_t* sel,
-                             const float* dy, float* dq, float* dk, float* dv, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+extern "C" int moba_backward(int B, int T, int H, int N, int chunk, int topk, const float* q,
+                             const float* k, const float* v, const float* y, const float* lse,
+                             const uint64_t* sel, const float* dy, float* dq, float* dk, float* dv,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
-  CHK(check_moba(B, T, H, N, chunk, 1));
+  CHK(check_moba(B, T, H, N, chunk, topk));
   const float* ptr[] = {q, k, v, y, lse, dy, dq, dk, dv, (const float*)ws};
   const char* nm[] = {"q", "k", "v", "y", "lse", "dy", "dq", "dk", "dv", "ws"};
   for (int i = 0; i < 10; i++) CHK(check_f32_ptr(ptr[i], nm[i], true));
   CHK(check_sel_ptr(sel, "sel"));
-  const size_t need = moba_workspace_bytes(B, T, H, N, chunk);
+  const size_t need = moba_workspace_bytes(B, T, H, N, chunk, topk);
   if (ws_bytes < need) return fail(WKV7_ENOSPC, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   {
     const size_t tok = (size_t)B * T * H * N * sizeof(float), row = (size_t)B * H * T;
@@ -2018,7 +2017,7 @@ extern "C" int moba_backward(int B, int T, int H, int N, int chunk, const float*
     sp.wr(ws, need, "ws");
     CHK(sp.check());
   }
-  HIPCHK(moba_launch_backward(B, T, H, chunk, q, k, v, y, lse, sel, dy, dq, dk, dv, (float*)ws, stream),
+  HIPCHK(moba_launch_backward(B, T, H, chunk, topk, q, k, v, y, lse, sel, dy, dq, dk, dv, ws, stream),
          "moba_backward launch");
   return WKV7_OK;
 }

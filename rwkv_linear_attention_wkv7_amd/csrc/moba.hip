@@ -9,8 +9,10 @@
 //   attended keys) V.
 //
 // Selection: one wave per (b, t, h), lane c scoring chunk c; the chosen
-// chunks are one 64-bit mask per query (at most 64 chunks).  The forward is
-// a flash-style pass: a workgroup per (b, h, 64-query tile) walks the
+// chunks are one 64-bit mask per query (at most 64 chunks).  Chunks of 64
+// keys take the gathered path further below, which computes only the
+// selected (query, chunk) pairs.  Other chunk lengths use tile kernels: the
+// forward is a flash-style pass: a workgroup per (b, h, 64-query tile) walks the
 // 64-key tiles up to its own, skipping tiles no query of the tile selected;
 // S = Q K^T and P V run as 64x64x64 register-tiled products from LDS
 // (thread (ty, tx) owns rows 4 ty.. and columns 4 tx..), with an online
@@ -21,6 +23,7 @@
 // (dV = P^T dY, dK = dS^T Q / 8), so every output is summed in a fixed
 // order by one workgroup (no atomics).
 
+#include <algorithm>
 #include <cstdint>
 
 #include "common.hpp"
@@ -392,36 +395,362 @@ __global__ __launch_bounds__(256) void bwd_dkv(int T, int H, int chunk, int nc, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sparse path for chunks of 64 keys (one key tile per chunk).  Per (b, h,
+// chunk c) the queries that selected c are gathered into an ordered list
+// (ascending position), and only those (query, chunk) pairs are computed, 64
+// gathered queries at a time:
+//   forward: per pair the chunk's softmax partial (row max m, sum l and the
+//   unnormalised P V) goes to slot j of the query (j = rank of c among the
+//   query's chunks); a merge combines the slots in chunk order into y and
+//   the log-sum-exp;
+//   backward: one workgroup per chunk walks its list: dV and dK of the chunk
+//   are summed over the gathered queries in list order, and each pair's dQ
+//   share goes to the query's slot j; a merge sums the slots in chunk order.
+
+// list[bh][c][0 .. cnt) = the positions t >= 64 c whose mask has bit c, in
+// ascending order.  Grid (chunks, B H), 256 threads.
+__global__ __launch_bounds__(256) void sp_list(int T, int nc, const uint64_t* __restrict__ sel,
+                                               int* __restrict__ list, int* __restrict__ cnt) {
+  __shared__ int wsum[4];
+  __shared__ int base;
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t* sb = sel + (size_t)bh * T;
+  int* out = list + ((size_t)bh * nc + c) * T;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int t0 = c * TS; t0 < T; t0 += 256) {
+    const int t = t0 + tid;
+    const bool on = t < T && ((sb[t] >> c) & 1);
+    const uint64_t bal = __ballot(on);
+    const int before = __popcll(bal & ((lane ? (~(uint64_t)0 >> (64 - lane)) : (uint64_t)0)));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; w++) off += wsum[w];
+    if (on) out[off + before] = t;
+    __syncthreads();
+    if (tid == 0) base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) cnt[(size_t)bh * nc + c] = base;
+}
+
+// Gathered tile loads: rows are the listed positions idx[0 .. n), rows past
+// n are zeros.
+__device__ __forceinline__ void gather_T(float (*X)[LP], const float* __restrict__ src, const int* idx,
+                                         int n, int b, int T, int C, int h) {
+  for (int i = threadIdx.x; i < TS * HN / 4; i += 256) {
+    const int row = i / (HN / 4), c = (i % (HN / 4)) * 4;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < n) v = *reinterpret_cast<const f4*>(src + ((size_t)b * T + idx[row]) * C + h * HN + c);
+    X[c][row] = v[0];
+    X[c + 1][row] = v[1];
+    X[c + 2][row] = v[2];
+    X[c + 3][row] = v[3];
+  }
+}
+__device__ __forceinline__ void gather_R(float (*X)[LP], const float* __restrict__ src, const int* idx,
+                                         int n, int b, int T, int C, int h) {
+  for (int i = threadIdx.x; i < TS * HN / 4; i += 256) {
+    const int row = i / (HN / 4), c = (i % (HN / 4)) * 4;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < n) v = *reinterpret_cast<const f4*>(src + ((size_t)b * T + idx[row]) * C + h * HN + c);
+    *reinterpret_cast<f4*>(&X[row][c]) = v;
+  }
+}
+
+// Slot of chunk c among the chunks of mask m (their rank in ascending order).
+__device__ __forceinline__ int slot_of(uint64_t m, int c) {
+  return __popcll(m & (c ? (~(uint64_t)0 >> (64 - c)) : (uint64_t)0));
+}
+
+// Forward partials: grid (blocks of 64 listed queries, chunks, B H).
+// po[bh][t][j][64] = sum_key e^(s - m) v, pm / pl[bh][t][j] = m and the sum of
+// e^(s - m) over the chunk's allowed keys (s = q.k / 8).
+__global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const float* __restrict__ q,
+                                              const float* __restrict__ k, const float* __restrict__ v,
+                                              const uint64_t* __restrict__ sel, const int* __restrict__ list,
+                                              const int* __restrict__ cnt, float* __restrict__ po,
+                                              float* __restrict__ pm, float* __restrict__ pl) {
+  __shared__ float qT[HN][LP], kT[HN][LP], vR[TS][LP], pT[TS][LP];
+  __shared__ int idx[TS];
+  const int blk = blockIdx.x, c = blockIdx.y, bh = blockIdx.z, b = bh / H, h = bh - b * H, C = H * HN;
+  const int n_all = cnt[(size_t)bh * nc + c];
+  if (blk * TS >= n_all) return;  // uniform
+  const int n = min(TS, n_all - blk * TS);
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int* lst = list + ((size_t)bh * nc + c) * T + blk * TS;
+  if (tid < TS) idx[tid] = tid < n ? lst[tid] : 0;
+  __syncthreads();
+  gather_T(qT, q, idx, n, b, T, C, h);
+  load_T(kT, k, b, T, C, h, c * TS);
+  load_R(vR, v, b, T, C, h, c * TS);
+  __syncthreads();
+  float s[4][4] = {};
+  mm_tt(qT, kT, ty, tx, s);
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 4 * ty + i;
+    const int t = r < n ? idx[r] : -1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int key = c * TS + 4 * tx + j;
+      const bool ok = t >= 0 && key <= t;  // key <= t < T
+      s[i][j] = ok ? s[i][j] * SCALE : -INFINITY;
+      mx = fmaxf(mx, s[i][j]);
+    }
+    m[i] = fmaxf(max16(mx), -1e30f);
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      s[i][j] = expf(s[i][j] - m[i]);
+      rs += s[i][j];
+    }
+    l[i] = sum16(rs);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) pT[4 * tx + j][4 * ty + i] = s[i][j];
+  __syncthreads();
+  float o[4][4] = {};
+  mm_rr(pT, vR, ty, tx, o);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 4 * ty + i;
+    if (r >= n) continue;
+    const int t = idx[r];
+    const int j = slot_of(sel[(size_t)bh * T + t], c);
+    if (j >= K) continue;  // a mask with more chunks than topk (not one the selection wrote)
+    const size_t e = ((size_t)bh * T + t) * K + j;
+    *reinterpret_cast<f4*>(po + e * HN + 4 * tx) = f4{o[i][0], o[i][1], o[i][2], o[i][3]};
+    if (tx == 0) {
+      pm[e] = m[i];
+      pl[e] = l[i];
+    }
+  }
+}
+
+// Merge: 16 lanes per (b, h, t); the query's slots combined in chunk order.
+__global__ __launch_bounds__(256) void sp_merge(int BHT, int T, int H, int K, const uint64_t* __restrict__ sel,
+                                                const float* __restrict__ po, const float* __restrict__ pm,
+                                                const float* __restrict__ pl, float* __restrict__ y,
+                                                float* __restrict__ lse) {
+  const int g = blockIdx.x * 16 + (threadIdx.x >> 4), l16 = threadIdx.x & 15;
+  if (g >= BHT) return;
+  const int bh = g / T, t = g - bh * T, b = bh / H, h = bh - b * H, C = H * HN;
+  const int ns = min(__popcll(sel[g]), K);
+  const size_t e0 = (size_t)g * K;
+  float M = -INFINITY;
+  for (int j = 0; j < ns; j++) M = fmaxf(M, pm[e0 + j]);
+  float L = 0.f;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < ns; j++) {
+    const float w = expf(pm[e0 + j] - M);
+    L += pl[e0 + j] * w;
+    o += w * *reinterpret_cast<const f4*>(po + (e0 + j) * HN + 4 * l16);
+  }
+  *reinterpret_cast<f4*>(y + ((size_t)b * T + t) * C + h * HN + 4 * l16) = o * (1.0f / L);
+  if (l16 == 0) lse[g] = M + logf(L);
+}
+
+// D[bh][t] = dy . y (16 lanes per row).
+__global__ __launch_bounds__(256) void sp_rowdot(int BHT, int T, int H, const float* __restrict__ y,
+                                                 const float* __restrict__ dy, float* __restrict__ D) {
+  const int g = blockIdx.x * 16 + (threadIdx.x >> 4), l16 = threadIdx.x & 15;
+  if (g >= BHT) return;  // whole 16-lane groups exit together
+  const int bh = g / T, t = g - bh * T, b = bh / H, h = bh - b * H, C = H * HN;
+  const size_t e = ((size_t)b * T + t) * C + h * HN + 4 * l16;
+  const f4 a = *reinterpret_cast<const f4*>(dy + e), c = *reinterpret_cast<const f4*>(y + e);
+  const float d = sum16(a[0] * c[0] + a[1] * c[1] + a[2] * c[2] + a[3] * c[3]);
+  if (l16 == 0) D[g] = d;
+}
+
+// Backward per chunk: grid (chunks, B H).  dk, dv of the chunk's keys; each
+// listed query's dq share into pq[bh][t][j][64] (scaled).
+__global__ __launch_bounds__(256) void sp_bwd(int T, int H, int nc, int K, const float* __restrict__ q,
+                                              const float* __restrict__ k, const float* __restrict__ v,
+                                              const float* __restrict__ lse, const float* __restrict__ Din,
+                                              const uint64_t* __restrict__ sel, const float* __restrict__ dy,
+                                              const int* __restrict__ list, const int* __restrict__ cnt,
+                                              float* __restrict__ dk, float* __restrict__ dv,
+                                              float* __restrict__ pq) {
+  __shared__ float kT[HN][LP], vT[HN][LP], kR[TS][LP], qT[HN][LP], doT[HN][LP], qR[TS][LP], doR[TS][LP];
+  __shared__ float pds[TS][LP], dsT[TS][LP];
+  __shared__ int idx[TS];
+  __shared__ float Ls[TS], Ds[TS];
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int n_all = cnt[(size_t)bh * nc + c];
+  const int* lst = list + ((size_t)bh * nc + c) * T;
+  load_T(kT, k, b, T, C, h, c * TS);
+  load_T(vT, v, b, T, C, h, c * TS);
+  load_R(kR, k, b, T, C, h, c * TS);
+  float adk[4][4] = {}, adv[4][4] = {};
+  for (int b0 = 0; b0 < n_all; b0 += TS) {
+    const int n = min(TS, n_all - b0);
+    __syncthreads();  // the previous block's readers are done
+    if (tid < TS) {
+      const int t = tid < n ? lst[b0 + tid] : 0;
+      idx[tid] = t;
+      Ls[tid] = tid < n ? lse[(size_t)bh * T + t] : 0.f;
+      Ds[tid] = tid < n ? Din[(size_t)bh * T + t] : 0.f;
+    }
+    __syncthreads();
+    gather_T(qT, q, idx, n, b, T, C, h);
+    gather_T(doT, dy, idx, n, b, T, C, h);
+    gather_R(qR, q, idx, n, b, T, C, h);
+    gather_R(doR, dy, idx, n, b, T, C, h);
+    __syncthreads();
+    // rows of S^T: keys 4 ty + i; columns: gathered queries 4 tx + j
+    float s[4][4] = {}, dp[4][4] = {};
+    mm_tt(kT, qT, ty, tx, s);
+    mm_tt(vT, doT, ty, tx, dp);
+    float ds[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int qi = 4 * tx + j;
+      const int t = qi < n ? idx[qi] : -1;
+      const float L = Ls[qi], D = Ds[qi];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int key = c * TS + 4 * ty + i;
+        const float p = (t >= 0 && key <= t) ? expf(s[i][j] * SCALE - L) : 0.f;
+        ds[i][j] = p * (dp[i][j] - D);
+        pds[qi][4 * ty + i] = p;
+        dsT[4 * ty + i][qi] = ds[i][j];
+      }
+    }
+    __syncthreads();
+    mm_rr(pds, doR, ty, tx, adv);  // dv[key][d] += sum_q P[q][key] dy[q][d]
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) pds[4 * tx + j][4 * ty + i] = ds[i][j];
+    __syncthreads();
+    mm_rr(pds, qR, ty, tx, adk);  // dk[key][d] += sum_q dS[q][key] q[q][d]
+    float aq[4][4] = {};
+    mm_rr(dsT, kR, ty, tx, aq);   // dq share[q][d] = sum_key dS[q][key] k[key][d]
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * ty + i;
+      if (r >= n) continue;
+      const int t = idx[r];
+      const int j = slot_of(sel[(size_t)bh * T + t], c);
+      if (j >= K) continue;  // as in sp_fwd
+      *reinterpret_cast<f4*>(pq + (((size_t)bh * T + t) * K + j) * HN + 4 * tx) =
+          f4{aq[i][0] * SCALE, aq[i][1] * SCALE, aq[i][2] * SCALE, aq[i][3] * SCALE};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int key = c * TS + 4 * ty + i;
+    if (key >= T) continue;
+    const size_t e = ((size_t)b * T + key) * C + h * HN + 4 * tx;
+    *reinterpret_cast<f4*>(dk + e) = f4{adk[i][0] * SCALE, adk[i][1] * SCALE, adk[i][2] * SCALE, adk[i][3] * SCALE};
+    *reinterpret_cast<f4*>(dv + e) = f4{adv[i][0], adv[i][1], adv[i][2], adv[i][3]};
+  }
+}
+
+// dq = sum over the query's slots in chunk order (16 lanes per row).
+__global__ __launch_bounds__(256) void sp_dq(int BHT, int T, int H, int K, const uint64_t* __restrict__ sel,
+                                             const float* __restrict__ pq, float* __restrict__ dq) {
+  const int g = blockIdx.x * 16 + (threadIdx.x >> 4), l16 = threadIdx.x & 15;
+  if (g >= BHT) return;
+  const int bh = g / T, t = g - bh * T, b = bh / H, h = bh - b * H, C = H * HN;
+  const int ns = min(__popcll(sel[g]), K);
+  f4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < ns; j++) a += *reinterpret_cast<const f4*>(pq + ((size_t)g * K + j) * HN + 4 * l16);
+  *reinterpret_cast<f4*>(dq + ((size_t)b * T + t) * C + h * HN + 4 * l16) = a;
+}
+
 }  // namespace mobak
 
 int moba_num_chunks(int T, int chunk) { return (T + chunk - 1) / chunk; }
 
-size_t moba_kbar_floats(int B, int T, int H, int chunk) {
-  return (size_t)B * H * moba_num_chunks(T, chunk) * mobak::HN;
+namespace {
+// Workspace layout (both directions): chunk means, the row sums D, and for
+// chunks of 64 the query lists, their counts and the per-slot partials.
+struct MobaWs {
+  float *kbar, *D, *part, *pm, *pl;
+  int *list, *cnt;
+  size_t bytes;
+};
+MobaWs moba_carve(void* base, int B, int T, int H, int chunk, int topk) {
+  const int nc = moba_num_chunks(T, chunk), K = std::min(topk, nc);
+  const size_t BH = (size_t)B * H, rows = BH * T;
+  MobaWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    off = (off + 255) & ~(size_t)255;
+    char* p = base ? (char*)base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  w.kbar = (float*)take(BH * nc * mobak::HN * sizeof(float));
+  w.D = (float*)take(rows * sizeof(float));
+  if (chunk == mobak::TS) {
+    w.list = (int*)take(BH * nc * T * sizeof(int));
+    w.cnt = (int*)take(BH * nc * sizeof(int));
+    w.part = (float*)take(rows * K * mobak::HN * sizeof(float));
+    w.pm = (float*)take(rows * K * sizeof(float));
+    w.pl = (float*)take(rows * K * sizeof(float));
+  }
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+size_t moba_ws_bytes(int B, int T, int H, int chunk, int topk) {
+  return moba_carve(nullptr, B, T, H, chunk, topk).bytes;
 }
 
 hipError_t moba_launch_forward(int B, int T, int H, int chunk, int topk, const float* q, const float* k,
-                               const float* v, float* y, float* lse, uint64_t* sel, float* kbar,
+                               const float* v, float* y, float* lse, uint64_t* sel, void* ws,
                                hipStream_t st) {
   const int nc = moba_num_chunks(T, chunk);
-  hipLaunchKernelGGL(mobak::kbar, dim3(nc, B * H), dim3(64), 0, st, T, H, chunk, k, kbar);
+  const MobaWs w = moba_carve(ws, B, T, H, chunk, topk);
+  hipLaunchKernelGGL(mobak::kbar, dim3(nc, B * H), dim3(64), 0, st, T, H, chunk, k, w.kbar);
   const size_t waves = (size_t)B * T * H;
   hipLaunchKernelGGL(mobak::select, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, B, T, H, chunk, nc,
-                     topk, q, kbar, sel);
+                     topk, q, w.kbar, sel);
   const int nqt = (T + mobak::TS - 1) / mobak::TS;
-  hipLaunchKernelGGL(mobak::fwd, dim3(nqt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, sel, y, lse);
+  if (chunk != mobak::TS) {
+    hipLaunchKernelGGL(mobak::fwd, dim3(nqt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, sel, y, lse);
+    return hipGetLastError();
+  }
+  const int K = std::min(topk, nc), BHT = B * H * T;
+  hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
+  hipLaunchKernelGGL(mobak::sp_fwd, dim3(nqt, nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, sel, w.list,
+                     w.cnt, w.part, w.pm, w.pl);
+  hipLaunchKernelGGL(mobak::sp_merge, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part,
+                     w.pm, w.pl, y, lse);
   return hipGetLastError();
 }
 
-hipError_t moba_launch_backward(int B, int T, int H, int chunk, const float* q, const float* k,
+hipError_t moba_launch_backward(int B, int T, int H, int chunk, int topk, const float* q, const float* k,
                                 const float* v, const float* y, const float* lse, const uint64_t* sel,
-                                const float* dy, float* dq, float* dk, float* dv, float* Dbuf,
+                                const float* dy, float* dq, float* dk, float* dv, void* ws,
                                 hipStream_t st) {
   const int nc = moba_num_chunks(T, chunk);
   const int nt = (T + mobak::TS - 1) / mobak::TS;
-  hipLaunchKernelGGL(mobak::bwd_dq, dim3(nt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, y, lse,
-                     sel, dy, dq, Dbuf);
-  hipLaunchKernelGGL(mobak::bwd_dkv, dim3(nt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, lse, Dbuf,
-                     sel, dy, dk, dv);
+  const MobaWs w = moba_carve(ws, B, T, H, chunk, topk);
+  if (chunk != mobak::TS) {
+    hipLaunchKernelGGL(mobak::bwd_dq, dim3(nt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, y, lse,
+                       sel, dy, dq, w.D);
+    hipLaunchKernelGGL(mobak::bwd_dkv, dim3(nt, B * H), dim3(256), 0, st, T, H, chunk, nc, q, k, v, lse, w.D,
+                       sel, dy, dk, dv);
+    return hipGetLastError();
+  }
+  const int K = std::min(topk, nc), BHT = B * H * T;
+  hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
+  hipLaunchKernelGGL(mobak::sp_rowdot, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, y, dy, w.D);
+  hipLaunchKernelGGL(mobak::sp_bwd, dim3(nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, lse, w.D, sel,
+                     dy, w.list, w.cnt, dk, dv, w.part);
+  hipLaunchKernelGGL(mobak::sp_dq, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part, dq);
   return hipGetLastError();
 }

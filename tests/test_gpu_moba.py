@@ -58,7 +58,7 @@ def _run(hip, B, T, H, chunk, topk, seed, heads=None):
     print(f"[moba] B={B} T={T} H={H} chunk={chunk} topk={topk}", flush=True)
     d = lambda x: torch.from_numpy(x).cuda()
     y, lse, sel = hip.moba_forward(d(q), d(k), d(v), H, chunk, topk)
-    dq, dk, dv = hip.moba_backward(d(q), d(k), d(v), y, lse, sel, d(dy), H, chunk)
+    dq, dk, dv = hip.moba_backward(d(q), d(k), d(v), y, lse, sel, d(dy), H, chunk, topk)
     torch.cuda.synchronize()
     nc = (T + chunk - 1) // chunk
     sb = _bits(sel.cpu().numpy(), nc)
@@ -86,6 +86,11 @@ def _run(hip, B, T, H, chunk, topk, seed, heads=None):
     (1, 64, 2, 1, 64),     # one key per chunk, every chunk selected: causal attention
     (1, 300, 2, 5, 64),    # 60 chunks, all selected
     (1, 96, 2, 32, 1),     # current chunk only
+    # chunks of 64 keys: the gathered (query, chunk) path
+    (1, 70, 2, 64, 2),     # two chunks, the second partial
+    (2, 300, 2, 64, 3),    # five chunks, partial last one
+    (1, 320, 1, 64, 1),    # current chunk only
+    (1, 512, 2, 64, 64),   # every chunk: causal attention
 ])
 def test_moba_parity_small(hip, B, T, H, chunk, topk):
     _run(hip, B, T, H, chunk, topk, seed=T + chunk + topk)
