@@ -465,7 +465,8 @@ __device__ __forceinline__ int slot_of(uint64_t m, int c) {
   return __popcll(m & (c ? (~(uint64_t)0 >> (64 - c)) : (uint64_t)0));
 }
 
-// Forward partials: grid (blocks of 64 listed queries, chunks, B H).
+// Forward partials: grid (chunks, B H); the workgroup walks the chunk's
+// list in blocks of 64 queries (K and V of the chunk loaded once).
 // po[bh][t][j][64] = sum_key e^(s - m) v, pm / pl[bh][t][j] = m and the sum of
 // e^(s - m) over the chunk's allowed keys (s = q.k / 8).
 __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const float* __restrict__ q,
@@ -475,61 +476,63 @@ __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const
                                               float* __restrict__ pm, float* __restrict__ pl) {
   __shared__ float qT[HN][LP], kT[HN][LP], vR[TS][LP], pT[TS][LP];
   __shared__ int idx[TS];
-  const int blk = blockIdx.x, c = blockIdx.y, bh = blockIdx.z, b = bh / H, h = bh - b * H, C = H * HN;
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
   const int n_all = cnt[(size_t)bh * nc + c];
-  if (blk * TS >= n_all) return;  // uniform
-  const int n = min(TS, n_all - blk * TS);
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int* lst = list + ((size_t)bh * nc + c) * T + blk * TS;
-  if (tid < TS) idx[tid] = tid < n ? lst[tid] : 0;
-  __syncthreads();
-  gather_T(qT, q, idx, n, b, T, C, h);
+  const int* lst = list + ((size_t)bh * nc + c) * T;
   load_T(kT, k, b, T, C, h, c * TS);
   load_R(vR, v, b, T, C, h, c * TS);
-  __syncthreads();
-  float s[4][4] = {};
-  mm_tt(qT, kT, ty, tx, s);
-  float m[4], l[4];
+  for (int b0 = 0; b0 < n_all; b0 += TS) {
+    const int n = min(TS, n_all - b0);
+    __syncthreads();  // the previous block's readers are done
+    if (tid < TS) idx[tid] = tid < n ? lst[b0 + tid] : 0;
+    __syncthreads();
+    gather_T(qT, q, idx, n, b, T, C, h);
+    __syncthreads();
+    float s[4][4] = {};
+    mm_tt(qT, kT, ty, tx, s);
+    float m[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = 4 * ty + i;
-    const int t = r < n ? idx[r] : -1;
-    float mx = -INFINITY;
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * ty + i;
+      const int t = r < n ? idx[r] : -1;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int key = c * TS + 4 * tx + j;
-      const bool ok = t >= 0 && key <= t;  // key <= t < T
-      s[i][j] = ok ? s[i][j] * SCALE : -INFINITY;
-      mx = fmaxf(mx, s[i][j]);
+      for (int j = 0; j < 4; j++) {
+        const int key = c * TS + 4 * tx + j;
+        const bool ok = t >= 0 && key <= t;  // key <= t < T
+        s[i][j] = ok ? s[i][j] * SCALE : -INFINITY;
+        mx = fmaxf(mx, s[i][j]);
+      }
+      m[i] = fmaxf(max16(mx), -1e30f);
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        s[i][j] = expf(s[i][j] - m[i]);
+        rs += s[i][j];
+      }
+      l[i] = sum16(rs);
     }
-    m[i] = fmaxf(max16(mx), -1e30f);
-    float rs = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      s[i][j] = expf(s[i][j] - m[i]);
-      rs += s[i][j];
-    }
-    l[i] = sum16(rs);
-  }
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+      for (int j = 0; j < 4; j++) pT[4 * tx + j][4 * ty + i] = s[i][j];
+    __syncthreads();
+    float o[4][4] = {};
+    mm_rr(pT, vR, ty, tx, o);
 #pragma unroll
-    for (int j = 0; j < 4; j++) pT[4 * tx + j][4 * ty + i] = s[i][j];
-  __syncthreads();
-  float o[4][4] = {};
-  mm_rr(pT, vR, ty, tx, o);
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int r = 4 * ty + i;
-    if (r >= n) continue;
-    const int t = idx[r];
-    const int j = slot_of(sel[(size_t)bh * T + t], c);
-    if (j >= K) continue;  // a mask with more chunks than topk (not one the selection wrote)
-    const size_t e = ((size_t)bh * T + t) * K + j;
-    *reinterpret_cast<f4*>(po + e * HN + 4 * tx) = f4{o[i][0], o[i][1], o[i][2], o[i][3]};
-    if (tx == 0) {
-      pm[e] = m[i];
-      pl[e] = l[i];
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * ty + i;
+      if (r >= n) continue;
+      const int t = idx[r];
+      const int j = slot_of(sel[(size_t)bh * T + t], c);
+      if (j >= K) continue;  // a mask with more chunks than topk (not one the selection wrote)
+      const size_t e = ((size_t)bh * T + t) * K + j;
+      *reinterpret_cast<f4*>(po + e * HN + 4 * tx) = f4{o[i][0], o[i][1], o[i][2], o[i][3]};
+      if (tx == 0) {
+        pm[e] = m[i];
+        pl[e] = l[i];
+      }
     }
   }
 }
@@ -725,7 +728,7 @@ hipError_t moba_launch_forward(int B, int T, int H, int chunk, int topk, const f
   }
   const int K = std::min(topk, nc), BHT = B * H * T;
   hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
-  hipLaunchKernelGGL(mobak::sp_fwd, dim3(nqt, nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, sel, w.list,
+  hipLaunchKernelGGL(mobak::sp_fwd, dim3(nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, sel, w.list,
                      w.cnt, w.part, w.pm, w.pl);
   hipLaunchKernelGGL(mobak::sp_merge, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part,
                      w.pm, w.pl, y, lse);

@@ -301,10 +301,11 @@ __host__ __device__ inline int sb_groups(int C) { return 256 / sb_lanes(C); }
 // Channel-mix token-shift backward: dx = dsh (1 - mu) + dsh[t+1] mu,
 // dx_prev (t = 0) = dsh mu, partial dmu = sum dsh (prev - x).
 // Grid (channel blocks of 256 float4 columns, token blocks).  A thread owns
-// one float4 column and walks SB_TOK consecutive tokens, carrying the
-// previous token's x and the next token's dsh in registers, so x, dsh and dx
-// each cross HBM once and every wave touches 1 KB of one row per access.
-// Each workgroup writes one partial row of dmu (its groups summed through LDS).
+// one float4 column and SB_TOK consecutive tokens: it loads x of those tokens
+// and the one before, and dsh of those tokens and the one after, all at once
+// (so their latencies overlap), then computes; x, dsh and dx cross HBM once
+// and every wave touches 1 KB of one row per access.  Each workgroup writes
+// one partial row of dmu (its groups summed through LDS).
 __global__ __launch_bounds__(256) void cm_shift_bwd(int BT, int T, int C, const float* __restrict__ x,
                                                     const float* __restrict__ x_prev,
                                                     const float* __restrict__ mu,
@@ -318,38 +319,35 @@ __global__ __launch_bounds__(256) void cm_shift_bwd(int BT, int T, int C, const 
   const f4* X = reinterpret_cast<const f4*>(x);
   const f4* D = reinterpret_cast<const f4*>(dsh);
   f4* DX = reinterpret_cast<f4*>(dx);
-  f4 pm = {0.f, 0.f, 0.f, 0.f};
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  f4 pm = zero;
   const int bt0 = (blockIdx.y * G + grp) * SB_TOK;
-  const int bt1 = min(BT, bt0 + SB_TOK);
-  if (grp < G && c4 < C4 && bt0 < bt1) {
+  if (grp < G && c4 < C4 && bt0 < BT) {
     const f4 m = reinterpret_cast<const f4*>(mu)[c4];
-    const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    auto xprev = [&](int b) {
-      return x_prev ? reinterpret_cast<const f4*>(x_prev)[(size_t)b * C4 + c4] : zero;
-    };
-    int t = bt0 % T, b = bt0 / T;
-    f4 prev = t > 0 ? X[(size_t)(bt0 - 1) * C4 + c4] : xprev(b);
-    f4 g = D[(size_t)bt0 * C4 + c4];
-    for (int bt = bt0; bt < bt1; bt++) {
-      const size_t e = (size_t)bt * C4 + c4;
-      const f4 xv = X[e];
-      const bool last = t == T - 1;
-      const f4 gn = last ? zero : D[e + C4];  // the next token of the same sequence
-      pm += g * (prev - xv);
-      DX[e] = g * (1.0f - m) + gn * m;
-      if (t == 0 && dx_prev) reinterpret_cast<f4*>(dx_prev)[(size_t)b * C4 + c4] = g * m;
-      if (last) {  // the next token opens sequence b + 1
-        t = 0;
+    // xs[i]: x of token bt0 - 1 + i; ds[i]: dsh of token bt0 + i (zeros outside [0, BT))
+    f4 xs[SB_TOK + 1], ds[SB_TOK + 1];
+#pragma unroll
+    for (int i = 0; i <= SB_TOK; i++) {
+      const int tx_ = bt0 - 1 + i, td = bt0 + i;
+      xs[i] = (tx_ >= 0 && tx_ < BT) ? X[(size_t)tx_ * C4 + c4] : zero;
+      ds[i] = td < BT ? D[(size_t)td * C4 + c4] : zero;
+    }
+    const int t0 = bt0 % T, b0 = bt0 / T;
+#pragma unroll
+    for (int i = 0; i < SB_TOK; i++) {
+      const int bt = bt0 + i;
+      if (bt >= BT) break;
+      int t = t0 + i, b = b0;
+      while (t >= T) {  // at most a few wraps (T >= 1)
+        t -= T;
         b++;
-        if (bt + 1 < bt1) {
-          prev = xprev(b);
-          g = D[e + C4];
-        }
-      } else {
-        t++;
-        prev = xv;
-        g = gn;
       }
+      const f4 prev = t > 0 ? xs[i] : (x_prev ? reinterpret_cast<const f4*>(x_prev)[(size_t)b * C4 + c4] : zero);
+      const f4 g = ds[i];
+      const f4 gn = t < T - 1 ? ds[i + 1] : zero;  // the next token of the same sequence
+      pm += g * (prev - xs[i + 1]);
+      DX[(size_t)bt * C4 + c4] = g * (1.0f - m) + gn * m;
+      if (t == 0 && dx_prev) reinterpret_cast<f4*>(dx_prev)[(size_t)b * C4 + c4] = g * m;
     }
   }
   red[threadIdx.x] = pm;
