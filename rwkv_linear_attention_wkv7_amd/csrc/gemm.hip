@@ -591,9 +591,14 @@ __device__ __forceinline__ void frags_bf(const char* X, int s, int woff, int i, 
 // BF: both operands are bf16 in global memory, k-contiguous (A [M][K], B
 // [N][K], leading dimensions in bf16 elements), copied as they are: 64 k per
 // stage and no conversion in the multiply loop.
-template <int TJ, bool TA, bool TB, bool BF = false>
+// NS: LDS stages (2 or 3).  A stage's copies are issued NS - 1 stages ahead
+// of its multiply, so with one wave per SIMD (TJ = 4), where a stage's
+// matrix work is shorter than a copy's latency, three stages keep two copies
+// in flight behind the one being multiplied.
+template <int TJ, bool TA, bool TB, bool BF = false, int NS = 2>
 __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch, int kslice) {
   static_assert(!BF || (!TA && TB), "bf16 operands come k-contiguous");
+  static_assert(NS == 2 || NS == 3, "two or three stages");
   constexpr int BM = 256, BN = 32 * TJ, NW = TJ == 8 ? 8 : 4;
   constexpr int ES = BF ? 2 : 4, KST = BF ? 64 : BK;  // element bytes, k per stage
   constexpr int FA = 2, FB = 4;  // 32-row fragments per wave
@@ -601,10 +606,9 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
   // the N side is always read in the interleaved order (float4 stores along
   // rows of C); the M side only when A is row-contiguous
   constexpr bool AIL = !AKC;
-  __shared__ __attribute__((aligned(1024))) float As0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float Bs0[BN * BK];
-  __shared__ __attribute__((aligned(1024))) float As1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float Bs1[BN * BK];
+  // each stage: the A tile (BM rows of 128 bytes) then the B tile (BN rows)
+  constexpr int SA = BM * 128, SB = BN * 128;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * (SA + SB)];
 
   const bool split = batch.count == 1 && gridDim.z > 1;
   const GemmProblem& P = batch.p[split ? 0 : blockIdx.z];
@@ -664,28 +668,31 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
     }
   };
 
-  // Two stages; the copy of stage s+1 runs while stage s is multiplied.
-  // Before a stage is read every wave waits for its own copies into it
-  // (vmcnt), then the barrier makes all waves' copies visible; the barrier
+  // NS stages in a ring; the copies of stage s + NS - 1 are issued before
+  // stage s is multiplied.  Before a stage is read every wave waits for its
+  // own copies into it (vmcnt: the copies of the later stages may stay in
+  // flight), then the barrier makes all waves' copies visible; the barrier
   // after the multiply frees the stage for the copy issued next.
-  const uint32_t la0 = (uint32_t)(size_t)(lds_void*)As0, lb0 = (uint32_t)(size_t)(lds_void*)Bs0;
-  const uint32_t la1 = (uint32_t)(size_t)(lds_void*)As1, lb1 = (uint32_t)(size_t)(lds_void*)Bs1;
+  const uint32_t l0 = (uint32_t)(size_t)(lds_void*)smem;
+  auto issue = [&](int st) {
+    const int bi = st % NS;
+    ca.issue(Ab + (size_t)st * astep, l0 + bi * (SA + SB), wave);
+    cb.issue(Bb + (size_t)st * bstep, l0 + bi * (SA + SB) + SA, wave);
+  };
   const int nk = (kend - kbeg) / KST;
-  ca.issue(Ab, la0, wave);
-  cb.issue(Bb, lb0, wave);
+  for (int st = 0; st < NS - 1 && st < nk; st++) issue(st);
   for (int s = 0; s < nk; s++) {
-    const bool odd = s & 1;
-    if (s + 1 < nk) {
-      Ab += astep;
-      Bb += bstep;
-      ca.issue(Ab, odd ? la0 : la1, wave);
-      cb.issue(Bb, odd ? lb0 : lb1, wave);
+    if (s + NS - 1 < nk) issue(s + NS - 1);
+    const int later = min(s + NS - 1, nk - 1) - s;  // stages after s still in flight
+    if (NS == 3 && later >= 2)
+      wait_vmcnt<2 * NDMA>();
+    else if (later >= 1)
       wait_vmcnt<NDMA>();
-    } else {
+    else
       wait_vmcnt<0>();
-    }
     lds_barrier();
-    compute(odd ? As1 : As0, odd ? Bs1 : Bs0);
+    const char* st_base = smem + (s % NS) * (SA + SB);
+    compute(reinterpret_cast<const float*>(st_base), reinterpret_cast<const float*>(st_base + SA));
     lds_barrier();
   }
 
@@ -904,7 +911,7 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
   if (tj == 8)
     hipLaunchKernelGGL((dmak::gemm_dma<8, false, true, true>), grid, dim3(512), 0, st, pb, kslice);
   else
-    hipLaunchKernelGGL((dmak::gemm_dma<4, false, true, true>), grid, dim3(256), 0, st, pb, kslice);
+    hipLaunchKernelGGL((dmak::gemm_dma<4, false, true, true, 3>), grid, dim3(256), 0, st, pb, kslice);
   return hipGetLastError();
 }
 
