@@ -432,19 +432,29 @@ __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int
         G[i] = gt * dsp;
       }
       dgp = rowsum16(dgp);
-      // sums over the wave's four columns (lanes l, l^16, l^32, l^48)
+      // sums over the wave's four columns (lanes l, l^16, l^32, l^48) as a
+      // reduce-scatter: the 2 RPL values (dq^ then dk^ shares of this lane's
+      // key rows) are split in four quarters of RPL / 2, and lane l ends with
+      // quarter l / 16 summed over the four columns
+      constexpr int NQ = RPL / 2;
+      float x[2 * RPL];
 #pragma unroll
       for (int i = 0; i < RPL; i++) {
-        pq[i] = rows4sum(pq[i]);
-        pk[i] = rows4sum(pk[i]);
+        x[i] = pq[i];
+        x[RPL + i] = pk[i];
       }
+      rows4_reduce_scatter<NQ>(x);
       const float sg = rows4sum(dgp), sb = rows4sum(du * vmk);
       const int slot = tt % RF;
-      if (lane < 16) {
+      {
+        const int qtr = lane >> 4;  // quarter: 0, 1 = dq^ rows, 2, 3 = dk^ rows
+        float* dst = &red[wave][slot][(qtr >> 1) * DK + rg * RPL + (qtr & 1) * NQ];
+        if constexpr (NQ % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < RPL; i += 4) {
-          st4(&red[wave][slot][rg * RPL + i], f4{pq[i], pq[i + 1], pq[i + 2], pq[i + 3]});
-          st4(&red[wave][slot][DK + rg * RPL + i], f4{pk[i], pk[i + 1], pk[i + 2], pk[i + 3]});
+          for (int i = 0; i < NQ; i += 4) st4(dst + i, f4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+        } else {
+#pragma unroll
+          for (int i = 0; i < NQ; i++) dst[i] = x[i];
         }
         if (lane == 0) {
           red[wave][slot][2 * DK] = sg;
