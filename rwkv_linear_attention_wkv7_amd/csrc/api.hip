@@ -69,10 +69,8 @@ size_t tok_bytes(int B, int T, int H, int dtype) {
 }
 size_t state_bytes(int B, int H) { return (size_t)B * H * WKV7_N * WKV7_N * sizeof(float); }
 
-size_t ckpt_floats(int B, int T, int H) {
-  const int L = wkv7_ckpt_interval_const();
-  return (size_t)B * H * ((T + L - 1) / L) * WKV7_N * WKV7_N;
-}
+// checkpoint states plus the forward's per-token sa (see wkv7_ckpt_sa)
+size_t ckpt_floats(int B, int T, int H) { return wkv7_ckpt_total_floats(B, T, H); }
 
 // bump allocator over a workspace (or a dry run for size queries)
 struct Carver {
@@ -223,11 +221,24 @@ extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r
   return WKV7_OK;
 }
 
+namespace {
+// fp32 floats of the region both backward paths share (only one of them
+// produces results): the two-pass path's dsa and boundary state gradients,
+// or the single-pass path's column partials and segment hand-over buffers.
+size_t wkv7_bwd_region_floats(int B, int T, int H) {
+  Carver one(nullptr), two(nullptr);
+  one.take(wkv7_bwd_partial_floats(B, T, H));
+  one.take((size_t)2 * B * H * WKV7_N * WKV7_N);  // state-gradient hand-over between segments
+  two.take(wkv7_bwd2_ws_floats(B, T, H));
+  return (std::max(one.off, two.off) + sizeof(float) - 1) / sizeof(float);
+}
+}  // namespace
+
 extern "C" size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt) {
   if (N != WKV7_N || B < 1 || T < 1 || H < 1) return 0;
   Carver c(nullptr);
-  c.take(wkv7_bwd_partial_floats(B, T, H));
-  c.take((size_t)2 * B * H * WKV7_N * WKV7_N);  // state-gradient hand-over between segments
+  c.take(wkv7_bwd_region_floats(B, T, H));
+  c.take(1);  // path flag
   if (!have_ckpt) c.take(ckpt_floats(B, T, H));
   return c.off;
 }
@@ -285,8 +296,8 @@ int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void*
                       void* dk, void* dv, void* da, void* db, float* ds0, void* ws,
                       const wkv7_side* sd, hipStream_t stream) {
   Carver cv(ws);
-  float* part = cv.take(wkv7_bwd_partial_floats(B, T, H));
-  float* gbuf = cv.take((size_t)2 * B * H * WKV7_N * WKV7_N);
+  float* region = cv.take(wkv7_bwd_region_floats(B, T, H));
+  int* gate = reinterpret_cast<int*>(cv.take(1));
   const float* ck = ckpt;
   if (!ck) {
     float* tmp = cv.take(ckpt_floats(B, T, H));
@@ -295,18 +306,29 @@ int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void*
            "wkv7_backward checkpoint recompute");
     ck = tmp;
   }
+  // The two-pass backward (reverse state-gradient scan, then per-chunk
+  // matrix-core products) serves decays in [1/256, 1]; its scan raises the
+  // flag on any other decay, and then the single-pass kernels, launched after
+  // it with the same flag, produce the results instead (the products return
+  // at once).  Both use the one region.
+  HIPCHK(stk_launch_fill_zero(reinterpret_cast<float*>(gate), 1, stream), "wkv7_backward flag");
+  HIPCHK(wkv7_launch_backward2(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
+                               db, ds0, region, gate, stream),
+         "wkv7_backward launch");
+  float* part = region;
+  float* gbuf = region + ((wkv7_bwd_partial_floats(B, T, H) + 63) & ~(size_t)63);
   if (sd && wkv7_bwd_segments(T) > 1) {
     // long sequence: the reverse pass runs in segments, each segment's
     // partial reduction on the side stream overlapping the next segment's
     // pass; without a side stream, one pass
     HIPCHK(wkv7_launch_backward_segmented(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk,
-                                          dv, da, db, ds0, part, gbuf, stream, sd->stream,
+                                          dv, da, db, ds0, part, gbuf, gate, stream, sd->stream,
                                           sd->ev[1], sd->ev[3]),
            "wkv7_backward launch");
     return WKV7_OK;
   }
   HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
-                              db, ds0, part, stream),
+                              db, ds0, part, gate, stream),
          "wkv7_backward launch");
   return WKV7_OK;
 }
@@ -444,8 +466,7 @@ struct TmBwdBufs {
   float *dtg, *dg, *dy_wkv, *dr, *dkmod, *dvmod, *gr, *gw, *gk, *gv, *gA, *gB;
   float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *d_la, *d_lw, *d_lg, *d_lv;
   float *dxr, *dxw, *dxk, *dxv, *dxa, *dxg, *part_post, *part_pre, *part_shift, *splitk, *out_tmp;
-  float* wkv_part;
-  float* wkv_g;  // state-gradient hand-over between backward segments
+  float* wkv_ws;  // the two-pass WKV7 backward's dsa and boundary state gradients
 };
 
 // split-K factor for a weight gradient [Mo][No] reduced over BT tokens
@@ -484,8 +505,7 @@ void carve_bwd(Carver& c, const tm_shape* s, int B, int T, TmBwdBufs& m) {
   m.part_pre = c.take((size_t)5 * nblk * s->C);
   m.part_shift = c.take((size_t)6 * nblk * s->C);
   m.splitk = c.take(splitk_scratch(s, (int)BT));
-  m.wkv_part = c.take(wkv7_bwd_partial_floats(B, T, s->H));
-  m.wkv_g = c.take((size_t)2 * B * s->H * WKV7_N * WKV7_N);
+  m.wkv_ws = c.take(wkv7_bwd2_ws_floats(B, T, s->H));
   m.out_tmp = nullptr;
 }
 
@@ -674,16 +694,11 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
 
   HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
-  if (sd && wkv7_bwd_segments(T) > 1)  // segment reductions overlap on the side stream
-    HIPCHK(wkv7_launch_backward_segmented(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv,
-                                          bb.dy_wkv, m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA,
-                                          bb.gB, ds0, bb.wkv_part, bb.wkv_g, st, ss, sd->ev[1],
-                                          sd->ev[3]),
-           "wkv7 backward");
-  else
-    HIPCHK(wkv7_launch_backward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
-                              m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
-                              bb.wkv_part, st),
+  // the time-mix decay exp(-0.606531 sigmoid(.)) lies in [0.545, 1]: the
+  // two-pass backward applies to every call, no flag needed
+  HIPCHK(wkv7_launch_backward2(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, bb.dy_wkv,
+                               m.ckpt, dsT, bb.gr, bb.gw, bb.gk, bb.gv, bb.gA, bb.gB, ds0,
+                               bb.wkv_ws, nullptr, st),
          "wkv7 backward");
   HIPCHK(tm_launch_pre_bwd(p, st), "pre-wkv backward");
   const int Dw = s->Dw, Da = s->Da, Dg = s->Dg, Dv = s->Dv;

@@ -4,6 +4,23 @@
 #include <stdint.h>
 
 #define WKV7_N 64  // head size; the kernels are written for N = 64 only
+#define WKV7_CKL 16  // checkpoint interval of the WKV7 forward (tokens)
+
+// The WKV7 checkpoint buffer: the state after every WKV7_CKL tokens,
+// [B][H][ceil(T/CKL)][N][N], then the forward's per-token sa = S a_t (old
+// state), [B][T][H][N]; all fp32.
+__host__ __device__ inline size_t wkv7_ckpt_state_floats(int B, int T, int H) {
+  return (size_t)B * H * ((T + WKV7_CKL - 1) / WKV7_CKL) * WKV7_N * WKV7_N;
+}
+__host__ __device__ inline size_t wkv7_ckpt_total_floats(int B, int T, int H) {
+  return wkv7_ckpt_state_floats(B, T, H) + (size_t)B * T * H * WKV7_N;
+}
+__host__ __device__ inline float* wkv7_ckpt_sa(float* ckpt, int B, int T, int H) {
+  return ckpt + wkv7_ckpt_state_floats(B, T, H);
+}
+__host__ __device__ inline const float* wkv7_ckpt_sa(const float* ckpt, int B, int T, int H) {
+  return ckpt + wkv7_ckpt_state_floats(B, T, H);
+}
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 

@@ -63,7 +63,7 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                 const void* k, const void* v, const void* a, const void* b,
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
-                                float* part, hipStream_t st);
+                                float* part, const int* gate, hipStream_t st);
 size_t wkv7_bwd_partial_floats(int B, int T, int H);
 // Long sequences: the reverse pass in wkv7_bwd_segments(T) launches (last
 // segment first, the state gradient handed over through gbuf, 2 x B*H*N*N
@@ -75,8 +75,22 @@ hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const 
                                           const void* a, const void* b, const void* dy,
                                           const float* ckpt, const float* dsT, void* dr, void* dw,
                                           void* dk, void* dv, void* da, void* db, float* ds0,
-                                          float* part, float* gbuf, hipStream_t st,
-                                          hipStream_t side, hipEvent_t ready, hipEvent_t done);
+                                          float* part, float* gbuf, const int* gate,
+                                          hipStream_t st, hipStream_t side, hipEvent_t ready,
+                                          hipEvent_t done);
+// wkv7_bwd.hip: the two-pass backward (reverse scan of the state gradient,
+// then per-chunk matrix-core products).  ckpt holds the forward's states and
+// per-token sa (wkv7_ckpt_sa).  ws: wkv7_bwd2_ws_floats() fp32.  gate: NULL
+// when every decay is known to lie in [1/256, 1] (the time-mix decay does);
+// otherwise a zeroed int that the scan sets when some decay does not, after
+// which the products return at once and the single-pass kernels, launched
+// with the same gate, produce the results.
+size_t wkv7_bwd2_ws_floats(int B, int T, int H);
+hipError_t wkv7_launch_backward2(int dtype, int B, int T, int H, const void* r, const void* w,
+                                 const void* k, const void* v, const void* a, const void* b,
+                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
+                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
+                                 float* ws, int* gate, hipStream_t st);
 hipError_t wkv7_launch_step(int dtype, int B, int H, const void* r, const void* w, const void* k,
                             const void* v, const void* a, const void* b, float* state, void* y,
                             hipStream_t st);

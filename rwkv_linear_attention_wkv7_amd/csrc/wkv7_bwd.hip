@@ -1,0 +1,479 @@
+// WKV7 backward in two passes: a token-sequential reverse scan of the state
+// gradient, then per-chunk matrix-core products for the gradients that are
+// column sums over the state's rows.
+//
+// Recurrence (per batch b, head h; S is 64x64 fp32, S[i][j] with i = value
+// row, j = key column), as in "Foundry/cuda_kernels/timemix.cu" (WKV7 kernel,
+// k_composites) and the WKV state-backward block of "infotheory
+// .../rwkv7/model.rs":
+//     sa_t = S_{t-1} a_t ;  S_t = S_{t-1} diag(w_t) + sa_t b_t^T + v_t k_t^T ;
+//     y_t = S_t r_t
+// With G_t = dL/dS_t (including dy_t r_t^T) the reverse step is
+//     dsa_t = G_t b_t ;  dv_t = G_t k_t ;  G_{t-1} = G_t diag(w_t) + dsa_t a_t^T + dy_{t-1} r_{t-1}^T
+// which never reads S: the state gradient is a recurrence of its own, rows
+// independent of each other, the same shape as the forward's.
+//
+// Pass 1 (bwd_scan, one workgroup per (b, h, row block), tokens last to
+// first, the forward's lane layout): G, dsa_t (to the workspace), dv_t (the
+// output), and G at every chunk boundary c*L (gradient of the state after c*L
+// tokens, G' in the derivation below) to the workspace.  It also checks that
+// every decay lies in [W_MIN, 1], where pass 2's exponent scaling and its
+// log-decay gradient are accurate in fp32; the caller falls back to the
+// single-pass kernel otherwise.
+//
+// Pass 2 (bwd_grad, one workgroup per (b, h, chunk of L = 16 tokens)).  With
+// g_t = sum_{tau <= t} ln w_tau (cumulative from the chunk start), S0 the
+// state entering the chunk (the forward's checkpoint), Ge the gradient of
+// the state after the chunk's last token from the later tokens, SA / dSA the
+// forward's sa_t and pass 1's dsa_t, and tokens as rows (a derivation of
+// ours; the pages only run the recurrence token by token):
+//   dr_t = S_t^T dy_t       : dR = (dY S0) .* e^{g_t}
+//                                  + [tril(dY SA^T) (B e^{-g}) + tril(dY V^T) (K e^{-g})] .* e^{g_t}
+//   da_t = S_{t-1}^T dsa_t  : dA = (dSA S0) .* e^{g_{t-1}}
+//                                  + [stril(dSA SA^T) (B e^{-g}) + stril(dSA V^T) (K e^{-g})] .* e^{g_{t-1}}
+//   dk_t = G_t^T v_t        : dK = (V Ge) .* e^{g_L - g_t}
+//                                  + [triu(V dY^T) (R e^{g}) + striu(V dSA^T) (A e^{g_{t-1}})] .* e^{-g_t}
+//   db_t = G_t^T sa_t       : dB as dK with SA in place of V
+// (tril: tau <= t, stril: tau < t; the e^{+-g} pairs are formed around the
+// chunk's 8th token so every factor stays in range).  The decay gradient
+// needs no product of G and S per token: with D'_t = sum_i G'_t .* S_t
+// (G'_t the gradient of S_t from tokens after t), D'_{t-1} = D'_t + e_t where
+// e_t = r dr - b db - k dk + a da (elementwise), and
+//   d(ln w_t) = D'_{t-1} - a_t .* da_t ,  dw_t = d(ln w_t) / w_t ,
+// so each chunk runs that sum forward from D'_{-1} = colsum(G'_start .* S0),
+// G'_start being pass 1's boundary gradient at the chunk start.
+//
+// Pass 2's products (per chunk: 4 of 16x64x64, 4 Gram 16x16x64, 8 of
+// 16x16x16) run on v_mfma_f32_16x16x4_f32; the four waves of a workgroup own
+// 16 key columns each, and the state fragments come straight from memory in
+// the MFMA B-operand layout.
+
+#include "common.hpp"
+
+namespace wkv7b {
+
+constexpr int N = WKV7_N;
+constexpr int L = WKV7_CKL;  // chunk = checkpoint interval
+constexpr int TT = L;        // scan staging block (tokens)
+constexpr int RS = N + 4;    // padded row stride of [L][N] LDS arrays
+constexpr int XS = L + 4;    // padded row stride of [L][L] LDS arrays
+constexpr int MID = 7;       // reference token of the exponent scaling
+// decays outside [W_MIN, 1] send the call to the single-pass kernel: within
+// a chunk |g_t - g_MID| <= 8 ln(1/W_MIN) = 44.4 keeps every factor finite,
+// and dividing d(ln w) by w stays accurate
+constexpr float W_MIN = 1.0f / 256.0f;
+
+__device__ __forceinline__ float dot4(const float (&s)[4], f4 v) {
+  return fmaf(s[3], v[3], fmaf(s[2], v[2], fmaf(s[1], v[1], s[0] * v[0])));
+}
+
+// c += A B over one group of 16 k: A fragment a (lane: row l%16, k 4(l/16)+s),
+// B fragment b (lane: k 4(l/16)+s, column l%16), s = MFMA step.  The result
+// tile: lane l element v holds C[4(l/16)+v][l%16].
+__device__ __forceinline__ f4 mma16(f4 a, f4 b, f4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
+// ------------------------------------------------------------------- pass 1
+// Grid: B*H*(64/(16*RPT)) workgroups of 256 threads; workgroup -> (b, h, row
+// block of 16*RPT rows).  Thread: column group cg = tid%16 (columns
+// 4cg..4cg+3), rows row0 + m, m < RPT.
+template <int RPT, typename T>
+__global__ __launch_bounds__(256) void bwd_scan(
+    int Tn, int H, const T* __restrict__ r, const T* __restrict__ w, const T* __restrict__ k,
+    const T* __restrict__ a, const T* __restrict__ bv, const T* __restrict__ dy,
+    const float* __restrict__ dsT, float* __restrict__ dsa_out, T* __restrict__ dv,
+    float* __restrict__ gb, float* __restrict__ ds0, int* __restrict__ gate) {
+  constexpr int ROWS = 16 * RPT;
+  constexpr int NRB = N / ROWS;
+  __shared__ __attribute__((aligned(16))) float sv[2][TT][5][N];  // r, w, k, a, b
+  __shared__ __attribute__((aligned(16))) float sdy[2][TT][ROWS];
+  typedef typename Raw<T>::v4 R4;
+  typedef typename Raw<T>::v1 R1;
+
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = g / NRB, rb = g - bh * NRB;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x, cg = tid & 15, rg = tid >> 4;
+  const int rloc0 = rg * RPT;
+  const int row0 = rb * ROWS + rloc0;
+  const size_t C = (size_t)H * N;
+  const size_t vbase = (size_t)b * Tn * C + (size_t)h * N;
+  const size_t sbase = (size_t)bh * N * N;
+  const int nck = (Tn + L - 1) / L;
+
+  float G[RPT][4];
+#pragma unroll
+  for (int m = 0; m < RPT; m++) {
+    f4 x = {0.f, 0.f, 0.f, 0.f};
+    if (dsT) x = *reinterpret_cast<const f4*>(dsT + sbase + (size_t)(row0 + m) * N + cg * 4);
+#pragma unroll
+    for (int c = 0; c < 4; c++) G[m][c] = x[c];
+  }
+
+  auto vec_ptr = [&](int vi) -> const T* {
+    return vi == 0 ? r : vi == 1 ? w : vi == 2 ? k : vi == 3 ? a : bv;
+  };
+  constexpr int NV4 = TT * 5 * 16;  // float4 slots per block
+  constexpr int NV4_PER = NV4 / 256;
+  static_assert(NV4 % 256 == 0, "block staging assumes 256 threads");
+  constexpr int NVV_PER = (TT * ROWS + 255) / 256;
+  R4 pre[NV4_PER];
+  R1 prev[NVV_PER];
+  const T* src4[NV4_PER];
+  int tok4[NV4_PER];
+#pragma unroll
+  for (int q = 0; q < NV4_PER; q++) {
+    const int f = tid + 256 * q;
+    const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+    src4[q] = vec_ptr(vi) + vbase + c4 * 4;
+    tok4[q] = tok;
+  }
+  // loads from clamped (always valid) token indices; tokens past the end
+  // are never used
+  auto load_block = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < NV4_PER; q++)
+      pre[q] = load_raw4(src4[q] + (size_t)min(t0 + tok4[q], Tn - 1) * C);
+#pragma unroll
+    for (int q = 0; q < NVV_PER; q++) {
+      const int f = min(tid + 256 * q, TT * ROWS - 1);
+      const int tok = f / ROWS, rr = f - tok * ROWS;
+      const int tc = min(t0 + tok, Tn - 1);
+      prev[q] = load_raw1(dy + vbase + (size_t)tc * C + rb * ROWS + rr);
+    }
+  };
+  bool bad = false;  // a decay outside [W_MIN, 1] (or not a number) was seen
+  auto store_block = [&](int bi) {
+#pragma unroll
+    for (int q = 0; q < NV4_PER; q++) {
+      const int f = tid + 256 * q;
+      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+      const f4 x = raw4_to_f4<T>(pre[q]);
+      if (vi == 1) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) bad |= !(x[c] >= W_MIN && x[c] <= 1.0f);
+      }
+      *reinterpret_cast<f4*>(&sv[bi][tok][vi][c4 * 4]) = x;
+    }
+#pragma unroll
+    for (int q = 0; q < NVV_PER; q++) {
+      const int f = tid + 256 * q;
+      if (f < TT * ROWS) {
+        const int tok = f / ROWS, rr = f - tok * ROWS;
+        sdy[bi][tok][rr] = raw1_to_f32<T>(prev[q]);
+      }
+    }
+  };
+
+  // one token, last to first; dsa and dv stay with the lane whose cg is tt
+  float dsab[RPT], dvb[RPT];
+  auto token = [&](int bi, int tt) {
+    const f4 rv = ld4(&sv[bi][tt][0][cg * 4]), wv = ld4(&sv[bi][tt][1][cg * 4]);
+    const f4 kv = ld4(&sv[bi][tt][2][cg * 4]), av = ld4(&sv[bi][tt][3][cg * 4]);
+    const f4 bb = ld4(&sv[bi][tt][4][cg * 4]);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      const float dyv = sdy[bi][tt][rloc0 + m];
+#pragma unroll
+      for (int c = 0; c < 4; c++) G[m][c] = fmaf(dyv, rv[c], G[m][c]);
+    }
+    float ds[RPT], dvv[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      ds[m] = dot4(G[m], bb);
+      dvv[m] = dot4(G[m], kv);
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      ds[m] = rowsum16(ds[m]);
+      dvv[m] = rowsum16(dvv[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+      dsab[m] = (cg == tt) ? ds[m] : dsab[m];
+      dvb[m] = (cg == tt) ? dvv[m] : dvb[m];
+#pragma unroll
+      for (int c = 0; c < 4; c++) G[m][c] = fmaf(ds[m], av[c], G[m][c] * wv[c]);
+    }
+  };
+
+  int bi = 0;
+  load_block((nck - 1) * TT);
+  store_block(0);
+  __syncthreads();
+  for (int c = nck - 1; c >= 0; c--, bi ^= 1) {
+    const int t0 = c * TT;
+    if (c > 0) load_block(t0 - TT);
+    const int nt = min(TT, Tn - t0);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) dsab[m] = dvb[m] = 0.f;
+    if (nt == TT) {
+#pragma unroll
+      for (int tt = TT - 1; tt >= 0; tt--) token(bi, tt);
+    } else {
+      for (int tt = nt - 1; tt >= 0; tt--) token(bi, tt);
+    }
+    if (cg < nt) {
+      const size_t o = vbase + (size_t)(t0 + cg) * C + row0;
+#pragma unroll
+      for (int m = 0; m < RPT; m++) {
+        dsa_out[o + m] = dsab[m];
+        store1(dv + o + m, dvb[m]);
+      }
+    }
+    // G is now the gradient of the state after t0 tokens (boundary c)
+    float* gp = gb + (((size_t)bh * nck + c) * N + row0) * N + cg * 4;
+#pragma unroll
+    for (int m = 0; m < RPT; m++)
+      *reinterpret_cast<f4*>(gp + (size_t)m * N) = f4{G[m][0], G[m][1], G[m][2], G[m][3]};
+    if (c > 0) store_block(bi ^ 1);
+    lds_barrier();
+  }
+  if (ds0) {
+#pragma unroll
+    for (int m = 0; m < RPT; m++)
+      *reinterpret_cast<f4*>(ds0 + sbase + (size_t)(row0 + m) * N + cg * 4) =
+          f4{G[m][0], G[m][1], G[m][2], G[m][3]};
+  }
+  if (gate && bad) *gate = 1;
+}
+
+// ------------------------------------------------------------------- pass 2
+// LDS of one chunk.  nat: R, K, A, B, V, dY, SA, dSA, w (token rows, fp32);
+// gc: g_t; sc: B e^{g_MID - g}, K e^{g_MID - g}, R e^{g - g_MID},
+// A e^{g_{t-1} - g_MID}; xn / xt: the masked Gram matrices and their
+// transposes (X1 = dY SA^T, X2 = dY V^T on tau <= t; X3 = dSA SA^T,
+// X4 = dSA V^T on tau < t).
+struct GradLds {
+  float nat[9][L][RS];
+  float gc[L][RS];
+  float sc[4][L][RS];
+  float xn[4][L][XS];
+  float xt[4][L][XS];
+};
+enum { NR = 0, NK, NA, NB, NV, NDY, NSA, NDSA, NW };
+enum { SBM = 0, SKM, SRM, SAM };
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_grad(
+    int Tn, int H, const T* __restrict__ r, const T* __restrict__ w, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ a, const T* __restrict__ bv,
+    const T* __restrict__ dy, const float* __restrict__ ck, const float* __restrict__ sa_in,
+    const float* __restrict__ dsa_in, const float* __restrict__ gb, const float* __restrict__ dsT,
+    T* __restrict__ dr, T* __restrict__ dw, T* __restrict__ dk, T* __restrict__ da,
+    T* __restrict__ db, const int* __restrict__ gate) {
+  if (gate && *gate) return;  // the single-pass kernel handles this call
+  __shared__ __attribute__((aligned(16))) GradLds s;
+
+  const int nck = (Tn + L - 1) / L;
+  const int gi = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = gi / nck, c = gi - bh * nck;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x, lane = tid & 63, jt = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const int col = 16 * jt + fr;  // key column of this lane's results
+  const size_t C = (size_t)H * N;
+  const size_t vbase = (size_t)b * Tn * C + (size_t)h * N;
+  const int t0 = c * L, nt = min(L, Tn - t0);
+
+  // state fragments in the B-operand layout: x[4kg+s] = X[16kg + 4fg + s][col]
+  const float* S0 = ck + ((size_t)bh * nck + c) * N * N;
+  const float* Gs = gb + ((size_t)bh * nck + c) * N * N;
+  const float* Ge = c + 1 < nck ? gb + ((size_t)bh * nck + c + 1) * N * N
+                                : (dsT ? dsT + (size_t)bh * N * N : nullptr);
+  float s0f[16], gef[16];
+  float d0 = 0.f;  // this lane's share of colsum(G'_start .* S0) at col
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const int i = 16 * (q >> 2) + 4 * fg + (q & 3);
+    s0f[q] = S0[(size_t)i * N + col];
+    gef[q] = Ge ? Ge[(size_t)i * N + col] : 0.f;
+    d0 = fmaf(Gs[(size_t)i * N + col], s0f[q], d0);
+  }
+
+  // stage the chunk: thread -> token tt, columns 4c4..4c4+3; tokens past the
+  // end are zero vectors with w = 1
+  {
+    const int tt = tid >> 4, c4 = (tid & 15) * 4;
+    const bool ok = tt < nt;
+    const size_t o = vbase + (size_t)(t0 + (ok ? tt : 0)) * C + c4;
+    const f4 z = {0.f, 0.f, 0.f, 0.f}, one = {1.f, 1.f, 1.f, 1.f};
+    const f4 xr = ok ? load4(r + o) : z, xk = ok ? load4(k + o) : z, xa = ok ? load4(a + o) : z;
+    const f4 xb = ok ? load4(bv + o) : z, xv = ok ? load4(v + o) : z, xdy = ok ? load4(dy + o) : z;
+    const f4 xsa = ok ? ld4(sa_in + o) : z, xds = ok ? ld4(dsa_in + o) : z;
+    const f4 xw = ok ? load4(w + o) : one;
+    *reinterpret_cast<f4*>(&s.nat[NR][tt][c4]) = xr;
+    *reinterpret_cast<f4*>(&s.nat[NK][tt][c4]) = xk;
+    *reinterpret_cast<f4*>(&s.nat[NA][tt][c4]) = xa;
+    *reinterpret_cast<f4*>(&s.nat[NB][tt][c4]) = xb;
+    *reinterpret_cast<f4*>(&s.nat[NV][tt][c4]) = xv;
+    *reinterpret_cast<f4*>(&s.nat[NDY][tt][c4]) = xdy;
+    *reinterpret_cast<f4*>(&s.nat[NSA][tt][c4]) = xsa;
+    *reinterpret_cast<f4*>(&s.nat[NDSA][tt][c4]) = xds;
+    *reinterpret_cast<f4*>(&s.nat[NW][tt][c4]) = xw;
+    __syncthreads();
+    // cumulative log-decay, one column per thread
+    if (tid < N) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < L; t++) {
+        acc += __logf(s.nat[NW][t][tid]);
+        s.gc[t][tid] = acc;
+      }
+    }
+    __syncthreads();
+    const f4 gt = ld4(&s.gc[tt][c4]), gm = ld4(&s.gc[MID][c4]);
+    const f4 gt1 = tt > 0 ? ld4(&s.gc[tt - 1][c4]) : z;
+    f4 bm, km, rm, am;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float eb = expf(gm[q] - gt[q]);
+      bm[q] = xb[q] * eb;
+      km[q] = xk[q] * eb;
+      rm[q] = xr[q] * expf(gt[q] - gm[q]);
+      am[q] = xa[q] * expf(gt1[q] - gm[q]);
+    }
+    *reinterpret_cast<f4*>(&s.sc[SBM][tt][c4]) = bm;
+    *reinterpret_cast<f4*>(&s.sc[SKM][tt][c4]) = km;
+    *reinterpret_cast<f4*>(&s.sc[SRM][tt][c4]) = rm;
+    *reinterpret_cast<f4*>(&s.sc[SAM][tt][c4]) = am;
+  }
+
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  // Gram matrix of this wave: q = jt
+  {
+    const int P = jt < 2 ? NDY : NDSA, Q = (jt & 1) ? NV : NSA;
+    f4 x = z;
+#pragma unroll
+    for (int kg = 0; kg < 4; kg++)
+      x = mma16(ld4(&s.nat[P][fr][16 * kg + 4 * fg]), ld4(&s.nat[Q][fr][16 * kg + 4 * fg]), x);
+    // x[vv] = X[t = 4fg + vv][tau = fr]
+    const bool strict = jt >= 2;
+#pragma unroll
+    for (int vv = 0; vv < 4; vv++) {
+      const int t = 4 * fg + vv;
+      x[vv] = (strict ? fr < t : fr <= t) ? x[vv] : 0.f;
+      s.xn[jt][t][fr] = x[vv];
+    }
+    *reinterpret_cast<f4*>(&s.xt[jt][fr][4 * fg]) = x;
+  }
+  // products with the states: U1 = dY S0, U2 = dSA S0, U3 = V Ge, U4 = SA Ge
+  f4 u1 = z, u2 = z, u3 = z, u4 = z;
+#pragma unroll
+  for (int kg = 0; kg < 4; kg++) {
+    const f4 sf = {s0f[4 * kg], s0f[4 * kg + 1], s0f[4 * kg + 2], s0f[4 * kg + 3]};
+    const f4 gf = {gef[4 * kg], gef[4 * kg + 1], gef[4 * kg + 2], gef[4 * kg + 3]};
+    u1 = mma16(ld4(&s.nat[NDY][fr][16 * kg + 4 * fg]), sf, u1);
+    u2 = mma16(ld4(&s.nat[NDSA][fr][16 * kg + 4 * fg]), sf, u2);
+    u3 = mma16(ld4(&s.nat[NV][fr][16 * kg + 4 * fg]), gf, u3);
+    u4 = mma16(ld4(&s.nat[NSA][fr][16 * kg + 4 * fg]), gf, u4);
+  }
+  __syncthreads();  // Gram matrices written
+
+  // intra-chunk products (tokens tau of the chunk, K = 16)
+  f4 bmf, kmf, rmf, amf;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    bmf[q] = s.sc[SBM][4 * fg + q][col];
+    kmf[q] = s.sc[SKM][4 * fg + q][col];
+    rmf[q] = s.sc[SRM][4 * fg + q][col];
+    amf[q] = s.sc[SAM][4 * fg + q][col];
+  }
+  f4 dri = mma16(ld4(&s.xn[0][fr][4 * fg]), bmf, z);
+  f4 dai = mma16(ld4(&s.xn[2][fr][4 * fg]), bmf, z);
+  f4 dki = mma16(ld4(&s.xt[1][fr][4 * fg]), rmf, z);
+  f4 dbi = mma16(ld4(&s.xt[0][fr][4 * fg]), rmf, z);
+  dri = mma16(ld4(&s.xn[1][fr][4 * fg]), kmf, dri);
+  dai = mma16(ld4(&s.xn[3][fr][4 * fg]), kmf, dai);
+  dki = mma16(ld4(&s.xt[3][fr][4 * fg]), amf, dki);
+  dbi = mma16(ld4(&s.xt[2][fr][4 * fg]), amf, dbi);
+
+  // combine; lane holds tokens t = 4fg + vv at column col
+  const float gm = s.gc[MID][col], gL = s.gc[L - 1][col];
+  float drv[4], dav[4], dkv[4], dbv[4], ev[4];
+#pragma unroll
+  for (int vv = 0; vv < 4; vv++) {
+    const int t = 4 * fg + vv;
+    const float gt = s.gc[t][col];
+    const float gt1 = t > 0 ? s.gc[t - 1][col] : 0.f;
+    drv[vv] = u1[vv] * expf(gt) + dri[vv] * expf(gt - gm);
+    dav[vv] = u2[vv] * expf(gt1) + dai[vv] * expf(gt1 - gm);
+    const float eL = expf(gL - gt), eh = expf(gm - gt);
+    dkv[vv] = u3[vv] * eL + dki[vv] * eh;
+    dbv[vv] = u4[vv] * eL + dbi[vv] * eh;
+    ev[vv] = s.nat[NR][t][col] * drv[vv] - s.nat[NB][t][col] * dbv[vv] -
+             s.nat[NK][t][col] * dkv[vv] + s.nat[NA][t][col] * dav[vv];
+  }
+  // D'_{t-1} = D'_{-1} - sum_{tau < t} e_tau; the lanes of one column hold
+  // tokens 4fg..4fg+3 for fg = 0..3
+  const float dstart = rows4sum(d0);
+  const float tot = (ev[0] + ev[1]) + (ev[2] + ev[3]);
+  const float t1 = __shfl(tot, fr), t2 = __shfl(tot, fr + 16), t3 = __shfl(tot, fr + 32);
+  float run = (fg > 0 ? t1 : 0.f) + (fg > 1 ? t2 : 0.f) + (fg > 2 ? t3 : 0.f);
+#pragma unroll
+  for (int vv = 0; vv < 4; vv++) {
+    const int t = 4 * fg + vv;
+    const float dlnw = (dstart - run) - s.nat[NA][t][col] * dav[vv];
+    const float dwv = dlnw / s.nat[NW][t][col];
+    run += ev[vv];
+    if (t < nt) {
+      const size_t o = vbase + (size_t)(t0 + t) * C + col;
+      store1(dr + o, drv[vv]);
+      store1(dk + o, dkv[vv]);
+      store1(db + o, dbv[vv]);
+      store1(da + o, dav[vv]);
+      store1(dw + o, dwv);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(int B, int T_, int H, const void* r, const void* w, const void* k,
+                    const void* v, const void* a, const void* b, const void* dy, const float* ckpt,
+                    const float* dsT, void* dr, void* dw, void* dk, void* dv, void* da, void* db,
+                    float* ds0, float* ws, int* gate, hipStream_t st) {
+  const int nck = (T_ + L - 1) / L;
+  const size_t tokf = (size_t)B * T_ * H * N;
+  float* dsa = ws;
+  float* gb = ws + tokf;
+  // 16-row scan workgroups (four per head) while B*H*4 <= 512, else 32-row
+  if ((long)B * H * 4 <= 512)
+    hipLaunchKernelGGL((bwd_scan<1, T>), dim3(B * H * 4), dim3(256), 0, st, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa,
+                       (T*)dv, gb, ds0, gate);
+  else
+    hipLaunchKernelGGL((bwd_scan<2, T>), dim3(B * H * 2), dim3(256), 0, st, T_, H, (const T*)r,
+                       (const T*)w, (const T*)k, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa,
+                       (T*)dv, gb, ds0, gate);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_grad<T>), dim3(B * H * nck), dim3(256), 0, st, T_, H, (const T*)r,
+                     (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
+                     (const T*)dy, ckpt, wkv7_ckpt_sa(ckpt, B, T_, H), dsa, gb, dsT, (T*)dr, (T*)dw,
+                     (T*)dk, (T*)da, (T*)db, gate);
+  return hipGetLastError();
+}
+
+}  // namespace wkv7b
+
+size_t wkv7_bwd2_ws_floats(int B, int T, int H) {
+  // dsa [B][T][H][N], then the boundary state gradients [B][H][nck][N][N]
+  return (size_t)B * T * H * WKV7_N + wkv7_ckpt_state_floats(B, T, H);
+}
+
+hipError_t wkv7_launch_backward2(int dtype, int B, int T, int H, const void* r, const void* w,
+                                 const void* k, const void* v, const void* a, const void* b,
+                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
+                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
+                                 float* ws, int* gate, hipStream_t st) {
+  if (dtype == 1)
+    return wkv7b::launch_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk, dv, da, db,
+                                   ds0, ws, gate, st);
+  return wkv7b::launch_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk, dv, da, db,
+                                ds0, ws, gate, st);
+}

@@ -49,7 +49,7 @@
 namespace wkv7c {
 
 constexpr int N = WKV7_N;
-constexpr int L = 16;      // chunk length = checkpoint interval
+constexpr int L = WKV7_CKL;  // chunk length = checkpoint interval
 constexpr int RS = N + 4;  // padded row stride of [L][N] arrays (floats)
 constexpr int TS = L + 4;  // padded row stride of [N][L] and [L][L] arrays
 constexpr float EXP_LIMIT = 40.f;
@@ -59,9 +59,10 @@ constexpr float EXP_LIMIT = 40.f;
 constexpr int O_AT = 0, O_RT = 1024, O_BH = 2048, O_KH = 3072, O_VT = 4096, O_QT = 5120,
               O_WT = 5376, O_LAM = 5632, O_FLAG = 5696, REC = 5760;
 constexpr int REC4 = REC / 4;
-// scan scratch per head after the records: L*N (y of tail tokens) + N*N
-// (checkpoint stores when none are wanted)
-constexpr int SINK = L * N + N * N;
+// scan scratch per head after the records: L*N (y of tail tokens), N*N
+// (checkpoint stores when none are wanted), L*N (sa of tail tokens, and all
+// of it when no checkpoints are wanted)
+constexpr int SINK = L * N + N * N + L * N;
 
 // The same data in LDS, rows padded for conflict-free 16-byte fragment reads.
 struct ChunkLds {
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void fwd_scan(
     int Tn, int H, const T* __restrict__ r, const T* __restrict__ w, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ a, const T* __restrict__ bv,
     float* __restrict__ rec, const float* __restrict__ s0, T* __restrict__ y,
-    float* __restrict__ sT, float* __restrict__ ckpt) {
+    float* __restrict__ sT, float* __restrict__ ckpt, float* __restrict__ sa_all) {
   __shared__ __attribute__((aligned(16))) ChunkLds buf[2];
   constexpr int PER = (REC4 + 255) / 256;
 
@@ -338,6 +339,8 @@ __global__ __launch_bounds__(256) void fwd_scan(
   T* sink = reinterpret_cast<T*>(sinkh);
   float* ckb = ckpt ? ckpt + (size_t)bh * nck * N * N : sinkh + L * N;
   const size_t ck_stride = ckpt ? (size_t)N * N : 0;
+  // sa of token t: sa_all[vbase + t*C + i] when wanted, else the sink
+  float* sa_sink = sinkh + L * N + N * N;
 
   f4 ST[4];
 #pragma unroll
@@ -406,6 +409,13 @@ __global__ __launch_bounds__(256) void fwd_scan(
           store1(dst, yv[uu]);
         }
       }
+      // sa, laid out like yv
+#pragma unroll
+      for (int uu = 0; uu < 4; uu++) {
+        const int t = t0 + 4 * fg + uu;
+        float* dst = (sa_all && t < Tn) ? sa_all + vbase + (size_t)t * C + row : sa_sink + (4 * fg + uu) * N + row;
+        *dst = sa[uu];
+      }
     } else {
       // token by token (extreme decay), inputs straight from memory
       const int ns = min(L, Tn - t0);
@@ -419,6 +429,7 @@ __global__ __launch_bounds__(256) void fwd_scan(
           for (int uu = 0; uu < 4; uu++) part = fmaf(ST[jt][uu], av[uu], part);
         }
         const float sav = rows4sum(part);
+        if (sa_all && fg == 0) sa_all[o + row] = sav;
         const float vv = load1(v + o + row);
         float yp = 0.f;
 #pragma unroll
@@ -476,6 +487,7 @@ hipError_t wkv7_launch_forward_chunked(int dtype, int B, int T, int H, const voi
                                        hipStream_t st) {
   const int nck = (T + wkv7c::L - 1) / wkv7c::L;
   const dim3 block(256);
+  float* sa = ckpt ? wkv7_ckpt_sa(ckpt, B, T, H) : nullptr;
   if (dtype == 1) {
     typedef bf16_t X;
     hipLaunchKernelGGL((wkv7c::fwd_prep<X>), dim3(B * H * nck), block, 0, st, T, H, nck,
@@ -486,11 +498,11 @@ hipError_t wkv7_launch_forward_chunked(int dtype, int B, int T, int H, const voi
     if (y)
       hipLaunchKernelGGL((wkv7c::fwd_scan<X, true>), dim3(B * H), block, 0, st, T, H, (const X*)r,
                          (const X*)w, (const X*)k, (const X*)v, (const X*)a, (const X*)b, ws, s0,
-                         (X*)y, sT, ckpt);
+                         (X*)y, sT, ckpt, sa);
     else
       hipLaunchKernelGGL((wkv7c::fwd_scan<X, false>), dim3(B * H), block, 0, st, T, H, (const X*)r,
                          (const X*)w, (const X*)k, (const X*)v, (const X*)a, (const X*)b, ws, s0,
-                         (X*)y, sT, ckpt);
+                         (X*)y, sT, ckpt, sa);
   } else {
     typedef float X;
     hipLaunchKernelGGL((wkv7c::fwd_prep<X>), dim3(B * H * nck), block, 0, st, T, H, nck,
@@ -501,11 +513,11 @@ hipError_t wkv7_launch_forward_chunked(int dtype, int B, int T, int H, const voi
     if (y)
       hipLaunchKernelGGL((wkv7c::fwd_scan<X, true>), dim3(B * H), block, 0, st, T, H, (const X*)r,
                          (const X*)w, (const X*)k, (const X*)v, (const X*)a, (const X*)b, ws, s0,
-                         (X*)y, sT, ckpt);
+                         (X*)y, sT, ckpt, sa);
     else
       hipLaunchKernelGGL((wkv7c::fwd_scan<X, false>), dim3(B * H), block, 0, st, T, H, (const X*)r,
                          (const X*)w, (const X*)k, (const X*)v, (const X*)a, (const X*)b, ws, s0,
-                         (X*)y, sT, ckpt);
+                         (X*)y, sT, ckpt, sa);
   }
   return hipGetLastError();
 }

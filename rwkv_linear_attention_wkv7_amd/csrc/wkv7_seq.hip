@@ -31,7 +31,7 @@ namespace wkv7k {
 
 constexpr int N = WKV7_N;
 constexpr int TT = 16;    // tokens per LDS staging block
-constexpr int CKL = 16;   // checkpoint interval (tokens) = backward chunk
+constexpr int CKL = WKV7_CKL;  // checkpoint interval (tokens) = backward chunk
 static_assert(CKL == TT, "checkpoints are taken at block starts");
 
 __device__ __forceinline__ float dot4(const float (&s)[4], f4 v) {
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void fwd_seq(
     int B, int Tn, int H, const T* __restrict__ r, const T* __restrict__ w,
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ a,
     const T* __restrict__ bv, const float* __restrict__ s0, T* __restrict__ y,
-    float* __restrict__ sT, float* __restrict__ ckpt) {
+    float* __restrict__ sT, float* __restrict__ ckpt, float* __restrict__ sa_out) {
   constexpr int ROWS = 16 * RPT;
   constexpr int NRB = N / ROWS;
   // staging: r, w, k, a, b of each token and v of this slice travel raw
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(256) void fwd_seq(
     }
   };
 
-  // one token; the row sums of y stay with the lane whose cg equals tt
-  float yb[RPT];
+  // one token; the row sums of y (and sa) stay with the lane whose cg equals tt
+  float yb[RPT], sab[RPT];
   struct Tok {
     f4 av, wv, kv, bb, rv;
     float vv[RPT];
@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256) void fwd_seq(
     for (int m = 0; m < RPT; m++) sa[m] = rowsum16(sa[m]);
 #pragma unroll
     for (int m = 0; m < RPT; m++) {
+      sab[m] = (cg == tt) ? sa[m] : sab[m];
 #pragma unroll
       for (int c = 0; c < 4; c++) S[m][c] = fmaf(in.vv[m], kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
     }
@@ -178,6 +179,7 @@ __global__ __launch_bounds__(256) void fwd_seq(
 #pragma unroll
     for (int m = 0; m < RPT; m++) {
       const float vv = load1(&svv[buf][tt][rloc0 + m]);
+      sab[m] = (cg == tt) ? sa[m] : sab[m];
 #pragma unroll
       for (int c = 0; c < 4; c++) S[m][c] = fmaf(vv, kv[c], fmaf(sa[m], bb[c], S[m][c] * wv[c]));
     }
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) void fwd_seq(
     }
     const int nt = min(TT, Tn - t0);
 #pragma unroll
-    for (int m = 0; m < RPT; m++) yb[m] = 0.f;
+    for (int m = 0; m < RPT; m++) yb[m] = sab[m] = 0.f;
     if (nt == TT) {
       // the next token's inputs are read from LDS while this one runs
       Tok tc, tn, tn2;
@@ -227,6 +229,11 @@ __global__ __launch_bounds__(256) void fwd_seq(
       T* yp = y + vbase + (size_t)(t0 + cg) * C + row0;
 #pragma unroll
       for (int m = 0; m < RPT; m++) store1(yp + m, yb[m]);
+    }
+    if (sa_out && cg < nt) {
+      float* sp = sa_out + vbase + (size_t)(t0 + cg) * C + row0;
+#pragma unroll
+      for (int m = 0; m < RPT; m++) sp[m] = sab[m];
     }
     if (more) store_block(buf ^ 1);
     lds_barrier();
@@ -253,10 +260,13 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ a,
     const T* __restrict__ bv, const T* __restrict__ dy, const float* __restrict__ ckpt,
     const float* __restrict__ dsT, float* __restrict__ part, T* __restrict__ dv,
-    float* __restrict__ ds0, int c_lo, int c_hi) {
+    float* __restrict__ ds0, int c_lo, int c_hi, const int* __restrict__ gate) {
   // chunks [c_lo, c_hi) of the sequence are processed (last to first); G
   // enters as dsT (the gradient of the state after chunk c_hi - 1) and leaves
-  // as ds0 (before chunk c_lo), so a long sequence can run as several launches
+  // as ds0 (before chunk c_lo), so a long sequence can run as several launches.
+  // gate: NULL, or a flag that is nonzero when this kernel (rather than the
+  // two-pass backward) is to produce the results; zero: return at once.
+  if (gate && !*gate) return;
   constexpr int ROWS = RPT * RG, NSPLIT = N / ROWS, NW = RG / 4, NT = 16 * RG;
   static_assert(RG % 4 == 0, "whole waves");
   // staging, double-buffered, widened to fp32 once on the way into LDS: the
@@ -529,7 +539,9 @@ __global__ __launch_bounds__(16 * RG) void bwd_seq(
 template <typename T, int NS>
 __global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int Tn, int t_lo, int t_len,
                                                            int C4, const float* __restrict__ part,
-                                                           T* dr, T* dk, T* db, T* dw, T* da) {
+                                                           T* dr, T* dk, T* db, T* dw, T* da,
+                                                           const int* __restrict__ gate) {
+  if (gate && !*gate) return;  // as in bwd_seq
   // U float4 per thread per pass, every slice's loads issued together
   // (clamped indices, guarded stores): enough loads in flight to stream the
   // partials at HBM rate.  The slices are summed in slice order.
@@ -592,14 +604,15 @@ template <typename T>
 hipError_t launch_forward_t(int B, int T_, int H, const void* r, const void* w, const void* k,
                             const void* v, const void* a, const void* b, const float* s0, void* y,
                             float* sT, float* ckpt, hipStream_t st) {
+  float* sa = ckpt ? wkv7_ckpt_sa(ckpt, B, T_, H) : nullptr;
   if (fwd_rpt(B, H) == 1)
     hipLaunchKernelGGL((fwd_seq<1, T>), dim3(B * H * 4), dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b, s0, (T*)y,
-                       sT, ckpt);
+                       sT, ckpt, sa);
   else
     hipLaunchKernelGGL((fwd_seq<2, T>), dim3(B * H * 2), dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b, s0, (T*)y,
-                       sT, ckpt);
+                       sT, ckpt, sa);
   return hipGetLastError();
 }
 
@@ -610,17 +623,18 @@ hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w,
                              const void* v, const void* a, const void* b, const void* dy,
                              const float* ckpt, const float* dsT, void* dr, void* dw, void* dk,
                              void* dv, void* da, void* db, float* ds0, float* part, int c_lo,
-                             int c_hi, hipStream_t st, hipStream_t rst, hipEvent_t ready) {
+                             int c_hi, hipStream_t st, hipStream_t rst, hipEvent_t ready,
+                             const int* gate) {
   const int ns = bwd_nsplit(B, H);
   const dim3 grid(B * H * ns);
   if (ns == 4)
     hipLaunchKernelGGL((bwd_seq<1, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi);
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi, gate);
   else
     hipLaunchKernelGGL((bwd_seq<2, 16, T>), grid, dim3(256), 0, st, B, T_, H, (const T*)r,
                        (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
-                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi);
+                       (const T*)dy, ckpt, dsT, part, (T*)dv, ds0, c_lo, c_hi, gate);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rst != st) {
@@ -634,10 +648,10 @@ hipError_t launch_backward_t(int B, int T_, int H, const void* r, const void* w,
   if (blocks > 4096) blocks = 4096;
   if (ns == 4)
     hipLaunchKernelGGL((reduce_bwd_partials<T, 4>), dim3((unsigned)blocks), dim3(256), 0, rst,
-                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da, gate);
   else
     hipLaunchKernelGGL((reduce_bwd_partials<T, 2>), dim3((unsigned)blocks), dim3(256), 0, rst,
-                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da);
+                       plane4, T_, t_lo, t_len, C4, part, (T*)dr, (T*)dk, (T*)db, (T*)dw, (T*)da, gate);
   return hipGetLastError();
 }
 
@@ -679,13 +693,13 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                 const void* k, const void* v, const void* a, const void* b,
                                 const void* dy, const float* ckpt, const float* dsT, void* dr,
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
-                                float* part, hipStream_t st) {
+                                float* part, const int* gate, hipStream_t st) {
   const int nck = (T + wkv7k::CKL - 1) / wkv7k::CKL;
   if (dtype == 1)
     return wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk,
-                                            dv, da, db, ds0, part, 0, nck, st, st, nullptr);
+                                            dv, da, db, ds0, part, 0, nck, st, st, nullptr, gate);
   return wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, dsT, dr, dw, dk, dv,
-                                         da, db, ds0, part, 0, nck, st, st, nullptr);
+                                         da, db, ds0, part, 0, nck, st, st, nullptr, gate);
 }
 
 int wkv7_bwd_segments(int T) {
@@ -699,8 +713,9 @@ hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const 
                                           const void* a, const void* b, const void* dy,
                                           const float* ckpt, const float* dsT, void* dr, void* dw,
                                           void* dk, void* dv, void* da, void* db, float* ds0,
-                                          float* part, float* gbuf, hipStream_t st,
-                                          hipStream_t side, hipEvent_t ready, hipEvent_t done) {
+                                          float* part, float* gbuf, const int* gate,
+                                          hipStream_t st, hipStream_t side, hipEvent_t ready,
+                                          hipEvent_t done) {
   const int nck = (T + wkv7k::CKL - 1) / wkv7k::CKL, nseg = wkv7_bwd_segments(T);
   const size_t gsz = (size_t)B * H * WKV7_N * WKV7_N;
   hipError_t e = hipSuccess;
@@ -711,10 +726,10 @@ hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const 
     float* gout = sgi == 0 ? ds0 : gbuf + (size_t)((sgi + 1) & 1) * gsz;
     if (dtype == 1)
       e = wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
-                                           da, db, gout, part, c_lo, c_hi, st, side, ready);
+                                           da, db, gout, part, c_lo, c_hi, st, side, ready, gate);
     else
       e = wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
-                                          da, db, gout, part, c_lo, c_hi, st, side, ready);
+                                          da, db, gout, part, c_lo, c_hi, st, side, ready, gate);
   }
   // join the reductions back, whatever happened
   hipError_t ej = hipEventRecord(done, side);

@@ -126,10 +126,12 @@ def test_step_rejects_null_state(Lfake):
 
 
 def test_checkpoint_sizes(L):
+    """Checkpoint buffer: the state every Lc tokens, then the forward's
+    per-token sa (one N-vector per token and head)."""
     Lc = L.wkv7_checkpoint_interval()
     assert Lc >= 1
     for T in (1, Lc, Lc + 1, 8192):
-        assert L.wkv7_checkpoint_floats(4, T, 32, 64) == 4 * 32 * (-(-T // Lc)) * 64 * 64
+        assert L.wkv7_checkpoint_floats(4, T, 32, 64) == 4 * 32 * (-(-T // Lc)) * 64 * 64 + 4 * T * 32 * 64
     assert L.wkv7_checkpoint_floats(4, 16, 32, 32) == 0
 
 
