@@ -307,7 +307,7 @@ int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void*
     ck = tmp;
   }
   // The two-pass backward (reverse state-gradient scan, then per-chunk
-  // matrix-core products) serves decays in [1/256, 1]; its scan raises the
+  // matrix-core products) serves decays in [1/8, 1]; its scan raises the
   // flag on any other decay, and then the single-pass kernels, launched after
   // it with the same flag, produce the results instead (the products return
   // at once).  Both use the one region.

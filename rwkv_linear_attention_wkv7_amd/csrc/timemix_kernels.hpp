@@ -81,7 +81,7 @@ hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const 
 // wkv7_bwd.hip: the two-pass backward (reverse scan of the state gradient,
 // then per-chunk matrix-core products).  ckpt holds the forward's states and
 // per-token sa (wkv7_ckpt_sa).  ws: wkv7_bwd2_ws_floats() fp32.  gate: NULL
-// when every decay is known to lie in [1/256, 1] (the time-mix decay does);
+// when every decay is known to lie in [1/8, 1] (the time-mix decay does);
 // otherwise a zeroed int that the scan sets when some decay does not, after
 // which the products return at once and the single-pass kernels, launched
 // with the same gate, produce the results.

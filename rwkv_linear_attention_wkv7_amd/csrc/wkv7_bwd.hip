@@ -34,8 +34,8 @@
 //   dk_t = G_t^T v_t        : dK = (V Ge) .* e^{g_L - g_t}
 //                                  + [triu(V dY^T) (R e^{g}) + striu(V dSA^T) (A e^{g_{t-1}})] .* e^{-g_t}
 //   db_t = G_t^T sa_t       : dB as dK with SA in place of V
-// (tril: tau <= t, stril: tau < t; the e^{+-g} pairs are formed around the
-// chunk's 8th token so every factor stays in range).  The decay gradient
+// (tril: tau <= t, stril: tau < t; with decays of at least W_MIN the factors
+// e^{+-g} of a 16-token chunk stay inside the fp32 range).  The decay gradient
 // needs no product of G and S per token: with D'_t = sum_i G'_t .* S_t
 // (G'_t the gradient of S_t from tokens after t), D'_{t-1} = D'_t + e_t where
 // e_t = r dr - b db - k dk + a da (elementwise), and
@@ -46,7 +46,9 @@
 // Pass 2's products (per chunk: 4 of 16x64x64, 4 Gram 16x16x64, 8 of
 // 16x16x16) run on v_mfma_f32_16x16x4_f32; the four waves of a workgroup own
 // 16 key columns each, and the state fragments come straight from memory in
-// the MFMA B-operand layout.
+// the MFMA B-operand layout.  Each gradient's products share one accumulator
+// and its per-token factor is applied once at the end; e_t needs no factor
+// at all (r dr = (R e^{g}) (dR e^{-g}) and so on).
 
 #include "common.hpp"
 
@@ -57,11 +59,10 @@ constexpr int L = WKV7_CKL;  // chunk = checkpoint interval
 constexpr int TT = L;        // scan staging block (tokens)
 constexpr int RS = N + 4;    // padded row stride of [L][N] LDS arrays
 constexpr int XS = L + 4;    // padded row stride of [L][L] LDS arrays
-constexpr int MID = 7;       // reference token of the exponent scaling
 // decays outside [W_MIN, 1] send the call to the single-pass kernel: within
-// a chunk |g_t - g_MID| <= 8 ln(1/W_MIN) = 44.4 keeps every factor finite,
-// and dividing d(ln w) by w stays accurate
-constexpr float W_MIN = 1.0f / 256.0f;
+// a chunk |g_t| <= 16 ln(1/W_MIN) = 33.3, so e^{+-g_t} stay well inside the
+// fp32 range, and dividing d(ln w) by w stays accurate
+constexpr float W_MIN = 0.125f;
 
 __device__ __forceinline__ float dot4(const float (&s)[4], f4 v) {
   return fmaf(s[3], v[3], fmaf(s[2], v[2], fmaf(s[1], v[1], s[0] * v[0])));
@@ -244,19 +245,19 @@ __global__ __launch_bounds__(256) void bwd_scan(
 }
 
 // ------------------------------------------------------------------- pass 2
-// LDS of one chunk.  nat: R, K, A, B, V, dY, SA, dSA, w (token rows, fp32);
-// gc: g_t; sc: B e^{g_MID - g}, K e^{g_MID - g}, R e^{g - g_MID},
-// A e^{g_{t-1} - g_MID}; xn / xt: the masked Gram matrices and their
-// transposes (X1 = dY SA^T, X2 = dY V^T on tau <= t; X3 = dSA SA^T,
-// X4 = dSA V^T on tau < t).
+// LDS of one chunk (53.8 KB: three workgroups per CU).  nat: V, dY, SA, dSA
+// (token rows, fp32); ex: e^{g_t}, e^{-g_t}; sc: B e^{-g}, K e^{-g}, R e^{g},
+// A e^{g_{t-1}}; xn / xt: the masked Gram matrices and their transposes
+// (X1 = dY SA^T, X2 = dY V^T on tau <= t; X3 = dSA SA^T, X4 = dSA V^T on
+// tau < t).
 struct GradLds {
-  float nat[9][L][RS];
-  float gc[L][RS];
+  float nat[4][L][RS];
+  float ex[2][L][RS];
   float sc[4][L][RS];
   float xn[4][L][XS];
   float xt[4][L][XS];
 };
-enum { NR = 0, NK, NA, NB, NV, NDY, NSA, NDSA, NW };
+enum { NV = 0, NDY, NSA, NDSA };
 enum { SBM = 0, SKM, SRM, SAM };
 
 template <typename T>
@@ -296,55 +297,46 @@ __global__ __launch_bounds__(256) void bwd_grad(
     d0 = fmaf(Gs[(size_t)i * N + col], s0f[q], d0);
   }
 
-  // stage the chunk: thread -> token tt, columns 4c4..4c4+3; tokens past the
+  // stage the chunk: thread -> token tt, columns c4..c4+3; tokens past the
   // end are zero vectors with w = 1
+  const int tt = tid >> 4, c4 = (tid & 15) * 4;
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
   {
-    const int tt = tid >> 4, c4 = (tid & 15) * 4;
     const bool ok = tt < nt;
     const size_t o = vbase + (size_t)(t0 + (ok ? tt : 0)) * C + c4;
-    const f4 z = {0.f, 0.f, 0.f, 0.f}, one = {1.f, 1.f, 1.f, 1.f};
+    const f4 one = {1.f, 1.f, 1.f, 1.f};
     const f4 xr = ok ? load4(r + o) : z, xk = ok ? load4(k + o) : z, xa = ok ? load4(a + o) : z;
     const f4 xb = ok ? load4(bv + o) : z, xv = ok ? load4(v + o) : z, xdy = ok ? load4(dy + o) : z;
     const f4 xsa = ok ? ld4(sa_in + o) : z, xds = ok ? ld4(dsa_in + o) : z;
     const f4 xw = ok ? load4(w + o) : one;
-    *reinterpret_cast<f4*>(&s.nat[NR][tt][c4]) = xr;
-    *reinterpret_cast<f4*>(&s.nat[NK][tt][c4]) = xk;
-    *reinterpret_cast<f4*>(&s.nat[NA][tt][c4]) = xa;
-    *reinterpret_cast<f4*>(&s.nat[NB][tt][c4]) = xb;
     *reinterpret_cast<f4*>(&s.nat[NV][tt][c4]) = xv;
     *reinterpret_cast<f4*>(&s.nat[NDY][tt][c4]) = xdy;
     *reinterpret_cast<f4*>(&s.nat[NSA][tt][c4]) = xsa;
     *reinterpret_cast<f4*>(&s.nat[NDSA][tt][c4]) = xds;
-    *reinterpret_cast<f4*>(&s.nat[NW][tt][c4]) = xw;
+    f4 lw;
+#pragma unroll
+    for (int q = 0; q < 4; q++) lw[q] = logf(xw[q]);
+    *reinterpret_cast<f4*>(&s.ex[0][tt][c4]) = lw;
     __syncthreads();
-    // cumulative log-decay, one column per thread
+    // cumulative log-decay g_t, one column per thread; e^{+-g_t}
     if (tid < N) {
       float acc = 0.f;
 #pragma unroll
       for (int t = 0; t < L; t++) {
-        acc += __logf(s.nat[NW][t][tid]);
-        s.gc[t][tid] = acc;
+        acc += s.ex[0][t][tid];
+        s.ex[0][t][tid] = expf(acc);
+        s.ex[1][t][tid] = expf(-acc);
       }
     }
     __syncthreads();
-    const f4 gt = ld4(&s.gc[tt][c4]), gm = ld4(&s.gc[MID][c4]);
-    const f4 gt1 = tt > 0 ? ld4(&s.gc[tt - 1][c4]) : z;
-    f4 bm, km, rm, am;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const float eb = expf(gm[q] - gt[q]);
-      bm[q] = xb[q] * eb;
-      km[q] = xk[q] * eb;
-      rm[q] = xr[q] * expf(gt[q] - gm[q]);
-      am[q] = xa[q] * expf(gt1[q] - gm[q]);
-    }
-    *reinterpret_cast<f4*>(&s.sc[SBM][tt][c4]) = bm;
-    *reinterpret_cast<f4*>(&s.sc[SKM][tt][c4]) = km;
-    *reinterpret_cast<f4*>(&s.sc[SRM][tt][c4]) = rm;
-    *reinterpret_cast<f4*>(&s.sc[SAM][tt][c4]) = am;
+    const f4 et = ld4(&s.ex[0][tt][c4]), eht = ld4(&s.ex[1][tt][c4]);
+    const f4 et1 = tt > 0 ? ld4(&s.ex[0][tt - 1][c4]) : f4{1.f, 1.f, 1.f, 1.f};
+    *reinterpret_cast<f4*>(&s.sc[SBM][tt][c4]) = xb * eht;
+    *reinterpret_cast<f4*>(&s.sc[SKM][tt][c4]) = xk * eht;
+    *reinterpret_cast<f4*>(&s.sc[SRM][tt][c4]) = xr * et;
+    *reinterpret_cast<f4*>(&s.sc[SAM][tt][c4]) = xa * et1;
   }
 
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
   // Gram matrix of this wave: q = jt
   {
     const int P = jt < 2 ? NDY : NDSA, Q = (jt & 1) ? NV : NSA;
@@ -362,16 +354,19 @@ __global__ __launch_bounds__(256) void bwd_grad(
     }
     *reinterpret_cast<f4*>(&s.xt[jt][fr][4 * fg]) = x;
   }
-  // products with the states: U1 = dY S0, U2 = dSA S0, U3 = V Ge, U4 = SA Ge
-  f4 u1 = z, u2 = z, u3 = z, u4 = z;
+  // products with the states, into the accumulators of the four gradients
+  // (before their per-token factors): dY S0 -> dR, dSA S0 -> dA,
+  // V (Ge e^{g_L}) -> dK, SA (Ge e^{g_L}) -> dB
+  const float eL = s.ex[0][L - 1][col];
+  f4 ar = z, aa = z, ak = z, ab = z;
 #pragma unroll
   for (int kg = 0; kg < 4; kg++) {
     const f4 sf = {s0f[4 * kg], s0f[4 * kg + 1], s0f[4 * kg + 2], s0f[4 * kg + 3]};
-    const f4 gf = {gef[4 * kg], gef[4 * kg + 1], gef[4 * kg + 2], gef[4 * kg + 3]};
-    u1 = mma16(ld4(&s.nat[NDY][fr][16 * kg + 4 * fg]), sf, u1);
-    u2 = mma16(ld4(&s.nat[NDSA][fr][16 * kg + 4 * fg]), sf, u2);
-    u3 = mma16(ld4(&s.nat[NV][fr][16 * kg + 4 * fg]), gf, u3);
-    u4 = mma16(ld4(&s.nat[NSA][fr][16 * kg + 4 * fg]), gf, u4);
+    const f4 gf = f4{gef[4 * kg], gef[4 * kg + 1], gef[4 * kg + 2], gef[4 * kg + 3]} * eL;
+    ar = mma16(ld4(&s.nat[NDY][fr][16 * kg + 4 * fg]), sf, ar);
+    aa = mma16(ld4(&s.nat[NDSA][fr][16 * kg + 4 * fg]), sf, aa);
+    ak = mma16(ld4(&s.nat[NV][fr][16 * kg + 4 * fg]), gf, ak);
+    ab = mma16(ld4(&s.nat[NSA][fr][16 * kg + 4 * fg]), gf, ab);
   }
   __syncthreads();  // Gram matrices written
 
@@ -384,30 +379,26 @@ __global__ __launch_bounds__(256) void bwd_grad(
     rmf[q] = s.sc[SRM][4 * fg + q][col];
     amf[q] = s.sc[SAM][4 * fg + q][col];
   }
-  f4 dri = mma16(ld4(&s.xn[0][fr][4 * fg]), bmf, z);
-  f4 dai = mma16(ld4(&s.xn[2][fr][4 * fg]), bmf, z);
-  f4 dki = mma16(ld4(&s.xt[1][fr][4 * fg]), rmf, z);
-  f4 dbi = mma16(ld4(&s.xt[0][fr][4 * fg]), rmf, z);
-  dri = mma16(ld4(&s.xn[1][fr][4 * fg]), kmf, dri);
-  dai = mma16(ld4(&s.xn[3][fr][4 * fg]), kmf, dai);
-  dki = mma16(ld4(&s.xt[3][fr][4 * fg]), amf, dki);
-  dbi = mma16(ld4(&s.xt[2][fr][4 * fg]), amf, dbi);
+  ar = mma16(ld4(&s.xn[0][fr][4 * fg]), bmf, ar);
+  aa = mma16(ld4(&s.xn[2][fr][4 * fg]), bmf, aa);
+  ak = mma16(ld4(&s.xt[1][fr][4 * fg]), rmf, ak);
+  ab = mma16(ld4(&s.xt[0][fr][4 * fg]), rmf, ab);
+  ar = mma16(ld4(&s.xn[1][fr][4 * fg]), kmf, ar);
+  aa = mma16(ld4(&s.xn[3][fr][4 * fg]), kmf, aa);
+  ak = mma16(ld4(&s.xt[3][fr][4 * fg]), amf, ak);
+  ab = mma16(ld4(&s.xt[2][fr][4 * fg]), amf, ab);
 
-  // combine; lane holds tokens t = 4fg + vv at column col
-  const float gm = s.gc[MID][col], gL = s.gc[L - 1][col];
-  float drv[4], dav[4], dkv[4], dbv[4], ev[4];
+  // lane holds tokens t = 4fg + vv at column col:
+  //   dr = ar e^{g_t}, da = aa e^{g_{t-1}}, dk = ak e^{-g_t}, db = ab e^{-g_t},
+  // and e_t = r dr - b db - k dk + a da = Rm ar - Bm ab - Km ak + Am aa
+  // (the factors cancel against the scaled inputs)
+  float ev[4], amv[4];
 #pragma unroll
   for (int vv = 0; vv < 4; vv++) {
     const int t = 4 * fg + vv;
-    const float gt = s.gc[t][col];
-    const float gt1 = t > 0 ? s.gc[t - 1][col] : 0.f;
-    drv[vv] = u1[vv] * expf(gt) + dri[vv] * expf(gt - gm);
-    dav[vv] = u2[vv] * expf(gt1) + dai[vv] * expf(gt1 - gm);
-    const float eL = expf(gL - gt), eh = expf(gm - gt);
-    dkv[vv] = u3[vv] * eL + dki[vv] * eh;
-    dbv[vv] = u4[vv] * eL + dbi[vv] * eh;
-    ev[vv] = s.nat[NR][t][col] * drv[vv] - s.nat[NB][t][col] * dbv[vv] -
-             s.nat[NK][t][col] * dkv[vv] + s.nat[NA][t][col] * dav[vv];
+    amv[vv] = s.sc[SAM][t][col] * aa[vv];
+    ev[vv] = s.sc[SRM][t][col] * ar[vv] - s.sc[SBM][t][col] * ab[vv] -
+             s.sc[SKM][t][col] * ak[vv] + amv[vv];
   }
   // D'_{t-1} = D'_{-1} - sum_{tau < t} e_tau; the lanes of one column hold
   // tokens 4fg..4fg+3 for fg = 0..3
@@ -418,15 +409,17 @@ __global__ __launch_bounds__(256) void bwd_grad(
 #pragma unroll
   for (int vv = 0; vv < 4; vv++) {
     const int t = 4 * fg + vv;
-    const float dlnw = (dstart - run) - s.nat[NA][t][col] * dav[vv];
-    const float dwv = dlnw / s.nat[NW][t][col];
+    const float et = s.ex[0][t][col], eht = s.ex[1][t][col];
+    const float et1 = t > 0 ? s.ex[0][t - 1][col] : 1.f;
+    // d(ln w_t) = D'_{t-1} - a_t da_t;  w_t = e^{g_t - g_{t-1}}
+    const float dwv = ((dstart - run) - amv[vv]) / (et * (t > 0 ? s.ex[1][t - 1][col] : 1.f));
     run += ev[vv];
     if (t < nt) {
       const size_t o = vbase + (size_t)(t0 + t) * C + col;
-      store1(dr + o, drv[vv]);
-      store1(dk + o, dkv[vv]);
-      store1(db + o, dbv[vv]);
-      store1(da + o, dav[vv]);
+      store1(dr + o, ar[vv] * et);
+      store1(dk + o, ak[vv] * eht);
+      store1(db + o, ab[vv] * eht);
+      store1(da + o, aa[vv] * et1);
       store1(dw + o, dwv);
     }
   }
