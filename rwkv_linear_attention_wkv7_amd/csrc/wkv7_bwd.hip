@@ -64,10 +64,6 @@ constexpr int XS = L + 4;    // padded row stride of [L][L] LDS arrays
 // fp32 range, and dividing d(ln w) by w stays accurate
 constexpr float W_MIN = 0.125f;
 
-__device__ __forceinline__ float dot4(const float (&s)[4], f4 v) {
-  return fmaf(s[3], v[3], fmaf(s[2], v[2], fmaf(s[1], v[1], s[0] * v[0])));
-}
-
 // c += A B over one group of 16 k: A fragment a (lane: row l%16, k 4(l/16)+s),
 // B fragment b (lane: k 4(l/16)+s, column l%16), s = MFMA step.  The result
 // tile: lane l element v holds C[4(l/16)+v][l%16].
@@ -85,13 +81,13 @@ __device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<con
 // 4cg..4cg+3), rows row0 + m, m < RPT.
 template <int RPT, typename T>
 __global__ __launch_bounds__(256) void bwd_scan(
-    int Tn, int H, const T* __restrict__ r, const T* __restrict__ w, const T* __restrict__ k,
-    const T* __restrict__ a, const T* __restrict__ bv, const T* __restrict__ dy,
-    const float* __restrict__ dsT, float* __restrict__ dsa_out, T* __restrict__ dv,
-    float* __restrict__ gb, float* __restrict__ ds0, int* __restrict__ gate) {
+    int Tn, int H, const T* __restrict__ r, const T* __restrict__ w, const T* __restrict__ a,
+    const T* __restrict__ bv, const T* __restrict__ dy, const float* __restrict__ dsT,
+    float* __restrict__ dsa_out, float* __restrict__ gb,
+    float* __restrict__ ds0, int* __restrict__ gate) {
   constexpr int ROWS = 16 * RPT;
   constexpr int NRB = N / ROWS;
-  __shared__ __attribute__((aligned(16))) float sv[2][TT][5][N];  // r, w, k, a, b
+  __shared__ __attribute__((aligned(16))) float sv[2][TT][4][N];  // r, w, a, b
   __shared__ __attribute__((aligned(16))) float sdy[2][TT][ROWS];
   typedef typename Raw<T>::v4 R4;
   typedef typename Raw<T>::v1 R1;
@@ -117,26 +113,26 @@ __global__ __launch_bounds__(256) void bwd_scan(
   }
 
   auto vec_ptr = [&](int vi) -> const T* {
-    return vi == 0 ? r : vi == 1 ? w : vi == 2 ? k : vi == 3 ? a : bv;
+    return vi == 0 ? r : vi == 1 ? w : vi == 2 ? a : bv;
   };
-  constexpr int NV4 = TT * 5 * 16;  // float4 slots per block
+  constexpr int NV4 = TT * 4 * 16;  // float4 slots per block
   constexpr int NV4_PER = NV4 / 256;
   static_assert(NV4 % 256 == 0, "block staging assumes 256 threads");
   constexpr int NVV_PER = (TT * ROWS + 255) / 256;
-  R4 pre[NV4_PER];
-  R1 prev[NVV_PER];
   const T* src4[NV4_PER];
   int tok4[NV4_PER];
 #pragma unroll
   for (int q = 0; q < NV4_PER; q++) {
     const int f = tid + 256 * q;
-    const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+    const int tok = f >> 6, rem = f & 63, vi = rem >> 4, c4 = rem & 15;
     src4[q] = vec_ptr(vi) + vbase + c4 * 4;
     tok4[q] = tok;
   }
   // loads from clamped (always valid) token indices; tokens past the end
   // are never used
-  auto load_block = [&](int t0) {
+  // a block's loads are issued two blocks before its tokens run (two
+  // register sets), so a block of compute covers a load's full latency
+  auto load_block = [&](R4 (&pre)[NV4_PER], R1 (&prev)[NVV_PER], int t0) {
 #pragma unroll
     for (int q = 0; q < NV4_PER; q++)
       pre[q] = load_raw4(src4[q] + (size_t)min(t0 + tok4[q], Tn - 1) * C);
@@ -149,11 +145,11 @@ __global__ __launch_bounds__(256) void bwd_scan(
     }
   };
   bool bad = false;  // a decay outside [W_MIN, 1] (or not a number) was seen
-  auto store_block = [&](int bi) {
+  auto store_block = [&](const R4 (&pre)[NV4_PER], const R1 (&prev)[NVV_PER], int bi) {
 #pragma unroll
     for (int q = 0; q < NV4_PER; q++) {
       const int f = tid + 256 * q;
-      const int tok = f / 80, rem = f - tok * 80, vi = rem >> 4, c4 = rem & 15;
+      const int tok = f >> 6, rem = f & 63, vi = rem >> 4, c4 = rem & 15;
       const f4 x = raw4_to_f4<T>(pre[q]);
       if (vi == 1) {
 #pragma unroll
@@ -171,69 +167,92 @@ __global__ __launch_bounds__(256) void bwd_scan(
     }
   };
 
-  // one token, last to first; dsa and dv stay with the lane whose cg is tt
-  float dsab[RPT], dvb[RPT];
-  auto token = [&](int bi, int tt) {
-    const f4 rv = ld4(&sv[bi][tt][0][cg * 4]), wv = ld4(&sv[bi][tt][1][cg * 4]);
-    const f4 kv = ld4(&sv[bi][tt][2][cg * 4]), av = ld4(&sv[bi][tt][3][cg * 4]);
-    const f4 bb = ld4(&sv[bi][tt][4][cg * 4]);
+  // one token, last to first; dsa and dv stay with the lane whose cg is tt.
+  // A token's LDS values are read into a Tok two tokens ahead of its use.
+  float dsab[RPT];
+  struct Tok {
+    f4 rv, wv, av, bb;
+    float dyv[RPT];
+  };
+  auto ldtok = [&](int bi, int tt, Tok& o) {
+    o.rv = ld4(&sv[bi][tt][0][cg * 4]);
+    o.bb = ld4(&sv[bi][tt][3][cg * 4]);
+    o.wv = ld4(&sv[bi][tt][1][cg * 4]);
+    o.av = ld4(&sv[bi][tt][2][cg * 4]);
+#pragma unroll
+    for (int m = 0; m < RPT; m++) o.dyv[m] = sdy[bi][tt][rloc0 + m];
+  };
+  auto token = [&](const Tok& in, int tt) {
 #pragma unroll
     for (int m = 0; m < RPT; m++) {
-      const float dyv = sdy[bi][tt][rloc0 + m];
 #pragma unroll
-      for (int c = 0; c < 4; c++) G[m][c] = fmaf(dyv, rv[c], G[m][c]);
+      for (int c = 0; c < 4; c++) G[m][c] = fmaf(in.dyv[m], in.rv[c], G[m][c]);
     }
-    float ds[RPT], dvv[RPT];
+    float ds[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; m++) {
-      ds[m] = dot4(G[m], bb);
-      dvv[m] = dot4(G[m], kv);
-    }
+    for (int m = 0; m < RPT; m++)
+      ds[m] = fmaf(G[m][3], in.bb[3], fmaf(G[m][2], in.bb[2], fmaf(G[m][1], in.bb[1], G[m][0] * in.bb[0])));
 #pragma unroll
-    for (int m = 0; m < RPT; m++) {
-      ds[m] = rowsum16(ds[m]);
-      dvv[m] = rowsum16(dvv[m]);
-    }
+    for (int m = 0; m < RPT; m++) ds[m] = rowsum16(ds[m]);
 #pragma unroll
     for (int m = 0; m < RPT; m++) {
       dsab[m] = (cg == tt) ? ds[m] : dsab[m];
-      dvb[m] = (cg == tt) ? dvv[m] : dvb[m];
 #pragma unroll
-      for (int c = 0; c < 4; c++) G[m][c] = fmaf(ds[m], av[c], G[m][c] * wv[c]);
+      for (int c = 0; c < 4; c++) G[m][c] = fmaf(ds[m], in.av[c], G[m][c] * in.wv[c]);
     }
   };
 
-  int bi = 0;
-  load_block((nck - 1) * TT);
-  store_block(0);
-  __syncthreads();
-  for (int c = nck - 1; c >= 0; c--, bi ^= 1) {
+  // block c of tokens runs from LDS buffer bi; ld/lv receive block c-2, the
+  // set st/sv (block c-1) goes to the other buffer at the end
+  auto run_block = [&](int c, int bi, R4 (&ld)[NV4_PER], R1 (&lv)[NVV_PER],
+                       const R4 (&stv)[NV4_PER], const R1 (&svv)[NVV_PER]) {
     const int t0 = c * TT;
-    if (c > 0) load_block(t0 - TT);
+    if (c >= 2) load_block(ld, lv, t0 - 2 * TT);
     const int nt = min(TT, Tn - t0);
 #pragma unroll
-    for (int m = 0; m < RPT; m++) dsab[m] = dvb[m] = 0.f;
+    for (int m = 0; m < RPT; m++) dsab[m] = 0.f;
     if (nt == TT) {
+      Tok tc, tn, tn2;
+      ldtok(bi, TT - 1, tc);
+      ldtok(bi, TT - 2, tn);
 #pragma unroll
-      for (int tt = TT - 1; tt >= 0; tt--) token(bi, tt);
+      for (int tt = TT - 1; tt >= 0; tt--) {
+        if (tt >= 2) ldtok(bi, tt - 2, tn2);
+        __builtin_amdgcn_sched_barrier(0);
+        token(tc, tt);
+        tc = tn;
+        tn = tn2;
+      }
     } else {
-      for (int tt = nt - 1; tt >= 0; tt--) token(bi, tt);
+      for (int tt = nt - 1; tt >= 0; tt--) {
+        Tok tc;
+        ldtok(bi, tt, tc);
+        token(tc, tt);
+      }
     }
     if (cg < nt) {
       const size_t o = vbase + (size_t)(t0 + cg) * C + row0;
 #pragma unroll
-      for (int m = 0; m < RPT; m++) {
-        dsa_out[o + m] = dsab[m];
-        store1(dv + o + m, dvb[m]);
-      }
+      for (int m = 0; m < RPT; m++) dsa_out[o + m] = dsab[m];
     }
     // G is now the gradient of the state after t0 tokens (boundary c)
     float* gp = gb + (((size_t)bh * nck + c) * N + row0) * N + cg * 4;
 #pragma unroll
     for (int m = 0; m < RPT; m++)
       *reinterpret_cast<f4*>(gp + (size_t)m * N) = f4{G[m][0], G[m][1], G[m][2], G[m][3]};
-    if (c > 0) store_block(bi ^ 1);
+    if (c >= 1) store_block(stv, svv, bi ^ 1);
     lds_barrier();
+  };
+  R4 preA[NV4_PER], preB[NV4_PER];
+  R1 prvA[NVV_PER], prvB[NVV_PER];
+  load_block(preA, prvA, (nck - 1) * TT);
+  if (nck >= 2) load_block(preB, prvB, (nck - 2) * TT);
+  store_block(preA, prvA, 0);
+  __syncthreads();
+  for (int c = nck - 1; c >= 0; c -= 2) {
+    run_block(c, 0, preA, prvA, preB, prvB);
+    if (c == 0) break;
+    run_block(c - 1, 1, preB, prvB, preA, prvA);
   }
   if (ds0) {
 #pragma unroll
@@ -245,17 +264,19 @@ __global__ __launch_bounds__(256) void bwd_scan(
 }
 
 // ------------------------------------------------------------------- pass 2
-// LDS of one chunk (53.8 KB: three workgroups per CU).  nat: V, dY, SA, dSA
-// (token rows, fp32); ex: e^{g_t}, e^{-g_t}; sc: B e^{-g}, K e^{-g}, R e^{g},
+// LDS of one chunk (52 KB: three workgroups per CU).  nat: V, dY, SA, dSA
+// (token rows, fp32); ex: e^{g_t}; sc: B e^{-g}, K e^{-g}, R e^{g},
 // A e^{g_{t-1}}; xn / xt: the masked Gram matrices and their transposes
 // (X1 = dY SA^T, X2 = dY V^T on tau <= t; X3 = dSA SA^T, X4 = dSA V^T on
-// tau < t).
+// tau < t); yn: the Gram matrices of dv, Y1 = (K e^{-g}) (R e^{g})^T on
+// tau >= t, Y2 = (K e^{-g}) (A e^{g_{t-1}})^T on tau > t.
 struct GradLds {
   float nat[4][L][RS];
-  float ex[2][L][RS];
+  float ex[L][RS];
   float sc[4][L][RS];
   float xn[4][L][XS];
   float xt[4][L][XS];
+  float yn[2][L][XS];
 };
 enum { NV = 0, NDY, NSA, NDSA };
 enum { SBM = 0, SKM, SRM, SAM };
@@ -266,8 +287,8 @@ __global__ __launch_bounds__(256) void bwd_grad(
     const T* __restrict__ v, const T* __restrict__ a, const T* __restrict__ bv,
     const T* __restrict__ dy, const float* __restrict__ ck, const float* __restrict__ sa_in,
     const float* __restrict__ dsa_in, const float* __restrict__ gb, const float* __restrict__ dsT,
-    T* __restrict__ dr, T* __restrict__ dw, T* __restrict__ dk, T* __restrict__ da,
-    T* __restrict__ db, const int* __restrict__ gate) {
+    T* __restrict__ dr, T* __restrict__ dw, T* __restrict__ dk, T* __restrict__ dv,
+    T* __restrict__ da, T* __restrict__ db, const int* __restrict__ gate) {
   if (gate && *gate) return;  // the single-pass kernel handles this call
   __shared__ __attribute__((aligned(16))) GradLds s;
 
@@ -277,17 +298,21 @@ __global__ __launch_bounds__(256) void bwd_grad(
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, lane = tid & 63, jt = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
-  const int col = 16 * jt + fr;  // key column of this lane's results
+  // this lane's results: key column col (dr, dk, db, da, dw), value row col (dv)
+  const int col = 16 * jt + fr;
   const size_t C = (size_t)H * N;
   const size_t vbase = (size_t)b * Tn * C + (size_t)h * N;
   const int t0 = c * L, nt = min(L, Tn - t0);
 
-  // state fragments in the B-operand layout: x[4kg+s] = X[16kg + 4fg + s][col]
+  // state fragments in the B-operand layout: x[4kg+s] = X[16kg + 4fg + s][col];
+  // for dv, Ge's row col: ger[kg] = Ge[col][16kg + 4fg .. +3]
   const float* S0 = ck + ((size_t)bh * nck + c) * N * N;
   const float* Gs = gb + ((size_t)bh * nck + c) * N * N;
   const float* Ge = c + 1 < nck ? gb + ((size_t)bh * nck + c + 1) * N * N
                                 : (dsT ? dsT + (size_t)bh * N * N : nullptr);
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
   float s0f[16], gef[16];
+  f4 ger[4];
   float d0 = 0.f;  // this lane's share of colsum(G'_start .* S0) at col
 #pragma unroll
   for (int q = 0; q < 16; q++) {
@@ -296,11 +321,12 @@ __global__ __launch_bounds__(256) void bwd_grad(
     gef[q] = Ge ? Ge[(size_t)i * N + col] : 0.f;
     d0 = fmaf(Gs[(size_t)i * N + col], s0f[q], d0);
   }
+#pragma unroll
+  for (int kg = 0; kg < 4; kg++) ger[kg] = Ge ? ld4(Ge + (size_t)col * N + 16 * kg + 4 * fg) : z;
 
   // stage the chunk: thread -> token tt, columns c4..c4+3; tokens past the
   // end are zero vectors with w = 1
   const int tt = tid >> 4, c4 = (tid & 15) * 4;
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
   {
     const bool ok = tt < nt;
     const size_t o = vbase + (size_t)(t0 + (ok ? tt : 0)) * C + c4;
@@ -316,28 +342,31 @@ __global__ __launch_bounds__(256) void bwd_grad(
     f4 lw;
 #pragma unroll
     for (int q = 0; q < 4; q++) lw[q] = logf(xw[q]);
-    *reinterpret_cast<f4*>(&s.ex[0][tt][c4]) = lw;
+    *reinterpret_cast<f4*>(&s.ex[tt][c4]) = lw;
     __syncthreads();
-    // cumulative log-decay g_t, one column per thread; e^{+-g_t}
+    // cumulative log-decay g_t, one column per thread, kept as e^{g_t}
     if (tid < N) {
       float acc = 0.f;
 #pragma unroll
       for (int t = 0; t < L; t++) {
-        acc += s.ex[0][t][tid];
-        s.ex[0][t][tid] = expf(acc);
-        s.ex[1][t][tid] = expf(-acc);
+        acc += s.ex[t][tid];
+        s.ex[t][tid] = expf(acc);
       }
     }
     __syncthreads();
-    const f4 et = ld4(&s.ex[0][tt][c4]), eht = ld4(&s.ex[1][tt][c4]);
-    const f4 et1 = tt > 0 ? ld4(&s.ex[0][tt - 1][c4]) : f4{1.f, 1.f, 1.f, 1.f};
+    const f4 et = ld4(&s.ex[tt][c4]);
+    const f4 et1 = tt > 0 ? ld4(&s.ex[tt - 1][c4]) : one;
+    f4 eht;
+#pragma unroll
+    for (int q = 0; q < 4; q++) eht[q] = __frcp_rn(et[q]);
     *reinterpret_cast<f4*>(&s.sc[SBM][tt][c4]) = xb * eht;
     *reinterpret_cast<f4*>(&s.sc[SKM][tt][c4]) = xk * eht;
     *reinterpret_cast<f4*>(&s.sc[SRM][tt][c4]) = xr * et;
     *reinterpret_cast<f4*>(&s.sc[SAM][tt][c4]) = xa * et1;
+    __syncthreads();
   }
 
-  // Gram matrix of this wave: q = jt
+  // Gram matrices: X_jt by wave jt; Y1, Y2 by waves 0, 1
   {
     const int P = jt < 2 ? NDY : NDSA, Q = (jt & 1) ? NV : NSA;
     f4 x = z;
@@ -353,12 +382,25 @@ __global__ __launch_bounds__(256) void bwd_grad(
       s.xn[jt][t][fr] = x[vv];
     }
     *reinterpret_cast<f4*>(&s.xt[jt][fr][4 * fg]) = x;
+    if (jt < 2) {
+      const int Q2 = jt == 0 ? SRM : SAM;
+      f4 y = z;
+#pragma unroll
+      for (int kg = 0; kg < 4; kg++)
+        y = mma16(ld4(&s.sc[SKM][fr][16 * kg + 4 * fg]), ld4(&s.sc[Q2][fr][16 * kg + 4 * fg]), y);
+      // y[vv] = Y[t = 4fg + vv][tau = fr]; Y1 keeps tau >= t, Y2 tau > t
+#pragma unroll
+      for (int vv = 0; vv < 4; vv++) {
+        const int t = 4 * fg + vv;
+        s.yn[jt][t][fr] = (jt == 0 ? fr >= t : fr > t) ? y[vv] : 0.f;
+      }
+    }
   }
-  // products with the states, into the accumulators of the four gradients
+  // products with the states, into the accumulators of the five gradients
   // (before their per-token factors): dY S0 -> dR, dSA S0 -> dA,
-  // V (Ge e^{g_L}) -> dK, SA (Ge e^{g_L}) -> dB
-  const float eL = s.ex[0][L - 1][col];
-  f4 ar = z, aa = z, ak = z, ab = z;
+  // V (Ge e^{g_L}) -> dK, SA (Ge e^{g_L}) -> dB, (K e^{-g}) (Ge e^{g_L})^T -> dV
+  const float eL = s.ex[L - 1][col];
+  f4 ar = z, aa = z, ak = z, ab = z, av = z;
 #pragma unroll
   for (int kg = 0; kg < 4; kg++) {
     const f4 sf = {s0f[4 * kg], s0f[4 * kg + 1], s0f[4 * kg + 2], s0f[4 * kg + 3]};
@@ -367,30 +409,36 @@ __global__ __launch_bounds__(256) void bwd_grad(
     aa = mma16(ld4(&s.nat[NDSA][fr][16 * kg + 4 * fg]), sf, aa);
     ak = mma16(ld4(&s.nat[NV][fr][16 * kg + 4 * fg]), gf, ak);
     ab = mma16(ld4(&s.nat[NSA][fr][16 * kg + 4 * fg]), gf, ab);
+    av = mma16(ld4(&s.sc[SKM][fr][16 * kg + 4 * fg]),
+               ger[kg] * ld4(&s.ex[L - 1][16 * kg + 4 * fg]), av);
   }
   __syncthreads();  // Gram matrices written
 
   // intra-chunk products (tokens tau of the chunk, K = 16)
-  f4 bmf, kmf, rmf, amf;
+  f4 bmf, kmf, rmf, amf, dyf, dsf;
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     bmf[q] = s.sc[SBM][4 * fg + q][col];
     kmf[q] = s.sc[SKM][4 * fg + q][col];
     rmf[q] = s.sc[SRM][4 * fg + q][col];
     amf[q] = s.sc[SAM][4 * fg + q][col];
+    dyf[q] = s.nat[NDY][4 * fg + q][col];
+    dsf[q] = s.nat[NDSA][4 * fg + q][col];
   }
   ar = mma16(ld4(&s.xn[0][fr][4 * fg]), bmf, ar);
   aa = mma16(ld4(&s.xn[2][fr][4 * fg]), bmf, aa);
   ak = mma16(ld4(&s.xt[1][fr][4 * fg]), rmf, ak);
   ab = mma16(ld4(&s.xt[0][fr][4 * fg]), rmf, ab);
+  av = mma16(ld4(&s.yn[0][fr][4 * fg]), dyf, av);
   ar = mma16(ld4(&s.xn[1][fr][4 * fg]), kmf, ar);
   aa = mma16(ld4(&s.xn[3][fr][4 * fg]), kmf, aa);
   ak = mma16(ld4(&s.xt[3][fr][4 * fg]), amf, ak);
   ab = mma16(ld4(&s.xt[2][fr][4 * fg]), amf, ab);
+  av = mma16(ld4(&s.yn[1][fr][4 * fg]), dsf, av);
 
   // lane holds tokens t = 4fg + vv at column col:
   //   dr = ar e^{g_t}, da = aa e^{g_{t-1}}, dk = ak e^{-g_t}, db = ab e^{-g_t},
-  // and e_t = r dr - b db - k dk + a da = Rm ar - Bm ab - Km ak + Am aa
+  //   dv = av;  e_t = r dr - b db - k dk + a da = Rm ar - Bm ab - Km ak + Am aa
   // (the factors cancel against the scaled inputs)
   float ev[4], amv[4];
 #pragma unroll
@@ -409,17 +457,19 @@ __global__ __launch_bounds__(256) void bwd_grad(
 #pragma unroll
   for (int vv = 0; vv < 4; vv++) {
     const int t = 4 * fg + vv;
-    const float et = s.ex[0][t][col], eht = s.ex[1][t][col];
-    const float et1 = t > 0 ? s.ex[0][t - 1][col] : 1.f;
-    // d(ln w_t) = D'_{t-1} - a_t da_t;  w_t = e^{g_t - g_{t-1}}
-    const float dwv = ((dstart - run) - amv[vv]) / (et * (t > 0 ? s.ex[1][t - 1][col] : 1.f));
+    const float et = s.ex[t][col];
+    const float et1 = t > 0 ? s.ex[t - 1][col] : 1.f;
+    // d(ln w_t) = D'_{t-1} - a_t da_t;  w_t = e^{g_t} / e^{g_{t-1}}
+    const float dwv = ((dstart - run) - amv[vv]) * et1 / et;
     run += ev[vv];
     if (t < nt) {
       const size_t o = vbase + (size_t)(t0 + t) * C + col;
+      const float eht = __frcp_rn(et);
       store1(dr + o, ar[vv] * et);
       store1(dk + o, ak[vv] * eht);
       store1(db + o, ab[vv] * eht);
       store1(da + o, aa[vv] * et1);
+      store1(dv + o, av[vv]);
       store1(dw + o, dwv);
     }
   }
@@ -437,18 +487,16 @@ hipError_t launch_t(int B, int T_, int H, const void* r, const void* w, const vo
   // 16-row scan workgroups (four per head) while B*H*4 <= 512, else 32-row
   if ((long)B * H * 4 <= 512)
     hipLaunchKernelGGL((bwd_scan<1, T>), dim3(B * H * 4), dim3(256), 0, st, T_, H, (const T*)r,
-                       (const T*)w, (const T*)k, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa,
-                       (T*)dv, gb, ds0, gate);
+                       (const T*)w, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa, gb, ds0, gate);
   else
     hipLaunchKernelGGL((bwd_scan<2, T>), dim3(B * H * 2), dim3(256), 0, st, T_, H, (const T*)r,
-                       (const T*)w, (const T*)k, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa,
-                       (T*)dv, gb, ds0, gate);
+                       (const T*)w, (const T*)a, (const T*)b, (const T*)dy, dsT, dsa, gb, ds0, gate);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad<T>), dim3(B * H * nck), dim3(256), 0, st, T_, H, (const T*)r,
                      (const T*)w, (const T*)k, (const T*)v, (const T*)a, (const T*)b,
                      (const T*)dy, ckpt, wkv7_ckpt_sa(ckpt, B, T_, H), dsa, gb, dsT, (T*)dr, (T*)dw,
-                     (T*)dk, (T*)da, (T*)db, gate);
+                     (T*)dk, (T*)dv, (T*)da, (T*)db, gate);
   return hipGetLastError();
 }
 
