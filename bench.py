@@ -141,7 +141,7 @@ def setup_wkv7_small():
     flops = 26.0 * N * N * B * T * H
     roof = dict(kernel="wkv7 backward call (B=1 T=64 H=4: 16 workgroups, latency bound)",
                 bound="alu", work=flops, unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom,
-                key="wkv7_bwd_small", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+                key="wkv7_bwd_small", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_bwd.hip"])
 
     def cpu():
         from oracle import wkv7 as ow
@@ -244,11 +244,12 @@ def setup_wkv7_long(chunked=False):
 
     # backward algorithmic work per token-head: 19 N^2 flop for the reverse
     # step (G += dy r^T, dr, dv, dk, db, dsa, dw, da: 2 N^2 each; G update
-    # 3 N^2) plus 7 N^2 to recompute sa and the state from the checkpoint.
+    # 3 N^2) plus 7 N^2 to recompute sa and the state from the checkpoint
+    # (the per-token recurrence's count, whatever form the kernels take).
     flops = 26.0 * N * N * B * T * H
-    roof = dict(kernel="wkv7 backward call (checkpointed, 4 reverse-pass segments)", bound="alu", work=flops,
-                unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom, key="wkv7_bwd_long",
-                src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
+    roof = dict(kernel="wkv7 backward call (reverse state-gradient scan + per-chunk matrix-core products)",
+                bound="alu", work=flops, unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom,
+                key="wkv7_bwd_long", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_bwd.hip"])
 
     def cpu():
         from oracle import wkv7 as ow

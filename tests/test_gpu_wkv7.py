@@ -88,6 +88,20 @@ def test_wkv7_extreme_decay(hip):
     _check(d, y, sT, g, True, 1e-4, 1e-3)
 
 
+@pytest.mark.parametrize("lo", [0.125, 0.2])
+def test_wkv7_strong_decay_two_pass(hip, lo):
+    """Decays spread over [lo, 1] (log-uniform), inside the range the two-pass
+    backward serves (the decay of a 16-token chunk reaches 0.125^16, so its
+    e^{+-g} factors span about e^{+-33}); ragged T, nonzero s0 and dsT; fp32
+    forward and gradients against the oracle."""
+    d = synth.wkv7_inputs(2, 150, 3, 64, seed=41, with_state=True)
+    g = np.random.default_rng(41)
+    d["w"] = np.exp(np.log(lo) * g.random(d["w"].shape)).astype(np.float32)
+    print(f"[wkv7 strong decay] B=2 T=150 H=3 w in [{lo}, 1]", flush=True)
+    y, sT, gr = _run(hip, d, torch.float32, True, False)
+    _check(d, y, sT, gr, True, 1e-4, 1e-3)
+
+
 def test_wkv7_backward_without_checkpoints(hip):
     from rwkv_linear_attention_wkv7_amd import binding
     d = synth.wkv7_inputs(2, 40, 2, 64, seed=5, with_state=True)
