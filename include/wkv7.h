@@ -73,7 +73,8 @@ int wkv7_side_destroy(wkv7_side *side);
 /* Checkpoint interval L used by wkv7_forward / wkv7_backward (tokens). */
 int wkv7_checkpoint_interval(void);
 
-/* Number of fp32 elements of the checkpoint buffer: B*H*ceil(T/L)*N*N. */
+/* Number of fp32 elements of the checkpoint buffer:
+ * B*H*ceil(T/L)*N*N (states) + B*T*H*N (the forward's sa per token). */
 size_t wkv7_checkpoint_floats(int B, int T, int H, int N);
 
 /*
@@ -89,9 +90,10 @@ size_t wkv7_checkpoint_floats(int B, int T, int H, int N);
  * r,w,k,v,a,b: [B][T][H][N] of `dtype`.  y: [B][T][H][N] of `dtype` (written).
  * s0: [B][H][N][N] fp32 or NULL.  sT: [B][H][N][N] fp32 or NULL (written;
  * may equal s0 for an in-place state update).  ckpt: NULL, or
- * wkv7_checkpoint_floats() fp32 laid out [B][H][ceil(T/L)][N][N], where
- * checkpoint c is the state after c*L tokens (c = 0 holds s0); it is what
- * wkv7_backward recomputes from.  T >= 1, B >= 1, H >= 1.
+ * wkv7_checkpoint_floats() fp32: [B][H][ceil(T/L)][N][N], where checkpoint c
+ * is the state after c*L tokens (c = 0 holds s0), then sa_t = S_{t-1} a_t of
+ * every token, [B][T][H][N]; it is what wkv7_backward works from.
+ * T >= 1, B >= 1, H >= 1.
  *
  * ws / ws_bytes: NULL, or device scratch of at least
  * wkv7_forward_workspace_bytes() bytes (16-byte aligned; contents
@@ -113,9 +115,11 @@ int wkv7_forward(int B, int T, int H, int N, int dtype,
                  const void *a, const void *b, const float *s0,
                  void *y, float *sT, float *ckpt, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes wkv7_backward needs: fp32 column partials of the reverse
- * pass, two B*H*N*N fp32 state-gradient buffers, plus, when have_ckpt is 0,
- * the checkpoints (recomputed by the token-sequential forward). */
+/* Workspace bytes wkv7_backward needs: one fp32 region shared by its two
+ * paths (the two-pass path's dsa per token, state gradient every L tokens and
+ * per-column sums; or the single-pass path's column partials and segment
+ * hand-over), a flag, plus, when have_ckpt is 0, the checkpoints
+ * (recomputed by the token-sequential forward). */
 size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
 
 /*
@@ -126,16 +130,25 @@ size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
  *     da_t = S_{t-1}^T dsa;  G = G diag(w_t) + dsa a_t^T ).
  * Same pages as wkv7_forward; the model.rs block gives these local terms.
  *
+ * Computed in two passes when every decay lies in [1/8, 1]: a reverse scan
+ * of G alone (it never reads S), then per-chunk matrix-core products that
+ * give the column sums from the checkpoints, the forward's sa and the scan's
+ * boundary gradients; dw from a running sum of r dr - b db - k dk + a da.
+ * Otherwise (the scan finds a decay outside that range) the single-pass
+ * kernel runs the step above token by token from the checkpoints; both agree
+ * with the recurrence to fp32 rounding.
+ *
  * ckpt: the forward's checkpoints, or NULL (then they are recomputed into the
  * workspace).  dy: [B][T][H][N] `dtype`.  dsT, s0: fp32 [B][H][N][N] or NULL.
  * dr,dw,dk,dv,da,db: [B][T][H][N] `dtype` (written).  ds0: fp32 or NULL.
  * ws: at least wkv7_backward_workspace_bytes() bytes (16-byte aligned;
  * contents undefined before and after).
- * side: NULL, or a wkv7_side; with one, from T = 1024 on the reverse pass runs
- * as 2-4 launches over consecutive token segments of at least 512 tokens
- * (last first, the state gradient handed over through the workspace), and
- * each segment's reduction of the column partials runs on the side stream,
- * overlapping the next segment's pass.
+ * side: NULL, or a wkv7_side; with one, when the single-pass kernel runs,
+ * from T = 1024 on its reverse pass runs as 2-4 launches over consecutive
+ * token segments of at least 512 tokens (last first, the state gradient
+ * handed over through the workspace), and each segment's reduction of the
+ * column partials runs on the side stream, overlapping the next segment's
+ * pass.
  */
 int wkv7_backward(int B, int T, int H, int N, int dtype,
                   const void *r, const void *w, const void *k, const void *v,
