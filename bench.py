@@ -56,6 +56,11 @@ METRIC = "WKV7 time-mix fwd+bwd tokens/s and decode steps/s; % of HBM/MFMA peak"
 PEAK = {"hbm": (8000.0, "GB/s"), "mfma_fp32": (157.3, "TFLOP/s"), "alu_fp32": (157.3, "TFLOP/s"),
         "mfma_bf16": (2500.0, "TFLOP/s")}
 PEAK_ALU_NO_PACKED = 256 * 64 * 2 * 2.4e9 / 1e12  # 78.6 TFLOP/s
+# The time-mix and training-step workloads overlap their weight-gradient GEMMs
+# with the rest of the backward on the library's side stream; --one-stream runs
+# them on the caller's stream alone, so that a counter run times every kernel
+# by itself.
+OPTS = {"side": True}
 N = 64
 
 
@@ -180,7 +185,7 @@ def setup_timemix():
     def step():
         f = binding.timemix_forward(s, W, x, v_first=vf, want_cache=True, want_state=False)
         binding.timemix_backward(s, W, x, dout, v_first=vf, cache=f["cache"], want_dx_prev=False,
-                                 want_ds0=False)
+                                 want_ds0=False, side=OPTS["side"])
 
     # dominant kernel: the fp32 MFMA GEMM of the C x C projections
     # (X [BT][C] . W [C][C]; 2*BT*C*C flop per launch)
@@ -375,7 +380,7 @@ def setup_train():
     ws = torch.empty(binding.rwkv7_train_workspace_bytes(dm, B, T), dtype=torch.uint8, device=dev)
 
     def step():
-        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws)
+        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws, side=OPTS["side"])
 
     # dominant kernels: the bf16 matrix-core GEMMs; the timed one is the
     # channel-mix key projection [8192][1024] . [1024][4096], as the training
@@ -445,7 +450,7 @@ def setup_hybrid():
     ws = torch.empty(binding.rwkv7_train_workspace_bytes(dm, B, T), dtype=torch.uint8, device=dev)
 
     def step():
-        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws)
+        binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws, side=OPTS["side"])
 
     # dominant kernel of the attention: the MoBA core backward of one block
     # ([4][2048][16 x 64] q, k, v), against the fp32 ALU ceiling: 5 products of
@@ -691,7 +696,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the time-mix and training-step workloads without the side stream (counter "
+                         "runs that time each kernel alone)")
     args = ap.parse_args()
+    OPTS["side"] = not args.one_stream
     if args.copy_calibration:
         import torch
         n = 64 * 1024 * 1024

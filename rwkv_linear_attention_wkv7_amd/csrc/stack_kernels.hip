@@ -203,9 +203,9 @@ __global__ __launch_bounds__(256) void fill_zero(size_t n, float* __restrict__ p
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.f;
 }
 
-constexpr int LN_ROWS = 16;  // rows per workgroup in the LayerNorm backward (partial sums)
+constexpr int LN_ROWS = 8;  // rows per workgroup in the LayerNorm backward (partial sums)
 
-// LayerNorm backward, one wave per row (row in registers), 4 waves x 4 rows
+// LayerNorm backward, one wave per row (row in registers), 4 waves x 2 rows
 // per workgroup.  dx = rstd (dn - mean(dn) - nhat mean(dn nhat)) + dres,
 // dn = dy w; per-channel partials of dw = sum dy nhat and db = sum dy are
 // written as part[0|1][blk][C] (summed later in a fixed order).
@@ -226,15 +226,19 @@ __global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* 
   for (int row = blk * LN_ROWS + wave; row < r_end; row += 4) {
     const f4* xr = reinterpret_cast<const f4*>(x + (size_t)row * C);
     const f4* gr = reinterpret_cast<const f4*>(dy + (size_t)row * C);
-    f4 xv[MAXC4], gv[MAXC4];
+    const f4* rr = dres ? reinterpret_cast<const f4*>(dres + (size_t)row * C) : nullptr;
+    f4 xv[MAXC4], gv[MAXC4], rv[MAXC4];
     float s = 0.f;
+    // the row's x, dy and residual gradient are all requested up front
 #pragma unroll
     for (int j = 0; j < MAXC4; j++) {
       const int c4 = lane + 64 * j;
       xv[j] = c4 < C4 ? xr[c4] : f4{0.f, 0.f, 0.f, 0.f};
       gv[j] = c4 < C4 ? gr[c4] : f4{0.f, 0.f, 0.f, 0.f};
-      s += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
+      rv[j] = (rr && c4 < C4) ? rr[c4] : f4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) s += (xv[j][0] + xv[j][1]) + (xv[j][2] + xv[j][3]);
     const float mean = wavesum(s) / C;
     float q = 0.f;
 #pragma unroll
@@ -264,13 +268,11 @@ __global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* 
     m1 = wavesum(m1) / C;
     m2 = wavesum(m2) / C;
     f4* dxr = reinterpret_cast<f4*>(dx + (size_t)row * C);
-    const f4* rr = dres ? reinterpret_cast<const f4*>(dres + (size_t)row * C) : nullptr;
 #pragma unroll
     for (int j = 0; j < MAXC4; j++) {
       const int c4 = lane + 64 * j;
       if (c4 < C4) {
-        f4 o = rstd * (gv[j] - m1 - xv[j] * m2);
-        if (rr) o += rr[c4];
+        f4 o = rstd * (gv[j] - m1 - xv[j] * m2) + rv[j];
         dxr[c4] = o;
       }
     }
