@@ -465,8 +465,55 @@ __device__ __forceinline__ int slot_of(uint64_t m, int c) {
   return __popcll(m & (c ? (~(uint64_t)0 >> (64 - c)) : (uint64_t)0));
 }
 
-// Forward partials: grid (chunks, B H); the workgroup walks the chunk's
-// list in blocks of 64 queries (K and V of the chunk loaded once).
+// Matrix-core helpers of the gathered kernels (v_mfma_f32_16x16x4_f32).
+// c += A B over one group of 16 k: lane l supplies A[l%16][4(l/16)+s] in
+// a[s] and B[4(l/16)+s][l%16] in b[s]; the result tile: lane l element v
+// holds C[4(l/16)+v][l%16].
+__device__ __forceinline__ f4 mma16(f4 a, f4 b, f4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ f4 ldf4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+// B fragment from a row-layout tile X[k][n]: X[k0 + 4 fg + s][n] for s < 4.
+__device__ __forceinline__ f4 colf4(const float (*X)[LP], int k0, int fg, int n) {
+  return f4{X[k0 + 4 * fg][n], X[k0 + 4 * fg + 1][n], X[k0 + 4 * fg + 2][n], X[k0 + 4 * fg + 3][n]};
+}
+// Max over the 16 lanes of a DPP row (every lane of the row receives it).
+__device__ __forceinline__ float rowmax16(float x) {
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(-INFINITY, x, 0xB1, 0xF, 0xF, false));
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(-INFINITY, x, 0x4E, 0xF, 0xF, false));
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(-INFINITY, x, 0x141, 0xF, 0xF, false));
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(-INFINITY, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+// Gathered rows (row layout X[row][c]) with any block size.
+template <int NT>
+__device__ __forceinline__ void gather_rows(float (*X)[LP], const float* __restrict__ src,
+                                            const int* idx, int n, int b, int T, int C, int h) {
+  for (int i = threadIdx.x; i < TS * HN / 4; i += NT) {
+    const int row = i / (HN / 4), c = (i % (HN / 4)) * 4;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < n) v = *reinterpret_cast<const f4*>(src + ((size_t)b * T + idx[row]) * C + h * HN + c);
+    *reinterpret_cast<f4*>(&X[row][c]) = v;
+  }
+}
+template <int NT>
+__device__ __forceinline__ void load_rows(float (*X)[LP], const float* __restrict__ src, int b, int T,
+                                          int C, int h, int r0) {
+  for (int i = threadIdx.x; i < TS * HN / 4; i += NT) {
+    const int row = i / (HN / 4), c = (i % (HN / 4)) * 4, t = r0 + row;
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (t < T) v = *reinterpret_cast<const f4*>(src + ((size_t)b * T + t) * C + h * HN + c);
+    *reinterpret_cast<f4*>(&X[row][c]) = v;
+  }
+}
+
+// Forward partials: grid (chunks, B H), 4 waves; the workgroup walks the
+// chunk's list in blocks of 64 queries (K and V of the chunk loaded once).
+// Wave w owns gathered queries 16w..16w+15: S = Q K^T and O = P V on the
+// matrix cores, the row max and sum over the chunk's 64 keys in-lane and
+// across the lanes of a DPP row.
 // po[bh][t][j][64] = sum_key e^(s - m) v, pm / pl[bh][t][j] = m and the sum of
 // e^(s - m) over the chunk's allowed keys (s = q.k / 8).
 __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const float* __restrict__ q,
@@ -474,64 +521,75 @@ __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const
                                               const uint64_t* __restrict__ sel, const int* __restrict__ list,
                                               const int* __restrict__ cnt, float* __restrict__ po,
                                               float* __restrict__ pm, float* __restrict__ pl) {
-  __shared__ float qT[HN][LP], kT[HN][LP], vR[TS][LP], pT[TS][LP];
+  __shared__ __attribute__((aligned(16))) float qR[TS][LP], kR[TS][LP], vR[TS][LP], pN[TS][LP];
   __shared__ int idx[TS];
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
   const int n_all = cnt[(size_t)bh * nc + c];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, fr = lane & 15, fg = lane >> 4;
   const int* lst = list + ((size_t)bh * nc + c) * T;
-  load_T(kT, k, b, T, C, h, c * TS);
-  load_R(vR, v, b, T, C, h, c * TS);
+  load_rows<256>(kR, k, b, T, C, h, c * TS);
+  load_rows<256>(vR, v, b, T, C, h, c * TS);
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 < n_all; b0 += TS) {
     const int n = min(TS, n_all - b0);
     __syncthreads();  // the previous block's readers are done
     if (tid < TS) idx[tid] = tid < n ? lst[b0 + tid] : 0;
     __syncthreads();
-    gather_T(qT, q, idx, n, b, T, C, h);
+    gather_rows<256>(qR, q, idx, n, b, T, C, h);
     __syncthreads();
-    float s[4][4] = {};
-    mm_tt(qT, kT, ty, tx, s);
+    // s[jt][vv] = S[query 16w + 4fg + vv][key 16jt + fr]
+    f4 s[4] = {z, z, z, z};
+#pragma unroll
+    for (int kg = 0; kg < 4; kg++) {
+      const f4 a = ldf4(&qR[16 * w + fr][16 * kg + 4 * fg]);
+#pragma unroll
+      for (int jt = 0; jt < 4; jt++) s[jt] = mma16(a, ldf4(&kR[16 * jt + fr][16 * kg + 4 * fg]), s[jt]);
+    }
     float m[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 4 * ty + i;
+    for (int vv = 0; vv < 4; vv++) {
+      const int r = 16 * w + 4 * fg + vv;
       const int t = r < n ? idx[r] : -1;
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int key = c * TS + 4 * tx + j;
+      for (int jt = 0; jt < 4; jt++) {
+        const int key = c * TS + 16 * jt + fr;
         const bool ok = t >= 0 && key <= t;  // key <= t < T
-        s[i][j] = ok ? s[i][j] * SCALE : -INFINITY;
-        mx = fmaxf(mx, s[i][j]);
+        s[jt][vv] = ok ? s[jt][vv] * SCALE : -INFINITY;
+        mx = fmaxf(mx, s[jt][vv]);
       }
-      m[i] = fmaxf(max16(mx), -1e30f);
+      m[vv] = fmaxf(rowmax16(mx), -1e30f);
       float rs = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        s[i][j] = expf(s[i][j] - m[i]);
-        rs += s[i][j];
+      for (int jt = 0; jt < 4; jt++) {
+        s[jt][vv] = expf(s[jt][vv] - m[vv]);
+        rs += s[jt][vv];
+        pN[r][16 * jt + fr] = s[jt][vv];
       }
-      l[i] = sum16(rs);
+      l[vv] = rowsum16(rs);
+    }
+    __syncthreads();
+    // o[jt][vv] = O[query 16w + 4fg + vv][d 16jt + fr] = sum_key P V
+    f4 o[4] = {z, z, z, z};
+#pragma unroll
+    for (int kg = 0; kg < 4; kg++) {
+      const f4 a = ldf4(&pN[16 * w + fr][16 * kg + 4 * fg]);
+#pragma unroll
+      for (int jt = 0; jt < 4; jt++) o[jt] = mma16(a, colf4(vR, 16 * kg, fg, 16 * jt + fr), o[jt]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) pT[4 * tx + j][4 * ty + i] = s[i][j];
-    __syncthreads();
-    float o[4][4] = {};
-    mm_rr(pT, vR, ty, tx, o);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 4 * ty + i;
+    for (int vv = 0; vv < 4; vv++) {
+      const int r = 16 * w + 4 * fg + vv;
       if (r >= n) continue;
       const int t = idx[r];
       const int j = slot_of(sel[(size_t)bh * T + t], c);
       if (j >= K) continue;  // a mask with more chunks than topk (not one the selection wrote)
       const size_t e = ((size_t)bh * T + t) * K + j;
-      *reinterpret_cast<f4*>(po + e * HN + 4 * tx) = f4{o[i][0], o[i][1], o[i][2], o[i][3]};
-      if (tx == 0) {
-        pm[e] = m[i];
-        pl[e] = l[i];
+#pragma unroll
+      for (int jt = 0; jt < 4; jt++) po[e * HN + 16 * jt + fr] = o[jt][vv];
+      if (fr == 0) {
+        pm[e] = m[vv];
+        pl[e] = l[vv];
       }
     }
   }
@@ -572,27 +630,34 @@ __global__ __launch_bounds__(256) void sp_rowdot(int BHT, int T, int H, const fl
   if (l16 == 0) D[g] = d;
 }
 
-// Backward per chunk: grid (chunks, B H).  dk, dv of the chunk's keys; each
-// listed query's dq share into pq[bh][t][j][64] (scaled).
-__global__ __launch_bounds__(256) void sp_bwd(int T, int H, int nc, int K, const float* __restrict__ q,
+// Backward per chunk: grid (chunks, B H), 8 waves.  dk, dv of the chunk's
+// keys; each listed query's dq share into pq[bh][t][j][64] (scaled).  Per
+// block of 64 gathered queries, on the matrix cores: S^T = K Q^T and
+// dP^T = V dY^T (wave w: keys of tile w%4, query tiles 2(w/4), 2(w/4)+1),
+// P and dS = P (dP - D) to LDS as [key][query], then dV += P^T dY and
+// dK += dS^T Q (keys of tile w%4, head dims of tiles 2(w/4)..) and the dq
+// shares dS K (queries of tile w%4).
+__global__ __launch_bounds__(512) void sp_bwd(int T, int H, int nc, int K, const float* __restrict__ q,
                                               const float* __restrict__ k, const float* __restrict__ v,
                                               const float* __restrict__ lse, const float* __restrict__ Din,
                                               const uint64_t* __restrict__ sel, const float* __restrict__ dy,
                                               const int* __restrict__ list, const int* __restrict__ cnt,
                                               float* __restrict__ dk, float* __restrict__ dv,
                                               float* __restrict__ pq) {
-  __shared__ float kT[HN][LP], vT[HN][LP], kR[TS][LP], qT[HN][LP], doT[HN][LP], qR[TS][LP], doR[TS][LP];
-  __shared__ float pds[TS][LP], dsT[TS][LP];
+  __shared__ __attribute__((aligned(16))) float kR[TS][LP], vR[TS][LP], qR[TS][LP], doR[TS][LP];
+  __shared__ __attribute__((aligned(16))) float pT[TS][LP], dsT[TS][LP];
   __shared__ int idx[TS];
   __shared__ float Ls[TS], Ds[TS];
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, fr = lane & 15, fg = lane >> 4;
+  const int rt = w & 3, cp = w >> 2;  // row tile, pair of column tiles
   const int n_all = cnt[(size_t)bh * nc + c];
   const int* lst = list + ((size_t)bh * nc + c) * T;
-  load_T(kT, k, b, T, C, h, c * TS);
-  load_T(vT, v, b, T, C, h, c * TS);
-  load_R(kR, k, b, T, C, h, c * TS);
-  float adk[4][4] = {}, adv[4][4] = {};
+  load_rows<512>(kR, k, b, T, C, h, c * TS);
+  load_rows<512>(vR, v, b, T, C, h, c * TS);
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  // adk[u][vv] = dK[key 16rt + 4fg + vv][d 16(2cp + u) + fr] (adv the same for dV)
+  f4 adk[2] = {z, z}, adv[2] = {z, z};
   for (int b0 = 0; b0 < n_all; b0 += TS) {
     const int n = min(TS, n_all - b0);
     __syncthreads();  // the previous block's readers are done
@@ -603,59 +668,79 @@ __global__ __launch_bounds__(256) void sp_bwd(int T, int H, int nc, int K, const
       Ds[tid] = tid < n ? Din[(size_t)bh * T + t] : 0.f;
     }
     __syncthreads();
-    gather_T(qT, q, idx, n, b, T, C, h);
-    gather_T(doT, dy, idx, n, b, T, C, h);
-    gather_R(qR, q, idx, n, b, T, C, h);
-    gather_R(doR, dy, idx, n, b, T, C, h);
+    gather_rows<512>(qR, q, idx, n, b, T, C, h);
+    gather_rows<512>(doR, dy, idx, n, b, T, C, h);
     __syncthreads();
-    // rows of S^T: keys 4 ty + i; columns: gathered queries 4 tx + j
-    float s[4][4] = {}, dp[4][4] = {};
-    mm_tt(kT, qT, ty, tx, s);
-    mm_tt(vT, doT, ty, tx, dp);
-    float ds[4][4];
+    // s[u][vv] = S^T[key 16rt + 4fg + vv][query 16(2cp + u) + fr]; dp likewise
+    f4 s[2] = {z, z}, dp[2] = {z, z};
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int qi = 4 * tx + j;
+    for (int kg = 0; kg < 4; kg++) {
+      const f4 ak = ldf4(&kR[16 * rt + fr][16 * kg + 4 * fg]);
+      const f4 av = ldf4(&vR[16 * rt + fr][16 * kg + 4 * fg]);
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int qr = 16 * (2 * cp + u) + fr;
+        s[u] = mma16(ak, ldf4(&qR[qr][16 * kg + 4 * fg]), s[u]);
+        dp[u] = mma16(av, ldf4(&doR[qr][16 * kg + 4 * fg]), dp[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int qi = 16 * (2 * cp + u) + fr;
       const int t = qi < n ? idx[qi] : -1;
       const float L = Ls[qi], D = Ds[qi];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int key = c * TS + 4 * ty + i;
-        const float p = (t >= 0 && key <= t) ? expf(s[i][j] * SCALE - L) : 0.f;
-        ds[i][j] = p * (dp[i][j] - D);
-        pds[qi][4 * ty + i] = p;
-        dsT[4 * ty + i][qi] = ds[i][j];
+      for (int vv = 0; vv < 4; vv++) {
+        const int kl = 16 * rt + 4 * fg + vv, key = c * TS + kl;
+        const float p = (t >= 0 && key <= t) ? expf(s[u][vv] * SCALE - L) : 0.f;
+        pT[kl][qi] = p;
+        dsT[kl][qi] = p * (dp[u][vv] - D);
       }
     }
     __syncthreads();
-    mm_rr(pds, doR, ty, tx, adv);  // dv[key][d] += sum_q P[q][key] dy[q][d]
-    __syncthreads();
+    // dV[key][d] += sum_q P^T[key][q] dY[q][d];  dK[key][d] += sum_q dS^T[key][q] Q[q][d]
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int kg = 0; kg < 4; kg++) {
+      const f4 ap = ldf4(&pT[16 * rt + fr][16 * kg + 4 * fg]);
+      const f4 ad = ldf4(&dsT[16 * rt + fr][16 * kg + 4 * fg]);
 #pragma unroll
-      for (int i = 0; i < 4; i++) pds[4 * tx + j][4 * ty + i] = ds[i][j];
-    __syncthreads();
-    mm_rr(pds, qR, ty, tx, adk);  // dk[key][d] += sum_q dS[q][key] q[q][d]
-    float aq[4][4] = {};
-    mm_rr(dsT, kR, ty, tx, aq);   // dq share[q][d] = sum_key dS[q][key] k[key][d]
+      for (int u = 0; u < 2; u++) {
+        const int dcol = 16 * (2 * cp + u) + fr;
+        adv[u] = mma16(ap, colf4(doR, 16 * kg, fg, dcol), adv[u]);
+        adk[u] = mma16(ad, colf4(qR, 16 * kg, fg, dcol), adk[u]);
+      }
+    }
+    // dq share[q][d] = sum_key dS[q][key] K[key][d]: queries of tile rt
+    f4 aq[2] = {z, z};
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 4 * ty + i;
+    for (int kg = 0; kg < 4; kg++) {
+      const f4 a = {dsT[16 * kg + 4 * fg][16 * rt + fr], dsT[16 * kg + 4 * fg + 1][16 * rt + fr],
+                    dsT[16 * kg + 4 * fg + 2][16 * rt + fr], dsT[16 * kg + 4 * fg + 3][16 * rt + fr]};
+#pragma unroll
+      for (int u = 0; u < 2; u++) aq[u] = mma16(a, colf4(kR, 16 * kg, fg, 16 * (2 * cp + u) + fr), aq[u]);
+    }
+#pragma unroll
+    for (int vv = 0; vv < 4; vv++) {
+      const int r = 16 * rt + 4 * fg + vv;
       if (r >= n) continue;
       const int t = idx[r];
       const int j = slot_of(sel[(size_t)bh * T + t], c);
       if (j >= K) continue;  // as in sp_fwd
-      *reinterpret_cast<f4*>(pq + (((size_t)bh * T + t) * K + j) * HN + 4 * tx) =
-          f4{aq[i][0] * SCALE, aq[i][1] * SCALE, aq[i][2] * SCALE, aq[i][3] * SCALE};
+      float* dst = pq + (((size_t)bh * T + t) * K + j) * HN;
+#pragma unroll
+      for (int u = 0; u < 2; u++) dst[16 * (2 * cp + u) + fr] = aq[u][vv] * SCALE;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int key = c * TS + 4 * ty + i;
+  for (int vv = 0; vv < 4; vv++) {
+    const int key = c * TS + 16 * rt + 4 * fg + vv;
     if (key >= T) continue;
-    const size_t e = ((size_t)b * T + key) * C + h * HN + 4 * tx;
-    *reinterpret_cast<f4*>(dk + e) = f4{adk[i][0] * SCALE, adk[i][1] * SCALE, adk[i][2] * SCALE, adk[i][3] * SCALE};
-    *reinterpret_cast<f4*>(dv + e) = f4{adv[i][0], adv[i][1], adv[i][2], adv[i][3]};
+    const size_t e = ((size_t)b * T + key) * C + h * HN;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      dk[e + 16 * (2 * cp + u) + fr] = adk[u][vv] * SCALE;
+      dv[e + 16 * (2 * cp + u) + fr] = adv[u][vv];
+    }
   }
 }
 
@@ -752,7 +837,7 @@ hipError_t moba_launch_backward(int B, int T, int H, int chunk, int topk, const 
   const int K = std::min(topk, nc), BHT = B * H * T;
   hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
   hipLaunchKernelGGL(mobak::sp_rowdot, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, y, dy, w.D);
-  hipLaunchKernelGGL(mobak::sp_bwd, dim3(nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, lse, w.D, sel,
+  hipLaunchKernelGGL(mobak::sp_bwd, dim3(nc, B * H), dim3(512), 0, st, T, H, nc, K, q, k, v, lse, w.D, sel,
                      dy, w.list, w.cnt, dk, dv, w.part);
   hipLaunchKernelGGL(mobak::sp_dq, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part, dq);
   return hipGetLastError();
