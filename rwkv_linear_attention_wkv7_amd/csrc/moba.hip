@@ -509,8 +509,9 @@ __device__ __forceinline__ void load_rows(float (*X)[LP], const float* __restric
   }
 }
 
-// Forward partials: grid (chunks, B H), 4 waves; the workgroup walks the
-// chunk's list in blocks of 64 queries (K and V of the chunk loaded once).
+// Forward partials: grid (half the chunks, B H), 4 waves; the workgroup walks
+// the lists of two chunks in blocks of 64 queries (K and V of a chunk loaded
+// once).
 // Wave w owns gathered queries 16w..16w+15: S = Q K^T and O = P V on the
 // matrix cores, the row max and sum over the chunk's 64 keys in-lane and
 // across the lanes of a DPP row.
@@ -523,13 +524,19 @@ __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const
                                               float* __restrict__ pm, float* __restrict__ pl) {
   __shared__ __attribute__((aligned(16))) float qR[TS][LP], kR[TS][LP], vR[TS][LP], pN[TS][LP];
   __shared__ int idx[TS];
-  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
-  const int n_all = cnt[(size_t)bh * nc + c];
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, fr = lane & 15, fg = lane >> 4;
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  // chunks x and nc-1-x: an early chunk (selected by many later queries)
+  // with a late one, so the workgroups carry similar work
+  for (int pass = 0; pass < 2; pass++) {
+  const int c = pass == 0 ? blockIdx.x : nc - 1 - blockIdx.x;
+  if (pass == 1 && c == blockIdx.x) break;
+  const int n_all = cnt[(size_t)bh * nc + c];
   const int* lst = list + ((size_t)bh * nc + c) * T;
+  __syncthreads();  // the previous chunk's readers are done
   load_rows<256>(kR, k, b, T, C, h, c * TS);
   load_rows<256>(vR, v, b, T, C, h, c * TS);
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 < n_all; b0 += TS) {
     const int n = min(TS, n_all - b0);
     __syncthreads();  // the previous block's readers are done
@@ -593,6 +600,7 @@ __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const
       }
     }
   }
+  }
 }
 
 // Merge: 16 lanes per (b, h, t); the query's slots combined in chunk order.
@@ -630,7 +638,7 @@ __global__ __launch_bounds__(256) void sp_rowdot(int BHT, int T, int H, const fl
   if (l16 == 0) D[g] = d;
 }
 
-// Backward per chunk: grid (chunks, B H), 8 waves.  dk, dv of the chunk's
+// Backward per chunk pair: grid (half the chunks, B H), 8 waves.  dk, dv of a chunk's
 // keys; each listed query's dq share into pq[bh][t][j][64] (scaled).  Per
 // block of 64 gathered queries, on the matrix cores: S^T = K Q^T and
 // dP^T = V dY^T (wave w: keys of tile w%4, query tiles 2(w/4), 2(w/4)+1),
@@ -648,14 +656,19 @@ __global__ __launch_bounds__(512) void sp_bwd(int T, int H, int nc, int K, const
   __shared__ __attribute__((aligned(16))) float pT[TS][LP], dsT[TS][LP];
   __shared__ int idx[TS];
   __shared__ float Ls[TS], Ds[TS];
-  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H, C = H * HN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, fr = lane & 15, fg = lane >> 4;
   const int rt = w & 3, cp = w >> 2;  // row tile, pair of column tiles
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  // chunks x and nc-1-x (as in sp_fwd)
+  for (int pass = 0; pass < 2; pass++) {
+  const int c = pass == 0 ? blockIdx.x : nc - 1 - blockIdx.x;
+  if (pass == 1 && c == blockIdx.x) break;
   const int n_all = cnt[(size_t)bh * nc + c];
   const int* lst = list + ((size_t)bh * nc + c) * T;
+  __syncthreads();  // the previous chunk's readers are done
   load_rows<512>(kR, k, b, T, C, h, c * TS);
   load_rows<512>(vR, v, b, T, C, h, c * TS);
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
   // adk[u][vv] = dK[key 16rt + 4fg + vv][d 16(2cp + u) + fr] (adv the same for dV)
   f4 adk[2] = {z, z}, adv[2] = {z, z};
   for (int b0 = 0; b0 < n_all; b0 += TS) {
@@ -742,6 +755,7 @@ __global__ __launch_bounds__(512) void sp_bwd(int T, int H, int nc, int K, const
       dv[e + 16 * (2 * cp + u) + fr] = adv[u][vv];
     }
   }
+  }
 }
 
 // dq = sum over the query's slots in chunk order (16 lanes per row).
@@ -813,7 +827,7 @@ hipError_t moba_launch_forward(int B, int T, int H, int chunk, int topk, const f
   }
   const int K = std::min(topk, nc), BHT = B * H * T;
   hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
-  hipLaunchKernelGGL(mobak::sp_fwd, dim3(nc, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, sel, w.list,
+  hipLaunchKernelGGL(mobak::sp_fwd, dim3((nc + 1) / 2, B * H), dim3(256), 0, st, T, H, nc, K, q, k, v, sel, w.list,
                      w.cnt, w.part, w.pm, w.pl);
   hipLaunchKernelGGL(mobak::sp_merge, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part,
                      w.pm, w.pl, y, lse);
@@ -837,7 +851,7 @@ hipError_t moba_launch_backward(int B, int T, int H, int chunk, int topk, const 
   const int K = std::min(topk, nc), BHT = B * H * T;
   hipLaunchKernelGGL(mobak::sp_list, dim3(nc, B * H), dim3(256), 0, st, T, nc, sel, w.list, w.cnt);
   hipLaunchKernelGGL(mobak::sp_rowdot, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, y, dy, w.D);
-  hipLaunchKernelGGL(mobak::sp_bwd, dim3(nc, B * H), dim3(512), 0, st, T, H, nc, K, q, k, v, lse, w.D, sel,
+  hipLaunchKernelGGL(mobak::sp_bwd, dim3((nc + 1) / 2, B * H), dim3(512), 0, st, T, H, nc, K, q, k, v, lse, w.D, sel,
                      dy, w.list, w.cnt, dk, dv, w.part);
   hipLaunchKernelGGL(mobak::sp_dq, dim3((BHT + 15) / 16), dim3(256), 0, st, BHT, T, H, K, sel, w.part, dq);
   return hipGetLastError();
