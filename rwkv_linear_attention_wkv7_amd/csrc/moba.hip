@@ -537,13 +537,30 @@ __global__ __launch_bounds__(256) void sp_fwd(int T, int H, int nc, int K, const
   __syncthreads();  // the previous chunk's readers are done
   load_rows<256>(kR, k, b, T, C, h, c * TS);
   load_rows<256>(vR, v, b, T, C, h, c * TS);
+  // Block b0's list entries and gathered q rows are fetched into registers
+  // while block b0 - 64 runs (thread: list entry tid; rows tid/16 + 16 j,
+  // 4 columns at 4 (tid%16)).
+  int pt = 0;
+  f4 pq4[4];
+  auto fetch = [&](int b0) {
+    const int n = min(TS, n_all - b0);
+    if (tid < TS) pt = tid < n ? lst[b0 + tid] : 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int row = (tid >> 4) + 16 * j, cc = (tid & 15) * 4;
+      pq4[j] = row < n ? *reinterpret_cast<const f4*>(q + ((size_t)b * T + lst[b0 + row]) * C + h * HN + cc) : z;
+    }
+  };
+  if (n_all > 0) fetch(0);
   for (int b0 = 0; b0 < n_all; b0 += TS) {
     const int n = min(TS, n_all - b0);
     __syncthreads();  // the previous block's readers are done
-    if (tid < TS) idx[tid] = tid < n ? lst[b0 + tid] : 0;
+    if (tid < TS) idx[tid] = pt;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      *reinterpret_cast<f4*>(&qR[(tid >> 4) + 16 * j][(tid & 15) * 4]) = pq4[j];
     __syncthreads();
-    gather_rows<256>(qR, q, idx, n, b, T, C, h);
-    __syncthreads();
+    if (b0 + TS < n_all) fetch(b0 + TS);
     // s[jt][vv] = S[query 16w + 4fg + vv][key 16jt + fr]
     f4 s[4] = {z, z, z, z};
 #pragma unroll
@@ -671,19 +688,47 @@ __global__ __launch_bounds__(512) void sp_bwd(int T, int H, int nc, int K, const
   load_rows<512>(vR, v, b, T, C, h, c * TS);
   // adk[u][vv] = dK[key 16rt + 4fg + vv][d 16(2cp + u) + fr] (adv the same for dV)
   f4 adk[2] = {z, z}, adv[2] = {z, z};
+  // Block b0's list entries, their lse and D, and its gathered q and dy rows
+  // are fetched into registers while block b0 - 64 runs (thread: list
+  // entry tid; rows tid/16 and tid/16 + 32, 4 columns at 4 (tid%16)).
+  int pt = 0;
+  float pL = 0.f, pD = 0.f;
+  f4 pq4[2], pd4[2];
+  auto fetch = [&](int b0) {
+    const int n = min(TS, n_all - b0);
+    if (tid < TS) {
+      pt = tid < n ? lst[b0 + tid] : 0;
+      pL = tid < n ? lse[(size_t)bh * T + pt] : 0.f;
+      pD = tid < n ? Din[(size_t)bh * T + pt] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int row = (tid >> 4) + 32 * j, cc = (tid & 15) * 4;
+      pq4[j] = pd4[j] = z;
+      if (row < n) {
+        const size_t o = ((size_t)b * T + lst[b0 + row]) * C + h * HN + cc;
+        pq4[j] = *reinterpret_cast<const f4*>(q + o);
+        pd4[j] = *reinterpret_cast<const f4*>(dy + o);
+      }
+    }
+  };
+  if (n_all > 0) fetch(0);
   for (int b0 = 0; b0 < n_all; b0 += TS) {
     const int n = min(TS, n_all - b0);
     __syncthreads();  // the previous block's readers are done
     if (tid < TS) {
-      const int t = tid < n ? lst[b0 + tid] : 0;
-      idx[tid] = t;
-      Ls[tid] = tid < n ? lse[(size_t)bh * T + t] : 0.f;
-      Ds[tid] = tid < n ? Din[(size_t)bh * T + t] : 0.f;
+      idx[tid] = pt;
+      Ls[tid] = pL;
+      Ds[tid] = pD;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int row = (tid >> 4) + 32 * j, cc = (tid & 15) * 4;
+      *reinterpret_cast<f4*>(&qR[row][cc]) = pq4[j];
+      *reinterpret_cast<f4*>(&doR[row][cc]) = pd4[j];
     }
     __syncthreads();
-    gather_rows<512>(qR, q, idx, n, b, T, C, h);
-    gather_rows<512>(doR, dy, idx, n, b, T, C, h);
-    __syncthreads();
+    if (b0 + TS < n_all) fetch(b0 + TS);
     // s[u][vv] = S^T[key 16rt + 4fg + vv][query 16(2cp + u) + fr]; dp likewise
     f4 s[2] = {z, z}, dp[2] = {z, z};
 #pragma unroll
