@@ -453,8 +453,9 @@ def setup_hybrid():
         binding.rwkv7_train_step(dm, grads, x, y, loss=loss, ws=ws, side=OPTS["side"])
 
     # dominant kernel of the attention: the MoBA core backward of one block
-    # ([4][2048][16 x 64] q, k, v), against the fp32 ALU ceiling: 5 products of
-    # 2 N flop per attended (query, key) pair (S recomputed, dP, dQ, dK, dV)
+    # ([4][2048][16 x 64] q, k, v); its products run as fp32 matrix-core tiles,
+    # so the ceiling is the fp32 MFMA peak: 5 products of 2 N flop per attended
+    # (query, key) pair (S recomputed, dP, dQ, dK, dV)
     g = torch.Generator(device=dev).manual_seed(0)
     q, k, v, dy = (torch.randn(B, T, C, device=dev, generator=g) for _ in range(4))
     yo, lse, sel = binding.moba_forward(q, k, v, H, chunk, topk)
@@ -466,8 +467,8 @@ def setup_hybrid():
 
     flops = 5.0 * 2 * 64 * moba_attended_keys(T, chunk, topk) * B * H
     roof = dict(kernel=f"moba_backward (B={B} T={T} H={H}, chunks of {chunk}, top-{topk}: dQ pass + "
-                       "dK/dV pass)", bound="alu", work=flops, unit="TFLOP/s",
-                peak=PEAK["alu_fp32"][0], fn=dom, key="moba_bwd",
+                       "dK/dV pass)", bound="mfma", work=flops, unit="TFLOP/s",
+                peak=PEAK["mfma_fp32"][0], fn=dom, key="moba_bwd",
                 src=["rwkv_linear_attention_wkv7_amd/csrc/moba.hip"])
 
     def cpu():
