@@ -562,7 +562,8 @@ void tm_weight_spans(Spans& sp, const tm_shape* s, const WT* W, bool written) {
 }
 
 // decode: T == 1 with the WKV state updated in place (s0 == sT, no checkpoint),
-// run by the bandwidth-bound step kernel.  out = out_beta * out + tg Wo.
+// run by one fused kernel (pre-WKV, the step on the state in place, post-WKV).
+// out = out_beta * out + tg Wo.
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
@@ -622,14 +623,14 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     if (s->layer_id > 0) g.p[g.count++] = prob(BT, C, s->Dv, m.lv, s->Dv, W->V2, C, m.ov, C, EPI_NONE);
     HIPCHK(gemm_batch(prec, false, false, g, st), "lora up");
   }
-  HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
-  if (decode)
-    HIPCHK(wkv7_launch_step(WKV7_F32, B, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, sT, m.y, st),
-           "wkv7 step");
-  else
+  if (decode) {
+    HIPCHK(tm_launch_step_fused(p, sT, st), "pre-wkv + wkv7 step + post-wkv");
+  } else {
+    HIPCHK(tm_launch_pre_fwd(p, st), "pre-wkv");
     HIPCHK(wkv7_launch_forward(WKV7_F32, B, T, s->H, m.r, m.w, m.kmod, m.vmod, m.A, m.Bv, s0, m.y, sT,
                                m.ckpt, m.wkv_ws, st), "wkv7 forward");
-  HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
+    HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
+  }
   HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;
 }

@@ -144,6 +144,104 @@ __global__ __launch_bounds__(256) void post_fwd(TmFwd p) {
   }
 }
 
+// Decode (T = 1): pre-WKV, the WKV7 step with the state updated in place, and
+// post-WKV in one workgroup per (b, h), the three steps above with the same
+// lane layouts, so the results equal those of pre_fwd, the step kernel and
+// post_fwd one after the other.  Lanes 0..15 form the head's pre-WKV vectors
+// (channel 4 l16 .. 4 l16 + 3 each) and share them through LDS while every
+// thread's state rows are in flight; thread (rg, cg) then owns state rows
+// rg + 16m (m < 4) x columns 4cg..4cg+3 (the step kernel's layout); y goes
+// back through LDS to lanes 0..15 for the group norm, the bonus and the gate.
+// Only v_first (layer 0) and tg are written: decode keeps no backward cache.
+__global__ __launch_bounds__(256) void step_fused(TmFwd p, float* __restrict__ state) {
+  __shared__ f4 sv[6][16];  // w, k', A, Bv, r, v' by channel group
+  __shared__ float sy[N];
+  const int H = p.C / N;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int bt = bh / H, h = bh - bt * H;  // token row = stream (T = 1)
+  const int tid = threadIdx.x, cg = tid & 15, rg = tid >> 4;
+  float* st = state + (size_t)bh * N * N;
+  f4 S[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+    S[m] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(st + (size_t)(rg + 16 * m) * N + cg * 4));
+
+  const int c = h * N + cg * 4;
+  const size_t e = (size_t)bt * p.C + c;
+  f4 r, kmod, vmod;
+  if (tid < 16) {
+    const f4 k = ld4(p.k + e), v = ld4(p.v + e), ow = ld4(p.ow + e), oa = ld4(p.oa + e);
+    const f4 w0 = ld4(p.w0 + c), a0 = ld4(p.a0 + c), kkw = ld4(p.k_k + c), ka = ld4(p.k_a + c);
+    r = ld4(p.r + e);
+    f4 w, a, tk;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      w[j] = expf(-DECAY * sigm(w0[j] + ow[j]));
+      a[j] = sigm(a0[j] + oa[j]);
+      tk[j] = k[j] * kkw[j];
+    }
+    const float nrm = sqrtf(rowsum16(hsum4(tk * tk)));
+    const float inv = 1.0f / (nrm + L2_EPS);
+    const f4 kk = tk * inv;
+#pragma unroll
+    for (int j = 0; j < 4; j++) kmod[j] = k[j] * (1.0f + (a[j] - 1.0f) * ka[j]);
+    if (p.layer_id == 0) {
+      vmod = v;
+      st4(p.v_first + e, v);
+    } else {
+      const f4 vf = ld4(p.v_first + e), ov = ld4(p.ov + e), v0 = ld4(p.v0 + c);
+#pragma unroll
+      for (int j = 0; j < 4; j++) vmod[j] = v[j] + (vf[j] - v[j]) * sigm(v0[j] + ov[j]);
+    }
+    sv[0][cg] = w;
+    sv[1][cg] = kmod;
+    sv[2][cg] = -kk;
+    sv[3][cg] = kk * a;
+    sv[4][cg] = r;
+    sv[5][cg] = vmod;
+  }
+  __syncthreads();
+  const f4 wv = sv[0][cg], kv = sv[1][cg], av = sv[2][cg], bb = sv[3][cg], rv = sv[4][cg];
+  const float* vrow = reinterpret_cast<const float*>(sv[5]);
+  float sa[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+    sa[m] = fmaf(S[m][3], av[3], fmaf(S[m][2], av[2], fmaf(S[m][1], av[1], S[m][0] * av[0])));
+#pragma unroll
+  for (int m = 0; m < 4; m++) sa[m] = rowsum16(sa[m]);
+  float yo[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const float vv = vrow[rg + 16 * m];
+#pragma unroll
+    for (int q = 0; q < 4; q++) S[m][q] = fmaf(vv, kv[q], fmaf(sa[m], bb[q], S[m][q] * wv[q]));
+    yo[m] = fmaf(S[m][3], rv[3], fmaf(S[m][2], rv[2], fmaf(S[m][1], rv[1], S[m][0] * rv[0])));
+  }
+#pragma unroll
+  for (int m = 0; m < 4; m++) yo[m] = rowsum16(yo[m]);
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+    __builtin_nontemporal_store(S[m], reinterpret_cast<f4*>(st + (size_t)(rg + 16 * m) * N + cg * 4));
+  if (cg < 4) {
+    float o = yo[0];
+#pragma unroll
+    for (int m = 1; m < 4; m++)
+      if (cg == m) o = yo[m];
+    sy[rg + 16 * cg] = o;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    const f4 y = ld4(&sy[4 * cg]);
+    const float mean = rowsum16(hsum4(y)) * (1.0f / N);
+    const f4 d = y - mean;
+    const float var = rowsum16(hsum4(d * d)) * (1.0f / N);
+    const float rstd = 1.0f / sqrtf(var + GN_EPS);
+    const float alpha = rowsum16(hsum4(r * kmod * ld4(p.r_k + c)));
+    const f4 ygn = d * rstd * ld4(p.ln_w + c) + ld4(p.ln_b + c);
+    st4(p.tg + e, (ygn + alpha * vmod) * ld4(p.g + e));
+  }
+}
+
 // ------------------------------------------------------------ backward ----
 // Grid (H, token blocks); 16 groups x 16 lanes; group handles tokens
 // blk*TB + grp + 16 i of head blockIdx.x.
@@ -335,6 +433,11 @@ hipError_t tm_launch_pre_fwd(const TmFwd& p, hipStream_t st) {
 hipError_t tm_launch_post_fwd(const TmFwd& p, hipStream_t st) {
   const size_t groups = (size_t)p.BT * (p.C / WKV7_N);
   hipLaunchKernelGGL(tmk::post_fwd, dim3((unsigned)((groups + 15) / 16)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+hipError_t tm_launch_step_fused(const TmFwd& p, float* state, hipStream_t st) {
+  hipLaunchKernelGGL(tmk::step_fused, dim3((unsigned)((size_t)p.BT * (p.C / WKV7_N))), dim3(256), 0, st,
+                     p, state);
   return hipGetLastError();
 }
 int tm_num_token_blocks(int BT) { return (BT + TB - 1) / TB; }

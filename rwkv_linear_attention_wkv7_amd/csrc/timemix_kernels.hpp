@@ -43,6 +43,9 @@ struct VecOut {
 hipError_t tm_launch_shift_fwd(const TmFwd& p, hipStream_t st);
 hipError_t tm_launch_pre_fwd(const TmFwd& p, hipStream_t st);
 hipError_t tm_launch_post_fwd(const TmFwd& p, hipStream_t st);
+// T = 1 (p.BT streams): pre-WKV, the WKV7 step on state [BT][H][N][N] in
+// place, post-WKV; writes p.tg (and p.v_first on layer 0) only
+hipError_t tm_launch_step_fused(const TmFwd& p, float* state, hipStream_t st);
 int tm_num_token_blocks(int BT);
 hipError_t tm_launch_post_bwd(const TmBwd& p, hipStream_t st);
 hipError_t tm_launch_pre_bwd(const TmBwd& p, hipStream_t st);
