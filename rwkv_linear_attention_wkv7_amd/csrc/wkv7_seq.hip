@@ -590,9 +590,17 @@ __global__ __launch_bounds__(256) void reduce_bwd_partials(size_t plane4, int Tn
 // slices (more slices would double the partial traffic and add passes).
 int bwd_nsplit(int B, int H) { return (long)B * H * 4 <= 256 ? 4 : 2; }
 
-// Forward rows per thread: 16-row workgroups (RPT = 1, four per head) while
-// B*H*4 <= 512 workgroups (at most two per CU), else 32-row ones.
-int fwd_rpt(int B, int H) { return (long)B * H * 4 <= 512 ? 1 : 2; }
+// Forward rows per thread: 16-row workgroups (RPT = 1, four per head) when
+// they fit one workgroup per CU, or fill whole rounds of the 256 CUs (up to
+// two per CU); else 32-row ones.  A part-filled second round leaves the CUs
+// that hold two 16-row workgroups to set the time: measured on MI355X, fp32,
+// B=8 T=1024 H=12 (384 or 192 workgroups) 215 us at 16 rows, 193 at 32;
+// B=4 T=2048 H=16 (256 / 128) 310 vs 371; bf16 B=4 T=8192 H=32 (512 / 256)
+// 1509 vs 1550.
+int fwd_rpt(int B, int H) {
+  const long wg = (long)B * H * 4;
+  return wg <= 256 || (wg <= 512 && wg % 256 == 0) ? 1 : 2;
+}
 
 }  // namespace wkv7k
 
