@@ -961,8 +961,12 @@ namespace {
 
 struct DecodeBufs {
   float *x, *h, *vf, *sh, *ka;
+  float* part;  // split-K partials of the channel-mix value product
   TmCache tm;
 };
+// Slices of the channel-mix value product (K = F) in decode: every layer but
+// the last leaves them for the next layer's LN1 to add to the residual.
+constexpr int DECODE_CM_SPLIT = 4;
 
 int check_cfg(const rwkv7_config* c, int B) {
   if (!c) return fail(WKV7_EINVAL, "config is NULL");
@@ -989,6 +993,7 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
   d.vf = c.take(BC);
   d.sh = c.take(BC);
   d.ka = c.take((size_t)B * cfg->F);
+  d.part = c.take((size_t)DECODE_CM_SPLIT * BC);
   tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, 1};
   carve_cache(c, &s, B, 1, d.tm, false);
 }
@@ -1035,17 +1040,20 @@ int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int
   logits += (size_t)b0 * V;
   HIPCHK(stk_launch_emb_gather(nb, C, V, tokens, M->emb, d.x, st), "embedding");
   if (cfg->use_ln0) HIPCHK(stk_launch_layernorm(nb, C, d.x, M->ln0_w, M->ln0_b, d.x, nullptr, nullptr, st), "ln0");
+  int pend = 0;  // split-K partials of the previous layer's channel-mix value product
   for (int l = 0; l < L; l++) {
     const rwkv7_block& bl = M->blocks[l];
     tm_shape s = {C, H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, l};
     float* axp = att_x_prev + (size_t)l * BC + (size_t)b0 * C;
     float* ast = att_state + ((size_t)l * B + b0) * H * NN;
     float* fxp = ffn_x_prev + (size_t)l * BC + (size_t)b0 * C;
-    {  // LN1 fused with the six time-mix lerps; att_x_prev <- this token's LN1 output
+    {  // (residual add,) LN1 fused with the six time-mix lerps; att_x_prev <- this token's LN1 output
       LnMix lm{nb, C, 6, d.x, bl.ln1_w, bl.ln1_b, axp, axp,
                {bl.tm.mu_r, bl.tm.mu_w, bl.tm.mu_k, bl.tm.mu_v, bl.tm.mu_a, bl.tm.mu_g},
-               {d.tm.xr, d.tm.xw, d.tm.xk, d.tm.xv, d.tm.xa, d.tm.xg}};
+               {d.tm.xr, d.tm.xw, d.tm.xk, d.tm.xv, d.tm.xa, d.tm.xg},
+               d.part, pend, d.x};
       HIPCHK(stk_launch_ln_mix(lm, st), "ln1 + shift");
+      pend = 0;
     }
     CHK(tm_forward_impl(&s, &bl.tm, nb, 1, nullptr, nullptr, d.vf, ast, ast, d.x, nullptr, d.tm, st,
                         true, 1.f, prec, true));
@@ -1054,7 +1062,11 @@ int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int
       HIPCHK(stk_launch_ln_mix(lm, st), "ln2 + shift");
     }
     HIPCHK(gemm_run(prec, false, false, nb, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(gemm_run(prec, false, false, nb, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
+    if (l + 1 < L)  // the next layer's LN1 adds the slices to the residual
+      HIPCHK(gemm_run_partials(prec, nb, C, F, d.ka, F, bl.cm_Wv, C, DECODE_CM_SPLIT, d.part, &pend, st),
+             "cm value");
+    else
+      HIPCHK(gemm_run(prec, false, false, nb, C, F, d.ka, F, bl.cm_Wv, C, d.x, C, 1.f, 0, nullptr, 1, nullptr, st), "cm value");
   }
   HIPCHK(stk_launch_layernorm(nb, C, d.x, M->ln_out_w, M->ln_out_b, d.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, nb, V, C, d.h, C, M->head, V, logits, V, 0.f, 0, nullptr, 1, nullptr, st), "head");

@@ -1002,6 +1002,22 @@ int gemm_splitk_slices(int prec, int M, int N, int K) {
   return want < 1 ? 1 : (int)want;
 }
 
+hipError_t gemm_run_partials(int prec, int M, int N, int K, const float* A, int lda,
+                             const float* B, int ldb, int split, float* part, int* slices,
+                             hipStream_t st) {
+  using namespace gemmk;
+  split = std::max(1, std::min(split, gemm_splitk_slices(prec, M, N, K)));
+  int kslice = (K + split - 1) / split;
+  kslice = (kslice + 63) / 64 * 64;
+  const int S = (K + kslice - 1) / kslice;
+  *slices = S;
+  if (M <= 0 || N <= 0) return hipSuccess;
+  GemmBatch b;
+  b.count = 1;
+  b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, part, N, 0.f, EPI_NONE, nullptr, part};
+  return dispatch(prec, false, false, b, S, kslice, kslice, st);
+}
+
 // C = epi(op(A) op(B) + beta C).  ws (may be NULL when split == 1) holds
 // split*M*N floats of split-K partials.
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,

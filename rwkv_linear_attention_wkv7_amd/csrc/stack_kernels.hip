@@ -97,7 +97,9 @@ __global__ __launch_bounds__(256) void cm_shift(int BT, int T, int C, const floa
 }
 
 // One token per stream (T = 1): LayerNorm of each row fused with the token
-// shift lerps that consume it.  h = LN(x); out_m = h + (prev - h) mu_m for
+// shift lerps that consume it (and, optionally, with the residual add of a
+// split-K product before it: x += sum of its partials, written back).
+// h = LN(x); out_m = h + (prev - h) mu_m for
 // each mix m, prev = the previous token's LN output (x_prev, or 0); x_last
 // receives h (it may be x_prev: each lane reads its prev before writing).
 // One wave per row, the row in registers as in layernorm_fwd.
@@ -114,8 +116,23 @@ __global__ __launch_bounds__(256) void ln_mix(LnMix p) {
   for (int j = 0; j < MAXC4; j++) {
     const int c4 = lane + 64 * j;
     v[j] = c4 < C4 ? xr[c4] : f4{0.f, 0.f, 0.f, 0.f};
-    s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
   }
+  if (p.nparts > 0) {  // x + (sum of the partials in slice order)
+    const size_t plane = (size_t)p.R * C;
+#pragma unroll
+    for (int j = 0; j < MAXC4; j++) {
+      const int c4 = lane + 64 * j;
+      if (c4 < C4) {
+        const f4* pr = reinterpret_cast<const f4*>(p.part + (size_t)row * C) + c4;
+        f4 ps = pr[0];
+        for (int z = 1; z < p.nparts; z++) ps += pr[z * plane / 4];
+        v[j] = ps + v[j];
+        reinterpret_cast<f4*>(p.x_sum + (size_t)row * C)[c4] = v[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXC4; j++) s += (v[j][0] + v[j][1]) + (v[j][2] + v[j][3]);
   const float mean = wavesum(s) / C;
   float q = 0.f;
 #pragma unroll

@@ -17,6 +17,12 @@ struct LnMix {
   float* x_last;        // receives this token's LN output (may equal x_prev)
   const float* mu[6];
   float* out[6];
+  // optional split-K partials of a product to add to x first: x_sum = x +
+  // (part[0] + ... + part[nparts-1]) ([nparts][R][C]), written to x_sum
+  // (which may be x) and normalised in place of x
+  const float* part;
+  int nparts;
+  float* x_sum;
 };
 hipError_t stk_launch_ln_mix(const LnMix& p, hipStream_t st);
 int stk_max_layernorm_width();
