@@ -563,11 +563,13 @@ void tm_weight_spans(Spans& sp, const tm_shape* s, const WT* W, bool written) {
 
 // decode: T == 1 with the WKV state updated in place (s0 == sT, no checkpoint),
 // run by one fused kernel (pre-WKV, the step on the state in place, post-WKV).
-// out = out_beta * out + tg Wo.
+// out = out_beta * out + tg Wo (out_proj = false: tg is left in m.tg and the
+// caller applies Wo).
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
-                    float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false) {
+                    float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false,
+                    bool out_proj = true) {
   const int BT = B * T, C = s->C;
   if (s->layer_id > 0 && (!m.lv || !m.ov))
     return fail(WKV7_EHIP, "internal: activation set without value-residual buffers for layer %d",
@@ -631,7 +633,8 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
                                m.ckpt, m.wkv_ws, st), "wkv7 forward");
     HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
   }
-  HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
+  if (out_proj)
+    HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;
 }
 
@@ -966,7 +969,9 @@ struct DecodeBufs {
 };
 // Slices of the channel-mix value product (K = F) in decode: every layer but
 // the last leaves them for the next layer's LN1 to add to the residual.
+// The output projection (K = C) leaves its slices for LN2 the same way.
 constexpr int DECODE_CM_SPLIT = 4;
+constexpr int DECODE_O_SPLIT = 2;
 
 int check_cfg(const rwkv7_config* c, int B) {
   if (!c) return fail(WKV7_EINVAL, "config is NULL");
@@ -993,7 +998,7 @@ void carve_decode(Carver& c, const rwkv7_config* cfg, int B, DecodeBufs& d) {
   d.vf = c.take(BC);
   d.sh = c.take(BC);
   d.ka = c.take((size_t)B * cfg->F);
-  d.part = c.take((size_t)DECODE_CM_SPLIT * BC);
+  d.part = c.take((size_t)std::max(DECODE_CM_SPLIT, DECODE_O_SPLIT) * BC);
   tm_shape s = {cfg->C, cfg->H, cfg->N, cfg->Dw, cfg->Da, cfg->Dv, cfg->Dg, 1};
   carve_cache(c, &s, B, 1, d.tm, false);
 }
@@ -1056,10 +1061,14 @@ int decode_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int b0, int
       pend = 0;
     }
     CHK(tm_forward_impl(&s, &bl.tm, nb, 1, nullptr, nullptr, d.vf, ast, ast, d.x, nullptr, d.tm, st,
-                        true, 1.f, prec, true));
-    {  // LN2 fused with the channel-mix lerp; ffn_x_prev <- this token's LN2 output
-      LnMix lm{nb, C, 1, d.x, bl.ln2_w, bl.ln2_b, fxp, fxp, {bl.cm_mu_k}, {d.sh}};
+                        true, 1.f, prec, true, false));
+    // output projection as split-K partials, added to the residual by LN2
+    HIPCHK(gemm_run_partials(prec, nb, C, C, d.tm.tg, C, bl.tm.Wo, C, DECODE_O_SPLIT, d.part, &pend, st),
+           "o proj");
+    {  // residual add, LN2 fused with the channel-mix lerp; ffn_x_prev <- this token's LN2 output
+      LnMix lm{nb, C, 1, d.x, bl.ln2_w, bl.ln2_b, fxp, fxp, {bl.cm_mu_k}, {d.sh}, d.part, pend, d.x};
       HIPCHK(stk_launch_ln_mix(lm, st), "ln2 + shift");
+      pend = 0;
     }
     HIPCHK(gemm_run(prec, false, false, nb, F, C, d.sh, C, bl.cm_Wk, F, d.ka, F, 0.f, 5, nullptr, 1, nullptr, st), "cm key");
     if (l + 1 < L)  // the next layer's LN1 adds the slices to the residual

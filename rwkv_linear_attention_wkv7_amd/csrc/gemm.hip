@@ -1006,7 +1006,7 @@ hipError_t gemm_run_partials(int prec, int M, int N, int K, const float* A, int 
                              const float* B, int ldb, int split, float* part, int* slices,
                              hipStream_t st) {
   using namespace gemmk;
-  split = std::max(1, std::min(split, gemm_splitk_slices(prec, M, N, K)));
+  split = std::max(1, std::min(split, K / 64));
   int kslice = (K + split - 1) / split;
   kslice = (kslice + 63) / 64 * 64;
   const int S = (K + kslice - 1) / kslice;

@@ -43,9 +43,9 @@ int gemm_splitk_slices(int prec, int M, int N, int K);
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
                     int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
                     const float* aux, int split, float* ws, hipStream_t st);
-// The split-K products alone: part[s][M][N] (leading dimension N) for the
-// *slices slices gemm_run would form with this split, left for the consumer
-// to add in slice order (no beta, no epilogue).
+// The split-K products alone: part[s][M][N] (leading dimension N), K cut
+// into *slices <= split slices of a multiple of 64 (at least 64 each), left
+// for the consumer to add in slice order (no beta, no epilogue).
 hipError_t gemm_run_partials(int prec, int M, int N, int K, const float* A, int lda,
                              const float* B, int ldb, int split, float* part, int* slices,
                              hipStream_t st);
