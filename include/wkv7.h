@@ -117,8 +117,8 @@ int wkv7_forward(int B, int T, int H, int N, int dtype,
 
 /* Workspace bytes wkv7_backward needs: one fp32 region shared by its two
  * paths (the two-pass path's dsa per token, state gradient every L tokens and
- * per-column sums; or the single-pass path's column partials and segment
- * hand-over), a flag, plus, when have_ckpt is 0, the checkpoints
+ * per-column sums; or the single-pass path's column partials), a flag, plus,
+ * when have_ckpt is 0, the checkpoints
  * (recomputed by the token-sequential forward). */
 size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
 
@@ -143,12 +143,8 @@ size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
  * dr,dw,dk,dv,da,db: [B][T][H][N] `dtype` (written).  ds0: fp32 or NULL.
  * ws: at least wkv7_backward_workspace_bytes() bytes (16-byte aligned;
  * contents undefined before and after).
- * side: NULL, or a wkv7_side; with one, when the single-pass kernel runs,
- * from T = 1024 on its reverse pass runs as 2-4 launches over consecutive
- * token segments of at least 512 tokens (last first, the state gradient
- * handed over through the workspace), and each segment's reduction of the
- * column partials runs on the side stream, overlapping the next segment's
- * pass.
+ * side: NULL or a wkv7_side (checked, not used: every launch of this call
+ * runs on `stream`).
  */
 int wkv7_backward(int B, int T, int H, int N, int dtype,
                   const void *r, const void *w, const void *k, const void *v,
@@ -262,8 +258,7 @@ int timemix_forward(const tm_shape *s, const tm_weights *W, int B, int T,
  * dx: [B][T][C]; dx_prev: [B][C] or NULL; dv_first_in: layer 0 only, [B][T][C]
  * or NULL; dv_first_out: layer > 0 only, [B][T][C] or NULL; ds0: fp32 or NULL.
  * side: NULL, or a wkv7_side on which the weight gradients (the X^T dY
- * products) run, overlapping the input-gradient chain on `stream` (and the
- * segmented WKV7 reverse pass as in wkv7_backward).
+ * products) run, overlapping the input-gradient chain on `stream`.
  */
 int timemix_backward(const tm_shape *s, const tm_weights *W, int B, int T,
                      const float *x, const float *x_prev, const float *v_first,

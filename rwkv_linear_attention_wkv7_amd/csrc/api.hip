@@ -224,11 +224,10 @@ extern "C" int wkv7_forward(int B, int T, int H, int N, int dtype, const void* r
 namespace {
 // fp32 floats of the region both backward paths share (only one of them
 // produces results): the two-pass path's dsa and boundary state gradients,
-// or the single-pass path's column partials and segment hand-over buffers.
+// or the single-pass path's column partials.
 size_t wkv7_bwd_region_floats(int B, int T, int H) {
   Carver one(nullptr), two(nullptr);
   one.take(wkv7_bwd_partial_floats(B, T, H));
-  one.take((size_t)2 * B * H * WKV7_N * WKV7_N);  // state-gradient hand-over between segments
   two.take(wkv7_bwd2_ws_floats(B, T, H));
   return (std::max(one.off, two.off) + sizeof(float) - 1) / sizeof(float);
 }
@@ -316,17 +315,7 @@ int wkv7_backward_run(int B, int T, int H, int dtype, const void* r, const void*
                                db, ds0, region, gate, stream),
          "wkv7_backward launch");
   float* part = region;
-  float* gbuf = region + ((wkv7_bwd_partial_floats(B, T, H) + 63) & ~(size_t)63);
-  if (sd && wkv7_bwd_segments(T) > 1) {
-    // long sequence: the reverse pass runs in segments, each segment's
-    // partial reduction on the side stream overlapping the next segment's
-    // pass; without a side stream, one pass
-    HIPCHK(wkv7_launch_backward_segmented(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk,
-                                          dv, da, db, ds0, part, gbuf, gate, stream, sd->stream,
-                                          sd->ev[1], sd->ev[3]),
-           "wkv7_backward launch");
-    return WKV7_OK;
-  }
+  (void)sd;  // every launch of this call runs on `stream`
   HIPCHK(wkv7_launch_backward(dtype, B, T, H, r, w, k, v, a, b, dy, ck, dsT, dr, dw, dk, dv, da,
                               db, ds0, part, gate, stream),
          "wkv7_backward launch");

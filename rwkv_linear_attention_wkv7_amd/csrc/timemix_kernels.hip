@@ -168,11 +168,16 @@ __global__ __launch_bounds__(256) void step_fused(TmFwd p, float* __restrict__ s
 
   const int c = h * N + cg * 4;
   const size_t e = (size_t)bt * p.C + c;
-  f4 r, kmod, vmod;
+  f4 r, kmod, vmod, rk, lnw, lnb, gg;
   if (tid < 16) {
     const f4 k = ld4(p.k + e), v = ld4(p.v + e), ow = ld4(p.ow + e), oa = ld4(p.oa + e);
     const f4 w0 = ld4(p.w0 + c), a0 = ld4(p.a0 + c), kkw = ld4(p.k_k + c), ka = ld4(p.k_a + c);
     r = ld4(p.r + e);
+    // the post-WKV inputs too, so no load waits after the state update
+    rk = ld4(p.r_k + c);
+    lnw = ld4(p.ln_w + c);
+    lnb = ld4(p.ln_b + c);
+    gg = ld4(p.g + e);
     f4 w, a, tk;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -236,9 +241,9 @@ __global__ __launch_bounds__(256) void step_fused(TmFwd p, float* __restrict__ s
     const f4 d = y - mean;
     const float var = rowsum16(hsum4(d * d)) * (1.0f / N);
     const float rstd = 1.0f / sqrtf(var + GN_EPS);
-    const float alpha = rowsum16(hsum4(r * kmod * ld4(p.r_k + c)));
-    const f4 ygn = d * rstd * ld4(p.ln_w + c) + ld4(p.ln_b + c);
-    st4(p.tg + e, (ygn + alpha * vmod) * ld4(p.g + e));
+    const float alpha = rowsum16(hsum4(r * kmod * rk));
+    const f4 ygn = d * rstd * lnw + lnb;
+    st4(p.tg + e, (ygn + alpha * vmod) * gg);
   }
 }
 

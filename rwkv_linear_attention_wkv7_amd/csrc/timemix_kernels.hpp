@@ -68,19 +68,6 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                 void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
                                 float* part, const int* gate, hipStream_t st);
 size_t wkv7_bwd_partial_floats(int B, int T, int H);
-// Long sequences: the reverse pass in wkv7_bwd_segments(T) launches (last
-// segment first, the state gradient handed over through gbuf, 2 x B*H*N*N
-// floats), each segment's partial reduction on `side` (after `ready` is
-// recorded on st) overlapping the next segment's pass; `done` joins side back.
-int wkv7_bwd_segments(int T);
-hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const void* r,
-                                          const void* w, const void* k, const void* v,
-                                          const void* a, const void* b, const void* dy,
-                                          const float* ckpt, const float* dsT, void* dr, void* dw,
-                                          void* dk, void* dv, void* da, void* db, float* ds0,
-                                          float* part, float* gbuf, const int* gate,
-                                          hipStream_t st, hipStream_t side, hipEvent_t ready,
-                                          hipEvent_t done);
 // wkv7_bwd.hip: the two-pass backward (reverse scan of the state gradient,
 // then per-chunk matrix-core products).  ckpt holds the forward's states and
 // per-token sa (wkv7_ckpt_sa).  ws: wkv7_bwd2_ws_floats() fp32.  gate: NULL

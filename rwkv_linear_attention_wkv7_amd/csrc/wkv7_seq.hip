@@ -710,39 +710,4 @@ hipError_t wkv7_launch_backward(int dtype, int B, int T, int H, const void* r, c
                                          da, db, ds0, part, 0, nck, st, st, nullptr, gate);
 }
 
-int wkv7_bwd_segments(int T) {
-  // segments of at least 512 tokens, at most 4
-  const int s = T / 512;
-  return s < 2 ? 1 : (s > 4 ? 4 : s);
-}
-
-hipError_t wkv7_launch_backward_segmented(int dtype, int B, int T, int H, const void* r,
-                                          const void* w, const void* k, const void* v,
-                                          const void* a, const void* b, const void* dy,
-                                          const float* ckpt, const float* dsT, void* dr, void* dw,
-                                          void* dk, void* dv, void* da, void* db, float* ds0,
-                                          float* part, float* gbuf, const int* gate,
-                                          hipStream_t st, hipStream_t side, hipEvent_t ready,
-                                          hipEvent_t done) {
-  const int nck = (T + wkv7k::CKL - 1) / wkv7k::CKL, nseg = wkv7_bwd_segments(T);
-  const size_t gsz = (size_t)B * H * WKV7_N * WKV7_N;
-  hipError_t e = hipSuccess;
-  // segments last to first; G is handed over through gbuf (ping-pong)
-  for (int sgi = nseg - 1; sgi >= 0 && e == hipSuccess; sgi--) {
-    const int c_lo = (int)((long)nck * sgi / nseg), c_hi = (int)((long)nck * (sgi + 1) / nseg);
-    const float* gin = sgi == nseg - 1 ? dsT : gbuf + (size_t)(sgi & 1) * gsz;
-    float* gout = sgi == 0 ? ds0 : gbuf + (size_t)((sgi + 1) & 1) * gsz;
-    if (dtype == 1)
-      e = wkv7k::launch_backward_t<bf16_t>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
-                                           da, db, gout, part, c_lo, c_hi, st, side, ready, gate);
-    else
-      e = wkv7k::launch_backward_t<float>(B, T, H, r, w, k, v, a, b, dy, ckpt, gin, dr, dw, dk, dv,
-                                          da, db, gout, part, c_lo, c_hi, st, side, ready, gate);
-  }
-  // join the reductions back, whatever happened
-  hipError_t ej = hipEventRecord(done, side);
-  if (ej == hipSuccess) ej = hipStreamWaitEvent(st, done, 0);
-  return e != hipSuccess ? e : ej;
-}
-
 int wkv7_ckpt_interval_const() { return wkv7k::CKL; }

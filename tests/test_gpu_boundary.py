@@ -33,8 +33,8 @@ def test_wkv7_forward_in_place_state(hip):
 
 
 def test_wkv7_backward_side_stream_bitwise(hip):
-    """T = 4200 runs segmented with the side stream and in one pass without:
-    the same chunk arithmetic in the same order, so the same bits."""
+    """T = 4200 with and without a side stream (accepted, every launch on the
+    caller's stream): the same bits."""
     d = synth.wkv7_inputs(1, 4200, 2, 64, seed=32, with_state=True)
     ins = [_dev(d[n]) for n in NAMES]
     s0, dsT, dy = _dev(d["s0"]), _dev(d["dsT"]), _dev(d["dy"])

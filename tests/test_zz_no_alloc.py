@@ -46,8 +46,7 @@ def test_backward_noalloc_two_calls(hip):
         assert_close(n, got[n].cpu().numpy(), gr[n], 1e-3)
 
 
-def test_backward_noalloc_bf16_and_segmented(hip):
-    """bf16 tensors, and T = 2100 with the side stream (segmented reverse
-    pass, reductions on the side stream) from the same scratch."""
+def test_backward_noalloc_bf16_and_long(hip):
+    """bf16 tensors, and T = 2100, from the same scratch."""
     _case(hip, 1, 2100, 2, seed=43, with_ckpt=True, dtype=torch.float32)
     _case(hip, 2, 77, 2, seed=44, with_ckpt=False, dtype=torch.bfloat16)
