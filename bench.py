@@ -144,9 +144,10 @@ def setup_wkv7_small():
         binding.wkv7_backward(*ins, dy, ckpt=ck, want_ds0=False)
 
     flops = 26.0 * N * N * B * T * H
-    roof = dict(kernel="wkv7 backward call (B=1 T=64 H=4: 16 workgroups, latency bound)",
+    roof = dict(kernel="wkv7 backward call (B=1 T=64 H=4: the single-pass reverse kernel and its "
+                       "column reduction, 16 workgroups, latency bound)",
                 bound="alu", work=flops, unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom,
-                key="wkv7_bwd_small", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_bwd.hip"])
+                key="wkv7_bwd_small", src=["rwkv_linear_attention_wkv7_amd/csrc/wkv7_seq.hip"])
 
     def cpu():
         from oracle import wkv7 as ow

@@ -130,13 +130,14 @@ size_t wkv7_backward_workspace_bytes(int B, int T, int H, int N, int have_ckpt);
  *     da_t = S_{t-1}^T dsa;  G = G diag(w_t) + dsa a_t^T ).
  * Same pages as wkv7_forward; the model.rs block gives these local terms.
  *
- * Computed in two passes when every decay lies in [1/8, 1]: a reverse scan
- * of G alone (it never reads S), then per-chunk matrix-core products that
- * give the column sums from the checkpoints, the forward's sa and the scan's
+ * Computed in two passes when every decay lies in [1/8, 1] and the call
+ * spans more than 512 (b, h, L-token chunk) triples: a reverse scan of G
+ * alone (it never reads S), then per-chunk matrix-core products that give
+ * the column sums from the checkpoints, the forward's sa and the scan's
  * boundary gradients; dw from a running sum of r dr - b db - k dk + a da.
- * Otherwise (the scan finds a decay outside that range) the single-pass
- * kernel runs the step above token by token from the checkpoints; both agree
- * with the recurrence to fp32 rounding.
+ * Otherwise (a smaller call, or the scan finds a decay outside that range)
+ * the single-pass kernel runs the step above token by token from the
+ * checkpoints; both agree with the recurrence to fp32 rounding.
  *
  * ckpt: the forward's checkpoints, or NULL (then they are recomputed into the
  * workspace).  dy: [B][T][H][N] `dtype`.  dsT, s0: fp32 [B][H][N][N] or NULL.

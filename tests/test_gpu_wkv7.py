@@ -60,6 +60,7 @@ def _check(d, y, sT, g, with_state, ftol, gtol, sel=None):
     (3, 16, 1, False),     # exactly one checkpoint chunk
     (2, 130, 2, True),     # many chunks, ragged
     (6, 40, 24, True),     # 144 heads: 32-row forward workgroups, two backward slices
+    (4, 130, 16, True),    # 576 (b, h, chunk) triples: the two-pass backward
 ])
 @pytest.mark.parametrize("chunked", [True, False])
 def test_wkv7_fp32_parity(hip, B, T, H, with_state, chunked):
@@ -72,18 +73,22 @@ def test_wkv7_fp32_parity(hip, B, T, H, with_state, chunked):
     _check(d, y, sT, g, with_state, 1e-4, 1e-3)
 
 
-def test_wkv7_extreme_decay(hip):
+@pytest.mark.parametrize("B,H", [(2, 2), (4, 24)])
+def test_wkv7_extreme_decay(hip, B, H):
     """Decays far outside the time-mix range: chunks whose cumulative decay
     leaves the matrix-core path's exponent window (w = 1e-3 over a chunk, an
     exact w = 0) run token by token, others (w = 1: no decay at all) stay on
-    the chunk path; forward and gradients against the oracle, fp32."""
-    d = synth.wkv7_inputs(2, 100, 2, 64, seed=21, with_state=True)
+    the chunk path; forward and gradients against the oracle, fp32.  The
+    backward of B=2 H=2 (28 chunk triples) runs the single-pass kernels
+    directly; that of B=4 H=24 (672) starts the two-pass path, whose scan
+    finds the decays outside [1/8, 1] and hands the call to them."""
+    d = synth.wkv7_inputs(B, 100, H, 64, seed=21, with_state=True)
     w = d["w"].copy()
     w[:, 16:32] = 1e-3
     w[0, 40, 1, 5] = 0.0
     w[:, 64:80] = 1.0
     d["w"] = w
-    print("[wkv7 extreme decay] B=2 T=100 H=2", flush=True)
+    print(f"[wkv7 extreme decay] B={B} T=100 H={H}", flush=True)
     y, sT, g = _run(hip, d, torch.float32, True)
     _check(d, y, sT, g, True, 1e-4, 1e-3)
 
@@ -93,11 +98,12 @@ def test_wkv7_strong_decay_two_pass(hip, lo):
     """Decays spread over [lo, 1] (log-uniform), inside the range the two-pass
     backward serves (the decay of a 16-token chunk reaches 0.125^16, so its
     e^{+-g} factors span about e^{+-33}); ragged T, nonzero s0 and dsT; fp32
-    forward and gradients against the oracle."""
-    d = synth.wkv7_inputs(2, 150, 3, 64, seed=41, with_state=True)
+    forward and gradients against the oracle.  B=4 H=16 T=150: 640 (b, h,
+    chunk) triples, above the size the single-pass kernels take directly."""
+    d = synth.wkv7_inputs(4, 150, 16, 64, seed=41, with_state=True)
     g = np.random.default_rng(41)
     d["w"] = np.exp(np.log(lo) * g.random(d["w"].shape)).astype(np.float32)
-    print(f"[wkv7 strong decay] B=2 T=150 H=3 w in [{lo}, 1]", flush=True)
+    print(f"[wkv7 strong decay] B=4 T=150 H=16 w in [{lo}, 1]", flush=True)
     y, sT, gr = _run(hip, d, torch.float32, True, False)
     _check(d, y, sT, gr, True, 1e-4, 1e-3)
 
