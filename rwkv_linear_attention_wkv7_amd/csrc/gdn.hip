@@ -240,31 +240,68 @@ struct Stage {
   float b[2][TT];
 };
 
+// The staging in two halves, so that a block's inputs can be fetched
+// into registers while the block before it runs: load_stage issues every
+// global load of the block (from clamped, always valid token indices, so all
+// are in flight together), store_stage writes them (zeros, or the identity
+// token past the end) to LDS buffer buf.
 template <int DK>
-__device__ __forceinline__ void stage_block(Stage<DK>& st, int buf, int t0, int T, int nv, int dv,
-                                            int cdim, int kvoff, size_t bT, int h, int ko,
-                                            int col0, const float* qh, const float* kh,
-                                            const float* cq, const float* gg, const float* be,
-                                            const float* dob, bool with_do, int nk) {
-  // k^, q^: TT * DK floats each, float4 per thread slot
+struct StageRegs {
+  static constexpr int NKQ = 2 * TT * DK / 4 / 256;  // float4 slots of k^, q^ per thread
+  f4 kq[NKQ];
+  float v, d, g, b;
+};
+
+template <int DK>
+__device__ __forceinline__ void load_stage(StageRegs<DK>& o, int t0, int T, int nv, int dv,
+                                           int cdim, int kvoff, size_t bT, int h, int ko,
+                                           int col0, const float* qh, const float* kh,
+                                           const float* cq, const float* gg, const float* be,
+                                           const float* dob, bool with_do, int nk) {
+  constexpr int NQ4 = TT * DK / 4;
+  static_assert(2 * NQ4 % 256 == 0 && TT * CB == 256, "staging assumes 256 threads");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < StageRegs<DK>::NKQ; q++) {
+    const int f = tid + 256 * q;
+    const int which = f / NQ4, r = f - which * NQ4, tok = r / (DK / 4), c4 = r - tok * (DK / 4);
+    const int t = min(t0 + tok, T - 1);
+    o.kq[q] = ld4((which ? qh : kh) + ((bT + t) * nk + ko) * DK + c4 * 4);
+  }
+  {
+    const int tok = tid / CB, c = tid - tok * CB, t = min(t0 + tok, T - 1);
+    o.v = cq[(bT + t) * cdim + kvoff + (size_t)h * dv + col0 + c];
+    o.d = with_do ? dob[((bT + t) * nv + h) * dv + col0 + c] : 0.f;
+  }
+  {
+    const int t = min(t0 + (tid & (TT - 1)), T - 1);
+    o.g = gg[(bT + t) * nv + h];
+    o.b = be[(bT + t) * nv + h];
+  }
+}
+
+template <int DK>
+__device__ __forceinline__ void store_stage(Stage<DK>& st, const StageRegs<DK>& o, int buf, int t0,
+                                            int T, bool with_do) {
   constexpr int NQ4 = TT * DK / 4;
   const int tid = threadIdx.x;
-  for (int f = tid; f < 2 * NQ4; f += 256) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < StageRegs<DK>::NKQ; q++) {
+    const int f = tid + 256 * q;
     const int which = f / NQ4, r = f - which * NQ4, tok = r / (DK / 4), c4 = r - tok * (DK / 4);
-    const int t = t0 + tok;
-    f4 x = {0.f, 0.f, 0.f, 0.f};
-    if (t < T) x = ld4((which ? qh : kh) + ((bT + t) * nk + ko) * DK + c4 * 4);
-    st4(which ? &st.q[buf][tok][c4 * 4] : &st.k[buf][tok][c4 * 4], x);
+    st4(which ? &st.q[buf][tok][c4 * 4] : &st.k[buf][tok][c4 * 4], t0 + tok < T ? o.kq[q] : z);
   }
-  for (int f = tid; f < TT * CB; f += 256) {
-    const int tok = f / CB, c = f - tok * CB, t = t0 + tok;
-    st.v[buf][tok][c] = t < T ? cq[(bT + t) * cdim + kvoff + (size_t)h * dv + col0 + c] : 0.f;
-    if (with_do) st.d[buf][tok][c] = t < T ? dob[((bT + t) * nv + h) * dv + col0 + c] : 0.f;
+  {
+    const int tok = tid / CB, c = tid - tok * CB;
+    const bool ok = t0 + tok < T;
+    st.v[buf][tok][c] = ok ? o.v : 0.f;
+    if (with_do) st.d[buf][tok][c] = ok ? o.d : 0.f;
   }
   if (tid < TT) {
-    const int t = t0 + tid;
-    st.g[buf][tid] = t < T ? gg[(bT + t) * nv + h] : 1.f;
-    st.b[buf][tid] = t < T ? be[(bT + t) * nv + h] : 0.f;
+    const bool ok = t0 + tid < T;
+    st.g[buf][tid] = ok ? o.g : 1.f;
+    st.b[buf][tid] = ok ? o.b : 0.f;
   }
 }
 
@@ -290,12 +327,18 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
   float s[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; i++) s[i] = 0.f;
-  stage_block<DK>(st, 0, 0, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be, nullptr,
-                  false, nk);
+  StageRegs<DK> nx;
+  load_stage<DK>(nx, 0, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be, nullptr, false,
+                 nk);
+  store_stage<DK>(st, nx, 0, 0, T, false);
   __syncthreads();
   int buf = 0;
   for (int blk = 0; blk < nblk; blk++, buf ^= 1) {
     const int t0 = blk * TT;
+    const bool more = blk + 1 < nblk;
+    if (more)  // in flight while this block runs
+      load_stage<DK>(nx, t0 + TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be,
+                     nullptr, false, nk);
     if (ckpt) {
       float* cp = ckpt + (((size_t)bh * nblk + blk) * dv + col) * DK + rg * RPL;
 #pragma unroll
@@ -330,12 +373,10 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
       ob = rg == tt ? ov : ob;
     }
     if (t0 + rg < T) o[((bT + t0 + rg) * nv + h) * dv + col] = ob;
-    __syncthreads();  // every wave is done with the other buffer's previous block
-    if (blk + 1 < nblk) {
-      stage_block<DK>(st, buf ^ 1, t0 + TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq,
-                      gg, be, nullptr, false, nk);
-      __syncthreads();
-    }
+    // the other buffer was last read in the block before, behind the
+    // previous barrier
+    if (more) store_stage<DK>(st, nx, buf ^ 1, t0 + TT, T, false);
+    lds_barrier();
   }
 }
 
@@ -371,17 +412,31 @@ __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int
 #pragma unroll
   for (int i = 0; i < RPL; i++) G[i] = 0.f;
   int buf = 0;
-  stage_block<DK>(st, 0, (nblk - 1) * TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg,
-                  be, dob, true, nk);
+  StageRegs<DK> nx;
+  load_stage<DK>(nx, (nblk - 1) * TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be,
+                 dob, true, nk);
+  store_stage<DK>(st, nx, 0, (nblk - 1) * TT, T, true);
+  // this lane's checkpoint rows of the current block, then of the one before
+  auto ck_rows = [&](int blk_, f4 (&o)[RPL / 4]) {
+    const float* cp = ckpt + (((size_t)bh * nblk + blk_) * dv + col) * DK + rg * RPL;
+#pragma unroll
+    for (int i = 0; i < RPL; i += 4) o[i / 4] = ld4(cp + i);
+  };
+  f4 ckc[RPL / 4], ckn[RPL / 4];
+  ck_rows(nblk - 1, ckc);
   __syncthreads();
   for (int blk = nblk - 1; blk >= 0; blk--, buf ^= 1) {
     const int t0 = blk * TT;
+    if (blk > 0) {  // in flight while this block runs
+      load_stage<DK>(nx, t0 - TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be, dob,
+                     true, nk);
+      ck_rows(blk - 1, ckn);
+    }
     // recompute: Sh[tt] = state before token tt, kvh[tt] = S_pre^T k^ (this column)
     float Sh[TT + 1][RPL], kvh[TT];
-    const float* cp = ckpt + (((size_t)bh * nblk + blk) * dv + col) * DK + rg * RPL;
 #pragma unroll
     for (int i = 0; i < RPL; i += 4) {
-      const f4 x = ld4(cp + i);
+      const f4 x = ckc[i / 4];
       Sh[0][i] = x[0]; Sh[0][i + 1] = x[1]; Sh[0][i + 2] = x[2]; Sh[0][i + 3] = x[3];
     }
 #pragma unroll
@@ -474,10 +529,12 @@ __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int
       }
     }
     if (t0 + rg < T) dcq[(bT + t0 + rg) * cdim + kvoff + (size_t)h * dv + col] = dvb;
-    if (blk > 0)
-      stage_block<DK>(st, buf ^ 1, t0 - TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg,
-                      be, dob, true, nk);
-    __syncthreads();  // red consumed; the next block's staging visible
+    if (blk > 0) {
+      store_stage<DK>(st, nx, buf ^ 1, t0 - TT, T, true);
+#pragma unroll
+      for (int i = 0; i < RPL / 4; i++) ckc[i] = ckn[i];
+    }
+    lds_barrier();  // red consumed; the next block's staging visible
   }
 }
 
