@@ -28,7 +28,7 @@ namespace gdnk {
 
 constexpr int TT = 16;   // tokens per staging block = checkpoint interval
 constexpr int CB = 16;   // value columns per workgroup
-constexpr int RF = 4;    // backward: tokens per flush of the cross-column sums
+constexpr int RF = 8;    // backward: tokens per flush of the cross-column sums
 constexpr float L2_EPS = 1e-6f;
 constexpr float SP_CUT = 20.0f;
 
