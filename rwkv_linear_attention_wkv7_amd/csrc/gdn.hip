@@ -98,6 +98,101 @@ __global__ __launch_bounds__(256) void conv_bwd(int BT, int T, int cdim, int kk,
   }
 }
 
+// The same two convolutions for KK taps, a thread sliding over TBK
+// consecutive tokens of one channel quad: its 4 x KK weights are read once,
+// and each input row (forward) or dpre = dcq silu'(pre) (backward) is loaded
+// or formed once for the TBK outputs that use it.  The sums run over the taps
+// in the order above.
+template <int KK, int TBK>
+__global__ __launch_bounds__(256) void conv_fwd_t(int B, int T, int cdim,
+                                                  const float* __restrict__ raw,
+                                                  const float* __restrict__ conv,
+                                                  float* __restrict__ pre, float* __restrict__ cq) {
+  const int C4 = cdim / 4, ntb = (T + TBK - 1) / TBK;
+  const size_t n = (size_t)B * ntb * C4;
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int c4 = (int)(i % C4);
+    const size_t rest = i / C4;
+    const int tb = (int)(rest % ntb);
+    const size_t b = rest / ntb;
+    const int c = 4 * c4, t0 = tb * TBK;
+    float w[4][KK];
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+      for (int j = 0; j < KK; j++) w[m][j] = conv[(size_t)(c + m) * KK + j];
+    // rows t0 - (KK-1) .. t0 + TBK - 1 (zero before the window)
+    f4 x[TBK + KK - 1];
+#pragma unroll
+    for (int q = 0; q < TBK + KK - 1; q++) {
+      const int t = t0 - (KK - 1) + q;
+      x[q] = t >= 0 && t < T ? ld4(raw + (b * T + t) * cdim + c) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < TBK; u++) {
+      if (t0 + u >= T) break;
+      f4 acc = z;
+#pragma unroll
+      for (int j = 0; j < KK; j++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) acc[m] = fmaf(x[u + j][m], w[m][j], acc[m]);
+      const size_t e = (b * T + t0 + u) * cdim + c;
+      st4(pre + e, acc);
+      f4 sl;
+#pragma unroll
+      for (int m = 0; m < 4; m++) sl[m] = silu(acc[m]);
+      st4(cq + e, sl);
+    }
+  }
+}
+
+template <int KK, int TBK>
+__global__ __launch_bounds__(256) void conv_bwd_t(int B, int T, int cdim,
+                                                  const float* __restrict__ pre,
+                                                  const float* __restrict__ dcq,
+                                                  const float* __restrict__ conv,
+                                                  float* __restrict__ draw) {
+  const int C4 = cdim / 4, ntb = (T + TBK - 1) / TBK;
+  const size_t n = (size_t)B * ntb * C4;
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int c4 = (int)(i % C4);
+    const size_t rest = i / C4;
+    const int tb = (int)(rest % ntb);
+    const size_t b = rest / ntb;
+    const int c = 4 * c4, t0 = tb * TBK;
+    float w[4][KK];
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+      for (int j = 0; j < KK; j++) w[m][j] = conv[(size_t)(c + m) * KK + j];
+    // dpre of rows t0 .. t0 + TBK + KK - 2 (zero past the window)
+    f4 dp[TBK + KK - 1];
+#pragma unroll
+    for (int q = 0; q < TBK + KK - 1; q++) {
+      const int t = t0 + q;
+      dp[q] = z;
+      if (t < T) {
+        const size_t e = (b * T + t) * cdim + c;
+        const f4 pv = ld4(pre + e), dv = ld4(dcq + e);
+#pragma unroll
+        for (int m = 0; m < 4; m++) dp[q][m] = dv[m] * silu_grad(pv[m]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TBK; u++) {
+      if (t0 + u >= T) break;
+      f4 acc = z;
+#pragma unroll
+      for (int j = 0; j < KK; j++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) acc[m] = fmaf(dp[u + KK - 1 - j][m], w[m][j], acc[m]);
+      st4(draw + (b * T + t0 + u) * cdim + c, acc);
+    }
+  }
+}
+
 // --------------------------------------------------- normalised q/k, gates --
 // One 16-lane group per (token, k-head): q^ and k^ (DK/16 values per lane);
 // lanes l < rep also make g and beta of v-head ko * rep + l.
@@ -633,8 +728,13 @@ size_t gdn_partial_floats(int B, int T, int nv, int dk, int dv) {
 
 hipError_t gdn_launch_forward(const GdnArgs& p, hipStream_t st) {
   const int BT = p.B * p.T, cdim = 2 * p.nk * p.dk + p.nv * p.dv;
-  hipLaunchKernelGGL(gdnk::conv_fwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT, p.T,
-                     cdim, p.kk, p.raw, p.conv, p.pre, p.cq);
+  if (p.kk == 4)
+    hipLaunchKernelGGL((gdnk::conv_fwd_t<4, 8>),
+                       dim3(grid4((size_t)p.B * ((p.T + 7) / 8) * cdim / 4)), dim3(256), 0, st,
+                       p.B, p.T, cdim, p.raw, p.conv, p.pre, p.cq);
+  else
+    hipLaunchKernelGGL(gdnk::conv_fwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT,
+                       p.T, cdim, p.kk, p.raw, p.conv, p.pre, p.cq);
   const unsigned gq = (unsigned)(((size_t)BT * p.nk + 15) / 16);
   if (p.dk == 128)
     hipLaunchKernelGGL(gdnk::prep<128>, dim3(gq), dim3(256), 0, st, BT, p.nk, p.nv, cdim, p.cq,
@@ -686,7 +786,12 @@ hipError_t gdn_launch_backward(const GdnArgs& p, hipStream_t st) {
   else
     hipLaunchKernelGGL(gdnk::chain<64>, dim3(gq), dim3(256), 0, st, p.B, p.T, p.nk, p.nv, ncb, cdim,
                        p.part, p.cq, p.a, p.A_log, p.dt_bias, p.g, p.beta, p.dcq, p.da, p.db);
-  hipLaunchKernelGGL(gdnk::conv_bwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT, p.T,
-                     cdim, p.kk, p.pre, p.dcq, p.conv, p.draw);
+  if (p.kk == 4)
+    hipLaunchKernelGGL((gdnk::conv_bwd_t<4, 8>),
+                       dim3(grid4((size_t)p.B * ((p.T + 7) / 8) * cdim / 4)), dim3(256), 0, st,
+                       p.B, p.T, cdim, p.pre, p.dcq, p.conv, p.draw);
+  else
+    hipLaunchKernelGGL(gdnk::conv_bwd, dim3(grid4((size_t)BT * cdim / 4)), dim3(256), 0, st, BT,
+                       p.T, cdim, p.kk, p.pre, p.dcq, p.conv, p.draw);
   return hipGetLastError();
 }
