@@ -210,17 +210,46 @@ __global__ __launch_bounds__(256) void fwd_seq(
 #pragma unroll
     for (int m = 0; m < RPT; m++) yb[m] = sab[m] = 0.f;
     if (nt == TT) {
-      // the next token's inputs are read from LDS while this one runs
+      // The next token's inputs are read from LDS while this one runs.  The
+      // state after token tt - 1 gives both y_{tt-1} (with r_{tt-1}) and
+      // sa_tt (with a_tt): the two dot products and row sums are formed
+      // together, so the read-out of one token overlaps the state step of
+      // the next instead of following it.
       Tok tc, tn, tn2;
       ldtok(buf, 0, tc);
       ldtok(buf, 1, tn);
+      f4 rprev = tc.rv;
 #pragma unroll
       for (int tt = 0; tt < TT; tt++) {
         if (tt + 2 < TT) ldtok(buf, tt + 2, tn2);
         __builtin_amdgcn_sched_barrier(0);
-        token_in(tc, tt);
+        float sa[RPT], yy[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          sa[m] = dot4(S[m], tc.av);
+          if (tt > 0) yy[m] = dot4(S[m], rprev);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          sa[m] = rowsum16(sa[m]);
+          if (tt > 0) yy[m] = rowsum16(yy[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; m++) {
+          sab[m] = (cg == tt) ? sa[m] : sab[m];
+          if (tt > 0) yb[m] = (cg == tt - 1) ? yy[m] : yb[m];
+#pragma unroll
+          for (int c = 0; c < 4; c++)
+            S[m][c] = fmaf(tc.vv[m], tc.kv[c], fmaf(sa[m], tc.bb[c], S[m][c] * tc.wv[c]));
+        }
+        rprev = tc.rv;
         tc = tn;
         tn = tn2;
+      }
+#pragma unroll
+      for (int m = 0; m < RPT; m++) {
+        const float y15 = rowsum16(dot4(S[m], rprev));
+        yb[m] = (cg == TT - 1) ? y15 : yb[m];
       }
     } else {
       for (int tt = 0; tt < nt; tt++) token(buf, tt);
