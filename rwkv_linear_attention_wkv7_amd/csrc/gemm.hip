@@ -918,7 +918,9 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
 template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid reaches 512 workgroups, or 256 when each workgroup
-  // still has >= 8M multiply-adds; else the smallest tile.  Small problems
+  // still has >= 8M multiply-adds; else the smallest tile.  Measured on
+  // MI355X, fp32 8192x768x768: 128x128 tiles (384 workgroups) 120 us, 128x64
+  // (768) 95 us.  Small problems
   // (the decode stack's 2048-row products) are latency bound and gain from
   // more, smaller workgroups; large ones keep the 128x128 tile.  Measured on
   // MI355X, fp32: 2048x256x256 7.2 us at 32x32 vs 8.6 at 64x32 and 11.6 at
@@ -932,7 +934,12 @@ hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipSt
     const long wg = (long)((maxM + bm - 1) / bm) * ((maxN + bn - 1) / bn) * gz;
     return maxN >= bn && (wg >= 512 || (wg >= 256 && (long)bm * bn * klen >= (8l << 20)));
   };
-  if (fits(128, 128)) return launch_bk<PREC, 4, 4, TA, TB>(b, gz, kslice, klen, st);
+  // a 128x128 grid that only part-fills a second round of the 256 CUs leaves
+  // the CUs holding two tiles to set the time: the 128x64 tiles then spread
+  // evenly (three per CU at 768 workgroups)
+  const long wg128 = (long)((maxM + 127) / 128) * ((maxN + 127) / 128) * gz;
+  const bool ragged = wg128 > 256 && wg128 < 512 && wg128 % 256 != 0;
+  if (fits(128, 128) && !(ragged && fits(128, 64))) return launch_bk<PREC, 4, 4, TA, TB>(b, gz, kslice, klen, st);
   if (fits(128, 64)) return launch_bk<PREC, 4, 2, TA, TB>(b, gz, kslice, klen, st);
   if (fits(64, 64)) return launch_bk<PREC, 2, 2, TA, TB>(b, gz, kslice, klen, st);
   if (fits(64, 32)) return launch_bk<PREC, 2, 1, TA, TB>(b, gz, kslice, klen, st);
