@@ -918,13 +918,12 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
 template <int PREC, bool TA, bool TB>
 hipError_t launch_layout(const GemmBatch& b, int gz, int kslice, int klen, hipStream_t st) {
   // Largest tile whose grid reaches 512 workgroups, or 256 when each workgroup
-  // still has >= 8M multiply-adds; else the smallest tile.  Measured on
-  // MI355X, fp32 8192x768x768: 128x128 tiles (384 workgroups) 120 us, 128x64
-  // (768) 95 us.  Small problems
+  // still has >= 8M multiply-adds; else the smallest tile.  Small problems
   // (the decode stack's 2048-row products) are latency bound and gain from
   // more, smaller workgroups; large ones keep the 128x128 tile.  Measured on
   // MI355X, fp32: 2048x256x256 7.2 us at 32x32 vs 8.6 at 64x32 and 11.6 at
-  // 64x64; 2048x1024x256 17.5 us at 64x64 vs 20.0 at 128x64.
+  // 64x64; 2048x1024x256 17.5 us at 64x64 vs 20.0 at 128x64; 8192x768x768
+  // 120 us at 128x128 (384 workgroups) vs 95 at 128x64 (768).
   int maxM = 0, maxN = 0;
   for (int i = 0; i < b.count; i++) {
     maxM = max(maxM, b.p[i].M);
