@@ -562,13 +562,13 @@ void tm_weight_spans(Spans& sp, const tm_shape* s, const WT* W, bool written) {
 
 // decode: T == 1 with the WKV state updated in place (s0 == sT, no checkpoint),
 // run by one fused kernel (pre-WKV, the step on the state in place, post-WKV).
-// out = out_beta * out + tg Wo (out_proj = false: tg is left in m.tg and the
-// caller applies Wo).
+// out = out_beta * out + tg Wo, or resid + tg Wo when resid is given
+// (out_proj = false: tg is left in m.tg and the caller applies Wo).
 int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const float* x,
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
                     float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false,
-                    bool out_proj = true) {
+                    bool out_proj = true, const float* resid = nullptr) {
   const int BT = B * T, C = s->C;
   if (s->layer_id > 0 && (!m.lv || !m.ov))
     return fail(WKV7_EHIP, "internal: activation set without value-residual buffers for layer %d",
@@ -632,7 +632,9 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
                                m.ckpt, m.wkv_ws, st), "wkv7 forward");
     HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
   }
-  if (out_proj)
+  if (out_proj && resid)  // out = resid + tg Wo
+    HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, 0.f, EPI_ADD, resid, 1, nullptr, st), "o proj");
+  else if (out_proj)
     HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
   return WKV7_OK;
 }
@@ -1437,10 +1439,10 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
   auto block_fwd = [&](int l, const float* xin, BlockActs& a) -> int {
     const rwkv7_block& bl = M->blocks[l];
     tm_shape s = block_shape(cfg, l);
-    HIPCHK(hipMemcpyAsync(a.x1, xin, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, xin, bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
+    // x1 = xin + the time mix (the residual added in the output projection)
     CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), nullptr, a.x1, nullptr, a.tm,
-                        st, false, 1.f, prec));
+                        st, false, 0.f, prec, false, true, xin));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
     HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
@@ -1450,7 +1452,6 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
   const int H = cfg->H;
   auto attn_fwd = [&](int i, const float* xin, TrainBufs::AttnActs& a) -> int {
     const rwkv7_attn_block& ab = M->attn[i];
-    HIPCHK(hipMemcpyAsync(a.x1, xin, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, xin, ab.ln1_w, ab.ln1_b, a.h, nullptr, nullptr, st), "attn ln1");
     {
       GemmBatch g;
@@ -1462,7 +1463,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     }
     HIPCHK(moba_launch_forward(B, T, H, cfg->moba_chunk, cfg->moba_topk, a.q, a.k, a.v, a.y, a.lse, a.sel,
                                t.mws, st), "moba forward");
-    HIPCHK(gemm_run(prec, false, false, BT, C, C, a.y, C, ab.Wo, C, a.x1, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "o proj");
+    HIPCHK(gemm_run(prec, false, false, BT, C, C, a.y, C, ab.Wo, C, a.x1, C, 0.f, EPI_ADD, xin, 1, nullptr, st), "o proj");
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, ab.ln2_w, ab.ln2_b, a.h2, nullptr, nullptr, st), "attn ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, ab.cm_mu_k, a.sh, nullptr, st), "attn cm shift");
     HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, ab.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "attn cm key");
@@ -1487,9 +1488,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
       CHK(attn_fwd(i, bin(pos), a));
       x1 = a.x1, ka = a.ka, Wv = M->attn[i].cm_Wv;
     }
-    float* xo = bin(pos + 1);
-    HIPCHK(hipMemcpyAsync(xo, x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(gemm_run(prec, false, false, BT, C, F, ka, F, Wv, C, xo, C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+    float* xo = bin(pos + 1);  // x1 + the channel mix
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, ka, F, Wv, C, xo, C, 0.f, EPI_ADD, x1, 1, nullptr, st), "cm value");
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(NB), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
@@ -1717,16 +1717,14 @@ int replay_run(const rwkv7_config* cfg, const rwkv7_model* M, int B, int T, cons
     const rwkv7_block& bl = M->blocks[l];
     tm_shape s = block_shape(cfg, l);
     float* st_l = ast + (size_t)l * B * cfg->H * NN;
-    HIPCHK(hipMemcpyAsync(a.x1, bin(l), tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
     HIPCHK(stk_launch_layernorm(BT, C, bin(l), bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
     CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, axp + (size_t)l * BC, t.vf, st_l, st_l, a.x1,
-                        xl + (size_t)l * BC, a.tm, st, false, 1.f, prec));
+                        xl + (size_t)l * BC, a.tm, st, false, 0.f, prec, false, true, bin(l)));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, fxp + (size_t)l * BC, bl.cm_mu_k, a.sh,
                                xl + (size_t)(L + l) * BC, st), "cm shift");
     HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
-    HIPCHK(hipMemcpyAsync(bin(l + 1), a.x1, tokC * sizeof(float), hipMemcpyDeviceToDevice, st), "residual copy");
-    HIPCHK(gemm_run(prec, false, false, BT, C, F, a.ka, F, bl.cm_Wv, C, bin(l + 1), C, 1.f, EPI_NONE, nullptr, 1, nullptr, st), "cm value");
+    HIPCHK(gemm_run(prec, false, false, BT, C, F, a.ka, F, bl.cm_Wv, C, bin(l + 1), C, 0.f, EPI_ADD, a.x1, 1, nullptr, st), "cm value");
   }
   HIPCHK(hipMemcpyAsync(axp, xl, (size_t)L * BC * sizeof(float), hipMemcpyDeviceToDevice, st), "state copy");
   HIPCHK(hipMemcpyAsync(fxp, xl + (size_t)L * BC, (size_t)L * BC * sizeof(float), hipMemcpyDeviceToDevice, st), "state copy");

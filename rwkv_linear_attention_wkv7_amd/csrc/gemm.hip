@@ -40,6 +40,7 @@ __device__ __forceinline__ float apply_epi(float acc, int epi, float aux) {
     case EPI_SIG_BWD: return acc * aux * (1.0f - aux);   // aux = sigmoid(.) of the forward
     case EPI_SQRELU: return acc > 0.f ? acc * acc : 0.f;  // relu(.)^2
     case EPI_SQRELU_BWD: return acc * 2.0f * sqrtf(aux);  // aux = relu(f)^2 of the forward
+    case EPI_ADD: return acc + aux;
     default: return acc;
   }
 }

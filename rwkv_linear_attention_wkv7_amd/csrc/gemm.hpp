@@ -7,7 +7,8 @@
 
 enum GemmEpi {
   EPI_NONE = 0, EPI_TANH = 1, EPI_SIGMOID = 2, EPI_TANH_BWD = 3, EPI_SIG_BWD = 4, EPI_SQRELU = 5,
-  EPI_SQRELU_BWD = 6  // acc * 2 relu(f) with aux = relu(f)^2 (so relu(f) = sqrt(aux))
+  EPI_SQRELU_BWD = 6,  // acc * 2 relu(f) with aux = relu(f)^2 (so relu(f) = sqrt(aux))
+  EPI_ADD = 7          // acc + aux (a residual from another buffer, same leading dimension)
 };
 
 constexpr int GEMM_MAX_BATCH = 8;
