@@ -521,10 +521,12 @@ def setup_gdn():
     # the backward's recurrence per token and value head: 5 dk dv flop to
     # recompute the state (decay, kv, update) and 14 dk dv for the reverse
     # step (dS += q^ do, S do, dS^T k^, dS_pre, dS u + S_pre dkv, <dS_pre, S>,
-    # g dS_pre)
+    # g dS_pre) -- the per-token recurrence's count, whatever form the
+    # kernels take
     flops = 19.0 * dk * dv * B * T * nv
-    roof = dict(kernel="gdn_backward call (recurrence from 16-token checkpoints + RMSNorm, "
-                       "gate and l2-norm chain, conv backward)", bound="alu", work=flops,
+    roof = dict(kernel="gdn_backward call (RMSNorm backward, reverse state-gradient scan, "
+                       "per-block matrix-core products, gate and l2-norm chain, conv backward)",
+                bound="alu", work=flops,
                 unit="TFLOP/s", peak=PEAK["alu_fp32"][0], fn=dom, key="gdn_bwd",
                 src=["rwkv_linear_attention_wkv7_amd/csrc/gdn.hip"])
 

@@ -1840,6 +1840,7 @@ void carve_gdn_cache(Carver& c, const gdn_shape* s, int B, int T, GdnArgs& p) {
   p.beta = c.take(BT * s->nv);
   p.o = c.take(BT * s->nv * s->dv);
   p.ckpt = c.take(gdn_ckpt_floats(B, T, s->nv, s->dk, s->dv));
+  p.kv = c.take(BT * s->nv * s->dv);
 }
 
 void carve_gdn_bwd(Carver& c, const gdn_shape* s, int B, int T, GdnArgs& p) {
@@ -1847,6 +1848,13 @@ void carve_gdn_bwd(Carver& c, const gdn_shape* s, int B, int T, GdnArgs& p) {
   p.dobuf = c.take(BT * s->nv * s->dv);
   p.dcq = c.take(BT * gdn_cdim(s));
   p.part = c.take(gdn_partial_floats(B, T, s->nv, s->dk, s->dv));
+  p.gend = p.du = p.anc = nullptr;
+  if (gdn_two_pass(s->dk, s->dv)) {
+    const size_t nblk = (T + 15) / 16;
+    p.gend = c.take(gdn_ckpt_floats(B, T, s->nv, s->dk, s->dv));
+    p.du = c.take(BT * s->nv * s->dv);
+    p.anc = c.take((size_t)B * s->nv * nblk * s->dv);
+  }
 }
 
 void gdn_fill(GdnArgs& p, const gdn_shape* s, const gdn_weights* W, int B, int T,

@@ -407,7 +407,8 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
                                                const float* __restrict__ cq,
                                                const float* __restrict__ gg,
                                                const float* __restrict__ be,
-                                               float* __restrict__ o, float* __restrict__ ckpt) {
+                                               float* __restrict__ o, float* __restrict__ ckpt,
+                                               float* __restrict__ kvo) {
   constexpr int RPL = DK / 16;
   __shared__ __attribute__((aligned(16))) Stage<DK> st;
   const int ncb = dv / CB;
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
 #pragma unroll
       for (int i = 0; i < RPL; i += 4) st4(cp + i, f4{s[i], s[i + 1], s[i + 2], s[i + 3]});
     }
-    float ob = 0.f;
+    float ob = 0.f, kb = 0.f;
 #pragma unroll
     for (int tt = 0; tt < TT; tt++) {
       const float gt = st.g[buf][tt], bt_ = st.b[buf][tt], vt = st.v[buf][tt][cl];
@@ -457,6 +458,7 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
         kv = fmaf(s[i], kr[i], kv);
       }
       kv = rowsum16(kv);
+      kb = rg == tt ? kv : kb;
       const float u = bt_ * (vt - kv);
       float ov = 0.f;
 #pragma unroll
@@ -467,7 +469,10 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
       ov = rowsum16(ov);
       ob = rg == tt ? ov : ob;
     }
-    if (t0 + rg < T) o[((bT + t0 + rg) * nv + h) * dv + col] = ob;
+    if (t0 + rg < T) {
+      o[((bT + t0 + rg) * nv + h) * dv + col] = ob;
+      if (kvo) kvo[((bT + t0 + rg) * nv + h) * dv + col] = kb;
+    }
     // the other buffer was last read in the block before, behind the
     // previous barrier
     if (more) store_stage<DK>(st, nx, buf ^ 1, t0 + TT, T, false);
@@ -475,8 +480,9 @@ __global__ __launch_bounds__(256) void fwd_seq(int B, int T, int nk, int nv, int
   }
 }
 
-// Partials per (column block, b, t, h): [0, DK) dq^, [DK, 2 DK) dk^, 2 DK dg,
-// 2 DK + 1 dbeta (sums over the block's 16 columns).
+// Partials per (column block, b, t, h): [0, DK) dq^, [DK, 2 DK) dk^, 2 DK
+// g dg (the gradient of log g), 2 DK + 1 dbeta (sums over the block's 16
+// columns).
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int dv, int cdim,
                                                const float* __restrict__ qh,
@@ -607,7 +613,7 @@ __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int
           for (int i = 0; i < NQ; i++) dst[i] = x[i];
         }
         if (lane == 0) {
-          red[wave][slot][2 * DK] = sg;
+          red[wave][slot][2 * DK] = sg * gt;  // g dg: the gradient of log g
           red[wave][slot][2 * DK + 1] = sb;
         }
       }
@@ -633,11 +639,339 @@ __global__ __launch_bounds__(256) void bwd_seq(int B, int T, int nk, int nv, int
   }
 }
 
+
+// ------------------------------------------------------ two-pass backward --
+// For dk = dv.  With G_t the gradient of the state after token t including
+// that token's read-out (G_t = dS_t + q^_t do_t^T), the reverse step is
+// G_{t-1} = q^_{t-1} do_{t-1}^T + g_t (G_t - beta_t k^_t du_t^T), du_t =
+// G_t^T k^_t: every value column of G evolves on its own, so the scan (pass 1)
+// runs without the states.  Pass 2 then gives, per 16-token block from the
+// checkpoint S0 and the gradient Ge entering the block's last token from later
+// tokens, with u_t = beta_t (v_t - kv_t) and the decay products
+// P(a, b) = g_{a+1} ... g_b, E_t = g_0 ... g_t (block-local tokens):
+//   dq^_t = S_t do_t = E_t S0 do_t + sum_{tau <= t} P(tau, t) k^_tau (u_tau . do_t)
+//   dk^_t = G_t u_t - beta_t g_t S_{t-1} du_t
+//         = P(t, 15) Ge u_t + sum_{tau >= t} P(t, tau) q^_tau (do_tau . u_t)
+//           - sum_{tau > t} P(t, tau) beta_tau k^_tau (du_tau . u_t)
+//           - beta_t [E_t S0 du_t + sum_{tau < t} P(tau, t) k^_tau (u_tau . du_t)]
+//   dbeta_t = du_t . (v_t - kv_t),  dv_t = beta_t du_t
+//   g_t dg_t = g_t <G_t - beta_t k^_t du_t^T, S_{t-1}> = Phi_t - beta_t du_t . v_t
+// with Phi_t = <G_t, S_t> carried backward from the block end,
+// Phi_{t-1} = Phi_t - beta_t du_t . v_t + o_{t-1} . do_{t-1}, and
+// Phi_{L-1} = <Ge, S_{L-1}> + o_{L-1} . do_{L-1} (S_{L-1} = the next checkpoint).
+// Every decay factor is a product of decays in (0, 1], so any g in that range
+// is taken without overflow, and no step divides by g.
+
+// Pass 1, workgroup and lane layout of bwd_seq.  Writes per block the
+// gradient entering its last token (gend, [bh][blk][dv][dk] like the
+// checkpoints) and that gradient's inner product with the state after the
+// block, by value column (anc [bh][blk][dv]); per token du and dv = beta du
+// (into dcq).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_scan(int B, int T, int nk, int nv, int dv, int cdim,
+                                                const float* __restrict__ qh,
+                                                const float* __restrict__ kh,
+                                                const float* __restrict__ cq,
+                                                const float* __restrict__ gg,
+                                                const float* __restrict__ be,
+                                                const float* __restrict__ dob,
+                                                const float* __restrict__ ckpt,
+                                                float* __restrict__ gend, float* __restrict__ du_out,
+                                                float* __restrict__ anc, float* __restrict__ dcq) {
+  constexpr int RPL = DK / 16;
+  __shared__ __attribute__((aligned(16))) Stage<DK> st;
+  const int ncb = dv / CB;
+  const int bh = blockIdx.x / ncb, cb = blockIdx.x - bh * ncb;
+  const int b = bh / nv, h = bh - b * nv, ko = h / (nv / nk);
+  const int tid = threadIdx.x, rg = tid & 15, cl = tid >> 4;
+  const int col0 = cb * CB, col = col0 + cl;
+  const size_t bT = (size_t)b * T;
+  const int kvoff = 2 * nk * DK;
+  const int nblk = (T + TT - 1) / TT;
+  float G[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; i++) G[i] = 0.f;
+  int buf = 0;
+  StageRegs<DK> nx;
+  load_stage<DK>(nx, (nblk - 1) * TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be,
+                 dob, true, nk);
+  store_stage<DK>(st, nx, 0, (nblk - 1) * TT, T, true);
+  __syncthreads();
+  for (int blk = nblk - 1; blk >= 0; blk--, buf ^= 1) {
+    const int t0 = blk * TT;
+    if (blk > 0)  // in flight while this block runs
+      load_stage<DK>(nx, t0 - TT, T, nv, dv, cdim, kvoff, bT, h, ko, col0, qh, kh, cq, gg, be, dob,
+                     true, nk);
+    {  // the gradient entering this block's last token, and its anchor
+      const size_t so = (((size_t)bh * nblk + blk) * dv + col) * DK + rg * RPL;
+      float an = 0.f;
+      const float* sn = blk + 1 < nblk ? ckpt + so + (size_t)dv * DK : nullptr;
+#pragma unroll
+      for (int i = 0; i < RPL; i += 4) {
+        st4(gend + so + i, f4{G[i], G[i + 1], G[i + 2], G[i + 3]});
+        if (sn) {
+          const f4 x = ld4(sn + i);
+          an = fmaf(G[i], x[0], fmaf(G[i + 1], x[1], fmaf(G[i + 2], x[2], fmaf(G[i + 3], x[3], an))));
+        }
+      }
+      an = rowsum16(an);
+      if (rg == 0) anc[((size_t)bh * nblk + blk) * dv + col] = an;
+    }
+    float dub = 0.f;
+#pragma unroll
+    for (int tt = TT - 1; tt >= 0; tt--) {
+      const float gt = st.g[buf][tt], bt_ = st.b[buf][tt], dot = st.d[buf][tt][cl];
+      float kr[RPL], qr[RPL];
+#pragma unroll
+      for (int i = 0; i < RPL; i += 4) {
+        const f4 x = ld4(&st.k[buf][tt][rg * RPL + i]), y = ld4(&st.q[buf][tt][rg * RPL + i]);
+        kr[i] = x[0]; kr[i + 1] = x[1]; kr[i + 2] = x[2]; kr[i + 3] = x[3];
+        qr[i] = y[0]; qr[i + 1] = y[1]; qr[i + 2] = y[2]; qr[i + 3] = y[3];
+      }
+      float du = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) {
+        G[i] = fmaf(qr[i], dot, G[i]);
+        du = fmaf(G[i], kr[i], du);
+      }
+      du = rowsum16(du);
+      dub = rg == tt ? du : dub;
+      const float c = -bt_ * du;
+#pragma unroll
+      for (int i = 0; i < RPL; i++) G[i] = gt * fmaf(kr[i], c, G[i]);
+    }
+    if (t0 + rg < T) {
+      const size_t t = bT + t0 + rg;
+      du_out[(t * nv + h) * dv + col] = dub;
+      dcq[t * cdim + kvoff + (size_t)h * dv + col] = st.b[buf][rg] * dub;
+    }
+    if (blk > 0) store_stage<DK>(st, nx, buf ^ 1, t0 - TT, T, true);
+    lds_barrier();
+  }
+}
+
+__device__ __forceinline__ f4 mma16(f4 a, f4 b, f4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; s++) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+// Pass 2: one workgroup per (b, v-head, 16-token block), D / 16 waves; wave w
+// owns key columns 16w..16w+15 of dq^ and dk^.  MFMA lane layout (16x16x4 f32
+// steps over a group of 16 k): A fragment lane l holds A[l%16][4(l/16)+s], B
+// fragment B[4(l/16)+s][l%16], result element v = C[4(l/16)+v][l%16].
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void bwd_blk(int B, int T, int nk, int nv, int cdim,
+                                                        const float* __restrict__ qh,
+                                                        const float* __restrict__ kh,
+                                                        const float* __restrict__ cq,
+                                                        const float* __restrict__ gg,
+                                                        const float* __restrict__ be,
+                                                        const float* __restrict__ o,
+                                                        const float* __restrict__ dob,
+                                                        const float* __restrict__ ckpt,
+                                                        const float* __restrict__ gend,
+                                                        const float* __restrict__ du_in,
+                                                        const float* __restrict__ kvi,
+                                                        const float* __restrict__ anc,
+                                                        float* __restrict__ part) {
+  constexpr int NW = D / 16, NT = 64 * NW, RS = D + 4, XS = TT + 4, PW = 2 * D + 2;
+  constexpr int SLOTS = TT * D / 4;  // float4 slots of one [TT][D] block
+  static_assert(SLOTS % NT == 0, "staging assumes whole passes");
+  __shared__ __attribute__((aligned(16))) float sDO[TT][RS];
+  __shared__ __attribute__((aligned(16))) float sDU[TT][RS];
+  __shared__ __attribute__((aligned(16))) float sU[TT][RS];
+  __shared__ __attribute__((aligned(16))) float sQ[TT][RS];   // q^_t
+  __shared__ __attribute__((aligned(16))) float sKB[TT][RS];  // beta_t k^_t
+  __shared__ __attribute__((aligned(16))) float sK[TT][RS];   // k^_t
+  // the Gram terms times their decay products
+  __shared__ __attribute__((aligned(16))) float xA1[TT][XS];  // P(tau, t) do_t . u_tau, tau <= t
+  __shared__ __attribute__((aligned(16))) float xB1[TT][XS];  // P(t, tau) u_t . do_tau, tau >= t
+  __shared__ __attribute__((aligned(16))) float xB2[TT][XS];  // P(t, tau) u_t . du_tau, tau > t
+  __shared__ __attribute__((aligned(16))) float xC2[TT][XS];  // P(tau, t) du_t . u_tau, tau < t
+  __shared__ float sP[TT][TT + 1];                            // P(a, b), a <= b
+  __shared__ float sE[TT], sG[TT], sBe[TT];
+  __shared__ float sDb[TT], sOd[TT], sDvb[TT];  // dbeta, o . do, beta du . v per token
+  __shared__ float sAnc;
+
+  const int nblk = (T + TT - 1) / TT;
+  const int gi = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = gi / nblk, blk = gi - bh * nblk;
+  const int b = bh / nv, h = bh - b * nv, ko = h / (nv / nk);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, fr = lane & 15, fg = lane >> 4;
+  const int t0 = blk * TT, n = min(TT, T - t0);
+  const size_t bT = (size_t)b * T;
+  const int kvoff = 2 * nk * D;
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+
+  // state fragments (B operand): sf[kg][s] = S0[i][16 kg + 4 fg + s], i = 16 w + fr
+  const int i_key = 16 * w + fr;
+  const size_t sb = ((size_t)bh * nblk + blk) * D * D;
+  f4 sf[NW], gf[NW];
+#pragma unroll
+  for (int kg = 0; kg < NW; kg++) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const size_t j = 16 * kg + 4 * fg + s;
+      sf[kg][s] = ckpt[sb + j * D + i_key];
+      gf[kg][s] = gend[sb + j * D + i_key];
+    }
+  }
+  if (tid < TT) {  // tokens past the end: g = 1, beta = 0
+    const bool ok = tid < n;
+    const size_t i = (bT + t0 + (ok ? tid : 0)) * nv + h;
+    sG[tid] = ok ? gg[i] : 1.f;
+    sBe[tid] = ok ? be[i] : 0.f;
+  }
+  if (w == 1) {  // the anchor: sum of the block end's per-column inner products
+    float a = 0.f;
+    for (int c = lane; c < D; c += 64) a += anc[((size_t)bh * nblk + blk) * D + c];
+    a = wavesum(a);
+    if (lane == 0) sAnc = a;
+  }
+  __syncthreads();
+  static_assert(TT * TT <= NT, "one thread per decay product");
+  if (tid < TT * TT) {  // products over the block's tokens, multiplied in token order
+    const int a0 = tid / TT, b0 = tid - a0 * TT;
+    float pr = 1.f;
+    for (int q = a0 + 1; q <= b0; q++) pr *= sG[q];
+    sP[a0][b0] = pr;
+    if (tid < TT) {
+      float e = 1.f;
+      for (int q = 0; q <= tid; q++) e *= sG[q];
+      sE[tid] = e;
+    }
+  }
+  // stage the block: thread -> (token, 4 columns); per-token dot products over
+  // the D columns summed by the D / 4 threads of a token
+  constexpr int TPT = D / 4;  // threads per token in one pass
+#pragma unroll
+  for (int pass = 0; pass < SLOTS / NT; pass++) {
+    const int f = tid + NT * pass, t = f / TPT, c4 = (f - t * TPT) * 4;
+    const bool ok = t < n;
+    const size_t tg = bT + t0 + (ok ? t : 0);
+    const size_t vi = (tg * nv + h) * D + c4;
+    const size_t ki = (tg * nk + ko) * D + c4;
+    const f4 xdo = ok ? ld4(dob + vi) : z, xdu = ok ? ld4(du_in + vi) : z;
+    const f4 xv = ok ? ld4(cq + tg * cdim + kvoff + (size_t)h * D + c4) : z;
+    const f4 xkv = ok ? ld4(kvi + vi) : z, xo = ok ? ld4(o + vi) : z;
+    const f4 xq = ok ? ld4(qh + ki) : z, xk = ok ? ld4(kh + ki) : z;
+    const float bt_ = sBe[t];
+    const f4 vk = xv - xkv;
+    const f4 u = bt_ * vk;
+    *reinterpret_cast<f4*>(&sDO[t][c4]) = xdo;
+    *reinterpret_cast<f4*>(&sDU[t][c4]) = xdu;
+    *reinterpret_cast<f4*>(&sU[t][c4]) = u;
+    *reinterpret_cast<f4*>(&sQ[t][c4]) = xq;
+    *reinterpret_cast<f4*>(&sKB[t][c4]) = bt_ * xk;
+    *reinterpret_cast<f4*>(&sK[t][c4]) = xk;
+    float pdb = 0.f, pod = 0.f, pdv = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      pdb = fmaf(xdu[c], vk[c], pdb);
+      pod = fmaf(xo[c], xdo[c], pod);
+      pdv = fmaf(xdu[c], xv[c], pdv);
+    }
+    // the TPT threads of token t are one aligned group of 16 or 32 lanes
+    pdb = rowsum16(pdb);
+    pod = rowsum16(pod);
+    pdv = rowsum16(pdv);
+    if (TPT == 32) {
+      auto sw = [](float x) {
+        auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      };
+      pdb = sw(pdb);
+      pod = sw(pod);
+      pdv = sw(pdv);
+    }
+    if (f - t * TPT == 0) {
+      sDb[t] = pdb;
+      sOd[t] = pod;
+      sDvb[t] = bt_ * pdv;
+    }
+  }
+  __syncthreads();
+  // Gram matrices over the D values: wave 0 do.u, wave 1 u.du
+  if (w < 2) {
+    const float(*P)[RS] = w == 0 ? sDO : sU;
+    const float(*Q)[RS] = w == 0 ? sU : sDU;
+    f4 x = z;
+#pragma unroll
+    for (int kg = 0; kg < NW; kg++)
+      x = mma16(*reinterpret_cast<const f4*>(&P[fr][16 * kg + 4 * fg]),
+                *reinterpret_cast<const f4*>(&Q[fr][16 * kg + 4 * fg]), x);
+    // x[v] = X[t = 4 fg + v][tau = fr]
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int t = 4 * fg + v;
+      if (w == 0) {  // X = do . u^T
+        const float y = x[v] * sP[fr][t];
+        xA1[t][fr] = fr <= t ? y : 0.f;
+        xB1[fr][t] = t >= fr ? y : 0.f;  // B1[t'][tau'] = X[tau'][t'], tau' >= t'
+      } else {  // X = u . du^T
+        const float y = x[v] * sP[t][fr];
+        xB2[t][fr] = fr > t ? y : 0.f;
+        xC2[fr][t] = t < fr ? y : 0.f;  // C2[t'][tau'] = X[tau'][t'], tau' < t'
+      }
+    }
+  }
+  __syncthreads();
+  f4 aq = z, ab = z, ak = z;  // dq, the S_{t-1} du part, the G u part
+#pragma unroll
+  for (int kg = 0; kg < NW; kg++) {
+    const f4 pdo = *reinterpret_cast<const f4*>(&sDO[fr][16 * kg + 4 * fg]);
+    const f4 pdu = *reinterpret_cast<const f4*>(&sDU[fr][16 * kg + 4 * fg]);
+    const f4 pu = *reinterpret_cast<const f4*>(&sU[fr][16 * kg + 4 * fg]);
+    aq = mma16(pdo, sf[kg], aq);
+    ab = mma16(pdu, sf[kg], ab);
+    ak = mma16(pu, gf[kg], ak);
+  }
+  // lane holds tokens t = 4 fg + v at key i_key: the block-start terms take
+  // their decays per token
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int t = 4 * fg + v;
+    aq[v] *= sE[t];
+    ab[v] *= sE[t];
+    ak[v] *= sP[t][TT - 1];
+  }
+  f4 fk, fq, fkb;
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    fk[s] = sK[4 * fg + s][i_key];
+    fq[s] = sQ[4 * fg + s][i_key];
+    fkb[s] = -sKB[4 * fg + s][i_key];
+  }
+  aq = mma16(*reinterpret_cast<const f4*>(&xA1[fr][4 * fg]), fk, aq);
+  ak = mma16(*reinterpret_cast<const f4*>(&xB1[fr][4 * fg]), fq, ak);
+  ak = mma16(*reinterpret_cast<const f4*>(&xB2[fr][4 * fg]), fkb, ak);
+  ab = mma16(*reinterpret_cast<const f4*>(&xC2[fr][4 * fg]), fk, ab);
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    const int t = 4 * fg + v;
+    if (t < n) {
+      float* pp = part + ((bT + t0 + t) * nv + h) * PW;
+      pp[i_key] = aq[v];
+      pp[D + i_key] = ak[v] - sBe[t] * ab[v];
+    }
+  }
+  if (tid == 0) {  // g dg by the carried inner product, dbeta
+    float phi = sAnc + sOd[n - 1];
+    for (int t = n - 1; t >= 0; t--) {
+      float* pp = part + ((bT + t0 + t) * nv + h) * PW;
+      pp[2 * D] = phi - sDvb[t];
+      pp[2 * D + 1] = sDb[t];
+      if (t > 0) phi = phi - sDvb[t] + sOd[t - 1];
+    }
+  }
+}
+
 // Sums the partials (column blocks, then the rep v-heads of the k-head, in
 // fixed order) and applies the chain rule of the normalisations and gates:
 // one 16-lane group per (token, k-head).
 //   dq = invq dq^ - q (dq^.q) invq / (|q|^2 + eps), likewise dk;
-//   da = dg g (-exp(A_log)) sigmoid(a + dt_bias);  db = dbeta beta (1 - beta)
+//   da = (g dg) (-exp(A_log)) sigmoid(a + dt_bias);  db = dbeta beta (1 - beta)
 template <int DK>
 __global__ __launch_bounds__(256) void chain(int B, int T, int nk, int nv, int ncb, int cdim,
                                              const float* __restrict__ part,
@@ -645,7 +979,6 @@ __global__ __launch_bounds__(256) void chain(int B, int T, int nk, int nv, int n
                                              const float* __restrict__ a,
                                              const float* __restrict__ A_log,
                                              const float* __restrict__ dt_bias,
-                                             const float* __restrict__ gg,
                                              const float* __restrict__ be,
                                              float* __restrict__ dcq, float* __restrict__ da,
                                              float* __restrict__ db) {
@@ -676,8 +1009,8 @@ __global__ __launch_bounds__(256) void chain(int B, int T, int nk, int nv, int n
     }
     if (l16 == 0) {
       const size_t i = bt * nv + h;
-      const float gt = gg[i], bt_ = be[i];
-      da[i] = sgd * gt * (-expf(A_log[h])) * sigm(a[i] + dt_bias[h]);
+      const float bt_ = be[i];
+      da[i] = sgd * (-expf(A_log[h])) * sigm(a[i] + dt_bias[h]);
       db[i] = sbd * bt_ * (1.0f - bt_);
     }
   }
@@ -719,11 +1052,14 @@ static unsigned grid4(size_t n4) {
   return (unsigned)(b > 8192 ? 8192 : (b < 1 ? 1 : b));
 }
 
+bool gdn_two_pass(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
+
 size_t gdn_ckpt_floats(int B, int T, int nv, int dk, int dv) {
   return (size_t)B * nv * ((T + gdnk::TT - 1) / gdnk::TT) * dv * dk;
 }
 size_t gdn_partial_floats(int B, int T, int nv, int dk, int dv) {
-  return (size_t)(dv / gdnk::CB) * B * T * nv * (2 * dk + 2);
+  const size_t ncb = gdn_two_pass(dk, dv) ? 1 : dv / gdnk::CB;
+  return ncb * B * T * nv * (2 * dk + 2);
 }
 
 hipError_t gdn_launch_forward(const GdnArgs& p, hipStream_t st) {
@@ -745,10 +1081,10 @@ hipError_t gdn_launch_forward(const GdnArgs& p, hipStream_t st) {
   const dim3 gs(p.B * p.nv * (p.dv / gdnk::CB));
   if (p.dk == 128)
     hipLaunchKernelGGL(gdnk::fwd_seq<128>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
-                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt);
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt, p.kv);
   else
     hipLaunchKernelGGL(gdnk::fwd_seq<64>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
-                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt);
+                       p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.ckpt, p.kv);
   const int BTH = BT * p.nv;
   const unsigned gr = (unsigned)(((size_t)BTH + 15) / 16);
   if (p.dv == 128)
@@ -771,21 +1107,40 @@ hipError_t gdn_launch_backward(const GdnArgs& p, hipStream_t st) {
     hipLaunchKernelGGL(gdnk::rms_bwd<1>, dim3(gr), dim3(256), 0, st, BTH, p.nv, p.rms_eps, p.o,
                        p.z, p.norm, p.dout, p.dz, p.dobuf);
   const dim3 gs(p.B * p.nv * (p.dv / gdnk::CB));
-  if (p.dk == 128)
+  const int nblk = (p.T + gdnk::TT - 1) / gdnk::TT;
+  int ncb = p.dv / gdnk::CB;  // partials per (token, head) summed by chain
+  if (gdn_two_pass(p.dk, p.dv)) {
+    ncb = 1;
+    const dim3 gb(p.B * p.nv * nblk);
+    if (p.dk == 128) {
+      hipLaunchKernelGGL(gdnk::bwd_scan<128>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                         p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.gend, p.du, p.anc,
+                         p.dcq);
+      hipLaunchKernelGGL(gdnk::bwd_blk<128>, gb, dim3(512), 0, st, p.B, p.T, p.nk, p.nv, cdim,
+                         p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.dobuf, p.ckpt, p.gend, p.du, p.kv,
+                         p.anc, p.part);
+    } else {
+      hipLaunchKernelGGL(gdnk::bwd_scan<64>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
+                         p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.gend, p.du, p.anc,
+                         p.dcq);
+      hipLaunchKernelGGL(gdnk::bwd_blk<64>, gb, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, cdim,
+                         p.qh, p.kh, p.cq, p.g, p.beta, p.o, p.dobuf, p.ckpt, p.gend, p.du, p.kv,
+                         p.anc, p.part);
+    }
+  } else if (p.dk == 128) {
     hipLaunchKernelGGL(gdnk::bwd_seq<128>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
                        p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.part, p.dcq);
-  else
+  } else {
     hipLaunchKernelGGL(gdnk::bwd_seq<64>, gs, dim3(256), 0, st, p.B, p.T, p.nk, p.nv, p.dv, cdim,
                        p.qh, p.kh, p.cq, p.g, p.beta, p.dobuf, p.ckpt, p.part, p.dcq);
+  }
   const unsigned gq = (unsigned)(((size_t)BT * p.nk + 15) / 16);
-  const int ncb = p.dv / gdnk::CB;
   if (p.dk == 128)
     hipLaunchKernelGGL(gdnk::chain<128>, dim3(gq), dim3(256), 0, st, p.B, p.T, p.nk, p.nv, ncb,
-                       cdim, p.part, p.cq, p.a, p.A_log, p.dt_bias, p.g, p.beta, p.dcq, p.da,
-                       p.db);
+                       cdim, p.part, p.cq, p.a, p.A_log, p.dt_bias, p.beta, p.dcq, p.da, p.db);
   else
     hipLaunchKernelGGL(gdnk::chain<64>, dim3(gq), dim3(256), 0, st, p.B, p.T, p.nk, p.nv, ncb, cdim,
-                       p.part, p.cq, p.a, p.A_log, p.dt_bias, p.g, p.beta, p.dcq, p.da, p.db);
+                       p.part, p.cq, p.a, p.A_log, p.dt_bias, p.beta, p.dcq, p.da, p.db);
   if (p.kk == 4)
     hipLaunchKernelGGL((gdnk::conv_bwd_t<4, 8>),
                        dim3(grid4((size_t)p.B * ((p.T + 7) / 8) * cdim / 4)), dim3(256), 0, st,
