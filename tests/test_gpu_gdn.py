@@ -100,3 +100,22 @@ def test_gdn_full_size_sampled_groups(hip):
     out, g = _run(hip, cfg, d)
     for grp in (0, 11):
         _check_window(cfg, d, 1, out, g, group=grp)
+
+
+@pytest.mark.parametrize("mode", ["no_decay", "full_decay"])
+def test_gdn_extreme_decays(hip, mode):
+    """The decay at the ends of its range, dk = dv = 64 (the two-pass backward):
+    g = 1 on every token (exp(A_log) ~ 1e-26), and every third token with
+    softplus argument 60 and exp(A_log) = e^3, so that g = exp(-1205) is 0 in
+    fp32 (the state forgets everything) while the other tokens keep N(0, 1)."""
+    cfg = synth.gdn_config(1, 2, 64, 64, kk=4, seed=11)
+    d = synth.gdn_inputs(2, 50, cfg, seed=12)
+    if mode == "no_decay":
+        cfg["A_log"] = np.full(2, -60.0, np.float32)
+    else:
+        cfg["A_log"] = np.full(2, 3.0, np.float32)
+        d["a"][:, ::3, :] = 60.0 - cfg["dt_bias"][None, None, :]
+    print(f"[gdn] extreme decays: {mode}", flush=True)
+    out, g = _run(hip, cfg, d)
+    for b in range(2):
+        _check_window(cfg, d, b, out, g)
