@@ -770,13 +770,32 @@ __global__ __launch_bounds__(256) void pack_bf16_t(int K, int N, const float* __
 }
 
 // Sum S split-K partials [S][M][N] (leading dim N) into C (ldc), with beta/epilogue.
+// The partials are added in slice order; each thread issues the loads of up
+// to eight slices before the first add, so that enough reads are in flight to
+// cover the memory latency (one load per add leaves the pass latency bound).
 __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const float* __restrict__ P,
                                                      float* __restrict__ C, int ldc, float beta,
                                                      int epi, const float* __restrict__ aux) {
-  const size_t n4 = (size_t)M * N / 4;
+  const size_t n4 = (size_t)M * N / 4, zs = (size_t)M * N / 4;
+  const f4* __restrict__ P4 = reinterpret_cast<const f4*>(P);
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    f4 s = reinterpret_cast<const f4*>(P)[i];
-    for (int z = 1; z < S; z++) s += reinterpret_cast<const f4*>(P + (size_t)z * M * N)[i];
+    f4 s = P4[i];
+    int z = 1;
+    for (; z + 8 <= S; z += 8) {
+      f4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) x[u] = P4[(size_t)(z + u) * zs + i];
+#pragma unroll
+      for (int u = 0; u < 8; u++) s += x[u];
+    }
+    for (; z + 4 <= S; z += 4) {
+      f4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) x[u] = P4[(size_t)(z + u) * zs + i];
+#pragma unroll
+      for (int u = 0; u < 4; u++) s += x[u];
+    }
+    for (; z < S; z++) s += P4[(size_t)z * zs + i];
     const size_t e = i * 4;
     const int row = (int)(e / N), col = (int)(e % N);
     const size_t o = (size_t)row * ldc + col;
