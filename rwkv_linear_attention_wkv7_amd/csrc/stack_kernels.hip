@@ -533,14 +533,30 @@ __global__ __launch_bounds__(256) void emb_count(int R, int V, const int* __rest
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p < R && (unsigned)tok[p] < (unsigned)V) atomicAdd(&count[tok[p]], 1);
 }
-// 2) exclusive scan of the counts (one workgroup of 1024 threads)
+// 2) exclusive scan of the counts (one workgroup of 1024 threads, each a
+// contiguous range; with V a multiple of 4 and at most 64 per thread the
+// range is held in registers, read and written as int4, all loads in flight
+// together)
 __global__ __launch_bounds__(1024) void emb_scan(int V, const int* __restrict__ count,
                                                  int* __restrict__ off) {
   __shared__ int sm[1024];
+  constexpr int MAXQ = 16;  // int4 per thread in the register path
   const int per = (V + 1023) / 1024;
   const int b = threadIdx.x * per, e = min(V, b + per);
+  const bool vec = V % 4 == 0 && per % 4 == 0 && per <= 4 * MAXQ;  // the same for every thread
+  int4 cv[MAXQ];
   int s = 0;
-  for (int i = b; i < e; i++) s += count[i];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      const int i = b + 4 * q;
+      cv[q] = 4 * q < per && i < e ? *reinterpret_cast<const int4*>(count + i) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) s += (cv[q].x + cv[q].y) + (cv[q].z + cv[q].w);
+  } else {
+    for (int i = b; i < e; i++) s += count[i];
+  }
   sm[threadIdx.x] = s;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
@@ -550,22 +566,52 @@ __global__ __launch_bounds__(1024) void emb_scan(int V, const int* __restrict__ 
     __syncthreads();
   }
   int run = sm[threadIdx.x] - s;  // exclusive prefix of this thread's range
-  for (int i = b; i < e; i++) {
-    off[i] = run;
-    run += count[i];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < MAXQ; q++) {
+      const int i = b + 4 * q;
+      if (4 * q < per && i < e) {
+        int4 o;
+        o.x = run; run += cv[q].x;
+        o.y = run; run += cv[q].y;
+        o.z = run; run += cv[q].z;
+        o.w = run; run += cv[q].w;
+        *reinterpret_cast<int4*>(off + i) = o;
+      }
+    }
+  } else {
+    for (int i = b; i < e; i++) {
+      off[i] = run;
+      run += count[i];
+    }
   }
 }
 // 3) position p goes to slot off[tok[p]] + #{q < p : tok[q] == tok[p]} (stable);
-// positions with an id outside [0, V) are not placed (no gradient row)
+// positions with an id outside [0, V) are not placed (no gradient row).  The
+// earlier ids are staged through LDS 256 at a time and read as broadcasts:
+// whole tiles before the workgroup's own count in full, the workgroup's own
+// tile up to the position.
 __global__ __launch_bounds__(256) void emb_place(int R, int V, const int* __restrict__ tok,
                                                  const int* __restrict__ off, int* __restrict__ perm) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= R) return;
-  const int v = tok[p];
-  if ((unsigned)v >= (unsigned)V) return;
+  __shared__ __attribute__((aligned(16))) int tile[256];
+  const int p0 = blockIdx.x * 256, tid = threadIdx.x, p = p0 + tid;
+  const int v = p < R ? tok[p] : -1;
   int rank = 0;
-  for (int q = 0; q < p; q++) rank += tok[q] == v;
-  perm[off[v] + rank] = p;
+  for (int q0 = 0; q0 <= p0; q0 += 256) {  // the same trip count for the whole workgroup
+    __syncthreads();                        // the previous tile consumed
+    tile[tid] = q0 + tid < R ? tok[q0 + tid] : -1;
+    __syncthreads();
+    if (q0 < p0) {
+#pragma unroll 8
+      for (int i = 0; i < 256; i += 4) {
+        const int4 x = *reinterpret_cast<const int4*>(&tile[i]);
+        rank += (x.x == v) + (x.y == v) + (x.z == v) + (x.w == v);
+      }
+    } else {
+      for (int i = 0; i < tid; i++) rank += tile[i] == v;
+    }
+  }
+  if (p < R && (unsigned)v < (unsigned)V) perm[off[v] + rank] = p;
 }
 // 4) demb[v] = sum of dx rows of its positions in position order; one wave per row
 __global__ __launch_bounds__(256) void emb_rows(int V, int C, const int* __restrict__ count,

@@ -387,36 +387,40 @@ __global__ __launch_bounds__(256) void shift_bwd(TmBwd p) {
   write_partials<6>(q, p.part_shift, nblk, blk, p.C, cb * N);
 }
 
-// out[v][c] = sum_blk part[v][blk][c], fixed order.  A workgroup owns 64
-// columns of one vector: lane = column, each of the 16 waves sums the rows
-// b = w, w + 16, ... (four loads in flight), and wave 0 adds the 16 wave sums
-// in wave order.
-constexpr int RP_WAVES = 16;
+// out[v][c] = sum_blk part[v][blk][c], fixed order.  A workgroup owns 16
+// columns of one vector and splits the rows over 64 row groups (lane l of
+// wave w: column l % 16, group 4 w + l / 16; group g sums rows g, g + 64, ...
+// with eight loads in flight into four accumulators); thread c < 16 then
+// adds the 64 group sums in group order.  Narrow workgroups spread a sum of
+// a few MB over enough CUs that per-CU load latency does not set its time.
+constexpr int RP_WAVES = 16, RP_COLS = 16, RP_GROUPS = RP_WAVES * 64 / RP_COLS;
 __global__ __launch_bounds__(64 * RP_WAVES) void reduce_partials(const float* __restrict__ part,
                                                                  int nblk, int C, VecOut outs) {
-  const int v = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int v = blockIdx.y, tid = threadIdx.x;
   float* o = outs.p[v];
   if (!o) return;
-  const int c = blockIdx.x * 64 + lane;
+  const int cl = tid % RP_COLS, grp = tid / RP_COLS;
+  const int c = blockIdx.x * RP_COLS + cl;
   const int cc = c < C ? c : C - 1;
   const float* src = part + (size_t)v * nblk * C + cc;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  int b = w;
-  for (; b + 3 * RP_WAVES < nblk; b += 4 * RP_WAVES) {
-    s0 += src[(size_t)b * C];
-    s1 += src[(size_t)(b + RP_WAVES) * C];
-    s2 += src[(size_t)(b + 2 * RP_WAVES) * C];
-    s3 += src[(size_t)(b + 3 * RP_WAVES) * C];
-  }
-  for (; b < nblk; b += RP_WAVES) s0 += src[(size_t)b * C];
-  __shared__ float red[RP_WAVES][64];
-  red[w][lane] = (s0 + s1) + (s2 + s3);
-  __syncthreads();
-  if (w == 0 && c < C) {
-    float s = 0.f;
+  float sa[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;  // loads in flight per lane
+  int b = grp;
+  for (; b + (U - 1) * RP_GROUPS < nblk; b += U * RP_GROUPS) {
+    float x[U];
 #pragma unroll
-    for (int i = 0; i < RP_WAVES; i++) s += red[i][lane];
-    o[c] = s;
+    for (int u = 0; u < U; u++) x[u] = src[(size_t)(b + u * RP_GROUPS) * C];
+#pragma unroll
+    for (int u = 0; u < U; u++) sa[u & 3] += x[u];
+  }
+  for (; b < nblk; b += RP_GROUPS) sa[0] += src[(size_t)b * C];
+  __shared__ float red[RP_GROUPS][RP_COLS];
+  red[grp][cl] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+  __syncthreads();
+  if (tid < RP_COLS && c < C) {
+    float sum = 0.f;
+    for (int i = 0; i < RP_GROUPS; i++) sum += red[i][tid];
+    o[c] = sum;
   }
 }
 
@@ -461,7 +465,7 @@ hipError_t tm_launch_shift_bwd(const TmBwd& p, hipStream_t st) {
 hipError_t tm_launch_reduce(const float* part, int nvec, int nblk, int C, const VecOut& outs,
                             hipStream_t st) {
   if (nvec < 1 || nvec > 8 || C < 1 || nblk < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tmk::reduce_partials, dim3((C + 63) / 64, nvec), dim3(64 * tmk::RP_WAVES), 0,
-                     st, part, nblk, C, outs);
+  hipLaunchKernelGGL(tmk::reduce_partials, dim3((C + tmk::RP_COLS - 1) / tmk::RP_COLS, nvec),
+                     dim3(64 * tmk::RP_WAVES), 0, st, part, nblk, C, outs);
   return hipGetLastError();
 }
