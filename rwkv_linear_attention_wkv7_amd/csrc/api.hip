@@ -1222,6 +1222,11 @@ struct TrainBufs {
   TmBwdBufs tb;
   float* pack = nullptr;  // bf16 operand copies of the GEMMs (gemm_dtype == WKV7_BF16)
   size_t pack_bytes = 0;
+  // bf16 copy [BT][F] of the channel-mix hidden activation (forward) or its
+  // gradient (backward), written by the producing product and read as the
+  // next product's A (gemm_dtype == WKV7_BF16; one buffer, reused per block
+  // on the caller's stream)
+  __bf16* act16 = nullptr;
   // attention blocks (n_attn > 0): activations of each (or one reused set)
   // and the backward's buffers
   struct AttnActs {
@@ -1276,6 +1281,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   if (cfg->gemm_dtype == WKV7_BF16) {
     t.pack_bytes = train_pack_bytes(cfg, BT);
     t.pack = c.take(t.pack_bytes / sizeof(float));
+    t.act16 = reinterpret_cast<__bf16*>(c.take(BT * cfg->F / 2));
   }
   const bool keep = cfg->train_recompute == 0;
   t.act.resize(keep ? L : 1);
@@ -1445,7 +1451,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
                         st, false, 0.f, prec, false, true, xin));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
-    HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "cm key");
+    HIPCHK(gemm_run_x(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1,
+                      nullptr, st, nullptr, t.act16), "cm key");
     return WKV7_OK;
   };
   // attention block i's forward from xin (its output is x1 + ka Wv)
@@ -1466,7 +1473,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     HIPCHK(gemm_run(prec, false, false, BT, C, C, a.y, C, ab.Wo, C, a.x1, C, 0.f, EPI_ADD, xin, 1, nullptr, st), "o proj");
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, ab.ln2_w, ab.ln2_b, a.h2, nullptr, nullptr, st), "attn ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, ab.cm_mu_k, a.sh, nullptr, st), "attn cm shift");
-    HIPCHK(gemm_run(prec, false, false, BT, F, C, a.sh, C, ab.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1, nullptr, st), "attn cm key");
+    HIPCHK(gemm_run_x(prec, false, false, BT, F, C, a.sh, C, ab.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1,
+                      nullptr, st, nullptr, t.act16), "attn cm key");
     return WKV7_OK;
   };
   const auto order = block_order(L, cfg->n_attn);
@@ -1489,7 +1497,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
       x1 = a.x1, ka = a.ka, Wv = M->attn[i].cm_Wv;
     }
     float* xo = bin(pos + 1);  // x1 + the channel mix
-    HIPCHK(gemm_run(prec, false, false, BT, C, F, ka, F, Wv, C, xo, C, 0.f, EPI_ADD, x1, 1, nullptr, st), "cm value");
+    HIPCHK(gemm_run_x(prec, false, false, BT, C, F, ka, F, Wv, C, xo, C, 0.f, EPI_ADD, x1, 1, nullptr, st,
+                      t.act16, nullptr), "cm value");
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(NB), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
@@ -1532,13 +1541,15 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     TrainBufs::AttnActs& a = t.aact[keep ? i : 0];
     if (!keep) CHK(attn_fwd(i, bin(pos), a));  // recompute this block's forward from its input
     // channel-mix backward (as in the RWKV-7 blocks)
-    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, ab.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "attn dfk");
+    HIPCHK(gemm_run_x(prec, false, true, BT, F, C, t.dx, C, ab.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1,
+                      nullptr, st, nullptr, t.act16), "attn dfk");
     HIPCHK(fork_here(), "backward fork");
     HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, ga.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                     splitk_for(F, C, BT), t.splitk, ss), "attn dWv");
     HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, ga.cm_Wk, F, 0.f, EPI_NONE, nullptr,
                     splitk_for(C, F, BT), t.splitk, ss), "attn dWk");
-    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, ab.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "attn dsh");
+    HIPCHK(gemm_run_x(prec, false, true, BT, C, F, t.dfk, F, ab.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1,
+                      nullptr, st, t.act16, nullptr), "attn dsh");
     HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, nullptr, ab.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "attn cm shift bwd");
     {
       VecOut o = {{ga.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
@@ -1582,13 +1593,15 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     BlockActs& a = t.act[keep ? l : 0];
     if (!keep) CHK(block_fwd(l, bin(pos), a));  // recompute this block's forward from its input
     // channel-mix backward
-    HIPCHK(gemm_run(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1, nullptr, st), "dfk");
+    HIPCHK(gemm_run_x(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1,
+                      nullptr, st, nullptr, t.act16), "dfk");
     HIPCHK(fork_here(), "backward fork");  // t.dx and t.dfk complete
     HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                         splitk_for(F, C, BT), t.splitk, ss), "dWv");
     HIPCHK(gemm_run(prec, true, false, C, F, BT, a.sh, C, t.dfk, F, gb.cm_Wk, F, 0.f, EPI_NONE, nullptr,
                         splitk_for(C, F, BT), t.splitk, ss), "dWk");
-    HIPCHK(gemm_run(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dsh");
+    HIPCHK(gemm_run_x(prec, false, true, BT, C, F, t.dfk, F, bl.cm_Wk, F, t.dsh, C, 0.f, EPI_NONE, nullptr, 1,
+                      nullptr, st, t.act16, nullptr), "dsh");
     HIPCHK(stk_launch_cm_shift_bwd(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, t.dsh, t.dh, nullptr, t.part_cm, st), "cm shift bwd");
     {
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};

@@ -56,6 +56,7 @@ __device__ __forceinline__ void store_acc(const GemmProblem& P, bool split, floa
   const float beta = split ? 0.f : P.beta;
   const int epi = split ? EPI_NONE : P.epi;
   const float* __restrict__ aux = split ? nullptr : P.aux;
+  __bf16* __restrict__ c16 = split ? nullptr : P.C16;
 #pragma unroll
   for (int i = 0; i < TI; i++) {
 #pragma unroll
@@ -71,6 +72,7 @@ __device__ __forceinline__ void store_acc(const GemmProblem& P, bool split, floa
         if (beta != 0.f) x += beta * C[o];
         x = apply_epi(x, epi, aux ? aux[(size_t)row * P.ldc + col] : 0.f);
         C[o] = x;
+        if (c16) c16[(size_t)row * N + col] = (__bf16)x;
       }
     }
   }
@@ -702,6 +704,7 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
   const float beta = split ? 0.f : P.beta;
   const int epi = split ? EPI_NONE : P.epi;
   const float* __restrict__ aux = split ? nullptr : P.aux;
+  __bf16* __restrict__ c16 = split ? nullptr : P.C16;
   const int col = n0 + wb + 4 * i;
 #pragma unroll
   for (int a = 0; a < FA; a++) {
@@ -718,6 +721,7 @@ __global__ __launch_bounds__(TJ == 8 ? 512 : 256) void gemm_dma(GemmBatch batch,
         for (int t = 0; t < 4; t++) x[t] = apply_epi(x[t], epi, ax[t]);
       }
       *reinterpret_cast<f4*>(o) = x;
+      if (c16) *reinterpret_cast<bf16x4*>(c16 + (size_t)row * P.N + col) = __builtin_convertvector(x, bf16x4);
     }
   }
 }
@@ -775,7 +779,8 @@ __global__ __launch_bounds__(256) void pack_bf16_t(int K, int N, const float* __
 // cover the memory latency (one load per add leaves the pass latency bound).
 __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const float* __restrict__ P,
                                                      float* __restrict__ C, int ldc, float beta,
-                                                     int epi, const float* __restrict__ aux) {
+                                                     int epi, const float* __restrict__ aux,
+                                                     __bf16* __restrict__ c16) {
   const size_t n4 = (size_t)M * N / 4, zs = (size_t)M * N / 4;
   const f4* __restrict__ P4 = reinterpret_cast<const f4*>(P);
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
@@ -803,7 +808,9 @@ __global__ __launch_bounds__(256) void splitk_reduce(int M, int N, int S, const 
     for (int c = 0; c < 4; c++) {
       float x = s[c];
       if (beta != 0.f) x += beta * C[o + c];
-      C[o + c] = apply_epi(x, epi, aux ? aux[o + c] : 0.f);
+      x = apply_epi(x, epi, aux ? aux[o + c] : 0.f);
+      C[o + c] = x;
+      if (c16) c16[e + c] = (__bf16)x;
     }
   }
 }
@@ -902,13 +909,18 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
   char* cur = tl_pack;
   for (int i = 0; i < b.count; i++) {
     const GemmProblem& q = b.p[i];
-    __bf16* pa = reinterpret_cast<__bf16*>(cur);
+    const __bf16* pa = q.A16;  // an A rounded to bf16 by its producer
+    if (!pa) {
+      __bf16* pw = reinterpret_cast<__bf16*>(cur);
+      pa = pw;
+      const size_t n8 = (size_t)q.M * q.K / 8;
+      hipLaunchKernelGGL(pack_bf16, dim3((int)std::min<size_t>((n8 + 255) / 256, 4096)), dim3(256), 0,
+                         st, q.M, q.K, q.A, q.lda, pw);
+    }
     cur += align256((size_t)q.M * q.K * 2);
     __bf16* pbm = reinterpret_cast<__bf16*>(cur);
     cur += align256((size_t)q.N * q.K * 2);
     auto blocks = [](size_t n8) { return (int)std::min<size_t>((n8 + 255) / 256, 4096); };
-    hipLaunchKernelGGL(pack_bf16, dim3(blocks((size_t)q.M * q.K / 8)), dim3(256), 0, st, q.M, q.K, q.A,
-                       q.lda, pa);
     if (transB)
       hipLaunchKernelGGL(pack_bf16, dim3(blocks((size_t)q.N * q.K / 8)), dim3(256), 0, st, q.N, q.K,
                          q.B, q.ldb, pbm);
@@ -1046,14 +1058,15 @@ hipError_t gemm_run_partials(int prec, int M, int N, int K, const float* A, int 
 
 // C = epi(op(A) op(B) + beta C).  ws (may be NULL when split == 1) holds
 // split*M*N floats of split-K partials.
-hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
-                    int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
-                    const float* aux, int split, float* ws, hipStream_t st) {
+hipError_t gemm_run_x(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
+                      int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                      const float* aux, int split, float* ws, hipStream_t st, const __bf16* A16,
+                      __bf16* C16) {
   using namespace gemmk;
   if (M <= 0 || N <= 0) return hipSuccess;
   GemmBatch b;
   b.count = 1;
-  b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, nullptr};
+  b.p[0] = GemmProblem{M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, nullptr, C16, A16};
   if (split > 1 && ws != nullptr) split = std::min(split, gemm_splitk_slices(prec, M, N, K));
   if (split <= 1 || ws == nullptr) return dispatch(prec, transA, transB, b, 1, K, K, st);
   int kslice = (K + split - 1) / split;
@@ -1065,6 +1078,13 @@ hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, con
   const size_t n4 = (size_t)M * N / 4;
   int blocks = (int)((n4 + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, st, M, N, S, ws, C, ldc, beta, epi, aux);
+  hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, st, M, N, S, ws, C, ldc, beta, epi, aux, C16);
   return hipGetLastError();
+}
+
+hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
+                    int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                    const float* aux, int split, float* ws, hipStream_t st) {
+  return gemm_run_x(prec, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, beta, epi, aux, split,
+                    ws, st, nullptr, nullptr);
 }

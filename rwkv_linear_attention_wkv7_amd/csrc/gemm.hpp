@@ -28,6 +28,12 @@ struct GemmProblem {
   int epi;
   const float* aux;
   float* part;  // split-K partials (internal)
+  // optional bf16 copy of the result (dense [M][N], rounded to nearest even),
+  // written by every path, for a later product that takes it as its A
+  __bf16* C16 = nullptr;
+  // optional A already rounded to bf16 (dense [M][K], e.g. an earlier C16):
+  // the bf16 matrix-core path then uses it instead of making its own copy
+  const __bf16* A16 = nullptr;
 };
 
 struct GemmBatch {
@@ -44,6 +50,12 @@ int gemm_splitk_slices(int prec, int M, int N, int K);
 hipError_t gemm_run(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
                     int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
                     const float* aux, int split, float* ws, hipStream_t st);
+// gemm_run with the optional bf16 operand A16 and result copy C16 (see
+// GemmProblem); NULL for either is gemm_run.
+hipError_t gemm_run_x(int prec, bool transA, bool transB, int M, int N, int K, const float* A,
+                      int lda, const float* B, int ldb, float* C, int ldc, float beta, int epi,
+                      const float* aux, int split, float* ws, hipStream_t st, const __bf16* A16,
+                      __bf16* C16);
 // The split-K products alone: part[s][M][N] (leading dimension N), K cut
 // into *slices <= split slices of a multiple of 64 (at least 64 each), left
 // for the consumer to add in slice order (no beta, no epilogue).
