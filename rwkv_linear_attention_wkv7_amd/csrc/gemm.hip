@@ -1024,17 +1024,21 @@ hipError_t gemm_batch(int prec, bool transA, bool transB, const GemmBatch& b, hi
   return gemmk::dispatch(prec, transA, transB, b, b.count, maxK, maxK, st);
 }
 
-// K slices that fill the chip: one workgroup per CU for the 256-row
-// direct-to-LDS bf16 tiles, two for the 128x128 tiles; each slice at least
-// 256 deep.
+// K slices for a product split along K (the weight gradients X^T dY, which run
+// beside the rest of the backward on a second stream): about 64 workgroups
+// of the 256-row direct-to-LDS bf16 tiles, 256 of the 128x128 ones, each
+// slice at least 256 deep.  Fewer slices than one workgroup per CU measured
+// faster in the training step and the online segment (less partial traffic,
+// and the products leave more CUs to the other stream); far fewer leave
+// single long products on the critical path.
 int gemm_splitk_slices(int prec, int M, int N, int K) {
   long want;
   if (prec == GEMM_BF16 && M % 256 == 0 && N % 128 == 0 && K % (2 * gemmk::dmak::BK) == 0) {
     const long tiles = (long)(M / 256) * (N % 256 == 0 ? N / 256 : N / 128);
-    want = (256 + tiles - 1) / tiles;
+    want = (64 + tiles - 1) / tiles;
   } else {
     const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-    want = (512 + tiles - 1) / tiles;
+    want = (256 + tiles - 1) / tiles;
   }
   want = std::min(want, (long)(K / 256));
   return want < 1 ? 1 : (int)want;
