@@ -70,6 +70,9 @@ def _check_window(cfg, d, b, out, g, ftol=1e-4, gtol=1e-3, group=None):
     (128, 128, 1, 2, 40, 4),    # head size 128
     (128, 64, 2, 2, 16, 3),     # exactly one block, dk != dv, one v-head per k-head
     (64, 128, 1, 3, 5, 1),      # shorter than a block, no convolution history
+    (64, 64, 1, 2, 7, 4),       # two-pass backward inside one partial block
+    (128, 128, 1, 1, 1, 4),     # one token
+    (64, 64, 2, 2, 32, 2),      # two whole blocks, no ragged tail
 ])
 def test_gdn_parity_small(hip, dk, dv, nk, nv, T, kk):
     cfg = synth.gdn_config(nk, nv, dk, dv, kk=kk, seed=dk + dv + T)
