@@ -1227,6 +1227,9 @@ struct TrainBufs {
   // next product's A (gemm_dtype == WKV7_BF16; one buffer, reused per block
   // on the caller's stream)
   __bf16* act16 = nullptr;
+  // bf16 copy [BT][V] of dlogits written by the cross-entropy kernel, the A of
+  // the head's input-gradient product (gemm_dtype == WKV7_BF16)
+  __bf16* logits16 = nullptr;
   // attention blocks (n_attn > 0): activations of each (or one reused set)
   // and the backward's buffers
   struct AttnActs {
@@ -1250,7 +1253,7 @@ size_t train_pack_bytes(const rwkv7_config* cfg, size_t BT) {
     up += gemm_pack_need(M, C, d);
   }
   best = std::max({best, down, up, gemm_pack_need(M, F, C), gemm_pack_need(M, C, F),
-                   gemm_pack_need(M, V, C), gemm_pack_need(M, C, V)});
+                   gemm_pack_need(M, V, C), gemm_pack_need(M, C, V), gemm_pack_need_b(M, C, V)});
   return best;
 }
 
@@ -1282,6 +1285,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
     t.pack_bytes = train_pack_bytes(cfg, BT);
     t.pack = c.take(t.pack_bytes / sizeof(float));
     t.act16 = reinterpret_cast<__bf16*>(c.take(BT * cfg->F / 2));
+    t.logits16 = reinterpret_cast<__bf16*>(c.take((BT * cfg->V + 1) / 2));
   }
   const bool keep = cfg->train_recompute == 0;
   t.act.resize(keep ? L : 1);
@@ -1502,7 +1506,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
   }
   HIPCHK(stk_launch_layernorm(BT, C, bin(NB), M->ln_out_w, M->ln_out_b, t.h, nullptr, nullptr, st), "ln_out");
   HIPCHK(gemm_run(prec, false, false, BT, V, C, t.h, C, M->head, V, t.logits, V, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "head");
-  HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, t.n_valid, st), "cross-entropy");
+  HIPCHK(stk_launch_ce(BT, V, t.logits, targets, t.loss_row, loss, t.n_valid, st, t.logits16), "cross-entropy");
 
   // ---------------- backward
   // Weight gradients run on the side stream (see tm_backward_impl): here the
@@ -1523,7 +1527,8 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     }
   } join{sd, st};
   HIPCHK(fork_here(), "backward fork");
-  HIPCHK(gemm_run(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1, nullptr, st), "dh");
+  HIPCHK(gemm_run_x(prec, false, true, BT, C, V, t.logits, V, M->head, V, t.dh, C, 0.f, EPI_NONE, nullptr, 1,
+                    nullptr, st, t.logits16, nullptr), "dh");
   HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
                       splitk_for(C, V, BT), t.splitk, ss), "dhead");
   HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(NB), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");

@@ -900,7 +900,8 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
                              hipStream_t st) {
   size_t need = 0;
   for (int i = 0; i < b.count; i++) {
-    const size_t n = gemm_pack_need(b.p[i].M, b.p[i].N, b.p[i].K);
+    const GemmProblem& q = b.p[i];
+    const size_t n = q.A16 ? gemm_pack_need_b(q.M, q.N, q.K) : gemm_pack_need(q.M, q.N, q.K);
     if (n == 0) return hipErrorNotSupported;
     need += n;
   }
@@ -909,15 +910,15 @@ hipError_t launch_dma_packed(const GemmBatch& b, bool transB, int tj, int gz, in
   char* cur = tl_pack;
   for (int i = 0; i < b.count; i++) {
     const GemmProblem& q = b.p[i];
-    const __bf16* pa = q.A16;  // an A rounded to bf16 by its producer
+    const __bf16* pa = q.A16;  // an A rounded to bf16 by its producer: no copy, no arena
     if (!pa) {
       __bf16* pw = reinterpret_cast<__bf16*>(cur);
       pa = pw;
       const size_t n8 = (size_t)q.M * q.K / 8;
       hipLaunchKernelGGL(pack_bf16, dim3((int)std::min<size_t>((n8 + 255) / 256, 4096)), dim3(256), 0,
                          st, q.M, q.K, q.A, q.lda, pw);
+      cur += align256((size_t)q.M * q.K * 2);
     }
-    cur += align256((size_t)q.M * q.K * 2);
     __bf16* pbm = reinterpret_cast<__bf16*>(cur);
     cur += align256((size_t)q.N * q.K * 2);
     auto blocks = [](size_t n8) { return (int)std::min<size_t>((n8 + 255) / 256, 4096); };
@@ -1004,6 +1005,13 @@ hipError_t dispatch(int prec, bool transA, bool transB, const GemmBatch& b, int 
 }
 
 }  // namespace gemmk
+
+size_t gemm_pack_need_b(int M, int N, int K) {
+  using namespace gemmk;
+  if (M % 256 || N % 128 || K % 64 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if ((size_t)N * K > PACK_MAX_B) return 0;
+  return align256((size_t)N * K * 2);
+}
 
 size_t gemm_pack_need(int M, int N, int K) {
   using namespace gemmk;

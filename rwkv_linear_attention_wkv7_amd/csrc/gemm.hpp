@@ -72,6 +72,8 @@ hipError_t gemm_run_partials(int prec, int M, int N, int K, const float* A, int 
 // workspace; the setting lasts until it is cleared (GemmPackScope), and the
 // GEMMs that use it must run one after another on one stream.
 size_t gemm_pack_need(int M, int N, int K);  // bytes, 0 when the shape does not qualify
+// the same when A comes already rounded (GemmProblem::A16): B's copy alone
+size_t gemm_pack_need_b(int M, int N, int K);
 void gemm_set_pack_arena(void* p, size_t bytes);
 struct GemmPackScope {
   GemmPackScope(void* p, size_t bytes) { gemm_set_pack_arena(p, bytes); }

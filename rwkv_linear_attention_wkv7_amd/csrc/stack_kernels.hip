@@ -396,10 +396,17 @@ __global__ __launch_bounds__(256) void count_valid(int R, int V, const int* __re
 // is exact; each exp(z - max) is an fp32 term in (0, 1], and their sum, its
 // log and so lse are in double (the fullmodel page's fm_k_ce_bwd keeps the
 // normaliser in double).
+// d16 (optional): a bf16 copy of dlogits (dense [R][V], rounded to nearest
+// even) for a later bf16 matrix product.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16(__bf16* d16, size_t e, f4 x) {
+  *reinterpret_cast<bf16x4_t*>(d16 + e) = __builtin_convertvector(x, bf16x4_t);
+}
 __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restrict__ z,
                                                   const int* __restrict__ targets,
                                                   const int* __restrict__ n_valid,
-                                                  float* __restrict__ loss_row) {
+                                                  float* __restrict__ loss_row,
+                                                  __bf16* __restrict__ d16) {
   __shared__ float smx[4];
   __shared__ double ssum[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -407,7 +414,10 @@ __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restric
   const int V4 = V / 4;
   const int tgt = targets[row];
   if ((unsigned)tgt >= (unsigned)V) {  // ignored row (uniform per workgroup)
-    for (int i = tid; i < V4; i += 256) zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = tid; i < V4; i += 256) {
+      zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+      if (d16) st16(d16, (size_t)row * V + 4 * i, f4{0.f, 0.f, 0.f, 0.f});
+    }
     if (tid == 0) loss_row[row] = 0.f;
     return;
   }
@@ -442,6 +452,7 @@ __global__ __launch_bounds__(256) void ce_fwd_bwd(int R, int V, float* __restric
 #pragma unroll
     for (int c = 0; c < 4; c++) p[c] = expf(v[c] - lse) - ((4 * i + c) == tgt ? 1.0f : 0.0f);
     zr[i] = p * inv_n;
+    if (d16) st16(d16, (size_t)row * V + 4 * i, p * inv_n);
   }
   if (tid == 0) loss_row[row] = (float)(lse_d - (double)zt);
 }
@@ -454,7 +465,8 @@ template <int NV4>
 __global__ __launch_bounds__(1024) void ce_fwd_bwd_reg(int R, int V, float* __restrict__ z,
                                                        const int* __restrict__ targets,
                                                        const int* __restrict__ n_valid,
-                                                       float* __restrict__ loss_row) {
+                                                       float* __restrict__ loss_row,
+                                                       __bf16* __restrict__ d16) {
   __shared__ float smx[16];
   __shared__ double ssum[16];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -462,7 +474,10 @@ __global__ __launch_bounds__(1024) void ce_fwd_bwd_reg(int R, int V, float* __re
   const int V4 = V / 4;
   const int tgt = targets[row];
   if ((unsigned)tgt >= (unsigned)V) {  // ignored row (uniform per workgroup)
-    for (int i = tid; i < V4; i += 1024) zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = tid; i < V4; i += 1024) {
+      zr[i] = f4{0.f, 0.f, 0.f, 0.f};
+      if (d16) st16(d16, (size_t)row * V + 4 * i, f4{0.f, 0.f, 0.f, 0.f});
+    }
     if (tid == 0) loss_row[row] = 0.f;
     return;
   }
@@ -501,6 +516,7 @@ __global__ __launch_bounds__(1024) void ce_fwd_bwd_reg(int R, int V, float* __re
 #pragma unroll
       for (int c = 0; c < 4; c++) p[c] = expf(v[i][c] - lse) - ((4 * idx + c) == tgt ? 1.0f : 0.0f);
       zr[idx] = p * inv_n;
+      if (d16) st16(d16, (size_t)row * V + 4 * idx, p * inv_n);
     }
   }
   if (tid == 0) loss_row[row] = (float)(lse_d - (double)zt);
@@ -662,19 +678,19 @@ hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const f
   return hipGetLastError();
 }
 hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
-                         int* n_valid, hipStream_t st) {
+                         int* n_valid, hipStream_t st, __bf16* d16) {
   hipLaunchKernelGGL(stk::count_valid, dim3(1), dim3(256), 0, st, R, V, targets, n_valid);
   const int V4 = V / 4;
   if (V4 >= 1024 && V4 <= 16 * 1024) {  // the row fits in the registers of 1024 threads
     const dim3 g(R), t(1024);
-    if (V4 <= 1024) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<1>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
-    else if (V4 <= 2048) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<2>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
-    else if (V4 <= 4096) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<4>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
-    else if (V4 <= 8192) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<8>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
-    else hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<16>, g, t, 0, st, R, V, z, targets, n_valid, loss_row);
+    if (V4 <= 1024) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<1>, g, t, 0, st, R, V, z, targets, n_valid, loss_row, d16);
+    else if (V4 <= 2048) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<2>, g, t, 0, st, R, V, z, targets, n_valid, loss_row, d16);
+    else if (V4 <= 4096) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<4>, g, t, 0, st, R, V, z, targets, n_valid, loss_row, d16);
+    else if (V4 <= 8192) hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<8>, g, t, 0, st, R, V, z, targets, n_valid, loss_row, d16);
+    else hipLaunchKernelGGL(stk::ce_fwd_bwd_reg<16>, g, t, 0, st, R, V, z, targets, n_valid, loss_row, d16);
   } else {
     hipLaunchKernelGGL(stk::ce_fwd_bwd, dim3(R), dim3(256), 0, st, R, V, z, targets, n_valid,
-                       loss_row);
+                       loss_row, d16);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

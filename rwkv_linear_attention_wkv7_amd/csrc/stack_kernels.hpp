@@ -35,9 +35,10 @@ hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const f
                                    const float* mu, const float* dsh, float* dx, float* dx_prev,
                                    float* part, hipStream_t st);
 // Fused CE over R rows of V logits (in place: dlogits); n_valid: one int of
-// scratch (the count of targets in [0, V)).
+// scratch (the count of targets in [0, V)); d16: NULL or a bf16 copy of
+// dlogits (dense [R][V], V a multiple of 4) for a later bf16 product.
 hipError_t stk_launch_ce(int R, int V, float* z, const int* targets, float* loss_row, float* loss,
-                         int* n_valid, hipStream_t st);
+                         int* n_valid, hipStream_t st, __bf16* d16 = nullptr);
 hipError_t stk_launch_emb_bwd(int R, int V, int C, const int* tok, const float* dx, int* count,
                               int* off, int* perm, float* demb, hipStream_t st);
 hipError_t stk_launch_fill_zero(float* p, size_t n, hipStream_t st);
