@@ -568,7 +568,9 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
                     const float* x_prev, float* v_first, const float* s0, float* sT, float* out,
                     float* x_last, const TmCache& m, hipStream_t st, bool decode = false,
                     float out_beta = 0.f, int prec = GEMM_F32, bool shifted = false,
-                    bool out_proj = true, const float* resid = nullptr) {
+                    bool out_proj = true, const float* resid = nullptr, __bf16* x16 = nullptr) {
+  // x16: NULL or 3 BT C bf16 of scratch for the shift's bf16 copies of xr,
+  // xk, xv, which the r/k/v products then take as their A operands
   const int BT = B * T, C = s->C;
   if (s->layer_id > 0 && (!m.lv || !m.ov))
     return fail(WKV7_EHIP, "internal: activation set without value-residual buffers for layer %d",
@@ -579,6 +581,12 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
   p.x = x; p.x_prev = x_prev;
   p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
   p.xr = m.xr; p.xw = m.xw; p.xk = m.xk; p.xv = m.xv; p.xa = m.xa; p.xg = m.xg; p.x_last = x_last;
+  const bool rkv16 = x16 && !shifted && prec == GEMM_BF16;  // the copies exist only if the shift runs here
+  if (rkv16) {
+    p.xr16 = x16;
+    p.xk16 = x16 + (size_t)BT * C;
+    p.xv16 = x16 + 2 * (size_t)BT * C;
+  }
   p.k = m.k; p.v = m.v; p.ow = m.ow; p.oa = m.oa; p.ov = m.ov;
   p.w0 = W->w0; p.a0 = W->a0; p.v0 = W->v0; p.k_k = W->k_k; p.k_a = W->k_a;
   p.v_first = v_first;
@@ -601,6 +609,11 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     g.p[0] = prob(BT, C, C, m.xr, C, W->Wr, C, m.r, C, EPI_NONE);
     g.p[1] = prob(BT, C, C, m.xk, C, W->Wk, C, m.k, C, EPI_NONE);
     g.p[2] = prob(BT, C, C, m.xv, C, W->Wv, C, m.v, C, EPI_NONE);
+    if (rkv16) {
+      g.p[0].A16 = p.xr16;
+      g.p[1].A16 = p.xk16;
+      g.p[2].A16 = p.xv16;
+    }
     GemmBatch l;
     l.count = 3;
     l.p[0] = prob(BT, s->Dw, C, m.xw, C, W->W1, s->Dw, m.tw, s->Dw, EPI_TANH);
@@ -1224,8 +1237,9 @@ struct TrainBufs {
   size_t pack_bytes = 0;
   // bf16 copy [BT][F] of the channel-mix hidden activation (forward) or its
   // gradient (backward), written by the producing product and read as the
-  // next product's A (gemm_dtype == WKV7_BF16; one buffer, reused per block
-  // on the caller's stream)
+  // next product's A, and before that in each block the time-mix shift's
+  // copies of xr, xk, xv [3][BT][C] (gemm_dtype == WKV7_BF16; one buffer,
+  // reused on the caller's stream)
   __bf16* act16 = nullptr;
   // bf16 copy [BT][V] of dlogits written by the cross-entropy kernel, the A of
   // the head's input-gradient product (gemm_dtype == WKV7_BF16)
@@ -1284,7 +1298,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   if (cfg->gemm_dtype == WKV7_BF16) {
     t.pack_bytes = train_pack_bytes(cfg, BT);
     t.pack = c.take(t.pack_bytes / sizeof(float));
-    t.act16 = reinterpret_cast<__bf16*>(c.take(BT * cfg->F / 2));
+    t.act16 = reinterpret_cast<__bf16*>(c.take(BT * std::max(cfg->F, 3 * cfg->C) / 2));
     t.logits16 = reinterpret_cast<__bf16*>(c.take((BT * cfg->V + 1) / 2));
   }
   const bool keep = cfg->train_recompute == 0;
@@ -1452,7 +1466,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     HIPCHK(stk_launch_layernorm(BT, C, xin, bl.ln1_w, bl.ln1_b, a.h, nullptr, nullptr, st), "ln1");
     // x1 = xin + the time mix (the residual added in the output projection)
     CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), nullptr, a.x1, nullptr, a.tm,
-                        st, false, 0.f, prec, false, true, xin));
+                        st, false, 0.f, prec, false, true, xin, t.act16));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
     HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
     HIPCHK(gemm_run_x(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1,

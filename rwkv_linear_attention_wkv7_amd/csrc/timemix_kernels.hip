@@ -48,6 +48,11 @@ __device__ __forceinline__ void write_partials(const f4 (&p)[NV], float* part, i
 }
 
 // ------------------------------------------------------------- forward ----
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st16(__bf16* d, size_t e, f4 x) {
+  *reinterpret_cast<bf16x4_t*>(d + e) = __builtin_convertvector(x, bf16x4_t);
+}
+
 // Token shift + lerp: xs_c = x + (prev - x) mu_c, prev = x[t-1] (x_prev or 0 at t=0).
 __global__ __launch_bounds__(256) void shift_fwd(TmFwd p) {
   const size_t n4 = (size_t)p.BT * p.C / 4;
@@ -61,10 +66,16 @@ __global__ __launch_bounds__(256) void shift_fwd(TmFwd p) {
     if (t > 0) prev = ld4(p.x + e - p.C);
     else if (p.x_prev) prev = ld4(p.x_prev + (bt / p.T) * p.C + c);
     const f4 d = prev - x;
-    st4(p.xr + e, x + d * ld4(p.mu_r + c));
+    const f4 xr = x + d * ld4(p.mu_r + c), xk = x + d * ld4(p.mu_k + c), xv = x + d * ld4(p.mu_v + c);
+    st4(p.xr + e, xr);
     st4(p.xw + e, x + d * ld4(p.mu_w + c));
-    st4(p.xk + e, x + d * ld4(p.mu_k + c));
-    st4(p.xv + e, x + d * ld4(p.mu_v + c));
+    st4(p.xk + e, xk);
+    st4(p.xv + e, xv);
+    if (p.xr16) {
+      st16(p.xr16, e, xr);
+      st16(p.xk16, e, xk);
+      st16(p.xv16, e, xv);
+    }
     st4(p.xa + e, x + d * ld4(p.mu_a + c));
     st4(p.xg + e, x + d * ld4(p.mu_g + c));
     if (p.x_last && t == p.T - 1) st4(p.x_last + (bt / p.T) * p.C + c, x);

@@ -11,6 +11,9 @@ struct TmFwd {
   const float *x, *x_prev;
   const float *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
   float *xr, *xw, *xk, *xv, *xa, *xg, *x_last;
+  // optional bf16 copies of xr, xk, xv (dense [BT][C], rounded to nearest
+  // even) for the r/k/v products' A operands
+  __bf16 *xr16, *xk16, *xv16;
   // pre-WKV
   const float *k, *v, *ow, *oa, *ov, *w0, *a0, *v0, *k_k, *k_a;
   float* v_first;  // written on layer 0, read otherwise
