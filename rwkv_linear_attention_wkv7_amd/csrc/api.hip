@@ -661,7 +661,11 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                      const float* x_prev, const float* v_first, const float* s0, const float* dout,
                      const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
                      float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
-                     float* ds0, hipStream_t st, int prec, const wkv7_side* sd) {
+                     float* ds0, hipStream_t st, int prec, const wkv7_side* sd,
+                     __bf16* x16 = nullptr) {
+  // x16: NULL or 3 BT C bf16 of scratch for the pre-WKV backward's bf16
+  // copies of dr, dk, dv, which the r/k/v input-gradient products then take
+  // as their A operands
   const int BT = B * T, C = s->C, L = s->layer_id;
 
   // The weight gradients (X^T dY products, split along the tokens) feed
@@ -710,6 +714,11 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   p.mu_r = W->mu_r; p.mu_w = W->mu_w; p.mu_k = W->mu_k; p.mu_v = W->mu_v; p.mu_a = W->mu_a; p.mu_g = W->mu_g;
   p.dxr = bb.dxr; p.dxw = bb.dxw; p.dxk = bb.dxk; p.dxv = bb.dxv; p.dxa = bb.dxa; p.dxg = bb.dxg;
   p.dx = dx; p.dx_prev = dx_prev; p.part_shift = bb.part_shift;
+  if (x16 && prec == GEMM_BF16) {
+    p.dr16 = x16;
+    p.dk16 = x16 + (size_t)BT * C;
+    p.dv16 = x16 + 2 * (size_t)BT * C;
+  }
 
   HIPCHK(tm_launch_post_bwd(p, st), "post-wkv backward");
   // the time-mix decay exp(-0.606531 sigmoid(.)) lies in [0.545, 1]: the
@@ -753,9 +762,12 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
   if (L > 0)
     HIPCHK(gemm_run(prec, true, false, C, Dv, BT, m.xv, C, bb.d_lv, Dv, G->V1, Dv, 0.f, 0, nullptr, splitk_for(C, Dv, BT), sk, ss), "dV1");
   // r, k, v projections
-  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st), "dxr");
-  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st), "dxk");
-  HIPCHK(gemm_run(prec, false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1, nullptr, st), "dxv");
+  HIPCHK(gemm_run_x(prec, false, true, BT, C, C, bb.dr, C, W->Wr, C, bb.dxr, C, 0.f, 0, nullptr, 1, nullptr, st,
+                    p.dr16, nullptr), "dxr");
+  HIPCHK(gemm_run_x(prec, false, true, BT, C, C, bb.dk, C, W->Wk, C, bb.dxk, C, 0.f, 0, nullptr, 1, nullptr, st,
+                    p.dk16, nullptr), "dxk");
+  HIPCHK(gemm_run_x(prec, false, true, BT, C, C, bb.dv, C, W->Wv, C, bb.dxv, C, L > 0 ? 1.f : 0.f, 0, nullptr, 1,
+                    nullptr, st, p.dv16, nullptr), "dxv");
 
   HIPCHK(tm_launch_shift_bwd(p, st), "token shift backward");
   const int nblk = tm_num_token_blocks(BT);
@@ -1631,7 +1643,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
     CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
-                         nullptr, st, prec, sd));
+                         nullptr, st, prec, sd, t.act16));
     HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }

@@ -310,7 +310,9 @@ __global__ __launch_bounds__(256) void pre_bwd(TmBwd p) {
   const size_t t_end = min((size_t)p.BT, (size_t)(blk + 1) * TB);
   for (size_t bt = (size_t)blk * TB + grp; bt < t_end; bt += 16) {
     const size_t e = bt * p.C + c;
-    st4(p.dr + e, ld4(p.dr + e) + ld4(p.gr + e));
+    const f4 drn = ld4(p.dr + e) + ld4(p.gr + e);
+    st4(p.dr + e, drn);
+    if (p.dr16) st16(p.dr16, e, drn);
     const f4 dkmod = ld4(p.dkmod + e) + ld4(p.gk + e);
     const f4 dvmod = ld4(p.dvmod + e) + ld4(p.gv + e);
     const f4 a = ld4(p.a + e), kk = ld4(p.kk + e), k = ld4(p.k + e);
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(256) void pre_bwd(TmBwd p) {
     dk += dtk * kkw;
     pkk += dtk * k;
     st4(p.dk + e, dk);
+    if (p.dk16) st16(p.dk16, e, dk);
     const f4 dpa = da * a * (1.0f - a);
     pa0 += dpa;
     st4(p.dpre_a + e, dpa);
@@ -344,12 +347,14 @@ __global__ __launch_bounds__(256) void pre_bwd(TmBwd p) {
       f4 dv = dvmod;
       if (p.dvf_in) dv += ld4(p.dvf_in + e);
       st4(p.dv + e, dv);
+      if (p.dv16) st16(p.dv16, e, dv);
     } else {
       const f4 ov = ld4(p.ov + e), vf = ld4(p.v_first + e), v = ld4(p.v + e);
       f4 nu;
 #pragma unroll
       for (int j = 0; j < 4; j++) nu[j] = sigm(v0[j] + ov[j]);
       st4(p.dv + e, dvmod * (1.0f - nu));
+      if (p.dv16) st16(p.dv16, e, dvmod * (1.0f - nu));
       if (p.dvf_out) st4(p.dvf_out + e, p.dvf_accum ? ld4(p.dvf_out + e) + dvmod * nu : dvmod * nu);
       const f4 dpv = dvmod * (vf - v) * nu * (1.0f - nu);
       pv0 += dpv;

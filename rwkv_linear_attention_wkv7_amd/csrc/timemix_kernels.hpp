@@ -32,6 +32,9 @@ struct TmBwd {
   const float *gr, *gk, *gv, *gw, *gA, *gB;  // WKV7 gradients
   const float *a, *kk, *k, *w, *ow, *ov, *v, *v_first, *k_a, *k_k, *w0, *v0, *dvf_in;
   float *dk, *dv, *dpre_a, *dpre_w, *dpre_v, *dvf_out, *part_pre;
+  // optional bf16 copies of the final dr, dk, dv (dense [BT][C], rounded to
+  // nearest even) for the input-gradient products' A operands
+  __bf16 *dr16, *dk16, *dv16;
   int dvf_accum;  // dvf_out += instead of =
   // token shift backward
   const float *x, *x_prev, *mu_r, *mu_w, *mu_k, *mu_v, *mu_a, *mu_g;
