@@ -586,6 +586,7 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     p.xr16 = x16;
     p.xk16 = x16 + (size_t)BT * C;
     p.xv16 = x16 + 2 * (size_t)BT * C;
+    if (!decode) p.tg16 = x16;  // after the r/k/v products have read xr16
   }
   p.k = m.k; p.v = m.v; p.ow = m.ow; p.oa = m.oa; p.ov = m.ov;
   p.w0 = W->w0; p.a0 = W->a0; p.v0 = W->v0; p.k_k = W->k_k; p.k_a = W->k_a;
@@ -646,9 +647,11 @@ int tm_forward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const 
     HIPCHK(tm_launch_post_fwd(p, st), "post-wkv");
   }
   if (out_proj && resid)  // out = resid + tg Wo
-    HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, 0.f, EPI_ADD, resid, 1, nullptr, st), "o proj");
+    HIPCHK(gemm_run_x(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, 0.f, EPI_ADD, resid, 1, nullptr, st,
+                      p.tg16, nullptr), "o proj");
   else if (out_proj)
-    HIPCHK(gemm_run(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st), "o proj");
+    HIPCHK(gemm_run_x(prec, false, false, BT, C, C, m.tg, C, W->Wo, C, out, C, out_beta, 0, nullptr, 1, nullptr, st,
+                      p.tg16, nullptr), "o proj");
   return WKV7_OK;
 }
 
@@ -1253,6 +1256,7 @@ struct TrainBufs {
   // copies of xr, xk, xv [3][BT][C] (gemm_dtype == WKV7_BF16; one buffer,
   // reused on the caller's stream)
   __bf16* act16 = nullptr;
+  __bf16* sh16 = nullptr;  // the channel-mix shift's bf16 copy, past act16's [BT][max(F, 3C)]
   // bf16 copy [BT][V] of dlogits written by the cross-entropy kernel, the A of
   // the head's input-gradient product (gemm_dtype == WKV7_BF16)
   __bf16* logits16 = nullptr;
@@ -1310,7 +1314,8 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
   if (cfg->gemm_dtype == WKV7_BF16) {
     t.pack_bytes = train_pack_bytes(cfg, BT);
     t.pack = c.take(t.pack_bytes / sizeof(float));
-    t.act16 = reinterpret_cast<__bf16*>(c.take(BT * std::max(cfg->F, 3 * cfg->C) / 2));
+    t.act16 = reinterpret_cast<__bf16*>(c.take(BT * (std::max(cfg->F, 3 * cfg->C) + cfg->C) / 2));
+    t.sh16 = t.act16 + BT * std::max(cfg->F, 3 * cfg->C);
     t.logits16 = reinterpret_cast<__bf16*>(c.take((BT * cfg->V + 1) / 2));
   }
   const bool keep = cfg->train_recompute == 0;
@@ -1480,9 +1485,9 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     CHK(tm_forward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), nullptr, a.x1, nullptr, a.tm,
                         st, false, 0.f, prec, false, true, xin, t.act16));
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, bl.ln2_w, bl.ln2_b, a.h2, nullptr, nullptr, st), "ln2");
-    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st), "cm shift");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, xp_cm(l), bl.cm_mu_k, a.sh, nullptr, st, t.sh16), "cm shift");
     HIPCHK(gemm_run_x(prec, false, false, BT, F, C, a.sh, C, bl.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1,
-                      nullptr, st, nullptr, t.act16), "cm key");
+                      nullptr, st, t.sh16, t.act16), "cm key");
     return WKV7_OK;
   };
   // attention block i's forward from xin (its output is x1 + ka Wv)
@@ -1502,9 +1507,9 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
                                t.mws, st), "moba forward");
     HIPCHK(gemm_run(prec, false, false, BT, C, C, a.y, C, ab.Wo, C, a.x1, C, 0.f, EPI_ADD, xin, 1, nullptr, st), "o proj");
     HIPCHK(stk_launch_layernorm(BT, C, a.x1, ab.ln2_w, ab.ln2_b, a.h2, nullptr, nullptr, st), "attn ln2");
-    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, ab.cm_mu_k, a.sh, nullptr, st), "attn cm shift");
+    HIPCHK(stk_launch_cm_shift(BT, T, C, a.h2, nullptr, ab.cm_mu_k, a.sh, nullptr, st, t.sh16), "attn cm shift");
     HIPCHK(gemm_run_x(prec, false, false, BT, F, C, a.sh, C, ab.cm_Wk, F, a.ka, F, 0.f, EPI_SQRELU, nullptr, 1,
-                      nullptr, st, nullptr, t.act16), "attn cm key");
+                      nullptr, st, t.sh16, t.act16), "attn cm key");
     return WKV7_OK;
   };
   const auto order = block_order(L, cfg->n_attn);

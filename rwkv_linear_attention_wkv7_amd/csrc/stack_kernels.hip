@@ -11,6 +11,8 @@
 
 namespace stk {
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 constexpr float LN_EPS = 1e-5f;
 constexpr int MAXC4_LIMIT = 16;  // LayerNorm keeps a row in registers: C <= 64 * 4 * 16
 
@@ -80,7 +82,8 @@ __global__ __launch_bounds__(256) void layernorm_fwd(int R, int C, const float* 
 // x_last may alias x_prev only when T == 1 (same thread reads then writes).
 __global__ __launch_bounds__(256) void cm_shift(int BT, int T, int C, const float* __restrict__ x,
                                                 const float* x_prev, const float* __restrict__ mu,
-                                                float* __restrict__ sh, float* x_last) {
+                                                float* __restrict__ sh, float* x_last,
+                                                __bf16* __restrict__ sh16) {
   const size_t n4 = (size_t)BT * C / 4;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
     const size_t e = i * 4;
@@ -91,7 +94,9 @@ __global__ __launch_bounds__(256) void cm_shift(int BT, int T, int C, const floa
     f4 prev = {0.f, 0.f, 0.f, 0.f};
     if (t > 0) prev = *reinterpret_cast<const f4*>(x + e - C);
     else if (x_prev) prev = *reinterpret_cast<const f4*>(x_prev + (bt / T) * C + c);
-    *reinterpret_cast<f4*>(sh + e) = xv + (prev - xv) * *reinterpret_cast<const f4*>(mu + c);
+    const f4 shv = xv + (prev - xv) * *reinterpret_cast<const f4*>(mu + c);
+    *reinterpret_cast<f4*>(sh + e) = shv;
+    if (sh16) *reinterpret_cast<bf16x4_t*>(sh16 + e) = __builtin_convertvector(shv, bf16x4_t);
     if (x_last && t == T - 1) *reinterpret_cast<f4*>(x_last + (bt / T) * C + c) = xv;
   }
 }
@@ -193,9 +198,10 @@ hipError_t stk_launch_layernorm(int R, int C, const float* x, const float* w, co
   return hipGetLastError();
 }
 hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float* x_prev,
-                               const float* mu, float* sh, float* x_last, hipStream_t st) {
+                               const float* mu, float* sh, float* x_last, hipStream_t st,
+                               __bf16* sh16) {
   hipLaunchKernelGGL(stk::cm_shift, dim3(grid_for((size_t)BT * C / 4)), dim3(256), 0, st, BT, T, C,
-                     x, x_prev, mu, sh, x_last);
+                     x, x_prev, mu, sh, x_last, sh16);
   return hipGetLastError();
 }
 int stk_max_layernorm_width() { return 64 * 4 * stk::MAXC4_LIMIT; }
@@ -398,7 +404,6 @@ __global__ __launch_bounds__(256) void count_valid(int R, int V, const int* __re
 // normaliser in double).
 // d16 (optional): a bf16 copy of dlogits (dense [R][V], rounded to nearest
 // even) for a later bf16 matrix product.
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void st16(__bf16* d16, size_t e, f4 x) {
   *reinterpret_cast<bf16x4_t*>(d16 + e) = __builtin_convertvector(x, bf16x4_t);
 }

@@ -6,8 +6,10 @@ hipError_t stk_launch_emb_gather(int R, int C, int V, const int* tok, const floa
                                  hipStream_t st);
 hipError_t stk_launch_layernorm(int R, int C, const float* x, const float* w, const float* b,
                                 float* y, float* mean, float* rstd, hipStream_t st);
+// sh16: NULL or a bf16 copy of sh (dense [BT][C]) for the key product's A
 hipError_t stk_launch_cm_shift(int BT, int T, int C, const float* x, const float* x_prev,
-                               const float* mu, float* sh, float* x_last, hipStream_t st);
+                               const float* mu, float* sh, float* x_last, hipStream_t st,
+                               __bf16* sh16 = nullptr);
 
 // LayerNorm fused with up to six token-shift lerps, one token per row (T = 1).
 struct LnMix {

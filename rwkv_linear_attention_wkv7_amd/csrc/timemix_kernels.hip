@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void post_fwd(TmFwd p) {
   const float alpha = rowsum16(hsum4(r * kmod * ld4(p.r_k + c)));
   const f4 ygn = d * rstd * ld4(p.ln_w + c) + ld4(p.ln_b + c);
   st4(p.tg + e, (ygn + alpha * vmod) * g);
+  if (p.tg16) st16(p.tg16, e, (ygn + alpha * vmod) * g);
   if (l16 == 0) {
     p.mean[gidx] = mean;
     p.rstd[gidx] = rstd;

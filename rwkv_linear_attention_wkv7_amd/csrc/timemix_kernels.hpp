@@ -21,6 +21,7 @@ struct TmFwd {
   // post-WKV
   const float *y, *r, *g, *r_k, *ln_w, *ln_b;
   float *tg, *mean, *rstd, *alpha;
+  __bf16* tg16;  // optional bf16 copy of tg (post_fwd), the output product's A
 };
 
 struct TmBwd {
