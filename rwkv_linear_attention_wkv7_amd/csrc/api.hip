@@ -665,10 +665,10 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
                      const float* dsT, const TmCache& m, const TmBwdBufs& bb, tm_grads* G, float* dx,
                      float* dx_prev, const float* dv_first_in, float* dv_first_out, bool dvf_accum,
                      float* ds0, hipStream_t st, int prec, const wkv7_side* sd,
-                     __bf16* x16 = nullptr) {
+                     __bf16* x16 = nullptr, const __bf16* dout16 = nullptr) {
   // x16: NULL or 3 BT C bf16 of scratch for the pre-WKV backward's bf16
   // copies of dr, dk, dv, which the r/k/v input-gradient products then take
-  // as their A operands
+  // as their A operands; dout16: NULL or dout already rounded to bf16
   const int BT = B * T, C = s->C, L = s->layer_id;
 
   // The weight gradients (X^T dY products, split along the tokens) feed
@@ -696,7 +696,8 @@ int tm_backward_impl(const tm_shape* s, const tm_weights* W, int B, int T, const
 
   HIPCHK(fork_at(0), "backward fork");
   // output projection
-  HIPCHK(gemm_run(prec, false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st), "dtg");
+  HIPCHK(gemm_run_x(prec, false, true, BT, C, C, dout, C, W->Wo, C, bb.dtg, C, 0.f, 0, nullptr, 1, nullptr, st,
+                    prec == GEMM_BF16 ? dout16 : nullptr, nullptr), "dtg");
   HIPCHK(gemm_run(prec, true, false, C, C, BT, m.tg, C, dout, C, G->Wo, C, 0.f, 0, nullptr, splitk_for(C, C, BT), bb.splitk, ss), "dWo");
   TmBwd p;
   memset(&p, 0, sizeof(p));
@@ -1257,6 +1258,10 @@ struct TrainBufs {
   // reused on the caller's stream)
   __bf16* act16 = nullptr;
   __bf16* sh16 = nullptr;  // the channel-mix shift's bf16 copy, past act16's [BT][max(F, 3C)]
+  // bf16 copy [BT][C] of the upstream gradient a LayerNorm backward leaves in
+  // dx (every producer of t.dx writes it; read by the channel-mix dfk product)
+  // or dx1 (read by the time-mix output product's input gradient)
+  __bf16* dx16 = nullptr;
   // bf16 copy [BT][V] of dlogits written by the cross-entropy kernel, the A of
   // the head's input-gradient product (gemm_dtype == WKV7_BF16)
   __bf16* logits16 = nullptr;
@@ -1316,6 +1321,7 @@ void carve_train(Carver& c, const rwkv7_config* cfg, int B, int T, TrainBufs& t)
     t.pack = c.take(t.pack_bytes / sizeof(float));
     t.act16 = reinterpret_cast<__bf16*>(c.take(BT * (std::max(cfg->F, 3 * cfg->C) + cfg->C) / 2));
     t.sh16 = t.act16 + BT * std::max(cfg->F, 3 * cfg->C);
+    t.dx16 = reinterpret_cast<__bf16*>(c.take(BT * cfg->C / 2));
     t.logits16 = reinterpret_cast<__bf16*>(c.take((BT * cfg->V + 1) / 2));
   }
   const bool keep = cfg->train_recompute == 0;
@@ -1562,7 +1568,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
                     nullptr, st, t.logits16, nullptr), "dh");
   HIPCHK(gemm_run(prec, true, false, C, V, BT, t.h, C, t.logits, V, G->head, V, 0.f, EPI_NONE, nullptr,
                       splitk_for(C, V, BT), t.splitk, ss), "dhead");
-  HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(NB), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st), "ln_out bwd");
+  HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(NB), M->ln_out_w, t.dh, nullptr, t.dx, t.part_ln, st, t.dx16), "ln_out bwd");
   HIPCHK(reduce_ln(G->ln_out_w, G->ln_out_b), "ln_out grads");
   HIPCHK(stk_launch_fill_zero(t.dvf, tokC, st), "zero dv_first");
   auto join_side = [&]() -> hipError_t {
@@ -1578,7 +1584,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     if (!keep) CHK(attn_fwd(i, bin(pos), a));  // recompute this block's forward from its input
     // channel-mix backward (as in the RWKV-7 blocks)
     HIPCHK(gemm_run_x(prec, false, true, BT, F, C, t.dx, C, ab.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1,
-                      nullptr, st, nullptr, t.act16), "attn dfk");
+                      nullptr, st, t.dx16, t.act16), "attn dfk");
     HIPCHK(fork_here(), "backward fork");
     HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, ga.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                     splitk_for(F, C, BT), t.splitk, ss), "attn dWv");
@@ -1613,7 +1619,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     // the side stream's weight gradients read t.dx, t.dx1 and this block's
     // activations: joined before t.dx is written again
     HIPCHK(join_side(), "backward join");
-    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), ab.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "attn ln1 bwd");
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), ab.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st, t.dx16), "attn ln1 bwd");
     HIPCHK(reduce_ln(ga.ln1_w, ga.ln1_b), "attn ln1 grads");
     return WKV7_OK;
   };
@@ -1630,7 +1636,7 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
     if (!keep) CHK(block_fwd(l, bin(pos), a));  // recompute this block's forward from its input
     // channel-mix backward
     HIPCHK(gemm_run_x(prec, false, true, BT, F, C, t.dx, C, bl.cm_Wv, C, t.dfk, F, 0.f, EPI_SQRELU_BWD, a.ka, 1,
-                      nullptr, st, nullptr, t.act16), "dfk");
+                      nullptr, st, t.dx16, t.act16), "dfk");
     HIPCHK(fork_here(), "backward fork");  // t.dx and t.dfk complete
     HIPCHK(gemm_run(prec, true, false, F, C, BT, a.ka, F, t.dx, C, gb.cm_Wv, C, 0.f, EPI_NONE, nullptr,
                         splitk_for(F, C, BT), t.splitk, ss), "dWv");
@@ -1643,13 +1649,13 @@ int train_run(const rwkv7_config* cfg, const rwkv7_model* M, rwkv7_model_grads* 
       VecOut o = {{gb.cm_mu_k, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr}};
       HIPCHK(tm_launch_reduce(t.part_cm, 1, stk_num_shift_blocks(BT, C), C, o, st), "cm mu grad");
     }
-    HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st), "ln2 bwd");
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, a.x1, bl.ln2_w, t.dh, t.dx, t.dx1, t.part_ln, st, t.dx16), "ln2 bwd");
     HIPCHK(reduce_ln(gb.ln2_w, gb.ln2_b), "ln2 grads");
     // time-mix backward (input h, upstream dx1); v_first gradient summed over layers > 0
     CHK(tm_backward_impl(&s, &bl.tm, B, T, a.h, xp_tm(l), t.vf, s0_tm(l), t.dx1, nullptr, a.tm, t.tb,
                          &gb.tm, t.dh, nullptr, l == 0 ? t.dvf : nullptr, l > 0 ? t.dvf : nullptr, true,
-                         nullptr, st, prec, sd, t.act16));
-    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st), "ln1 bwd");
+                         nullptr, st, prec, sd, t.act16, t.dx16));
+    HIPCHK(stk_launch_layernorm_bwd(BT, C, bin(pos), bl.ln1_w, t.dh, t.dx1, t.dx, t.part_ln, st, t.dx16), "ln1 bwd");
     HIPCHK(reduce_ln(gb.ln1_w, gb.ln1_b), "ln1 grads");
   }
   const float* demb_src = t.dx;

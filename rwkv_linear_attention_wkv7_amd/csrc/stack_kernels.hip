@@ -237,7 +237,8 @@ __global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* 
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ dy,
                                                      const float* dres, float* dx,
-                                                     float* __restrict__ part) {
+                                                     float* __restrict__ part,
+                                                     __bf16* __restrict__ dx16) {
   __shared__ f4 red[2][4][MAXC4][64];
   const int blk = blockIdx.x, nblk = gridDim.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd(int R, int C, const float* 
       if (c4 < C4) {
         f4 o = rstd * (gv[j] - m1 - xv[j] * m2) + rv[j];
         dxr[c4] = o;
+        if (dx16) *reinterpret_cast<bf16x4_t*>(dx16 + (size_t)row * C + 4 * c4) = __builtin_convertvector(o, bf16x4_t);
       }
     }
   }
@@ -664,14 +666,15 @@ int stk_num_shift_blocks(int BT, int C) {
 }
 
 hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
-                                    const float* dres, float* dx, float* part, hipStream_t st) {
+                                    const float* dres, float* dx, float* part, hipStream_t st,
+                                    __bf16* dx16) {
   const dim3 g(stk_num_ln_blocks(R)), t(256);
   switch (ln_chunks(C)) {
-    case 1: hipLaunchKernelGGL(stk::layernorm_bwd<1>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
-    case 2: hipLaunchKernelGGL(stk::layernorm_bwd<2>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
-    case 4: hipLaunchKernelGGL(stk::layernorm_bwd<4>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
-    case 8: hipLaunchKernelGGL(stk::layernorm_bwd<8>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
-    default: hipLaunchKernelGGL(stk::layernorm_bwd<16>, g, t, 0, st, R, C, x, w, dy, dres, dx, part); break;
+    case 1: hipLaunchKernelGGL(stk::layernorm_bwd<1>, g, t, 0, st, R, C, x, w, dy, dres, dx, part, dx16); break;
+    case 2: hipLaunchKernelGGL(stk::layernorm_bwd<2>, g, t, 0, st, R, C, x, w, dy, dres, dx, part, dx16); break;
+    case 4: hipLaunchKernelGGL(stk::layernorm_bwd<4>, g, t, 0, st, R, C, x, w, dy, dres, dx, part, dx16); break;
+    case 8: hipLaunchKernelGGL(stk::layernorm_bwd<8>, g, t, 0, st, R, C, x, w, dy, dres, dx, part, dx16); break;
+    default: hipLaunchKernelGGL(stk::layernorm_bwd<16>, g, t, 0, st, R, C, x, w, dy, dres, dx, part, dx16); break;
   }
   return hipGetLastError();
 }

@@ -31,8 +31,10 @@ int stk_max_layernorm_width();
 int stk_num_ln_blocks(int R);
 // partial rows of the channel-mix shift backward (one per workgroup of tokens)
 int stk_num_shift_blocks(int BT, int C);
+// dx16: NULL or a bf16 copy of dx (dense [R][C]) for a later product's A
 hipError_t stk_launch_layernorm_bwd(int R, int C, const float* x, const float* w, const float* dy,
-                                    const float* dres, float* dx, float* part, hipStream_t st);
+                                    const float* dres, float* dx, float* part, hipStream_t st,
+                                    __bf16* dx16 = nullptr);
 hipError_t stk_launch_cm_shift_bwd(int BT, int T, int C, const float* x, const float* x_prev,
                                    const float* mu, const float* dsh, float* dx, float* dx_prev,
                                    float* part, hipStream_t st);
