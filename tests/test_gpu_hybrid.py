@@ -8,6 +8,8 @@ _compare).  The chunk selection inside the stack is taken on the GPU's fp32
 scores and the oracle's f64 ones; the seeded inputs here have no near-tie at
 any selection boundary, and a selection that differed would show as
 gradients far outside these tolerances."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -120,6 +122,29 @@ def test_hybrid_recompute_gives_the_same_bits(hip):
     loss_r = hip.rwkv7_train_step(dm_r, gr, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
     torch.cuda.synchronize()
     assert float(loss_r.item()) == loss
+    for (n, a, _), (_, b, _) in zip(_pairs(grads.g, _dummy(grads.g)), _pairs(gr.g, _dummy(gr.g))):
+        assert torch.equal(a, b), n
+
+
+def test_hybrid_recompute_bf16_handoffs_give_the_same_bits(hip):
+    """The same with bf16 GEMMs at a width whose products take the bf16
+    direct-to-LDS path (B=2 T=2048 C=1024 F=4096): there the producers' bf16
+    copies (shift, post-WKV, channel-mix shift and key product, pre-WKV and
+    LayerNorm backwards, cross-entropy) feed the products through one reused
+    buffer, which the recomputed forward of each block rewrites inside the
+    backward; the results must not depend on it."""
+    from rwkv_linear_attention_wkv7_amd import binding
+    C, H, F, V = 1024, 16, 4096, 1024
+    m, cfg, dm, grads, x, y, loss = _setup(hip, 2, 1, C, H, F, V, 2, 2048, 64, 4, seed=21, std=0.02,
+                                           perturbed=True, gemm="bf16")
+    dm_r = binding.DecodeModel(dict(n_layer=2, C=C, H=H, F=F, V=V, ranks=(64, 64, 32, 128), use_ln0=0,
+                                    gemm_dtype="bf16", train_recompute=1, n_attn=1, moba_chunk=64,
+                                    moba_topk=4), dm.w)
+    gr = binding.TrainGrads(dm_r)
+    print("[hybrid] bf16 recompute at width 1024", flush=True)
+    loss_r = hip.rwkv7_train_step(dm_r, gr, torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda())
+    torch.cuda.synchronize()
+    assert math.isfinite(loss) and float(loss_r.item()) == loss
     for (n, a, _), (_, b, _) in zip(_pairs(grads.g, _dummy(grads.g)), _pairs(gr.g, _dummy(gr.g))):
         assert torch.equal(a, b), n
 
